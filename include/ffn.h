@@ -1,0 +1,161 @@
+/*
+ * ffn.h — C ABI of libffn.so: the forward hot path of a Llama-style dense
+ * SwiGLU FFN block and its FP8 single-token decode form, on AMD MI355X (gfx950).
+ *
+ * Conventions for every entry point
+ *   - Every pointer is DEVICE memory (hipMalloc / torch CUDA tensors) unless
+ *     stated otherwise.  The caller allocates and owns every buffer; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (0 = the null stream).  Results are
+ *     valid once the stream has been synchronised; no call synchronises.
+ *   - Matrices are row-major and contiguous.  Weights are [out, in], so both
+ *     operands of every matmul are contiguous along the reduction dimension.
+ *   - bf16 = IEEE binary32 truncated to 16 bits (round to nearest even);
+ *     e4m3 = OCP E4M3FN (max 448, NaN 0x7F/0xFF, no infinities).
+ *   - Abs-max outputs are OVERWRITTEN with max|x| of the tensor just written
+ *     (the library clears them itself on `stream` first).
+ *   - A dequantisation scale is absmax/448 (1.0 when absmax == 0); codes are
+ *     e4m3(x * (448/absmax)), with the product taken in fp32, rounded to
+ *     nearest even and saturated at +-448.
+ *   - Errors are return values.  Arguments are validated before any HIP call:
+ *     a NULL required pointer, a negative size or an unknown enum gives
+ *     FFN_ERR_INVALID; a size the kernels do not support, or a pointer not
+ *     aligned to 16 bytes, gives FFN_ERR_UNSUPPORTED; a failed launch gives
+ *     FFN_ERR_HIP.  Nothing is launched when validation fails.  A zero row
+ *     count (N or M == 0) is valid and launches nothing.  ffn_last_error()
+ *     returns a thread-local description of the last non-OK status.
+ *   - Calls that share an output buffer on different streams race; calls on one
+ *     stream are ordered.
+ *
+ * Citations name the page and the function on it that defines the operation:
+ *   [llmq model]  IST-DASLab llmq, src/models/llama_model.cpp
+ *   [llmq state]  IST-DASLab llmq, src/models/llama_run_state.cpp
+ *   [metrale]     metrale_model_layers/layers/dense_ffn_decode.rs
+ */
+#ifndef FFN_H
+#define FFN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    FFN_OK = 0,
+    FFN_ERR_INVALID = 1,      /* NULL required pointer, negative size, bad enum   */
+    FFN_ERR_UNSUPPORTED = 2,  /* size / alignment outside what the kernels handle */
+    FFN_ERR_HIP = 3           /* a HIP launch or runtime call failed               */
+} ffn_status_t;
+
+typedef enum {
+    FFN_BF16 = 0,             /* bf16 operands, no scales                          */
+    FFN_E4M3 = 1              /* e4m3 operands with per-tensor fp32 scales         */
+} ffn_dtype_t;
+
+/* Fused residual add + RMSNorm, saving rstd, with the output's abs-max.
+ * [llmq model] LLamaModel::_forward_block, fused_residual_rmsnorm_forward
+ * (residual stream + attention output -> LN2, LN2_Rstd, LN2 abs-max);
+ * LLamaModel::forward, rmsnorm_forward for the form without a residual.
+ * [llmq state] allocate_basic_fwd_tensors: rstd is fp32 [B,T]; the norm output
+ * may overwrite its input.
+ *
+ *   r      = bf16(inp + addend)                 -> residual_out   (bf16 [N,C])
+ *   rstd_i = 1 / sqrt(sum_j r_ij^2 / C + eps)   -> rstd           (fp32 [N])
+ *   y      = bf16(r * rstd * weight)            -> y              (bf16 [N,C])
+ *   max|y|                                      -> absmax         (fp32 [1])
+ *
+ * addend == NULL: plain RMSNorm, r = inp, residual_out must be NULL.
+ * absmax may be NULL (not computed).  y may alias inp or addend (each row is
+ * read completely before it is written); residual_out may alias inp.
+ * Supported: C % 8 == 0, 8 <= C <= 16384.  N >= 0. */
+ffn_status_t ffn_rmsnorm_fwd(void* y, float* rstd, void* residual_out, float* absmax,
+                             const void* inp, const void* addend, const void* weight,
+                             float eps, int64_t N, int64_t C, hipStream_t stream);
+
+/* Per-tensor abs-max FP8 e4m3 quantisation of a bf16 tensor of n elements.
+ * [llmq model] forward_qmm, quantize_with_abs_max(inp.Quant, inp.Quant.scale(),
+ * inp.Value, inp.Quant.abs_max(), B*T*C); LLamaModel::_forward_block, abs_max.
+ * [llmq state] allocate_fwd_quant_tensors: e4m3 copies, fp32 abs-max and scale.
+ *
+ *   compute_absmax != 0: *absmax = max|x| is computed first (overwritten);
+ *   compute_absmax == 0: *absmax is read as given (e.g. from ffn_rmsnorm_fwd
+ *                        or the fused ffn_gateup epilogue).
+ *   *scale = absmax/448 (1 if absmax == 0);  q = e4m3(x * 448/absmax).
+ * q: e4m3 [n]; x: bf16 [n]; scale, absmax: fp32 [1].  Any n >= 0. */
+ffn_status_t ffn_quant_absmax(uint8_t* q, float* scale, float* absmax, const void* x,
+                              int64_t n, int compute_absmax, hipStream_t stream);
+
+/* Per-row abs-max e4m3 quantisation of a bf16 weight [rows, cols]: the
+ * QuantizedWeight { weight, row_scale } layout the FP8 decode consumes.
+ * [metrale] DenseFfnLayer::forward, FP8 arm (gate_proj/up_proj/down_proj
+ * weight + row_scale).  An offline weight-preparation step, not part of the
+ * per-token path.  q: e4m3 [rows, cols]; row_scale: fp32 [rows].
+ * Supported: cols % 8 == 0. */
+ffn_status_t ffn_quant_rows(uint8_t* q, float* row_scale, const void* w,
+                            int64_t rows, int64_t cols, hipStream_t stream);
+
+/* Fused gate+up projection, optionally with the SwiGLU epilogue.
+ * [llmq model] LLamaModel::_forward_block, forward_qmm(MlpUp, LN2, MLP_Up_w,
+ * B, T, C, 2*D) and swiglu_forward; forward_qmm: matmul TN, scaled by
+ * weight.scale() and inp.Quant.scale() when the operands are FP8.
+ *
+ *   GU[n,o] = sum_k x[n,k] * w[o,k]  (* x_scale * w_scale for E4M3), o < 2H,
+ *   rows [0,H) of w are the gate, rows [H,2H) the up projection.
+ *   fuse_swiglu == 0: out = bf16(GU)                      bf16 [N, 2H]
+ *   fuse_swiglu != 0: out = bf16(silu(g) * u), g = bf16(GU[:, :H]),
+ *                     u = bf16(GU[:, H:])                 bf16 [N, H]
+ *   out_absmax (nullable) = max|out|.
+ * x: bf16 or e4m3 [N,C]; w: same dtype [2H,C]; x_scale, w_scale: fp32 [1],
+ * required for E4M3, ignored for BF16.  fp32 accumulation.
+ * Supported: C % 128 == 0, H % 128 == 0, N >= 0. */
+ffn_status_t ffn_gateup(void* out, float* out_absmax, const void* x, const float* x_scale,
+                        const void* w, const float* w_scale, ffn_dtype_t dtype, int fuse_swiglu,
+                        int64_t N, int64_t C, int64_t H, hipStream_t stream);
+
+/* SwiGLU on an unfused gate+up output, with the output's abs-max.
+ * [llmq model] LLamaModel::_forward_block, swiglu_forward(SwiGLu, MlpUp,
+ * SwiGLu abs-max, B, T, D).  h = bf16(silu(g) * u), g = gu[:, :H], u = gu[:, H:].
+ * h: bf16 [N,H]; gateup: bf16 [N,2H]; absmax nullable.  Supported: H % 8 == 0. */
+ffn_status_t ffn_swiglu(void* h, float* absmax, const void* gateup,
+                        int64_t N, int64_t H, hipStream_t stream);
+
+/* Down projection.  [llmq model] LLamaModel::_forward_block,
+ * forward_qmm(MlpDown, SwiGLu, MLP_Down_w, B, T, D, C).
+ *   out[n,c] = bf16(sum_j h[n,j] * w[c,j]  (* h_scale * w_scale for E4M3))
+ * out: bf16 [N,C]; h: bf16 or e4m3 [N,H]; w: same dtype [C,H]; scales fp32 [1]
+ * (E4M3 only).  Supported: C % 128 == 0, H % 128 == 0. */
+ffn_status_t ffn_down(void* out, const void* h, const float* h_scale,
+                      const void* w, const float* w_scale, ffn_dtype_t dtype,
+                      int64_t N, int64_t H, int64_t C, hipStream_t stream);
+
+/* FP8-weight, bf16-activation decode FFN for M tokens (split-SiLU arm).
+ * [metrale] DenseFfnLayer::forward, FP8 arm: w8a16_gemv_dual (gate and up in
+ * one pass, per-row scales), silu_mul in place, w8a16_gemv for the down
+ * projection.  The SiLU * up product is fused into the dual GEMV's epilogue.
+ *
+ *   g = bf16(s_gate[n] * sum_k w_gate[n,k] x[m,k]),  u likewise,
+ *   h = bf16(silu(g) * u)                                    -> h   bf16 [M,H]
+ *   out[m,c] = bf16(s_down[c] * sum_n w_down[c,n] h[m,n])    -> out bf16 [M,C]
+ * x: bf16 [M,C]; w_gate, w_up: e4m3 [H,C]; w_down: e4m3 [C,H];
+ * s_gate, s_up: fp32 [H]; s_down: fp32 [C].  h is caller-provided and also
+ * returned.  Supported: 0 <= M <= 32, C % 128 == 0, H % 128 == 0. */
+ffn_status_t ffn_decode_gemv(void* out, void* h, const void* x,
+                             const uint8_t* w_gate, const float* s_gate,
+                             const uint8_t* w_up, const float* s_up,
+                             const uint8_t* w_down, const float* s_down,
+                             int64_t M, int64_t C, int64_t H, hipStream_t stream);
+
+/* Thread-local text for the last non-OK status of this thread ("" if none). */
+const char* ffn_last_error(void);
+
+/* Library version string. */
+const char* ffn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFN_H */

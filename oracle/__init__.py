@@ -29,7 +29,11 @@ from .codecs import (
 )
 from .ffn import (
     residual_add,
+    rms_rstd,
+    rms_apply,
     rmsnorm_fwd,
+    absmax_of,
+    scales_from_absmax,
     quant_absmax,
     quant_rows,
     gemm_bf16,
@@ -38,13 +42,16 @@ from .ffn import (
     swiglu,
     gateup,
     down,
+    decode_dual,
+    decode_down,
     decode_gemv,
     block_forward,
 )
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "bf16_round", "e4m3_decode",
-    "e4m3_encode", "E4M3_MAX", "residual_add", "rmsnorm_fwd", "quant_absmax",
+    "e4m3_encode", "E4M3_MAX", "residual_add", "rms_rstd", "rms_apply", "rmsnorm_fwd",
+    "absmax_of", "scales_from_absmax", "quant_absmax",
     "quant_rows", "gemm_bf16", "gemm_fp8", "silu", "swiglu", "gateup", "down",
-    "decode_gemv", "block_forward",
+    "decode_dual", "decode_down", "decode_gemv", "block_forward",
 ]

@@ -44,6 +44,26 @@ def residual_add(a_bits, b_bits):
     return f64_to_bf16_bits(bf16_bits_to_f64(a_bits) + bf16_bits_to_f64(b_bits))
 
 
+def rms_rstd(r_bits, eps):
+    """rstd_i = fp32( 1 / sqrt( sum_j r_ij^2 / C + eps ) ) for a bf16 [N, C]
+    tensor (the rstd that ``fused_residual_rmsnorm_forward`` saves, fp32
+    ``[B, T]``).  Reading: eps inside the square root, mean by division by C."""
+    r = bf16_bits_to_f64(r_bits)
+    C = r.shape[-1]
+    ms = np.sum(r * r, axis=-1) / C
+    return (1.0 / np.sqrt(ms + np.float64(_f32(eps)))).astype(np.float32)
+
+
+def rms_apply(r_bits, rstd, weight_bits):
+    """y_ij = bf16( r_ij * rstd_i * w_j ) with the stored fp32 rstd, and
+    max |y| over the stored bf16 y.  Returns (y_bits, absmax float32)."""
+    r = bf16_bits_to_f64(r_bits)
+    w = bf16_bits_to_f64(weight_bits)
+    y = bf16_round(r * np.asarray(rstd, np.float32).astype(np.float64)[..., None] * w[None, :])
+    absmax = _f32(np.max(np.abs(y))) if y.size else _f32(0.0)
+    return f64_to_bf16_bits(y), absmax
+
+
 def rmsnorm_fwd(inp_bits, addend_bits, weight_bits, eps):
     """Fused residual add + RMSNorm with saved rstd and the output's abs-max.
 
@@ -62,20 +82,15 @@ def rmsnorm_fwd(inp_bits, addend_bits, weight_bits, eps):
 
     Returns (residual_bits or None, y_bits, rstd float32[N], absmax float32).
     """
-    a = bf16_bits_to_f64(inp_bits)
     if addend_bits is None:
         r_bits = None
-        r = a
+        r = np.asarray(inp_bits)
     else:
         r_bits = residual_add(inp_bits, addend_bits)
-        r = bf16_bits_to_f64(r_bits)
-    C = r.shape[-1]
-    ms = np.sum(r * r, axis=-1) / C
-    rstd = (1.0 / np.sqrt(ms + np.float64(_f32(eps)))).astype(np.float32)
-    w = bf16_bits_to_f64(weight_bits)
-    y = bf16_round(r * rstd.astype(np.float64)[..., None] * w[None, :])
-    absmax = _f32(np.max(np.abs(y))) if y.size else _f32(0.0)
-    return r_bits, f64_to_bf16_bits(y), rstd, absmax
+        r = r_bits
+    rstd = rms_rstd(r, eps)
+    y, absmax = rms_apply(r, rstd, weight_bits)
+    return r_bits, y, rstd, absmax
 
 
 def absmax_of(bits):
@@ -194,24 +209,34 @@ def down(h, w, h_scale=None, w_scale=None):
     return gemm_fp8(h, h_scale, w, w_scale)
 
 
-def decode_gemv(x_bits, wg, sg, wu, su, wd, sd):
-    """Single-token (or few-token) FP8 W8A16 decode FFN, split-SiLU arm
-    (dense_ffn_decode.rs, ``DenseFfnLayer::forward``, FP8 arm):
+def decode_dual(x_bits, wg, sg, wu, su):
+    """The dual gate/up GEMV with the SiLU product (dense_ffn_decode.rs,
+    ``DenseFfnLayer::forward``, FP8 arm: ``w8a16_gemv_dual`` then ``silu_mul``):
 
-      g[m,n] = bf16( sg[n] * sum_k dec(Wg[n,k]) * x[m,k] )      w8a16_gemv_dual
-      u[m,n] = bf16( su[n] * sum_k dec(Wu[n,k]) * x[m,k] )
-      h[m,n] = bf16( silu(g) * u )                              silu_mul, in place
-      y[m,c] = bf16( sd[c] * sum_n dec(Wd[c,n]) * h[m,n] )      w8a16_gemv (down)
+      g[m,n] = bf16( sg[n] * sum_k dec(Wg[n,k]) * x[m,k] ),  u likewise
+      h[m,n] = bf16( silu(g) * u )
 
     Readings: the intermediates are bf16 (16-bit activations); each row scale
-    multiplies the finished dot product.
-    Returns (y_bits [M, C], h_bits [M, H])."""
+    multiplies the finished dot product.  Returns h_bits [M, H]."""
     x = bf16_bits_to_f64(x_bits)
     g = bf16_round(_matmul_nt(x, e4m3_decode(wg)) * np.asarray(sg, np.float32).astype(np.float64)[None, :])
     u = bf16_round(_matmul_nt(x, e4m3_decode(wu)) * np.asarray(su, np.float32).astype(np.float64)[None, :])
-    h = bf16_round(silu(g) * u)
-    y = bf16_round(_matmul_nt(h, e4m3_decode(wd)) * np.asarray(sd, np.float32).astype(np.float64)[None, :])
-    return f64_to_bf16_bits(y), f64_to_bf16_bits(h)
+    return f64_to_bf16_bits(silu(g) * u)
+
+
+def decode_down(h_bits, wd, sd):
+    """The down GEMV (``w8a16_gemv`` with the down weight, n_out = hidden,
+    k_in = intermediate): y[m,c] = bf16( sd[c] * sum_n dec(Wd[c,n]) * h[m,n] )."""
+    h = bf16_bits_to_f64(h_bits)
+    return f64_to_bf16_bits(_matmul_nt(h, e4m3_decode(wd)) * np.asarray(sd, np.float32).astype(np.float64)[None, :])
+
+
+def decode_gemv(x_bits, wg, sg, wu, su, wd, sd):
+    """Single-token (or few-token) FP8 W8A16 decode FFN, split-SiLU arm (the
+    default arm of dense_ffn_decode.rs, ``DenseFfnLayer::forward``, FP8 arm):
+    ``decode_dual`` then ``decode_down``.  Returns (y_bits [M, C], h_bits [M, H])."""
+    h = decode_dual(x_bits, wg, sg, wu, su)
+    return decode_down(h, wd, sd), h
 
 
 def block_forward(inp, addend, w_norm, w_gu, w_d, eps, fp8=False):

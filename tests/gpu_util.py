@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: moving bit patterns between numpy and
+device tensors, and the error measures the tests apply."""
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import codecs as K
+
+
+def say(msg):
+    """Name the case before each GPU step, flushed, so a fault names it."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev_u8(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).cuda()
+
+
+def dev_f32(v):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(v, np.float32)).reshape(-1)).cuda()
+
+
+def host_bits(t):
+    """bf16 device tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_u8(t):
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+def host_f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def empty_bf16(*shape):
+    return torch.empty(*shape, dtype=torch.bfloat16, device="cuda")
+
+
+def empty_f32(*shape):
+    return torch.empty(*shape, dtype=torch.float32, device="cuda")
+
+
+def empty_u8(*shape):
+    return torch.empty(*shape, dtype=torch.uint8, device="cuda")
+
+
+def rel_err(got_bits, ref_bits):
+    """max_i |g_i - r_i| / max(|r_i|, rms(r)) over bf16 tensors: a relative
+    error that falls back to the tensor's RMS where r_i is near zero."""
+    g = K.bf16_bits_to_f64(got_bits).reshape(-1)
+    r = K.bf16_bits_to_f64(ref_bits).reshape(-1)
+    if r.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(r * r))
+    den = np.maximum(np.abs(r), rms)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.abs(g - r) / den))
+
+
+def ulp_diff(a_bits, b_bits):
+    a = np.asarray(a_bits).astype(np.int32)
+    b = np.asarray(b_bits).astype(np.int32)
+    ka = np.where(a & 0x8000, -(a & 0x7FFF), a)
+    kb = np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ka - kb)

@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: libffn.so loads, exports every entry point that
+include/ffn.h declares, and rejects bad arguments before touching HIP.
+
+Every call below is built to fail validation (NULL, negative, unsupported or
+misaligned arguments), so no kernel is ever launched; the fake addresses are
+never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffn.h")
+LIB = os.path.join(ROOT, "transformer_ffn_block_residual_amd", "libffn.so")
+
+INVALID, UNSUPPORTED = 1, 2
+A = 0x10000          # aligned fake device address (never dereferenced)
+MIS = 0x10004        # misaligned fake address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:ffn_status_t|const char\*)\s+(ffn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libffn.so not built (run __graft_entry__.build())")
+    from transformer_ffn_block_residual_amd import binding
+    return binding._lib
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_swiglu", "ffn_down",
+              "ffn_decode_gemv", "ffn_last_error", "ffn_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert b"gfx950" in lib.ffn_version()
+
+
+def _err(lib):
+    return lib.ffn_last_error().decode()
+
+
+def test_rmsnorm_validation(lib):
+    f = lib.ffn_rmsnorm_fwd
+    assert f(None, A, A, A, A, A, A, 1e-5, 4, 256, None) == INVALID
+    assert "y is NULL" in _err(lib)
+    assert f(A, A, A, A, A, A, A, 1e-5, -1, 256, None) == INVALID
+    assert f(A, A, None, A, A, A, A, 1e-5, 4, 256, None) == INVALID      # addend without residual_out
+    assert f(A, A, A, A, A, None, A, 1e-5, 4, 256, None) == INVALID      # residual_out without addend
+    assert f(A, A, A, A, A, A, A, -1.0, 4, 256, None) == INVALID
+    assert f(A, A, A, A, A, A, A, 1e-5, 4, 12, None) == UNSUPPORTED      # C % 8
+    assert f(A, A, A, A, A, A, A, 1e-5, 4, 32768, None) == UNSUPPORTED   # C too large
+    assert f(MIS, A, A, A, A, A, A, 1e-5, 4, 256, None) == UNSUPPORTED
+    assert "aligned" in _err(lib)
+
+
+def test_quant_validation(lib):
+    f = lib.ffn_quant_absmax
+    assert f(A, A, None, A, 16, 1, None) == INVALID
+    assert f(A, A, A, A, -3, 1, None) == INVALID
+    assert f(A, A + 64, A + 64, A, 16, 0, None) == INVALID  # scale aliases absmax
+    assert f(MIS, A, A + 64, A, 16, 0, None) == UNSUPPORTED
+    g = lib.ffn_quant_rows
+    assert g(A, A, A, 4, 12, None) == UNSUPPORTED
+    assert g(A, None, A, 4, 16, None) == INVALID
+
+
+def test_gemm_validation(lib):
+    f = lib.ffn_gateup
+    assert f(A, None, A, None, A, None, 1, 1, 64, 256, 768, None) == INVALID   # fp8 without scales
+    assert f(A, None, A, A, A, A, 7, 1, 64, 256, 768, None) == INVALID         # unknown dtype
+    assert f(A, None, A, None, A, None, 0, 1, 64, 200, 768, None) == UNSUPPORTED  # C % 128
+    assert f(A, None, A, None, A, None, 0, 1, 64, 256, 100, None) == UNSUPPORTED  # H % 128
+    assert f(A, None, A, None, A, None, 0, 1, -64, 256, 768, None) == INVALID
+    assert f(A, None, MIS, None, A, None, 0, 1, 64, 256, 768, None) == UNSUPPORTED
+    assert f(A, None, A, None, A, None, 0, 1, 1 << 20, 4096, 768, None) == UNSUPPORTED  # > 4 GiB operand
+    d = lib.ffn_down
+    assert d(A, A, None, A, None, 1, 64, 768, 256, None) == INVALID
+    assert d(A, A, None, A, None, 0, 64, 700, 256, None) == UNSUPPORTED
+    assert d(None, A, None, A, None, 0, 64, 768, 256, None) == INVALID
+    s = lib.ffn_swiglu
+    assert s(A, None, A, 4, 12, None) == UNSUPPORTED
+    assert s(None, None, A, 4, 16, None) == INVALID
+
+
+def test_decode_validation(lib):
+    f = lib.ffn_decode_gemv
+    args = [A, A + 4096, A + 8192, A, A, A, A, A, A]
+    assert f(*args, 33, 4096, 14336, None) == UNSUPPORTED
+    assert f(*args, 1, 4000, 14336, None) == UNSUPPORTED
+    assert f(*args, -1, 4096, 14336, None) == INVALID
+    bad = list(args)
+    bad[4] = None
+    assert f(*bad, 1, 4096, 14336, None) == INVALID
+    alias = list(args)
+    alias[1] = alias[2]
+    assert f(*alias, 1, 4096, 14336, None) == INVALID
+    mis = list(args)
+    mis[3] = MIS
+    assert f(*mis, 1, 4096, 14336, None) == UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors_and_short_buffers():
+    if not os.path.exists(LIB):
+        pytest.skip("libffn.so not built")
+    import torch
+    import transformer_ffn_block_residual_amd as F
+    with pytest.raises(F.FFNError):
+        F.ffn_swiglu(torch.empty(8, dtype=torch.bfloat16), None, torch.empty(16, dtype=torch.bfloat16), 1, 8)

@@ -1,0 +1,298 @@
+"""GPU parity of each HIP kernel against the CPU oracle, through the C ABI.
+
+Bit-exact where the result is unique (residual sums, abs-maxes, e4m3 codes given
+the same input and abs-max, GEMMs on integer-valued inputs, fused vs unfused
+SwiGLU); within a stated tolerance where fp32 summation order or the hardware
+exp/rsqrt decides the last bit.  Shapes span several tiles and ragged tails.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import codecs as K
+from transformer_ffn_block_residual_amd import workloads as W
+from tests.gpu_util import (say, dev_bf16, dev_u8, dev_f32, host_bits, host_u8, host_f32, empty_bf16,
+                            empty_f32, empty_u8, rel_err, ulp_diff)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_ffn_block_residual_amd as F
+    return F
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+
+RMS_SHAPES = [(64, 256, True), (37, 384, True), (300, 4096, True), (129, 3584, True), (5, 8192, False),
+              (3, 16384, True), (1, 8, True), (77, 1000, False)]
+
+
+@pytest.mark.parametrize("N,C,add", RMS_SHAPES)
+def test_rmsnorm(F, N, C, add):
+    say(f"rmsnorm N={N} C={C} add={add}")
+    d = W.block_inputs(N, C, 128, seed=N * 7 + C, outliers=(C == 4096))
+    inp, addend, w = d["inp"], d["addend"] if add else None, d["w_norm"]
+    y, rstd, am = empty_bf16(N, C), empty_f32(N), empty_f32(1)
+    res = empty_bf16(N, C) if add else None
+    F.ffn_rmsnorm_fwd(y, rstd, res, am, dev_bf16(inp), dev_bf16(addend) if add else None, dev_bf16(w),
+                      1e-5, N, C)
+    torch.cuda.synchronize()
+    r_ref, y_ref, rstd_ref, am_ref = O.rmsnorm_fwd(inp, addend, w, 1e-5)
+    if add:
+        assert np.array_equal(host_bits(res), r_ref)                       # unique: bit-exact
+    g_rstd = host_f32(rstd)
+    assert np.max(np.abs(g_rstd / rstd_ref - 1)) < 1e-5
+    gy = host_bits(y)
+    # y given the GPU's own rstd: the oracle's single rounding vs the kernel's
+    # two fp32 roundings can differ by one bf16 ulp, rarely
+    y_cond, _ = O.rms_apply(r_ref if add else inp, g_rstd, w)
+    assert ulp_diff(gy, y_cond).max() <= 1
+    assert np.mean(ulp_diff(gy, y_cond) != 0) < 1e-3
+    assert rel_err(gy, y_ref) < 2e-2
+    assert host_f32(am)[0] == np.max(np.abs(K.bf16_bits_to_f64(gy)))  # abs-max of what was stored
+
+
+def test_rmsnorm_in_place_and_empty(F):
+    N, C = 50, 2048
+    say(f"rmsnorm in place N={N} C={C}")
+    d = W.block_inputs(N, C, 128, seed=3)
+    inp = dev_bf16(d["inp"])
+    addend = dev_bf16(d["addend"])
+    res, rstd, am = empty_bf16(N, C), empty_f32(N), empty_f32(1)
+    F.ffn_rmsnorm_fwd(addend, rstd, res, am, inp, addend, dev_bf16(d["w_norm"]), 1e-5, N, C)  # y overwrites addend
+    torch.cuda.synchronize()
+    r_ref, y_ref, _, am_ref = O.rmsnorm_fwd(d["inp"], d["addend"], d["w_norm"], 1e-5)
+    assert np.array_equal(host_bits(res), r_ref)
+    assert rel_err(host_bits(addend), y_ref) < 2e-2
+    # N = 0: nothing launched except clearing the abs-max
+    am.fill_(5.0)
+    F.ffn_rmsnorm_fwd(empty_bf16(1, C), empty_f32(1), None, am, inp, None, dev_bf16(d["w_norm"]), 1e-5, 0, C)
+    torch.cuda.synchronize()
+    assert host_f32(am)[0] == 0.0
+
+
+def test_rmsnorm_zero_rows(F):
+    N, C = 8, 512
+    say("rmsnorm zero rows")
+    z = np.zeros((N, C), np.uint16)
+    w = W.uniform_bf16((C,), 0.5, 1.5, 1, 3)
+    y, rstd, am = empty_bf16(N, C), empty_f32(N), empty_f32(1)
+    F.ffn_rmsnorm_fwd(y, rstd, None, am, dev_bf16(z), None, dev_bf16(w), 1e-5, N, C)
+    torch.cuda.synchronize()
+    assert np.all(K.bf16_bits_to_f64(host_bits(y)) == 0)
+    assert np.allclose(host_f32(rstd), 1 / np.sqrt(np.float32(1e-5)), rtol=1e-6)
+    assert host_f32(am)[0] == 0.0
+
+
+# ----------------------------------------------------------------------------- quantisation
+
+@pytest.mark.parametrize("n,outl", [(64 * 256, False), (300 * 4096, True), (1_000_003, False), (7, False)])
+def test_quant_absmax_bit_exact(F, n, outl):
+    say(f"quant n={n}")
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n).astype(np.float32)
+    if outl:
+        x[rng.random(n) < 1e-3] *= 50
+    xb = W.to_bf16_bits(x)
+    q, scale, am = empty_u8(n), empty_f32(1), empty_f32(1)
+    F.ffn_quant_absmax(q, scale, am, dev_bf16(xb), n, 1)
+    torch.cuda.synchronize()
+    q_ref, s_ref, am_ref = O.quant_absmax(xb)
+    assert host_f32(am)[0] == am_ref
+    assert host_f32(scale)[0] == s_ref
+    assert np.array_equal(host_u8(q), q_ref)
+
+
+def test_quant_every_bf16_pattern_bit_exact(F):
+    # every finite bf16 value, quantised against several given abs-maxes
+    say("quant exhaustive bf16 patterns")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = K.bf16_bits_to_f64(bits)
+    bits = bits[np.isfinite(v)]
+    n = bits.size
+    x = dev_bf16(bits)
+    for am_v in [1.0, 3.5, 448.0, 1e-3, 2.0 ** -100, 3.0e38, 0.0]:
+        q, scale, am = empty_u8(n), empty_f32(1), dev_f32([am_v])
+        F.ffn_quant_absmax(q, scale, am, x, n, 0)
+        torch.cuda.synchronize()
+        q_ref, s_ref, _ = O.quant_absmax(bits, np.float32(am_v))
+        assert host_f32(scale)[0] == s_ref, am_v
+        assert np.array_equal(host_u8(q), q_ref), am_v
+
+
+@pytest.mark.parametrize("rows,cols", [(300, 1024), (64, 4104), (1, 8)])
+def test_quant_rows_bit_exact(F, rows, cols):
+    say(f"quant_rows {rows}x{cols}")
+    w = W.normal_bf16((rows, cols), 0.02, rows + cols, 1)
+    q, s = empty_u8(rows, cols), empty_f32(rows)
+    F.ffn_quant_rows(q, s, dev_bf16(w), rows, cols)
+    torch.cuda.synchronize()
+    q_ref, s_ref = O.quant_rows(w)
+    assert np.array_equal(host_f32(s), s_ref)
+    assert np.array_equal(host_u8(q), q_ref)
+
+
+# ----------------------------------------------------------------------------- SwiGLU
+
+@pytest.mark.parametrize("N,H", [(64, 768), (33, 14336), (5, 8)])
+def test_swiglu(F, N, H):
+    say(f"swiglu N={N} H={H}")
+    gu = W.normal_bf16((N, 2 * H), 2.0, N + H, 2)
+    h, am = empty_bf16(N, H), empty_f32(1)
+    F.ffn_swiglu(h, am, dev_bf16(gu), N, H)
+    torch.cuda.synchronize()
+    h_ref, am_ref = O.swiglu(gu)
+    gh = host_bits(h)
+    assert ulp_diff(gh, h_ref).max() <= 1           # hardware exp / reciprocal: <= 1 bf16 ulp
+    assert np.mean(ulp_diff(gh, h_ref) != 0) < 1e-2
+    assert host_f32(am)[0] == np.max(np.abs(K.bf16_bits_to_f64(gh)))
+
+
+# ----------------------------------------------------------------------------- GEMMs
+
+def _int_bf16(shape, seed, lo=-3, hi=4):
+    return W.to_bf16_bits(np.random.default_rng(seed).integers(lo, hi, shape).astype(np.float32))
+
+
+def _int_e4m3(shape, seed):
+    # codes of the integers -4..4 (exact in e4m3): every partial sum is an exact integer
+    vals = np.random.default_rng(seed).integers(-4, 5, shape).astype(np.float32)
+    return K.e4m3_encode(vals)
+
+
+GEMM_SHAPES = [(64, 256, 768), (300, 512, 384), (257, 384, 256), (1, 128, 128)]
+
+
+@pytest.mark.parametrize("N,C,H", GEMM_SHAPES)
+def test_gateup_bf16_integer_inputs_bit_exact(F, N, C, H):
+    say(f"gateup bf16 int N={N} C={C} H={H}")
+    x = _int_bf16((N, C), 1)
+    w = _int_bf16((2 * H, C), 2)
+    out = empty_bf16(N, 2 * H)
+    F.ffn_gateup(out, None, dev_bf16(x), None, dev_bf16(w), None, F.FFN_BF16, 0, N, C, H)
+    torch.cuda.synchronize()
+    # every partial sum is an integer below 2^24, exact in fp32 in any order;
+    # the one bf16 rounding of that exact sum is unique
+    assert np.array_equal(host_bits(out), O.gemm_bf16(x, w))
+
+
+@pytest.mark.parametrize("N,C,H", GEMM_SHAPES)
+def test_gateup_fp8_integer_inputs_bit_exact(F, N, C, H):
+    say(f"gateup fp8 int N={N} C={C} H={H}")
+    qx = _int_e4m3((N, C), 3)
+    qw = _int_e4m3((2 * H, C), 4)
+    one = dev_f32([1.0])
+    out = empty_bf16(N, 2 * H)
+    F.ffn_gateup(out, None, dev_u8(qx), one, dev_u8(qw), one, F.FFN_E4M3, 0, N, C, H)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), O.gemm_fp8(qx, np.float32(1), qw, np.float32(1)))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("N,C,H", [(64, 256, 768), (300, 512, 384)])
+def test_gateup_random_and_fused_equals_unfused(F, fp8, N, C, H):
+    say(f"gateup random fp8={fp8} N={N} C={C} H={H}")
+    d = W.block_inputs(N, C, H, seed=N + C + H, w_std=0.0)
+    if fp8:
+        qx, sx, _ = O.quant_absmax(d["inp"])
+        qw, sw, _ = O.quant_absmax(d["w_gu"])
+        xa, wa, xs, ws, dt = dev_u8(qx), dev_u8(qw), dev_f32([sx]), dev_f32([sw]), F.FFN_E4M3
+        ref = O.gemm_fp8(qx, sx, qw, sw)
+    else:
+        xa, wa, xs, ws, dt = dev_bf16(d["inp"]), dev_bf16(d["w_gu"]), None, None, F.FFN_BF16
+        ref = O.gemm_bf16(d["inp"], d["w_gu"])
+    gu = empty_bf16(N, 2 * H)
+    F.ffn_gateup(gu, None, xa, xs, wa, ws, dt, 0, N, C, H)
+    h_f, am_f = empty_bf16(N, H), empty_f32(1)
+    F.ffn_gateup(h_f, am_f, xa, xs, wa, ws, dt, 1, N, C, H)
+    h_u, am_u = empty_bf16(N, H), empty_f32(1)
+    F.ffn_swiglu(h_u, am_u, gu, N, H)
+    torch.cuda.synchronize()
+    g_gu = host_bits(gu)
+    assert rel_err(g_gu, ref) < 1e-2
+    assert np.mean(ulp_diff(g_gu, ref) > 1) < 1e-3
+    # the fused epilogue is the unfused pair exactly
+    assert np.array_equal(host_bits(h_f), host_bits(h_u))
+    assert host_f32(am_f)[0] == host_f32(am_u)[0]
+    h_ref, _ = O.swiglu(ref)
+    assert rel_err(host_bits(h_f), h_ref) < 3e-2
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("N,H,C", [(64, 768, 256), (300, 384, 512), (513, 256, 384)])
+def test_down(F, fp8, N, H, C):
+    say(f"down fp8={fp8} N={N} H={H} C={C}")
+    h = W.normal_bf16((N, H), 1.0, N + H, 3)
+    w = W.normal_bf16((C, H), 1 / np.sqrt(H), N + H, 4)
+    if fp8:
+        qh, sh, _ = O.quant_absmax(h)
+        qw, sw, _ = O.quant_absmax(w)
+        args = (dev_u8(qh), dev_f32([sh]), dev_u8(qw), dev_f32([sw]), F.FFN_E4M3)
+        ref = O.gemm_fp8(qh, sh, qw, sw)
+    else:
+        args = (dev_bf16(h), None, dev_bf16(w), None, F.FFN_BF16)
+        ref = O.gemm_bf16(h, w)
+    out = empty_bf16(N, C)
+    F.ffn_down(out, *args, N, H, C)
+    torch.cuda.synchronize()
+    g = host_bits(out)
+    assert rel_err(g, ref) < 1e-2
+    assert np.mean(ulp_diff(g, ref) > 1) < 1e-3
+
+
+def test_gemm_integer_down_bit_exact_and_deterministic(F):
+    N, H, C = 260, 512, 384
+    say("down int bit-exact")
+    h = _int_bf16((N, H), 5)
+    w = _int_bf16((C, H), 6)
+    out1, out2 = empty_bf16(N, C), empty_bf16(N, C)
+    F.ffn_down(out1, dev_bf16(h), None, dev_bf16(w), None, F.FFN_BF16, N, H, C)
+    F.ffn_down(out2, dev_bf16(h), None, dev_bf16(w), None, F.FFN_BF16, N, H, C)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out1), O.gemm_bf16(h, w))
+    assert torch.equal(out1, out2)
+
+
+# ----------------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("M,C,H", [(1, 256, 768), (1, 4096, 1024), (1, 3584, 384), (3, 512, 640), (16, 384, 896),
+                                   (32, 256, 256)])
+def test_decode(F, M, C, H):
+    say(f"decode M={M} C={C} H={H}")
+    d = W.decode_inputs(M, C, H, seed=M * 13 + C + H)
+    wq, ws = {}, {}
+    for k in ("w_gate", "w_up", "w_down"):
+        rows, cols = d[k].shape
+        q, s = empty_u8(rows, cols), empty_f32(rows)
+        F.ffn_quant_rows(q, s, dev_bf16(d[k]), rows, cols)
+        wq[k], ws[k] = q, s
+    out, h = empty_bf16(M, C), empty_bf16(M, H)
+    F.ffn_decode_gemv(out, h, dev_bf16(d["x"]), wq["w_gate"], ws["w_gate"], wq["w_up"], ws["w_up"],
+                      wq["w_down"], ws["w_down"], M, C, H)
+    torch.cuda.synchronize()
+    ref_q = {k: O.quant_rows(d[k]) for k in ("w_gate", "w_up", "w_down")}
+    for k in ref_q:
+        assert np.array_equal(host_u8(wq[k]), ref_q[k][0])
+        assert np.array_equal(host_f32(ws[k]), ref_q[k][1])
+    (qg, sg), (qu, su), (qd, sd) = ref_q["w_gate"], ref_q["w_up"], ref_q["w_down"]
+    y_ref, h_ref = O.decode_gemv(d["x"], qg, sg, qu, su, qd, sd)
+    gh, gy = host_bits(h), host_bits(out)
+    assert rel_err(gh, h_ref) < 2e-2
+    # the down GEMV given the GPU's own h
+    assert rel_err(gy, O.decode_down(gh, qd, sd)) < 1e-2
+    assert rel_err(gy, y_ref) < 3e-2
+
+
+def test_decode_empty_batch(F):
+    say("decode M=0")
+    C, H = 256, 256
+    z = empty_u8(H, C).zero_()
+    s = empty_f32(H).fill_(1.0)
+    F.ffn_decode_gemv(empty_bf16(1, C), empty_bf16(1, H), empty_bf16(1, C), z, s, z, s, z, s, 0, C, H)
+    torch.cuda.synchronize()

@@ -1,0 +1,24 @@
+"""ffn-mi355x: the forward hot path of a Llama-style dense SwiGLU FFN block
+(fused residual RMSNorm, per-tensor e4m3 quantisation, fused gate+up with
+SwiGLU, down projection) and its FP8 single-token decode, as hand-written HIP
+kernels for MI355X (gfx950) behind the C ABI of ``include/ffn.h``.
+
+The binding functions (``ffn_rmsnorm_fwd``, ``ffn_quant_absmax``,
+``ffn_quant_rows``, ``ffn_gateup``, ``ffn_swiglu``, ``ffn_down``,
+``ffn_decode_gemv``) live in ``binding``; accessing any of them here loads
+``libffn.so`` and raises if it has not been built.  ``workloads`` (seeded
+synthetic inputs) and ``build`` import without the library.
+"""
+
+_BINDING_NAMES = {
+    "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_swiglu", "ffn_down",
+    "ffn_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_OK", "FFN_ERR_INVALID",
+    "FFN_ERR_UNSUPPORTED", "FFN_ERR_HIP", "version", "last_error", "LIB_PATH",
+}
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,173 @@
+"""Python binding of libffn.so: the FFN block's hot path on MI355X.
+
+Each function has the name and argument order of its C entry point in
+``include/ffn.h`` and only marshals arguments: it checks that every tensor is a
+contiguous device tensor of the element type and size the call will touch
+(so that no kernel is launched on a buffer that is too small), passes raw device
+pointers and the stream, and turns a non-OK status into ``FFNError``.  All
+arithmetic happens in the HIP kernels.  torch supplies device memory and the
+stream (the current torch stream unless one is given).
+
+There is no fallback: if the library is missing, importing this package raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libffn.so")
+
+FFN_OK, FFN_ERR_INVALID, FFN_ERR_UNSUPPORTED, FFN_ERR_HIP = 0, 1, 2, 3
+FFN_BF16, FFN_E4M3 = 0, 1
+_STATUS = {1: "FFN_ERR_INVALID", 2: "FFN_ERR_UNSUPPORTED", 3: "FFN_ERR_HIP"}
+
+
+class FFNError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m transformer_ffn_block_residual_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    sig = {
+        "ffn_rmsnorm_fwd": [P, P, P, P, P, P, P, F32, I64, I64, P],
+        "ffn_quant_absmax": [P, P, P, P, I64, I32, P],
+        "ffn_quant_rows": [P, P, P, I64, I64, P],
+        "ffn_gateup": [P, P, P, P, P, P, I32, I32, I64, I64, I64, P],
+        "ffn_swiglu": [P, P, P, I64, I64, P],
+        "ffn_down": [P, P, P, P, P, I32, I64, I64, I64, P],
+        "ffn_decode_gemv": [P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ffn_last_error.restype = ctypes.c_char_p
+    lib.ffn_last_error.argtypes = []
+    lib.ffn_version.restype = ctypes.c_char_p
+    lib.ffn_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def version():
+    return _lib.ffn_version().decode()
+
+
+def last_error():
+    return _lib.ffn_last_error().decode()
+
+
+def _check(status):
+    if status != FFN_OK:
+        raise FFNError(status, last_error())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+_ELT = {torch.bfloat16: 2, torch.float32: 4, torch.uint8: 1, torch.float8_e4m3fn: 1, torch.int16: 2}
+
+
+def _ptr(t, name, numel, dtypes, optional=False):
+    """Device pointer of tensor t after checking it holds >= numel elements of
+    one of dtypes, contiguous, on a GPU."""
+    if t is None:
+        if optional:
+            return None
+        raise FFNError(FFN_ERR_INVALID, f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise FFNError(FFN_ERR_INVALID, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise FFNError(FFN_ERR_INVALID, f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise FFNError(FFN_ERR_INVALID, f"{name}: dtype {t.dtype} not in {dtypes}")
+    if numel is not None and t.numel() < numel:
+        raise FFNError(FFN_ERR_INVALID, f"{name}: {t.numel()} elements < {numel} needed")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+BF16 = (torch.bfloat16, torch.int16)
+F32 = (torch.float32,)
+E4M3 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def ffn_rmsnorm_fwd(y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C, stream=None):
+    _check(_lib.ffn_rmsnorm_fwd(
+        _ptr(y, "y", N * C, BF16), _ptr(rstd, "rstd", N, F32),
+        _ptr(residual_out, "residual_out", N * C, BF16, optional=True),
+        _ptr(absmax, "absmax", 1, F32, optional=True),
+        _ptr(inp, "inp", N * C, BF16), _ptr(addend, "addend", N * C, BF16, optional=True),
+        _ptr(weight, "weight", C, BF16), float(eps), int(N), int(C), _stream(stream)))
+
+
+def ffn_quant_absmax(q, scale, absmax, x, n, compute_absmax, stream=None):
+    _check(_lib.ffn_quant_absmax(
+        _ptr(q, "q", n, E4M3), _ptr(scale, "scale", 1, F32), _ptr(absmax, "absmax", 1, F32),
+        _ptr(x, "x", n, BF16), int(n), int(bool(compute_absmax)), _stream(stream)))
+
+
+def ffn_quant_rows(q, row_scale, w, rows, cols, stream=None):
+    _check(_lib.ffn_quant_rows(
+        _ptr(q, "q", rows * cols, E4M3), _ptr(row_scale, "row_scale", rows, F32),
+        _ptr(w, "w", rows * cols, BF16), int(rows), int(cols), _stream(stream)))
+
+
+def _dt_elems(dtype):
+    return E4M3 if dtype == FFN_E4M3 else BF16
+
+
+def ffn_gateup(out, out_absmax, x, x_scale, w, w_scale, dtype, fuse_swiglu, N, C, H, stream=None):
+    fp8 = dtype == FFN_E4M3
+    _check(_lib.ffn_gateup(
+        _ptr(out, "out", N * (H if fuse_swiglu else 2 * H), BF16),
+        _ptr(out_absmax, "out_absmax", 1, F32, optional=True),
+        _ptr(x, "x", N * C, _dt_elems(dtype)), _ptr(x_scale, "x_scale", 1, F32, optional=not fp8),
+        _ptr(w, "w", 2 * H * C, _dt_elems(dtype)), _ptr(w_scale, "w_scale", 1, F32, optional=not fp8),
+        int(dtype), int(bool(fuse_swiglu)), int(N), int(C), int(H), _stream(stream)))
+
+
+def ffn_swiglu(h, absmax, gateup, N, H, stream=None):
+    _check(_lib.ffn_swiglu(
+        _ptr(h, "h", N * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=True),
+        _ptr(gateup, "gateup", N * 2 * H, BF16), int(N), int(H), _stream(stream)))
+
+
+def ffn_down(out, h, h_scale, w, w_scale, dtype, N, H, C, stream=None):
+    fp8 = dtype == FFN_E4M3
+    _check(_lib.ffn_down(
+        _ptr(out, "out", N * C, BF16), _ptr(h, "h", N * H, _dt_elems(dtype)),
+        _ptr(h_scale, "h_scale", 1, F32, optional=not fp8),
+        _ptr(w, "w", C * H, _dt_elems(dtype)), _ptr(w_scale, "w_scale", 1, F32, optional=not fp8),
+        int(dtype), int(N), int(H), int(C), _stream(stream)))
+
+
+def ffn_decode_gemv(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
+    _check(_lib.ffn_decode_gemv(
+        _ptr(out, "out", M * C, BF16), _ptr(h, "h", M * H, BF16), _ptr(x, "x", M * C, BF16),
+        _ptr(w_gate, "w_gate", H * C, E4M3), _ptr(s_gate, "s_gate", H, F32),
+        _ptr(w_up, "w_up", H * C, E4M3), _ptr(s_up, "s_up", H, F32),
+        _ptr(w_down, "w_down", C * H, E4M3), _ptr(s_down, "s_down", C, F32),
+        int(M), int(C), int(H), _stream(stream)))
+
+
+__all__ = [
+    "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_swiglu", "ffn_down",
+    "ffn_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
+]

@@ -1,0 +1,222 @@
+// C ABI of libffn.so (declared in include/ffn.h): argument validation, then the
+// kernel launches.  Validation touches no HIP API, so every error path can be
+// exercised on a machine without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/ffn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ffn_status_t fail(ffn_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+ffn_status_t hip_status(hipError_t e, const char* fn) {
+    if (e == hipSuccess) return FFN_OK;
+    return fail(FFN_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+#define REQUIRE(ptr)                                                                  \
+    do {                                                                              \
+        if (!(ptr)) return fail(FFN_ERR_INVALID, "%s: %s is NULL", __func__, #ptr);   \
+    } while (0)
+#define ALIGNED(ptr)                                                                                   \
+    do {                                                                                               \
+        if ((ptr) && misaligned(ptr))                                                                  \
+            return fail(FFN_ERR_UNSUPPORTED, "%s: %s is not 16-byte aligned", __func__, #ptr);         \
+    } while (0)
+#define NONNEG(v)                                                                                      \
+    do {                                                                                               \
+        if ((v) < 0) return fail(FFN_ERR_INVALID, "%s: %s = %lld is negative", __func__, #v, (long long)(v)); \
+    } while (0)
+
+const int64_t kMaxDim = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+const char* ffn_last_error(void) { return g_err; }
+
+const char* ffn_version(void) { return "ffn-mi355x 0.1 (gfx950)"; }
+
+ffn_status_t ffn_rmsnorm_fwd(void* y, float* rstd, void* residual_out, float* absmax, const void* inp,
+                             const void* addend, const void* weight, float eps, int64_t N, int64_t C,
+                             hipStream_t stream) {
+    REQUIRE(y);
+    REQUIRE(rstd);
+    REQUIRE(inp);
+    REQUIRE(weight);
+    NONNEG(N);
+    NONNEG(C);
+    if (addend && !residual_out) return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: addend given without residual_out");
+    if (!addend && residual_out)
+        return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: residual_out given without addend");
+    if (!(eps >= 0.0f)) return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: eps must be >= 0");
+    if (C < 8 || C > 16384 || C % 8 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_fwd: C = %lld (need 8 <= C <= 16384, C %% 8 == 0)",
+                    (long long)C);
+    if (N > (int64_t)1 << 31) return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_fwd: N too large");
+    ALIGNED(y);
+    ALIGNED(inp);
+    ALIGNED(addend);
+    ALIGNED(residual_out);
+    ALIGNED(weight);
+    if (residual_out && (residual_out == y || residual_out == addend))
+        return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: residual_out may alias only inp");
+    return hip_status(ffn::launch_rmsnorm((uint16_t*)y, rstd, (uint16_t*)residual_out, absmax,
+                                          (const uint16_t*)inp, (const uint16_t*)addend, (const uint16_t*)weight,
+                                          eps, N, (int)C, stream),
+                      "ffn_rmsnorm_fwd");
+}
+
+ffn_status_t ffn_quant_absmax(uint8_t* q, float* scale, float* absmax, const void* x, int64_t n,
+                              int compute_absmax, hipStream_t stream) {
+    REQUIRE(q);
+    REQUIRE(scale);
+    REQUIRE(absmax);
+    REQUIRE(x);
+    NONNEG(n);
+    if ((void*)scale == (void*)absmax) return fail(FFN_ERR_INVALID, "ffn_quant_absmax: scale and absmax alias");
+    if (n > ((int64_t)1 << 36)) return fail(FFN_ERR_UNSUPPORTED, "ffn_quant_absmax: n too large");
+    ALIGNED(q);
+    ALIGNED(x);
+    return hip_status(ffn::launch_quant(q, scale, absmax, (const uint16_t*)x, n, compute_absmax != 0, stream),
+                      "ffn_quant_absmax");
+}
+
+ffn_status_t ffn_quant_rows(uint8_t* q, float* row_scale, const void* w, int64_t rows, int64_t cols,
+                            hipStream_t stream) {
+    REQUIRE(q);
+    REQUIRE(row_scale);
+    REQUIRE(w);
+    NONNEG(rows);
+    NONNEG(cols);
+    if (cols < 8 || cols % 8 != 0 || cols > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_quant_rows: cols = %lld (need cols %% 8 == 0)", (long long)cols);
+    if (rows > (int64_t)1 << 31) return fail(FFN_ERR_UNSUPPORTED, "ffn_quant_rows: rows too large");
+    ALIGNED(q);
+    ALIGNED(w);
+    return hip_status(ffn::launch_quant_rows(q, row_scale, (const uint16_t*)w, rows, (int)cols, stream),
+                      "ffn_quant_rows");
+}
+
+static ffn_status_t check_gemm_dims(const char* fn, int64_t N, int64_t K, int64_t O, int elt) {
+    if (K < 128 || K % 128 != 0 || K > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: reduction size %lld must be a positive multiple of 128", fn,
+                    (long long)K);
+    if (O < 128 || O % 128 != 0 || O > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: output features %lld must be a positive multiple of 128", fn,
+                    (long long)O);
+    // byte offsets inside one operand are kept in 32 bits
+    if (O * K * elt >= ((int64_t)1 << 32) || N * K * elt >= ((int64_t)1 << 32))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: an operand exceeds 4 GiB", fn);
+    if (N > ((int64_t)1 << 31) - 256) return fail(FFN_ERR_UNSUPPORTED, "%s: N too large", fn);
+    return FFN_OK;
+}
+
+ffn_status_t ffn_gateup(void* out, float* out_absmax, const void* x, const float* x_scale, const void* w,
+                        const float* w_scale, ffn_dtype_t dtype, int fuse_swiglu, int64_t N, int64_t C, int64_t H,
+                        hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(x);
+    REQUIRE(w);
+    NONNEG(N);
+    NONNEG(C);
+    NONNEG(H);
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3) return fail(FFN_ERR_INVALID, "ffn_gateup: unknown dtype %d", (int)dtype);
+    if (dtype == FFN_E4M3) {
+        REQUIRE(x_scale);
+        REQUIRE(w_scale);
+    }
+    const int elt = dtype == FFN_E4M3 ? 1 : 2;
+    if (ffn_status_t st = check_gemm_dims("ffn_gateup", N, C, 2 * H, elt)) return st;
+    if (H % 128 != 0) return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup: H = %lld must be a multiple of 128", (long long)H);
+    ALIGNED(out);
+    ALIGNED(x);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(out, out_absmax, x, x_scale, w, w_scale, dtype == FFN_E4M3, fuse_swiglu != 0,
+                                       N, (int)C, (int)(2 * H), stream),
+                      "ffn_gateup");
+}
+
+ffn_status_t ffn_swiglu(void* h, float* absmax, const void* gateup, int64_t N, int64_t H, hipStream_t stream) {
+    REQUIRE(h);
+    REQUIRE(gateup);
+    NONNEG(N);
+    NONNEG(H);
+    if (H < 8 || H % 8 != 0 || H > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_swiglu: H = %lld (need H %% 8 == 0)", (long long)H);
+    if (N * H > ((int64_t)1 << 36)) return fail(FFN_ERR_UNSUPPORTED, "ffn_swiglu: tensor too large");
+    ALIGNED(h);
+    ALIGNED(gateup);
+    return hip_status(ffn::launch_swiglu((uint16_t*)h, absmax, (const uint16_t*)gateup, N, (int)H, stream),
+                      "ffn_swiglu");
+}
+
+ffn_status_t ffn_down(void* out, const void* h, const float* h_scale, const void* w, const float* w_scale,
+                      ffn_dtype_t dtype, int64_t N, int64_t H, int64_t C, hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(h);
+    REQUIRE(w);
+    NONNEG(N);
+    NONNEG(H);
+    NONNEG(C);
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3) return fail(FFN_ERR_INVALID, "ffn_down: unknown dtype %d", (int)dtype);
+    if (dtype == FFN_E4M3) {
+        REQUIRE(h_scale);
+        REQUIRE(w_scale);
+    }
+    const int elt = dtype == FFN_E4M3 ? 1 : 2;
+    if (ffn_status_t st = check_gemm_dims("ffn_down", N, H, C, elt)) return st;
+    ALIGNED(out);
+    ALIGNED(h);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(out, nullptr, h, h_scale, w, w_scale, dtype == FFN_E4M3, false, N, (int)H,
+                                       (int)C, stream),
+                      "ffn_down");
+}
+
+ffn_status_t ffn_decode_gemv(void* out, void* h, const void* x, const uint8_t* w_gate, const float* s_gate,
+                             const uint8_t* w_up, const float* s_up, const uint8_t* w_down, const float* s_down,
+                             int64_t M, int64_t C, int64_t H, hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(h);
+    REQUIRE(x);
+    REQUIRE(w_gate);
+    REQUIRE(s_gate);
+    REQUIRE(w_up);
+    REQUIRE(s_up);
+    REQUIRE(w_down);
+    REQUIRE(s_down);
+    NONNEG(M);
+    NONNEG(C);
+    NONNEG(H);
+    if (M > 32) return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_gemv: M = %lld > 32", (long long)M);
+    if (C < 128 || C % 128 != 0 || C > kMaxDim || H < 128 || H % 128 != 0 || H > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_gemv: C = %lld, H = %lld must be positive multiples of 128",
+                    (long long)C, (long long)H);
+    if (C * H >= ((int64_t)1 << 31)) return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_gemv: weights exceed 2 GiB");
+    ALIGNED(out);
+    ALIGNED(h);
+    ALIGNED(x);
+    ALIGNED(w_gate);
+    ALIGNED(w_up);
+    ALIGNED(w_down);
+    if (h == x || out == h) return fail(FFN_ERR_INVALID, "ffn_decode_gemv: h must not alias x or out");
+    return hip_status(ffn::launch_decode((uint16_t*)out, (uint16_t*)h, (const uint16_t*)x, w_gate, s_gate, w_up,
+                                         s_up, w_down, s_down, (int)M, (int)C, (int)H, stream),
+                      "ffn_decode_gemv");
+}
+
+}  // extern "C"

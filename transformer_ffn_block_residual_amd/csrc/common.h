@@ -1,0 +1,92 @@
+// Device helpers shared by the FFN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffn {
+
+constexpr int kWave = 64;
+constexpr float kE4M3Max = 448.0f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// bf16 bits (low 16 bits of u) -> fp32, exact.
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two fp32 -> two bf16 packed in one dword (a in the low half), round to nearest
+// even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2_t v = {a, b};
+    bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// fp32 -> bf16 -> fp32: the value a bf16 store would hold.
+__device__ __forceinline__ float round_bf16(float a) { return bf16lo(pack_bf16x2(a, 0.0f)); }
+
+// SiLU(g) * u in fp32: g / (1 + exp(-g)) * u.  The exponential uses the
+// hardware 2^x (v_exp_f32) and the division the hardware reciprocal; both are
+// within a few fp32 ulps, far below the bf16 rounding that follows.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// Four fp32 -> four e4m3 codes in one dword (a in the lowest byte).  Values are
+// clamped to +-448 first so the conversion never depends on an overflow mode;
+// v_cvt_pk_fp8_f32 rounds to nearest even.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    a = __builtin_fminf(__builtin_fmaxf(a, -kE4M3Max), kE4M3Max);
+    b = __builtin_fminf(__builtin_fmaxf(b, -kE4M3Max), kE4M3Max);
+    c = __builtin_fminf(__builtin_fmaxf(c, -kE4M3Max), kE4M3Max);
+    d = __builtin_fminf(__builtin_fmaxf(d, -kE4M3Max), kE4M3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Bytes 0,1 (hi=false) or 2,3 (hi=true) of a dword of e4m3 codes -> fp32, exact.
+__device__ __forceinline__ f32x2_t e4m3x2_to_f32(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+// max into a non-negative fp32 in global memory: for v >= 0 the IEEE order is
+// the unsigned order of the bit patterns, so an integer atomic max is exact and
+// independent of the order in which blocks arrive.
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
+    atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+// Block-wide max of a per-thread value, then one atomic per block.  All threads
+// of the block must call it.  `red` is LDS scratch of at least nwaves floats.
+__device__ __forceinline__ void block_absmax_commit(float v, float* red, float* out) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = red[0];
+        for (int i = 1; i < (int)(blockDim.x / kWave); ++i) m = __builtin_fmaxf(m, red[i]);
+        atomic_max_nonneg(out, m);
+    }
+}
+
+}  // namespace ffn

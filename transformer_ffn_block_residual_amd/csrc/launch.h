@@ -1,0 +1,30 @@
+// Host-side launchers of the FFN kernels (internal to libffn.so).  Each returns
+// the HIP status of its launches; arguments are validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffn {
+
+hipError_t launch_fill(float* p, int n, float v, hipStream_t s);
+hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
+                          const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s);
+hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_t s);
+hipError_t launch_quant(uint8_t* q, float* scale, float* absmax, const uint16_t* x, int64_t n, bool compute,
+                        hipStream_t s);
+hipError_t launch_quant_rows(uint8_t* q, float* row_scale, const uint16_t* w, int64_t rows, int cols,
+                             hipStream_t s);
+hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t N, int H, hipStream_t s);
+
+// GEMM: out[n, o] = sum_k x[n, k] * w[o, k] (optionally scaled, optionally
+// SwiGLU-fused).  fp8 selects e4m3 operands with device scales.
+hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
+                       const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
+                       hipStream_t s);
+
+hipError_t launch_decode(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg, const float* sg,
+                         const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd, int M, int C,
+                         int H, hipStream_t s);
+
+}  // namespace ffn

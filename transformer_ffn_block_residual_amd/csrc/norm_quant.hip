@@ -1,0 +1,299 @@
+// Bandwidth-bound kernels of the FFN block: fused residual add + RMSNorm with
+// rstd and abs-max, abs-max reduction, e4m3 quantisation (per tensor and per
+// row) and the standalone SwiGLU.
+//
+// Every kernel reads and writes HBM in 16-byte vectors per lane, consecutive
+// lanes on consecutive addresses, and folds its abs-max into the same pass
+// (one atomic per workgroup on the bit pattern of a non-negative float).
+#include "common.h"
+#include "launch.h"
+
+namespace ffn {
+
+// ---------------------------------------------------------------------------
+// Fill: clears abs-max slots.  A kernel rather than hipMemsetAsync so that a
+// captured graph replays it reliably.
+__global__ void fill_f32_kernel(float* p, int n, float v) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill(float* p, int n, float v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((n + 63) / 64), dim3(64), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused residual add + RMSNorm (llmq llama_model.cpp, LLamaModel::_forward_block,
+// fused_residual_rmsnorm_forward).  One wave per row; the row stays in
+// registers (CPL 16-byte chunks per lane), so y may overwrite inp or addend.
+//   r = bf16(inp + addend); rstd = 1/sqrt(sum r^2 / C + eps);
+//   y = bf16((r * rstd) * w); absmax = max |y|.
+template <int CPL, bool kAdd>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(
+    uint16_t* y, float* rstd_out, uint16_t* res_out, float* absmax,
+    const uint16_t* inp, const uint16_t* addend, const uint16_t* w,
+    float eps, int64_t N, int C) {
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nch = C >> 3;  // 8 bf16 per 16-byte chunk
+    float amax = 0.0f;
+    if (row < N) {
+        const uint4* a4 = reinterpret_cast<const uint4*>(inp + row * C);
+        const uint4* b4 = reinterpret_cast<const uint4*>(addend + row * C);
+        uint4 r[CPL];
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * 64;
+            if (c < nch) {
+                uint4 av = a4[c];
+                if (kAdd) {
+                    uint4 bv = b4[c];
+                    uint32_t* ap = reinterpret_cast<uint32_t*>(&av);
+                    const uint32_t* bp = reinterpret_cast<const uint32_t*>(&bv);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        ap[q] = pack_bf16x2(bf16lo(ap[q]) + bf16lo(bp[q]), bf16hi(ap[q]) + bf16hi(bp[q]));
+                }
+                r[i] = av;
+                const uint32_t* rp = reinterpret_cast<const uint32_t*>(&av);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float lo = bf16lo(rp[q]), hi = bf16hi(rp[q]);
+                    ss += lo * lo;
+                    ss += hi * hi;
+                }
+            }
+        }
+        ss = wave_sum(ss);
+        const float rs = 1.0f / sqrtf(ss / (float)C + eps);
+        if (lane == 0) rstd_out[row] = rs;
+        const uint4* w4 = reinterpret_cast<const uint4*>(w);
+        uint4* y4 = reinterpret_cast<uint4*>(y + row * C);
+        uint4* o4 = kAdd ? reinterpret_cast<uint4*>(res_out + row * C) : nullptr;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * 64;
+            if (c < nch) {
+                const uint4 wv = w4[c];
+                const uint32_t* rp = reinterpret_cast<const uint32_t*>(&r[i]);
+                const uint32_t* wp = reinterpret_cast<const uint32_t*>(&wv);
+                uint4 yv;
+                uint32_t* yp = reinterpret_cast<uint32_t*>(&yv);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    yp[q] = pack_bf16x2((bf16lo(rp[q]) * rs) * bf16lo(wp[q]), (bf16hi(rp[q]) * rs) * bf16hi(wp[q]));
+                    amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16lo(yp[q])), __builtin_fabsf(bf16hi(yp[q]))));
+                }
+                if (kAdd) o4[c] = r[i];
+                y4[c] = yv;
+            }
+        }
+    }
+    if (absmax) block_absmax_commit(amax, red, absmax);
+}
+
+template <int CPL>
+static void launch_rmsnorm_cpl(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
+                               const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C,
+                               hipStream_t s) {
+    dim3 grid((unsigned)((N + 3) / 4)), block(256);
+    if (add)
+        hipLaunchKernelGGL((rmsnorm_kernel<CPL, true>), grid, block, 0, s, y, rstd, res, absmax, inp, add, w, eps, N, C);
+    else
+        hipLaunchKernelGGL((rmsnorm_kernel<CPL, false>), grid, block, 0, s, y, rstd, res, absmax, inp, add, w, eps, N, C);
+}
+
+hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
+                          const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s) {
+    if (absmax) {
+        hipError_t e = launch_fill(absmax, 1, 0.0f, s);
+        if (e != hipSuccess) return e;
+    }
+    if (N == 0) return hipSuccess;
+    const int need = (C / 8 + 63) / 64;  // chunks per lane
+    if (need <= 1) launch_rmsnorm_cpl<1>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 2) launch_rmsnorm_cpl<2>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 4) launch_rmsnorm_cpl<4>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 8) launch_rmsnorm_cpl<8>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 16) launch_rmsnorm_cpl<16>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else launch_rmsnorm_cpl<32>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Standalone abs-max of a bf16 tensor (llmq llama_model.cpp, _forward_block,
+// abs_max).  Grid-stride over 16-byte chunks; any length (scalar tail).
+__global__ __launch_bounds__(256) void absmax_kernel(float* out, const uint16_t* __restrict__ x, int64_t n) {
+    __shared__ float red[4];
+    float m = 0.0f;
+    const int64_t nch = n >> 3;
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nch; c += stride) {
+        const uint4 v = x4[c];
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(&v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(p[q])), __builtin_fabsf(bf16hi(p[q]))));
+    }
+    for (int64_t i = (nch << 3) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        m = __builtin_fmaxf(m, __builtin_fabsf(bf16lo(x[i])));
+    block_absmax_commit(m, red, out);
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor e4m3 quantisation with a known abs-max (llmq llama_model.cpp,
+// forward_qmm, quantize_with_abs_max).  16 elements per thread: two 16-byte
+// loads, one 16-byte store.  inv = 448/absmax in IEEE fp32; codes from the fp32
+// product x*inv.  Block 0 also writes the scale absmax/448.
+__device__ __forceinline__ void scale_pair(float am, float& scale, float& inv) {
+    if (am > 0.0f) {
+        scale = am / kE4M3Max;
+        inv = kE4M3Max / am;
+    } else {
+        scale = 1.0f;
+        inv = 1.0f;
+    }
+}
+
+__global__ __launch_bounds__(256) void quant_kernel(uint8_t* __restrict__ q, float* __restrict__ scale_out,
+                                                    const float* __restrict__ absmax,
+                                                    const uint16_t* __restrict__ x, int64_t n) {
+    float scale, inv;
+    scale_pair(*absmax, scale, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = scale;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t base = t * 16;
+    if (base + 16 <= n) {
+        const uint4* x4 = reinterpret_cast<const uint4*>(x + base);
+        const uint4 v0 = x4[0], v1 = x4[1];
+        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&v0);
+        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&v1);
+        uint4 o;
+        o.x = pack_e4m3x4(bf16lo(p0[0]) * inv, bf16hi(p0[0]) * inv, bf16lo(p0[1]) * inv, bf16hi(p0[1]) * inv);
+        o.y = pack_e4m3x4(bf16lo(p0[2]) * inv, bf16hi(p0[2]) * inv, bf16lo(p0[3]) * inv, bf16hi(p0[3]) * inv);
+        o.z = pack_e4m3x4(bf16lo(p1[0]) * inv, bf16hi(p1[0]) * inv, bf16lo(p1[1]) * inv, bf16hi(p1[1]) * inv);
+        o.w = pack_e4m3x4(bf16lo(p1[2]) * inv, bf16hi(p1[2]) * inv, bf16lo(p1[3]) * inv, bf16hi(p1[3]) * inv);
+        *reinterpret_cast<uint4*>(q + base) = o;
+    } else if (base < n) {
+        for (int64_t i = base; i < n; ++i) {
+            const float v = bf16lo(x[i]) * inv;
+            q[i] = (uint8_t)(pack_e4m3x4(v, 0.0f, 0.0f, 0.0f) & 0xff);
+        }
+    }
+}
+
+hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_t s) {
+    hipError_t e = launch_fill(absmax, 1, 0.0f, s);
+    if (e != hipSuccess || n == 0) return e;
+    int64_t nch = (n + 7) / 8;
+    int64_t blocks = (nch + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, absmax, x, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant(uint8_t* q, float* scale, float* absmax, const uint16_t* x, int64_t n, bool compute,
+                        hipStream_t s) {
+    if (compute) {
+        hipError_t e = launch_absmax(absmax, x, n, s);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t threads = (n + 15) / 16;
+    const int64_t blocks = threads > 0 ? (threads + 255) / 256 : 1;  // n == 0 still writes the scale
+    hipLaunchKernelGGL(quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, absmax, x, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-row e4m3 quantisation of a weight matrix (the row_scale layout of the FP8
+// decode weights, metrale dense_ffn_decode.rs, DenseFfnLayer::forward).  One
+// workgroup per row: pass 1 finds the row's abs-max, pass 2 (re-reading the row
+// from cache) writes the codes.  cols % 8 == 0.
+__global__ __launch_bounds__(256) void quant_rows_kernel(uint8_t* __restrict__ q, float* __restrict__ row_scale,
+                                                         const uint16_t* __restrict__ w, int cols) {
+    __shared__ float red[4];
+    __shared__ float am_s;
+    const int64_t row = blockIdx.x;
+    const uint4* w4 = reinterpret_cast<const uint4*>(w + row * cols);
+    const int nch = cols >> 3;
+    float m = 0.0f;
+    for (int c = threadIdx.x; c < nch; c += 256) {
+        const uint4 v = w4[c];
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(&v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(p[k])), __builtin_fabsf(bf16hi(p[k]))));
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) am_s = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    __syncthreads();
+    float scale, inv;
+    scale_pair(am_s, scale, inv);
+    if (threadIdx.x == 0) row_scale[row] = scale;
+    uint2* q2 = reinterpret_cast<uint2*>(q + row * cols);
+    for (int c = threadIdx.x; c < nch; c += 256) {
+        const uint4 v = w4[c];
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(&v);
+        uint2 o;
+        o.x = pack_e4m3x4(bf16lo(p[0]) * inv, bf16hi(p[0]) * inv, bf16lo(p[1]) * inv, bf16hi(p[1]) * inv);
+        o.y = pack_e4m3x4(bf16lo(p[2]) * inv, bf16hi(p[2]) * inv, bf16lo(p[3]) * inv, bf16hi(p[3]) * inv);
+        q2[c] = o;
+    }
+}
+
+hipError_t launch_quant_rows(uint8_t* q, float* row_scale, const uint16_t* w, int64_t rows, int cols,
+                             hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, q, row_scale, w, cols);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Standalone SwiGLU (llmq llama_model.cpp, _forward_block, swiglu_forward):
+// h[n,j] = bf16(silu(g) * u), g = gu[n,j], u = gu[n,H+j], plus max|h|.
+// 8 outputs per thread: one 16-byte load from each half, one 16-byte store.
+__global__ __launch_bounds__(256) void swiglu_kernel(uint16_t* __restrict__ h, float* absmax,
+                                                     const uint16_t* __restrict__ gu, int64_t N, int H) {
+    __shared__ float red[4];
+    const int hch = H >> 3;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    float m = 0.0f;
+    if (t < N * hch) {
+        const int64_t n = t / hch;
+        const int c = (int)(t - n * hch);
+        const uint4 gv = reinterpret_cast<const uint4*>(gu + n * 2 * H)[c];
+        const uint4 uv = reinterpret_cast<const uint4*>(gu + n * 2 * H + H)[c];
+        const uint32_t* gp = reinterpret_cast<const uint32_t*>(&gv);
+        const uint32_t* up = reinterpret_cast<const uint32_t*>(&uv);
+        uint4 o;
+        uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            op[k] = pack_bf16x2(silu_mul(bf16lo(gp[k]), bf16lo(up[k])), silu_mul(bf16hi(gp[k]), bf16hi(up[k])));
+            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(op[k])), __builtin_fabsf(bf16hi(op[k]))));
+        }
+        reinterpret_cast<uint4*>(h + n * H)[c] = o;
+    }
+    if (absmax) block_absmax_commit(m, red, absmax);
+}
+
+hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t N, int H, hipStream_t s) {
+    if (absmax) {
+        hipError_t e = launch_fill(absmax, 1, 0.0f, s);
+        if (e != hipSuccess) return e;
+    }
+    if (N == 0) return hipSuccess;
+    const int64_t threads = N * (H / 8);
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, h, absmax, gu, N, H);
+    return hipGetLastError();
+}
+
+}  // namespace ffn
