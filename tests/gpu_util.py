@@ -72,3 +72,22 @@ def ulp_diff(a_bits, b_bits):
     ka = np.where(a & 0x8000, -(a & 0x7FFF), a)
     kb = np.where(b & 0x8000, -(b & 0x7FFF), b)
     return np.abs(ka - kb)
+
+
+def normwise_err(got_bits, ref_bits):
+    """max_i |g_i - r_i| / max_i |r_i|: the error measured against the tensor's
+    abs-max, the quantity that sets a per-tensor quantisation grid."""
+    g = K.bf16_bits_to_f64(got_bits).reshape(-1)
+    r = K.bf16_bits_to_f64(ref_bits).reshape(-1)
+    m = np.max(np.abs(r)) if r.size else 0.0
+    return float(np.max(np.abs(g - r)) / m) if m > 0 else float(np.max(np.abs(g - r), initial=0.0))
+
+
+def within_dot_bound(got_bits, exact, mag, rel_out=2.0 ** -8, rel_sum=2.0 ** -14):
+    """True where |g - exact| <= rel_out*|exact| + rel_sum*mag: one bf16 rounding
+    of the result plus an accumulation error proportional to sum_k |a_k b_k|
+    (mag).  rel_sum = 2^-14 covers fp32 accumulation over the K used in the tests
+    and the f8f6f4 MFMA, whose 64-term dot products carry about 2^-16 of their
+    sum of magnitudes."""
+    g = K.bf16_bits_to_f64(got_bits)
+    return np.abs(g - exact) <= rel_out * np.abs(exact) + rel_sum * mag
