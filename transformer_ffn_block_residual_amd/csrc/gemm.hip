@@ -7,23 +7,24 @@
 //   out[n, o] = sum_k x[n, k] * w[o, k]        (both operands K-contiguous)
 //
 // Tiling.  A workgroup of 4 waves owns a 256 (weight rows) x 256 (token rows)
-// output tile and walks K in steps of 128 bytes per row (64 bf16 or 128 e4m3),
-// so both dtypes share one LDS layout: per stage 256 rows x 128 B for each
-// operand (64 KiB), two stages (128 KiB of the 160 KiB LDS).  Each wave owns a
+// output tile and walks K in steps of 64 bytes per row (32 bf16 or 64 e4m3),
+// so both dtypes share one LDS layout: per stage 256 rows x 64 B for each
+// operand (32 KiB), a ring of four stages (128 KiB of the 160 KiB LDS).  Each wave owns a
 // 128 x 128 sub-tile = 4 x 4 blocks of the 32x32 MFMA (v_mfma_f32_32x32x16_bf16
 // or v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales), 256 fp32 accumulators
 // per lane.  The weight is the MFMA's A operand, so each lane ends up holding
 // four consecutive output features of one token: 8-byte bf16 stores.
 //
-// LDS layout.  Row r of a stage occupies 128 bytes = 8 chunks of 16 bytes;
-// chunk c is stored at position c ^ (r & 7).  A fragment read (32 lanes on 32
-// consecutive rows, one chunk each) then touches 8 distinct 16-byte positions
-// in every group of 8 lanes: no bank conflicts.  Global loads put 8 lanes on
-// the 8 chunks of one row (one 128-byte line).
+// LDS layout.  Row r of a stage occupies 64 bytes = 4 chunks of 16 bytes;
+// chunk c is stored at position c ^ ((r / 2) % 4).  A fragment read (32 lanes
+// on 32 consecutive rows, one chunk each) then gives every group of 8 lanes 8
+// distinct (row parity, position) pairs, i.e. 8 distinct 16-byte bank groups:
+// no bank conflicts.  Global loads put 4 lanes on the 4 chunks of one row.
 //
-// Pipeline.  The next K-step is loaded straight from global memory into the
-// other LDS stage (global_load_lds_dwordx4, no registers) while the MFMAs
-// consume the current stage; one wait + barrier per K-step.
+// Pipeline.  K-steps are loaded straight from global memory into the LDS ring
+// (global_load_lds_dwordx4, no registers), three steps ahead of the MFMAs, so
+// about three K-steps of MFMA time cover the load latency; per K-step one
+// counted wait (vmcnt) for this wave's loads of that step, then one barrier.
 //
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin; the linear id is
 // remapped so that each XCD receives a contiguous range of tiles, and inside it
@@ -42,10 +43,12 @@ namespace ffn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;        // weight rows per tile
 constexpr int kBN = 256;        // token rows per tile
-constexpr int kRowBytes = 128;  // bytes per row per K-step
+constexpr int kRowBytes = 64;   // bytes per row per K-step (32 bf16 or 64 e4m3)
+constexpr int kStages = 4;      // LDS ring: three K-steps in flight ahead of the MFMAs
 constexpr int kStage = (kBM + kBN) * kRowBytes;
 constexpr int kGroupM = 4;
 
@@ -65,6 +68,21 @@ struct GemmArgs {
     int tiles_n;   // token-row tiles
 };
 
+// One wave-wide direct load: each lane's 16 bytes at gptr land in LDS at
+// lds_base + 16 * lane.  Issued as inline assembly so that the compiler does
+// not treat every later LDS read as dependent on it (it would otherwise wait
+// for all outstanding loads before each read); the kernel orders these loads
+// against its LDS reads itself, with counted vmcnt waits and barriers.
+__device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
 __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int T = tiles_m * tiles_n;
     int t = (T % 8 == 0) ? (b % 8) * (T / 8) + (b / 8) : b;
@@ -80,7 +98,7 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 template <bool kFP8, bool kFused>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
 
     int tm, tn;
     tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
@@ -91,16 +109,16 @@ void gemm_kernel(GemmArgs a) {
     const int wm = wave >> 1, wn = wave & 1;
 
     // ---- global -> LDS: direct loads (global_load_lds_dwordx4).  One wave
-    // instruction fills 1 KiB of LDS = 8 rows; lane l lands at position
-    // (row l/8, slot l%8) and so fetches chunk (l%8) ^ (l/8) of its row, which
-    // realises the XOR swizzle.  Wave w fills rows [64 w, 64 w + 64) of both
-    // operands.
-    const int lrow = lane >> 3;
-    const int lch = (lane & 7) ^ lrow;
-    uint32_t a_off[8], b_off[8];
+    // instruction fills 1 KiB of LDS = 16 rows of 64 bytes; lane l lands at
+    // (row l/4, slot l%4) and so fetches chunk (l%4) ^ ((row/2)%4) of its row,
+    // which realises the XOR swizzle.  Wave w fills rows [64 w, 64 w + 64) of
+    // both operands: 4 instructions each.
+    const int lrow = lane >> 2;
+    const int lch = (lane & 3) ^ ((lane >> 3) & 3);
+    uint32_t a_off[4], b_off[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int R = wave * 64 + i * 8 + lrow;
+    for (int i = 0; i < 4; ++i) {
+        const int R = wave * 64 + i * 16 + lrow;
         int wrow;
         if (kFused) {
             wrow = ((R & 64) ? a.H : 0) + tm * 128 + (R >> 7) * 64 + (R & 63);
@@ -120,75 +138,86 @@ void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // LDS byte address of this wave's first row (wave-uniform: an SGPR)
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 64 * kRowBytes);
 #define FFN_GLOAD(KT, ST)                                                                              \
     do {                                                                                               \
         const uint32_t kb_ = (uint32_t)(KT) * kRowBytes;                                               \
-        uint8_t* sbase_ = lds + (ST) * kStage + wave * 64 * kRowBytes;                                 \
-        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                             \
-            __builtin_amdgcn_global_load_lds((const void*)(a.w + a_off[i_] + kb_),                     \
-                (__attribute__((address_space(3))) void*)(sbase_ + i_ * 8 * kRowBytes), 16, 0, 0);     \
-            __builtin_amdgcn_global_load_lds((const void*)(a.x + b_off[i_] + kb_),                     \
-                (__attribute__((address_space(3))) void*)(sbase_ + kBM * kRowBytes + i_ * 8 * kRowBytes), \
-                16, 0, 0);                                                                             \
+        const uint32_t sb_ = lds_wave + (uint32_t)((ST) * kStage);                                     \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                             \
+            load_lds16(a.w + a_off[i_] + kb_, sb_ + i_ * 16 * kRowBytes);                              \
+            load_lds16(a.x + b_off[i_] + kb_, sb_ + kBM * kRowBytes + i_ * 16 * kRowBytes);            \
         }                                                                                              \
     } while (0)
 
-    // fragment rows of this lane
+    // fragment rows of this lane: row fr of each 32-row block, K half fh
     const int fr = lane & 31, fh = lane >> 5;
-    const int fsw = fr & 7;
+    const int fsw = (fr >> 1) & 3;
+    // Fragments of one K-step.  bf16: per 32-row block two 16-byte pieces,
+    // one per 16-value K sub-step (chunk 2*p + fh).  e4m3: per block the lane's
+    // 32 bytes (chunks 2*fh and 2*fh + 1) for one 32x32x64 MFMA.
+    typedef i32x4_t piece_t;
+    struct Frags {
+        piece_t a[4][2], b[4][2];
+    };
+    int coff[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) coff[p] = ((kFP8 ? (2 * fh + p) : (2 * p + fh)) ^ fsw) << 4;
+    const int a_row = (wm * 128 + fr) * kRowBytes;
+    const int b_row = kBM * kRowBytes + (wn * 128 + fr) * kRowBytes;
 
-    const int KT = a.K_bytes / kRowBytes;
-    FFN_GLOAD(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < KT) FFN_GLOAD(kt + 1, st ^ 1);
-        const uint8_t* As = lds + st * kStage + (wm * 128 + fr) * kRowBytes;
-        const uint8_t* Bs = lds + st * kStage + kBM * kRowBytes + (wn * 128 + fr) * kRowBytes;
+    auto read_frags = [&](Frags& f, int st) {
+        const uint8_t* base = lds + st * kStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                f.a[i][p] = *reinterpret_cast<const piece_t*>(base + a_row + i * 32 * kRowBytes + coff[p]);
+                f.b[i][p] = *reinterpret_cast<const piece_t*>(base + b_row + i * 32 * kRowBytes + coff[p]);
+            }
+    };
+    auto mfmas = [&](const Frags& f) {
         if (!kFP8) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int c = ((2 * kk + fh) ^ fsw) << 4;
-                bf16x8_t fa[4], fb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    fa[i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * kRowBytes + c);
-                    fb[i] = *reinterpret_cast<const bf16x8_t*>(Bs + i * 32 * kRowBytes + c);
-                }
+            for (int p = 0; p < 2; ++p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-            }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, f.a[i][p]), __builtin_bit_cast(bf16x8_t, f.b[j][p]),
+                            acc[i][j], 0, 0, 0);
         } else {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int c0 = ((4 * kk + 2 * fh) ^ fsw) << 4;
-                const int c1 = ((4 * kk + 2 * fh + 1) ^ fsw) << 4;
-                i32x8_t fa[4], fb[4];
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint4 a0 = *reinterpret_cast<const uint4*>(As + i * 32 * kRowBytes + c0);
-                    const uint4 a1 = *reinterpret_cast<const uint4*>(As + i * 32 * kRowBytes + c1);
-                    const uint4 b0 = *reinterpret_cast<const uint4*>(Bs + i * 32 * kRowBytes + c0);
-                    const uint4 b1 = *reinterpret_cast<const uint4*>(Bs + i * 32 * kRowBytes + c1);
-                    fa[i] = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                    fb[i] = i32x8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
-                                                                                     127, 0, 127);
-            }
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        __builtin_shufflevector(f.a[i][0], f.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                        __builtin_shufflevector(f.b[j][0], f.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[i][j], 0, 0,
+                        0, 127, 0, 127);
         }
-        // own direct loads for the next stage have landed, then everyone's
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    };
+
+    const int KT = a.K_bytes / kRowBytes;
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < KT) FFN_GLOAD(s, s);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        // step kt has landed for this wave once only the loads of the (at most
+        // two) steps after it are outstanding; the barrier extends that to every
+        // wave and retires all reads of step kt-1's stage, refilled next
+        const int after = min(kt + 2, KT - 1) - kt;
+        if (after >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (after == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + kStages - 1 < KT) FFN_GLOAD(kt + kStages - 1, (kt + kStages - 1) % kStages);
+        Frags f;
+        read_frags(f, kt % kStages);
+        mfmas(f);
     }
 #undef FFN_GLOAD
 
