@@ -7,140 +7,176 @@
 //   h[m,n] = bf16(silu(g) * u)
 //   y[m,c] = bf16(sd[c] * sum_n Wd[c,n] h[m,n])
 //
-// The weights are streamed once from HBM: every wave owns RPW weight rows (of
-// each matrix in the dual pass) and walks K in 1 KiB segments, one 16-byte
-// load (16 e4m3 codes) per lane per row per segment, two segments in flight.
-// Codes are decoded with v_cvt_pk_f32_fp8 (exact) and accumulated in fp32
-// against the activations, which are re-read per segment from L1/L2 (they are
-// a few KiB and shared by every wave).  A row's partial sums are reduced across
-// the wave at the end; lane m writes token m.
+// Both passes stream their weights from HBM once and are bound by it.  A
+// workgroup of 8 waves owns 16 weight rows (of each matrix in the dual pass);
+// its waves split K into 256-byte chunks, dealt round-robin.  Per chunk a lane
+// loads four 16-byte pieces of one row, the 4 lanes of a row covering 64
+// contiguous bytes per load instruction; the codes are widened to bf16 with
+// v_cvt_scalef32_pk_bf16_fp8 (exact: every e4m3 value is a bf16 value) and fed
+// as the A operand of v_mfma_f32_16x16x32_bf16, whose B operand holds the
+// matching activations of up to 16 tokens (zero beyond M).  The MFMA's K order
+// is free as long as A and B agree, so each lane's 8 codes per MFMA are simply
+// the 8 it loaded.  The eight partial 16 x 16 results are summed through LDS;
+// the row scale multiplies the finished fp32 sum.
 #include "common.h"
 #include "launch.h"
 
 namespace ffn {
 
-constexpr int kSeg = 1024;  // bytes of one weight row per wave-wide 16-byte load
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
 
-template <int MT>
-__device__ __forceinline__ void load_act(float (&xv)[MT][16], const uint16_t* __restrict__ x, int64_t ldx, int k,
-                                         bool ok, int M) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-        if (ok && m < M) {
-            const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + k);
-            v0 = p[0];
-            v1 = p[1];
-        }
-        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            xv[m][2 * q] = bf16lo(w[q]);
-            xv[m][2 * q + 1] = bf16hi(w[q]);
-        }
-    }
-}
+constexpr int kDecWaves = 8;
+constexpr int kChunk = 256;  // K bytes (= e4m3 codes) per wave per step
+constexpr int kPieces = kChunk / 64;  // 16-byte loads per lane per row per step
 
-template <int MT>
-__device__ __forceinline__ void fma_row(float (&acc)[MT], const uint4 wq, const float (&xv)[MT][16]) {
-    const uint32_t w[4] = {wq.x, wq.y, wq.z, wq.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f32x2_t lo = e4m3x2_to_f32(w[q], false);
-        const f32x2_t hi = e4m3x2_to_f32(w[q], true);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            acc[m] = __builtin_fmaf(lo[0], xv[m][4 * q + 0], acc[m]);
-            acc[m] = __builtin_fmaf(lo[1], xv[m][4 * q + 1], acc[m]);
-            acc[m] = __builtin_fmaf(hi[0], xv[m][4 * q + 2], acc[m]);
-            acc[m] = __builtin_fmaf(hi[1], xv[m][4 * q + 3], acc[m]);
-        }
-    }
+// 8 e4m3 codes (two dwords) -> 8 bf16 in MFMA operand order.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const bf16x2_t2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2_t2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2_t2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2_t2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // kDual: rows of w0 (gate) and w1 (up) with the SiLU epilogue -> out = h [M, rows].
-// else : rows of w0 (down) -> out = y [M, rows].
-template <int MT, int RPW, bool kDual>
-__global__ __launch_bounds__(256) void gemv_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ x,
-                                                   const uint8_t* __restrict__ w0, const float* __restrict__ s0,
-                                                   const uint8_t* __restrict__ w1, const float* __restrict__ s1,
-                                                   int M, int K, int rows) {
+// else : rows of w0 (down) -> out = y [M, rows].  x: [M, K] bf16.  TB = 16-token
+// blocks (M <= 16 * TB).
+template <bool kDual, int TB>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w0,
+    const float* __restrict__ s0, const uint8_t* __restrict__ w1, const float* __restrict__ s1, int M, int K,
+    int rows) {
     constexpr int NMAT = kDual ? 2 : 1;
+    __shared__ f32x4_t red[kDecWaves][NMAT][TB][64];
+
     const int lane = threadIdx.x & 63;
-    const int wave_g = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int row0 = wave_g * RPW;
-    if (row0 >= rows) return;
+    const int wave = threadIdx.x >> 6;
+    const int row0 = blockIdx.x * 16;
+    const int lr = lane & 15;   // weight row within the block / token within a token block
+    const int lq = lane >> 4;   // which 32-code quarter of the chunk
+    const int row = min(row0 + lr, rows - 1);
 
-    float acc[NMAT][RPW][MT];
+    const uint8_t* wrow[NMAT];
+    wrow[0] = w0 + (int64_t)row * K + lq * 16;
+    if (kDual) wrow[NMAT - 1] = w1 + (int64_t)row * K + lq * 16;
+    const uint16_t* xrow[TB];
+    bool tok_ok[TB];
 #pragma unroll
-    for (int a = 0; a < NMAT; ++a)
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[a][r][m] = 0.0f;
-
-    const uint8_t* wp[NMAT][RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int row = min(row0 + r, rows - 1);
-        wp[0][r] = w0 + (int64_t)row * K;
-        if (kDual) wp[NMAT - 1][r] = w1 + (int64_t)row * K;
+    for (int tb = 0; tb < TB; ++tb) {
+        const int tok = tb * 16 + lr;
+        tok_ok[tb] = tok < M;
+        xrow[tb] = x + (int64_t)min(tok, M - 1) * K + lq * 16;
     }
 
-    const int nseg = (K + kSeg - 1) / kSeg;
-    for (int sg = 0; sg < nseg; ++sg) {
-        const int k = sg * kSeg + lane * 16;
-        const bool ok = k < K;
-        uint4 wq[NMAT][RPW];
+    f32x4_t acc[NMAT][TB];
 #pragma unroll
-        for (int a = 0; a < NMAT; ++a)
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int r = 0; r < RPW; ++r)
-                wq[a][r] = ok ? *reinterpret_cast<const uint4*>(wp[a][r] + k) : make_uint4(0, 0, 0, 0);
-        float xv[MT][16];
-        load_act<MT>(xv, x, K, k, ok, M);
-#pragma unroll
-        for (int a = 0; a < NMAT; ++a)
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) fma_row<MT>(acc[a][r], wq[a][r], xv);
-    }
+        for (int tb = 0; tb < TB; ++tb) acc[m][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // Chunks go to the waves round-robin.  Each workgroup starts its walk
+    // along K at a different chunk, so the rows that the workgroups stream at
+    // one moment are not all at the same column offset (with power-of-two row
+    // lengths those addresses would crowd the same HBM channels).
+    const int nchunks = (K + kChunk - 1) / kChunk;  // K % 128 == 0: the last chunk may be half
+    const int rot = (int)(((unsigned)blockIdx.x * 5u) % (unsigned)nchunks);
+    for (int cw = wave; cw < nchunks; cw += kDecWaves) {
+        const int c = cw + rot < nchunks ? cw + rot : cw + rot - nchunks;
+        const int kb = c * kChunk;
+        // piece i of a row: bytes [kb + 64 i + 16 lq, +16): the 4 lanes of a
+        // row read 64 contiguous bytes per instruction
+        uint4 wq[NMAT][kPieces];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int row = row0 + r;
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            float v0 = wave_sum(acc[0][r][m]);
-            float v1 = kDual ? wave_sum(acc[NMAT - 1][r][m]) : 0.0f;
-            if (lane == m && row < rows && m < M) {
-                float o;
-                if (kDual) {
-                    const float g = round_bf16(s0[row] * v0);
-                    const float u = round_bf16(s1[row] * v1);
-                    o = silu_mul(g, u);
-                } else {
-                    o = s0[row] * v0;
+            for (int i = 0; i < kPieces; ++i)
+                wq[m][i] = (kb + 64 * i < K) ? *reinterpret_cast<const uint4*>(wrow[m] + kb + 64 * i)
+                                             : make_uint4(0, 0, 0, 0);
+        // the matching activations: 8 values per MFMA, piece i half q
+        bf16x8_t xb[TB][kPieces][2];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (tok_ok[tb] && kb + 64 * i < K)
+                        v = *reinterpret_cast<const uint4*>(xrow[tb] + kb + 64 * i + 8 * q);
+                    xb[tb][i][q] = __builtin_bit_cast(bf16x8_t, v);
                 }
-                out[(int64_t)m * rows + row] = (uint16_t)(pack_bf16x2(o, 0.0f) & 0xffffu);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) {
+                const bf16x8_t a0 = e4m3x8_to_bf16(wq[m][i].x, wq[m][i].y);
+                const bf16x8_t a1 = e4m3x8_to_bf16(wq[m][i].z, wq[m][i].w);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    acc[m][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xb[tb][i][0], acc[m][tb], 0, 0, 0);
+                    acc[m][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xb[tb][i][1], acc[m][tb], 0, 0, 0);
+                }
+            }
+    }
+
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) red[wave][m][tb][lane] = acc[m][tb];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            f32x4_t v = red[0][m][tb][lane];
+#pragma unroll
+            for (int w = 1; w < kDecWaves; ++w) {
+                const f32x4_t u = red[w][m][tb][lane];
+                v[0] += u[0];
+                v[1] += u[1];
+                v[2] += u[2];
+                v[3] += u[3];
+            }
+            acc[m][tb] = v;
+        }
+    // 16x16 MFMA result: lane holds token (lane % 16) of the token block and
+    // weight rows 4 * (lane / 16) + r, r = 0..3.
+    const int orow0 = row0 + 4 * lq;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int tok = tb * 16 + lr;
+        if (tok >= M || orow0 >= rows) continue;
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = orow0 + r;
+            if (kDual) {
+                const float g = round_bf16(s0[rr] * acc[0][tb][r]);
+                const float u = round_bf16(s1[rr] * acc[NMAT - 1][tb][r]);
+                o[r] = silu_mul(g, u);
+            } else {
+                o[r] = s0[rr] * acc[0][tb][r];
             }
         }
+        uint2 v;
+        v.x = pack_bf16x2(o[0], o[1]);
+        v.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2*>(out + (int64_t)tok * rows + orow0) = v;
     }
 }
 
-template <int MT>
-static hipError_t launch_decode_mt(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg,
+template <int TB>
+static hipError_t launch_decode_tb(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg,
                                    const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
                                    const float* sd, int M, int C, int H, hipStream_t s) {
-    constexpr int RPW_DUAL = MT <= 2 ? 4 : (MT <= 8 ? 2 : 1);
-    constexpr int RPW_DOWN = MT <= 2 ? 2 : 1;
-    const int waves_dual = (H + RPW_DUAL - 1) / RPW_DUAL;
-    hipLaunchKernelGGL((gemv_kernel<MT, RPW_DUAL, true>), dim3((waves_dual + 3) / 4), dim3(256), 0, s, h, x, wg,
-                       sg, wu, su, M, C, H);
+    hipLaunchKernelGGL((decode_kernel<true, TB>), dim3((H + 15) / 16), dim3(64 * kDecWaves), 0, s, h, x, wg, sg, wu,
+                       su, M, C, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int waves_down = (C + RPW_DOWN - 1) / RPW_DOWN;
-    hipLaunchKernelGGL((gemv_kernel<MT, RPW_DOWN, false>), dim3((waves_down + 3) / 4), dim3(256), 0, s, out, h,
-                       wd, sd, nullptr, nullptr, M, H, C);
+    hipLaunchKernelGGL((decode_kernel<false, TB>), dim3((C + 15) / 16), dim3(64 * kDecWaves), 0, s, out, h, wd, sd,
+                       nullptr, nullptr, M, H, C);
     return hipGetLastError();
 }
 
@@ -148,12 +184,8 @@ hipError_t launch_decode(uint16_t* out, uint16_t* h, const uint16_t* x, const ui
                          const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd, int M, int C,
                          int H, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    if (M == 1) return launch_decode_mt<1>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    if (M <= 2) return launch_decode_mt<2>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    if (M <= 4) return launch_decode_mt<4>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    if (M <= 8) return launch_decode_mt<8>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    if (M <= 16) return launch_decode_mt<16>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    return launch_decode_mt<32>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    if (M <= 16) return launch_decode_tb<1>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    return launch_decode_tb<2>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
 }
 
 }  // namespace ffn
