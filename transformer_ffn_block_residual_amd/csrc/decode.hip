@@ -26,7 +26,9 @@ namespace ffn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
 
-constexpr int kDecWaves = 8;
+// waves per workgroup per pass; row blocks per workgroup of the dual pass
+// when several tokens share each weight (activation reuse)
+constexpr int kDualWaves = 8, kDownWaves = 8, kDualRB = 1;
 constexpr int kChunk = 256;  // K bytes (= e4m3 codes) per wave per step
 constexpr int kPieces = kChunk / 64;  // 16-byte loads per lane per row per step
 
@@ -41,25 +43,29 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 // kDual: rows of w0 (gate) and w1 (up) with the SiLU epilogue -> out = h [M, rows].
 // else : rows of w0 (down) -> out = y [M, rows].  x: [M, K] bf16.  TB = 16-token
-// blocks (M <= 16 * TB).
-template <bool kDual, int TB>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
+// blocks (M <= 16 * TB); RB = 16-row blocks per workgroup (each activation
+// fragment is multiplied into RB * NMAT row blocks).
+template <bool kDual, int TB, int RB, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w0,
     const float* __restrict__ s0, const uint8_t* __restrict__ w1, const float* __restrict__ s1, int M, int K,
     int rows) {
     constexpr int NMAT = kDual ? 2 : 1;
-    __shared__ f32x4_t red[kDecWaves][NMAT][TB][64];
+    __shared__ f32x4_t red[kWaves][RB][NMAT][TB][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int row0 = blockIdx.x * 16;
-    const int lr = lane & 15;   // weight row within the block / token within a token block
-    const int lq = lane >> 4;   // which 32-code quarter of the chunk
-    const int row = min(row0 + lr, rows - 1);
+    const int row0 = blockIdx.x * 16 * RB;
+    const int lr = lane & 15;   // weight row within a block / token within a token block
+    const int lq = lane >> 4;   // which 16-byte quarter of each 64-byte piece
 
-    const uint8_t* wrow[NMAT];
-    wrow[0] = w0 + (int64_t)row * K + lq * 16;
-    if (kDual) wrow[NMAT - 1] = w1 + (int64_t)row * K + lq * 16;
+    const uint8_t* wrow[RB][NMAT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = min(row0 + rb * 16 + lr, rows - 1);
+        wrow[rb][0] = w0 + (int64_t)row * K + lq * 16;
+        if (kDual) wrow[rb][NMAT - 1] = w1 + (int64_t)row * K + lq * 16;
+    }
     const uint16_t* xrow[TB];
     bool tok_ok[TB];
 #pragma unroll
@@ -69,30 +75,34 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
         xrow[tb] = x + (int64_t)min(tok, M - 1) * K + lq * 16;
     }
 
-    f32x4_t acc[NMAT][TB];
+    f32x4_t acc[RB][NMAT][TB];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[m][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[rb][m][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // Chunks go to the waves round-robin.  Each workgroup starts its walk
     // along K at a different chunk, so the rows that the workgroups stream at
     // one moment are not all at the same column offset (with power-of-two row
-    // lengths those addresses would crowd the same HBM channels).
+    // lengths those addresses crowd the same HBM channels).
     const int nchunks = (K + kChunk - 1) / kChunk;  // K % 128 == 0: the last chunk may be half
     const int rot = (int)(((unsigned)blockIdx.x * 5u) % (unsigned)nchunks);
-    for (int cw = wave; cw < nchunks; cw += kDecWaves) {
+    for (int cw = wave; cw < nchunks; cw += kWaves) {
         const int c = cw + rot < nchunks ? cw + rot : cw + rot - nchunks;
         const int kb = c * kChunk;
         // piece i of a row: bytes [kb + 64 i + 16 lq, +16): the 4 lanes of a
         // row read 64 contiguous bytes per instruction
-        uint4 wq[NMAT][kPieces];
+        uint4 wq[RB][NMAT][kPieces];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i)
-                wq[m][i] = (kb + 64 * i < K) ? *reinterpret_cast<const uint4*>(wrow[m] + kb + 64 * i)
-                                             : make_uint4(0, 0, 0, 0);
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int i = 0; i < kPieces; ++i)
+                    wq[rb][m][i] = (kb + 64 * i < K) ? *reinterpret_cast<const uint4*>(wrow[rb][m] + kb + 64 * i)
+                                                     : make_uint4(0, 0, 0, 0);
         // the matching activations: 8 values per MFMA, piece i half q
         bf16x8_t xb[TB][kPieces][2];
 #pragma unroll
@@ -107,43 +117,52 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
                     xb[tb][i][q] = __builtin_bit_cast(bf16x8_t, v);
                 }
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
-                const bf16x8_t a0 = e4m3x8_to_bf16(wq[m][i].x, wq[m][i].y);
-                const bf16x8_t a1 = e4m3x8_to_bf16(wq[m][i].z, wq[m][i].w);
+            for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    acc[m][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xb[tb][i][0], acc[m][tb], 0, 0, 0);
-                    acc[m][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xb[tb][i][1], acc[m][tb], 0, 0, 0);
+                for (int i = 0; i < kPieces; ++i) {
+                    const bf16x8_t a0 = e4m3x8_to_bf16(wq[rb][m][i].x, wq[rb][m][i].y);
+                    const bf16x8_t a1 = e4m3x8_to_bf16(wq[rb][m][i].z, wq[rb][m][i].w);
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        acc[rb][m][tb] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xb[tb][i][0], acc[rb][m][tb], 0, 0, 0);
+                        acc[rb][m][tb] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xb[tb][i][1], acc[rb][m][tb], 0, 0, 0);
+                    }
                 }
-            }
     }
 
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) red[wave][m][tb][lane] = acc[m][tb];
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) red[wave][rb][m][tb][lane] = acc[rb][m][tb];
     __syncthreads();
-    if (wave != 0) return;
+    // wave rb < RB finishes row block rb
+    if (wave >= RB) return;
+    const int rb = wave;
+    f32x4_t fin[NMAT][TB];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            f32x4_t v = red[0][m][tb][lane];
+            f32x4_t v = red[0][rb][m][tb][lane];
 #pragma unroll
-            for (int w = 1; w < kDecWaves; ++w) {
-                const f32x4_t u = red[w][m][tb][lane];
+            for (int w = 1; w < kWaves; ++w) {
+                const f32x4_t u = red[w][rb][m][tb][lane];
                 v[0] += u[0];
                 v[1] += u[1];
                 v[2] += u[2];
                 v[3] += u[3];
             }
-            acc[m][tb] = v;
+            fin[m][tb] = v;
         }
     // 16x16 MFMA result: lane holds token (lane % 16) of the token block and
-    // weight rows 4 * (lane / 16) + r, r = 0..3.
-    const int orow0 = row0 + 4 * lq;
+    // weight rows 4 * (lane / 16) + r, r = 0..3, of the row block.
+    const int orow0 = row0 + rb * 16 + 4 * lq;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const int tok = tb * 16 + lr;
@@ -153,11 +172,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
         for (int r = 0; r < 4; ++r) {
             const int rr = orow0 + r;
             if (kDual) {
-                const float g = round_bf16(s0[rr] * acc[0][tb][r]);
-                const float u = round_bf16(s1[rr] * acc[NMAT - 1][tb][r]);
+                const float g = round_bf16(s0[rr] * fin[0][tb][r]);
+                const float u = round_bf16(s1[rr] * fin[NMAT - 1][tb][r]);
                 o[r] = silu_mul(g, u);
             } else {
-                o[r] = s0[rr] * acc[0][tb][r];
+                o[r] = s0[rr] * fin[0][tb][r];
             }
         }
         uint2 v;
@@ -167,16 +186,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
     }
 }
 
-template <int TB>
+template <int TB, int RB_DUAL>
 static hipError_t launch_decode_tb(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg,
                                    const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
                                    const float* sd, int M, int C, int H, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<true, TB>), dim3((H + 15) / 16), dim3(64 * kDecWaves), 0, s, h, x, wg, sg, wu,
-                       su, M, C, H);
+    // H and C are multiples of 128, so whole row blocks always
+    hipLaunchKernelGGL((decode_kernel<true, TB, RB_DUAL, kDualWaves>), dim3(H / (16 * RB_DUAL)),
+                       dim3(64 * kDualWaves), 0, s, h, x, wg, sg, wu, su, M, C, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_kernel<false, TB>), dim3((C + 15) / 16), dim3(64 * kDecWaves), 0, s, out, h, wd, sd,
-                       nullptr, nullptr, M, H, C);
+    hipLaunchKernelGGL((decode_kernel<false, TB, 1, kDownWaves>), dim3(C / 16), dim3(64 * kDownWaves), 0, s, out, h,
+                       wd, sd, nullptr, nullptr, M, H, C);
     return hipGetLastError();
 }
 
@@ -184,8 +204,9 @@ hipError_t launch_decode(uint16_t* out, uint16_t* h, const uint16_t* x, const ui
                          const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd, int M, int C,
                          int H, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    if (M <= 16) return launch_decode_tb<1>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    return launch_decode_tb<2>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    if (M <= 4) return launch_decode_tb<1, 1>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    if (M <= 16) return launch_decode_tb<1, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    return launch_decode_tb<2, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
 }
 
 }  // namespace ffn
