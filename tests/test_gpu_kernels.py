@@ -200,7 +200,7 @@ def test_gateup_fp8_integer_inputs_bit_exact(F, N, C, H):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("N,C,H", [(64, 256, 768), (300, 512, 384)])
+@pytest.mark.parametrize("N,C,H", [(64, 256, 768), (300, 512, 384), (1100, 256, 7680)])
 def test_gateup_random_and_fused_equals_unfused(F, fp8, N, C, H):
     say(f"gateup random fp8={fp8} N={N} C={C} H={H}")
     d = W.block_inputs(N, C, H, seed=N + C + H, w_std=0.0)
@@ -232,7 +232,7 @@ def test_gateup_random_and_fused_equals_unfused(F, fp8, N, C, H):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("N,H,C", [(64, 768, 256), (300, 384, 512), (513, 256, 384)])
+@pytest.mark.parametrize("N,H,C", [(64, 768, 256), (300, 384, 512), (513, 256, 384), (3100, 384, 5248)])
 def test_down(F, fp8, N, H, C):
     say(f"down fp8={fp8} N={N} H={H} C={C}")
     h = W.normal_bf16((N, H), 1.0, N + H, 3)
@@ -255,6 +255,44 @@ def test_down(F, fp8, N, H, C):
     assert np.all(within_dot_bound(g, exact, mag))
     if not fp8:  # fp32 accumulation: beyond the last bit only where the sum cancels
         assert np.mean(ulp_diff(g, ref) > 1) < 1e-3
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("fused", [False, True])
+def test_gemm_writes_stay_inside_the_output(F, fp8, fused):
+    # More tiles than workgroups (each workgroup walks several), a ragged last
+    # token tile and, for the down projection, a half-filled last feature
+    # tile: nothing past the output may be written.
+    if fused:
+        N, R, O_ = 1100, 384, 7680          # gate+up, H = 7680: 60 x 5 tiles
+    else:
+        N, R, O_ = 3100, 384, 5248          # down, C = 41 * 128: 21 x 13 tiles
+    say(f"gemm guard fp8={fp8} fused={fused}")
+    x = _int_e4m3((N, R), 11) if fp8 else _int_bf16((N, R), 11)
+    w_rows = 2 * O_ if fused else O_
+    w = _int_e4m3((w_rows, R), 12) if fp8 else _int_bf16((w_rows, R), 12)
+    guard = torch.full(((N + 3) * O_,), 0x7B7B, dtype=torch.int16, device="cuda")
+    out = guard[: N * O_].view(N, O_).view(torch.bfloat16)
+    one = dev_f32([1.0])
+    xa, wa = (dev_u8(x), dev_u8(w)) if fp8 else (dev_bf16(x), dev_bf16(w))
+    xs, ws, dt = (one, one, F.FFN_E4M3) if fp8 else (None, None, F.FFN_BF16)
+    if fused:
+        F.ffn_gateup(out, None, xa, xs, wa, ws, dt, 1, N, R, O_)
+    else:
+        F.ffn_down(out, xa, xs, wa, ws, dt, N, R, O_)
+    torch.cuda.synchronize()
+    assert torch.all(guard[N * O_:] == 0x7B7B)
+    ref = O.gemm_fp8(x, np.float32(1), w, np.float32(1)) if fp8 else O.gemm_bf16(x, w)
+    g = host_bits(out)
+    if fused:
+        # integer g and u are exact; only the hardware exp / reciprocal of the
+        # SiLU can move a result by one bf16 step, or, where silu(g) underflows
+        # (g below about -80), leave 0 for a value under 1e-30
+        h_ref, _ = O.swiglu(ref)
+        tiny = (np.abs(K.bf16_bits_to_f64(h_ref)) < 1e-30) & (np.abs(K.bf16_bits_to_f64(g)) < 1e-30)
+        assert np.all((ulp_diff(g, h_ref) <= 1) | tiny)
+    else:
+        assert np.array_equal(g, ref)
 
 
 def test_gemm_integer_down_bit_exact_and_deterministic(F):

@@ -49,7 +49,6 @@ namespace ffn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;        // weight rows per tile
 constexpr int kBN = 256;        // token rows per tile
@@ -79,18 +78,28 @@ struct GemmArgs {
     int tiles_n;   // token-row tiles
 };
 
-// One wave-wide direct load: lane l's 16 bytes at base + off land in LDS at
-// lds_addr + 16 l.  Issued as inline assembly so that the compiler does not
-// treat every later LDS read as dependent on it (it would otherwise wait for
-// all outstanding loads before each read); the kernel orders these loads
-// against its LDS reads itself, with counted vmcnt waits and barriers.
-__device__ __forceinline__ void load_lds16(uint32_t off, const uint8_t* base, uint32_t lds_addr) {
+// A buffer resource (V#) for raw byte addressing: base address, no stride,
+// num_records bytes; accesses at or beyond num_records read zero and drop
+// stores (the range check of buffer instructions).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t num_records) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4_t{(int)(uint32_t)p, (int)(uint32_t)(p >> 32) & 0xffff, (int)num_records, 0x00020000};
+}
+
+// One wave-wide direct load: lane l's 16 bytes at rsrc + soff + voff land in
+// LDS at lds_addr + 16 l (zeros where the range check fails).  Issued as
+// inline assembly so that the compiler does not treat every later LDS read as
+// dependent on it (it would otherwise wait for all outstanding loads before
+// each read); the kernel orders these loads against its LDS reads itself, with
+// counted vmcnt waits and barriers.
+__device__ __forceinline__ void load_lds16(uint32_t voff, i32x4_t rsrc, uint32_t soff, uint32_t lds_addr) {
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
         :
-        : "v"(off), "s"(base), "s"(lds_addr)
+        : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
         : "memory");
 }
 
@@ -123,15 +132,19 @@ struct Frags {
 
 // Where a wave's loads and reads of a K-step go.
 struct StepIO {
-    const uint8_t* lds;     // the ring (generic pointer)
-    uint32_t lds_wave;      // LDS address of this wave's first load row in stage 0
-    uint32_t a_off[kLoads];  // byte offsets of this lane's load rows in w and x
-    uint32_t b_off[kLoads];
-    int a_rd[2], b_rd[2];   // byte offsets of this lane's fragment pieces in a stage
+    const uint8_t* lds;       // the ring (generic pointer)
+    uint32_t lds_wave;        // LDS address of this wave's first load row in stage 0
+    uint32_t voff[kLoads];    // byte offset of this lane's row of load i in its wave's 64-row slab
+    int a_rd[2], b_rd[2];     // byte offsets of this lane's fragment pieces in a stage
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const StepIO& io, int step) {
-    const uint8_t* st = io.lds + (step % kStages) * kStage;
+// The 64-row slabs of w and x that one wave loads for one tile.
+struct TileRsrc {
+    i32x4_t a, b;
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const StepIO& io, int g) {
+    const uint8_t* st = io.lds + (g % kStages) * kStage;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int blk = (r & 7) >> 1, p = r & 1;
@@ -140,26 +153,30 @@ __device__ __forceinline__ void read_frags(Frags& f, const StepIO& io, int step)
     }
 }
 
-// Load instruction l (0 .. 2 kLoads - 1; A first) of K-step `step`.
-__device__ __forceinline__ void load_part(const GemmArgs& a, const StepIO& io, int step, int l) {
-    const uint32_t kb = (uint32_t)step * kRowBytes;
-    const uint32_t st = io.lds_wave + (uint32_t)((step % kStages) * kStage);
-    if (l < kLoads) load_lds16(io.a_off[l], a.w + kb, st + l * 16 * kRowBytes);
-    else load_lds16(io.b_off[l - kLoads], a.x + kb, st + kBM * kRowBytes + (l - kLoads) * 16 * kRowBytes);
+// Load instruction l (0 .. 2 kLoads - 1; A first) of K-step kk of the tile
+// whose slabs are `tr`, into ring slot `stage`.
+__device__ __forceinline__ void load_part(const StepIO& io, const TileRsrc& tr, int stage, int kk, int l) {
+    const uint32_t kb = (uint32_t)kk * kRowBytes;
+    const uint32_t st = io.lds_wave + (uint32_t)(stage * kStage);
+    if (l < kLoads) load_lds16(io.voff[l], tr.a, kb, st + l * 16 * kRowBytes);
+    else load_lds16(io.voff[l - kLoads], tr.b, kb, st + kBM * kRowBytes + (l - kLoads) * 16 * kRowBytes);
 }
 
-// The MFMAs of K-step k from `cur`; with kRead the fragments of step k + 1 are
-// read into `nxt` meanwhile, with kLoad the loads of step k + kAhead issued.
-template <bool kFP8, bool kLoad, bool kRead>
+// The MFMAs of stream step g from `cur`, while the fragments of step g + 1 are
+// read into `nxt` and the loads of step g + kAhead (K-step ld_k of the tile
+// whose slabs are `tr`) are issued.  The code must be free of branches: the
+// scheduling fences order instructions within a basic block only.
+template <bool kFP8>
 __device__ __forceinline__ void k_step(f32x16_t (&acc)[4][4], const Frags& cur, Frags& nxt, const GemmArgs& a,
-                                       const StepIO& io, int k) {
+                                       const StepIO& io, int g, const TileRsrc& tr, int ld_k) {
     constexpr int kM = kFP8 ? 16 : 32;  // MFMAs per step
     constexpr int kPerRead = kM / 16, kPerLoad = kM / (2 * kLoads);
-    const uint8_t* st = io.lds + ((k + 1) % kStages) * kStage;
-    const int kl = k + kAhead;
+    const uint8_t* st = io.lds + ((g + 1) % kStages) * kStage;
+    const int ld_stage = (g + kAhead) % kStages;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < kM; ++m) {
-        if (kRead && m % kPerRead == 0) {
+        if (m % kPerRead == 0) {
             const int r = m / kPerRead, blk = (r & 7) >> 1, p = r & 1;
             if (r < 8) nxt.a[blk][p] = *reinterpret_cast<const i32x4_t*>(st + io.a_rd[p] + blk * kBlockBytes);
             else nxt.b[blk][p] = *reinterpret_cast<const i32x4_t*>(st + io.b_rd[p] + blk * kBlockBytes);
@@ -176,8 +193,166 @@ __device__ __forceinline__ void k_step(f32x16_t (&acc)[4][4], const Frags& cur, 
                                                                 __builtin_bit_cast(bf16x8_t, cur.b[j][p]),
                                                                 acc[i][j], 0, 0, 0);
         }
-        if (kLoad && m % kPerLoad == kPerLoad - 1) load_part(a, io, kl, m / kPerLoad);
+        if (m % kPerLoad == kPerLoad - 1) load_part(io, tr, ld_stage, ld_k, m / kPerLoad);
         __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The slabs of w and x that wave `wave` loads for tile t (launch order).
+// Weight rows: plain, rows [256 tm + 64 wave, +64) of w; SwiGLU-fused, the
+// tile's 128 gate rows [128 tm, +128) of w followed by the matching up rows
+// [H + 128 tm, +128), so wave w takes gate rows (w & 1) = 0 or up rows
+// (w & 1) = 1, half w >> 1.  Rows past O (plain) and tokens past N are cut
+// off by num_records and load as zeros.
+template <bool kFused>
+__device__ __forceinline__ TileRsrc tile_rsrc(const GemmArgs& a, int t, int wave) {
+    int tm, tn;
+    tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t kb = a.K_bytes;
+    int64_t wrow0, wrows;
+    if (kFused) {
+        wrow0 = (int64_t)((wave & 1) ? a.H : 0) + (int64_t)tm * 128 + (wave >> 1) * 64;
+        wrows = 64;
+    } else {
+        wrow0 = (int64_t)tm * kBM + wave * 64;
+        wrows = min((int64_t)64, max((int64_t)0, (int64_t)a.O - wrow0));
+    }
+    const int64_t xrow0 = (int64_t)tn * kBN + wave * 64;
+    const int64_t xrows = min((int64_t)64, max((int64_t)0, a.N - xrow0));
+    TileRsrc r;
+    r.a = make_rsrc(a.w + wrow0 * kb, (uint32_t)(wrows * kb));
+    r.b = make_rsrc(a.x + xrow0 * kb, (uint32_t)(xrows * kb));
+    return r;
+}
+
+__device__ __forceinline__ TileRsrc select_rsrc(bool c, const TileRsrc& x, const TileRsrc& y) {
+    TileRsrc r;
+    r.a = c ? x.a : y.a;
+    r.b = c ? x.b : y.b;
+    return r;
+}
+
+// Store instructions per lane in one tile's epilogue (16-byte stores).
+template <bool kFused>
+constexpr int epilogue_stores() { return kFused ? 16 : 32; }
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// The 16 accumulators of one MFMA block, copied to ordinary registers right
+// here.  Written as assembly so that the compiler cannot gather the copies of
+// all 256 accumulators at the start of the epilogue (which would exhaust the
+// registers); kHazardPad adds the wait states an accumulator read needs after
+// the MFMA that wrote it (the first block read after the K loop).
+template <bool kHazardPad>
+__device__ __forceinline__ f32x16_t read_acc(const f32x16_t& x) {
+    f32x16_t v;
+    if (kHazardPad) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    asm volatile(
+        "v_accvgpr_read_b32 %0, %16\n\tv_accvgpr_read_b32 %1, %17\n\t"
+        "v_accvgpr_read_b32 %2, %18\n\tv_accvgpr_read_b32 %3, %19\n\t"
+        "v_accvgpr_read_b32 %4, %20\n\tv_accvgpr_read_b32 %5, %21\n\t"
+        "v_accvgpr_read_b32 %6, %22\n\tv_accvgpr_read_b32 %7, %23\n\t"
+        "v_accvgpr_read_b32 %8, %24\n\tv_accvgpr_read_b32 %9, %25\n\t"
+        "v_accvgpr_read_b32 %10, %26\n\tv_accvgpr_read_b32 %11, %27\n\t"
+        "v_accvgpr_read_b32 %12, %28\n\tv_accvgpr_read_b32 %13, %29\n\t"
+        "v_accvgpr_read_b32 %14, %30\n\tv_accvgpr_read_b32 %15, %31"
+        : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]), "=v"(v[7]),
+          "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]), "=v"(v[14]), "=v"(v[15])
+        : "a"(x[0]), "a"(x[1]), "a"(x[2]), "a"(x[3]), "a"(x[4]), "a"(x[5]), "a"(x[6]), "a"(x[7]), "a"(x[8]),
+          "a"(x[9]), "a"(x[10]), "a"(x[11]), "a"(x[12]), "a"(x[13]), "a"(x[14]), "a"(x[15]));
+    return v;
+}
+
+// Lanes l and l + 32 hold the same token row and interleaved runs of four
+// features: lane l runs 0 and 2 of each 32-feature block (features 0-3,
+// 16-19), lane l + 32 runs 1 and 3 (4-7, ...), as fh * 4 + 8 g.  One
+// v_permlane32_swap per dword pair regroups runs 2q and 2q + 1 so that lane l
+// holds features 16q + 0..7 and lane l + 32 features 16q + 8..15: one 16-byte
+// store each.  x = run 2q, y = run 2q + 1 (two packed dwords each).
+__device__ __forceinline__ u32x4_t regroup_runs(uint32_t x0, uint32_t x1, uint32_t y0, uint32_t y1) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    return u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+}
+
+// One tile's output.  Every lane issues exactly epilogue_stores() buffer
+// stores; rows past N and features past O are dropped by the buffer's range
+// check (their offsets point past num_records), so the count of outstanding
+// memory operations stays exact for the pipeline's counted waits.
+template <bool kFP8, bool kFused>
+__device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmArgs& a, int t, float s, int wm,
+                                              int wn, int fr, int fh, float& amax) {
+    int tm, tn;
+    tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
+    // recomputed per tile: kept out of registers across the K loop
+    asm volatile("" : "+v"(fr), "+v"(fh));
+    const int64_t n0 = (int64_t)tn * kBN;
+    uint8_t* base = reinterpret_cast<uint8_t*>(a.out) + n0 * a.ld_out * 2;
+    const int64_t rem = (a.N - n0) * (int64_t)a.ld_out * 2;
+    const uint32_t nrec = (uint32_t)(rem < ((int64_t)1 << 30) ? rem : ((int64_t)1 << 30));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)nrec, 0x00020000);
+    const uint32_t row_bytes = (uint32_t)a.ld_out * 2;
+    const int r_base = wn * 128 + fr;  // token row within the tile, block j adds 32 j
+    if (!kFused) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x16_t blk = (i == 0 && j == 0) ? read_acc<true>(acc[i][j]) : read_acc<false>(acc[i][j]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    uint32_t d[4];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int g = 2 * q + h;
+                        d[2 * h] = pack_bf16x2(blk[4 * g + 0] * s, blk[4 * g + 1] * s);
+                        d[2 * h + 1] = pack_bf16x2(blk[4 * g + 2] * s, blk[4 * g + 3] * s);
+                    }
+                    const u32x4_t v = regroup_runs(d[0], d[1], d[2], d[3]);
+                    const int o = tm * kBM + wm * 128 + i * 32 + 16 * q + 8 * fh;
+                    const uint32_t off = o < a.O ? (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * 2
+                                                 : 0x7fffffffu;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool ok = n0 + r_base + 32 * j < a.N;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const f32x16_t gb = (i == 0 && j == 0) ? read_acc<true>(acc[i][j]) : read_acc<false>(acc[i][j]);
+                const f32x16_t ub = read_acc<false>(acc[i + 2][j]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    uint32_t d[4];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int g = 2 * q + h;
+                        float hv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float gg = round_bf16(gb[4 * g + e] * s);
+                            const float uu = round_bf16(ub[4 * g + e] * s);
+                            hv[e] = silu_mul(gg, uu);
+                        }
+                        d[2 * h] = pack_bf16x2(hv[0], hv[1]);
+                        d[2 * h + 1] = pack_bf16x2(hv[2], hv[3]);
+                    }
+                    float m = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(d[e])), __builtin_fabsf(bf16hi(d[e]))));
+                    amax = __builtin_fmaxf(amax, ok ? m : 0.0f);
+                    const u32x4_t v = regroup_runs(d[0], d[1], d[2], d[3]);
+                    const int o = tm * 128 + wm * 64 + i * 32 + 16 * q + 8 * fh;
+                    const uint32_t off = (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * 2;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
     }
 }
 
@@ -186,9 +361,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void gemm_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
+    constexpr int kStoreCnt = epilogue_stores<kFused>();
+    static_assert(2 * kLoads * (kAhead - 2) + kStoreCnt <= 63, "vmcnt holds at most 63");
 
-    int tm, tn;
-    tile_coords(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    // Persistent: workgroup b takes tiles b, b + G, b + 2G, ... (launch order,
+    // mapped to tile coordinates by tile_coords).  Its K-steps form one stream
+    // across its tiles, so the ring never drains between tiles: the first
+    // steps of the next tile load while the current tile finishes.
+    const int T = a.tiles_m * a.tiles_n;
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int KT = a.K_bytes / kRowBytes;  // even: the ABI requires K % 128 == 0 (elements)
+
+    float s = 1.0f;
+    if (kFP8) s = (*a.x_scale) * (*a.w_scale);
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -197,6 +383,7 @@ void gemm_kernel(GemmArgs a) {
 
     StepIO io;
     io.lds = lds;
+    f32x16_t acc[4][4];
     // ---- global -> LDS.  One wave instruction fills 1 KiB of a stage = 16
     // rows of 64 bytes; lane l lands at (row l/4, slot l%4) and so fetches
     // chunk (l%4) ^ ((row/4)%4) of its row, which realises the XOR swizzle.
@@ -204,18 +391,7 @@ void gemm_kernel(GemmArgs a) {
     const int lrow = lane >> 2;
     const int lch = (lane & 3) ^ ((lane >> 4) & 3);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int R = wave * 16 * kLoads + i * 16 + lrow;
-        int wrow;
-        if (kFused) {
-            wrow = ((R & 64) ? a.H : 0) + tm * 128 + (R >> 7) * 64 + (R & 63);
-        } else {
-            wrow = min(tm * kBM + R, a.O - 1);
-        }
-        const int64_t xrow = min((int64_t)tn * kBN + R, a.N - 1);
-        io.a_off[i] = (uint32_t)wrow * (uint32_t)a.K_bytes + (uint32_t)(lch << 4);
-        io.b_off[i] = (uint32_t)xrow * (uint32_t)a.K_bytes + (uint32_t)(lch << 4);
-    }
+    for (int i = 0; i < kLoads; ++i) io.voff[i] = (uint32_t)(i * 16 + lrow) * (uint32_t)a.K_bytes + (uint32_t)(lch << 4);
     io.lds_wave = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 16 * kLoads * kRowBytes);
 
@@ -229,118 +405,115 @@ void gemm_kernel(GemmArgs a) {
         io.b_rd[p] = kBM * kRowBytes + (wn * 128 + fr) * kRowBytes + coff;
     }
 
-    f32x16_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // Loads run kAhead K-steps ahead of the MFMAs, so the last steps of a tile
+    // load the first steps of the workgroup's next tile.  After its last tile
+    // a workgroup keeps loading steps of that tile again: those loads fill
+    // stages that are never read and keep every step's load count, and so the
+    // counted waits, uniform.  With KT < kAhead the loads would run more than
+    // one tile ahead; such problems get one tile per workgroup (G = T), where
+    // every load past the tile's own steps is one of these stand-ins.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    TileRsrc tr_cur = tile_rsrc<kFused>(a, b, wave_u);
+    TileRsrc tr_nxt = tile_rsrc<kFused>(a, b + G < T ? b + G : b, wave_u);
+    // K-step of the load issued during step kk of a tile (tile-relative
+    // kk + kAhead, wrapped into the next tile)
+    auto wrap_k = [&](int k) {
+        if (k >= KT) k -= KT;
+        if (k >= KT) k -= KT;
+        return k;
+    };
 
-    // K-steps: KT is even (the ABI requires K % 128 == 0 elements).  Step k
-    // lives in stage k % 5.  Before the MFMAs of step k, steps k and k + 1 are
-    // in LDS and visible to every wave (the fragments of k are in registers),
-    // and this wave has issued the loads of steps up to k + 3.  During step k
-    // it issues the loads of step k + 4 into the stage of step k - 1, whose
-    // fragments every wave finished reading before the barrier that closed
-    // step k - 1; after step k it waits for its loads of step k + 2 and meets
-    // the others at the barrier.
-    const int KT = a.K_bytes / kRowBytes;
-    Frags f0, f1;
-    const int n0 = min(kAhead, KT);
+    // Stream step g lives in stage g % 5.  Before the MFMAs of step g, steps
+    // g and g + 1 are in LDS and visible to every wave (the fragments of g are
+    // in registers) and this wave has issued the loads of steps up to g + 3.
+    // During step g it issues the loads of step g + 4 into the stage of step
+    // g - 1, whose fragments every wave finished reading before the barrier
+    // that closed step g - 1; after step g it waits for its loads of step
+    // g + 2 and meets the others at the barrier.  Memory operations complete
+    // in issue order, so "the loads of g + 2 have landed" is "at most the
+    // operations issued after them are outstanding": the loads of g + 3 and
+    // g + 4, plus, in the first two steps of a tile, the stores of the
+    // previous tile's epilogue.
 #pragma unroll
-    for (int s = 0; s < kAhead; ++s)
-        if (s < n0)
+    for (int g = 0; g < kAhead; ++g) {
+        const TileRsrc tr = select_rsrc(g < KT, tr_cur, tr_nxt);
+        const int k = g < KT ? g : wrap_k(g);
 #pragma unroll
-            for (int l = 0; l < 2 * kLoads; ++l) load_part(a, io, s, l);
-    if (n0 == kAhead) wait_vmcnt<2 * kLoads * (kAhead - 2)>();
-    else wait_vmcnt<0>();
+        for (int l = 0; l < 2 * kLoads; ++l) load_part(io, tr, g, k, l);
+    }
+    // Stand-ins for the stores of a previous tile's epilogue (dropped by the
+    // range check: num_records is 0), so that the first tile's first two
+    // waits count the same operations as every later tile's.
+    {
+        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, 0, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < kStoreCnt; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, none, 16 * i, 0, 0);
+    }
+    constexpr int kWait = 2 * kLoads * (kAhead - 2);
+    wait_vmcnt<kWait + kStoreCnt>();
     barrier();
+    Frags f0, f1;
     read_frags(f0, io, 0);
 
-    int k = 0;
-    for (; k + kAhead < KT; k += 2) {
-        k_step<kFP8, true, true>(acc, f0, f1, a, io, k);
-        wait_vmcnt<2 * kLoads * (kAhead - 2)>();
-        barrier();
-        k_step<kFP8, true, true>(acc, f1, f0, a, io, k + 1);
-        wait_vmcnt<2 * kLoads * (kAhead - 2)>();
-        barrier();
-    }
-    // the last steps issue no loads: KT - 4 and KT - 3 (when KT >= 4) drain
-    // the loads in flight, KT - 2 and KT - 1 need no more barriers
-    static_assert(kAhead == 4, "the drain below is written for four steps in flight");
-    if (k + 2 < KT) {
-        k_step<kFP8, false, true>(acc, f0, f1, a, io, k);
-        wait_vmcnt<2 * kLoads>();
-        barrier();
-        k_step<kFP8, false, true>(acc, f1, f0, a, io, k + 1);
-        wait_vmcnt<0>();
-        barrier();
-        k += 2;
-    }
-    k_step<kFP8, false, true>(acc, f0, f1, a, io, k);
-    k_step<kFP8, false, false>(acc, f1, f0, a, io, k + 1);
-
-    // ---- epilogue
-    float s = 1.0f;
-    if (kFP8) s = (*a.x_scale) * (*a.w_scale);
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    const int64_t n_base = (int64_t)tn * kBN + wn * 128 + fr;
-    if (!kFused) {
-        const int o_base = tm * kBM + wm * 128 + fh * 4;
+    float amax = 0.0f;
+    int g = 0;
+    for (int c_t = b; c_t < T; c_t += G) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n_base + j * 32;
-            if (n >= a.N) continue;
-            uint16_t* orow = out + n * a.ld_out;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int o = o_base + i * 32 + g * 8;
-                    if (o < a.O) {
-                        uint2 v;
-                        v.x = pack_bf16x2(acc[i][j][4 * g + 0] * s, acc[i][j][4 * g + 1] * s);
-                        v.y = pack_bf16x2(acc[i][j][4 * g + 2] * s, acc[i][j][4 * g + 3] * s);
-                        *reinterpret_cast<uint2*>(orow + o) = v;
-                    }
-                }
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        // the first pair follows the previous tile's epilogue stores
+        {
+            const bool own = kAhead < KT;
+            const TileRsrc tr = select_rsrc(own, tr_cur, tr_nxt);
+            const int k0 = own ? kAhead : wrap_k(kAhead);
+            const int k1 = own ? kAhead + 1 : wrap_k(kAhead + 1);
+            k_step<kFP8>(acc, f0, f1, a, io, g, tr, k0);
+            wait_vmcnt<kWait + kStoreCnt>();
+            barrier();
+            k_step<kFP8>(acc, f1, f0, a, io, g + 1, tr, k1);
+            wait_vmcnt<kWait + kStoreCnt>();
+            barrier();
+            g += 2;
         }
-    } else {
-        // the ring is free once every wave is past its last MFMA reads
+        for (int kk = 2; kk < KT; kk += 2, g += 2) {
+            const bool own = kk + kAhead < KT;
+            const TileRsrc tr = select_rsrc(own, tr_cur, tr_nxt);
+            const int k0 = own ? kk + kAhead : wrap_k(kk + kAhead);
+            k_step<kFP8>(acc, f0, f1, a, io, g, tr, k0);
+            wait_vmcnt<kWait>();
+            barrier();
+            k_step<kFP8>(acc, f1, f0, a, io, g + 1, tr, k0 + 1);
+            wait_vmcnt<kWait>();
+            barrier();
+        }
+        tile_epilogue<kFP8, kFused>(acc, a, c_t, s, wm, wn, fr, fh, amax);
+        const int t2 = c_t + 2 * G;
+        tr_cur = tr_nxt;
+        tr_nxt = tile_rsrc<kFused>(a, t2 < T ? t2 : (c_t + G < T ? c_t + G : c_t), wave_u);
+    }
+    // the loads past the end still write the ring: let them land before the
+    // workgroup's LDS is reused or released
+    wait_vmcnt<0>();
+    if (kFused && a.absmax) {
         __syncthreads();
-        float* red = reinterpret_cast<float*>(lds);
-        float amax = 0.0f;
-        const int j_base = tm * 128 + wm * 64 + fh * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n_base + j * 32;
-            const bool ok = n < a.N;
-            uint16_t* orow = out + n * a.ld_out;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float hv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gg = round_bf16(acc[i][j][4 * g + e] * s);
-                        const float uu = round_bf16(acc[i + 2][j][4 * g + e] * s);
-                        hv[e] = silu_mul(gg, uu);
-                    }
-                    uint2 v;
-                    v.x = pack_bf16x2(hv[0], hv[1]);
-                    v.y = pack_bf16x2(hv[2], hv[3]);
-                    if (ok) {
-                        amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(bf16lo(v.x)), __builtin_fabsf(bf16hi(v.x))),
-                                                                     __builtin_fmaxf(__builtin_fabsf(bf16lo(v.y)), __builtin_fabsf(bf16hi(v.y)))));
-                        *reinterpret_cast<uint2*>(orow + j_base + i * 32 + g * 8) = v;
-                    }
-                }
-        }
-        if (a.absmax) block_absmax_commit(amax, red, a.absmax);
+        block_absmax_commit(amax, reinterpret_cast<float*>(lds), a.absmax);
     }
+}
+
+static int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 // Abs-max of a plain (unfused) GEMM output, when asked for: a separate pass.
@@ -366,7 +539,9 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     a.ld_out = fuse_swiglu ? O / 2 : O;
     a.tiles_m = fuse_swiglu ? (O / 2) / 128 : (O + kBM - 1) / kBM;
     a.tiles_n = (int)((N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+    const int T = a.tiles_m * a.tiles_n;
+    const int KT = a.K_bytes / kRowBytes;
+    const dim3 grid((unsigned)(KT >= kAhead ? min(T, cu_count()) : T)), block(kThreads);
     if (fp8) {
         if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, s, a);
