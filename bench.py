@@ -13,7 +13,7 @@ Other workloads (same line format, for the per-configuration figures):
   prefill8  FP8 block, same shape, 0.1% x50 outliers
   decode    single-token FP8 decode, C=4096, H=14336 (value in GB/s)
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload qwen7b8] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 25] [--workload qwen7b8] [--no-cpu-baseline]
 
 Prints one JSON line.  For block workloads value = whole-step algorithmic
 FLOP/s (the block's dense contractions: 6*N*C*H for the prefill, 6*M*C*H for
@@ -46,12 +46,16 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=25)
     p.add_argument("--workload", default="qwen7b8", choices=["qwen7b8", "prefill", "prefill8", "decode"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="prefill rows in the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
+    p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no benchmark: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                        "rocprofv3 run of this script (--copy-calibration) into the workload's entry of "
+                        "profiles/traffic.json")
     return p.parse_args()
 
 
@@ -70,6 +74,62 @@ def measured_traffic(key, src):
         return rec.get("bytes_per_launch")
     except (OSError, ValueError, KeyError):
         return None
+
+
+# dominant kernel per workload: traffic.json key, its source file, the kernel
+# name fragments whose per-dispatch counters make up one launch of the entry
+# point, and the algorithmic bytes of that launch
+def traffic_spec(workload):
+    from transformer_ffn_block_residual_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    N, C, H = w.N, w.C, w.H
+    if workload == "decode":
+        return ("decode_decode", "decode.hip", ["decode_kernel<true", "decode_kernel<false"],
+                f"decode_kernel<true,...> + decode_kernel<false,...> (one ffn_decode_gemv), M=1 C={C} H={H}",
+                3 * H * C + (2 * H + C) * 4 + 2 * (C + H) * 2)
+    elt = 1 if w.fp8 else 2
+    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{'true' if w.fp8 else 'false'}, true>"],
+            f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
+            N * C * elt + 2 * H * C * elt + N * H * 2)
+
+
+def ingest_pmc(a):
+    """HBM bytes per launch of the workload's dominant kernel from two
+    rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
+    scaled by what the counter reads for the 1 GiB calibration copy."""
+    import csv
+    key, src, frags, desc, algo = traffic_spec(a.workload)
+    rec = {"kernel": desc, "src": f"transformer_ffn_block_residual_amd/csrc/{src}", "src_sha256": src_digest(src)}
+    total = 0.0
+    for counter, path, truth_kb in (("FETCH_SIZE", a.ingest_pmc[0], 1 << 20), ("WRITE_SIZE", a.ingest_pmc[1], 1 << 20)):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit(f"{path}: no calibration copy (run bench.py with --copy-calibration)")
+        factor = truth_kb / max(copies)
+        per_launch = 0.0
+        for f in frags:
+            vals = [float(r["Counter_Value"]) for r in rows if f in r["Kernel_Name"]]
+            if not vals:
+                raise SystemExit(f"{path}: no dispatch of {f}")
+            per_launch += sum(vals) / len(vals)
+        tag = counter.split("_")[0].lower()
+        rec[f"{tag}_kb_raw"] = per_launch
+        rec[f"{tag}_factor"] = factor
+        total += per_launch * factor * 1024
+    rec["bytes_per_launch"] = total
+    rec["algorithmic_bytes"] = algo
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[key] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps({key: rec}))
+    return 0
 
 
 def blas_threads():
@@ -321,6 +381,8 @@ def bench_decode(a, torch, np, B, block, W):
 
 def main():
     a = parse()
+    if a.ingest_pmc:
+        return ingest_pmc(a)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this FFN block path has no "
               "multi-GPU mode.", file=sys.stderr)
