@@ -322,9 +322,17 @@ def test_decode(F, M, C, H):
         F.ffn_quant_rows(q, s, dev_bf16(d[k]), rows, cols)
         wq[k], ws[k] = q, s
     out, h = empty_bf16(M, C), empty_bf16(M, H)
-    F.ffn_decode_gemv(out, h, dev_bf16(d["x"]), wq["w_gate"], ws["w_gate"], wq["w_up"], ws["w_up"],
+    xd = dev_bf16(d["x"])
+    F.ffn_decode_gemv(out, h, xd, wq["w_gate"], ws["w_gate"], wq["w_up"], ws["w_up"],
                       wq["w_down"], ws["w_down"], M, C, H)
+    # the pre-bound form issues the identical call
+    out2, h2 = empty_bf16(M, C), empty_bf16(M, H)
+    call = F.bind_decode_gemv(out2, h2, xd, wq["w_gate"], ws["w_gate"], wq["w_up"], ws["w_up"],
+                              wq["w_down"], ws["w_down"], M, C, H)
+    call()
+    call()
     torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(h2, h)
     ref_q = {k: O.quant_rows(d[k]) for k in ("w_gate", "w_up", "w_down")}
     for k in ref_q:
         assert np.array_equal(host_u8(wq[k]), ref_q[k][0])

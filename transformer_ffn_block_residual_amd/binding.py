@@ -158,16 +158,33 @@ def ffn_down(out, h, h_scale, w, w_scale, dtype, N, H, C, stream=None):
         int(dtype), int(N), int(H), int(C), _stream(stream)))
 
 
+def _decode_gemv_args(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream):
+    return (_ptr(out, "out", M * C, BF16), _ptr(h, "h", M * H, BF16), _ptr(x, "x", M * C, BF16),
+            _ptr(w_gate, "w_gate", H * C, E4M3), _ptr(s_gate, "s_gate", H, F32),
+            _ptr(w_up, "w_up", H * C, E4M3), _ptr(s_up, "s_up", H, F32),
+            _ptr(w_down, "w_down", C * H, E4M3), _ptr(s_down, "s_down", C, F32),
+            int(M), int(C), int(H), _stream(stream))
+
+
 def ffn_decode_gemv(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
-    _check(_lib.ffn_decode_gemv(
-        _ptr(out, "out", M * C, BF16), _ptr(h, "h", M * H, BF16), _ptr(x, "x", M * C, BF16),
-        _ptr(w_gate, "w_gate", H * C, E4M3), _ptr(s_gate, "s_gate", H, F32),
-        _ptr(w_up, "w_up", H * C, E4M3), _ptr(s_up, "s_up", H, F32),
-        _ptr(w_down, "w_down", C * H, E4M3), _ptr(s_down, "s_down", C, F32),
-        int(M), int(C), int(H), _stream(stream)))
+    _check(_lib.ffn_decode_gemv(*_decode_gemv_args(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down,
+                                                   M, C, H, stream)))
+
+
+def bind_decode_gemv(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
+    """ffn_decode_gemv with its arguments checked and marshalled once: returns
+    a no-argument callable that issues the same call (same tensors, sizes and
+    stream) again.  For per-token loops where the checks would cost more host
+    time than the GPU spends on the call; the tensors must stay alive."""
+    args = _decode_gemv_args(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream)
+    fn = _lib.ffn_decode_gemv
+
+    def call():
+        _check(fn(*args))
+    return call
 
 
 __all__ = [
     "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_swiglu", "ffn_down",
-    "ffn_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
+    "ffn_decode_gemv", "bind_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
 ]

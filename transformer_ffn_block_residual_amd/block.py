@@ -121,3 +121,10 @@ class DecodeBlock:
         B.ffn_decode_gemv(self.out, self.h, x, self.wg, self.sg, self.wu, self.su, self.wd, self.sd,
                           M, self.C, self.H, stream)
         return self.out
+
+    def bind(self, x, M=None, stream=None):
+        """A no-argument callable that runs forward(x, M, stream) with the
+        argument checks done once (for per-token loops)."""
+        M = self.M if M is None else M
+        return B.bind_decode_gemv(self.out, self.h, x, self.wg, self.sg, self.wu, self.su, self.wd, self.sd,
+                                  M, self.C, self.H, stream)
