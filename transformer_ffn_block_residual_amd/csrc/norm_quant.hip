@@ -43,30 +43,35 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
     if (row < N) {
         const uint4* a4 = reinterpret_cast<const uint4*>(inp + row * C);
         const uint4* b4 = reinterpret_cast<const uint4*>(addend + row * C);
-        uint4 r[CPL];
+        // All loads are issued before any use: chunks past the row end load
+        // the row's last chunk again (in bounds, no branch that would make the
+        // compiler wait after every load) and are left out of the sum.
+        uint4 r[CPL], bv[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = min(lane + i * 64, nch - 1);
+            r[i] = a4[c];
+            if (kAdd) bv[i] = b4[c];
+        }
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = lane + i * 64;
-            if (c < nch) {
-                uint4 av = a4[c];
-                if (kAdd) {
-                    uint4 bv = b4[c];
-                    uint32_t* ap = reinterpret_cast<uint32_t*>(&av);
-                    const uint32_t* bp = reinterpret_cast<const uint32_t*>(&bv);
+            if (kAdd) {
+                uint32_t* ap = reinterpret_cast<uint32_t*>(&r[i]);
+                const uint32_t* bp = reinterpret_cast<const uint32_t*>(&bv[i]);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        ap[q] = pack_bf16x2(bf16lo(ap[q]) + bf16lo(bp[q]), bf16hi(ap[q]) + bf16hi(bp[q]));
-                }
-                r[i] = av;
-                const uint32_t* rp = reinterpret_cast<const uint32_t*>(&av);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float lo = bf16lo(rp[q]), hi = bf16hi(rp[q]);
-                    ss += lo * lo;
-                    ss += hi * hi;
-                }
+                for (int q = 0; q < 4; ++q)
+                    ap[q] = pack_bf16x2(bf16lo(ap[q]) + bf16lo(bp[q]), bf16hi(ap[q]) + bf16hi(bp[q]));
             }
+            const uint32_t* rp = reinterpret_cast<const uint32_t*>(&r[i]);
+            float part = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float lo = bf16lo(rp[q]), hi = bf16hi(rp[q]);
+                part += lo * lo;
+                part += hi * hi;
+            }
+            ss += lane + i * 64 < nch ? part : 0.0f;
         }
         ss = wave_sum(ss);
         const float rs = 1.0f / sqrtf(ss / (float)C + eps);
@@ -74,11 +79,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
         const uint4* w4 = reinterpret_cast<const uint4*>(w);
         uint4* y4 = reinterpret_cast<uint4*>(y + row * C);
         uint4* o4 = kAdd ? reinterpret_cast<uint4*>(res_out + row * C) : nullptr;
+        uint4 wr[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) wr[i] = w4[min(lane + i * 64, nch - 1)];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * 64;
             if (c < nch) {
-                const uint4 wv = w4[c];
+                const uint4 wv = wr[i];
                 const uint32_t* rp = reinterpret_cast<const uint32_t*>(&r[i]);
                 const uint32_t* wp = reinterpret_cast<const uint32_t*>(&wv);
                 uint4 yv;
