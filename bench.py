@@ -50,7 +50,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=25)
     p.add_argument("--workload", default="qwen7b8", choices=["qwen7b8", "prefill", "prefill8", "decode"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=256, help="prefill rows in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="prefill rows in the CPU oracle sample (default: min(N, 4096), about 10 s)")
+    p.add_argument("--cpu-decodes", type=int, default=30,
+                   help="decode calls in the CPU oracle sample of the decode workload (about 10 s)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -175,18 +178,46 @@ def cpu_block_sample(w, d, rows, dec_x=None):
             "sample": f"{what}; weights quantised beforehand; {dt:.2f} s wall"}
 
 
-def cpu_decode_sample(d_q, x):
+def cpu_decode_sample(d_q, x, calls):
     """The oracle decode of one token over the full weights (already
-    quantised), in GB/s of algorithmic bytes."""
+    quantised), `calls` times, in GB/s of algorithmic bytes."""
     import oracle as O
     qg, sg, qu, su, qd, sd = d_q
     H, C = qg.shape
     t0 = time.perf_counter()
-    O.decode_gemv(x, qg, sg, qu, su, qd, sd)
+    for _ in range(calls):
+        O.decode_gemv(x, qg, sg, qu, su, qd, sd)
     dt = time.perf_counter() - t0
-    nbytes = 3.0 * H * C + (2 * H + C) * 4 + 2.0 * (C + H) * 2
+    nbytes = calls * (3.0 * H * C + (2 * H + C) * 4 + 2.0 * (C + H) * 2)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"one full single-token decode (C={C}, H={H}); {dt:.2f} s wall"}
+            "sample": f"{calls} full single-token decodes (C={C}, H={H}); {dt:.2f} s wall"}
+
+
+def decode_graph_ms(torch, decs, x, M, steps):
+    """Average duration of one decode call when `steps` calls (rotating the
+    weight copies) are captured in one HIP graph and replayed: the decode
+    without host launch gaps.  The calls launch kernels only (no memset), so
+    the graph replays them exactly."""
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        cur = torch.cuda.current_stream()
+        calls = [db.bind(x, M, cur) for db in decs]
+        for i in range(steps):
+            calls[i % len(calls)]()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (reps * steps)
 
 
 class Timer:
@@ -210,6 +241,14 @@ class Timer:
     def mean_ms(self):
         import numpy as np
         return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in self.ev.items()}
+
+    def median_min_ms(self):
+        import numpy as np
+        out = {}
+        for k, v in self.ev.items():
+            t = [a.elapsed_time(b) for a, b in v]
+            out[k] = {"median": float(np.median(t)), "min": float(np.min(t))}
+        return out
 
 
 def run_steps(torch, stream, step, a, marks_per_step=8):
@@ -235,6 +274,7 @@ def run_steps(torch, stream, step, a, marks_per_step=8):
     for i in range(a.steps):
         step(a.steps + i, timer)
     torch.cuda.synchronize()
+    run_steps.spread = timer.median_min_ms()
     return ms, timer.mean_ms()
 
 
@@ -289,6 +329,7 @@ def bench_block(a, torch, np, B, block, W):
             decs[i % DECODE_COPIES].forward(x_dec, M, stream)
         m6 = tm.mark() if (tm and M) else None
         if tm:
+            tm.add("step", m0, m6 if M else m5)
             tm.add("rmsnorm", m0, m1)
             if w.fp8:
                 tm.add("quant_y", m1, m2)
@@ -299,6 +340,7 @@ def bench_block(a, torch, np, B, block, W):
                 tm.add("decode", m5, m6)
 
     ms, km = run_steps(torch, stream, step, a)
+    spread = run_steps.spread
     peak = PEAK[dt]
     gu_tflops = 4.0 * N * C * H / (km["gateup"] * 1e-3) / 1e12
     kernels = {
@@ -333,10 +375,11 @@ def bench_block(a, torch, np, B, block, W):
                      "achieved": gu_tflops, "peak": peak, "unit": "TFLOP/s", "frac": gu_tflops / peak,
                      "traffic": measured_traffic(f"gateup_{a.workload}", "gemm.hip")},
         "kernels": kernels,
+        "spread_ms": spread,
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_block_sample(w, d, a.cpu_rows, dec_x)
+        out["cpu_baseline"] = cpu_block_sample(w, d, a.cpu_rows or min(N, 4096), dec_x)
     return out
 
 
@@ -370,8 +413,10 @@ def bench_decode(a, torch, np, B, block, W):
             tm.add("decode", m0, tm.mark())
 
     ms, km = run_steps(torch, stream, step, a)
+    spread = run_steps.spread
     nbytes = 3.0 * H * C + (2 * H + C) * 4 + 2.0 * M * (C + H) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
+    graph_ms = decode_graph_ms(torch, decs, x, M, a.steps)
     # a step is exactly one ffn_decode_gemv call (both of its kernels), so the
     # call's average duration is the timed region's; the event-bracketed pass
     # reads longer by the events' own cost and is reported beside it
@@ -388,7 +433,8 @@ def bench_decode(a, torch, np, B, block, W):
                      "frac": nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": measured_traffic("decode_decode", "decode.hip")},
         "kernels": {"decode": {"ms": call_ms, "GB/s": nbytes / call_ms / 1e6,
-                               "ms_between_events": km["decode"]}},
+                               "ms_between_events": km["decode"], "median_min_between_events": spread["decode"],
+                               "ms_in_hip_graph": graph_ms, "GB/s_in_hip_graph": nbytes / graph_ms / 1e6}},
     }
     if not a.no_cpu_baseline:
         import oracle as O
@@ -396,7 +442,7 @@ def bench_decode(a, torch, np, B, block, W):
         qg, sg = O.quant_rows(d["w_gate"])
         qu, su = O.quant_rows(d["w_up"])
         qd, sd = O.quant_rows(d["w_down"])
-        out["cpu_baseline"] = cpu_decode_sample((qg, sg, qu, su, qd, sd), d["x"])
+        out["cpu_baseline"] = cpu_decode_sample((qg, sg, qu, su, qd, sd), d["x"], a.cpu_decodes)
     return out
 
 
