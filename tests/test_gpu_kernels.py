@@ -310,7 +310,7 @@ def test_gemm_integer_down_bit_exact_and_deterministic(F):
 
 # ----------------------------------------------------------------------------- decode
 
-@pytest.mark.parametrize("M,C,H", [(1, 256, 768), (1, 4096, 1024), (1, 3584, 384), (3, 512, 640), (4, 1024, 9216), (16, 384, 896),
+@pytest.mark.parametrize("M,C,H", [(1, 256, 768), (1, 4096, 1024), (1, 3584, 384), (2, 1152, 640), (3, 512, 640), (4, 1024, 9216), (4, 640, 2304), (16, 384, 896),
                                    (32, 256, 256)])
 def test_decode(F, M, C, H):
     say(f"decode M={M} C={C} H={H}")

@@ -7,8 +7,9 @@
 //   h[m,n] = bf16(silu(g) * u)
 //   y[m,c] = bf16(sd[c] * sum_n Wd[c,n] h[m,n])
 //
-// Both passes stream their weights from HBM once and are bound by it.  A
-// workgroup of 8 waves owns 16 weight rows (of each matrix in the dual pass);
+// Both passes stream their weights from HBM once and are bound by it.  For
+// one to four tokens the lanes split K instead (gemv_small_kernel below).  For
+// more, a workgroup of 8 waves owns 16 weight rows (of each matrix in the dual pass);
 // its waves split K into 256-byte chunks, dealt round-robin.  Per chunk a lane
 // loads four 16-byte pieces of one row, the 4 lanes of a row covering 64
 // contiguous bytes per load instruction; the codes are widened to bf16 with
@@ -186,6 +187,155 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
     }
 }
 
+// Few-token form (M <= 4) of both passes, on the vector ALU.  With one to
+// four tokens the MFMA above multiplies mostly zero columns and spends as many
+// load instructions on activations as on weights.  Here the 64 lanes of a wave
+// split K instead: one load instruction reads 1 KiB of one weight row (lane l:
+// bytes [1024 w + 16 l, +16)), full cache lines in order, and the matching 16
+// activations of each token, loaded once per 1 KiB window, serve all R rows
+// (NMAT * R row streams) of the wave.  Each lane keeps fp32 partial sums per
+// (row, token); one cross-lane sum per (row, token) at the end.
+//   kDual: g, u rows of w0, w1 -> h = bf16(silu(bf16(s0 g)) * bf16(s1 u)), out [M, rows]
+//   else : rows of w0 -> out = bf16(s0 * y), out [M, rows]
+// U windows of loads are issued before any is used.
+template <bool kDual, int MT, int R, int U, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w0,
+    const float* __restrict__ s0, const uint8_t* __restrict__ w1, const float* __restrict__ s1, int M, int K,
+    int rows) {
+    constexpr int NMAT = kDual ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int row0 = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;  // rows % R == 0
+    if (row0 >= rows) return;
+    const uint8_t* wr[R][NMAT];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        wr[r][0] = w0 + (int64_t)(row0 + r) * K;
+        if (kDual) wr[r][NMAT - 1] = w1 + (int64_t)(row0 + r) * K;
+    }
+    float acc[R][NMAT][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[r][m][t] = 0.0f;
+
+    const int nwin = (K + 1023) / 1024;
+    for (int w = 0; w < nwin; w += U) {
+        uint4 wv[U][R][NMAT], xv[U][MT][2];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // past the row end (a partial last window, or a window past the
+            // last): load the row's last 16 bytes, and zero the activations
+            const int k = (w + u) * 1024 + lane * 16;
+            ok[u] = k < K;
+            const int kc = ok[u] ? k : K - 16;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) wv[u][r][m] = *reinterpret_cast<const uint4*>(wr[r][m] + kc);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const uint16_t* xt = x + (int64_t)min(t, M - 1) * K + kc;
+                xv[u][t][0] = *reinterpret_cast<const uint4*>(xt);
+                xv[u][t][1] = *reinterpret_cast<const uint4*>(xt + 8);
+            }
+        }
+        // every load of the U windows is in flight before the first use (the
+        // compiler would otherwise trade them for registers one at a time)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float xf[MT][16];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const bool use = ok[u] && t < M;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t* q = reinterpret_cast<const uint32_t*>(&xv[u][t][h]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xf[t][8 * h + 2 * e] = use ? bf16lo(q[e]) : 0.0f;
+                        xf[t][8 * h + 2 * e + 1] = use ? bf16hi(q[e]) : 0.0f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    const uint32_t* q = reinterpret_cast<const uint32_t*>(&wv[u][r][m]);
+                    float wf[16];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const f32x2_t lo = e4m3x2_to_f32(q[e], false), hi = e4m3x2_to_f32(q[e], true);
+                        wf[4 * e] = lo[0];
+                        wf[4 * e + 1] = lo[1];
+                        wf[4 * e + 2] = hi[0];
+                        wf[4 * e + 3] = hi[1];
+                    }
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        float a = acc[r][m][t];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) a = __builtin_fmaf(wf[j], xf[t][j], a);
+                        acc[r][m][t] = a;
+                    }
+                }
+        }
+    }
+    // lane 0 finishes the rows
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[r][m][t] = wave_sum(acc[r][m][t]);
+    if (lane != 0) return;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t >= M) continue;
+            float o;
+            if (kDual) {
+                const float g = round_bf16(s0[row] * acc[r][0][t]);
+                const float u = round_bf16(s1[row] * acc[r][NMAT - 1][t]);
+                o = silu_mul(g, u);
+            } else {
+                o = s0[row] * acc[r][0][t];
+            }
+            out[(int64_t)t * rows + row] = (uint16_t)(pack_bf16x2(o, 0.0f) & 0xffffu);
+        }
+    }
+}
+
+// Rows per wave, windows in flight per wave and waves per workgroup of the
+// few-token passes (measured at M = 1 over R in 1..8, U in 1..8 and 2..8 waves:
+// more loads in flight per wave than this run slower, the HBM serving many
+// concurrent row streams less well than fewer longer ones).
+constexpr int kSmallDualR = 1, kSmallDualU = 4, kSmallDownR = 2, kSmallDownU = 2, kSmallWaves = 4;
+
+template <int MT>
+static hipError_t launch_decode_small(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg,
+                                      const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
+                                      const float* sd, int M, int C, int H, hipStream_t s) {
+    // H and C are multiples of 128: whole waves of rows
+    const int dual_waves = H / kSmallDualR, down_waves = C / kSmallDownR;
+    hipLaunchKernelGGL((gemv_small_kernel<true, MT, kSmallDualR, kSmallDualU, kSmallWaves>),
+                       dim3((dual_waves + kSmallWaves - 1) / kSmallWaves), dim3(64 * kSmallWaves), 0, s, h, x, wg,
+                       sg, wu, su, M, C, H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_small_kernel<false, MT, kSmallDownR, kSmallDownU, kSmallWaves>),
+                       dim3((down_waves + kSmallWaves - 1) / kSmallWaves), dim3(64 * kSmallWaves), 0, s, out, h, wd,
+                       sd, nullptr, nullptr, M, H, C);
+    return hipGetLastError();
+}
+
 template <int TB, int RB_DUAL>
 static hipError_t launch_decode_tb(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg,
                                    const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
@@ -204,7 +354,9 @@ hipError_t launch_decode(uint16_t* out, uint16_t* h, const uint16_t* x, const ui
                          const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd, int M, int C,
                          int H, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    if (M <= 4) return launch_decode_tb<1, 1>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    if (M == 1) return launch_decode_small<1>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    if (M == 2) return launch_decode_small<2>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    if (M <= 4) return launch_decode_small<4>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
     if (M <= 16) return launch_decode_tb<1, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
     return launch_decode_tb<2, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
 }
