@@ -115,6 +115,28 @@ ffn_status_t ffn_gateup(void* out, float* out_absmax, const void* x, const float
                         const void* w, const float* w_scale, ffn_dtype_t dtype, int fuse_swiglu,
                         int64_t N, int64_t C, int64_t H, hipStream_t stream);
 
+/* Fused gate+up projection with the SwiGLU epilogue storing e4m3 codes of h
+ * quantised with an abs-max known beforehand (one pass instead of bf16 h, then
+ * ffn_quant_absmax).  [llmq model] LLamaModel::_recompute_block:
+ * swiglu_forward_quant(SwiGLu.Quant, its scale, MlpUp, its abs-max), which
+ * re-creates the quantised SwiGLU output under the abs-max the forward pass
+ * recorded; forward_qmm with reuse_inp_quant then feeds it to the down GEMM.
+ *
+ *   h = bf16(silu(g) * u) exactly as ffn_gateup with fuse_swiglu;
+ *   *q_scale = A/448 (1 if A == 0),  q = e4m3(h * 448/A),  A = *h_absmax_known;
+ *   h_absmax (nullable) = max|h| of this call's h (e.g. the next call's A).
+ * q is bit-identical to ffn_gateup(fuse_swiglu) followed by
+ * ffn_quant_absmax(compute_absmax = 0) with absmax = A; values beyond A
+ * saturate to +-448.
+ * q: e4m3 [N,H]; q_scale, h_absmax, h_absmax_known: fp32 [1]; x, w, scales as
+ * ffn_gateup.  h_absmax_known is required and must differ from h_absmax and
+ * q_scale (both are written while it is read).  Supported: C % 128 == 0,
+ * H % 128 == 0, N >= 0. */
+ffn_status_t ffn_gateup_swiglu_quant(uint8_t* q, float* q_scale, float* h_absmax,
+                                     const float* h_absmax_known, const void* x, const float* x_scale,
+                                     const void* w, const float* w_scale, ffn_dtype_t dtype,
+                                     int64_t N, int64_t C, int64_t H, hipStream_t stream);
+
 /* SwiGLU on an unfused gate+up output, with the output's abs-max.
  * [llmq model] LLamaModel::_forward_block, swiglu_forward(SwiGLu, MlpUp,
  * SwiGLu abs-max, B, T, D).  h = bf16(silu(g) * u), g = gu[:, :H], u = gu[:, H:].

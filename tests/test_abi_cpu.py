@@ -36,8 +36,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_swiglu", "ffn_down",
-              "ffn_decode_gemv", "ffn_last_error", "ffn_version"]:
+    for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
+              "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_last_error", "ffn_version"]:
         assert n in names
 
 
@@ -85,6 +85,17 @@ def test_gemm_validation(lib):
     assert f(A, None, A, None, A, None, 0, 1, -64, 256, 768, None) == INVALID
     assert f(A, None, MIS, None, A, None, 0, 1, 64, 256, 768, None) == UNSUPPORTED
     assert f(A, None, A, None, A, None, 0, 1, 1 << 20, 4096, 768, None) == UNSUPPORTED  # > 4 GiB operand
+    g = lib.ffn_gateup_swiglu_quant   # q, q_scale, h_absmax, h_absmax_known, x, xs, w, ws, dtype, N, C, H
+    B, C_, D = 0x20000, 0x30000, 0x40000
+    assert g(A, B, C_, None, A, None, A, None, 0, 64, 256, 768, None) == INVALID      # no known abs-max
+    assert "h_absmax_known is NULL" in _err(lib)
+    assert g(A, B, C_, C_, A, None, A, None, 0, 64, 256, 768, None) == INVALID        # known aliases h_absmax
+    assert g(A, B, C_, B, A, None, A, None, 0, 64, 256, 768, None) == INVALID         # known aliases q_scale
+    assert "alias" in _err(lib)
+    assert g(A, B, C_, D, A, None, A, None, 1, 64, 256, 768, None) == INVALID         # fp8 without scales
+    assert g(A, B, C_, D, A, None, A, None, 0, 64, 256, 100, None) == UNSUPPORTED     # H % 128
+    assert g(MIS, B, C_, D, A, None, A, None, 0, 64, 256, 768, None) == UNSUPPORTED   # misaligned q
+    assert g(A, None, C_, D, A, None, A, None, 0, 64, 256, 768, None) == INVALID      # no q_scale
     d = lib.ffn_down
     assert d(A, A, None, A, None, 1, 64, 768, 256, None) == INVALID
     assert d(A, A, None, A, None, 0, 64, 700, 256, None) == UNSUPPORTED

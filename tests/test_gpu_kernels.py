@@ -232,6 +232,40 @@ def test_gateup_random_and_fused_equals_unfused(F, fp8, N, C, H):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("N,C,H", [(64, 256, 768), (300, 512, 384), (1100, 256, 7680)])
+def test_gateup_swiglu_quant_known_absmax(F, fp8, N, C, H):
+    # the one-pass form equals the two-pass chain (fused gate+up -> bf16 h ->
+    # ffn_quant_absmax with the abs-max given) bit for bit, and the oracle's
+    # quantiser on the same h, for the exact abs-max, a stale smaller one
+    # (saturating codes) and zero
+    say(f"gateup swiglu quant fp8={fp8} N={N} C={C} H={H}")
+    d = W.block_inputs(N, C, H, seed=N + C + H + 7, w_std=0.0)
+    if fp8:
+        qx, sx, _ = O.quant_absmax(d["inp"])
+        qw, sw, _ = O.quant_absmax(d["w_gu"])
+        xa, wa, xs, ws, dt = dev_u8(qx), dev_u8(qw), dev_f32([sx]), dev_f32([sw]), F.FFN_E4M3
+    else:
+        xa, wa, xs, ws, dt = dev_bf16(d["inp"]), dev_bf16(d["w_gu"]), None, None, F.FFN_BF16
+    h, am = empty_bf16(N, H), empty_f32(1)
+    F.ffn_gateup(h, am, xa, xs, wa, ws, dt, 1, N, C, H)
+    torch.cuda.synchronize()
+    amax = float(host_f32(am)[0])
+    hb = host_bits(h)
+    for known in (amax, amax * 0.5, 0.0):
+        q2, s2 = empty_u8(N, H), empty_f32(1)
+        F.ffn_quant_absmax(q2, s2, dev_f32([known]), h, N * H, 0)
+        q, qs, ham = empty_u8(N, H), empty_f32(1), empty_f32(1)
+        F.ffn_gateup_swiglu_quant(q, qs, ham, dev_f32([known]), xa, xs, wa, ws, dt, N, C, H)
+        torch.cuda.synchronize()
+        assert torch.equal(q, q2)
+        assert host_f32(qs)[0] == host_f32(s2)[0]
+        assert host_f32(ham)[0] == np.float32(amax)
+        qo, so, _ = O.quant_absmax(hb, np.float32(known))
+        assert np.array_equal(host_u8(q), qo)
+        assert host_f32(qs)[0] == so
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("N,H,C", [(64, 768, 256), (300, 384, 512), (513, 256, 384), (3100, 384, 5248)])
 def test_down(F, fp8, N, H, C):
     say(f"down fp8={fp8} N={N} H={H} C={C}")

@@ -4,7 +4,8 @@ SwiGLU, down projection) and its FP8 single-token decode, as hand-written HIP
 kernels for MI355X (gfx950) behind the C ABI of ``include/ffn.h``.
 
 The binding functions (``ffn_rmsnorm_fwd``, ``ffn_quant_absmax``,
-``ffn_quant_rows``, ``ffn_gateup``, ``ffn_swiglu``, ``ffn_down``,
+``ffn_quant_rows``, ``ffn_gateup``, ``ffn_gateup_swiglu_quant``, ``ffn_swiglu``,
+``ffn_down``,
 ``ffn_decode_gemv``, and ``bind_decode_gemv``, its checked-once form) live in
 ``binding``; accessing any of them here loads
 ``libffn.so`` and raises if it has not been built.  ``workloads`` (seeded
@@ -12,7 +13,8 @@ synthetic inputs) and ``build`` import without the library.
 """
 
 _BINDING_NAMES = {
-    "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_swiglu", "ffn_down",
+    "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
+    "ffn_swiglu", "ffn_down",
     "ffn_decode_gemv", "bind_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_OK", "FFN_ERR_INVALID",
     "FFN_ERR_UNSUPPORTED", "FFN_ERR_HIP", "version", "last_error", "LIB_PATH",
 }

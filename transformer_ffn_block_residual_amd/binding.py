@@ -41,6 +41,7 @@ def _load():
         "ffn_quant_absmax": [P, P, P, P, I64, I32, P],
         "ffn_quant_rows": [P, P, P, I64, I64, P],
         "ffn_gateup": [P, P, P, P, P, P, I32, I32, I64, I64, I64, P],
+        "ffn_gateup_swiglu_quant": [P, P, P, P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_swiglu": [P, P, P, I64, I64, P],
         "ffn_down": [P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_decode_gemv": [P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
@@ -143,6 +144,17 @@ def ffn_gateup(out, out_absmax, x, x_scale, w, w_scale, dtype, fuse_swiglu, N, C
         int(dtype), int(bool(fuse_swiglu)), int(N), int(C), int(H), _stream(stream)))
 
 
+def ffn_gateup_swiglu_quant(q, q_scale, h_absmax, h_absmax_known, x, x_scale, w, w_scale, dtype, N, C, H,
+                            stream=None):
+    fp8 = dtype == FFN_E4M3
+    _check(_lib.ffn_gateup_swiglu_quant(
+        _ptr(q, "q", N * H, E4M3), _ptr(q_scale, "q_scale", 1, F32),
+        _ptr(h_absmax, "h_absmax", 1, F32, optional=True), _ptr(h_absmax_known, "h_absmax_known", 1, F32),
+        _ptr(x, "x", N * C, _dt_elems(dtype)), _ptr(x_scale, "x_scale", 1, F32, optional=not fp8),
+        _ptr(w, "w", 2 * H * C, _dt_elems(dtype)), _ptr(w_scale, "w_scale", 1, F32, optional=not fp8),
+        int(dtype), int(N), int(C), int(H), _stream(stream)))
+
+
 def ffn_swiglu(h, absmax, gateup, N, H, stream=None):
     _check(_lib.ffn_swiglu(
         _ptr(h, "h", N * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=True),
@@ -185,6 +197,6 @@ def bind_decode_gemv(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C
 
 
 __all__ = [
-    "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_swiglu", "ffn_down",
-    "ffn_decode_gemv", "bind_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
+    "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
+    "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "bind_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
 ]

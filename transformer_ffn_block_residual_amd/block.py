@@ -9,6 +9,10 @@
   ffn_quant_absmax  h -> e4m3 with max|h|                       (FP8 only)
   ffn_down          [N,H] x [C,H]^T
 
+``forward_known_h_absmax`` is the FP8 form whose gate+up epilogue quantises h
+under an abs-max known beforehand (``ffn_gateup_swiglu_quant``), as the
+trainer's recompute pass re-creates its quantised SwiGLU output.
+
 The residual that closes the block (r + down) is the next block's first
 ``ffn_rmsnorm_fwd`` (``LLamaModel::forward`` fuses it there), so a chain of
 blocks feeds ``(r, down)`` of one block into ``(inp, addend)`` of the next.
@@ -91,6 +95,23 @@ class PrefillBlock:
         else:
             B.ffn_gateup(self.h, self.am_h, self.y, None, self.w_gu, None, B.FFN_BF16, 1, N, C, H, stream)
             B.ffn_down(self.out, self.h, None, self.w_d, None, B.FFN_BF16, N, H, C, stream)
+        return self.out
+
+    def forward_known_h_absmax(self, inp, addend, h_absmax_known, h_absmax_out, stream=None):
+        """FP8 block forward whose h is quantised in the gate+up epilogue with
+        an abs-max known beforehand (the recompute form: llmq llama_model.cpp,
+        ``LLamaModel::_recompute_block``, ``swiglu_forward_quant``): no bf16 h
+        and no separate quantisation pass.  ``h_absmax_out`` receives this
+        call's abs-max of h (the next call's known value; it must be another
+        buffer than ``h_absmax_known``)."""
+        assert self.fp8, "the known-abs-max form is an FP8 path"
+        N, C, H = self.N, self.C, self.H
+        B.ffn_rmsnorm_fwd(self.y, self.rstd, self.r if addend is not None else None, self.am_y,
+                          inp, addend, self.w_norm, self.eps, N, C, stream)
+        B.ffn_quant_absmax(self.qy, self.s_y, self.am_y, self.y, N * C, 0, stream)
+        B.ffn_gateup_swiglu_quant(self.qh, self.s_h, h_absmax_out, h_absmax_known, self.qy, self.s_y, self.w_gu,
+                                  self.s_gu, B.FFN_E4M3, N, C, H, stream)
+        B.ffn_down(self.out, self.qh, self.s_h, self.w_d, self.s_d, B.FFN_E4M3, N, H, C, stream)
         return self.out
 
 

@@ -150,6 +150,37 @@ ffn_status_t ffn_gateup(void* out, float* out_absmax, const void* x, const float
                       "ffn_gateup");
 }
 
+ffn_status_t ffn_gateup_swiglu_quant(uint8_t* q, float* q_scale, float* h_absmax, const float* h_absmax_known,
+                                     const void* x, const float* x_scale, const void* w, const float* w_scale,
+                                     ffn_dtype_t dtype, int64_t N, int64_t C, int64_t H, hipStream_t stream) {
+    REQUIRE(q);
+    REQUIRE(q_scale);
+    REQUIRE(h_absmax_known);
+    REQUIRE(x);
+    REQUIRE(w);
+    NONNEG(N);
+    NONNEG(C);
+    NONNEG(H);
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3)
+        return fail(FFN_ERR_INVALID, "ffn_gateup_swiglu_quant: unknown dtype %d", (int)dtype);
+    if (dtype == FFN_E4M3) {
+        REQUIRE(x_scale);
+        REQUIRE(w_scale);
+    }
+    if (h_absmax_known == h_absmax || h_absmax_known == q_scale)
+        return fail(FFN_ERR_INVALID, "ffn_gateup_swiglu_quant: h_absmax_known must not alias h_absmax or q_scale");
+    const int elt = dtype == FFN_E4M3 ? 1 : 2;
+    if (ffn_status_t st = check_gemm_dims("ffn_gateup_swiglu_quant", N, C, 2 * H, elt)) return st;
+    if (H % 128 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup_swiglu_quant: H = %lld must be a multiple of 128", (long long)H);
+    ALIGNED(q);
+    ALIGNED(x);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(q, h_absmax, x, x_scale, w, w_scale, dtype == FFN_E4M3, true, N, (int)C,
+                                       (int)(2 * H), stream, h_absmax_known, q_scale),
+                      "ffn_gateup_swiglu_quant");
+}
+
 ffn_status_t ffn_swiglu(void* h, float* absmax, const void* gateup, int64_t N, int64_t H, hipStream_t stream) {
     REQUIRE(h);
     REQUIRE(gateup);

@@ -50,6 +50,19 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)w;
 }
 
+// Per-tensor e4m3 scale pair from an abs-max: the dequantisation factor
+// absmax/448 and its quantisation inverse 448/absmax, both IEEE fp32 quotients;
+// 1 and 1 for an all-zero tensor.
+__device__ __forceinline__ void scale_pair(float am, float& scale, float& inv) {
+    if (am > 0.0f) {
+        scale = am / kE4M3Max;
+        inv = kE4M3Max / am;
+    } else {
+        scale = 1.0f;
+        inv = 1.0f;
+    }
+}
+
 // Bytes 0,1 (hi=false) or 2,3 (hi=true) of a dword of e4m3 codes -> fp32, exact.
 __device__ __forceinline__ f32x2_t e4m3x2_to_f32(uint32_t w, bool hi) {
     return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);

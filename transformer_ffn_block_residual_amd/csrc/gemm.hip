@@ -76,6 +76,8 @@ struct GemmArgs {
     int ld_out;    // output row stride in elements
     int tiles_m;   // weight-row tiles
     int tiles_n;   // token-row tiles
+    const float* q_absmax;  // SwiGLU + quantise: the known abs-max of h
+    float* q_scale;         // ... and where its dequantisation scale goes
 };
 
 // A buffer resource (V#) for raw byte addressing: base address, no stride,
@@ -232,7 +234,8 @@ __device__ __forceinline__ TileRsrc select_rsrc(bool c, const TileRsrc& x, const
     return r;
 }
 
-// Store instructions per lane in one tile's epilogue (16-byte stores).
+// Store instructions per lane in one tile's epilogue (16-byte stores; 8-byte
+// stores of e4m3 codes when quantising).
 template <bool kFused>
 constexpr int epilogue_stores() { return kFused ? 16 : 32; }
 
@@ -278,20 +281,24 @@ __device__ __forceinline__ u32x4_t regroup_runs(uint32_t x0, uint32_t x1, uint32
 // One tile's output.  Every lane issues exactly epilogue_stores() buffer
 // stores; rows past N and features past O are dropped by the buffer's range
 // check (their offsets point past num_records), so the count of outstanding
-// memory operations stays exact for the pipeline's counted waits.
-template <bool kFP8, bool kFused>
-__device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmArgs& a, int t, float s, int wm,
-                                              int wn, int fr, int fh, float& amax) {
+// memory operations stays exact for the pipeline's counted waits.  kQuant
+// (SwiGLU only): h is rounded to bf16 as always, its abs-max kept, and the
+// stored output is e4m3(h * qinv), the codes ffn_quant_absmax would give h
+// with that abs-max.
+template <bool kFP8, bool kFused, bool kQuant>
+__device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmArgs& a, int t, float s, float qinv,
+                                              int wm, int wn, int fr, int fh, float& amax) {
     int tm, tn;
     tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
     // recomputed per tile: kept out of registers across the K loop
     asm volatile("" : "+v"(fr), "+v"(fh));
     const int64_t n0 = (int64_t)tn * kBN;
-    uint8_t* base = reinterpret_cast<uint8_t*>(a.out) + n0 * a.ld_out * 2;
-    const int64_t rem = (a.N - n0) * (int64_t)a.ld_out * 2;
+    constexpr int kOutElt = kQuant ? 1 : 2;  // bytes per output element
+    uint8_t* base = reinterpret_cast<uint8_t*>(a.out) + n0 * a.ld_out * kOutElt;
+    const int64_t rem = (a.N - n0) * (int64_t)a.ld_out * kOutElt;
     const uint32_t nrec = (uint32_t)(rem < ((int64_t)1 << 30) ? rem : ((int64_t)1 << 30));
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)nrec, 0x00020000);
-    const uint32_t row_bytes = (uint32_t)a.ld_out * 2;
+    const uint32_t row_bytes = (uint32_t)a.ld_out * kOutElt;
     const int r_base = wn * 128 + fr;  // token row within the tile, block j adds 32 j
     if (!kFused) {
 #pragma unroll
@@ -347,8 +354,16 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
                     amax = __builtin_fmaxf(amax, ok ? m : 0.0f);
                     const u32x4_t v = regroup_runs(d[0], d[1], d[2], d[3]);
                     const int o = tm * 128 + wm * 64 + i * 32 + 16 * q + 8 * fh;
-                    const uint32_t off = (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * 2;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 0);
+                    const uint32_t off = (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * kOutElt;
+                    if (kQuant) {
+                        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                        const u32x2_t c = {
+                            pack_e4m3x4(bf16lo(v[0]) * qinv, bf16hi(v[0]) * qinv, bf16lo(v[1]) * qinv, bf16hi(v[1]) * qinv),
+                            pack_e4m3x4(bf16lo(v[2]) * qinv, bf16hi(v[2]) * qinv, bf16lo(v[3]) * qinv, bf16hi(v[3]) * qinv)};
+                        __builtin_amdgcn_raw_buffer_store_b64(c, rsrc, off, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 0);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -356,9 +371,10 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     }
 }
 
-template <bool kFP8, bool kFused>
+template <bool kFP8, bool kFused, bool kQuant>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a) {
+    static_assert(kFused || !kQuant, "quantised output is a SwiGLU epilogue");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
     constexpr int kStoreCnt = epilogue_stores<kFused>();
@@ -375,6 +391,12 @@ void gemm_kernel(GemmArgs a) {
 
     float s = 1.0f;
     if (kFP8) s = (*a.x_scale) * (*a.w_scale);
+    float qinv = 1.0f;
+    if (kQuant) {
+        float qscale;
+        scale_pair(*a.q_absmax, qscale, qinv);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *a.q_scale = qscale;
+    }
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -490,7 +512,7 @@ void gemm_kernel(GemmArgs a) {
             wait_vmcnt<kWait>();
             barrier();
         }
-        tile_epilogue<kFP8, kFused>(acc, a, c_t, s, wm, wn, fr, fh, amax);
+        tile_epilogue<kFP8, kFused, kQuant>(acc, a, c_t, s, qinv, wm, wn, fr, fh, amax);
         const int t2 = c_t + 2 * G;
         tr_cur = tr_nxt;
         tr_nxt = tile_rsrc<kFused>(a, t2 < T ? t2 : (c_t + G < T ? c_t + G : c_t), wave_u);
@@ -517,9 +539,11 @@ static int cu_count() {
 }
 
 // Abs-max of a plain (unfused) GEMM output, when asked for: a separate pass.
+// q_absmax / q_scale (SwiGLU only, both or neither): store e4m3 codes of h
+// under that known abs-max instead of bf16 h, and its scale.
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
-                       hipStream_t s) {
+                       hipStream_t s, const float* q_absmax, float* q_scale) {
     if (absmax && (fuse_swiglu || N == 0)) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
@@ -539,15 +563,20 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     a.ld_out = fuse_swiglu ? O / 2 : O;
     a.tiles_m = fuse_swiglu ? (O / 2) / 128 : (O + kBM - 1) / kBM;
     a.tiles_n = (int)((N + kBN - 1) / kBN);
+    a.q_absmax = q_absmax;
+    a.q_scale = q_scale;
+    const bool quant = fuse_swiglu && q_absmax;
     const int T = a.tiles_m * a.tiles_n;
     const int KT = a.K_bytes / kRowBytes;
     const dim3 grid((unsigned)(KT >= kAhead ? min(T, cu_count()) : T)), block(kThreads);
     if (fp8) {
-        if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<true, false>), grid, block, 0, s, a);
+        if (quant) hipLaunchKernelGGL((gemm_kernel<true, true, true>), grid, block, 0, s, a);
+        else if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<true, true, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<true, false, false>), grid, block, 0, s, a);
     } else {
-        if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<false, false>), grid, block, 0, s, a);
+        if (quant) hipLaunchKernelGGL((gemm_kernel<false, true, true>), grid, block, 0, s, a);
+        else if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<false, true, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, false>), grid, block, 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || fuse_swiglu || !absmax) return e;

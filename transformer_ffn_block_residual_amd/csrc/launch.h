@@ -19,9 +19,11 @@ hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t
 
 // GEMM: out[n, o] = sum_k x[n, k] * w[o, k] (optionally scaled, optionally
 // SwiGLU-fused).  fp8 selects e4m3 operands with device scales.
+// q_absmax / q_scale: SwiGLU only; out then holds e4m3 codes of h quantised
+// with the known abs-max *q_absmax, and *q_scale receives its scale.
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
-                       hipStream_t s);
+                       hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr);
 
 hipError_t launch_decode(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg, const float* sg,
                          const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd, int M, int C,

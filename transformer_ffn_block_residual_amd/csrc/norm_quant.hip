@@ -158,15 +158,6 @@ __global__ __launch_bounds__(256) void absmax_kernel(float* out, const uint16_t*
 // forward_qmm, quantize_with_abs_max).  16 elements per thread: two 16-byte
 // loads, one 16-byte store.  inv = 448/absmax in IEEE fp32; codes from the fp32
 // product x*inv.  Block 0 also writes the scale absmax/448.
-__device__ __forceinline__ void scale_pair(float am, float& scale, float& inv) {
-    if (am > 0.0f) {
-        scale = am / kE4M3Max;
-        inv = kE4M3Max / am;
-    } else {
-        scale = 1.0f;
-        inv = 1.0f;
-    }
-}
 
 __global__ __launch_bounds__(256) void quant_kernel(uint8_t* __restrict__ q, float* __restrict__ scale_out,
                                                     const float* __restrict__ absmax,
