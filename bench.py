@@ -196,19 +196,17 @@ def cpu_decode_sample(d_q, x, calls):
             "sample": f"{calls} full single-token decodes (C={C}, H={H}); {dt:.2f} s wall"}
 
 
-def decode_graph_ms(torch, decs, x, M, steps):
-    """Average duration of one decode call when `steps` calls (rotating the
-    weight copies) are captured in one HIP graph and replayed: the decode
-    without host launch gaps.  The calls launch kernels only (no memset), so
-    the graph replays them exactly."""
+def graph_step_ms(torch, issue, steps):
+    """Average duration of one step when `steps` steps are captured in one HIP
+    graph and replayed: the path without host launch gaps.  issue(stream)
+    issues the steps on the capturing stream; the path launches kernels only
+    (its abs-max clearing is a kernel, not a memset), so the graph replays
+    them exactly."""
     side = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=side):
-        cur = torch.cuda.current_stream()
-        calls = [db.bind(x, M, cur) for db in decs]
-        for i in range(steps):
-            calls[i % len(calls)]()
+        issue(torch.cuda.current_stream())
     for _ in range(3):
         graph.replay()
     torch.cuda.synchronize()
@@ -317,7 +315,7 @@ def bench_block(a, torch, np, B, block, W):
         am_pp = [pre.am_h.clone(), torch.empty_like(pre.am_h)]
         torch.cuda.synchronize()
 
-    def step(i, tm):
+    def step(i, tm, stream=stream):
         m0 = tm.mark() if tm else None
         B.ffn_rmsnorm_fwd(pre.y, pre.rstd, pre.r, pre.am_y, inp, addend, pre.w_norm, pre.eps, N, C, stream)
         m1 = tm.mark() if tm else None
@@ -361,6 +359,11 @@ def bench_block(a, torch, np, B, block, W):
 
     ms, km = run_steps(torch, stream, step, a)
     spread = run_steps.spread
+
+    def issue(cur):
+        for i in range(a.steps):
+            step(i, None, cur)
+    graph_ms = graph_step_ms(torch, issue, a.steps)
     peak = PEAK[dt]
     gu_tflops = 4.0 * N * C * H / (km["gateup"] * 1e-3) / 1e12
     kernels = {
@@ -399,6 +402,7 @@ def bench_block(a, torch, np, B, block, W):
                      "traffic": measured_traffic(("gateupq_" if known else "gateup_") + a.workload, "gemm.hip")},
         "kernels": kernels,
         "spread_ms": spread,
+        "ms_per_step_in_hip_graph": graph_ms,
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -439,7 +443,11 @@ def bench_decode(a, torch, np, B, block, W):
     spread = run_steps.spread
     nbytes = 3.0 * H * C + (2 * H + C) * 4 + 2.0 * M * (C + H) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
-    graph_ms = decode_graph_ms(torch, decs, x, M, a.steps)
+    def issue(cur):
+        calls_g = [db.bind(x, M, cur) for db in decs]
+        for i in range(a.steps):
+            calls_g[i % len(calls_g)]()
+    graph_ms = graph_step_ms(torch, issue, a.steps)
     # a step is exactly one ffn_decode_gemv call (both of its kernels), so the
     # call's average duration is the timed region's; the event-bracketed pass
     # reads longer by the events' own cost and is reported beside it

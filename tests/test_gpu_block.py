@@ -79,6 +79,50 @@ def test_block_end_to_end_small(blk, fp8, N, C, H, outl):
         assert rel_err(host_bits(b.out), d_c) < TOL_FP8
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_block_and_decode_replay_from_a_hip_graph(blk, fp8):
+    # a captured block forward (and a captured decode) replays to the eager
+    # result, bit for bit, on every replay, with eager work and
+    # synchronisations between the replays
+    N, C, H = 300, 512, 384
+    say(f"graph replay fp8={fp8}")
+    d = W.block_inputs(N, C, H, seed=77, w_std=0.0)
+    b = blk.PrefillBlock(N, C, H, 1e-5, fp8)
+    b.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+    inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
+    M = 3
+    db = blk.DecodeBlock(M, C, H)
+    dd = W.decode_inputs(M, C, H, seed=78, with_weights=True)
+    db.load_master_weights(dd["w_gate"], dd["w_up"], dd["w_down"])
+    xd = dev_bf16(dd["x"])
+    b.forward(inp, add)
+    db.forward(xd, M)
+    torch.cuda.synchronize()
+    names = ["r", "y", "rstd", "am_y", "h", "am_h", "out"] + (["qy", "s_y", "qh", "s_h"] if fp8 else [])
+    eager = {n: getattr(b, n).clone() for n in names}
+    eager_dec = (db.out.clone(), db.h.clone())
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        b.forward(inp, add)
+        db.forward(xd, M)
+    scratch_y, scratch_rstd = empty_bf16(N, C), empty_f32(N)
+    from transformer_ffn_block_residual_amd import binding as B
+    for rep in range(3):
+        for n in names:
+            getattr(b, n).zero_()
+        db.out.zero_()
+        db.h.zero_()
+        B.ffn_rmsnorm_fwd(scratch_y, scratch_rstd, None, None, inp, None, b.w_norm, 1e-5, N, C)  # eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(b, n), eager[n]), (rep, n)
+        assert torch.equal(db.out, eager_dec[0]) and torch.equal(db.h, eager_dec[1]), rep
+
+
 def test_block_deterministic(blk):
     N, C, H = 300, 512, 384
     say("block determinism")
