@@ -45,6 +45,7 @@ from .ffn import (
     decode_dual,
     decode_down,
     decode_gemv,
+    decode_gemv_bf16,
     block_forward,
 )
 
@@ -53,5 +54,5 @@ __all__ = [
     "e4m3_encode", "E4M3_MAX", "residual_add", "rms_rstd", "rms_apply", "rmsnorm_fwd",
     "absmax_of", "scales_from_absmax", "quant_absmax",
     "quant_rows", "gemm_bf16", "gemm_fp8", "silu", "swiglu", "gateup", "down",
-    "decode_dual", "decode_down", "decode_gemv", "block_forward",
+    "decode_dual", "decode_down", "decode_gemv", "decode_gemv_bf16", "block_forward",
 ]

@@ -239,6 +239,21 @@ def decode_gemv(x_bits, wg, sg, wu, su, wd, sd):
     return decode_down(h, wd, sd), h
 
 
+def decode_gemv_bf16(x_bits, wg_bits, wu_bits, wd_bits):
+    """Few-token decode FFN with bf16 weights (dense_ffn_decode.rs,
+    ``DenseFfnLayer::forward``, bf16 arm: ``dense_gemv`` for gate and for up,
+    ``silu_mul``, ``dense_gemv`` for down):
+
+      g = bf16( sum_k Wg[n,k] x[m,k] ),  u likewise,  h = bf16( silu(g) * u )
+      y = bf16( sum_n Wd[c,n] h[m,n] )
+
+    Returns (y_bits [M, C], h_bits [M, H])."""
+    g = bf16_bits_to_f64(gemm_bf16(x_bits, wg_bits))
+    u = bf16_bits_to_f64(gemm_bf16(x_bits, wu_bits))
+    h = f64_to_bf16_bits(silu(g) * u)
+    return gemm_bf16(h, wd_bits), h
+
+
 def block_forward(inp, addend, w_norm, w_gu, w_d, eps, fp8=False):
     """One FFN block as ``_forward_block`` runs it from LN2 on, plus the closing
     residual that the next fused RMSNorm applies (``LLamaModel::forward``).

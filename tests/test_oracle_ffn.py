@@ -284,6 +284,56 @@ def test_decode_brute_force():
     assert np.array_equal(K.bf16_bits_to_f64(y), yb)
 
 
+def _brute_decode_bf16(x, wg, wu, wd):
+    """Loops over exact fractions with bf16 weights, rounding where the
+    definition rounds."""
+    M, C = x.shape
+    H = wg.shape[0]
+    xv = K.bf16_bits_to_f64(x)
+    dg, du, dd = K.bf16_bits_to_f64(wg), K.bf16_bits_to_f64(wu), K.bf16_bits_to_f64(wd)
+    y = np.zeros((M, C))
+    h = np.zeros((M, H))
+    for m in range(M):
+        for n in range(H):
+            g = K.bf16_round(np.array([float(sum((Fraction(dg[n, k]) * Fraction(xv[m, k]) for k in range(C)),
+                                                 Fraction(0)))]))[0]
+            u = K.bf16_round(np.array([float(sum((Fraction(du[n, k]) * Fraction(xv[m, k]) for k in range(C)),
+                                                 Fraction(0)))]))[0]
+            h[m, n] = K.bf16_round(np.array([g / (1 + np.exp(-g)) * u]))[0]
+        for c in range(C):
+            acc = sum((Fraction(dd[c, n]) * Fraction(h[m, n]) for n in range(H)), Fraction(0))
+            y[m, c] = K.bf16_round(np.array([float(acc)]))[0]
+    return y, h
+
+
+def test_decode_bf16_brute_force():
+    d = W.decode_inputs(2, 16, 12, seed=19, w_std=0.3)
+    y, h = O.decode_gemv_bf16(d["x"], d["w_gate"], d["w_up"], d["w_down"])
+    yb, hb = _brute_decode_bf16(d["x"], d["w_gate"], d["w_up"], d["w_down"])
+    assert np.array_equal(K.bf16_bits_to_f64(h), hb)
+    assert np.array_equal(K.bf16_bits_to_f64(y), yb)
+
+
+def test_decode_bf16_equals_fp8_decode_on_e4m3_weights_with_unit_scales():
+    # bf16 weights that are exactly e4m3 values, and the FP8 decode with all row
+    # scales 1: the two definitions coincide
+    d = W.decode_inputs(3, 64, 48, seed=20, w_std=2.0)
+    codes = {k: K.e4m3_encode(K.bf16_bits_to_f64(d[k])) for k in ("w_gate", "w_up", "w_down")}
+    wb = {k: W.to_bf16_bits(K.e4m3_decode(c).astype(np.float32)) for k, c in codes.items()}
+    assert all(np.array_equal(K.bf16_bits_to_f64(wb[k]), K.e4m3_decode(codes[k])) for k in wb)
+    ones_h, ones_c = np.ones(48, np.float32), np.ones(64, np.float32)
+    y8, h8 = O.decode_gemv(d["x"], codes["w_gate"], ones_h, codes["w_up"], ones_h, codes["w_down"], ones_c)
+    yb, hb = O.decode_gemv_bf16(d["x"], wb["w_gate"], wb["w_up"], wb["w_down"])
+    assert np.array_equal(hb, h8) and np.array_equal(yb, y8)
+
+
+def test_decode_bf16_zero_gate_gives_zero():
+    d = W.decode_inputs(2, 32, 24, seed=21, w_std=0.5)
+    zg = np.zeros_like(d["w_gate"])
+    y, h = O.decode_gemv_bf16(d["x"], zg, d["w_up"], d["w_down"])
+    assert not np.any(K.bf16_bits_to_f64(h)) and not np.any(K.bf16_bits_to_f64(y))
+
+
 # ----------------------------------------------------------------------------- block invariants
 
 @pytest.mark.parametrize("fp8", [False, True])
