@@ -11,7 +11,9 @@ synthetic tensors already resident in HBM when the timed region starts.
 Other workloads (same line format, for the per-configuration figures):
   prefill   bf16 block, N=4096, C=4096, H=14336
   prefill8  FP8 block, same shape, 0.1% x50 outliers
-  decode    single-token FP8 decode, C=4096, H=14336 (value in GB/s)
+  decode    single-token FP8 decode, C=4096, H=14336 (value in GB/s);
+            --decode-arm picks the arm (split SiLU, fused SiLU input,
+            per projection, or bf16 weights), --decode-m the tokens (1..4)
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 25] [--workload qwen7b8] [--no-cpu-baseline]
 
@@ -40,6 +42,14 @@ PEAK = {"fp8": 5000.0, "bf16": 2500.0}   # MI355X dense MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0                    # MI355X HBM3E
 DECODE_COPIES = 3                        # rotating decode weight copies: > 256 MB MALL
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# decode arms: (ffn_decode_gemv_arm arm, or None for ffn_decode_gemv / "bf16"
+# for ffn_decode_gemv_bf16; description)
+DECODE_ARMS = {
+    "split": (None, "split SiLU: dual gate/up GEMV with silu_mul in its epilogue, then the down GEMV"),
+    "silu_input": (1, "fused SiLU input: dual gate/up GEMV to g|u, then the down GEMV forming silu(g)*u itself"),
+    "per_projection": (2, "per projection: gate GEMV, up GEMV, silu_mul, down GEMV"),
+    "bf16": ("bf16", "bf16 weights: dense gate/up GEMV with silu_mul, then the dense down GEMV"),
+}
 CSRC = os.path.join(ROOT, "transformer_ffn_block_residual_amd", "csrc")
 
 
@@ -54,6 +64,9 @@ def parse():
                    help="prefill rows in the CPU oracle sample (default: min(N, 4096), about 10 s)")
     p.add_argument("--cpu-decodes", type=int, default=30,
                    help="decode calls in the CPU oracle sample of the decode workload (about 10 s)")
+    p.add_argument("--decode-arm", default="split", choices=list(DECODE_ARMS),
+                   help="decode workload: which arm of the decode FFN runs")
+    p.add_argument("--decode-m", type=int, default=1, help="decode workload: tokens per call (1..4 off split)")
     p.add_argument("--known-h-absmax", action="store_true",
                    help="FP8 block workloads: quantise h in the gate+up epilogue with the previous step's abs-max "
                         "(ffn_gateup_swiglu_quant, the recompute form) instead of bf16 h + ffn_quant_absmax")
@@ -182,18 +195,33 @@ def cpu_block_sample(w, d, rows, dec_x=None):
 
 
 def cpu_decode_sample(d_q, x, calls):
-    """The oracle decode of one token over the full weights (already
+    """The oracle decode of x's M tokens over the full weights (already
     quantised), `calls` times, in GB/s of algorithmic bytes."""
     import oracle as O
     qg, sg, qu, su, qd, sd = d_q
     H, C = qg.shape
+    M = x.shape[0]
     t0 = time.perf_counter()
     for _ in range(calls):
         O.decode_gemv(x, qg, sg, qu, su, qd, sd)
     dt = time.perf_counter() - t0
-    nbytes = calls * (3.0 * H * C + (2 * H + C) * 4 + 2.0 * (C + H) * 2)
+    nbytes = calls * (3.0 * H * C + (2 * H + C) * 4 + 2.0 * M * (C + H) * 2)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"{calls} full single-token decodes (C={C}, H={H}); {dt:.2f} s wall"}
+            "sample": f"{calls} full {M}-token FP8 decodes (C={C}, H={H}); {dt:.2f} s wall"}
+
+
+def cpu_decode_sample_bf16(d, calls):
+    """The oracle bf16-weight decode, `calls` times, in GB/s of algorithmic bytes."""
+    import oracle as O
+    H, C = d["w_gate"].shape
+    M = d["x"].shape[0]
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        O.decode_gemv_bf16(d["x"], d["w_gate"], d["w_up"], d["w_down"])
+    dt = time.perf_counter() - t0
+    nbytes = calls * (6.0 * H * C + 2.0 * M * (C + H) * 2)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{calls} full {M}-token bf16-weight decodes (C={C}, H={H}); {dt:.2f} s wall"}
 
 
 def graph_step_ms(torch, issue, steps):
@@ -412,26 +440,42 @@ def bench_block(a, torch, np, B, block, W):
 
 def bench_decode(a, torch, np, B, block, W):
     w = W.WORKLOADS["decode"]
-    M, C, H = 1, w.C, w.H
-    print(f"[bench] generating decode inputs (seed {w.seed})", file=sys.stderr, flush=True)
+    M, C, H = a.decode_m, w.C, w.H
+    arm, arm_what = DECODE_ARMS[a.decode_arm]
+    bf16w = arm == "bf16"
+    print(f"[bench] generating decode inputs (seed {w.seed}), arm {a.decode_arm}, M={M}", file=sys.stderr,
+          flush=True)
     d = W.decode_inputs(M, C, H, w.seed, w.w_std)
 
     def dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    first = block.DecodeBlock(M, C, H)
-    first.load_master_weights(d["w_gate"], d["w_up"], d["w_down"])
-    decs = [first]
-    for _ in range(DECODE_COPIES - 1):
-        db = block.DecodeBlock(M, C, H)
-        db.set_fp8_weights(first.wg.clone(), first.sg.clone(), first.wu.clone(), first.su.clone(),
-                           first.wd.clone(), first.sd.clone())
-        decs.append(db)
+    decs = []
+    if bf16w:
+        wts = [dev(d[k]) for k in ("w_gate", "w_up", "w_down")]
+        for i in range(DECODE_COPIES):
+            db = block.DecodeBlockBf16(M, C, H)
+            db.load_weights(*(wts if i == 0 else [t.clone() for t in wts]))
+            decs.append(db)
+    else:
+        first = block.DecodeBlock(M, C, H)
+        first.load_master_weights(d["w_gate"], d["w_up"], d["w_down"])
+        decs.append(first)
+        for _ in range(DECODE_COPIES - 1):
+            db = block.DecodeBlock(M, C, H)
+            db.set_fp8_weights(first.wg.clone(), first.sg.clone(), first.wu.clone(), first.su.clone(),
+                               first.wd.clone(), first.sd.clone())
+            decs.append(db)
     x = dev(d["x"])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    calls = [db.bind(x, M, stream) for db in decs]
+    def bind_all(cur):
+        if bf16w or arm is None:
+            return [db.bind(x, M, cur) for db in decs]
+        return [db.bind(x, M, cur, arm=arm) for db in decs]
+
+    calls = bind_all(stream)
 
     def step(i, tm):
         m0 = tm.mark() if tm else None
@@ -441,28 +485,34 @@ def bench_decode(a, torch, np, B, block, W):
 
     ms, km = run_steps(torch, stream, step, a)
     spread = run_steps.spread
-    nbytes = 3.0 * H * C + (2 * H + C) * 4 + 2.0 * M * (C + H) * 2
+    # algorithmic bytes: each weight (and row scale) once, x, h and out once
+    wbytes = (6.0 * H * C) if bf16w else (3.0 * H * C + (2 * H + C) * 4)
+    nbytes = wbytes + 2.0 * M * (C + H) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
+
     def issue(cur):
-        calls_g = [db.bind(x, M, cur) for db in decs]
+        calls_g = bind_all(cur)
         for i in range(a.steps):
             calls_g[i % len(calls_g)]()
     graph_ms = graph_step_ms(torch, issue, a.steps)
-    # a step is exactly one ffn_decode_gemv call (both of its kernels), so the
-    # call's average duration is the timed region's; the event-bracketed pass
-    # reads longer by the events' own cost and is reported beside it
+    # a step is exactly one decode call (all of its kernels), so the call's
+    # average duration is the timed region's; the event-bracketed pass reads
+    # longer by the events' own cost and is reported beside it
     call_ms = ms
+    wdesc = ("bf16" if bf16w else "e4m3 with per-row fp32 scales")
+    entry = {None: "ffn_decode_gemv", "bf16": "ffn_decode_gemv_bf16"}.get(arm, "ffn_decode_gemv_arm")
+    default = a.decode_arm == "split" and M == 1
     out = {
         "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
-        "data": "synthetic",
-        "config": {"workload": "single-token FP8 decode FFN: x[1,4096] bf16, gate/up [14336,4096] and down "
-                               "[4096,14336] e4m3 with per-row fp32 scales", "M": M, "C": C, "H": H,
-                   "seed": w.seed, "weight_copies": DECODE_COPIES},
-        "roofline": {"bound": "hbm", "kernel": "ffn_decode_gemv (dual gate/up + down GEMV)",
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16w else "fp8", "data": "synthetic",
+        "config": {"workload": f"{'single' if M == 1 else str(M)}-token decode FFN: x[{M},{C}] bf16, gate/up "
+                               f"[{H},{C}] and down [{C},{H}] {wdesc}; {arm_what}",
+                   "M": M, "C": C, "H": H, "seed": w.seed, "weight_copies": DECODE_COPIES, "arm": a.decode_arm},
+        "roofline": {"bound": "hbm", "kernel": f"{entry} ({arm_what})",
                      "achieved": nbytes / (call_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": measured_traffic("decode_decode", "decode.hip")},
+                     "traffic": measured_traffic("decode_decode", "decode.hip") if default else None},
         "kernels": {"decode": {"ms": call_ms, "GB/s": nbytes / call_ms / 1e6,
                                "ms_between_events": km["decode"], "median_min_between_events": spread["decode"],
                                "ms_in_hip_graph": graph_ms, "GB/s_in_hip_graph": nbytes / graph_ms / 1e6}},
@@ -470,10 +520,13 @@ def bench_decode(a, torch, np, B, block, W):
     if not a.no_cpu_baseline:
         import oracle as O
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        qg, sg = O.quant_rows(d["w_gate"])
-        qu, su = O.quant_rows(d["w_up"])
-        qd, sd = O.quant_rows(d["w_down"])
-        out["cpu_baseline"] = cpu_decode_sample((qg, sg, qu, su, qd, sd), d["x"], a.cpu_decodes)
+        if bf16w:
+            out["cpu_baseline"] = cpu_decode_sample_bf16(d, a.cpu_decodes)
+        else:
+            qg, sg = O.quant_rows(d["w_gate"])
+            qu, su = O.quant_rows(d["w_up"])
+            qd, sd = O.quant_rows(d["w_down"])
+            out["cpu_baseline"] = cpu_decode_sample((qg, sg, qu, su, qd, sd), d["x"], a.cpu_decodes)
     return out
 
 

@@ -170,6 +170,44 @@ ffn_status_t ffn_decode_gemv(void* out, void* h, const void* x,
                              const uint8_t* w_down, const float* s_down,
                              int64_t M, int64_t C, int64_t H, hipStream_t stream);
 
+/* The arms of the FP8 decode FFN.  [metrale] DenseFfnLayer::forward, FP8 arm,
+ * and the note beside it: the split-SiLU arm (the default, ffn_decode_gemv)
+ * forms silu(g) * u once before the down GEMV; the fused SiLU-input arm
+ * (w8a16_gemv_silu_input) forms it inside the down GEMV, recomputing it for
+ * every output; the per-projection arm runs gate and up as two GEMVs, then
+ * silu_mul, then the down GEMV. */
+typedef enum {
+    FFN_DECODE_SPLIT_SILU = 0,
+    FFN_DECODE_SILU_INPUT = 1,
+    FFN_DECODE_PER_PROJECTION = 2
+} ffn_decode_arm_t;
+
+/* ffn_decode_gemv through a chosen arm.  All arms compute the same rounded
+ * quantities (g, u and h = bf16(silu(g) * u) in bf16, the down GEMV on h), so
+ * out is bit-identical across arms; only the kernels differ.
+ * gu: bf16 [M, 2H] workspace (g in columns [0,H), u in [H,2H)), required by the
+ * SiLU-input and per-projection arms, ignored by the split arm; h: bf16 [M,H],
+ * written by the split and per-projection arms (the SiLU-input arm never forms
+ * it).  Other arguments as ffn_decode_gemv.  Supported: M <= 32 for the split
+ * arm, M <= 4 for the others; gu must not alias x, out or h. */
+ffn_status_t ffn_decode_gemv_arm(void* out, void* h, void* gu, const void* x,
+                                 const uint8_t* w_gate, const float* s_gate,
+                                 const uint8_t* w_up, const float* s_up,
+                                 const uint8_t* w_down, const float* s_down,
+                                 ffn_decode_arm_t arm, int64_t M, int64_t C, int64_t H,
+                                 hipStream_t stream);
+
+/* Decode FFN with bf16 weights (no quantisation).  [metrale]
+ * DenseFfnLayer::forward, bf16 arm: dense_gemv for gate and up, silu_mul,
+ * dense_gemv for the down projection.
+ *   g = bf16(sum_k w_gate[n,k] x[m,k]),  u likewise,  h = bf16(silu(g) * u),
+ *   out[m,c] = bf16(sum_n w_down[c,n] h[m,n]).
+ * x: bf16 [M,C]; w_gate, w_up: bf16 [H,C]; w_down: bf16 [C,H]; h: bf16 [M,H]
+ * workspace, returned.  Supported: 0 <= M <= 4, C % 128 == 0, H % 128 == 0. */
+ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
+                                  const void* w_gate, const void* w_up, const void* w_down,
+                                  int64_t M, int64_t C, int64_t H, hipStream_t stream);
+
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
 const char* ffn_last_error(void);
 

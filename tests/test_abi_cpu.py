@@ -37,7 +37,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
-              "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_last_error", "ffn_version"]:
+              "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16",
+              "ffn_last_error", "ffn_version"]:
         assert n in names
 
 
@@ -120,6 +121,24 @@ def test_decode_validation(lib):
     mis = list(args)
     mis[3] = MIS
     assert f(*mis, 1, 4096, 14336, None) == UNSUPPORTED
+
+
+def test_decode_arm_and_bf16_validation(lib):
+    B, C_, D = 0x20000, 0x30000, 0x40000
+    f = lib.ffn_decode_gemv_arm   # out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H
+    assert f(A, B, C_, D, A, A, A, A, A, A, 7, 1, 256, 768, None) == INVALID          # unknown arm
+    assert f(A, B, None, D, A, A, A, A, A, A, 1, 1, 256, 768, None) == INVALID        # SiLU-input arm needs gu
+    assert f(A, B, B, D, A, A, A, A, A, A, 2, 1, 256, 768, None) == INVALID           # gu aliases h
+    assert f(A, B, C_, D, A, A, A, A, A, A, 1, 5, 256, 768, None) == UNSUPPORTED      # M > 4 off the split arm
+    assert f(A, B, None, D, A, A, A, A, A, A, 0, 33, 256, 768, None) == UNSUPPORTED   # M > 32
+    assert f(A, B, C_, D, A, None, A, A, A, A, 0, 1, 256, 768, None) == INVALID       # no gate scales
+    assert f(A, B, MIS, D, A, A, A, A, A, A, 1, 1, 256, 768, None) == UNSUPPORTED     # misaligned gu
+    g = lib.ffn_decode_gemv_bf16  # out, h, x, wg, wu, wd, M, C, H
+    assert g(A, B, D, A, A, None, 1, 256, 768, None) == INVALID                       # no down weight
+    assert g(A, B, D, A, A, A, 5, 256, 768, None) == UNSUPPORTED                      # M > 4
+    assert g(A, B, D, A, A, A, 1, 200, 768, None) == UNSUPPORTED                      # C % 128
+    assert g(A, A, D, A, A, A, 1, 256, 768, None) == INVALID                          # h aliases out
+    assert g(A, B, D, A, A, A, 1, 32768, 32768, None) == UNSUPPORTED                  # > 2 GiB of weights
 
 
 def test_binding_rejects_host_tensors_and_short_buffers():

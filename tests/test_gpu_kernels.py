@@ -380,6 +380,71 @@ def test_decode(F, M, C, H):
     assert rel_err(gy, y_ref) < 3e-2
 
 
+def _decode_weights(F, d):
+    wq, ws = {}, {}
+    for k in ("w_gate", "w_up", "w_down"):
+        rows, cols = d[k].shape
+        q, s = empty_u8(rows, cols), empty_f32(rows)
+        F.ffn_quant_rows(q, s, dev_bf16(d[k]), rows, cols)
+        wq[k], ws[k] = q, s
+    return wq, ws
+
+
+# partial windows of 1024 (FP8) and 512 (bf16) weights per row in C and in H
+ARM_SHAPES = [(1, 256, 768), (1, 3584, 384), (2, 1152, 640), (3, 512, 640), (4, 640, 2304), (4, 4096, 1024)]
+
+
+@pytest.mark.parametrize("M,C,H", ARM_SHAPES)
+def test_decode_arms_agree_bit_for_bit(F, M, C, H):
+    say(f"decode arms M={M} C={C} H={H}")
+    d = W.decode_inputs(M, C, H, seed=M * 31 + C + H)
+    wq, ws = _decode_weights(F, d)
+    xd = dev_bf16(d["x"])
+    args = (xd, wq["w_gate"], ws["w_gate"], wq["w_up"], ws["w_up"], wq["w_down"], ws["w_down"])
+    out, h = empty_bf16(M, C), empty_bf16(M, H)
+    F.ffn_decode_gemv(out, h, *args, M, C, H)
+    res = {}
+    for arm in (F.FFN_DECODE_SPLIT_SILU, F.FFN_DECODE_SILU_INPUT, F.FFN_DECODE_PER_PROJECTION):
+        o2, h2, gu = empty_bf16(M, C).fill_(7.0), empty_bf16(M, H).fill_(7.0), empty_bf16(M, 2 * H).fill_(7.0)
+        F.ffn_decode_gemv_arm(o2, h2, gu, *args, arm, M, C, H)
+        res[arm] = (o2, h2, gu)
+    torch.cuda.synchronize()
+    for arm, (o2, h2, gu) in res.items():
+        assert torch.equal(o2, out), arm
+        if arm != F.FFN_DECODE_SILU_INPUT:
+            assert torch.equal(h2, h), arm
+        if arm != F.FFN_DECODE_SPLIT_SILU:
+            # the workspace holds g then u: the oracle's SwiGLU of it is the split
+            # arm's h up to the hardware exp's last bit
+            dh = ulp_diff(O.swiglu(host_bits(gu))[0], host_bits(h))
+            assert dh.max() <= 1 and np.mean(dh != 0) < 1e-2, arm
+    # and the split arm against the oracle, as in test_decode
+    ref_q = {k: O.quant_rows(d[k]) for k in ("w_gate", "w_up", "w_down")}
+    (qg, sg), (qu, su), (qd, sd) = ref_q["w_gate"], ref_q["w_up"], ref_q["w_down"]
+    y_ref, h_ref = O.decode_gemv(d["x"], qg, sg, qu, su, qd, sd)
+    assert rel_err(host_bits(h), h_ref) < 2e-2
+    assert rel_err(host_bits(out), y_ref) < 3e-2
+
+
+@pytest.mark.parametrize("M,C,H", ARM_SHAPES + [(1, 128, 128)])
+def test_decode_bf16_weights(F, M, C, H):
+    say(f"decode bf16 weights M={M} C={C} H={H}")
+    d = W.decode_inputs(M, C, H, seed=M * 17 + C + H)
+    out, h = empty_bf16(M, C).fill_(7.0), empty_bf16(M, H).fill_(7.0)
+    F.ffn_decode_gemv_bf16(out, h, dev_bf16(d["x"]), dev_bf16(d["w_gate"]), dev_bf16(d["w_up"]),
+                           dev_bf16(d["w_down"]), M, C, H)
+    torch.cuda.synchronize()
+    y_ref, h_ref = O.decode_gemv_bf16(d["x"], d["w_gate"], d["w_up"], d["w_down"])
+    gh, gy = host_bits(h), host_bits(out)
+    # fp32 sums in another order than the oracle's fp64: g and u can land one
+    # bf16 ulp apart, rarely
+    assert rel_err(gh, h_ref) < 2e-2
+    # the down GEMV given the GPU's own h: one rounding of an fp32 sum
+    y_cond = O.gemm_bf16(gh, d["w_down"])
+    assert ulp_diff(gy, y_cond).max() <= 1
+    assert rel_err(gy, y_ref) < 2e-2
+
+
 def test_decode_empty_batch(F):
     say("decode M=0")
     C, H = 256, 256

@@ -6,7 +6,8 @@ kernels for MI355X (gfx950) behind the C ABI of ``include/ffn.h``.
 The binding functions (``ffn_rmsnorm_fwd``, ``ffn_quant_absmax``,
 ``ffn_quant_rows``, ``ffn_gateup``, ``ffn_gateup_swiglu_quant``, ``ffn_swiglu``,
 ``ffn_down``,
-``ffn_decode_gemv``, and ``bind_decode_gemv``, its checked-once form) live in
+``ffn_decode_gemv``, its arms ``ffn_decode_gemv_arm``, its bf16-weight form
+``ffn_decode_gemv_bf16``, and ``bind_decode_gemv``, its checked-once form) live in
 ``binding``; accessing any of them here loads
 ``libffn.so`` and raises if it has not been built.  ``workloads`` (seeded
 synthetic inputs) and ``build`` import without the library.
@@ -15,7 +16,9 @@ synthetic inputs) and ``build`` import without the library.
 _BINDING_NAMES = {
     "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
     "ffn_swiglu", "ffn_down",
-    "ffn_decode_gemv", "bind_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_OK", "FFN_ERR_INVALID",
+    "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
+    "bind_decode_gemv_arm", "bind_decode_gemv_bf16",
+    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_OK", "FFN_ERR_INVALID",
     "FFN_ERR_UNSUPPORTED", "FFN_ERR_HIP", "version", "last_error", "LIB_PATH",
 }
 

@@ -45,6 +45,8 @@ def _load():
         "ffn_swiglu": [P, P, P, I64, I64, P],
         "ffn_down": [P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_decode_gemv": [P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
+        "ffn_decode_gemv_arm": [P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P],
+        "ffn_decode_gemv_bf16": [P, P, P, P, P, P, I64, I64, I64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -183,20 +185,63 @@ def ffn_decode_gemv(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C,
                                                    M, C, H, stream)))
 
 
-def bind_decode_gemv(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
-    """ffn_decode_gemv with its arguments checked and marshalled once: returns
-    a no-argument callable that issues the same call (same tensors, sizes and
-    stream) again.  For per-token loops where the checks would cost more host
-    time than the GPU spends on the call; the tensors must stay alive."""
-    args = _decode_gemv_args(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream)
-    fn = _lib.ffn_decode_gemv
+FFN_DECODE_SPLIT_SILU, FFN_DECODE_SILU_INPUT, FFN_DECODE_PER_PROJECTION = 0, 1, 2
 
+
+def _decode_arm_args(out, h, gu, x, w_gate, s_gate, w_up, s_up, w_down, s_down, arm, M, C, H, stream):
+    split = arm == FFN_DECODE_SPLIT_SILU
+    return (_ptr(out, "out", M * C, BF16), _ptr(h, "h", M * H, BF16),
+            _ptr(gu, "gu", M * 2 * H, BF16, optional=split), _ptr(x, "x", M * C, BF16),
+            _ptr(w_gate, "w_gate", H * C, E4M3), _ptr(s_gate, "s_gate", H, F32),
+            _ptr(w_up, "w_up", H * C, E4M3), _ptr(s_up, "s_up", H, F32),
+            _ptr(w_down, "w_down", C * H, E4M3), _ptr(s_down, "s_down", C, F32),
+            int(arm), int(M), int(C), int(H), _stream(stream))
+
+
+def ffn_decode_gemv_arm(out, h, gu, x, w_gate, s_gate, w_up, s_up, w_down, s_down, arm, M, C, H, stream=None):
+    _check(_lib.ffn_decode_gemv_arm(*_decode_arm_args(out, h, gu, x, w_gate, s_gate, w_up, s_up, w_down, s_down,
+                                                      arm, M, C, H, stream)))
+
+
+def _decode_bf16_args(out, h, x, w_gate, w_up, w_down, M, C, H, stream):
+    return (_ptr(out, "out", M * C, BF16), _ptr(h, "h", M * H, BF16), _ptr(x, "x", M * C, BF16),
+            _ptr(w_gate, "w_gate", H * C, BF16), _ptr(w_up, "w_up", H * C, BF16),
+            _ptr(w_down, "w_down", C * H, BF16), int(M), int(C), int(H), _stream(stream))
+
+
+def ffn_decode_gemv_bf16(out, h, x, w_gate, w_up, w_down, M, C, H, stream=None):
+    _check(_lib.ffn_decode_gemv_bf16(*_decode_bf16_args(out, h, x, w_gate, w_up, w_down, M, C, H, stream)))
+
+
+def _bound(fn, args):
     def call():
         _check(fn(*args))
     return call
 
 
+def bind_decode_gemv(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
+    """ffn_decode_gemv with its arguments checked and marshalled once: returns
+    a no-argument callable that issues the same call (same tensors, sizes and
+    stream) again.  For per-token loops where the checks would cost more host
+    time than the GPU spends on the call; the tensors must stay alive."""
+    return _bound(_lib.ffn_decode_gemv,
+                  _decode_gemv_args(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream))
+
+
+def bind_decode_gemv_arm(out, h, gu, x, w_gate, s_gate, w_up, s_up, w_down, s_down, arm, M, C, H, stream=None):
+    """ffn_decode_gemv_arm bound once, as bind_decode_gemv."""
+    return _bound(_lib.ffn_decode_gemv_arm,
+                  _decode_arm_args(out, h, gu, x, w_gate, s_gate, w_up, s_up, w_down, s_down, arm, M, C, H, stream))
+
+
+def bind_decode_gemv_bf16(out, h, x, w_gate, w_up, w_down, M, C, H, stream=None):
+    """ffn_decode_gemv_bf16 bound once, as bind_decode_gemv."""
+    return _bound(_lib.ffn_decode_gemv_bf16, _decode_bf16_args(out, h, x, w_gate, w_up, w_down, M, C, H, stream))
+
+
 __all__ = [
     "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
-    "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "bind_decode_gemv", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
+    "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
+    "bind_decode_gemv_arm", "bind_decode_gemv_bf16",
+    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
 ]

@@ -19,7 +19,9 @@ blocks feeds ``(r, down)`` of one block into ``(inp, addend)`` of the next.
 
 ``DecodeBlock`` holds FP8 weights with per-row scales and runs
 ``ffn_decode_gemv`` for 1..32 tokens (metrale dense_ffn_decode.rs,
-``DenseFfnLayer::forward``, FP8 arm).
+``DenseFfnLayer::forward``, FP8 arm), or one of its other arms
+(``ffn_decode_gemv_arm``, 1..4 tokens); ``DecodeBlockBf16`` holds bf16
+weights and runs ``ffn_decode_gemv_bf16`` (the bf16 arm, 1..4 tokens).
 
 Buffers are allocated once, at construction, through torch; the calls
 themselves allocate nothing.  Every step of the arithmetic runs in libffn.so.
@@ -143,9 +145,45 @@ class DecodeBlock:
                           M, self.C, self.H, stream)
         return self.out
 
-    def bind(self, x, M=None, stream=None):
-        """A no-argument callable that runs forward(x, M, stream) with the
-        argument checks done once (for per-token loops)."""
+    def _gu(self):
+        if not hasattr(self, "gu"):
+            self.gu = _bf16(max(self.M, 1), 2 * self.H)   # g | u workspace of the non-split arms
+        return self.gu
+
+    def forward_arm(self, x, arm, M=None, stream=None):
         M = self.M if M is None else M
-        return B.bind_decode_gemv(self.out, self.h, x, self.wg, self.sg, self.wu, self.su, self.wd, self.sd,
-                                  M, self.C, self.H, stream)
+        B.ffn_decode_gemv_arm(self.out, self.h, self._gu(), x, self.wg, self.sg, self.wu, self.su, self.wd,
+                              self.sd, arm, M, self.C, self.H, stream)
+        return self.out
+
+    def bind(self, x, M=None, stream=None, arm=None):
+        """A no-argument callable that runs forward(x, M, stream) (or
+        forward_arm with ``arm``) with the argument checks done once (for
+        per-token loops)."""
+        M = self.M if M is None else M
+        if arm is None:
+            return B.bind_decode_gemv(self.out, self.h, x, self.wg, self.sg, self.wu, self.su, self.wd, self.sd,
+                                      M, self.C, self.H, stream)
+        return B.bind_decode_gemv_arm(self.out, self.h, self._gu(), x, self.wg, self.sg, self.wu, self.su,
+                                      self.wd, self.sd, arm, M, self.C, self.H, stream)
+
+
+class DecodeBlockBf16:
+    def __init__(self, M, C, H):
+        self.M, self.C, self.H = M, C, H
+        self.h = _bf16(max(M, 1), H)
+        self.out = _bf16(max(M, 1), C)
+
+    def load_weights(self, w_gate, w_up, w_down):
+        """bf16 weights: device tensors (kept as given) or host bit patterns (copied)."""
+        as_dev = (lambda w: w if isinstance(w, torch.Tensor) else _bf16_dev(w))
+        self.wg, self.wu, self.wd = as_dev(w_gate), as_dev(w_up), as_dev(w_down)
+
+    def forward(self, x, M=None, stream=None):
+        M = self.M if M is None else M
+        B.ffn_decode_gemv_bf16(self.out, self.h, x, self.wg, self.wu, self.wd, M, self.C, self.H, stream)
+        return self.out
+
+    def bind(self, x, M=None, stream=None):
+        M = self.M if M is None else M
+        return B.bind_decode_gemv_bf16(self.out, self.h, x, self.wg, self.wu, self.wd, M, self.C, self.H, stream)

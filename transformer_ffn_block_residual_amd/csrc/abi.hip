@@ -218,36 +218,69 @@ ffn_status_t ffn_down(void* out, const void* h, const float* h_scale, const void
                       "ffn_down");
 }
 
+// Checks shared by the decode entry points (elt: weight bytes per element).
+static ffn_status_t check_decode(const char* fn, const void* out, const void* h, const void* x, const void* wg,
+                                 const void* wu, const void* wd, int64_t M, int64_t C, int64_t H, int elt,
+                                 int64_t max_m) {
+    if (!out || !h || !x || !wg || !wu || !wd) return fail(FFN_ERR_INVALID, "%s: a required pointer is NULL", fn);
+    if (M < 0 || C < 0 || H < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);
+    if (M > max_m) return fail(FFN_ERR_UNSUPPORTED, "%s: M = %lld > %lld", fn, (long long)M, (long long)max_m);
+    if (C < 128 || C % 128 != 0 || C > kMaxDim || H < 128 || H % 128 != 0 || H > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: C = %lld, H = %lld must be positive multiples of 128", fn,
+                    (long long)C, (long long)H);
+    if (C * H * elt >= ((int64_t)1 << 31)) return fail(FFN_ERR_UNSUPPORTED, "%s: weights exceed 2 GiB", fn);
+    if (misaligned(out) || misaligned(h) || misaligned(x) || misaligned(wg) || misaligned(wu) || misaligned(wd))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
+    if (h == x || out == h) return fail(FFN_ERR_INVALID, "%s: h must not alias x or out", fn);
+    return FFN_OK;
+}
+
 ffn_status_t ffn_decode_gemv(void* out, void* h, const void* x, const uint8_t* w_gate, const float* s_gate,
                              const uint8_t* w_up, const float* s_up, const uint8_t* w_down, const float* s_down,
                              int64_t M, int64_t C, int64_t H, hipStream_t stream) {
-    REQUIRE(out);
-    REQUIRE(h);
-    REQUIRE(x);
-    REQUIRE(w_gate);
     REQUIRE(s_gate);
-    REQUIRE(w_up);
     REQUIRE(s_up);
-    REQUIRE(w_down);
     REQUIRE(s_down);
-    NONNEG(M);
-    NONNEG(C);
-    NONNEG(H);
-    if (M > 32) return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_gemv: M = %lld > 32", (long long)M);
-    if (C < 128 || C % 128 != 0 || C > kMaxDim || H < 128 || H % 128 != 0 || H > kMaxDim)
-        return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_gemv: C = %lld, H = %lld must be positive multiples of 128",
-                    (long long)C, (long long)H);
-    if (C * H >= ((int64_t)1 << 31)) return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_gemv: weights exceed 2 GiB");
-    ALIGNED(out);
-    ALIGNED(h);
-    ALIGNED(x);
-    ALIGNED(w_gate);
-    ALIGNED(w_up);
-    ALIGNED(w_down);
-    if (h == x || out == h) return fail(FFN_ERR_INVALID, "ffn_decode_gemv: h must not alias x or out");
-    return hip_status(ffn::launch_decode((uint16_t*)out, (uint16_t*)h, (const uint16_t*)x, w_gate, s_gate, w_up,
-                                         s_up, w_down, s_down, (int)M, (int)C, (int)H, stream),
+    if (ffn_status_t st = check_decode("ffn_decode_gemv", out, h, x, w_gate, w_up, w_down, M, C, H, 1, 32)) return st;
+    return hip_status(ffn::launch_decode((uint16_t*)out, (uint16_t*)h, nullptr, (const uint16_t*)x, w_gate, s_gate,
+                                         w_up, s_up, w_down, s_down, ffn::kDecodeSplitSilu, false, (int)M, (int)C,
+                                         (int)H, stream),
                       "ffn_decode_gemv");
+}
+
+ffn_status_t ffn_decode_gemv_arm(void* out, void* h, void* gu, const void* x, const uint8_t* w_gate,
+                                 const float* s_gate, const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                                 const float* s_down, ffn_decode_arm_t arm, int64_t M, int64_t C, int64_t H,
+                                 hipStream_t stream) {
+    REQUIRE(s_gate);
+    REQUIRE(s_up);
+    REQUIRE(s_down);
+    if (arm != FFN_DECODE_SPLIT_SILU && arm != FFN_DECODE_SILU_INPUT && arm != FFN_DECODE_PER_PROJECTION)
+        return fail(FFN_ERR_INVALID, "ffn_decode_gemv_arm: unknown arm %d", (int)arm);
+    const int64_t max_m = arm == FFN_DECODE_SPLIT_SILU ? 32 : 4;
+    if (ffn_status_t st = check_decode("ffn_decode_gemv_arm", out, h, x, w_gate, w_up, w_down, M, C, H, 1, max_m))
+        return st;
+    if (arm != FFN_DECODE_SPLIT_SILU) {
+        REQUIRE(gu);
+        ALIGNED(gu);
+        if (gu == x || gu == out || gu == h)
+            return fail(FFN_ERR_INVALID, "ffn_decode_gemv_arm: gu must not alias x, out or h");
+    }
+    return hip_status(ffn::launch_decode((uint16_t*)out, (uint16_t*)h, (uint16_t*)gu, (const uint16_t*)x, w_gate,
+                                         s_gate, w_up, s_up, w_down, s_down, (int)arm, false, (int)M, (int)C, (int)H,
+                                         stream),
+                      "ffn_decode_gemv_arm");
+}
+
+ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x, const void* w_gate, const void* w_up,
+                                  const void* w_down, int64_t M, int64_t C, int64_t H, hipStream_t stream) {
+    if (ffn_status_t st = check_decode("ffn_decode_gemv_bf16", out, h, x, w_gate, w_up, w_down, M, C, H, 2, 4))
+        return st;
+    return hip_status(ffn::launch_decode((uint16_t*)out, (uint16_t*)h, nullptr, (const uint16_t*)x,
+                                         (const uint8_t*)w_gate, nullptr, (const uint8_t*)w_up, nullptr,
+                                         (const uint8_t*)w_down, nullptr, ffn::kDecodeSplitSilu, true, (int)M, (int)C,
+                                         (int)H, stream),
+                      "ffn_decode_gemv_bf16");
 }
 
 }  // extern "C"

@@ -68,6 +68,20 @@ __device__ __forceinline__ f32x2_t e4m3x2_to_f32(uint32_t w, bool hi) {
     return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
 }
 
+// Bytes 0,1 (hi=false) or 2,3 (hi=true) of a dword of e4m3 codes -> a packed
+// bf16 pair (element 0 in the low half), exact.
+__device__ __forceinline__ bf16x2_t e4m3x2_to_bf16(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+
+// c + w.lo * x.lo + w.hi * x.hi on packed bf16 pairs, fp32 accumulation
+// (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t x, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), c,
+                                           false);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);

@@ -25,7 +25,6 @@
 namespace ffn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
 
 // waves per workgroup per pass; row blocks per workgroup of the dual pass
 // when several tokens share each weight (activation reuse)
@@ -35,10 +34,8 @@ constexpr int kPieces = kChunk / 64;  // 16-byte loads per lane per row per step
 
 // 8 e4m3 codes (two dwords) -> 8 bf16 in MFMA operand order.
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
-    const bf16x2_t2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-    const bf16x2_t2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-    const bf16x2_t2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-    const bf16x2_t2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    const bf16x2_t a = e4m3x2_to_bf16(w0, false), b = e4m3x2_to_bf16(w0, true);
+    const bf16x2_t c = e4m3x2_to_bf16(w1, false), d = e4m3x2_to_bf16(w1, true);
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
@@ -187,31 +184,52 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
     }
 }
 
-// Few-token form (M <= 4) of both passes, on the vector ALU.  With one to
+// Few-token form (M <= 4) of the passes, on the vector ALU.  With one to
 // four tokens the MFMA above multiplies mostly zero columns and spends as many
 // load instructions on activations as on weights.  Here the 64 lanes of a wave
 // split K instead: one load instruction reads 1 KiB of one weight row (lane l:
-// bytes [1024 w + 16 l, +16)), full cache lines in order, and the matching 16
+// bytes [1024 w + 16 l, +16)), full cache lines in order, and the matching
 // activations of each token, loaded once per 1 KiB window, serve all R rows
-// (NMAT * R row streams) of the wave.  Each lane keeps fp32 partial sums per
-// (row, token); one cross-lane sum per (row, token) at the end.
-//   kDual: g, u rows of w0, w1 -> h = bf16(silu(bf16(s0 g)) * bf16(s1 u)), out [M, rows]
-//   else : rows of w0 -> out = bf16(s0 * y), out [M, rows]
-// U windows of loads are issued before any is used.
-template <bool kDual, int MT, int R, int U, int kWaves>
+// (NMAT * R row streams) of the wave.  Products accumulate two at a time with
+// v_dot2c_f32_bf16 on packed bf16 pairs (the e4m3 weights widened exactly to
+// bf16), so neither operand is unpacked to fp32: at four tokens the unpacking
+// and one FMA per element per token would otherwise make the pass VALU-bound.
+// Each lane keeps fp32 partial sums per (row, token); one cross-lane sum per
+// (row, token) at the end.  Every (row, token) sum sees the same sequence of
+// dot2 steps whatever R and U are, so the passes below agree bit for bit with
+// each other on the same rows.
+//   kSmallDualSilu : g, u rows of w0, w1 -> out[t, row] = bf16(silu(bf16(s0 g)) * bf16(s1 u))
+//   kSmallDualGU   : g, u rows of w0, w1 -> out[t, row] = bf16(s0 g), out[t, rows + row] = bf16(s1 u)
+//   kSmallSingle   : rows of w0 -> out[t, row] = bf16(s0 y), activations x[t, k]
+//   kSmallSingleSiluIn: the same with activations bf16(silu(g) * u) formed on
+//                    the fly from g = x[t, k], u = x[t, K + k] (the fused
+//                    SiLU-input down projection: the product is recomputed by
+//                    every wave that needs it)
+// kBf16W: bf16 weights without scales (8 per 16-byte load, 512 K per window).
+// U windows of loads are issued before any is used.  out_ld / x_ld: row
+// strides in elements.
+enum : int { kSmallDualSilu = 0, kSmallDualGU = 1, kSmallSingle = 2, kSmallSingleSiluIn = 3 };
+
+template <int kMode, bool kBf16W, int MT, int R, int U, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w0,
-    const float* __restrict__ s0, const uint8_t* __restrict__ w1, const float* __restrict__ s1, int M, int K,
-    int rows) {
+    uint16_t* __restrict__ out, int out_ld, const uint16_t* __restrict__ x, int x_ld,
+    const uint8_t* __restrict__ w0, const float* __restrict__ s0, const uint8_t* __restrict__ w1,
+    const float* __restrict__ s1, int M, int K, int rows) {
+    constexpr bool kDual = kMode == kSmallDualSilu || kMode == kSmallDualGU;
+    constexpr bool kSiluIn = kMode == kSmallSingleSiluIn;
     constexpr int NMAT = kDual ? 2 : 1;
+    constexpr int kWB = kBf16W ? 2 : 1;   // weight bytes per element
+    constexpr int kEPL = 16 / kWB;        // elements per lane per window (one 16-byte load)
+    constexpr int kWin = 64 * kEPL;       // elements per window
+    constexpr int kXL = kEPL / 8;         // 16-byte activation loads per token per window (x2 for g and u)
     const int lane = threadIdx.x & 63;
     const int row0 = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;  // rows % R == 0
     if (row0 >= rows) return;
     const uint8_t* wr[R][NMAT];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        wr[r][0] = w0 + (int64_t)(row0 + r) * K;
-        if (kDual) wr[r][NMAT - 1] = w1 + (int64_t)(row0 + r) * K;
+        wr[r][0] = w0 + (int64_t)(row0 + r) * K * kWB;
+        if (kDual) wr[r][NMAT - 1] = w1 + (int64_t)(row0 + r) * K * kWB;
     }
     float acc[R][NMAT][MT];
 #pragma unroll
@@ -221,26 +239,29 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[r][m][t] = 0.0f;
 
-    const int nwin = (K + 1023) / 1024;
+    const int nwin = (K + kWin - 1) / kWin;
     for (int w = 0; w < nwin; w += U) {
-        uint4 wv[U][R][NMAT], xv[U][MT][2];
+        uint4 wv[U][R][NMAT], xv[U][MT][kSiluIn ? 2 : 1][kXL];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // past the row end (a partial last window, or a window past the
             // last): load the row's last 16 bytes, and zero the activations
-            const int k = (w + u) * 1024 + lane * 16;
+            const int k = (w + u) * kWin + lane * kEPL;
             ok[u] = k < K;
-            const int kc = ok[u] ? k : K - 16;
+            const int kc = ok[u] ? k : K - kEPL;
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m) wv[u][r][m] = *reinterpret_cast<const uint4*>(wr[r][m] + kc);
+                for (int m = 0; m < NMAT; ++m) wv[u][r][m] = *reinterpret_cast<const uint4*>(wr[r][m] + kc * kWB);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                const uint16_t* xt = x + (int64_t)min(t, M - 1) * K + kc;
-                xv[u][t][0] = *reinterpret_cast<const uint4*>(xt);
-                xv[u][t][1] = *reinterpret_cast<const uint4*>(xt + 8);
+                const uint16_t* xt = x + (int64_t)min(t, M - 1) * x_ld + kc;
+#pragma unroll
+                for (int p = 0; p < (kSiluIn ? 2 : 1); ++p)
+#pragma unroll
+                    for (int c = 0; c < kXL; ++c)
+                        xv[u][t][p][c] = *reinterpret_cast<const uint4*>(xt + p * K + 8 * c);
             }
         }
         // every load of the U windows is in flight before the first use (the
@@ -248,17 +269,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float xf[MT][16];
+            // activations stay packed bf16 pairs (zero past the row end or the
+            // last token); the fused SiLU input rounds silu(g) * u to bf16 first
+            uint32_t xp[MT][kEPL / 2];
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 const bool use = ok[u] && t < M;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t* q = reinterpret_cast<const uint32_t*>(&xv[u][t][h]);
+                for (int c = 0; c < kXL; ++c) {
+                    const uint32_t* q = reinterpret_cast<const uint32_t*>(&xv[u][t][0][c]);
+                    const uint32_t* qu = reinterpret_cast<const uint32_t*>(&xv[u][t][kSiluIn ? 1 : 0][c]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        xf[t][8 * h + 2 * e] = use ? bf16lo(q[e]) : 0.0f;
-                        xf[t][8 * h + 2 * e + 1] = use ? bf16hi(q[e]) : 0.0f;
+                        uint32_t v = q[e];
+                        if (kSiluIn)
+                            v = pack_bf16x2(silu_mul(bf16lo(q[e]), bf16lo(qu[e])), silu_mul(bf16hi(q[e]), bf16hi(qu[e])));
+                        xp[t][4 * c + e] = use ? v : 0u;
                     }
                 }
             }
@@ -266,21 +292,24 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
+                    // weights as bf16 pairs: e4m3 widens exactly (every e4m3
+                    // value is a bf16 value)
                     const uint32_t* q = reinterpret_cast<const uint32_t*>(&wv[u][r][m]);
-                    float wf[16];
+                    uint32_t wp[kEPL / 2];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const f32x2_t lo = e4m3x2_to_f32(q[e], false), hi = e4m3x2_to_f32(q[e], true);
-                        wf[4 * e] = lo[0];
-                        wf[4 * e + 1] = lo[1];
-                        wf[4 * e + 2] = hi[0];
-                        wf[4 * e + 3] = hi[1];
+                        if (kBf16W) {
+                            wp[e] = q[e];
+                        } else {
+                            wp[2 * e] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16(q[e], false));
+                            wp[2 * e + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16(q[e], true));
+                        }
                     }
 #pragma unroll
                     for (int t = 0; t < MT; ++t) {
                         float a = acc[r][m][t];
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) a = __builtin_fmaf(wf[j], xf[t][j], a);
+                        for (int j = 0; j < kEPL / 2; ++j) a = dot2_bf16(wp[j], xp[t][j], a);
                         acc[r][m][t] = a;
                     }
                 }
@@ -297,18 +326,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int row = row0 + r;
+        const float sa = kBf16W ? 1.0f : s0[row];
+        const float sb = (kBf16W || !kDual) ? 1.0f : s1[row];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             if (t >= M) continue;
-            float o;
-            if (kDual) {
-                const float g = round_bf16(s0[row] * acc[r][0][t]);
-                const float u = round_bf16(s1[row] * acc[r][NMAT - 1][t]);
-                o = silu_mul(g, u);
+            uint16_t* o = out + (int64_t)t * out_ld;
+            if (kMode == kSmallDualSilu) {
+                const float g = round_bf16(sa * acc[r][0][t]);
+                const float u = round_bf16(sb * acc[r][NMAT - 1][t]);
+                o[row] = (uint16_t)(pack_bf16x2(silu_mul(g, u), 0.0f) & 0xffffu);
+            } else if (kMode == kSmallDualGU) {
+                o[row] = (uint16_t)(pack_bf16x2(sa * acc[r][0][t], 0.0f) & 0xffffu);
+                o[rows + row] = (uint16_t)(pack_bf16x2(sb * acc[r][NMAT - 1][t], 0.0f) & 0xffffu);
             } else {
-                o = s0[row] * acc[r][0][t];
+                o[row] = (uint16_t)(pack_bf16x2(sa * acc[r][0][t], 0.0f) & 0xffffu);
             }
-            out[(int64_t)t * rows + row] = (uint16_t)(pack_bf16x2(o, 0.0f) & 0xffffu);
         }
     }
 }
@@ -318,22 +351,64 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
 // more loads in flight per wave than this run slower, the HBM serving many
 // concurrent row streams less well than fewer longer ones).
 constexpr int kSmallDualR = 1, kSmallDualU = 4, kSmallDownR = 2, kSmallDownU = 2, kSmallWaves = 4;
+// the same at three and four tokens, where the activation loads outnumber the
+// weight loads (measured at M = 3, 4 over R in 1..8, U in 1..4): two rows per
+// wave share each activation load, one window in flight
+constexpr int kSmallDualR4 = 2, kSmallDualU4 = 1, kSmallDownR4 = 2, kSmallDownU4 = 1;
 
-template <int MT>
-static hipError_t launch_decode_small(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg,
-                                      const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
-                                      const float* sd, int M, int C, int H, hipStream_t s) {
-    // H and C are multiples of 128: whole waves of rows
-    const int dual_waves = H / kSmallDualR, down_waves = C / kSmallDownR;
-    hipLaunchKernelGGL((gemv_small_kernel<true, MT, kSmallDualR, kSmallDualU, kSmallWaves>),
-                       dim3((dual_waves + kSmallWaves - 1) / kSmallWaves), dim3(64 * kSmallWaves), 0, s, h, x, wg,
-                       sg, wu, su, M, C, H);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemv_small_kernel<false, MT, kSmallDownR, kSmallDownU, kSmallWaves>),
-                       dim3((down_waves + kSmallWaves - 1) / kSmallWaves), dim3(64 * kSmallWaves), 0, s, out, h, wd,
-                       sd, nullptr, nullptr, M, H, C);
+template <int kMode, bool kBf16W, int MT>
+static hipError_t small_pass(uint16_t* out, int out_ld, const uint16_t* x, int x_ld, const uint8_t* w0,
+                             const float* s0, const uint8_t* w1, const float* s1, int M, int K, int rows,
+                             hipStream_t s) {
+    constexpr bool kDual = kMode == kSmallDualSilu || kMode == kSmallDualGU;
+    constexpr bool kWide = MT > 2;
+    constexpr int R = kDual ? (kWide ? kSmallDualR4 : kSmallDualR) : (kWide ? kSmallDownR4 : kSmallDownR);
+    constexpr int U = kDual ? (kWide ? kSmallDualU4 : kSmallDualU) : (kWide ? kSmallDownU4 : kSmallDownU);
+    const int waves = rows / R;  // rows are multiples of 128: whole waves of rows
+    hipLaunchKernelGGL((gemv_small_kernel<kMode, kBf16W, MT, R, U, kSmallWaves>),
+                       dim3((waves + kSmallWaves - 1) / kSmallWaves), dim3(64 * kSmallWaves), 0, s, out, out_ld, x,
+                       x_ld, w0, s0, w1, s1, M, K, rows);
     return hipGetLastError();
+}
+
+// The three arms of the few-token decode (gu: [M, 2H] workspace of the
+// non-split arms).
+template <bool kBf16W, int MT>
+static hipError_t launch_decode_small(uint16_t* out, uint16_t* h, uint16_t* gu, const uint16_t* x,
+                                      const uint8_t* wg, const float* sg, const uint8_t* wu, const float* su,
+                                      const uint8_t* wd, const float* sd, int arm, int M, int C, int H,
+                                      hipStream_t s) {
+    hipError_t e;
+    switch (arm) {
+        case kDecodeSiluInput:
+            e = small_pass<kSmallDualGU, kBf16W, MT>(gu, 2 * H, x, C, wg, sg, wu, su, M, C, H, s);
+            if (e != hipSuccess) return e;
+            return small_pass<kSmallSingleSiluIn, kBf16W, MT>(out, C, gu, 2 * H, wd, sd, nullptr, nullptr, M, H,
+                                                              C, s);
+        case kDecodePerProjection:
+            e = small_pass<kSmallSingle, kBf16W, MT>(gu, 2 * H, x, C, wg, sg, nullptr, nullptr, M, C, H, s);
+            if (e != hipSuccess) return e;
+            e = small_pass<kSmallSingle, kBf16W, MT>(gu + H, 2 * H, x, C, wu, su, nullptr, nullptr, M, C, H, s);
+            if (e != hipSuccess) return e;
+            e = launch_swiglu(h, nullptr, gu, M, H, s);
+            if (e != hipSuccess) return e;
+            return small_pass<kSmallSingle, kBf16W, MT>(out, C, h, H, wd, sd, nullptr, nullptr, M, H, C, s);
+        default:
+            e = small_pass<kSmallDualSilu, kBf16W, MT>(h, H, x, C, wg, sg, wu, su, M, C, H, s);
+            if (e != hipSuccess) return e;
+            return small_pass<kSmallSingle, kBf16W, MT>(out, C, h, H, wd, sd, nullptr, nullptr, M, H, C, s);
+    }
+}
+
+template <bool kBf16W>
+static hipError_t launch_decode_small_m(uint16_t* out, uint16_t* h, uint16_t* gu, const uint16_t* x,
+                                        const uint8_t* wg, const float* sg, const uint8_t* wu, const float* su,
+                                        const uint8_t* wd, const float* sd, int arm, int M, int C, int H,
+                                        hipStream_t s) {
+    if (M == 1) return launch_decode_small<kBf16W, 1>(out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H, s);
+    if (M == 2) return launch_decode_small<kBf16W, 2>(out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H, s);
+    if (M == 3) return launch_decode_small<kBf16W, 3>(out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H, s);
+    return launch_decode_small<kBf16W, 4>(out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H, s);
 }
 
 template <int TB, int RB_DUAL>
@@ -350,13 +425,13 @@ static hipError_t launch_decode_tb(uint16_t* out, uint16_t* h, const uint16_t* x
     return hipGetLastError();
 }
 
-hipError_t launch_decode(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg, const float* sg,
-                         const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd, int M, int C,
-                         int H, hipStream_t s) {
+hipError_t launch_decode(uint16_t* out, uint16_t* h, uint16_t* gu, const uint16_t* x, const uint8_t* wg,
+                         const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd,
+                         int arm, bool bf16_weights, int M, int C, int H, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    if (M == 1) return launch_decode_small<1>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    if (M == 2) return launch_decode_small<2>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
-    if (M <= 4) return launch_decode_small<4>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+    if (bf16_weights)
+        return launch_decode_small_m<true>(out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H, s);
+    if (M <= 4) return launch_decode_small_m<false>(out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H, s);
     if (M <= 16) return launch_decode_tb<1, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
     return launch_decode_tb<2, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
 }

@@ -25,8 +25,11 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr);
 
-hipError_t launch_decode(uint16_t* out, uint16_t* h, const uint16_t* x, const uint8_t* wg, const float* sg,
-                         const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd, int M, int C,
-                         int H, hipStream_t s);
+// Decode arms (the caller has checked: arms other than the split one, and bf16
+// weights, only for M <= 4; gu is a [M, 2H] bf16 workspace for those arms).
+enum : int { kDecodeSplitSilu = 0, kDecodeSiluInput = 1, kDecodePerProjection = 2 };
+hipError_t launch_decode(uint16_t* out, uint16_t* h, uint16_t* gu, const uint16_t* x, const uint8_t* wg,
+                         const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd,
+                         int arm, bool bf16_weights, int M, int C, int H, hipStream_t s);
 
 }  // namespace ffn
