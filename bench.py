@@ -99,16 +99,24 @@ def measured_traffic(key, src):
 # dominant kernel per workload: traffic.json key, its source file, the kernel
 # name fragments whose per-dispatch counters make up one launch of the entry
 # point, and the algorithmic bytes of that launch
-def traffic_spec(workload):
+def traffic_spec(workload, known_h_absmax=False):
+    """(traffic.json key, source file, kernel-name fragments of one launch,
+    description, algorithmic bytes of one launch) for the dominant kernel."""
     from transformer_ffn_block_residual_amd import workloads as W
     w = W.WORKLOADS[workload]
     N, C, H = w.N, w.C, w.H
     if workload == "decode":
-        return ("decode_decode", "decode.hip", ["decode_kernel<true", "decode_kernel<false"],
-                f"decode_kernel<true,...> + decode_kernel<false,...> (one ffn_decode_gemv), M=1 C={C} H={H}",
+        return ("decode_decode", "decode.hip", ["gemv_small_kernel<0, false, 1,", "gemv_small_kernel<2, false, 1,"],
+                f"gemv_small_kernel<dual SiLU> + gemv_small_kernel<single> (one ffn_decode_gemv), M=1 C={C} H={H}",
                 3 * H * C + (2 * H + C) * 4 + 2 * (C + H) * 2)
     elt = 1 if w.fp8 else 2
-    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{'true' if w.fp8 else 'false'}, true>"],
+    fp8 = "true" if w.fp8 else "false"
+    if known_h_absmax:
+        # reads x and w, writes the e4m3 codes of h
+        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true>"],
+                f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation) of ffn_gateup_swiglu_quant, "
+                f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H)
+    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false>"],
             f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
             N * C * elt + 2 * H * C * elt + N * H * 2)
 
@@ -118,7 +126,7 @@ def ingest_pmc(a):
     rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
     scaled by what the counter reads for the 1 GiB calibration copy."""
     import csv
-    key, src, frags, desc, algo = traffic_spec(a.workload)
+    key, src, frags, desc, algo = traffic_spec(a.workload, a.known_h_absmax)
     rec = {"kernel": desc, "src": f"transformer_ffn_block_residual_amd/csrc/{src}", "src_sha256": src_digest(src)}
     total = 0.0
     for counter, path, truth_kb in (("FETCH_SIZE", a.ingest_pmc[0], 1 << 20), ("WRITE_SIZE", a.ingest_pmc[1], 1 << 20)):
