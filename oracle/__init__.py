@@ -48,6 +48,15 @@ from .ffn import (
     decode_gemv_bf16,
     block_forward,
 )
+from .backward import (
+    sigmoid,
+    swiglu_bwd,
+    rmsnorm_bwd,
+    transpose,
+    matmul_tn,
+    linear_bwd,
+    block_backward,
+)
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "bf16_round", "e4m3_decode",
@@ -55,4 +64,5 @@ __all__ = [
     "absmax_of", "scales_from_absmax", "quant_absmax",
     "quant_rows", "gemm_bf16", "gemm_fp8", "silu", "swiglu", "gateup", "down",
     "decode_dual", "decode_down", "decode_gemv", "decode_gemv_bf16", "block_forward",
+    "sigmoid", "swiglu_bwd", "rmsnorm_bwd", "transpose", "matmul_tn", "linear_bwd", "block_backward",
 ]

@@ -269,8 +269,8 @@ def block_forward(inp, addend, w_norm, w_gu, w_d, eps, fp8=False):
     """
     out = {}
     r, y, rstd, am_y = rmsnorm_fwd(inp, addend, w_norm, eps)
-    out.update(residual=r, y=y, rstd=rstd, absmax_y=am_y)
     r_vals = inp if r is None else r
+    out.update(residual=r, rms_input=r_vals, y=y, rstd=rstd, absmax_y=am_y)
     if not fp8:
         gu = gemm_bf16(y, w_gu)
         h, am_h = swiglu(gu)

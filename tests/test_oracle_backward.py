@@ -1,0 +1,302 @@
+"""Pins for the oracle's backward steps.
+
+The derivatives are checked against torch's CPU autograd in float64 (an
+independent differentiation of the forward formulas), central finite
+differences, closed forms at special points and invariants of RMSNorm; the
+FP8 weight-gradient and data-gradient products against the bf16 path on
+e4m3-valued operands with unit scales, and against exact scaling laws.
+"""
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+from oracle import codecs as K
+from transformer_ffn_block_residual_amd import workloads as W
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def t64(bits):
+    return torch.from_numpy(K.bf16_bits_to_f64(bits))
+
+
+def bf16_of(t):
+    """A float64 torch tensor rounded to bf16 bits by torch (via fp32: may
+    round twice, so comparisons allow one ulp on rare elements)."""
+    return t.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp_diff(a_bits, b_bits):
+    a = np.asarray(a_bits).astype(np.int32)
+    b = np.asarray(b_bits).astype(np.int32)
+    ka = np.where(a & 0x8000, -(a & 0x7FFF), a)
+    kb = np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ka - kb)
+
+
+def rand_bits(shape, std, seed):
+    rng = np.random.default_rng(seed)
+    return W.to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def rel(got, ref):
+    g, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    return np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-300)
+
+
+# ----------------------------------------------------------------------------- SwiGLU backward
+
+def test_swiglu_bwd_matches_torch_autograd():
+    N, H = 33, 96
+    gu = rand_bits((N, 2 * H), 3.0, 1)
+    dh = rand_bits((N, H), 1.0, 2)
+    g = t64(gu[:, :H]).requires_grad_()
+    u = t64(gu[:, H:]).requires_grad_()
+    (F.silu(g) * u).backward(t64(dh))
+    want = np.concatenate([bf16_of(g.grad), bf16_of(u.grad)], axis=1)
+    got, am = O.swiglu_bwd(dh, gu)
+    d = ulp_diff(got, want)
+    assert d.max() <= 1 and np.mean(d != 0) < 2e-3
+    assert am == np.max(np.abs(K.bf16_bits_to_f64(got)))
+
+
+def test_swiglu_bwd_finite_differences():
+    # d/dg and d/du of silu(g) * u by central differences in float64
+    g = np.linspace(-12, 12, 97)
+    u = np.cos(g) + 2
+    eps = 1e-6
+    silu = lambda x: x / (1 + np.exp(-x))
+    fd_g = (silu(g + eps) - silu(g - eps)) * u / (2 * eps)
+    fd_u = silu(g)
+    gu = W.to_bf16_bits(np.concatenate([g, u]).astype(np.float32)[None, :])
+    gv = K.bf16_bits_to_f64(gu)[0]
+    # rebuild the differences on the bf16 grid the oracle sees
+    gb, ub = gv[:97], gv[97:]
+    fd_g = (silu(gb + eps) - silu(gb - eps)) * ub / (2 * eps)
+    fd_u = silu(gb)
+    ones = W.to_bf16_bits(np.ones((1, 97), np.float32))
+    dgu, _ = O.swiglu_bwd(ones, gu)
+    got = K.bf16_bits_to_f64(dgu)[0]
+    assert np.allclose(got[:97], fd_g, rtol=2 ** -8, atol=1e-9)
+    assert np.allclose(got[97:], fd_u, rtol=2 ** -8, atol=1e-9)
+
+
+def test_swiglu_bwd_special_points_and_placement():
+    H = 4
+    g = np.array([0.0, 40.0, -40.0, 1.0], np.float32)
+    u = np.array([3.0, 2.0, 5.0, 0.0], np.float32)
+    gu = W.to_bf16_bits(np.concatenate([g, u])[None, :])
+    dh = W.to_bf16_bits(np.array([[2.0, 0.5, 1.0, 1.0]], np.float32))
+    dgu, _ = O.swiglu_bwd(dh, gu)
+    v = K.bf16_bits_to_f64(dgu)[0]
+    # g = 0: silu'(0) = 1/2, silu(0) = 0
+    assert v[0] == 2.0 * 3.0 * 0.5 and v[H + 0] == 0.0
+    # large g: silu' -> 1, silu(g) -> g
+    assert v[1] == 0.5 * 2.0 and v[H + 1] == 0.5 * 40.0
+    # very negative g: both vanish (to bf16 precision)
+    assert abs(v[2]) < 1e-15 and abs(v[H + 2]) < 1e-15
+    # u = 0: no gate gradient
+    assert v[3] == 0.0
+    # one-hot dh at column j touches exactly columns j and H + j
+    N, H2 = 3, 8
+    gu2 = rand_bits((N, 2 * H2), 1.0, 3)
+    for j in range(H2):
+        oh = np.zeros((N, H2), np.float32)
+        oh[:, j] = 1.0
+        d, _ = O.swiglu_bwd(W.to_bf16_bits(oh), gu2)
+        nz = np.nonzero(np.any(K.bf16_bits_to_f64(d) != 0, axis=0))[0]
+        assert set(nz) <= {j, H2 + j}
+
+
+# ----------------------------------------------------------------------------- RMSNorm backward
+
+def _torch_rmsnorm_grads(r_bits, w_bits, dy_bits, eps):
+    r = t64(r_bits).requires_grad_()
+    w = t64(w_bits).requires_grad_()
+    y = F.rms_norm(r, (r.shape[-1],), weight=w, eps=eps)
+    y.backward(t64(dy_bits))
+    return r.grad, w.grad
+
+
+def test_rmsnorm_bwd_matches_torch_autograd():
+    N, C, eps = 29, 384, 1e-5
+    d = W.block_inputs(N, C, 128, seed=7)
+    r = O.residual_add(d["inp"], d["addend"])
+    rstd = O.rms_rstd(r, eps)
+    dy = rand_bits((N, C), 1.0, 4)
+    dres = rand_bits((N, C), 0.5, 5)
+    dw0 = np.random.default_rng(6).standard_normal(C).astype(np.float32)
+    dinp, dw, am = O.rmsnorm_bwd(dres, dy, r, d["w_norm"], rstd, dw0)
+    gr, gw = _torch_rmsnorm_grads(r, d["w_norm"], dy, eps)
+    want = bf16_of(t64(dres) + gr)
+    dd = ulp_diff(dinp, want)
+    assert dd.max() <= 1 and np.mean(dd != 0) < 5e-3
+    assert rel(dw, dw0.astype(np.float64) + gw.numpy()) < 1e-6
+    assert am == np.max(np.abs(K.bf16_bits_to_f64(dinp)))
+
+
+def test_rmsnorm_bwd_is_orthogonal_to_the_input_without_eps():
+    # with eps = 0, RMSNorm is invariant to scaling its input row, so the input
+    # gradient is orthogonal to the row: sum_j dx_j r_j = 0
+    N, C = 16, 512
+    r = rand_bits((N, C), 2.0, 8)
+    w = W.to_bf16_bits(np.random.default_rng(9).uniform(0.5, 1.5, C).astype(np.float32))
+    dy = rand_bits((N, C), 1.0, 10)
+    rstd = O.rms_rstd(r, 0.0)
+    zero = np.zeros((N, C), np.uint16)
+    dinp, _, _ = O.rmsnorm_bwd(zero, dy, r, w, rstd)
+    dx, rv = K.bf16_bits_to_f64(dinp), K.bf16_bits_to_f64(r)
+    dot = np.sum(dx * rv, axis=1)
+    mag = np.sum(np.abs(dx * rv), axis=1)
+    assert np.all(np.abs(dot) <= 2 ** -7 * mag)
+
+
+def test_rmsnorm_bwd_weight_gradient_closed_form_and_accumulation():
+    # unit rows scaled so rstd = 1 exactly: xh = r, dweight = sum_n dy * r
+    C = 256
+    r = W.to_bf16_bits(np.where(np.arange(C) % 2 == 0, 1.0, -1.0).astype(np.float32)[None, :].repeat(3, 0))
+    rstd = O.rms_rstd(r, 0.0)
+    assert np.all(rstd == 1.0)
+    dy = rand_bits((3, C), 1.0, 11)
+    w = W.to_bf16_bits(np.ones(C, np.float32))
+    _, dw1, _ = O.rmsnorm_bwd(np.zeros((3, C), np.uint16), dy, r, w, rstd)
+    assert np.array_equal(dw1, np.sum(K.bf16_bits_to_f64(dy) * K.bf16_bits_to_f64(r), axis=0).astype(np.float32))
+    _, dw2, _ = O.rmsnorm_bwd(np.zeros((3, C), np.uint16), dy, r, w, rstd, dw1)
+    assert np.array_equal(dw2, (2.0 * dw1.astype(np.float64)).astype(np.float32))
+
+
+def test_rmsnorm_bwd_zero_upstream_passes_the_residual_gradient():
+    N, C = 5, 128
+    r = rand_bits((N, C), 1.0, 12)
+    dres = rand_bits((N, C), 1.0, 13)
+    w = W.to_bf16_bits(np.ones(C, np.float32))
+    dinp, dw, am = O.rmsnorm_bwd(dres, np.zeros((N, C), np.uint16), r, w, O.rms_rstd(r, 1e-5))
+    assert np.array_equal(dinp, dres) and not np.any(dw)
+
+
+# ----------------------------------------------------------------------------- GEMMs of the backward
+
+def test_matmul_tn_and_accumulate():
+    a, b = rand_bits((7, 48), 1.0, 14), rand_bits((5, 48), 1.0, 15)
+    want = bf16_of(t64(a) @ t64(b).T)
+    assert ulp_diff(O.matmul_tn(a, b), want).max() <= 1
+    acc = rand_bits((7, 5), 4.0, 16)
+    want = bf16_of(t64(a) @ t64(b).T + t64(acc))
+    assert ulp_diff(O.matmul_tn(a, b, accumulate=acc), want).max() <= 1
+    # integer-valued operands: every partial sum exact, so the result is unique
+    rng = np.random.default_rng(17)
+    ai = W.to_bf16_bits(rng.integers(-4, 5, (9, 64)).astype(np.float32))
+    bi = W.to_bf16_bits(rng.integers(-4, 5, (6, 64)).astype(np.float32))
+    exact = (K.bf16_bits_to_f64(ai) @ K.bf16_bits_to_f64(bi).T)
+    assert np.array_equal(K.bf16_bits_to_f64(O.matmul_tn(ai, bi)), exact)
+
+
+def test_linear_bwd_bf16_matches_torch_autograd():
+    N, C, OC = 21, 64, 40
+    x, w, dy = rand_bits((N, C), 1.0, 18), rand_bits((OC, C), 0.1, 19), rand_bits((N, OC), 1.0, 20)
+    xt, wt = t64(x).requires_grad_(), t64(w).requires_grad_()
+    (xt @ wt.T).backward(t64(dy))
+    res = O.linear_bwd(dy, x, w)
+    assert ulp_diff(res["dx"], bf16_of(xt.grad)).max() <= 1
+    assert ulp_diff(res["dw"], bf16_of(wt.grad)).max() <= 1
+    acc = rand_bits((OC, C), 1.0, 21)
+    res2 = O.linear_bwd(dy, x, w, dw_acc=acc)
+    assert ulp_diff(res2["dw"], bf16_of(wt.grad + t64(acc))).max() <= 1
+
+
+def _e4m3_valued(shape, seed):
+    """bf16 bits of e4m3 values whose abs-max is 448 (so the per-tensor scale
+    is 1 and quantisation returns the same values)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x7F, shape).astype(np.uint8) | (rng.integers(0, 2, shape).astype(np.uint8) << 7)
+    codes.flat[0] = 0x7E
+    return W.to_bf16_bits(K.e4m3_decode(codes).astype(np.float32))
+
+
+def test_linear_bwd_fp8_equals_bf16_on_e4m3_values_with_unit_scales():
+    N, C, OC = 24, 64, 32
+    x, w, dy = _e4m3_valued((N, C), 22), _e4m3_valued((OC, C), 23), _e4m3_valued((N, OC), 24)
+    qx, sx, _ = O.quant_absmax(x)
+    qw, sw, _ = O.quant_absmax(w)
+    assert sx == 1 and sw == 1
+    f8 = O.linear_bwd(dy, x, w, fp8=True, qx=qx, sx=sx, qw=qw, sw=sw)
+    b16 = O.linear_bwd(dy, x, w)
+    assert f8["sdy"] == 1
+    assert np.array_equal(f8["dx"], b16["dx"]) and np.array_equal(f8["dw"], b16["dw"])
+
+
+def test_linear_bwd_fp8_scales_exactly_with_the_gradient():
+    N, C, OC = 16, 64, 32
+    x, w = rand_bits((N, C), 1.0, 25), rand_bits((OC, C), 0.1, 26)
+    dy = rand_bits((N, OC), 1.0, 27)
+    dy2 = O.f64_to_bf16_bits(2.0 * K.bf16_bits_to_f64(dy))
+    qx, sx, _ = O.quant_absmax(x)
+    qw, sw, _ = O.quant_absmax(w)
+    a = O.linear_bwd(dy, x, w, fp8=True, qx=qx, sx=sx, qw=qw, sw=sw)
+    b = O.linear_bwd(dy2, x, w, fp8=True, qx=qx, sx=sx, qw=qw, sw=sw)
+    assert np.array_equal(a["qdy"], b["qdy"]) and b["sdy"] == 2 * a["sdy"]
+    for k in ("dx", "dw"):
+        assert np.array_equal(2.0 * K.bf16_bits_to_f64(a[k]), K.bf16_bits_to_f64(b[k]))
+
+
+# ----------------------------------------------------------------------------- the block
+
+def _torch_block_grads(d, eps, d_out):
+    """Autograd of the unrounded block in float64: r -> RMSNorm -> gate/up ->
+    SwiGLU -> down; the block output's gradient also passes the residual."""
+    r = t64(O.residual_add(d["inp"], d["addend"])).requires_grad_()
+    wn = t64(d["w_norm"]).requires_grad_()
+    wgu = t64(d["w_gu"]).requires_grad_()
+    wd = t64(d["w_d"]).requires_grad_()
+    y = F.rms_norm(r, (r.shape[-1],), weight=wn, eps=eps)
+    gu = y @ wgu.T
+    H = wgu.shape[0] // 2
+    h = F.silu(gu[:, :H]) * gu[:, H:]
+    out = r + h @ wd.T
+    out.backward(t64(d_out))
+    return {"d_residual": r.grad, "dw_norm": wn.grad, "dw_gu": wgu.grad, "dw_d": wd.grad}
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_block_backward_matches_torch_autograd(fp8):
+    # weights ~N(0, 0.1) so the FFN branch's share of the residual gradient
+    # is as large as the pass-through's and an error in it shows
+    N, C, H, eps = 48, 128, 96, 1e-5
+    d = W.block_inputs(N, C, H, seed=31, w_std=0.1)
+    d_out = rand_bits((N, C), 1.0, 32)
+    fwd = O.block_forward(d["inp"], d["addend"], d["w_norm"], d["w_gu"], d["w_d"], eps, fp8=fp8)
+    bwd = O.block_backward(fwd, d_out, d["w_norm"], d["w_gu"], d["w_d"], fp8=fp8)
+    ref = _torch_block_grads(d, eps, d_out)
+    # bf16 chain: a few bf16 roundings per value (measured 0.5%); FP8: e4m3
+    # codes of every GEMM operand, gradients included (measured 5-8%), both
+    # against each tensor's max
+    tol = 2e-2 if not fp8 else 0.12
+    for k in ("d_residual", "dw_gu", "dw_d"):
+        assert rel(K.bf16_bits_to_f64(bwd[k]), ref[k].numpy()) < tol, k
+    assert rel(bwd["dw_norm"], ref["dw_norm"].numpy()) < tol
+    branch = K.bf16_bits_to_f64(bwd["d_residual"]) - K.bf16_bits_to_f64(d_out)
+    assert rel(branch, ref["d_residual"].numpy() - K.bf16_bits_to_f64(d_out)) < tol
+    assert rel(K.bf16_bits_to_f64(bwd["dh"]), K.bf16_bits_to_f64(d_out) @ K.bf16_bits_to_f64(d["w_d"])) < tol
+
+
+def test_block_backward_zero_gate_and_accumulators():
+    N, C, H, eps = 16, 128, 64, 1e-5
+    d = W.block_inputs(N, C, H, seed=33)
+    wz = K.bf16_bits_to_f64(d["w_gu"]).copy()
+    wz[:H] = 0.0
+    w_gu = O.f64_to_bf16_bits(wz)
+    d_out = rand_bits((N, C), 1.0, 34)
+    fwd = O.block_forward(d["inp"], d["addend"], d["w_norm"], w_gu, d["w_d"], eps)
+    bwd = O.block_backward(fwd, d_out, d["w_norm"], w_gu, d["w_d"])
+    # h = 0: no down-weight gradient and no up-half gradient (du = dh * silu(0) = 0)
+    assert not np.any(K.bf16_bits_to_f64(bwd["dw_d"]))
+    assert not np.any(K.bf16_bits_to_f64(bwd["dgu"])[:, H:])
+    # accumulators add to the fresh gradients before the one rounding
+    acc = {"dw_d": rand_bits((C, H), 1.0, 35), "dw_gu": rand_bits((2 * H, C), 1.0, 36),
+           "dw_norm": np.ones(C, np.float32)}
+    bwd2 = O.block_backward(fwd, d_out, d["w_norm"], w_gu, d["w_d"], acc=acc)
+    assert np.array_equal(bwd2["dw_d"], acc["dw_d"])
+    assert np.array_equal(bwd2["dw_norm"], (bwd["dw_norm"].astype(np.float64) + 1.0).astype(np.float32))
