@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--decode-arm", default="split", choices=list(DECODE_ARMS),
                    help="decode workload: which arm of the decode FFN runs")
     p.add_argument("--decode-m", type=int, default=1, help="decode workload: tokens per call (1..4 off split)")
+    p.add_argument("--backward", action="store_true",
+                   help="block workloads: time the FFN block backward (after one forward) instead of the forward")
     p.add_argument("--known-h-absmax", action="store_true",
                    help="FP8 block workloads: quantise h in the gate+up epilogue with the previous step's abs-max "
                         "(ffn_gateup_swiglu_quant, the recompute form) instead of bf16 h + ffn_quant_absmax")
@@ -446,6 +448,125 @@ def bench_block(a, torch, np, B, block, W):
     return out
 
 
+BWD_PHASES = {
+    # phase: (kind, work) with work in flop ("mfma") or bytes ("hbm") given N, C, H, element bytes e
+    "quant_dout": ("hbm", lambda N, C, H, e: 3 * N * C),
+    "transpose_w_down": ("hbm", lambda N, C, H, e: 2 * C * H * e),
+    "dx_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
+    "transpose_down_operands": ("hbm", lambda N, C, H, e: (2 + e) * N * C + 2 * N * H * e),
+    "dw_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
+    "swiglu_bwd": ("hbm", lambda N, C, H, e: 10 * N * H),
+    "quant_dgu": ("hbm", lambda N, C, H, e: 6 * N * H),
+    "transpose_w_up": ("hbm", lambda N, C, H, e: 4 * C * H * e),
+    "dx_up": ("mfma", lambda N, C, H, e: 4 * N * C * H),
+    "transpose_up_operands": ("hbm", lambda N, C, H, e: (2 + e) * 2 * N * H + 2 * N * C * e),
+    "dw_up": ("mfma", lambda N, C, H, e: 4 * N * C * H),
+    "rmsnorm_bwd": ("hbm", lambda N, C, H, e: 5 * N * C * 2 + N * 4),
+}
+
+
+def cpu_backward_sample(w, d, rows):
+    """The oracle forward + backward of the block over the first `rows` token
+    rows (full weights; FP8 weights quantised beforehand, as in the forward
+    sample); only the backward is timed."""
+    import oracle as O
+    import numpy as np
+    d_out = _bwd_dout(np, w, rows)
+    fwd = O.block_forward(d["inp"][:rows], d["addend"][:rows], d["w_norm"], d["w_gu"], d["w_d"], w.eps, fp8=w.fp8)
+    t0 = time.perf_counter()
+    O.block_backward(fwd, d_out, d["w_norm"], d["w_gu"], d["w_d"], fp8=w.fp8)
+    dt = time.perf_counter() - t0
+    flops = 12.0 * rows * w.C * w.H
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"block backward over the first {rows} of {w.N} token rows (full weights); {dt:.2f} s wall"}
+
+
+def _bwd_dout(np, w, rows):
+    """The incoming gradient of the block output: ~N(0, 1) bf16, seeded."""
+    from transformer_ffn_block_residual_amd import workloads as W
+    g = np.random.default_rng([w.seed, 99]).standard_normal((rows, w.C), dtype=np.float32)
+    return W.to_bf16_bits(g)
+
+
+def bench_backward(a, torch, np, B, block, W):
+    w = W.WORKLOADS[a.workload]
+    N, C, H = w.N, w.C, w.H
+    dt = "fp8" if w.fp8 else "bf16"
+    e = 1 if w.fp8 else 2
+    print(f"[bench] generating {a.workload} inputs (seed {w.seed}) for the backward", file=sys.stderr, flush=True)
+    d = W.block_inputs(N, C, H, w.seed, w.w_std, w.outliers)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    pre = block.PrefillBlock(N, C, H, w.eps, w.fp8)
+    pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+    bb = block.BackwardBlock(pre, in_place=False)
+    bb.forward(dev(d["inp"]), dev(d["addend"]))
+    d_out = dev(_bwd_dout(np, w, N))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    names = list(BWD_PHASES)
+
+    def step(i, tm, stream=stream):
+        if tm is None:
+            bb.backward(d_out, stream)
+            return
+        marks = [tm.mark()]
+        seen = []
+
+        def mark(label):
+            marks.append(tm.mark())
+            seen.append(label)
+        bb.backward(d_out, stream, mark)
+        tm.add("step", marks[0], marks[-1])
+        for k, label in enumerate(seen):
+            tm.add(label, marks[k], marks[k + 1])
+
+    ms, km = run_steps(torch, stream, step, a, marks_per_step=16)
+    spread = run_steps.spread
+
+    def issue(cur):
+        for i in range(a.steps):
+            step(i, None, cur)
+    graph_ms = graph_step_ms(torch, issue, a.steps)
+    peak = PEAK[dt]
+    kernels = {}
+    for name in names:
+        if name not in km:
+            continue
+        kind, work = BWD_PHASES[name]
+        wv = work(N, C, H, e)
+        if kind == "mfma":
+            tf = wv / (km[name] * 1e-3) / 1e12
+            kernels[name] = {"ms": km[name], "TFLOP/s": tf, "frac_peak": tf / peak}
+        else:
+            kernels[name] = {"ms": km[name], "GB/s": wv / km[name] / 1e6,
+                             "frac_hbm": wv / km[name] / 1e6 / PEAK_HBM_GBS}
+    flops = 12.0 * N * C * H
+    dw_tf = kernels["dw_up"]["TFLOP/s"]
+    out = {
+        "metric": METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": f"FFN block backward of the {a.workload} workload: N={N} C={C} H={H}, "
+                               + ("FP8 (per-tensor e4m3 weights, activations and gradients)" if w.fp8 else "bf16")
+                               + "; down and up backward_qmm (data and weight gradients), SwiGLU and RMSNorm "
+                                 "backward, weight transposes included",
+                   "N": N, "C": C, "H": H, "seed": w.seed, "backward": True},
+        "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({'e4m3' if w.fp8 else 'bf16'}, accumulate): "
+                                                 "the up projection's weight gradient [2H, C], K = N",
+                     "achieved": dw_tf, "peak": peak, "unit": "TFLOP/s", "frac": dw_tf / peak, "traffic": None},
+        "kernels": kernels,
+        "spread_ms": spread,
+        "ms_per_step_in_hip_graph": graph_ms,
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_backward_sample(w, d, a.cpu_rows or min(N, 256))
+    return out
+
+
 def bench_decode(a, torch, np, B, block, W):
     w = W.WORKLOADS["decode"]
     M, C, H = a.decode_m, w.C, w.H
@@ -555,6 +676,8 @@ def main():
     torch.cuda.set_device(0)
     if a.workload == "decode":
         out = bench_decode(a, torch, np, B, block, W)
+    elif a.backward:
+        out = bench_backward(a, torch, np, B, block, W)
     else:
         out = bench_block(a, torch, np, B, block, W)
     if a.copy_calibration:

@@ -208,6 +208,74 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
                                   const void* w_gate, const void* w_up, const void* w_down,
                                   int64_t M, int64_t C, int64_t H, hipStream_t stream);
 
+/* ------------------------------------------------------------------ backward
+ * The FFN half of [llmq model] LLamaModel::_backward_block, as the calls it
+ * is made of: backward_qmm through the down projection, swiglu_backward,
+ * backward_qmm through the [2H, C] up weight, rmsnorm_backward.  backward_qmm
+ * with e4m3 weights quantises the output gradient with its abs-max,
+ * transposes the weight, the input codes and the gradient codes, and runs two
+ * scaled TN matmuls; ffn_matmul_tn is that matmul (with bf16 operands as well)
+ * and ffn_transpose / ffn_quant_transpose the transposes. */
+
+/* TN matmul: out[m,n] = bf16(acc + sum_k a[m,k] * b[n,k] (* a_scale * b_scale
+ * for E4M3)), acc = out[m,n] when accumulate != 0 (the accumulate_gradient flag
+ * of backward_qmm: one rounding of the fp32 sum), else 0.  [llmq model]
+ * backward_qmm, matmul(..., EMMTranspose::TN, accumulate_gradient).
+ * out: bf16 [M,N]; a: [M,K], b: [N,K], both bf16 or both e4m3; scales fp32 [1]
+ * (E4M3 only).  Supported: K % 128 == 0, N % 128 == 0, any M >= 0; out must
+ * not alias a or b. */
+ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale,
+                           const void* b, const float* b_scale, ffn_dtype_t dtype,
+                           int accumulate, int64_t M, int64_t N, int64_t K,
+                           hipStream_t stream);
+
+/* Transpose: out[c, r] = in[r, c] for r < rows, and 0 for rows <= r < ld_out
+ * (zero padding that rounds a token count up to ffn_matmul_tn's K granularity).
+ * [llmq model] backward_qmm, transpose(weight_tp, ...), transpose(activation_tp,
+ * ...), transpose(grad_tp, ...).  in: [rows, cols]; out: [cols, ld_out];
+ * elt_bytes 2 (bf16) or 1 (e4m3 codes).  Supported: cols % 16 == 0,
+ * ld_out % 16 == 0, ld_out >= rows; out must not alias in. */
+ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols,
+                           int64_t ld_out, int elt_bytes, hipStream_t stream);
+
+/* Quantise with a known abs-max and transpose in one pass: q_t[c, r] =
+ * e4m3(x[r, c] * 448 / absmax), *scale = absmax / 448 (1 and 1 for absmax 0),
+ * zero codes for rows <= r < ld_out.  [llmq model] backward_qmm,
+ * quantize_and_transpose_with_abs_max.  x: bf16 [rows, cols]; q_t: e4m3
+ * [cols, ld_out]; absmax: fp32 [1] (device, read).  Constraints as
+ * ffn_transpose. */
+ffn_status_t ffn_quant_transpose(uint8_t* q_t, float* scale, const void* x,
+                                 const float* absmax, int64_t rows, int64_t cols,
+                                 int64_t ld_out, hipStream_t stream);
+
+/* SwiGLU backward.  [llmq model] _backward_block, swiglu_backward(DMlpUp,
+ * DSwiGLU, MlpUp, DMlpUp abs-max, B, T, D).  With g = gu[n,j], u = gu[n,H+j],
+ * s = 1/(1+exp(-g)):
+ *   dgu[n,j]   = bf16(dh[n,j] * u * s * (1 + g * (1 - s)))
+ *   dgu[n,H+j] = bf16(dh[n,j] * g * s)
+ * dgu: bf16 [N,2H] (may be gu itself: the trainer writes it over MlpUp);
+ * dh: bf16 [N,H]; absmax (nullable) receives max |dgu|.  Supported: H % 8 == 0;
+ * dgu must not alias dh. */
+ffn_status_t ffn_swiglu_bwd(void* dgu, float* absmax, const void* dh, const void* gu,
+                            int64_t N, int64_t H, hipStream_t stream);
+
+/* RMSNorm backward with the saved rstd, added to the residual stream's
+ * gradient.  [llmq model] _backward_block, rmsnorm_backward(DResAtt, LN2_w
+ * grad, scratch, DResFFN, DLN2, ResidualAtt, LN2_w, LN2_Rstd, DResAtt abs-max,
+ * B, T, C).  With xh = r * rstd, gy = dy * w, m = sum_j gy_j xh_j / C:
+ *   dinp[n,j]  = bf16(dresidual[n,j] + rstd_n * (gy_j - xh_j * m))
+ *   dweight[j] += sum_n dy[n,j] * xh[n,j]      (fp32, fixed summation order)
+ * dinp, dresidual, dy, r: bf16 [N,C] (dinp may be dresidual); weight: bf16 [C];
+ * rstd: fp32 [N]; dweight: fp32 [C], accumulated; absmax (nullable) receives
+ * max |dinp|; scratch: device memory of ffn_rmsnorm_bwd_scratch_bytes(N, C)
+ * bytes (the per-wave partial weight gradients; its size is not checked).
+ * Supported: C % 8 == 0, C <= 8192. */
+int64_t ffn_rmsnorm_bwd_scratch_bytes(int64_t N, int64_t C);
+ffn_status_t ffn_rmsnorm_bwd(void* dinp, float* dweight, float* scratch,
+                             const void* dresidual, const void* dy, const void* r,
+                             const void* weight, const float* rstd, float* absmax,
+                             int64_t N, int64_t C, hipStream_t stream);
+
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
 const char* ffn_last_error(void);
 

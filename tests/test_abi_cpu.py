@@ -23,7 +23,7 @@ MIS = 0x10004        # misaligned fake address
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:ffn_status_t|const char\*)\s+(ffn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:ffn_status_t|const char\*|int64_t)\s+(ffn_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
               "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16",
-              "ffn_last_error", "ffn_version"]:
+              "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
+              "ffn_rmsnorm_bwd_scratch_bytes", "ffn_last_error", "ffn_version"]:
         assert n in names
 
 
@@ -139,6 +140,42 @@ def test_decode_arm_and_bf16_validation(lib):
     assert g(A, B, D, A, A, A, 1, 200, 768, None) == UNSUPPORTED                      # C % 128
     assert g(A, A, D, A, A, A, 1, 256, 768, None) == INVALID                          # h aliases out
     assert g(A, B, D, A, A, A, 1, 32768, 32768, None) == UNSUPPORTED                  # > 2 GiB of weights
+
+
+def test_backward_validation(lib):
+    B_, C_, D = 0x20000, 0x30000, 0x40000
+    m = lib.ffn_matmul_tn  # out, a, sa, b, sb, dtype, accumulate, M, N, K
+    assert m(None, B_, None, C_, None, 0, 0, 64, 256, 128, None) == INVALID
+    assert m(A, B_, None, C_, None, 1, 0, 64, 256, 128, None) == INVALID           # E4M3 without scales
+    assert m(A, B_, None, C_, None, 5, 0, 64, 256, 128, None) == INVALID           # unknown dtype
+    assert m(A, B_, None, C_, None, 0, 0, 64, 200, 128, None) == UNSUPPORTED       # N % 128
+    assert m(A, B_, None, C_, None, 0, 0, 64, 256, 96, None) == UNSUPPORTED        # K % 128
+    assert m(A, A, None, C_, None, 0, 0, 64, 256, 128, None) == INVALID            # out aliases a
+    assert m(A, B_, None, MIS, None, 0, 0, 64, 256, 128, None) == UNSUPPORTED      # misaligned b
+    assert m(A, B_, None, C_, None, 0, 0, -1, 256, 128, None) == INVALID
+    t = lib.ffn_transpose  # out, in, rows, cols, ld_out, elt
+    assert t(A, B_, 37, 64, 48, 3, None) == INVALID                                # element size
+    assert t(A, B_, 37, 64, 32, 2, None) == INVALID                                # ld_out < rows
+    assert t(A, B_, 37, 40, 48, 2, None) == UNSUPPORTED                            # cols % 16
+    assert t(A, B_, 37, 64, 40, 2, None) == UNSUPPORTED                            # ld_out % 16
+    assert t(A, A, 37, 64, 48, 2, None) == INVALID                                 # in place
+    assert t(A, MIS, 37, 64, 48, 1, None) == UNSUPPORTED
+    q = lib.ffn_quant_transpose  # q_t, scale, x, absmax, rows, cols, ld_out
+    assert q(A, B_, C_, None, 37, 64, 48, None) == INVALID                         # no abs-max
+    assert q(A, B_, C_, D, 37, 64, 32, None) == INVALID
+    g = lib.ffn_swiglu_bwd  # dgu, absmax, dh, gu, N, H
+    assert g(A, None, A, C_, 4, 64, None) == INVALID                               # dgu aliases dh
+    assert g(A, None, B_, C_, 4, 60, None) == UNSUPPORTED                          # H % 8
+    assert g(A, None, B_, None, 4, 64, None) == INVALID
+    r = lib.ffn_rmsnorm_bwd  # dinp, dweight, scratch, dres, dy, r, w, rstd, absmax, N, C
+    assert r(A, B_, C_, A, D, 0x50000, 0x60000, 0x70000, None, 4, 8200, None) == UNSUPPORTED  # C > 8192
+    assert r(A, B_, C_, A, D, 0x50000, 0x60000, 0x70000, None, 4, 100, None) == UNSUPPORTED   # C % 8
+    assert r(A, B_, None, A, D, 0x50000, 0x60000, 0x70000, None, 4, 256, None) == INVALID     # no scratch
+    assert r(A, B_, C_, A, A, 0x50000, 0x60000, 0x70000, None, 4, 256, None) == INVALID       # dinp aliases dy
+    assert r(A, B_, C_, A, D, 0x50000, 0x60000, 0x70000, None, -4, 256, None) == INVALID
+    sb = lib.ffn_rmsnorm_bwd_scratch_bytes
+    assert sb(0, 4096) == 0 and sb(8192, 4096) == 512 * 4096 * 4 and sb(3, 256) == 3 * 256 * 4
+    assert sb(4, 9000) == -1
 
 
 def test_binding_rejects_host_tensors_and_short_buffers():

@@ -47,11 +47,18 @@ def _load():
         "ffn_decode_gemv": [P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_decode_gemv_arm": [P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_decode_gemv_bf16": [P, P, P, P, P, P, I64, I64, I64, P],
+        "ffn_matmul_tn": [P, P, P, P, P, I32, I32, I64, I64, I64, P],
+        "ffn_transpose": [P, P, I64, I64, I64, I32, P],
+        "ffn_quant_transpose": [P, P, P, P, I64, I64, I64, P],
+        "ffn_swiglu_bwd": [P, P, P, P, I64, I64, P],
+        "ffn_rmsnorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.ffn_rmsnorm_bwd_scratch_bytes.argtypes = [I64, I64]
+    lib.ffn_rmsnorm_bwd_scratch_bytes.restype = ctypes.c_int64
     lib.ffn_last_error.restype = ctypes.c_char_p
     lib.ffn_last_error.argtypes = []
     lib.ffn_version.restype = ctypes.c_char_p
@@ -239,9 +246,55 @@ def bind_decode_gemv_bf16(out, h, x, w_gate, w_up, w_down, M, C, H, stream=None)
     return _bound(_lib.ffn_decode_gemv_bf16, _decode_bf16_args(out, h, x, w_gate, w_up, w_down, M, C, H, stream))
 
 
+# ----------------------------------------------------------------------------- backward
+
+def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, accumulate, M, N, K, stream=None):
+    fp8 = dtype == FFN_E4M3
+    _check(_lib.ffn_matmul_tn(
+        _ptr(out, "out", M * N, BF16), _ptr(a, "a", M * K, _dt_elems(dtype)),
+        _ptr(a_scale, "a_scale", 1, F32, optional=not fp8), _ptr(b, "b", N * K, _dt_elems(dtype)),
+        _ptr(b_scale, "b_scale", 1, F32, optional=not fp8), int(dtype), int(bool(accumulate)),
+        int(M), int(N), int(K), _stream(stream)))
+
+
+def ffn_transpose(out, inp, rows, cols, ld_out, elt_bytes, stream=None):
+    dt = BF16 if elt_bytes == 2 else E4M3
+    _check(_lib.ffn_transpose(
+        _ptr(out, "out", cols * ld_out, dt), _ptr(inp, "in", rows * cols, dt), int(rows), int(cols), int(ld_out),
+        int(elt_bytes), _stream(stream)))
+
+
+def ffn_quant_transpose(q_t, scale, x, absmax, rows, cols, ld_out, stream=None):
+    _check(_lib.ffn_quant_transpose(
+        _ptr(q_t, "q_t", cols * ld_out, E4M3), _ptr(scale, "scale", 1, F32), _ptr(x, "x", rows * cols, BF16),
+        _ptr(absmax, "absmax", 1, F32), int(rows), int(cols), int(ld_out), _stream(stream)))
+
+
+def ffn_swiglu_bwd(dgu, absmax, dh, gu, N, H, stream=None):
+    _check(_lib.ffn_swiglu_bwd(
+        _ptr(dgu, "dgu", N * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=True),
+        _ptr(dh, "dh", N * H, BF16), _ptr(gu, "gu", N * 2 * H, BF16), int(N), int(H), _stream(stream)))
+
+
+def ffn_rmsnorm_bwd_scratch_bytes(N, C):
+    return int(_lib.ffn_rmsnorm_bwd_scratch_bytes(int(N), int(C)))
+
+
+def ffn_rmsnorm_bwd(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absmax, N, C, stream=None):
+    need = ffn_rmsnorm_bwd_scratch_bytes(N, C)
+    _check(_lib.ffn_rmsnorm_bwd(
+        _ptr(dinp, "dinp", N * C, BF16), _ptr(dweight, "dweight", C, F32),
+        _ptr(scratch, "scratch", max(need, 0) // 4, F32), _ptr(dresidual, "dresidual", N * C, BF16),
+        _ptr(dy, "dy", N * C, BF16), _ptr(r, "r", N * C, BF16), _ptr(weight, "weight", C, BF16),
+        _ptr(rstd, "rstd", N, F32), _ptr(absmax, "absmax", 1, F32, optional=True), int(N), int(C),
+        _stream(stream)))
+
+
 __all__ = [
     "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
     "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16",
+    "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
+    "ffn_rmsnorm_bwd_scratch_bytes",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
 ]

@@ -23,6 +23,15 @@ blocks feeds ``(r, down)`` of one block into ``(inp, addend)`` of the next.
 (``ffn_decode_gemv_arm``, 1..4 tokens); ``DecodeBlockBf16`` holds bf16
 weights and runs ``ffn_decode_gemv_bf16`` (the bf16 arm, 1..4 tokens).
 
+``BackwardBlock`` runs the FFN half of the trainer's ``_backward_block`` for
+a ``PrefillBlock``: a forward that keeps the up-projection output (``MlpUp``,
+as the trainer keeps or recomputes it), then ``backward_qmm`` through the down
+projection, ``swiglu_backward``, ``backward_qmm`` through the up projection and
+``rmsnorm_backward`` (llmq llama_model.cpp, ``LLamaModel::_backward_block``,
+``backward_qmm``).  The transposed operands that the TN products need are made
+by ``ffn_transpose`` / ``ffn_quant_transpose`` with the token dimension padded
+to a multiple of 128 (zeros), the GEMM's K granularity.
+
 Buffers are allocated once, at construction, through torch; the calls
 themselves allocate nothing.  Every step of the arithmetic runs in libffn.so.
 """
@@ -187,3 +196,132 @@ class DecodeBlockBf16:
     def bind(self, x, M=None, stream=None):
         M = self.M if M is None else M
         return B.bind_decode_gemv_bf16(self.out, self.h, x, self.wg, self.wu, self.wd, M, self.C, self.H, stream)
+
+
+def _round_up(n, m):
+    return (n + m - 1) // m * m
+
+
+class BackwardBlock:
+    """Forward (keeping gu) and backward of one FFN block; gradients of the
+    three weights accumulate across calls (``zero_grads`` clears them).
+    in_place: the SwiGLU backward overwrites gu with its gradient, as the
+    trainer does; otherwise it goes to a buffer of its own (``dgu``) and gu
+    survives for another backward."""
+
+    def __init__(self, fwd, in_place=True):
+        self.f = fwd
+        N, C, H = fwd.N, fwd.C, fwd.H
+        self.Np = _round_up(max(N, 1), 128)
+        self.gu = _bf16(N, 2 * H)            # MlpUp
+        self.dgu = self.gu if in_place else _bf16(N, 2 * H)   # dMlpUp
+        self.dh = _bf16(N, H)                # dSwiGLU
+        self.dy = _bf16(N, C)                # dLN2
+        self.d_res = _bf16(N, C)             # dResAtt
+        self.dw_d = _bf16(C, H)
+        self.dw_gu = _bf16(2 * H, C)
+        self.dw_norm = _f32(C)
+        self.scratch = _f32(max(B.ffn_rmsnorm_bwd_scratch_bytes(N, C), 4) // 4)
+        self.am_dout, self.am_dgu, self.am_dres = _f32(1), _f32(1), _f32(1)
+        if fwd.fp8:
+            self.qdout, self.s_dout = _u8(N, C), _f32(1)
+            self.qdgu, self.s_dgu = _u8(N, 2 * H), _f32(1)
+            self.wd_t, self.wgu_t = _u8(H, C), _u8(C, 2 * H)
+            self.dout_t, self.h_t = _u8(C, self.Np), _u8(H, self.Np)
+            self.dgu_t, self.y_t = _u8(2 * H, self.Np), _u8(C, self.Np)
+        else:
+            self.wd_t, self.wgu_t = _bf16(H, C), _bf16(C, 2 * H)
+            self.dout_t, self.h_t = _bf16(C, self.Np), _bf16(H, self.Np)
+            self.dgu_t, self.y_t = _bf16(2 * H, self.Np), _bf16(C, self.Np)
+        self.zero_grads()
+
+    def zero_grads(self):
+        self.dw_d.zero_()
+        self.dw_gu.zero_()
+        self.dw_norm.zero_()
+
+    def forward(self, inp, addend, stream=None):
+        """The block forward with the up-projection output kept: RMSNorm,
+        (quantise y), gate+up GEMM to gu [N, 2H], SwiGLU with its abs-max,
+        (quantise h), down GEMM.  Returns the down output [N, C]."""
+        f = self.f
+        N, C, H = f.N, f.C, f.H
+        B.ffn_rmsnorm_fwd(f.y, f.rstd, f.r if addend is not None else None, f.am_y, inp, addend, f.w_norm, f.eps,
+                          N, C, stream)
+        self.r = f.r if addend is not None else inp
+        if f.fp8:
+            B.ffn_quant_absmax(f.qy, f.s_y, f.am_y, f.y, N * C, 0, stream)
+            B.ffn_gateup(self.gu, None, f.qy, f.s_y, f.w_gu, f.s_gu, B.FFN_E4M3, 0, N, C, H, stream)
+            B.ffn_swiglu(f.h, f.am_h, self.gu, N, H, stream)
+            B.ffn_quant_absmax(f.qh, f.s_h, f.am_h, f.h, N * H, 0, stream)
+            B.ffn_down(f.out, f.qh, f.s_h, f.w_d, f.s_d, B.FFN_E4M3, N, H, C, stream)
+        else:
+            B.ffn_gateup(self.gu, None, f.y, None, f.w_gu, None, B.FFN_BF16, 0, N, C, H, stream)
+            B.ffn_swiglu(f.h, f.am_h, self.gu, N, H, stream)
+            B.ffn_down(f.out, f.h, None, f.w_d, None, B.FFN_BF16, N, H, C, stream)
+        return f.out
+
+    def backward(self, d_out, stream=None, mark=None):
+        """Backward from d_out [N, C] (the gradient of the block's output
+        residual stream, DResFFN) after ``forward``.  Returns d_res (DResAtt);
+        dw_d, dw_gu (bf16) and dw_norm (fp32) accumulate.  mark(label), when
+        given, is called after each phase (for per-phase timing)."""
+        f = self.f
+        N, C, H, Np = f.N, f.C, f.H, self.Np
+        dgu = self.dgu
+        mk = mark or (lambda label: None)
+        if f.fp8:
+            E = B.FFN_E4M3
+            # backward_qmm through the down projection (input h, weight [C, H])
+            B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, stream)
+            mk("quant_dout")
+            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, stream)
+            mk("transpose_w_down")
+            B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, 0, N, H, C, stream)
+            mk("dx_down")
+            B.ffn_quant_transpose(self.dout_t, self.s_dout, d_out, self.am_dout, N, C, Np, stream)
+            B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, stream)
+            mk("transpose_down_operands")
+            B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, 1, C, H, Np, stream)
+            mk("dw_down")
+            B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
+            mk("swiglu_bwd")
+            # backward_qmm through the up projection (input y, weight [2H, C])
+            B.ffn_quant_absmax(self.qdgu, self.s_dgu, self.am_dgu, dgu, N * 2 * H, 0, stream)
+            mk("quant_dgu")
+            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 1, stream)
+            mk("transpose_w_up")
+            B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, 0, N, C, 2 * H, stream)
+            mk("dx_up")
+            B.ffn_quant_transpose(self.dgu_t, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream)
+            B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, stream)
+            mk("transpose_up_operands")
+            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, 1, 2 * H, C, Np, stream)
+            mk("dw_up")
+        else:
+            Bf = B.FFN_BF16
+            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 2, stream)
+            mk("transpose_w_down")
+            B.ffn_matmul_tn(self.dh, d_out, None, self.wd_t, None, Bf, 0, N, H, C, stream)
+            mk("dx_down")
+            B.ffn_transpose(self.dout_t, d_out, N, C, Np, 2, stream)
+            B.ffn_transpose(self.h_t, f.h, N, H, Np, 2, stream)
+            mk("transpose_down_operands")
+            B.ffn_matmul_tn(self.dw_d, self.dout_t, None, self.h_t, None, Bf, 1, C, H, Np, stream)
+            mk("dw_down")
+            B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
+            mk("swiglu_bwd")
+            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 2, stream)
+            mk("transpose_w_up")
+            B.ffn_matmul_tn(self.dy, dgu, None, self.wgu_t, None, Bf, 0, N, C, 2 * H, stream)
+            mk("dx_up")
+            B.ffn_transpose(self.dgu_t, dgu, N, 2 * H, Np, 2, stream)
+            B.ffn_transpose(self.y_t, f.y, N, C, Np, 2, stream)
+            mk("transpose_up_operands")
+            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, None, self.y_t, None, Bf, 1, 2 * H, C, Np, stream)
+            mk("dw_up")
+        # rmsnorm_backward: DResAtt = DResFFN + the RMSNorm input's gradient
+        B.ffn_rmsnorm_bwd(self.d_res, self.dw_norm, self.scratch, d_out, self.dy, self.r, f.w_norm, f.rstd,
+                          self.am_dres, N, C, stream)
+        mk("rmsnorm_bwd")
+        return self.d_res

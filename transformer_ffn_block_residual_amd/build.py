@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libffn.so")
-SOURCES = ["abi.hip", "norm_quant.hip", "gemm.hip", "decode.hip"]
+SOURCES = ["abi.hip", "norm_quant.hip", "gemm.hip", "decode.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

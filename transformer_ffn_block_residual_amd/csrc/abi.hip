@@ -283,4 +283,121 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x, const void*
                       "ffn_decode_gemv_bf16");
 }
 
+// ----------------------------------------------------------------------------- backward
+
+ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const void* b, const float* b_scale,
+                           ffn_dtype_t dtype, int accumulate, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(a);
+    REQUIRE(b);
+    NONNEG(M);
+    NONNEG(N);
+    NONNEG(K);
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3) return fail(FFN_ERR_INVALID, "ffn_matmul_tn: unknown dtype %d", (int)dtype);
+    if (dtype == FFN_E4M3) {
+        REQUIRE(a_scale);
+        REQUIRE(b_scale);
+    }
+    const int elt = dtype == FFN_E4M3 ? 1 : 2;
+    if (ffn_status_t st = check_gemm_dims("ffn_matmul_tn", M, K, N, elt)) return st;
+    ALIGNED(out);
+    ALIGNED(a);
+    ALIGNED(b);
+    if (out == a || out == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn: out must not alias an operand");
+    return hip_status(ffn::launch_gemm(out, nullptr, a, a_scale, b, b_scale, dtype == FFN_E4M3, false, M, (int)K,
+                                       (int)N, stream, nullptr, nullptr, accumulate != 0),
+                      "ffn_matmul_tn");
+}
+
+static ffn_status_t check_transpose(const char* fn, const void* out, const void* in, int64_t rows, int64_t cols,
+                                    int64_t ld_out) {
+    if (rows < 0 || cols < 0 || ld_out < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);
+    if (ld_out < rows) return fail(FFN_ERR_INVALID, "%s: ld_out = %lld < rows = %lld", fn, (long long)ld_out,
+                                   (long long)rows);
+    if (cols % 16 != 0 || ld_out % 16 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: cols and ld_out must be multiples of 16", fn);
+    if (cols > kMaxDim || ld_out > ((int64_t)65535 * 64))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: cols or ld_out too large", fn);
+    if (misaligned(out) || misaligned(in)) return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
+    if (out == in) return fail(FFN_ERR_INVALID, "%s: out must not alias in", fn);
+    return FFN_OK;
+}
+
+ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols, int64_t ld_out, int elt_bytes,
+                           hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(in);
+    if (elt_bytes != 1 && elt_bytes != 2)
+        return fail(FFN_ERR_INVALID, "ffn_transpose: element size %d (need 1 or 2)", elt_bytes);
+    if (ffn_status_t st = check_transpose("ffn_transpose", out, in, rows, cols, ld_out)) return st;
+    return hip_status(ffn::launch_transpose(out, nullptr, nullptr, in, rows, (int)cols, ld_out, elt_bytes, elt_bytes,
+                                            stream),
+                      "ffn_transpose");
+}
+
+ffn_status_t ffn_quant_transpose(uint8_t* q_t, float* scale, const void* x, const float* absmax, int64_t rows,
+                                 int64_t cols, int64_t ld_out, hipStream_t stream) {
+    REQUIRE(q_t);
+    REQUIRE(scale);
+    REQUIRE(x);
+    REQUIRE(absmax);
+    if (ffn_status_t st = check_transpose("ffn_quant_transpose", q_t, x, rows, cols, ld_out)) return st;
+    return hip_status(ffn::launch_transpose(q_t, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream),
+                      "ffn_quant_transpose");
+}
+
+ffn_status_t ffn_swiglu_bwd(void* dgu, float* absmax, const void* dh, const void* gu, int64_t N, int64_t H,
+                            hipStream_t stream) {
+    REQUIRE(dgu);
+    REQUIRE(dh);
+    REQUIRE(gu);
+    NONNEG(N);
+    NONNEG(H);
+    if (H < 8 || H % 8 != 0 || H > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_swiglu_bwd: H = %lld (need H %% 8 == 0)", (long long)H);
+    if (N * H > ((int64_t)1 << 36)) return fail(FFN_ERR_UNSUPPORTED, "ffn_swiglu_bwd: tensor too large");
+    ALIGNED(dgu);
+    ALIGNED(dh);
+    ALIGNED(gu);
+    if (dgu == dh) return fail(FFN_ERR_INVALID, "ffn_swiglu_bwd: dgu must not alias dh");
+    return hip_status(ffn::launch_swiglu_bwd((uint16_t*)dgu, absmax, (const uint16_t*)dh, (const uint16_t*)gu, N,
+                                             (int)H, stream),
+                      "ffn_swiglu_bwd");
+}
+
+int64_t ffn_rmsnorm_bwd_scratch_bytes(int64_t N, int64_t C) {
+    if (N < 0 || C < 0 || C > 8192) return -1;
+    return ffn::rmsnorm_bwd_scratch_floats(N, (int)C) * (int64_t)sizeof(float);
+}
+
+ffn_status_t ffn_rmsnorm_bwd(void* dinp, float* dweight, float* scratch, const void* dresidual, const void* dy,
+                             const void* r, const void* weight, const float* rstd, float* absmax, int64_t N,
+                             int64_t C, hipStream_t stream) {
+    REQUIRE(dinp);
+    REQUIRE(dweight);
+    REQUIRE(scratch);
+    REQUIRE(dresidual);
+    REQUIRE(dy);
+    REQUIRE(r);
+    REQUIRE(weight);
+    REQUIRE(rstd);
+    NONNEG(N);
+    NONNEG(C);
+    if (C < 8 || C % 8 != 0 || C > 8192)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_bwd: C = %lld (need C %% 8 == 0, C <= 8192)", (long long)C);
+    if (N > ((int64_t)1 << 31)) return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_bwd: N too large");
+    ALIGNED(dinp);
+    ALIGNED(dweight);
+    ALIGNED(scratch);
+    ALIGNED(dresidual);
+    ALIGNED(dy);
+    ALIGNED(r);
+    ALIGNED(weight);
+    if (dinp == dy || dinp == r) return fail(FFN_ERR_INVALID, "ffn_rmsnorm_bwd: dinp must not alias dy or r");
+    return hip_status(ffn::launch_rmsnorm_bwd((uint16_t*)dinp, dweight, scratch, (const uint16_t*)dresidual,
+                                              (const uint16_t*)dy, (const uint16_t*)r, (const uint16_t*)weight, rstd,
+                                              absmax, N, (int)C, stream),
+                      "ffn_rmsnorm_bwd");
+}
+
 }  // extern "C"

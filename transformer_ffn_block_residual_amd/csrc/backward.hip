@@ -1,0 +1,348 @@
+// The FFN block's backward kernels (llmq llama_model.cpp,
+// LLamaModel::_backward_block and backward_qmm): transposes (with an optional
+// e4m3 quantisation on the way) that put the backward products' operands in
+// the K-contiguous layout of the MFMA GEMM, the SwiGLU backward and the
+// RMSNorm backward.  All are HBM-bound; none allocates.
+
+#include "common.h"
+#include "launch.h"
+
+namespace ffn {
+
+// ---------------------------------------------------------------------------
+// Transpose: out[c, r] = in[r, c] for r < rows, zero for rows <= r < ld_out
+// (the padding that rounds a token count up to the GEMM's K granularity).
+// kIn / kOut: element bytes of input and output (2, 2: bf16; 1, 1: e4m3
+// codes; 2, 1 with kQuant: e4m3(x * inv), the codes quantize_with_abs_max
+// gives, in the transposed layout).  A workgroup moves one 64 x 64 tile
+// through LDS: 16-byte loads along input rows, 16-byte stores along output
+// rows.  The LDS row pitch is an odd number of dwords so that the column
+// gathers spread over the banks.
+template <int kIn, int kOut, bool kQuant>
+__global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ out, float* __restrict__ scale_out,
+                                                        const float* __restrict__ absmax,
+                                                        const uint8_t* __restrict__ in, int64_t rows, int cols,
+                                                        int64_t ld_out) {
+    constexpr int kT = 64;                        // tile edge (elements)
+    constexpr int kPitch = kT * kOut + 4;         // LDS bytes per tile row
+    constexpr int kInEl = 16 / kIn;               // input elements per 16-byte chunk
+    constexpr int kOutEl = 16 / kOut;             // output elements per 16-byte chunk
+    constexpr int kInCpr = kT / kInEl;            // input chunks per tile row
+    constexpr int kOutCpr = kT / kOutEl;          // output chunks per output tile row
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kT * kPitch];
+    const int c0 = blockIdx.x * kT;
+    const int64_t r0 = (int64_t)blockIdx.y * kT;
+    float inv = 1.0f;
+    if (kQuant) {
+        float scale;
+        scale_pair(*absmax, scale, inv);
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *scale_out = scale;
+    }
+    // all loads first, then the LDS writes
+    uint4 v[kT * kInCpr / 256];
+#pragma unroll
+    for (int i = 0; i < kT * kInCpr / 256; ++i) {
+        const int k = threadIdx.x + 256 * i;
+        const int row = k / kInCpr, cc = k % kInCpr;
+        const int64_t gr = r0 + row;
+        const int gc = c0 + cc * kInEl;
+        v[i] = (gr < rows && gc < cols) ? *reinterpret_cast<const uint4*>(in + (gr * cols + gc) * kIn)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < kT * kInCpr / 256; ++i) {
+        const int k = threadIdx.x + 256 * i;
+        const int row = k / kInCpr, cc = k % kInCpr;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * kPitch + cc * kInEl * kOut);
+        if (kQuant) {
+            dst[0] = pack_e4m3x4(bf16lo(v[i].x) * inv, bf16hi(v[i].x) * inv, bf16lo(v[i].y) * inv,
+                                 bf16hi(v[i].y) * inv);
+            dst[1] = pack_e4m3x4(bf16lo(v[i].z) * inv, bf16hi(v[i].z) * inv, bf16lo(v[i].w) * inv,
+                                 bf16hi(v[i].w) * inv);
+        } else {
+            dst[0] = v[i].x;
+            dst[1] = v[i].y;
+            dst[2] = v[i].z;
+            dst[3] = v[i].w;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kT * kOutCpr / 256; ++i) {
+        const int k = threadIdx.x + 256 * i;
+        const int c = k / kOutCpr, rc = k % kOutCpr;
+        const int go_row = c0 + c;
+        const int64_t go_col = r0 + rc * kOutEl;
+        uint32_t w[4];
+        if (kOut == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = *reinterpret_cast<const uint16_t*>(tile + (rc * 8 + 2 * e) * kPitch + c * 2);
+                const uint32_t hi = *reinterpret_cast<const uint16_t*>(tile + (rc * 8 + 2 * e + 1) * kPitch + c * 2);
+                w[e] = lo | (hi << 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) x |= (uint32_t)tile[(rc * 16 + 4 * e + b) * kPitch + c] << (8 * b);
+                w[e] = x;
+            }
+        }
+        if (go_row < cols && go_col < ld_out)
+            *reinterpret_cast<uint4*>(out + ((int64_t)go_row * ld_out + go_col) * kOut) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+hipError_t launch_transpose(void* out, float* scale, const float* absmax, const void* in, int64_t rows, int cols,
+                            int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s) {
+    if (cols == 0 || ld_out == 0) return hipSuccess;
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((ld_out + 63) / 64)), block(256);
+    uint8_t* o = static_cast<uint8_t*>(out);
+    const uint8_t* x = static_cast<const uint8_t*>(in);
+    if (in_bytes == 2 && out_bytes == 2)
+        hipLaunchKernelGGL((transpose_kernel<2, 2, false>), grid, block, 0, s, o, nullptr, nullptr, x, rows, cols,
+                           ld_out);
+    else if (in_bytes == 1 && out_bytes == 1)
+        hipLaunchKernelGGL((transpose_kernel<1, 1, false>), grid, block, 0, s, o, nullptr, nullptr, x, rows, cols,
+                           ld_out);
+    else
+        hipLaunchKernelGGL((transpose_kernel<2, 1, true>), grid, block, 0, s, o, scale, absmax, x, rows, cols,
+                           ld_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU backward (swiglu_backward): from dh [N, H] and the up-projection
+// output gu [N, 2H] (gate columns, then up columns),
+//   s = 1 / (1 + exp(-g)),  dg = bf16(dh * u * s * (1 + g * (1 - s))),
+//   du = bf16(dh * g * s)
+// into dgu [N, 2H] in the same layout, with max |dgu|.  Eight elements of h
+// per thread (16-byte loads and stores), grid-stride.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dgu, float* __restrict__ absmax,
+                                                         const uint16_t* __restrict__ dh,
+                                                         const uint16_t* gu, int64_t N, int H) {
+    __shared__ float red[4];
+    const int cpr = H >> 3;  // chunks of 8 per row of h
+    const int64_t total = N * cpr;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    float m = 0.0f;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+        const int64_t n = t / cpr;
+        const int j = (int)(t - n * cpr) * 8;
+        const uint4 d4 = *reinterpret_cast<const uint4*>(dh + n * H + j);
+        const uint4 g4 = *reinterpret_cast<const uint4*>(gu + n * 2 * H + j);
+        const uint4 u4 = *reinterpret_cast<const uint4*>(gu + n * 2 * H + H + j);
+        const uint32_t* dp = reinterpret_cast<const uint32_t*>(&d4);
+        const uint32_t* gp = reinterpret_cast<const uint32_t*>(&g4);
+        const uint32_t* up = reinterpret_cast<const uint32_t*>(&u4);
+        uint4 og, ou;
+        uint32_t* ogp = reinterpret_cast<uint32_t*>(&og);
+        uint32_t* oup = reinterpret_cast<uint32_t*>(&ou);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float rg[2], ru[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float d = h ? bf16hi(dp[q]) : bf16lo(dp[q]);
+                const float g = h ? bf16hi(gp[q]) : bf16lo(gp[q]);
+                const float u = h ? bf16hi(up[q]) : bf16lo(up[q]);
+                const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+                const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+                rg[h] = d * u * sg * (1.0f + g * (1.0f - sg));
+                ru[h] = d * g * sg;
+            }
+            ogp[q] = pack_bf16x2(rg[0], rg[1]);
+            oup[q] = pack_bf16x2(ru[0], ru[1]);
+            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(ogp[q])), __builtin_fabsf(bf16hi(ogp[q]))));
+            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(oup[q])), __builtin_fabsf(bf16hi(oup[q]))));
+        }
+        *reinterpret_cast<uint4*>(dgu + n * 2 * H + j) = og;
+        *reinterpret_cast<uint4*>(dgu + n * 2 * H + H + j) = ou;
+    }
+    if (absmax) block_absmax_commit(m, red, absmax);
+}
+
+hipError_t launch_swiglu_bwd(uint16_t* dgu, float* absmax, const uint16_t* dh, const uint16_t* gu, int64_t N, int H,
+                             hipStream_t s) {
+    if (absmax) {
+        hipError_t e = launch_fill(absmax, 1, 0.0f, s);
+        if (e != hipSuccess) return e;
+    }
+    if (N == 0) return hipSuccess;
+    const int64_t total = N * (H / 8);
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s, dgu,
+                       absmax, dh, gu, N, H);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm backward (rmsnorm_backward), with the saved rstd:
+//   xh = r * rstd,  gy = dy * w,  m = sum_j gy_j xh_j / C,
+//   dinp = bf16(dresidual + rstd * (gy - xh * m)),  max |dinp|,
+//   dweight[j] += sum_n dy[n, j] * xh[n, j]   (fp32)
+// A workgroup of 256 threads takes one row at a time, each thread CPT
+// 16-byte chunks of it (columns 8 * (t + 256 i)); the row's dot product is
+// summed per wave, then over the four waves through LDS in a fixed order.
+// Each workgroup walks a fixed set of rows and keeps its share of the weight
+// gradient in registers (8 * CPT floats per thread); at the end it writes
+// them as one row of `scratch` [workgroups, C].  A second kernel adds the
+// rows of scratch in a fixed order to dweight, so the result does not depend
+// on scheduling.  dinp may overwrite dresidual (each thread reads its chunks
+// before it writes them).
+constexpr int kBwdMaxGroups = 512;
+
+static int rmsnorm_bwd_groups(int64_t N) { return (int)(N < kBwdMaxGroups ? N : kBwdMaxGroups); }
+
+int64_t rmsnorm_bwd_scratch_floats(int64_t N, int C) { return N > 0 ? (int64_t)rmsnorm_bwd_groups(N) * C : 0; }
+
+template <int CPT>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(uint16_t* dinp, float* __restrict__ scratch,
+                                                          float* __restrict__ absmax, const uint16_t* dres,
+                                                          const uint16_t* __restrict__ dy,
+                                                          const uint16_t* __restrict__ r,
+                                                          const uint16_t* __restrict__ w,
+                                                          const float* __restrict__ rstd, int64_t N, int C) {
+    __shared__ float red[2][4];
+    __shared__ float amax_red[4];
+    const int t = threadIdx.x;
+    const int lane = t & 63, wid = t >> 6;
+    const int nch = C >> 3;
+    float acc[CPT][8];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+    float amax = 0.0f;
+    // the weight chunks are the same for every row
+    const uint4* w4 = reinterpret_cast<const uint4*>(w);
+    uint4 vw[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) vw[i] = w4[min(t + i * 256, nch - 1)];
+    int parity = 0;
+    for (int64_t row = blockIdx.x; row < N; row += gridDim.x, parity ^= 1) {
+        const uint4* dy4 = reinterpret_cast<const uint4*>(dy + row * C);
+        const uint4* r4 = reinterpret_cast<const uint4*>(r + row * C);
+        const uint4* dr4 = reinterpret_cast<const uint4*>(dres + row * C);
+        // every load of the row first; chunks past the row end load the last
+        // chunk again and are left out
+        uint4 vy[CPT], vr[CPT], vd[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = min(t + i * 256, nch - 1);
+            vy[i] = dy4[c];
+            vr[i] = r4[c];
+            vd[i] = dr4[c];
+        }
+        const float rs = rstd[row];
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const uint32_t* yp = reinterpret_cast<const uint32_t*>(&vy[i]);
+            const uint32_t* rp = reinterpret_cast<const uint32_t*>(&vr[i]);
+            const uint32_t* wp = reinterpret_cast<const uint32_t*>(&vw[i]);
+            float p = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                p += (bf16lo(yp[q]) * bf16lo(wp[q])) * (bf16lo(rp[q]) * rs);
+                p += (bf16hi(yp[q]) * bf16hi(wp[q])) * (bf16hi(rp[q]) * rs);
+            }
+            part += t + i * 256 < nch ? p : 0.0f;
+        }
+        part = wave_sum(part);
+        // alternate two LDS slots by row so that one barrier per row suffices
+        if (lane == 0) red[parity][wid] = part;
+        __syncthreads();
+        const float m = (((red[parity][0] + red[parity][1]) + red[parity][2]) + red[parity][3]) / (float)C;
+        uint4* o4 = reinterpret_cast<uint4*>(dinp + row * C);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = t + i * 256;
+            const bool ok = c < nch;
+            const uint32_t* yp = reinterpret_cast<const uint32_t*>(&vy[i]);
+            const uint32_t* rp = reinterpret_cast<const uint32_t*>(&vr[i]);
+            const uint32_t* wp = reinterpret_cast<const uint32_t*>(&vw[i]);
+            const uint32_t* dp = reinterpret_cast<const uint32_t*>(&vd[i]);
+            uint4 ov;
+            uint32_t* op = reinterpret_cast<uint32_t*>(&ov);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float res[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float yv = h ? bf16hi(yp[q]) : bf16lo(yp[q]);
+                    const float xh = (h ? bf16hi(rp[q]) : bf16lo(rp[q])) * rs;
+                    const float gy = yv * (h ? bf16hi(wp[q]) : bf16lo(wp[q]));
+                    res[h] = (h ? bf16hi(dp[q]) : bf16lo(dp[q])) + rs * (gy - xh * m);
+                    acc[i][2 * q + h] += ok ? yv * xh : 0.0f;
+                }
+                op[q] = pack_bf16x2(res[0], res[1]);
+                amax = __builtin_fmaxf(amax, ok ? __builtin_fmaxf(__builtin_fabsf(bf16lo(op[q])),
+                                                                  __builtin_fabsf(bf16hi(op[q])))
+                                                : 0.0f);
+            }
+            if (ok) o4[c] = ov;
+        }
+    }
+    float* srow = scratch + (int64_t)blockIdx.x * C;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = t + i * 256;
+        if (c < nch) {
+            reinterpret_cast<float4*>(srow + 8 * c)[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+            reinterpret_cast<float4*>(srow + 8 * c)[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+        }
+    }
+    if (absmax) block_absmax_commit(amax, amax_red, absmax);
+}
+
+// dweight[c] += sum over the scratch rows, in a fixed order: four row
+// partitions per column, each summed in row order, then combined in
+// partition order.
+__global__ __launch_bounds__(256) void rmsnorm_dw_reduce_kernel(float* __restrict__ dweight,
+                                                                const float* __restrict__ scratch, int rows, int C) {
+    __shared__ float part[4][64];
+    const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int p = threadIdx.x >> 6;
+    float s = 0.0f;
+    if (c < C)
+        for (int w = p; w < rows; w += 4) s += scratch[(int64_t)w * C + c];
+    part[p][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (p == 0 && c < C) {
+        const int l = threadIdx.x;
+        dweight[c] = dweight[c] + (((part[0][l] + part[1][l]) + part[2][l]) + part[3][l]);
+    }
+}
+
+template <int CPT>
+static void launch_rmsnorm_bwd_cpt(uint16_t* dinp, float* scratch, float* absmax, const uint16_t* dres,
+                                   const uint16_t* dy, const uint16_t* r, const uint16_t* w, const float* rstd,
+                                   int64_t N, int C, int groups, hipStream_t s) {
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<CPT>), dim3((unsigned)groups), dim3(256), 0, s, dinp, scratch, absmax,
+                       dres, dy, r, w, rstd, N, C);
+}
+
+hipError_t launch_rmsnorm_bwd(uint16_t* dinp, float* dweight, float* scratch, const uint16_t* dres,
+                              const uint16_t* dy, const uint16_t* r, const uint16_t* w, const float* rstd,
+                              float* absmax, int64_t N, int C, hipStream_t s) {
+    if (absmax) {
+        hipError_t e = launch_fill(absmax, 1, 0.0f, s);
+        if (e != hipSuccess) return e;
+    }
+    if (N == 0) return hipSuccess;
+    const int groups = rmsnorm_bwd_groups(N);
+    const int need = (C / 8 + 255) / 256;  // chunks per thread
+    if (need <= 1) launch_rmsnorm_bwd_cpt<1>(dinp, scratch, absmax, dres, dy, r, w, rstd, N, C, groups, s);
+    else if (need <= 2) launch_rmsnorm_bwd_cpt<2>(dinp, scratch, absmax, dres, dy, r, w, rstd, N, C, groups, s);
+    else launch_rmsnorm_bwd_cpt<4>(dinp, scratch, absmax, dres, dy, r, w, rstd, N, C, groups, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rmsnorm_dw_reduce_kernel, dim3((unsigned)((C + 63) / 64)), dim3(256), 0, s, dweight, scratch,
+                       groups, C);
+    return hipGetLastError();
+}
+
+}  // namespace ffn

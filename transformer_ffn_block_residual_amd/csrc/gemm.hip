@@ -284,8 +284,12 @@ __device__ __forceinline__ u32x4_t regroup_runs(uint32_t x0, uint32_t x1, uint32
 // memory operations stays exact for the pipeline's counted waits.  kQuant
 // (SwiGLU only): h is rounded to bf16 as always, its abs-max kept, and the
 // stored output is e4m3(h * qinv), the codes ffn_quant_absmax would give h
-// with that abs-max.
-template <bool kFP8, bool kFused, bool kQuant>
+// with that abs-max.  kAccum (plain output only): each 32-row block of the
+// tile first loads the bf16 values it will overwrite (out of range: zero),
+// waits for them, and stores bf16(old + acc * s), one rounding.  The loads and
+// the wait only add memory operations after the pipeline's in-flight loads,
+// which keeps its counted waits safe (they wait for at least as much).
+template <bool kFP8, bool kFused, bool kQuant, bool kAccum>
 __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmArgs& a, int t, float s, float qinv,
                                               int wm, int wn, int fr, int fh, float& amax) {
     int tm, tn;
@@ -302,18 +306,48 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     const int r_base = wn * 128 + fr;  // token row within the tile, block j adds 32 j
     if (!kFused) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            // the previous values of this block's outputs, in the stored
+            // (regrouped) order; v_permlane32_swap is its own inverse, so
+            // swapping them back gives the accumulator order
+            u32x4_t old[4][2];
+            if (kAccum) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int o = tm * kBM + wm * 128 + i * 32 + 16 * q + 8 * fh;
+                        const uint32_t off = o < a.O ? (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * 2
+                                                     : 0x7fffffffu;
+                        old[i][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+                    }
+                wait_vmcnt<0>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x16_t blk = (i == 0 && j == 0) ? read_acc<true>(acc[i][j]) : read_acc<false>(acc[i][j]);
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
+                    float add[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+                    if (kAccum) {
+                        const u32x4_t ov = old[i][q];
+                        const auto s0 = __builtin_amdgcn_permlane32_swap(ov[0], ov[2], false, false);
+                        const auto s1 = __builtin_amdgcn_permlane32_swap(ov[1], ov[3], false, false);
+                        const uint32_t od[4] = {s0[0], s1[0], s0[1], s1[1]};  // d[0], d[1], d[2], d[3]
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            add[2 * e] = bf16lo(od[e]);
+                            add[2 * e + 1] = bf16hi(od[e]);
+                        }
+                    }
                     uint32_t d[4];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int g = 2 * q + h;
-                        d[2 * h] = pack_bf16x2(blk[4 * g + 0] * s, blk[4 * g + 1] * s);
-                        d[2 * h + 1] = pack_bf16x2(blk[4 * g + 2] * s, blk[4 * g + 3] * s);
+                        d[2 * h] = pack_bf16x2(blk[4 * g + 0] * s + add[4 * h], blk[4 * g + 1] * s + add[4 * h + 1]);
+                        d[2 * h + 1] =
+                            pack_bf16x2(blk[4 * g + 2] * s + add[4 * h + 2], blk[4 * g + 3] * s + add[4 * h + 3]);
                     }
                     const u32x4_t v = regroup_runs(d[0], d[1], d[2], d[3]);
                     const int o = tm * kBM + wm * 128 + i * 32 + 16 * q + 8 * fh;
@@ -323,6 +357,7 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -371,10 +406,11 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     }
 }
 
-template <bool kFP8, bool kFused, bool kQuant>
+template <bool kFP8, bool kFused, bool kQuant, bool kAccum>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a) {
     static_assert(kFused || !kQuant, "quantised output is a SwiGLU epilogue");
+    static_assert(!(kFused && kAccum), "accumulation is a plain-output epilogue");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
     constexpr int kStoreCnt = epilogue_stores<kFused>();
@@ -512,7 +548,7 @@ void gemm_kernel(GemmArgs a) {
             wait_vmcnt<kWait>();
             barrier();
         }
-        tile_epilogue<kFP8, kFused, kQuant>(acc, a, c_t, s, qinv, wm, wn, fr, fh, amax);
+        tile_epilogue<kFP8, kFused, kQuant, kAccum>(acc, a, c_t, s, qinv, wm, wn, fr, fh, amax);
         const int t2 = c_t + 2 * G;
         tr_cur = tr_nxt;
         tr_nxt = tile_rsrc<kFused>(a, t2 < T ? t2 : (c_t + G < T ? c_t + G : c_t), wave_u);
@@ -543,7 +579,7 @@ static int cu_count() {
 // under that known abs-max instead of bf16 h, and its scale.
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
-                       hipStream_t s, const float* q_absmax, float* q_scale) {
+                       hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate) {
     if (absmax && (fuse_swiglu || N == 0)) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
@@ -569,14 +605,17 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const int T = a.tiles_m * a.tiles_n;
     const int KT = a.K_bytes / kRowBytes;
     const dim3 grid((unsigned)(KT >= kAhead ? min(T, cu_count()) : T)), block(kThreads);
+    const bool acc = accumulate && !fuse_swiglu;
     if (fp8) {
-        if (quant) hipLaunchKernelGGL((gemm_kernel<true, true, true>), grid, block, 0, s, a);
-        else if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<true, true, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<true, false, false>), grid, block, 0, s, a);
+        if (quant) hipLaunchKernelGGL((gemm_kernel<true, true, true, false>), grid, block, 0, s, a);
+        else if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<true, true, false, false>), grid, block, 0, s, a);
+        else if (acc) hipLaunchKernelGGL((gemm_kernel<true, false, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<true, false, false, false>), grid, block, 0, s, a);
     } else {
-        if (quant) hipLaunchKernelGGL((gemm_kernel<false, true, true>), grid, block, 0, s, a);
-        else if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<false, true, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<false, false, false>), grid, block, 0, s, a);
+        if (quant) hipLaunchKernelGGL((gemm_kernel<false, true, true, false>), grid, block, 0, s, a);
+        else if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<false, true, false, false>), grid, block, 0, s, a);
+        else if (acc) hipLaunchKernelGGL((gemm_kernel<false, false, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, false, false>), grid, block, 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || fuse_swiglu || !absmax) return e;

@@ -21,9 +21,24 @@ hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t
 // SwiGLU-fused).  fp8 selects e4m3 operands with device scales.
 // q_absmax / q_scale: SwiGLU only; out then holds e4m3 codes of h quantised
 // with the known abs-max *q_absmax, and *q_scale receives its scale.
+// accumulate (plain output only): out = bf16(out + product), one rounding.
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
-                       hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr);
+                       hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr,
+                       bool accumulate = false);
+
+// Backward: out[c, r] = in[r, c], zero for rows <= r < ld_out.  (in_bytes,
+// out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3
+// with *absmax on the way (scale written to *scale).
+hipError_t launch_transpose(void* out, float* scale, const float* absmax, const void* in, int64_t rows, int cols,
+                            int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s);
+hipError_t launch_swiglu_bwd(uint16_t* dgu, float* absmax, const uint16_t* dh, const uint16_t* gu, int64_t N, int H,
+                             hipStream_t s);
+// scratch: rmsnorm_bwd_scratch_floats(N, C) floats.
+int64_t rmsnorm_bwd_scratch_floats(int64_t N, int C);
+hipError_t launch_rmsnorm_bwd(uint16_t* dinp, float* dweight, float* scratch, const uint16_t* dres,
+                              const uint16_t* dy, const uint16_t* r, const uint16_t* w, const float* rstd,
+                              float* absmax, int64_t N, int C, hipStream_t s);
 
 // Decode arms (the caller has checked: arms other than the split one, and bf16
 // weights, only for M <= 4; gu is a [M, 2H] bf16 workspace for those arms).
