@@ -93,3 +93,73 @@ def test_bf16_truncation_is_caught(monkeypatch):
         return ((v.view(np.uint32) >> 16) << 16).view(np.float32).astype(np.float64)
     monkeypatch.setattr(K, "bf16_round", trunc)
     _fails(TC.test_bf16_round_of_float64_by_nearest_search)
+
+
+# ----------------------------------------------------------------------------- backward
+
+import oracle.backward as OB
+from tests import test_oracle_backward as TB
+
+
+def _patch_b(monkeypatch, name, fn):
+    monkeypatch.setattr(OB, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def test_swapped_gate_and_up_gradients_are_caught(monkeypatch):
+    good = OB.swiglu_bwd
+
+    def swapped(dh, gu):
+        dgu, am = good(dh, gu)
+        H = dgu.shape[-1] // 2
+        return np.concatenate([dgu[..., H:], dgu[..., :H]], axis=-1), am
+    _patch_b(monkeypatch, "swiglu_bwd", swapped)
+    _fails(TB.test_swiglu_bwd_matches_torch_autograd)
+    _fails(TB.test_block_backward_zero_gate_and_accumulators)
+
+
+def test_silu_derivative_without_its_second_term_is_caught(monkeypatch):
+    def bad(dh_bits, gu_bits):
+        dh, gu = K.bf16_bits_to_f64(dh_bits), K.bf16_bits_to_f64(gu_bits)
+        H = gu.shape[-1] // 2
+        g, u = gu[..., :H], gu[..., H:]
+        s = OB.sigmoid(g)
+        dgu = np.concatenate([K.bf16_round(dh * u * s), K.bf16_round(dh * g * s)], axis=-1)
+        return K.f64_to_bf16_bits(dgu), np.float32(np.max(np.abs(dgu)))
+    _patch_b(monkeypatch, "swiglu_bwd", bad)
+    _fails(TB.test_swiglu_bwd_finite_differences)
+    _fails(TB.test_swiglu_bwd_matches_torch_autograd)
+
+
+def test_rmsnorm_backward_without_the_normalisation_term_is_caught(monkeypatch):
+    good = OB.rmsnorm_bwd
+
+    def bad(dres, dy, r, w, rstd, dweight=None):
+        _, dw, _ = good(dres, dy, r, w, rstd, dweight)
+        rs = np.asarray(rstd, np.float32).astype(np.float64)[..., None]
+        dinp = K.bf16_round(K.bf16_bits_to_f64(dres) + rs * K.bf16_bits_to_f64(dy) * K.bf16_bits_to_f64(w)[None, :])
+        return K.f64_to_bf16_bits(dinp), dw, np.float32(np.max(np.abs(dinp)))
+    _patch_b(monkeypatch, "rmsnorm_bwd", bad)
+    _fails(TB.test_rmsnorm_bwd_matches_torch_autograd)
+    _fails(TB.test_rmsnorm_bwd_is_orthogonal_to_the_input_without_eps)
+    _fails(lambda: TB.test_block_backward_matches_torch_autograd(False))
+
+
+def test_weight_gradient_without_accumulation_is_caught(monkeypatch):
+    good = OB.matmul_tn
+    _patch_b(monkeypatch, "matmul_tn", lambda a, b, a_scale=None, b_scale=None, accumulate=None:
+             good(a, b, a_scale, b_scale))
+    _fails(TB.test_matmul_tn_and_accumulate)
+    _fails(TB.test_linear_bwd_bf16_matches_torch_autograd)
+
+
+def test_fp8_gradient_scaled_by_the_input_scale_is_caught(monkeypatch):
+    good = OB.linear_bwd
+
+    def bad(dy, x, w, fp8=False, dy_absmax=None, qx=None, sx=None, qw=None, sw=None, dw_acc=None):
+        out = good(dy, x, w, fp8, dy_absmax, qx, sx, qw, sw, dw_acc)
+        if fp8:
+            out["dx"] = OB.matmul_tn(out["qdy"], OB.transpose(qw), sx, sw)
+        return out
+    _patch_b(monkeypatch, "linear_bwd", bad)
+    _fails(TB.test_linear_bwd_fp8_scales_exactly_with_the_gradient)
