@@ -450,7 +450,7 @@ def bench_block(a, torch, np, B, block, W):
 
 BWD_PHASES = {
     # phase: (kind, work) with work in flop ("mfma") or bytes ("hbm") given N, C, H, element bytes e
-    "quant_dout": ("hbm", lambda N, C, H, e: 3 * N * C),
+    "quant_dout": ("hbm", lambda N, C, H, e: 3 * N * C),   # abs-max handed over by its producer
     "transpose_w_down": ("hbm", lambda N, C, H, e: 2 * C * H * e),
     "dx_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
     "transpose_down_operands": ("hbm", lambda N, C, H, e: (2 + e) * N * C + 2 * N * H * e),
@@ -504,13 +504,18 @@ def bench_backward(a, torch, np, B, block, W):
     bb = block.BackwardBlock(pre, in_place=False)
     bb.forward(dev(d["inp"]), dev(d["addend"]))
     d_out = dev(_bwd_dout(np, w, N))
+    # the abs-max of d_out, as its producer (the next block's RMSNorm backward)
+    # would hand it over
+    am_dout = torch.empty(1, dtype=torch.float32, device="cuda")
+    B.ffn_quant_absmax(bb.qdout if w.fp8 else torch.empty(N * C, dtype=torch.uint8, device="cuda"),
+                       torch.empty(1, dtype=torch.float32, device="cuda"), am_dout, d_out, N * C, 1)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     names = list(BWD_PHASES)
 
     def step(i, tm, stream=stream):
         if tm is None:
-            bb.backward(d_out, stream)
+            bb.backward(d_out, stream, d_out_absmax=am_dout)
             return
         marks = [tm.mark()]
         seen = []
@@ -518,7 +523,7 @@ def bench_backward(a, torch, np, B, block, W):
         def mark(label):
             marks.append(tm.mark())
             seen.append(label)
-        bb.backward(d_out, stream, mark)
+        bb.backward(d_out, stream, mark, d_out_absmax=am_dout)
         tm.add("step", marks[0], marks[-1])
         for k, label in enumerate(seen):
             tm.add(label, marks[k], marks[k + 1])
@@ -552,7 +557,8 @@ def bench_backward(a, torch, np, B, block, W):
         "config": {"workload": f"FFN block backward of the {a.workload} workload: N={N} C={C} H={H}, "
                                + ("FP8 (per-tensor e4m3 weights, activations and gradients)" if w.fp8 else "bf16")
                                + "; down and up backward_qmm (data and weight gradients), SwiGLU and RMSNorm "
-                                 "backward, weight transposes included",
+                                 "backward, weight transposes included; the abs-max of the incoming gradient comes "
+                                 "with it (its producer, the next block's RMSNorm backward, writes it)",
                    "N": N, "C": C, "H": H, "seed": w.seed, "backward": True},
         "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({'e4m3' if w.fp8 else 'bf16'}, accumulate): "
                                                  "the up projection's weight gradient [2H, C], K = N",

@@ -267,12 +267,15 @@ def test_block_backward_accumulates_weight_gradients(F):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-def test_block_backward_out_of_place_keeps_gu(F, fp8):
+def test_block_backward_out_of_place_and_given_absmax(F, fp8):
     say(f"block backward out of place fp8={fp8}")
     from transformer_ffn_block_residual_amd import block
     N, C, H = 96, 256, 384
     d = W.block_inputs(N, C, H, seed=9, w_std=0.1)
     d_out = dev_bf16(rand_bits((N, C), 1.0, 10))
+    # the second run takes d_out's abs-max from outside, as from its producer
+    am = empty_f32(1)
+    F.ffn_quant_absmax(empty_u8(N * C), empty_f32(1), am, d_out, N * C, 1)
     res = []
     for in_place in (True, False):
         pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
@@ -280,7 +283,7 @@ def test_block_backward_out_of_place_keeps_gu(F, fp8):
         bb = block.BackwardBlock(pb, in_place=in_place)
         bb.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
         gu0 = bb.gu.clone()
-        bb.backward(d_out)
+        bb.backward(d_out, d_out_absmax=None if in_place else am)
         torch.cuda.synchronize()
         res.append((bb.dgu.clone(), bb.d_res.clone(), bb.dw_d.clone(), bb.dw_gu.clone(), bb.dw_norm.clone()))
         if not in_place:

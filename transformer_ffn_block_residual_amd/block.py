@@ -261,11 +261,14 @@ class BackwardBlock:
             B.ffn_down(f.out, f.h, None, f.w_d, None, B.FFN_BF16, N, H, C, stream)
         return f.out
 
-    def backward(self, d_out, stream=None, mark=None):
+    def backward(self, d_out, stream=None, mark=None, d_out_absmax=None):
         """Backward from d_out [N, C] (the gradient of the block's output
         residual stream, DResFFN) after ``forward``.  Returns d_res (DResAtt);
-        dw_d, dw_gu (bf16) and dw_norm (fp32) accumulate.  mark(label), when
-        given, is called after each phase (for per-phase timing)."""
+        dw_d, dw_gu (bf16) and dw_norm (fp32) accumulate.  d_out_absmax: the
+        abs-max of d_out when its producer already wrote it (the upstream
+        ``ffn_rmsnorm_bwd`` does, as the trainer's rmsnorm_backward does for
+        DResFFN); None computes it here.  mark(label), when given, is called
+        after each phase (for per-phase timing)."""
         f = self.f
         N, C, H, Np = f.N, f.C, f.H, self.Np
         dgu = self.dgu
@@ -273,7 +276,11 @@ class BackwardBlock:
         if f.fp8:
             E = B.FFN_E4M3
             # backward_qmm through the down projection (input h, weight [C, H])
-            B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, stream)
+            if d_out_absmax is None:
+                B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, stream)
+            else:
+                self.am_dout = d_out_absmax
+                B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 0, stream)
             mk("quant_dout")
             B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, stream)
             mk("transpose_w_down")

@@ -96,9 +96,15 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // max into a non-negative fp32 in global memory: for v >= 0 the IEEE order is
 // the unsigned order of the bit patterns, so an integer atomic max is exact and
-// independent of the order in which blocks arrive.
+// independent of the order in which blocks arrive.  The stored maximum only
+// grows while blocks commit, so the atomic is skipped when the value already
+// there (read from L2, device scope) is at least v: a stale read can only
+// cost an unneeded atomic, never skip a needed one.  Thousands of blocks that
+// finish together otherwise queue on the one address.
 __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
-    atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+    unsigned int* u = reinterpret_cast<unsigned int*>(p);
+    const unsigned int cur = __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(v) > cur) atomicMax(u, __float_as_uint(v));
 }
 
 // Block-wide max of a per-thread value, then one atomic per block.  All threads

@@ -206,11 +206,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
 //                    SiLU-input down projection: the product is recomputed by
 //                    every wave that needs it)
 // kBf16W: bf16 weights without scales (8 per 16-byte load, 512 K per window).
-// U windows of loads are issued before any is used.  out_ld / x_ld: row
-// strides in elements.
+// U windows of loads are issued before any is used.  kKS > 1 splits each row's
+// windows over kKS waves of the workgroup (part p takes windows p, p + kKS,
+// ...: an order that depends on kKS alone, not on R or U); the parts' sums
+// meet in LDS and are added in part order.  Long rows (the down projection)
+// then keep more bytes in flight.  out_ld / x_ld: row strides in elements.
 enum : int { kSmallDualSilu = 0, kSmallDualGU = 1, kSmallSingle = 2, kSmallSingleSiluIn = 3 };
 
-template <int kMode, bool kBf16W, int MT, int R, int U, int kWaves>
+template <int kMode, bool kBf16W, int MT, int R, int U, int kWaves, int kKS>
 __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
     uint16_t* __restrict__ out, int out_ld, const uint16_t* __restrict__ x, int x_ld,
     const uint8_t* __restrict__ w0, const float* __restrict__ s0, const uint8_t* __restrict__ w1,
@@ -222,14 +225,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
     constexpr int kEPL = 16 / kWB;        // elements per lane per window (one 16-byte load)
     constexpr int kWin = 64 * kEPL;       // elements per window
     constexpr int kXL = kEPL / 8;         // 16-byte activation loads per token per window (x2 for g and u)
+    static_assert(kWaves % kKS == 0, "whole groups of waves per row set");
+    constexpr int kGroups = kWaves / kKS;
     const int lane = threadIdx.x & 63;
-    const int row0 = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;  // rows % R == 0
-    if (row0 >= rows) return;
+    const int wid = threadIdx.x >> 6;
+    const int part = wid % kKS;
+    const int row0 = (blockIdx.x * kGroups + wid / kKS) * R;  // rows % R == 0
+    // (with kKS > 1 every wave reaches the barrier below; a wave past the
+    // last row reads row 0 and stores nothing)
+    if (kKS == 1 && row0 >= rows) return;
+    const bool valid = row0 < rows;
+    const int rowa = valid ? row0 : 0;
     const uint8_t* wr[R][NMAT];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        wr[r][0] = w0 + (int64_t)(row0 + r) * K * kWB;
-        if (kDual) wr[r][NMAT - 1] = w1 + (int64_t)(row0 + r) * K * kWB;
+        wr[r][0] = w0 + (int64_t)(rowa + r) * K * kWB;
+        if (kDual) wr[r][NMAT - 1] = w1 + (int64_t)(rowa + r) * K * kWB;
     }
     float acc[R][NMAT][MT];
 #pragma unroll
@@ -240,14 +251,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
             for (int t = 0; t < MT; ++t) acc[r][m][t] = 0.0f;
 
     const int nwin = (K + kWin - 1) / kWin;
-    for (int w = 0; w < nwin; w += U) {
+    for (int i = 0; i * kKS + part < nwin; i += U) {
         uint4 wv[U][R][NMAT], xv[U][MT][kSiluIn ? 2 : 1][kXL];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // past the row end (a partial last window, or a window past the
             // last): load the row's last 16 bytes, and zero the activations
-            const int k = (w + u) * kWin + lane * kEPL;
+            const int k = ((i + u) * kKS + part) * kWin + lane * kEPL;
             ok[u] = k < K;
             const int kc = ok[u] ? k : K - kEPL;
 #pragma unroll
@@ -322,7 +333,31 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[r][m][t] = wave_sum(acc[r][m][t]);
-    if (lane != 0) return;
+    if (kKS > 1) {
+        __shared__ float part_sum[kWaves][R * NMAT * MT];
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) part_sum[wid][(r * NMAT + m) * MT + t] = acc[r][m][t];
+        }
+        __syncthreads();
+        if (part != 0) return;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    float v = part_sum[wid][(r * NMAT + m) * MT + t];
+#pragma unroll
+                    for (int p = 1; p < kKS; ++p) v += part_sum[wid + p][(r * NMAT + m) * MT + t];
+                    acc[r][m][t] = v;
+                }
+    }
+    if (lane != 0 || !valid) return;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int row = row0 + r;
@@ -355,6 +390,13 @@ constexpr int kSmallDualR = 1, kSmallDualU = 4, kSmallDownR = 2, kSmallDownU = 2
 // weight loads (measured at M = 3, 4 over R in 1..8, U in 1..4): two rows per
 // wave share each activation load, one window in flight
 constexpr int kSmallDualR4 = 2, kSmallDualU4 = 1, kSmallDownR4 = 2, kSmallDownU4 = 1;
+// waves per row: bf16 rows (twice the windows of e4m3 rows) are split over
+// four waves, which took the single-token bf16 decode from 64 to 60 us; e4m3
+// rows gained nothing from a split (2 or 4 waves, the down pass alone or
+// both), nor from starting each row group's walk at a rotated window.  The
+// choice depends on the weight type alone, so every pass over e4m3 weights
+// sums in the same order.
+constexpr int kSmallKSFp8 = 1, kSmallKSBf16 = 4;
 
 template <int kMode, bool kBf16W, int MT>
 static hipError_t small_pass(uint16_t* out, int out_ld, const uint16_t* x, int x_ld, const uint8_t* w0,
@@ -365,9 +407,10 @@ static hipError_t small_pass(uint16_t* out, int out_ld, const uint16_t* x, int x
     constexpr int R = kDual ? (kWide ? kSmallDualR4 : kSmallDualR) : (kWide ? kSmallDownR4 : kSmallDownR);
     constexpr int U = kDual ? (kWide ? kSmallDualU4 : kSmallDualU) : (kWide ? kSmallDownU4 : kSmallDownU);
     const int waves = rows / R;  // rows are multiples of 128: whole waves of rows
-    hipLaunchKernelGGL((gemv_small_kernel<kMode, kBf16W, MT, R, U, kSmallWaves>),
-                       dim3((waves + kSmallWaves - 1) / kSmallWaves), dim3(64 * kSmallWaves), 0, s, out, out_ld, x,
-                       x_ld, w0, s0, w1, s1, M, K, rows);
+    constexpr int KS = kBf16W ? kSmallKSBf16 : kSmallKSFp8;
+    constexpr int G = kSmallWaves / KS;  // row groups per workgroup
+    hipLaunchKernelGGL((gemv_small_kernel<kMode, kBf16W, MT, R, U, kSmallWaves, KS>), dim3((waves + G - 1) / G),
+                       dim3(64 * kSmallWaves), 0, s, out, out_ld, x, x_ld, w0, s0, w1, s1, M, K, rows);
     return hipGetLastError();
 }
 

@@ -284,11 +284,12 @@ __device__ __forceinline__ u32x4_t regroup_runs(uint32_t x0, uint32_t x1, uint32
 // memory operations stays exact for the pipeline's counted waits.  kQuant
 // (SwiGLU only): h is rounded to bf16 as always, its abs-max kept, and the
 // stored output is e4m3(h * qinv), the codes ffn_quant_absmax would give h
-// with that abs-max.  kAccum (plain output only): each 32-row block of the
-// tile first loads the bf16 values it will overwrite (out of range: zero),
-// waits for them, and stores bf16(old + acc * s), one rounding.  The loads and
-// the wait only add memory operations after the pipeline's in-flight loads,
-// which keeps its counted waits safe (they wait for at least as much).
+// with that abs-max.  kAccum (plain output only): the epilogue loads the bf16
+// values it will overwrite (out of range: zero) and stores bf16(old + acc * s),
+// one rounding.  The loads of 32-row block j + 1 are issued before the wait for
+// block j's, so each wait overlaps a block's work.  The loads and waits only
+// add memory operations after the pipeline's in-flight loads, which keeps its
+// counted waits safe (they wait for at least as much).
 template <bool kFP8, bool kFused, bool kQuant, bool kAccum>
 __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmArgs& a, int t, float s, float qinv,
                                               int wm, int wn, int fr, int fh, float& amax) {
@@ -305,23 +306,31 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     const uint32_t row_bytes = (uint32_t)a.ld_out * kOutElt;
     const int r_base = wn * 128 + fr;  // token row within the tile, block j adds 32 j
     if (!kFused) {
+        // the previous values of a block's outputs, in the stored (regrouped)
+        // order; v_permlane32_swap is its own inverse, so swapping them back
+        // gives the accumulator order.  Two blocks' worth, double-buffered.
+        u32x4_t oldv[2][4][2];
+        auto load_old = [&](int j, u32x4_t (&dst)[4][2]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int o = tm * kBM + wm * 128 + i * 32 + 16 * q + 8 * fh;
+                    const uint32_t off = o < a.O ? (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * 2
+                                                 : 0x7fffffffu;
+                    dst[i][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+                }
+        };
+        if (kAccum) load_old(0, oldv[0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            // the previous values of this block's outputs, in the stored
-            // (regrouped) order; v_permlane32_swap is its own inverse, so
-            // swapping them back gives the accumulator order
-            u32x4_t old[4][2];
+            u32x4_t (&old)[4][2] = oldv[j & 1];
             if (kAccum) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int o = tm * kBM + wm * 128 + i * 32 + 16 * q + 8 * fh;
-                        const uint32_t off = o < a.O ? (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * 2
-                                                     : 0x7fffffffu;
-                        old[i][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
-                    }
-                wait_vmcnt<0>();
+                // 8 loads and 8 stores per block; after block j's loads come
+                // block j + 1's loads and (from j = 1) block j - 1's stores
+                if (j + 1 < 4) load_old(j + 1, oldv[(j + 1) & 1]);
+                if (j == 0 || j == 3) wait_vmcnt<8>();
+                else wait_vmcnt<16>();
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll

@@ -134,22 +134,31 @@ hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax
 
 // ---------------------------------------------------------------------------
 // Standalone abs-max of a bf16 tensor (llmq llama_model.cpp, _forward_block,
-// abs_max).  Grid-stride over 16-byte chunks; any length (scalar tail).
+// abs_max).  Grid-stride over groups of four 16-byte chunks per thread (four
+// loads in flight before any is used); any length (scalar tail).
 __global__ __launch_bounds__(256) void absmax_kernel(float* out, const uint16_t* __restrict__ x, int64_t n) {
     __shared__ float red[4];
     float m = 0.0f;
     const int64_t nch = n >> 3;
     const uint4* x4 = reinterpret_cast<const uint4*>(x);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nch; c += stride) {
-        const uint4 v = x4[c];
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(&v);
+    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t c = t0; c < nch; c += 4 * stride) {
+        uint4 v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(p[q])), __builtin_fabsf(bf16hi(p[q]))));
+        for (int i = 0; i < 4; ++i) {
+            const int64_t ci = c + i * stride;
+            v[i] = ci < nch ? x4[ci] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(&v[i]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(p[q])), __builtin_fabsf(bf16hi(p[q]))));
+        }
     }
-    for (int64_t i = (nch << 3) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        m = __builtin_fmaxf(m, __builtin_fabsf(bf16lo(x[i])));
+    for (int64_t i = (nch << 3) + t0; i < n; i += stride) m = __builtin_fmaxf(m, __builtin_fabsf(bf16lo(x[i])));
     block_absmax_commit(m, red, out);
 }
 
@@ -190,8 +199,8 @@ hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_
     hipError_t e = launch_fill(absmax, 1, 0.0f, s);
     if (e != hipSuccess || n == 0) return e;
     int64_t nch = (n + 7) / 8;
-    int64_t blocks = (nch + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    int64_t blocks = (nch + 1023) / 1024;  // four chunks per thread per pass
+    if (blocks > 2048) blocks = 2048;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, absmax, x, n);
     return hipGetLastError();
