@@ -450,16 +450,18 @@ def bench_block(a, torch, np, B, block, W):
 
 BWD_PHASES = {
     # phase: (kind, work) with work in flop ("mfma") or bytes ("hbm") given N, C, H, element bytes e
-    "quant_dout": ("hbm", lambda N, C, H, e: 3 * N * C),   # abs-max handed over by its producer
+    # FP8: codes in both layouts from one read (abs-max handed over by its producer)
+    "quant_dout": ("hbm", lambda N, C, H, e: 4 * N * C),
     "transpose_w_down": ("hbm", lambda N, C, H, e: 2 * C * H * e),
     "dx_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
-    "transpose_down_operands": ("hbm", lambda N, C, H, e: (2 + e) * N * C + 2 * N * H * e),
+    # bf16: the gradient and h transposed; FP8: the forward's codes of h
+    "transpose_down_operands": ("hbm", lambda N, C, H, e: (4 * N * C if e == 2 else 0) + 2 * N * H * e),
     "dw_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
     "swiglu_bwd": ("hbm", lambda N, C, H, e: 10 * N * H),
-    "quant_dgu": ("hbm", lambda N, C, H, e: 6 * N * H),
+    "quant_dgu": ("hbm", lambda N, C, H, e: 8 * N * H),
     "transpose_w_up": ("hbm", lambda N, C, H, e: 4 * C * H * e),
     "dx_up": ("mfma", lambda N, C, H, e: 4 * N * C * H),
-    "transpose_up_operands": ("hbm", lambda N, C, H, e: (2 + e) * 2 * N * H + 2 * N * C * e),
+    "transpose_up_operands": ("hbm", lambda N, C, H, e: (8 * N * H if e == 2 else 0) + 2 * N * C * e),
     "dw_up": ("mfma", lambda N, C, H, e: 4 * N * C * H),
     "rmsnorm_bwd": ("hbm", lambda N, C, H, e: 5 * N * C * 2 + N * 4),
 }

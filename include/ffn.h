@@ -241,10 +241,12 @@ ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols
 /* Quantise with a known abs-max and transpose in one pass: q_t[c, r] =
  * e4m3(x[r, c] * 448 / absmax), *scale = absmax / 448 (1 and 1 for absmax 0),
  * zero codes for rows <= r < ld_out.  [llmq model] backward_qmm,
- * quantize_and_transpose_with_abs_max.  x: bf16 [rows, cols]; q_t: e4m3
- * [cols, ld_out]; absmax: fp32 [1] (device, read).  Constraints as
- * ffn_transpose. */
-ffn_status_t ffn_quant_transpose(uint8_t* q_t, float* scale, const void* x,
+ * quantize_and_transpose_with_abs_max (and, with q, quantize_with_abs_max of
+ * the same tensor from the same read: backward_qmm quantises the output
+ * gradient in both layouts).  x: bf16 [rows, cols]; q_t: e4m3 [cols, ld_out];
+ * q (nullable): e4m3 [rows, cols], the codes in x's layout; absmax: fp32 [1]
+ * (device, read).  Constraints as ffn_transpose; q must not alias q_t or x. */
+ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const void* x,
                                  const float* absmax, int64_t rows, int64_t cols,
                                  int64_t ld_out, hipStream_t stream);
 

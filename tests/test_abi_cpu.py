@@ -160,9 +160,11 @@ def test_backward_validation(lib):
     assert t(A, B_, 37, 64, 40, 2, None) == UNSUPPORTED                            # ld_out % 16
     assert t(A, A, 37, 64, 48, 2, None) == INVALID                                 # in place
     assert t(A, MIS, 37, 64, 48, 1, None) == UNSUPPORTED
-    q = lib.ffn_quant_transpose  # q_t, scale, x, absmax, rows, cols, ld_out
-    assert q(A, B_, C_, None, 37, 64, 48, None) == INVALID                         # no abs-max
-    assert q(A, B_, C_, D, 37, 64, 32, None) == INVALID
+    q = lib.ffn_quant_transpose  # q_t, q, scale, x, absmax, rows, cols, ld_out
+    assert q(A, None, B_, C_, None, 37, 64, 48, None) == INVALID                   # no abs-max
+    assert q(A, None, B_, C_, D, 37, 64, 32, None) == INVALID                      # ld_out < rows
+    assert q(A, A, B_, C_, D, 37, 64, 48, None) == INVALID                         # q aliases q_t
+    assert q(A, MIS, B_, C_, D, 37, 64, 48, None) == UNSUPPORTED                   # misaligned q
     g = lib.ffn_swiglu_bwd  # dgu, absmax, dh, gu, N, H
     assert g(A, None, A, C_, 4, 64, None) == INVALID                               # dgu aliases dh
     assert g(A, None, B_, C_, 4, 60, None) == UNSUPPORTED                          # H % 8

@@ -84,11 +84,15 @@ def test_quant_transpose(F, rows, cols, ld):
     x = rand_bits((rows, cols), 3.0, rows * 3 + cols)
     am = O.absmax_of(x)
     for given in (am, np.float32(am * 0.5), np.float32(0.0)):
-        qt, sc = empty_u8(cols, ld).fill_(5), empty_f32(1)
-        F.ffn_quant_transpose(qt, sc, dev_bf16(x), dev_f32([given]), rows, cols, ld)
+        qt, q, sc = empty_u8(cols, ld).fill_(5), empty_u8(rows, cols).fill_(6), empty_f32(1)
+        F.ffn_quant_transpose(qt, q, sc, dev_bf16(x), dev_f32([given]), rows, cols, ld)
+        qt2 = empty_u8(cols, ld).fill_(5)
+        F.ffn_quant_transpose(qt2, None, sc, dev_bf16(x), dev_f32([given]), rows, cols, ld)
         torch.cuda.synchronize()
         q_ref, s_ref, _ = O.quant_absmax(x, given)
         assert np.array_equal(host_u8(qt), padded_t(q_ref, ld))
+        assert np.array_equal(host_u8(q), q_ref)
+        assert torch.equal(qt, qt2)
         assert host_f32(sc)[0] == s_ref
 
 

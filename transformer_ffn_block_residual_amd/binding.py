@@ -49,7 +49,7 @@ def _load():
         "ffn_decode_gemv_bf16": [P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_matmul_tn": [P, P, P, P, P, I32, I32, I64, I64, I64, P],
         "ffn_transpose": [P, P, I64, I64, I64, I32, P],
-        "ffn_quant_transpose": [P, P, P, P, I64, I64, I64, P],
+        "ffn_quant_transpose": [P, P, P, P, P, I64, I64, I64, P],
         "ffn_swiglu_bwd": [P, P, P, P, I64, I64, P],
         "ffn_rmsnorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, P],
     }
@@ -264,9 +264,10 @@ def ffn_transpose(out, inp, rows, cols, ld_out, elt_bytes, stream=None):
         int(elt_bytes), _stream(stream)))
 
 
-def ffn_quant_transpose(q_t, scale, x, absmax, rows, cols, ld_out, stream=None):
+def ffn_quant_transpose(q_t, q, scale, x, absmax, rows, cols, ld_out, stream=None):
     _check(_lib.ffn_quant_transpose(
-        _ptr(q_t, "q_t", cols * ld_out, E4M3), _ptr(scale, "scale", 1, F32), _ptr(x, "x", rows * cols, BF16),
+        _ptr(q_t, "q_t", cols * ld_out, E4M3), _ptr(q, "q", rows * cols, E4M3, optional=True),
+        _ptr(scale, "scale", 1, F32), _ptr(x, "x", rows * cols, BF16),
         _ptr(absmax, "absmax", 1, F32), int(rows), int(cols), int(ld_out), _stream(stream)))
 
 

@@ -276,17 +276,17 @@ class BackwardBlock:
         if f.fp8:
             E = B.FFN_E4M3
             # backward_qmm through the down projection (input h, weight [C, H])
+            # the gradient's codes in both layouts from one read
             if d_out_absmax is None:
                 B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, stream)
             else:
                 self.am_dout = d_out_absmax
-                B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 0, stream)
+            B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, stream)
             mk("quant_dout")
             B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, stream)
             mk("transpose_w_down")
             B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, 0, N, H, C, stream)
             mk("dx_down")
-            B.ffn_quant_transpose(self.dout_t, self.s_dout, d_out, self.am_dout, N, C, Np, stream)
             B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, stream)
             mk("transpose_down_operands")
             B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, 1, C, H, Np, stream)
@@ -294,13 +294,12 @@ class BackwardBlock:
             B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
             mk("swiglu_bwd")
             # backward_qmm through the up projection (input y, weight [2H, C])
-            B.ffn_quant_absmax(self.qdgu, self.s_dgu, self.am_dgu, dgu, N * 2 * H, 0, stream)
+            B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream)
             mk("quant_dgu")
             B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 1, stream)
             mk("transpose_w_up")
             B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, 0, N, C, 2 * H, stream)
             mk("dx_up")
-            B.ffn_quant_transpose(self.dgu_t, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream)
             B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, stream)
             mk("transpose_up_operands")
             B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, 1, 2 * H, C, Np, stream)

@@ -330,19 +330,22 @@ ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols
     if (elt_bytes != 1 && elt_bytes != 2)
         return fail(FFN_ERR_INVALID, "ffn_transpose: element size %d (need 1 or 2)", elt_bytes);
     if (ffn_status_t st = check_transpose("ffn_transpose", out, in, rows, cols, ld_out)) return st;
-    return hip_status(ffn::launch_transpose(out, nullptr, nullptr, in, rows, (int)cols, ld_out, elt_bytes, elt_bytes,
-                                            stream),
+    return hip_status(ffn::launch_transpose(out, nullptr, nullptr, nullptr, in, rows, (int)cols, ld_out, elt_bytes,
+                                            elt_bytes, stream),
                       "ffn_transpose");
 }
 
-ffn_status_t ffn_quant_transpose(uint8_t* q_t, float* scale, const void* x, const float* absmax, int64_t rows,
-                                 int64_t cols, int64_t ld_out, hipStream_t stream) {
+ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const void* x, const float* absmax,
+                                 int64_t rows, int64_t cols, int64_t ld_out, hipStream_t stream) {
     REQUIRE(q_t);
     REQUIRE(scale);
     REQUIRE(x);
     REQUIRE(absmax);
     if (ffn_status_t st = check_transpose("ffn_quant_transpose", q_t, x, rows, cols, ld_out)) return st;
-    return hip_status(ffn::launch_transpose(q_t, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream),
+    ALIGNED(q);
+    if (q && (q == q_t || (const void*)q == x))
+        return fail(FFN_ERR_INVALID, "ffn_quant_transpose: q must not alias q_t or x");
+    return hip_status(ffn::launch_transpose(q_t, q, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream),
                       "ffn_quant_transpose");
 }
 

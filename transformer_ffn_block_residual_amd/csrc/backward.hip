@@ -14,12 +14,14 @@ namespace ffn {
 // (the padding that rounds a token count up to the GEMM's K granularity).
 // kIn / kOut: element bytes of input and output (2, 2: bf16; 1, 1: e4m3
 // codes; 2, 1 with kQuant: e4m3(x * inv), the codes quantize_with_abs_max
-// gives, in the transposed layout).  A workgroup moves one 64 x 64 tile
+// gives, in the transposed layout, and with q_rows also in the input's
+// layout, from the same read).  A workgroup moves one 64 x 64 tile
 // through LDS: 16-byte loads along input rows, 16-byte stores along output
 // rows.  The LDS row pitch is an odd number of dwords so that the column
 // gathers spread over the banks.
 template <int kIn, int kOut, bool kQuant>
-__global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ out, float* __restrict__ scale_out,
+__global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ out, uint8_t* __restrict__ q_rows,
+                                                        float* __restrict__ scale_out,
                                                         const float* __restrict__ absmax,
                                                         const uint8_t* __restrict__ in, int64_t rows, int cols,
                                                         int64_t ld_out) {
@@ -55,10 +57,16 @@ __global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ ou
         const int row = k / kInCpr, cc = k % kInCpr;
         uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * kPitch + cc * kInEl * kOut);
         if (kQuant) {
-            dst[0] = pack_e4m3x4(bf16lo(v[i].x) * inv, bf16hi(v[i].x) * inv, bf16lo(v[i].y) * inv,
-                                 bf16hi(v[i].y) * inv);
-            dst[1] = pack_e4m3x4(bf16lo(v[i].z) * inv, bf16hi(v[i].z) * inv, bf16lo(v[i].w) * inv,
-                                 bf16hi(v[i].w) * inv);
+            const uint32_t q0 = pack_e4m3x4(bf16lo(v[i].x) * inv, bf16hi(v[i].x) * inv, bf16lo(v[i].y) * inv,
+                                            bf16hi(v[i].y) * inv);
+            const uint32_t q1 = pack_e4m3x4(bf16lo(v[i].z) * inv, bf16hi(v[i].z) * inv, bf16lo(v[i].w) * inv,
+                                            bf16hi(v[i].w) * inv);
+            dst[0] = q0;
+            dst[1] = q1;
+            const int64_t gr = r0 + row;
+            const int gc = c0 + cc * kInEl;
+            if (q_rows && gr < rows && gc < cols)
+                *reinterpret_cast<uint2*>(q_rows + gr * cols + gc) = make_uint2(q0, q1);
         } else {
             dst[0] = v[i].x;
             dst[1] = v[i].y;
@@ -95,21 +103,21 @@ __global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ ou
     }
 }
 
-hipError_t launch_transpose(void* out, float* scale, const float* absmax, const void* in, int64_t rows, int cols,
-                            int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s) {
+hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
+                            int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s) {
     if (cols == 0 || ld_out == 0) return hipSuccess;
     const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((ld_out + 63) / 64)), block(256);
     uint8_t* o = static_cast<uint8_t*>(out);
     const uint8_t* x = static_cast<const uint8_t*>(in);
     if (in_bytes == 2 && out_bytes == 2)
-        hipLaunchKernelGGL((transpose_kernel<2, 2, false>), grid, block, 0, s, o, nullptr, nullptr, x, rows, cols,
-                           ld_out);
+        hipLaunchKernelGGL((transpose_kernel<2, 2, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x, rows,
+                           cols, ld_out);
     else if (in_bytes == 1 && out_bytes == 1)
-        hipLaunchKernelGGL((transpose_kernel<1, 1, false>), grid, block, 0, s, o, nullptr, nullptr, x, rows, cols,
-                           ld_out);
+        hipLaunchKernelGGL((transpose_kernel<1, 1, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x, rows,
+                           cols, ld_out);
     else
-        hipLaunchKernelGGL((transpose_kernel<2, 1, true>), grid, block, 0, s, o, scale, absmax, x, rows, cols,
-                           ld_out);
+        hipLaunchKernelGGL((transpose_kernel<2, 1, true>), grid, block, 0, s, o, q_rows, scale, absmax, x, rows,
+                           cols, ld_out);
     return hipGetLastError();
 }
 

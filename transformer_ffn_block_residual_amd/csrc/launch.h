@@ -29,9 +29,10 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
 
 // Backward: out[c, r] = in[r, c], zero for rows <= r < ld_out.  (in_bytes,
 // out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3
-// with *absmax on the way (scale written to *scale).
-hipError_t launch_transpose(void* out, float* scale, const float* absmax, const void* in, int64_t rows, int cols,
-                            int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s);
+// with *absmax on the way (scale written to *scale; q_rows, if not null, also
+// receives the codes in the input's [rows, cols] layout).
+hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
+                            int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s);
 hipError_t launch_swiglu_bwd(uint16_t* dgu, float* absmax, const uint16_t* dh, const uint16_t* gu, int64_t N, int H,
                              hipStream_t s);
 // scratch: rmsnorm_bwd_scratch_floats(N, C) floats.
