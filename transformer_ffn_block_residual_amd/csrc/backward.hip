@@ -19,6 +19,7 @@ namespace ffn {
 // through LDS: 16-byte loads along input rows, 16-byte stores along output
 // rows.  The LDS row pitch is an odd number of dwords so that the column
 // gathers spread over the banks.
+// (Used for bf16; the byte-output forms use transpose8_kernel below.)
 template <int kIn, int kOut, bool kQuant>
 __global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ out, uint8_t* __restrict__ q_rows,
                                                         float* __restrict__ scale_out,
@@ -103,21 +104,107 @@ __global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ ou
     }
 }
 
+// Byte-output form (e4m3 codes, plain or quantised on the way): a workgroup
+// moves a 128 x 128 tile.  The store side reads LDS a dword at a time (four
+// columns of one row) and transposes 4 x 4 byte blocks in registers, so each
+// thread writes four 16-byte output chunks (four columns, 16 rows) from 16
+// LDS reads, instead of one 16-byte chunk from 16 single-byte reads.  Eight
+// consecutive lanes hold the eight 16-row groups of the same four columns, so
+// each store instruction writes whole 128-byte lines of eight output rows; the
+// row pitch (35 dwords) spreads those lanes' LDS reads over four bank groups.
+template <int kIn, bool kQuant>
+__global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ out, uint8_t* __restrict__ q_rows,
+                                                         float* __restrict__ scale_out,
+                                                         const float* __restrict__ absmax,
+                                                         const uint8_t* __restrict__ in, int64_t rows, int cols,
+                                                         int64_t ld_out) {
+    constexpr int kT = 128;                   // tile edge (elements)
+    constexpr int kPitch = kT + 12;           // LDS bytes per tile row (35 dwords)
+    constexpr int kInEl = 16 / kIn;           // input elements per 16-byte chunk
+    constexpr int kInCpr = kT / kInEl;        // input chunks per tile row
+    constexpr int kLoads = kT * kInCpr / 256; // input chunks per thread
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kT * kPitch];
+    const int c0 = blockIdx.x * kT;
+    const int64_t r0 = (int64_t)blockIdx.y * kT;
+    float inv = 1.0f;
+    if (kQuant) {
+        float scale;
+        scale_pair(*absmax, scale, inv);
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *scale_out = scale;
+    }
+    uint4 v[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int k = threadIdx.x + 256 * i;
+        const int row = k / kInCpr, cc = k % kInCpr;
+        const int64_t gr = r0 + row;
+        const int gc = c0 + cc * kInEl;
+        v[i] = (gr < rows && gc < cols) ? *reinterpret_cast<const uint4*>(in + (gr * cols + gc) * kIn)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int k = threadIdx.x + 256 * i;
+        const int row = k / kInCpr, cc = k % kInCpr;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * kPitch + cc * kInEl);  // 4-byte aligned
+        if (kQuant) {
+            const uint32_t q0 = pack_e4m3x4(bf16lo(v[i].x) * inv, bf16hi(v[i].x) * inv, bf16lo(v[i].y) * inv,
+                                            bf16hi(v[i].y) * inv);
+            const uint32_t q1 = pack_e4m3x4(bf16lo(v[i].z) * inv, bf16hi(v[i].z) * inv, bf16lo(v[i].w) * inv,
+                                            bf16hi(v[i].w) * inv);
+            dst[0] = q0;
+            dst[1] = q1;
+            const int64_t gr = r0 + row;
+            const int gc = c0 + cc * kInEl;
+            if (q_rows && gr < rows && gc < cols)
+                *reinterpret_cast<uint2*>(q_rows + gr * cols + gc) = make_uint2(q0, q1);
+        } else {
+            dst[0] = v[i].x;
+            dst[1] = v[i].y;
+            dst[2] = v[i].z;
+            dst[3] = v[i].w;
+        }
+    }
+    __syncthreads();
+    const int rg = threadIdx.x & 7;    // rows 16 rg .. 16 rg + 15 of the tile
+    const int cg = threadIdx.x >> 3;   // columns 4 cg .. 4 cg + 3 of the tile
+    uint32_t d[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[i] = *reinterpret_cast<const uint32_t*>(tile + (16 * rg + i) * kPitch + 4 * cg);
+    const int64_t go_col = r0 + 16 * rg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // byte j of d[4e .. 4e + 3] -> dword e of column 4 cg + j
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = ((d[4 * e] >> (8 * j)) & 0xffu) | (((d[4 * e + 1] >> (8 * j)) & 0xffu) << 8) |
+                   (((d[4 * e + 2] >> (8 * j)) & 0xffu) << 16) | (((d[4 * e + 3] >> (8 * j)) & 0xffu) << 24);
+        const int go_row = c0 + 4 * cg + j;
+        if (go_row < cols && go_col < ld_out)
+            *reinterpret_cast<uint4*>(out + (int64_t)go_row * ld_out + go_col) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
                             int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s) {
     if (cols == 0 || ld_out == 0) return hipSuccess;
-    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((ld_out + 63) / 64)), block(256);
     uint8_t* o = static_cast<uint8_t*>(out);
     const uint8_t* x = static_cast<const uint8_t*>(in);
-    if (in_bytes == 2 && out_bytes == 2)
+    const dim3 block(256);
+    if (in_bytes == 2 && out_bytes == 2) {
+        const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((ld_out + 63) / 64));
         hipLaunchKernelGGL((transpose_kernel<2, 2, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x, rows,
                            cols, ld_out);
-    else if (in_bytes == 1 && out_bytes == 1)
-        hipLaunchKernelGGL((transpose_kernel<1, 1, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x, rows,
-                           cols, ld_out);
-    else
-        hipLaunchKernelGGL((transpose_kernel<2, 1, true>), grid, block, 0, s, o, q_rows, scale, absmax, x, rows,
-                           cols, ld_out);
+    } else {
+        const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((ld_out + 127) / 128));
+        if (in_bytes == 1)
+            hipLaunchKernelGGL((transpose8_kernel<1, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x,
+                               rows, cols, ld_out);
+        else
+            hipLaunchKernelGGL((transpose8_kernel<2, true>), grid, block, 0, s, o, q_rows, scale, absmax, x, rows,
+                               cols, ld_out);
+    }
     return hipGetLastError();
 }
 
