@@ -101,26 +101,37 @@ def measured_traffic(key, src):
 # dominant kernel per workload: traffic.json key, its source file, the kernel
 # name fragments whose per-dispatch counters make up one launch of the entry
 # point, and the algorithmic bytes of that launch
-def traffic_spec(workload, known_h_absmax=False):
+def traffic_spec(workload, known_h_absmax=False, backward=False):
     """(traffic.json key, source file, kernel-name fragments of one launch,
-    description, algorithmic bytes of one launch) for the dominant kernel."""
+    description, algorithmic bytes of one launch, dispatch stride) for the
+    dominant kernel.  A stride of 2 takes every second matching dispatch
+    (starting with the second): the backward's two weight-gradient GEMMs share
+    one kernel, and the up projection's is the second of each step."""
     from transformer_ffn_block_residual_amd import workloads as W
     w = W.WORKLOADS[workload]
     N, C, H = w.N, w.C, w.H
+    if backward:
+        e = 1 if w.fp8 else 2
+        fp8 = "true" if w.fp8 else "false"
+        # reads dgu^T [2H, N] and y^T [C, N] once, reads and writes dW_gu [2H, C]
+        return (f"dwup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, false, false, true>"],
+                f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, accumulating) of the up projection's weight "
+                f"gradient, [2H, C] = [{2 * H}, {C}], K = N = {N}",
+                2 * H * N * e + C * N * e + 2 * (2 * H * C * 2), 2)
     if workload == "decode":
         return ("decode_decode", "decode.hip", ["gemv_small_kernel<0, false, 1,", "gemv_small_kernel<2, false, 1,"],
                 f"gemv_small_kernel<dual SiLU> + gemv_small_kernel<single> (one ffn_decode_gemv), M=1 C={C} H={H}",
-                3 * H * C + (2 * H + C) * 4 + 2 * (C + H) * 2)
+                3 * H * C + (2 * H + C) * 4 + 2 * (C + H) * 2, 1)
     elt = 1 if w.fp8 else 2
     fp8 = "true" if w.fp8 else "false"
     if known_h_absmax:
         # reads x and w, writes the e4m3 codes of h
-        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true>"],
+        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false>"],
                 f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation) of ffn_gateup_swiglu_quant, "
-                f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H)
-    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false>"],
+                f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, 1)
+    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false>"],
             f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
-            N * C * elt + 2 * H * C * elt + N * H * 2)
+            N * C * elt + 2 * H * C * elt + N * H * 2, 1)
 
 
 def ingest_pmc(a):
@@ -128,7 +139,7 @@ def ingest_pmc(a):
     rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
     scaled by what the counter reads for the 1 GiB calibration copy."""
     import csv
-    key, src, frags, desc, algo = traffic_spec(a.workload, a.known_h_absmax)
+    key, src, frags, desc, algo, stride = traffic_spec(a.workload, a.known_h_absmax, a.backward)
     rec = {"kernel": desc, "src": f"transformer_ffn_block_residual_amd/csrc/{src}", "src_sha256": src_digest(src)}
     total = 0.0
     for counter, path, truth_kb in (("FETCH_SIZE", a.ingest_pmc[0], 1 << 20), ("WRITE_SIZE", a.ingest_pmc[1], 1 << 20)):
@@ -140,6 +151,7 @@ def ingest_pmc(a):
         per_launch = 0.0
         for f in frags:
             vals = [float(r["Counter_Value"]) for r in rows if f in r["Kernel_Name"]]
+            vals = vals[stride - 1::stride]
             if not vals:
                 raise SystemExit(f"{path}: no dispatch of {f}")
             per_launch += sum(vals) / len(vals)
@@ -564,7 +576,8 @@ def bench_backward(a, torch, np, B, block, W):
                    "N": N, "C": C, "H": H, "seed": w.seed, "backward": True},
         "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({'e4m3' if w.fp8 else 'bf16'}, accumulate): "
                                                  "the up projection's weight gradient [2H, C], K = N",
-                     "achieved": dw_tf, "peak": peak, "unit": "TFLOP/s", "frac": dw_tf / peak, "traffic": None},
+                     "achieved": dw_tf, "peak": peak, "unit": "TFLOP/s", "frac": dw_tf / peak,
+                     "traffic": measured_traffic(f"dwup_{a.workload}", "gemm.hip")},
         "kernels": kernels,
         "spread_ms": spread,
         "ms_per_step_in_hip_graph": graph_ms,

@@ -393,22 +393,36 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(uint16_t* dinp, float*
     if (absmax) block_absmax_commit(amax, amax_red, absmax);
 }
 
-// dweight[c] += sum over the scratch rows, in a fixed order: four row
-// partitions per column, each summed in row order, then combined in
-// partition order.
+// dweight[c] += sum over the scratch rows, in a fixed order: sixteen row
+// partitions per column (partition p: rows p, p + 16, ..., eight loads in
+// flight), each summed in row order, then combined in partition order.  A
+// workgroup covers 16 columns.
+constexpr int kReduceParts = 16;
+
 __global__ __launch_bounds__(256) void rmsnorm_dw_reduce_kernel(float* __restrict__ dweight,
                                                                 const float* __restrict__ scratch, int rows, int C) {
-    __shared__ float part[4][64];
-    const int c = blockIdx.x * 64 + (threadIdx.x & 63);
-    const int p = threadIdx.x >> 6;
+    __shared__ float part[kReduceParts][16];
+    const int col = threadIdx.x & 15, p = threadIdx.x >> 4;
+    const int c = blockIdx.x * 16 + col;
     float s = 0.0f;
-    if (c < C)
-        for (int w = p; w < rows; w += 4) s += scratch[(int64_t)w * C + c];
-    part[p][threadIdx.x & 63] = s;
+    if (c < C) {
+        int w = p;
+        for (; w + 7 * kReduceParts < rows; w += 8 * kReduceParts) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = scratch[(int64_t)(w + u * kReduceParts) * C + c];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; w < rows; w += kReduceParts) s += scratch[(int64_t)w * C + c];
+    }
+    part[p][col] = s;
     __syncthreads();
     if (p == 0 && c < C) {
-        const int l = threadIdx.x;
-        dweight[c] = dweight[c] + (((part[0][l] + part[1][l]) + part[2][l]) + part[3][l]);
+        float t = part[0][col];
+#pragma unroll
+        for (int q = 1; q < kReduceParts; ++q) t += part[q][col];
+        dweight[c] = dweight[c] + t;
     }
 }
 
@@ -435,7 +449,7 @@ hipError_t launch_rmsnorm_bwd(uint16_t* dinp, float* dweight, float* scratch, co
     else launch_rmsnorm_bwd_cpt<4>(dinp, scratch, absmax, dres, dy, r, w, rstd, N, C, groups, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(rmsnorm_dw_reduce_kernel, dim3((unsigned)((C + 63) / 64)), dim3(256), 0, s, dweight, scratch,
+    hipLaunchKernelGGL(rmsnorm_dw_reduce_kernel, dim3((unsigned)((C + 15) / 16)), dim3(256), 0, s, dweight, scratch,
                        groups, C);
     return hipGetLastError();
 }
