@@ -26,6 +26,9 @@ from .codecs import (
     e4m3_decode,
     e4m3_encode,
     E4M3_MAX,
+    e5m2_decode,
+    e5m2_encode,
+    E5M2_MAX,
 )
 from .ffn import (
     residual_add,
@@ -60,7 +63,7 @@ from .backward import (
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "bf16_round", "e4m3_decode",
-    "e4m3_encode", "E4M3_MAX", "residual_add", "rms_rstd", "rms_apply", "rmsnorm_fwd",
+    "e4m3_encode", "E4M3_MAX", "e5m2_decode", "e5m2_encode", "E5M2_MAX", "residual_add", "rms_rstd", "rms_apply", "rmsnorm_fwd",
     "absmax_of", "scales_from_absmax", "quant_absmax",
     "quant_rows", "gemm_bf16", "gemm_fp8", "silu", "swiglu", "gateup", "down",
     "decode_dual", "decode_down", "decode_gemv", "decode_gemv_bf16", "block_forward",

@@ -24,7 +24,7 @@ in fp64, one rounding to each stored type.
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, f64_to_bf16_bits, bf16_round, e4m3_decode
+from .codecs import bf16_bits_to_f64, f64_to_bf16_bits, bf16_round, FP8_FORMATS
 from .ffn import _f32, _matmul_nt, absmax_of, quant_absmax
 
 
@@ -99,25 +99,26 @@ def transpose(x):
     return np.ascontiguousarray(np.asarray(x).T)
 
 
-def matmul_tn(a, b, a_scale=None, b_scale=None, accumulate=None):
+def matmul_tn(a, b, a_scale=None, b_scale=None, accumulate=None, a_fmt="e4m3", b_fmt="e4m3"):
     """out[m, n] = bf16( acc[m,n] + (sum_k A[m,k] * B[n,k]) * s ) — the TN
     matmul of ``backward_qmm`` in row-major terms (both operands K-contiguous).
-    bf16 operands when the scales are None (s = 1), else e4m3 codes with
-    s = fp32(a_scale * b_scale).  ``accumulate`` is the bf16 output it adds to
-    (the ``accumulate_gradient`` flag); None means a plain store.  Reading:
-    the accumulation happens before the single rounding to bf16, as a
-    matmul's ``C + A*B`` does in its fp32 compute type."""
+    bf16 operands when the scales are None (s = 1), else FP8 codes (a_fmt,
+    b_fmt: "e4m3" or "e5m2") with s = fp32(a_scale * b_scale).  ``accumulate``
+    is the bf16 output it adds to (the ``accumulate_gradient`` flag); None
+    means a plain store.  Reading: the accumulation happens before the single
+    rounding to bf16, as a matmul's ``C + A*B`` does in its fp32 compute type."""
     if a_scale is None:
         prod = _matmul_nt(bf16_bits_to_f64(a), bf16_bits_to_f64(b))
     else:
         s = np.float64(_f32(np.float64(_f32(a_scale)) * np.float64(_f32(b_scale))))
-        prod = _matmul_nt(e4m3_decode(a), e4m3_decode(b)) * s
+        prod = _matmul_nt(FP8_FORMATS[a_fmt][1](a), FP8_FORMATS[b_fmt][1](b)) * s
     if accumulate is not None:
         prod = prod + bf16_bits_to_f64(accumulate)
     return f64_to_bf16_bits(prod)
 
 
-def linear_bwd(dy, x, w, fp8=False, dy_absmax=None, qx=None, sx=None, qw=None, sw=None, dw_acc=None):
+def linear_bwd(dy, x, w, fp8=False, dy_absmax=None, qx=None, sx=None, qw=None, sw=None, dw_acc=None,
+               grad_fmt="e4m3"):
     """``backward_qmm`` for out = x * W^T with x ``[N, C]``, W ``[OC, C]``,
     dy ``[N, OC]``.  Returns a dict with dx ``[N, C]`` and dw ``[OC, C]``
     (bf16 bits) and, for FP8, the quantised gradient.
@@ -127,8 +128,9 @@ def linear_bwd(dy, x, w, fp8=False, dy_absmax=None, qx=None, sx=None, qw=None, s
            dx = bf16( (qdy * qW) * (sW * sdy) )          (W transposed, TN)
            dw = bf16( dw_acc + (qdy^T * qx) * (sx * sdy) )  (both transposed, TN)
     qx/sx: the input's forward codes and scale (reused, as ``reuse_inp`` does);
-    qw/sw: the weight's codes and scale.  Reading: gradient codes are e4m3
-    (the grad dtype the pages allow beside e5m2)."""
+    qw/sw: the weight's codes and scale (e4m3).  grad_fmt: the gradient's
+    codes, e4m3 or e5m2 (the two FP8 grad dtypes the pages allow), each with
+    its own largest value in the scale."""
     if not fp8:
         wt = transpose(w)
         dx = matmul_tn(dy, wt)
@@ -136,13 +138,13 @@ def linear_bwd(dy, x, w, fp8=False, dy_absmax=None, qx=None, sx=None, qw=None, s
         return {"dx": dx, "dw": dw}
     if dy_absmax is None:
         dy_absmax = absmax_of(dy)
-    qdy, sdy, _ = quant_absmax(dy, dy_absmax)
-    dx = matmul_tn(qdy, transpose(qw), sdy, sw)
-    dw = matmul_tn(transpose(qdy), transpose(qx), sdy, sx, accumulate=dw_acc)
+    qdy, sdy, _ = quant_absmax(dy, dy_absmax, grad_fmt)
+    dx = matmul_tn(qdy, transpose(qw), sdy, sw, a_fmt=grad_fmt)
+    dw = matmul_tn(transpose(qdy), transpose(qx), sdy, sx, accumulate=dw_acc, a_fmt=grad_fmt)
     return {"dx": dx, "dw": dw, "qdy": qdy, "sdy": sdy}
 
 
-def block_backward(fwd, d_out, w_norm, w_gu, w_d, fp8=False, acc=None):
+def block_backward(fwd, d_out, w_norm, w_gu, w_d, fp8=False, acc=None, grad_fmt="e4m3"):
     """The FFN half of ``LLamaModel::_backward_block``.
 
     fwd: ``block_forward``'s dict for the same inputs (the RMSNorm input, y,
@@ -158,17 +160,18 @@ def block_backward(fwd, d_out, w_norm, w_gu, w_d, fp8=False, acc=None):
       dy            = up backward of dgu            (dLN2 [N, C]); dW_gu
       d_residual    = rmsnorm_bwd(d_out, dy, r, ...); dw_norm
 
-    FP8: d_out is quantised with its own abs-max, dgu with swiglu_bwd's.
+    FP8: d_out is quantised with its own abs-max, dgu with swiglu_bwd's, both
+    to grad_fmt codes (e4m3 or e5m2).
     """
     acc = acc or {}
     out = {}
     r = fwd["rms_input"]
     down = linear_bwd(d_out, fwd["h"], w_d, fp8, qx=fwd.get("qh"), sx=fwd.get("s_h"), qw=fwd.get("qw_d"),
-                      sw=fwd.get("s_d"), dw_acc=acc.get("dw_d"))
+                      sw=fwd.get("s_d"), dw_acc=acc.get("dw_d"), grad_fmt=grad_fmt)
     dh = down["dx"]
     dgu, am_dgu = swiglu_bwd(dh, fwd["gu"])
     up = linear_bwd(dgu, fwd["y"], w_gu, fp8, dy_absmax=am_dgu, qx=fwd.get("qy"), sx=fwd.get("s_y"),
-                    qw=fwd.get("qw_gu"), sw=fwd.get("s_gu"), dw_acc=acc.get("dw_gu"))
+                    qw=fwd.get("qw_gu"), sw=fwd.get("s_gu"), dw_acc=acc.get("dw_gu"), grad_fmt=grad_fmt)
     dres, dw_norm, am_res = rmsnorm_bwd(d_out, up["dx"], r, w_norm, fwd["rstd"], acc.get("dw_norm"))
     out.update(dh=dh, dw_d=down["dw"], dgu=dgu, absmax_dgu=am_dgu, dy=up["dx"], dw_gu=up["dw"],
                d_residual=dres, dw_norm=dw_norm, absmax_d_residual=am_res)

@@ -11,6 +11,13 @@
   infinities, 0x7F/0xFF NaN, largest finite magnitude 448, smallest normal
   2^-6, smallest subnormal 2^-9.  Encoding rounds to nearest, ties to the even
   code, and saturates magnitudes at or above 448 to 448.
+* e5m2 — the other FP8 gradient type the trainer accepts (llmq
+  llama_run_state.cpp: ``use_fp8`` holds for a grad dtype of ``FP8_E4M3`` or
+  ``FP8_E5M2``; the transposed gradient of ``backward_qmm`` is allocated in the
+  grad dtype).  Read as the OCP E5M2 layout: bias 15, infinities at
+  0x7C/0xFC, NaN above them, largest finite magnitude 57344, smallest normal
+  2^-14, smallest subnormal 2^-16.  Encoding rounds to nearest, ties to the
+  even code, and saturates at 57344 as the e4m3 encoder does at 448.
 
 Each routine is written from those definitions, on whole numpy arrays, with no
 bit tricks beyond reading a float32's bit pattern.
@@ -19,6 +26,7 @@ bit tricks beyond reading a float32's bit pattern.
 import numpy as np
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 BF16_MAX = float.fromhex("0x1.fe00000000000p+127")  # (2 - 2^-7) * 2^127
 
 
@@ -115,3 +123,57 @@ def e4m3_encode(v):
     out = (code.astype(np.uint8) | sign).astype(np.uint8)
     out[nan] = 0x7F | sign[nan]
     return out.reshape(shape)
+
+
+def _e5m2_table():
+    codes = np.arange(256, dtype=np.uint16)
+    s = (codes >> 7) & 1
+    e = ((codes >> 2) & 0x1F).astype(np.int64)
+    m = (codes & 0x3).astype(np.float64)
+    mag = np.where(e == 0, (m / 4.0) * 2.0 ** -14, (1.0 + m / 4.0) * np.power(2.0, e - 15))
+    val = np.where(s == 1, -mag, mag)
+    val[(e == 31) & (m == 0)] = np.where(s[(e == 31) & (m == 0)] == 1, -np.inf, np.inf)
+    val[(e == 31) & (m != 0)] = np.nan
+    return val
+
+
+_E5M2_VALUES = _e5m2_table()
+
+
+def e5m2_decode(codes):
+    """e5m2 codes (uint8) -> float64 values (+-inf for 0x7C / 0xFC, NaN above)."""
+    return _E5M2_VALUES[np.asarray(codes).astype(np.uint8)]
+
+
+def e5m2_encode(v):
+    """Values -> e5m2 codes (uint8): round to nearest, ties to the even code,
+    saturate at 57344, NaN -> 0x7E with the sign bit, -0.0 -> 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    shape = v.shape
+    v = v.reshape(-1)
+    sign = np.where(np.signbit(v), 0x80, 0x00).astype(np.uint8)
+    a = np.abs(v)
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, np.minimum(a, E5M2_MAX))
+    code = np.zeros(a.shape, dtype=np.int64)
+    # Subnormal range: the grid is 2^-16, four steps up to the smallest normal.
+    sub = a < 2.0 ** -14
+    code[sub] = np.rint(a[sub] * 2.0 ** 16).astype(np.int64)  # 4 lands on code 0x04 = 2^-14
+    # Normal range: a = (1 + m/4) * 2^e with e = floor(log2 a) in [-14, 15].
+    nrm = ~sub
+    f, ex = np.frexp(a[nrm])
+    e = ex - 1
+    m = np.rint((np.ldexp(a[nrm], -e) - 1.0) * 4.0).astype(np.int64)
+    carry = m == 4
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    code[nrm] = ((e + 15) << 2) | m
+    out = (code.astype(np.uint8) | sign).astype(np.uint8)
+    out[nan] = 0x7E | sign[nan]
+    return out.reshape(shape)
+
+
+FP8_FORMATS = {
+    "e4m3": (e4m3_encode, e4m3_decode, E4M3_MAX),
+    "e5m2": (e5m2_encode, e5m2_decode, E5M2_MAX),
+}

@@ -29,7 +29,7 @@ fp32 scalars and vectors as float32.
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, f64_to_bf16_bits, bf16_round, e4m3_decode, e4m3_encode, E4M3_MAX
+from .codecs import bf16_bits_to_f64, f64_to_bf16_bits, bf16_round, e4m3_decode, e4m3_encode, E4M3_MAX, FP8_FORMATS
 
 
 def _f32(x):
@@ -100,35 +100,38 @@ def absmax_of(bits):
     return _f32(np.max(np.abs(x))) if x.size else _f32(0.0)
 
 
-def scales_from_absmax(absmax):
+def scales_from_absmax(absmax, fmt="e4m3"):
     """(scale, inv) for a per-tensor abs-max.
 
     Reading (the pages only name a ``scale()`` slot next to ``abs_max()``,
     llama_run_state.cpp ``allocate_fwd_quant_tensors``): scale is the
-    dequantisation factor absmax/448 and inv = 448/absmax multiplies the input;
+    dequantisation factor absmax/max and inv = max/absmax multiplies the input,
+    with max the format's largest finite value (448 for e4m3, 57344 for e5m2);
     both are IEEE fp32 quotients.  An all-zero tensor gets scale = inv = 1.
     """
+    fmax = FP8_FORMATS[fmt][2]
     am = np.float64(_f32(absmax))
     if am > 0:
-        return _f32(am / E4M3_MAX), _f32(E4M3_MAX / am)
+        return _f32(am / fmax), _f32(fmax / am)
     return _f32(1.0), _f32(1.0)
 
 
-def quant_absmax(x_bits, absmax=None):
+def quant_absmax(x_bits, absmax=None, fmt="e4m3"):
     """Per-tensor abs-max e4m3 quantisation (llama_model.cpp, ``forward_qmm``:
     ``quantize_with_abs_max(inp.Quant, inp.Quant.scale(), inp.Value,
     inp.Quant.abs_max(), ...)``).  With absmax None it is computed first.
 
       q = e4m3( fp32( x * inv ) ),   scale = absmax / 448
 
-    The product that decides the code is taken in fp32.
+    The product that decides the code is taken in fp32.  fmt "e5m2" gives the
+    other FP8 gradient format, with its own largest value.
     Returns (codes uint8, scale float32, absmax float32).
     """
     if absmax is None:
         absmax = absmax_of(x_bits)
-    scale, inv = scales_from_absmax(absmax)
+    scale, inv = scales_from_absmax(absmax, fmt)
     x32 = bf16_bits_to_f64(x_bits).astype(np.float32)
-    q = e4m3_encode(x32 * inv)
+    q = FP8_FORMATS[fmt][0](x32 * inv)
     return q, scale, _f32(absmax)
 
 

@@ -300,3 +300,50 @@ def test_block_backward_zero_gate_and_accumulators():
     bwd2 = O.block_backward(fwd, d_out, d["w_norm"], w_gu, d["w_d"], acc=acc)
     assert np.array_equal(bwd2["dw_d"], acc["dw_d"])
     assert np.array_equal(bwd2["dw_norm"], (bwd["dw_norm"].astype(np.float64) + 1.0).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- e5m2 gradients
+
+def _e5m2_valued(shape, seed):
+    """bf16 bits of e5m2 values of magnitude at most 2^15 whose abs-max is
+    57344 (so the per-tensor e5m2 scale is 1 and quantisation returns them)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x7C, shape).astype(np.uint8) | (rng.integers(0, 2, shape).astype(np.uint8) << 7)
+    codes.flat[0] = 0x7B
+    return W.to_bf16_bits(K.e5m2_decode(codes).astype(np.float32))
+
+
+def test_linear_bwd_e5m2_gradient_equals_bf16_with_unit_scales():
+    N, C, OC = 24, 64, 32
+    x, w = _e4m3_valued((N, C), 40), _e4m3_valued((OC, C), 41)
+    dy = _e5m2_valued((N, OC), 42)
+    qx, sx, _ = O.quant_absmax(x)
+    qw, sw, _ = O.quant_absmax(w)
+    f8 = O.linear_bwd(dy, x, w, fp8=True, qx=qx, sx=sx, qw=qw, sw=sw, grad_fmt="e5m2")
+    b16 = O.linear_bwd(dy, x, w)
+    assert f8["sdy"] == 1
+    assert np.array_equal(K.e5m2_decode(f8["qdy"]), K.bf16_bits_to_f64(dy))
+    assert np.array_equal(f8["dx"], b16["dx"]) and np.array_equal(f8["dw"], b16["dw"])
+
+
+def test_e5m2_gradient_scale_uses_its_own_maximum():
+    dy = rand_bits((16, 32), 1.0, 43)
+    am = O.absmax_of(dy)
+    q, s, _ = O.quant_absmax(dy, am, "e5m2")
+    assert s == np.float32(np.float64(am) / 57344.0)
+    assert np.max(np.abs(K.e5m2_decode(q))) == 57344.0
+
+
+@pytest.mark.parametrize("grad_fmt", ["e4m3", "e5m2"])
+def test_block_backward_fp8_gradient_formats_against_autograd(grad_fmt):
+    N, C, H, eps = 48, 128, 96, 1e-5
+    d = W.block_inputs(N, C, H, seed=31, w_std=0.1)
+    d_out = rand_bits((N, C), 1.0, 32)
+    fwd = O.block_forward(d["inp"], d["addend"], d["w_norm"], d["w_gu"], d["w_d"], eps, fp8=True)
+    bwd = O.block_backward(fwd, d_out, d["w_norm"], d["w_gu"], d["w_d"], fp8=True, grad_fmt=grad_fmt)
+    ref = _torch_block_grads(d, eps, d_out)
+    # e5m2 keeps two mantissa bits against e4m3's three
+    tol = 0.12 if grad_fmt == "e4m3" else 0.2
+    for k in ("d_residual", "dw_gu", "dw_d"):
+        assert rel(K.bf16_bits_to_f64(bwd[k]), ref[k].numpy()) < tol, k
+    assert rel(bwd["dw_norm"], ref["dw_norm"].numpy()) < tol

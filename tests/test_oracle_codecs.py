@@ -157,3 +157,83 @@ def test_e4m3_encode_special_values():
     # subnormal grid 2^-9 with ties to even: 0.5 ulp -> 0, 1.5 ulp -> 2, 2.5 -> 2
     s = 2.0 ** -9
     assert list(K.e4m3_encode(np.array([0.5 * s, 1.5 * s, 2.5 * s, 7.5 * s]))) == [0, 2, 2, 8]
+
+
+# ----------------------------------------------------------------------------- e5m2
+
+def test_e5m2_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    got = K.e5m2_decode(codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])          # includes +-inf at 0x7C / 0xFC
+    assert set(np.flatnonzero(nan)) == {0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF}
+
+
+def test_e5m2_format_landmarks():
+    fi = torch.finfo(torch.float8_e5m2)
+    d = K.e5m2_decode(np.arange(256, dtype=np.uint8))
+    fin = np.isfinite(d)
+    assert np.max(d[fin]) == K.E5M2_MAX == fi.max == 57344.0
+    assert d[0x04] == fi.smallest_normal == 2.0 ** -14
+    assert d[0x01] == 2.0 ** -16
+    assert d[0x3C] == 1.0 and d[0xBC] == -1.0
+    assert d[0x7B] == 57344.0 and d[0xFB] == -57344.0
+    assert d[0x7C] == np.inf and d[0xFC] == -np.inf
+    assert fin.sum() == 248 and len(np.unique(d[fin])) == 247
+
+
+def _brute_e5m2(x):
+    """Nearest finite code by exhaustive search; ties to the code with an even
+    mantissa; |x| >= 57344 saturates; the sign of zero is kept."""
+    codes = np.arange(128, dtype=np.int64)
+    vals = K.e5m2_decode(codes.astype(np.uint8))
+    fin = np.isfinite(vals)
+    codes, vals = codes[fin], vals[fin]
+    out = np.empty(x.shape, np.uint8)
+    for idx, v in enumerate(x):
+        a = min(abs(v), K.E5M2_MAX)
+        d = np.abs(vals - a)
+        cand = codes[np.flatnonzero(d == d.min())]
+        if len(cand) > 1:
+            cand = cand[(cand & 1) == 0]
+        c = int(cand[0])
+        if np.signbit(v):
+            c |= 0x80
+        out[idx] = c
+    return out
+
+
+def test_e5m2_encode_brute_force():
+    rng = np.random.default_rng(12)
+    vals = K.e5m2_decode(np.arange(0, 0x7C, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([
+        rng.standard_normal(3000) * np.exp(rng.uniform(-12, 11, 3000)),
+        mids, -mids, vals, -vals,
+        [0.0, -0.0, 57344.0, 61440.0, 65536.0, 1e9, -1e9, 2.0 ** -17, 3 * 2.0 ** -17, 2.0 ** -18],
+    ])
+    assert np.array_equal(K.e5m2_encode(x), _brute_e5m2(x))
+
+
+def test_e5m2_encode_matches_torch_on_all_bf16_times_scales():
+    bits = _all_bf16()
+    x = K.bf16_bits_to_f64(bits).astype(np.float32)
+    x = x[np.isfinite(x)]
+    for inv in [1.0, 0.37, 3.1, 279.72677, 1.0 / 57344.0, 57344.0 / 7.5]:
+        p = x * np.float32(inv)
+        p = p[np.isfinite(p)]
+        want = torch.from_numpy(np.clip(p, -57344, 57344)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+        got = K.e5m2_encode(p)
+        assert np.array_equal(got, want), inv
+
+
+def test_e5m2_encode_special_values():
+    assert K.e5m2_encode(np.array([np.nan]))[0] == 0x7E
+    assert K.e5m2_encode(np.array([-np.nan]))[0] == 0xFE
+    assert K.e5m2_encode(np.array([-0.0]))[0] == 0x80
+    assert K.e5m2_encode(np.array([1e30]))[0] == 0x7B
+    assert K.e5m2_encode(np.array([-np.inf]))[0] == 0xFB
+    s = 2.0 ** -16
+    assert list(K.e5m2_encode(np.array([0.5 * s, 1.5 * s, 2.5 * s, 3.5 * s]))) == [0, 2, 2, 4]
