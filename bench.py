@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--decode-m", type=int, default=1, help="decode workload: tokens per call (1..4 off split)")
     p.add_argument("--backward", action="store_true",
                    help="block workloads: time the FFN block backward (after one forward) instead of the forward")
+    p.add_argument("--grad-dtype", default="e4m3", choices=["e4m3", "e5m2"],
+                   help="FP8 backward: the format of the quantised gradients (weights and activations stay e4m3)")
     p.add_argument("--known-h-absmax", action="store_true",
                    help="FP8 block workloads: quantise h in the gate+up epilogue with the previous step's abs-max "
                         "(ffn_gateup_swiglu_quant, the recompute form) instead of bf16 h + ffn_quant_absmax")
@@ -78,7 +80,10 @@ def parse():
                    help="no benchmark: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
                         "rocprofv3 run of this script (--copy-calibration) into the workload's entry of "
                         "profiles/traffic.json")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.grad_dtype != "e4m3" and not a.backward:
+        p.error("--grad-dtype applies to the backward (--backward)")
+    return a
 
 
 def src_digest(name):
@@ -101,7 +106,7 @@ def measured_traffic(key, src):
 # dominant kernel per workload: traffic.json key, its source file, the kernel
 # name fragments whose per-dispatch counters make up one launch of the entry
 # point, and the algorithmic bytes of that launch
-def traffic_spec(workload, known_h_absmax=False, backward=False):
+def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3"):
     """(traffic.json key, source file, kernel-name fragments of one launch,
     description, algorithmic bytes of one launch, dispatch stride) for the
     dominant kernel.  A stride of 2 takes every second matching dispatch
@@ -113,9 +118,12 @@ def traffic_spec(workload, known_h_absmax=False, backward=False):
     if backward:
         e = 1 if w.fp8 else 2
         fp8 = "true" if w.fp8 else "false"
+        e5 = w.fp8 and grad_dtype == "e5m2"
+        what = ("e5m2 x e4m3" if e5 else "e4m3") if w.fp8 else "bf16"
         # reads dgu^T [2H, N] and y^T [C, N] once, reads and writes dW_gu [2H, C]
-        return (f"dwup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, false, false, true>"],
-                f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, accumulating) of the up projection's weight "
+        return (f"dwup{'5' if e5 else ''}_{workload}", "gemm.hip",
+                [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}>"],
+                f"gemm_kernel ({what}, accumulating) of the up projection's weight "
                 f"gradient, [2H, C] = [{2 * H}, {C}], K = N = {N}",
                 2 * H * N * e + C * N * e + 2 * (2 * H * C * 2), 2)
     if workload == "decode":
@@ -126,10 +134,10 @@ def traffic_spec(workload, known_h_absmax=False, backward=False):
     fp8 = "true" if w.fp8 else "false"
     if known_h_absmax:
         # reads x and w, writes the e4m3 codes of h
-        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false>"],
+        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false, false>"],
                 f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation) of ffn_gateup_swiglu_quant, "
                 f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, 1)
-    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false>"],
+    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false>"],
             f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
             N * C * elt + 2 * H * C * elt + N * H * 2, 1)
 
@@ -139,7 +147,7 @@ def ingest_pmc(a):
     rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
     scaled by what the counter reads for the 1 GiB calibration copy."""
     import csv
-    key, src, frags, desc, algo, stride = traffic_spec(a.workload, a.known_h_absmax, a.backward)
+    key, src, frags, desc, algo, stride = traffic_spec(a.workload, a.known_h_absmax, a.backward, a.grad_dtype)
     rec = {"kernel": desc, "src": f"transformer_ffn_block_residual_amd/csrc/{src}", "src_sha256": src_digest(src)}
     total = 0.0
     for counter, path, truth_kb in (("FETCH_SIZE", a.ingest_pmc[0], 1 << 20), ("WRITE_SIZE", a.ingest_pmc[1], 1 << 20)):
@@ -479,7 +487,7 @@ BWD_PHASES = {
 }
 
 
-def cpu_backward_sample(w, d, rows):
+def cpu_backward_sample(w, d, rows, grad_fmt="e4m3"):
     """The oracle forward + backward of the block over the first `rows` token
     rows (full weights; FP8 weights quantised beforehand, as in the forward
     sample); only the backward is timed."""
@@ -488,7 +496,7 @@ def cpu_backward_sample(w, d, rows):
     d_out = _bwd_dout(np, w, rows)
     fwd = O.block_forward(d["inp"][:rows], d["addend"][:rows], d["w_norm"], d["w_gu"], d["w_d"], w.eps, fp8=w.fp8)
     t0 = time.perf_counter()
-    O.block_backward(fwd, d_out, d["w_norm"], d["w_gu"], d["w_d"], fp8=w.fp8)
+    O.block_backward(fwd, d_out, d["w_norm"], d["w_gu"], d["w_d"], fp8=w.fp8, grad_fmt=grad_fmt)
     dt = time.perf_counter() - t0
     flops = 12.0 * rows * w.C * w.H
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
@@ -515,7 +523,8 @@ def bench_backward(a, torch, np, B, block, W):
 
     pre = block.PrefillBlock(N, C, H, w.eps, w.fp8)
     pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pre, in_place=False)
+    gd = a.grad_dtype if w.fp8 else "e4m3"
+    bb = block.BackwardBlock(pre, in_place=False, grad_dtype=gd)
     bb.forward(dev(d["inp"]), dev(d["addend"]))
     d_out = dev(_bwd_dout(np, w, N))
     # the abs-max of d_out, as its producer (the next block's RMSNorm backward)
@@ -569,22 +578,26 @@ def bench_backward(a, torch, np, B, block, W):
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": f"FFN block backward of the {a.workload} workload: N={N} C={C} H={H}, "
-                               + ("FP8 (per-tensor e4m3 weights, activations and gradients)" if w.fp8 else "bf16")
+                               + (("FP8 (per-tensor e4m3 weights, activations and gradients)" if gd == "e4m3" else
+                                   "FP8 (per-tensor e4m3 weights and activations, e5m2 gradients)") if w.fp8
+                                  else "bf16")
                                + "; down and up backward_qmm (data and weight gradients), SwiGLU and RMSNorm "
                                  "backward, weight transposes included; the abs-max of the incoming gradient comes "
                                  "with it (its producer, the next block's RMSNorm backward, writes it)",
-                   "N": N, "C": C, "H": H, "seed": w.seed, "backward": True},
-        "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({'e4m3' if w.fp8 else 'bf16'}, accumulate): "
+                   "N": N, "C": C, "H": H, "seed": w.seed, "backward": True,
+                   **({"grad_dtype": gd} if w.fp8 else {})},
+        "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({(gd if w.fp8 else 'bf16')}, accumulate): "
                                                  "the up projection's weight gradient [2H, C], K = N",
                      "achieved": dw_tf, "peak": peak, "unit": "TFLOP/s", "frac": dw_tf / peak,
-                     "traffic": measured_traffic(f"dwup_{a.workload}", "gemm.hip")},
+                     "traffic": measured_traffic(traffic_spec(a.workload, backward=True, grad_dtype=gd)[0],
+                                                 "gemm.hip")},
         "kernels": kernels,
         "spread_ms": spread,
         "ms_per_step_in_hip_graph": graph_ms,
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_backward_sample(w, d, a.cpu_rows or min(N, 256))
+        out["cpu_baseline"] = cpu_backward_sample(w, d, a.cpu_rows or min(N, 256), gd)
     return out
 
 

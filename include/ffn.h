@@ -52,7 +52,10 @@ typedef enum {
 
 typedef enum {
     FFN_BF16 = 0,             /* bf16 operands, no scales                          */
-    FFN_E4M3 = 1              /* e4m3 operands with per-tensor fp32 scales         */
+    FFN_E4M3 = 1,             /* e4m3 operands with per-tensor fp32 scales         */
+    FFN_E5M2 = 2              /* e5m2 gradient codes (scale absmax / 57344) beside
+                                 e4m3 weights and activations: the backward's other
+                                 FP8 grad dtype                                     */
 } ffn_dtype_t;
 
 /* Fused residual add + RMSNorm, saving rstd, with the output's abs-max.
@@ -218,12 +221,15 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
  * and ffn_transpose / ffn_quant_transpose the transposes. */
 
 /* TN matmul: out[m,n] = bf16(acc + sum_k a[m,k] * b[n,k] (* a_scale * b_scale
- * for E4M3)), acc = out[m,n] when accumulate != 0 (the accumulate_gradient flag
+ * for FP8)), acc = out[m,n] when accumulate != 0 (the accumulate_gradient flag
  * of backward_qmm: one rounding of the fp32 sum), else 0.  [llmq model]
- * backward_qmm, matmul(..., EMMTranspose::TN, accumulate_gradient).
- * out: bf16 [M,N]; a: [M,K], b: [N,K], both bf16 or both e4m3; scales fp32 [1]
- * (E4M3 only).  Supported: K % 128 == 0, N % 128 == 0, any M >= 0; out must
- * not alias a or b. */
+ * backward_qmm, matmul(..., EMMTranspose::TN, accumulate_gradient); the
+ * gradient operand is allocated in the grad dtype (e4m3 or e5m2), the weight
+ * and activation operands in e4m3.
+ * out: bf16 [M,N]; a: [M,K], b: [N,K]; dtype FFN_BF16: both bf16, FFN_E4M3:
+ * both e4m3, FFN_E5M2: a e5m2 (the gradient), b e4m3; scales fp32 [1] (FP8
+ * only).  Supported: K % 128 == 0, N % 128 == 0, any M >= 0; out must not
+ * alias a or b. */
 ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale,
                            const void* b, const float* b_scale, ffn_dtype_t dtype,
                            int accumulate, int64_t M, int64_t N, int64_t K,
@@ -239,16 +245,18 @@ ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols
                            int64_t ld_out, int elt_bytes, hipStream_t stream);
 
 /* Quantise with a known abs-max and transpose in one pass: q_t[c, r] =
- * e4m3(x[r, c] * 448 / absmax), *scale = absmax / 448 (1 and 1 for absmax 0),
- * zero codes for rows <= r < ld_out.  [llmq model] backward_qmm,
- * quantize_and_transpose_with_abs_max (and, with q, quantize_with_abs_max of
- * the same tensor from the same read: backward_qmm quantises the output
- * gradient in both layouts).  x: bf16 [rows, cols]; q_t: e4m3 [cols, ld_out];
- * q (nullable): e4m3 [rows, cols], the codes in x's layout; absmax: fp32 [1]
- * (device, read).  Constraints as ffn_transpose; q must not alias q_t or x. */
+ * fp8(x[r, c] * max / absmax), *scale = absmax / max (1 and 1 for absmax 0),
+ * zero codes for rows <= r < ld_out; max = 448 for code_dtype FFN_E4M3, 57344
+ * for FFN_E5M2 (codes saturate at +-max).  [llmq model] backward_qmm,
+ * quantize_and_transpose_with_abs_max into the grad dtype (and, with q,
+ * quantize_with_abs_max of the same tensor from the same read: backward_qmm
+ * quantises the output gradient in both layouts).  x: bf16 [rows, cols]; q_t:
+ * codes [cols, ld_out]; q (nullable): codes [rows, cols] in x's layout;
+ * absmax: fp32 [1] (device, read).  Constraints as ffn_transpose; q must not
+ * alias q_t or x. */
 ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const void* x,
-                                 const float* absmax, int64_t rows, int64_t cols,
-                                 int64_t ld_out, hipStream_t stream);
+                                 const float* absmax, ffn_dtype_t code_dtype, int64_t rows,
+                                 int64_t cols, int64_t ld_out, hipStream_t stream);
 
 /* SwiGLU backward.  [llmq model] _backward_block, swiglu_backward(DMlpUp,
  * DSwiGLU, MlpUp, DMlpUp abs-max, B, T, D).  With g = gu[n,j], u = gu[n,H+j],

@@ -82,6 +82,7 @@ def test_gemm_validation(lib):
     f = lib.ffn_gateup
     assert f(A, None, A, None, A, None, 1, 1, 64, 256, 768, None) == INVALID   # fp8 without scales
     assert f(A, None, A, A, A, A, 7, 1, 64, 256, 768, None) == INVALID         # unknown dtype
+    assert f(A, None, A, A, A, A, 2, 1, 64, 256, 768, None) == INVALID         # e5m2: gradients only
     assert f(A, None, A, None, A, None, 0, 1, 64, 200, 768, None) == UNSUPPORTED  # C % 128
     assert f(A, None, A, None, A, None, 0, 1, 64, 256, 100, None) == UNSUPPORTED  # H % 128
     assert f(A, None, A, None, A, None, 0, 1, -64, 256, 768, None) == INVALID
@@ -147,7 +148,9 @@ def test_backward_validation(lib):
     m = lib.ffn_matmul_tn  # out, a, sa, b, sb, dtype, accumulate, M, N, K
     assert m(None, B_, None, C_, None, 0, 0, 64, 256, 128, None) == INVALID
     assert m(A, B_, None, C_, None, 1, 0, 64, 256, 128, None) == INVALID           # E4M3 without scales
+    assert m(A, B_, None, C_, None, 2, 0, 64, 256, 128, None) == INVALID           # E5M2 without scales
     assert m(A, B_, None, C_, None, 5, 0, 64, 256, 128, None) == INVALID           # unknown dtype
+    assert m(A, B_, D, C_, D, 2, 0, 64, 200, 128, None) == UNSUPPORTED             # E5M2, N % 128
     assert m(A, B_, None, C_, None, 0, 0, 64, 200, 128, None) == UNSUPPORTED       # N % 128
     assert m(A, B_, None, C_, None, 0, 0, 64, 256, 96, None) == UNSUPPORTED        # K % 128
     assert m(A, A, None, C_, None, 0, 0, 64, 256, 128, None) == INVALID            # out aliases a
@@ -160,11 +163,13 @@ def test_backward_validation(lib):
     assert t(A, B_, 37, 64, 40, 2, None) == UNSUPPORTED                            # ld_out % 16
     assert t(A, A, 37, 64, 48, 2, None) == INVALID                                 # in place
     assert t(A, MIS, 37, 64, 48, 1, None) == UNSUPPORTED
-    q = lib.ffn_quant_transpose  # q_t, q, scale, x, absmax, rows, cols, ld_out
-    assert q(A, None, B_, C_, None, 37, 64, 48, None) == INVALID                   # no abs-max
-    assert q(A, None, B_, C_, D, 37, 64, 32, None) == INVALID                      # ld_out < rows
-    assert q(A, A, B_, C_, D, 37, 64, 48, None) == INVALID                         # q aliases q_t
-    assert q(A, MIS, B_, C_, D, 37, 64, 48, None) == UNSUPPORTED                   # misaligned q
+    q = lib.ffn_quant_transpose  # q_t, q, scale, x, absmax, code dtype, rows, cols, ld_out
+    assert q(A, None, B_, C_, None, 1, 37, 64, 48, None) == INVALID                # no abs-max
+    assert q(A, None, B_, C_, D, 1, 37, 64, 32, None) == INVALID                   # ld_out < rows
+    assert q(A, A, B_, C_, D, 2, 37, 64, 48, None) == INVALID                      # q aliases q_t
+    assert q(A, MIS, B_, C_, D, 1, 37, 64, 48, None) == UNSUPPORTED                # misaligned q
+    assert q(A, None, B_, C_, D, 0, 37, 64, 48, None) == INVALID                   # bf16 is no code format
+    assert q(A, None, B_, C_, D, 3, 37, 64, 48, None) == INVALID                   # unknown code format
     g = lib.ffn_swiglu_bwd  # dgu, absmax, dh, gu, N, H
     assert g(A, None, A, C_, 4, 64, None) == INVALID                               # dgu aliases dh
     assert g(A, None, B_, C_, 4, 60, None) == UNSUPPORTED                          # H % 8

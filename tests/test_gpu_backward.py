@@ -96,6 +96,37 @@ def test_quant_transpose(F, rows, cols, ld):
         assert host_f32(sc)[0] == s_ref
 
 
+def wide_bits(shape, seed):
+    """bf16 values with magnitudes 2^-40 .. 2^3, evenly spread in the exponent,
+    random signs and mantissas: quantised against their abs-max they reach
+    the e5m2 subnormals and zero as well as its normals."""
+    rng = np.random.default_rng(seed)
+    v = np.exp2(rng.uniform(-40.0, 3.0, shape)) * rng.choice([-1.0, 1.0], shape)
+    return W.to_bf16_bits(v.astype(np.float32))
+
+
+@pytest.mark.parametrize("rows,cols,ld", [(37, 64, 48), (300, 3584, 384), (256, 128, 256)])
+def test_quant_transpose_e5m2(F, rows, cols, ld):
+    say(f"quant_transpose e5m2 rows={rows} cols={cols} ld={ld}")
+    x = wide_bits((rows, cols), rows + 5 * cols)
+    am = O.absmax_of(x)
+    for given in (am, np.float32(am * 0.25), np.float32(0.0)):
+        qt, q, sc = empty_u8(cols, ld).fill_(5), empty_u8(rows, cols).fill_(6), empty_f32(1)
+        F.ffn_quant_transpose(qt, q, sc, dev_bf16(x), dev_f32([given]), rows, cols, ld, code_dtype=F.FFN_E5M2)
+        torch.cuda.synchronize()
+        q_ref, s_ref, _ = O.quant_absmax(x, given, "e5m2")
+        codes = host_u8(q)
+        assert np.array_equal(host_u8(qt), padded_t(q_ref, ld))
+        assert np.array_equal(codes, q_ref)
+        assert host_f32(sc)[0] == s_ref
+        if given == am:
+            # the spread reaches every e5m2 binade: subnormal codes and zeros
+            assert np.any(((codes & 0x7C) == 0) & ((codes & 0x03) != 0)) and np.any((codes & 0x7F) == 0)
+        if given == np.float32(am * 0.25):
+            # values beyond the given abs-max saturate at +-57344 (0x7B / 0xFB)
+            assert np.any((codes & 0x7F) == 0x7B) and not np.any((codes & 0x7C) == 0x7C)
+
+
 # ----------------------------------------------------------------------------- TN products
 
 MM_SHAPES = [(1, 128, 128), (37, 256, 640), (300, 384, 256), (513, 128, 1024)]
@@ -141,6 +172,46 @@ def test_matmul_tn_random_fp8_scaled_accumulate(F, M, N, Kd):
     s = np.float64(np.float32(np.float64(sa) * np.float64(sb)))
     exact = (K.e4m3_decode(qa) @ K.e4m3_decode(qb).T) * s + K.bf16_bits_to_f64(acc0)
     mag = (np.abs(K.e4m3_decode(qa)) @ np.abs(K.e4m3_decode(qb)).T) * s + np.abs(K.bf16_bits_to_f64(acc0))
+    assert np.all(within_dot_bound(host_bits(out), exact, mag))
+
+
+@pytest.mark.parametrize("M,N,Kd", MM_SHAPES)
+def test_matmul_tn_e5m2_gradient_exact(F, M, N, Kd):
+    """a in e5m2, b in e4m3 (FFN_E5M2): integer-valued codes and e5m2
+    subnormals times small integers, whose fp32 sums are exact, so the bf16
+    result is unique; plain and accumulating."""
+    say(f"matmul_tn e5m2 exact M={M} N={N} K={Kd}")
+    rng = np.random.default_rng(M * 3 + Kd)
+    # e5m2 codes of -4..4 and of the subnormals +-2^-16 .. +-3 * 2^-16
+    ints = K.e5m2_encode(rng.integers(-4, 5, (M, Kd)).astype(np.float64))
+    subn = rng.choice(np.array([0x00, 0x01, 0x02, 0x03, 0x81, 0x82, 0x83], np.uint8), (M, Kd))
+    qb = K.e4m3_encode(rng.integers(-2, 3, (N, Kd)).astype(np.float64))
+    one = dev_f32([1.0])
+    acc0 = int_bits((M, N), -8, 8, M + 99)
+    for qa in (ints, subn):
+        out = empty_bf16(M, N).fill_(3.0)
+        F.ffn_matmul_tn(out, dev_u8(qa), one, dev_u8(qb), one, F.FFN_E5M2, 0, M, N, Kd)
+        acc = dev_bf16(acc0)
+        F.ffn_matmul_tn(acc, dev_u8(qa), one, dev_u8(qb), one, F.FFN_E5M2, 1, M, N, Kd)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), O.matmul_tn(qa, qb, 1.0, 1.0, a_fmt="e5m2"))
+        assert np.array_equal(host_bits(acc), O.matmul_tn(qa, qb, 1.0, 1.0, accumulate=acc0, a_fmt="e5m2"))
+
+
+@pytest.mark.parametrize("M,N,Kd", [(37, 256, 640), (300, 384, 1024)])
+def test_matmul_tn_random_e5m2_scaled_accumulate(F, M, N, Kd):
+    say(f"matmul_tn e5m2 random M={M} N={N} K={Kd}")
+    a, b = wide_bits((M, Kd), 21), rand_bits((N, Kd), 1.0, 22)
+    qa, sa, _ = O.quant_absmax(a, fmt="e5m2")
+    qb, sb, _ = O.quant_absmax(b)
+    acc0 = rand_bits((M, N), 50.0, 23)
+    out = dev_bf16(acc0)
+    F.ffn_matmul_tn(out, dev_u8(qa), dev_f32([sa]), dev_u8(qb), dev_f32([sb]), F.FFN_E5M2, 1, M, N, Kd)
+    torch.cuda.synchronize()
+    s = np.float64(np.float32(np.float64(sa) * np.float64(sb)))
+    da, db = K.e5m2_decode(qa), K.e4m3_decode(qb)
+    exact = (da @ db.T) * s + K.bf16_bits_to_f64(acc0)
+    mag = (np.abs(da) @ np.abs(db).T) * s + np.abs(K.bf16_bits_to_f64(acc0))
     assert np.all(within_dot_bound(host_bits(out), exact, mag))
 
 
@@ -206,12 +277,12 @@ def test_rmsnorm_bwd(F, N, C):
 
 # ----------------------------------------------------------------------------- the block
 
-def _run_block(F, N, C, H, fp8, seed, w_std=0.1):
+def _run_block(F, N, C, H, fp8, seed, w_std=0.1, in_place=True, grad_dtype="e4m3"):
     from transformer_ffn_block_residual_amd import block
     d = W.block_inputs(N, C, H, seed=seed, w_std=w_std)
     pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
     pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pb)
+    bb = block.BackwardBlock(pb, in_place=in_place, grad_dtype=grad_dtype)
     d_out = rand_bits((N, C), 1.0, seed + 1)
     bb.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
     d_out_dev = dev_bf16(d_out)
@@ -253,6 +324,60 @@ def test_block_backward_against_the_oracle(F, N, C, H, fp8):
         assert err < tol, (name, err)
     dwn = host_f32(bb.dw_norm)
     assert np.max(np.abs(dwn - ref["dw_norm"])) <= tol * np.max(np.abs(ref["dw_norm"]))
+
+
+@pytest.mark.parametrize("N,C,H", [(200, 384, 256), (129, 256, 640)])
+def test_block_backward_e5m2_gradients(F, N, C, H):
+    """The FP8 backward with e5m2 gradient codes.  Stage by stage on the
+    GPU's own upstream tensors: the gradient codes and scales exactly, each TN
+    product within the dot bound of its exact value; then end to end against
+    the oracle's e5m2 chain, normwise within 6e-2 (twice the e4m3 chain's
+    3e-2: e5m2 keeps one mantissa bit less)."""
+    say(f"block backward e5m2 N={N} C={C} H={H}")
+    d, pb, bb, d_out = _run_block(F, N, C, H, True, seed=N + H + 1, in_place=False, grad_dtype="e5m2")
+    dec5, dec4 = K.e5m2_decode, K.e4m3_decode
+    f32 = lambda v: np.float64(np.float32(v))
+
+    def tn_close(got, a_codes, b_codes, sa, sb):
+        s = f32(np.float64(sa) * np.float64(sb))
+        A, Bm = dec5(a_codes), dec4(b_codes)
+        return np.all(within_dot_bound(got, (A @ Bm.T) * s, (np.abs(A) @ np.abs(Bm).T) * s))
+
+    # output gradient: abs-max computed here, codes in both layouts
+    q_dout, s_dout, _ = O.quant_absmax(d_out, fmt="e5m2")
+    assert np.array_equal(host_u8(bb.qdout), q_dout) and host_f32(bb.s_dout)[0] == s_dout
+    assert np.array_equal(host_u8(bb.dout_t), padded_t(q_dout, bb.Np))
+    wd, s_d = host_u8(pb.w_d), host_f32(pb.s_d)[0]           # [C, H] e4m3
+    g_dh = host_bits(bb.dh)
+    assert tn_close(g_dh, q_dout, O.transpose(wd), s_dout, s_d)
+    qh, s_h = host_u8(pb.qh), host_f32(pb.s_h)[0]
+    assert tn_close(host_bits(bb.dw_d), O.transpose(q_dout), O.transpose(qh), s_dout, s_h)
+    # dMlpUp from the GPU's dh and gu, its abs-max, its e5m2 codes
+    g_dgu = host_bits(bb.dgu)
+    dgu_ref, _ = O.swiglu_bwd(g_dh, host_bits(bb.gu))
+    assert rel_err(g_dgu, dgu_ref) < 1e-2
+    am_dgu = host_f32(bb.am_dgu)[0]
+    assert am_dgu == O.absmax_of(g_dgu)
+    q_dgu, s_dgu, _ = O.quant_absmax(g_dgu, am_dgu, "e5m2")
+    assert np.array_equal(host_u8(bb.qdgu), q_dgu) and host_f32(bb.s_dgu)[0] == s_dgu
+    assert np.array_equal(host_u8(bb.dgu_t), padded_t(q_dgu, bb.Np))
+    wgu, s_gu = host_u8(pb.w_gu), host_f32(pb.s_gu)[0]       # [2H, C] e4m3
+    assert tn_close(host_bits(bb.dy), q_dgu, O.transpose(wgu), s_dgu, s_gu)
+    qy, s_y = host_u8(pb.qy), host_f32(pb.s_y)[0]
+    assert tn_close(host_bits(bb.dw_gu), O.transpose(q_dgu), O.transpose(qy), s_dgu, s_y)
+    # end to end against the oracle's e5m2 chain
+    fwd = O.block_forward(d["inp"], d["addend"], d["w_norm"], d["w_gu"], d["w_d"], 1e-5, fp8=True)
+    ref = O.block_backward(fwd, d_out, d["w_norm"], d["w_gu"], d["w_d"], fp8=True, grad_fmt="e5m2")
+
+    def normwise(g, r):
+        g, r = K.bf16_bits_to_f64(g), K.bf16_bits_to_f64(r)
+        return np.max(np.abs(g - r)) / np.max(np.abs(r))
+    for name, got in (("dh", g_dh), ("dgu", g_dgu), ("dy", host_bits(bb.dy)),
+                      ("d_residual", host_bits(bb.d_res)), ("dw_d", host_bits(bb.dw_d)),
+                      ("dw_gu", host_bits(bb.dw_gu))):
+        err = normwise(got, ref[name])
+        assert err < 6e-2, (name, err)
+    assert np.max(np.abs(host_f32(bb.dw_norm) - ref["dw_norm"])) <= 6e-2 * np.max(np.abs(ref["dw_norm"]))
 
 
 def test_block_backward_accumulates_weight_gradients(F):

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libffn.so")
 
 FFN_OK, FFN_ERR_INVALID, FFN_ERR_UNSUPPORTED, FFN_ERR_HIP = 0, 1, 2, 3
-FFN_BF16, FFN_E4M3 = 0, 1
+FFN_BF16, FFN_E4M3, FFN_E5M2 = 0, 1, 2
 _STATUS = {1: "FFN_ERR_INVALID", 2: "FFN_ERR_UNSUPPORTED", 3: "FFN_ERR_HIP"}
 
 
@@ -49,7 +49,7 @@ def _load():
         "ffn_decode_gemv_bf16": [P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_matmul_tn": [P, P, P, P, P, I32, I32, I64, I64, I64, P],
         "ffn_transpose": [P, P, I64, I64, I64, I32, P],
-        "ffn_quant_transpose": [P, P, P, P, P, I64, I64, I64, P],
+        "ffn_quant_transpose": [P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_swiglu_bwd": [P, P, P, P, I64, I64, P],
         "ffn_rmsnorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, P],
     }
@@ -116,6 +116,7 @@ def _ptr(t, name, numel, dtypes, optional=False):
 BF16 = (torch.bfloat16, torch.int16)
 F32 = (torch.float32,)
 E4M3 = (torch.uint8, torch.float8_e4m3fn)
+E5M2 = (torch.uint8, torch.float8_e5m2)
 
 
 def ffn_rmsnorm_fwd(y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C, stream=None):
@@ -249,10 +250,14 @@ def bind_decode_gemv_bf16(out, h, x, w_gate, w_up, w_down, M, C, H, stream=None)
 # ----------------------------------------------------------------------------- backward
 
 def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, accumulate, M, N, K, stream=None):
-    fp8 = dtype == FFN_E4M3
+    """dtype FFN_BF16 / FFN_E4M3: both operands in it; FFN_E5M2: a holds e5m2
+    codes (the gradient), b e4m3 codes."""
+    fp8 = dtype in (FFN_E4M3, FFN_E5M2)
+    a_dt = E5M2 if dtype == FFN_E5M2 else _dt_elems(dtype)
+    b_dt = E4M3 if fp8 else BF16
     _check(_lib.ffn_matmul_tn(
-        _ptr(out, "out", M * N, BF16), _ptr(a, "a", M * K, _dt_elems(dtype)),
-        _ptr(a_scale, "a_scale", 1, F32, optional=not fp8), _ptr(b, "b", N * K, _dt_elems(dtype)),
+        _ptr(out, "out", M * N, BF16), _ptr(a, "a", M * K, a_dt),
+        _ptr(a_scale, "a_scale", 1, F32, optional=not fp8), _ptr(b, "b", N * K, b_dt),
         _ptr(b_scale, "b_scale", 1, F32, optional=not fp8), int(dtype), int(bool(accumulate)),
         int(M), int(N), int(K), _stream(stream)))
 
@@ -264,11 +269,13 @@ def ffn_transpose(out, inp, rows, cols, ld_out, elt_bytes, stream=None):
         int(elt_bytes), _stream(stream)))
 
 
-def ffn_quant_transpose(q_t, q, scale, x, absmax, rows, cols, ld_out, stream=None):
+def ffn_quant_transpose(q_t, q, scale, x, absmax, rows, cols, ld_out, stream=None, code_dtype=FFN_E4M3):
+    """code_dtype: FFN_E4M3 (default) or FFN_E5M2, the format of q_t and q."""
+    dt = E5M2 if code_dtype == FFN_E5M2 else E4M3
     _check(_lib.ffn_quant_transpose(
-        _ptr(q_t, "q_t", cols * ld_out, E4M3), _ptr(q, "q", rows * cols, E4M3, optional=True),
+        _ptr(q_t, "q_t", cols * ld_out, dt), _ptr(q, "q", rows * cols, dt, optional=True),
         _ptr(scale, "scale", 1, F32), _ptr(x, "x", rows * cols, BF16),
-        _ptr(absmax, "absmax", 1, F32), int(rows), int(cols), int(ld_out), _stream(stream)))
+        _ptr(absmax, "absmax", 1, F32), int(code_dtype), int(rows), int(cols), int(ld_out), _stream(stream)))
 
 
 def ffn_swiglu_bwd(dgu, absmax, dh, gu, N, H, stream=None):
@@ -297,5 +304,5 @@ __all__ = [
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16",
     "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",
-    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "version", "last_error", "LIB_PATH",
+    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "version", "last_error", "LIB_PATH",
 ]

@@ -207,9 +207,17 @@ class BackwardBlock:
     three weights accumulate across calls (``zero_grads`` clears them).
     in_place: the SwiGLU backward overwrites gu with its gradient, as the
     trainer does; otherwise it goes to a buffer of its own (``dgu``) and gu
-    survives for another backward."""
+    survives for another backward.  grad_dtype ("e4m3" or "e5m2", FP8 blocks
+    only): the format of the quantised gradients (the output gradient and
+    dMlpUp), each scaled by its abs-max over that format's largest value;
+    weights and activations stay e4m3."""
 
-    def __init__(self, fwd, in_place=True):
+    def __init__(self, fwd, in_place=True, grad_dtype="e4m3"):
+        if grad_dtype not in ("e4m3", "e5m2"):
+            raise ValueError(f"grad_dtype {grad_dtype!r}: need 'e4m3' or 'e5m2'")
+        if grad_dtype == "e5m2" and not fwd.fp8:
+            raise ValueError("an e5m2 gradient needs an FP8 block")
+        self.grad_dtype = grad_dtype
         self.f = fwd
         N, C, H = fwd.N, fwd.C, fwd.H
         self.Np = _round_up(max(N, 1), 128)
@@ -274,14 +282,15 @@ class BackwardBlock:
         dgu = self.dgu
         mk = mark or (lambda label: None)
         if f.fp8:
-            E = B.FFN_E4M3
+            # gradient codes (the TN matmuls' a operand) in the grad dtype
+            E = B.FFN_E5M2 if self.grad_dtype == "e5m2" else B.FFN_E4M3
             # backward_qmm through the down projection (input h, weight [C, H])
             # the gradient's codes in both layouts from one read
             if d_out_absmax is None:
                 B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, stream)
             else:
                 self.am_dout = d_out_absmax
-            B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, stream)
+            B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, stream, E)
             mk("quant_dout")
             B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, stream)
             mk("transpose_w_down")
@@ -294,7 +303,7 @@ class BackwardBlock:
             B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
             mk("swiglu_bwd")
             # backward_qmm through the up projection (input y, weight [2H, C])
-            B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream)
+            B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream, E)
             mk("quant_dgu")
             B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 1, stream)
             mk("transpose_w_up")

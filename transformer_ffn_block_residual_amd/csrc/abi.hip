@@ -293,19 +293,21 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const
     NONNEG(M);
     NONNEG(N);
     NONNEG(K);
-    if (dtype != FFN_BF16 && dtype != FFN_E4M3) return fail(FFN_ERR_INVALID, "ffn_matmul_tn: unknown dtype %d", (int)dtype);
-    if (dtype == FFN_E4M3) {
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
+        return fail(FFN_ERR_INVALID, "ffn_matmul_tn: unknown dtype %d", (int)dtype);
+    const bool fp8 = dtype != FFN_BF16;
+    if (fp8) {
         REQUIRE(a_scale);
         REQUIRE(b_scale);
     }
-    const int elt = dtype == FFN_E4M3 ? 1 : 2;
+    const int elt = fp8 ? 1 : 2;
     if (ffn_status_t st = check_gemm_dims("ffn_matmul_tn", M, K, N, elt)) return st;
     ALIGNED(out);
     ALIGNED(a);
     ALIGNED(b);
     if (out == a || out == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn: out must not alias an operand");
-    return hip_status(ffn::launch_gemm(out, nullptr, a, a_scale, b, b_scale, dtype == FFN_E4M3, false, M, (int)K,
-                                       (int)N, stream, nullptr, nullptr, accumulate != 0),
+    return hip_status(ffn::launch_gemm(out, nullptr, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)N, stream,
+                                       nullptr, nullptr, accumulate != 0, dtype == FFN_E5M2),
                       "ffn_matmul_tn");
 }
 
@@ -336,16 +338,20 @@ ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols
 }
 
 ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const void* x, const float* absmax,
-                                 int64_t rows, int64_t cols, int64_t ld_out, hipStream_t stream) {
+                                 ffn_dtype_t code_dtype, int64_t rows, int64_t cols, int64_t ld_out,
+                                 hipStream_t stream) {
     REQUIRE(q_t);
     REQUIRE(scale);
     REQUIRE(x);
     REQUIRE(absmax);
+    if (code_dtype != FFN_E4M3 && code_dtype != FFN_E5M2)
+        return fail(FFN_ERR_INVALID, "ffn_quant_transpose: code dtype %d (need FFN_E4M3 or FFN_E5M2)", (int)code_dtype);
     if (ffn_status_t st = check_transpose("ffn_quant_transpose", q_t, x, rows, cols, ld_out)) return st;
     ALIGNED(q);
     if (q && (q == q_t || (const void*)q == x))
         return fail(FFN_ERR_INVALID, "ffn_quant_transpose: q must not alias q_t or x");
-    return hip_status(ffn::launch_transpose(q_t, q, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream),
+    return hip_status(ffn::launch_transpose(q_t, q, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream,
+                                            code_dtype == FFN_E5M2),
                       "ffn_quant_transpose");
 }
 

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ ou
 // consecutive lanes hold the eight 16-row groups of the same four columns, so
 // each store instruction writes whole 128-byte lines of eight output rows; the
 // row pitch (35 dwords) spreads those lanes' LDS reads over four bank groups.
-template <int kIn, bool kQuant>
+// kBf8: the quantised codes are e5m2 (scale absmax / 57344) instead of e4m3.
+template <int kIn, bool kQuant, bool kBf8 = false>
 __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ out, uint8_t* __restrict__ q_rows,
                                                          float* __restrict__ scale_out,
                                                          const float* __restrict__ absmax,
@@ -129,9 +130,12 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
     float inv = 1.0f;
     if (kQuant) {
         float scale;
-        scale_pair(*absmax, scale, inv);
+        scale_pair(*absmax, scale, inv, kBf8 ? kE5M2Max : kE4M3Max);
         if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *scale_out = scale;
     }
+    auto pack4 = [](float a, float b, float c, float d) {
+        return kBf8 ? pack_e5m2x4(a, b, c, d) : pack_e4m3x4(a, b, c, d);
+    };
     uint4 v[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -148,10 +152,10 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
         const int row = k / kInCpr, cc = k % kInCpr;
         uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * kPitch + cc * kInEl);  // 4-byte aligned
         if (kQuant) {
-            const uint32_t q0 = pack_e4m3x4(bf16lo(v[i].x) * inv, bf16hi(v[i].x) * inv, bf16lo(v[i].y) * inv,
-                                            bf16hi(v[i].y) * inv);
-            const uint32_t q1 = pack_e4m3x4(bf16lo(v[i].z) * inv, bf16hi(v[i].z) * inv, bf16lo(v[i].w) * inv,
-                                            bf16hi(v[i].w) * inv);
+            const uint32_t q0 = pack4(bf16lo(v[i].x) * inv, bf16hi(v[i].x) * inv, bf16lo(v[i].y) * inv,
+                                      bf16hi(v[i].y) * inv);
+            const uint32_t q1 = pack4(bf16lo(v[i].z) * inv, bf16hi(v[i].z) * inv, bf16lo(v[i].w) * inv,
+                                      bf16hi(v[i].w) * inv);
             dst[0] = q0;
             dst[1] = q1;
             const int64_t gr = r0 + row;
@@ -187,7 +191,8 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
 }
 
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
-                            int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s) {
+                            int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s,
+                            bool e5m2) {
     if (cols == 0 || ld_out == 0) return hipSuccess;
     uint8_t* o = static_cast<uint8_t*>(out);
     const uint8_t* x = static_cast<const uint8_t*>(in);
@@ -200,6 +205,9 @@ hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const floa
         const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((ld_out + 127) / 128));
         if (in_bytes == 1)
             hipLaunchKernelGGL((transpose8_kernel<1, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x,
+                               rows, cols, ld_out);
+        else if (e5m2)
+            hipLaunchKernelGGL((transpose8_kernel<2, true, true>), grid, block, 0, s, o, q_rows, scale, absmax, x,
                                rows, cols, ld_out);
         else
             hipLaunchKernelGGL((transpose8_kernel<2, true>), grid, block, 0, s, o, q_rows, scale, absmax, x, rows,

@@ -8,6 +8,7 @@ namespace ffn {
 
 constexpr int kWave = 64;
 constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -50,13 +51,25 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)w;
 }
 
-// Per-tensor e4m3 scale pair from an abs-max: the dequantisation factor
-// absmax/448 and its quantisation inverse 448/absmax, both IEEE fp32 quotients;
-// 1 and 1 for an all-zero tensor.
-__device__ __forceinline__ void scale_pair(float am, float& scale, float& inv) {
+// Four fp32 -> four e5m2 codes in one dword (a in the lowest byte), clamped
+// to +-57344 first; v_cvt_pk_bf8_f32 rounds to nearest even.
+__device__ __forceinline__ uint32_t pack_e5m2x4(float a, float b, float c, float d) {
+    a = __builtin_fminf(__builtin_fmaxf(a, -kE5M2Max), kE5M2Max);
+    b = __builtin_fminf(__builtin_fmaxf(b, -kE5M2Max), kE5M2Max);
+    c = __builtin_fminf(__builtin_fmaxf(c, -kE5M2Max), kE5M2Max);
+    d = __builtin_fminf(__builtin_fmaxf(d, -kE5M2Max), kE5M2Max);
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Per-tensor FP8 scale pair from an abs-max: the dequantisation factor
+// absmax/max and its quantisation inverse max/absmax (max = 448 for e4m3,
+// 57344 for e5m2), both IEEE fp32 quotients; 1 and 1 for an all-zero tensor.
+__device__ __forceinline__ void scale_pair(float am, float& scale, float& inv, float fmax = kE4M3Max) {
     if (am > 0.0f) {
-        scale = am / kE4M3Max;
-        inv = kE4M3Max / am;
+        scale = am / fmax;
+        inv = fmax / am;
     } else {
         scale = 1.0f;
         inv = 1.0f;

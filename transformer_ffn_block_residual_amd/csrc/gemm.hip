@@ -168,7 +168,9 @@ __device__ __forceinline__ void load_part(const StepIO& io, const TileRsrc& tr, 
 // read into `nxt` and the loads of step g + kAhead (K-step ld_k of the tile
 // whose slabs are `tr`) are issued.  The code must be free of branches: the
 // scheduling fences order instructions within a basic block only.
-template <bool kFP8>
+// kXBf8: the x fragments (the MFMA's B operand) hold e5m2 codes, selected by
+// the instruction's B-format field; the w fragments stay e4m3.
+template <bool kFP8, bool kXBf8 = false>
 __device__ __forceinline__ void k_step(f32x16_t (&acc)[4][4], const Frags& cur, Frags& nxt, const GemmArgs& a,
                                        const StepIO& io, int g, const TileRsrc& tr, int ld_k) {
     constexpr int kM = kFP8 ? 16 : 32;  // MFMAs per step
@@ -187,8 +189,8 @@ __device__ __forceinline__ void k_step(f32x16_t (&acc)[4][4], const Frags& cur, 
             const int i = m >> 2, j = m & 3;
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 __builtin_shufflevector(cur.a[i][0], cur.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7),
-                __builtin_shufflevector(cur.b[j][0], cur.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[i][j], 0, 0, 0,
-                127, 0, 127);
+                __builtin_shufflevector(cur.b[j][0], cur.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[i][j], 0,
+                kXBf8 ? 1 : 0, 0, 127, 0, 127);
         } else {
             const int i = m >> 3, j = (m >> 1) & 3, p = m & 1;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.a[i][p]),
@@ -415,11 +417,12 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     }
 }
 
-template <bool kFP8, bool kFused, bool kQuant, bool kAccum>
+template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kXBf8 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a) {
     static_assert(kFused || !kQuant, "quantised output is a SwiGLU epilogue");
     static_assert(!(kFused && kAccum), "accumulation is a plain-output epilogue");
+    static_assert(kFP8 || !kXBf8, "e5m2 x is an FP8 operand");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
     constexpr int kStoreCnt = epilogue_stores<kFused>();
@@ -538,10 +541,10 @@ void gemm_kernel(GemmArgs a) {
             const TileRsrc tr = select_rsrc(own, tr_cur, tr_nxt);
             const int k0 = own ? kAhead : wrap_k(kAhead);
             const int k1 = own ? kAhead + 1 : wrap_k(kAhead + 1);
-            k_step<kFP8>(acc, f0, f1, a, io, g, tr, k0);
+            k_step<kFP8, kXBf8>(acc, f0, f1, a, io, g, tr, k0);
             wait_vmcnt<kWait + kStoreCnt>();
             barrier();
-            k_step<kFP8>(acc, f1, f0, a, io, g + 1, tr, k1);
+            k_step<kFP8, kXBf8>(acc, f1, f0, a, io, g + 1, tr, k1);
             wait_vmcnt<kWait + kStoreCnt>();
             barrier();
             g += 2;
@@ -550,10 +553,10 @@ void gemm_kernel(GemmArgs a) {
             const bool own = kk + kAhead < KT;
             const TileRsrc tr = select_rsrc(own, tr_cur, tr_nxt);
             const int k0 = own ? kk + kAhead : wrap_k(kk + kAhead);
-            k_step<kFP8>(acc, f0, f1, a, io, g, tr, k0);
+            k_step<kFP8, kXBf8>(acc, f0, f1, a, io, g, tr, k0);
             wait_vmcnt<kWait>();
             barrier();
-            k_step<kFP8>(acc, f1, f0, a, io, g + 1, tr, k0 + 1);
+            k_step<kFP8, kXBf8>(acc, f1, f0, a, io, g + 1, tr, k0 + 1);
             wait_vmcnt<kWait>();
             barrier();
         }
@@ -585,10 +588,12 @@ static int cu_count() {
 
 // Abs-max of a plain (unfused) GEMM output, when asked for: a separate pass.
 // q_absmax / q_scale (SwiGLU only, both or neither): store e4m3 codes of h
-// under that known abs-max instead of bf16 h, and its scale.
+// under that known abs-max instead of bf16 h, and its scale.  x_e5m2 (fp8,
+// plain output): x holds e5m2 codes.
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
-                       hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate) {
+                       hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2) {
+    if (x_e5m2 && (!fp8 || fuse_swiglu)) return hipErrorInvalidValue;
     if (absmax && (fuse_swiglu || N == 0)) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
@@ -615,7 +620,10 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const int KT = a.K_bytes / kRowBytes;
     const dim3 grid((unsigned)(KT >= kAhead ? min(T, cu_count()) : T)), block(kThreads);
     const bool acc = accumulate && !fuse_swiglu;
-    if (fp8) {
+    if (fp8 && x_e5m2) {
+        if (acc) hipLaunchKernelGGL((gemm_kernel<true, false, false, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true>), grid, block, 0, s, a);
+    } else if (fp8) {
         if (quant) hipLaunchKernelGGL((gemm_kernel<true, true, true, false>), grid, block, 0, s, a);
         else if (fuse_swiglu) hipLaunchKernelGGL((gemm_kernel<true, true, false, false>), grid, block, 0, s, a);
         else if (acc) hipLaunchKernelGGL((gemm_kernel<true, false, false, true>), grid, block, 0, s, a);

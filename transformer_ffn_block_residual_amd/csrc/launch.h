@@ -22,17 +22,19 @@ hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t
 // q_absmax / q_scale: SwiGLU only; out then holds e4m3 codes of h quantised
 // with the known abs-max *q_absmax, and *q_scale receives its scale.
 // accumulate (plain output only): out = bf16(out + product), one rounding.
+// x_e5m2 (fp8, plain output only): x holds e5m2 codes (w stays e4m3).
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr,
-                       bool accumulate = false);
+                       bool accumulate = false, bool x_e5m2 = false);
 
 // Backward: out[c, r] = in[r, c], zero for rows <= r < ld_out.  (in_bytes,
 // out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3
 // with *absmax on the way (scale written to *scale; q_rows, if not null, also
-// receives the codes in the input's [rows, cols] layout).
+// receives the codes in the input's [rows, cols] layout; e5m2: e5m2 codes).
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
-                            int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s);
+                            int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s,
+                            bool e5m2 = false);
 hipError_t launch_swiglu_bwd(uint16_t* dgu, float* absmax, const uint16_t* dh, const uint16_t* gu, int64_t N, int H,
                              hipStream_t s);
 // scratch: rmsnorm_bwd_scratch_floats(N, C) floats.
