@@ -69,6 +69,12 @@ def parse():
     p.add_argument("--decode-m", type=int, default=1, help="decode workload: tokens per call (1..4 off split)")
     p.add_argument("--backward", action="store_true",
                    help="block workloads: time the FFN block backward (after one forward) instead of the forward")
+    p.add_argument("--decode-overlap", default="none", choices=["none", "tail", "start"],
+                   help="qwen7b8: where the step's decode runs.  none: after the down GEMM on the same stream; "
+                        "tail: on a second stream from the end of the h quantisation on, beside the down GEMM "
+                        "(whose persistent grid leaves 32 CUs free); start: on a second stream from the start of "
+                        "the step.  Each step joins the second stream before it ends.  Both overlaps measure "
+                        "slower than none (the decode needs more than the free CUs)")
     p.add_argument("--grad-dtype", default="e4m3", choices=["e4m3", "e5m2"],
                    help="FP8 backward: the format of the quantised gradients (weights and activations stay e4m3)")
     p.add_argument("--known-h-absmax", action="store_true",
@@ -288,10 +294,10 @@ class Timer:
         self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(n_marks)]
         self.used = 0
 
-    def mark(self):
+    def mark(self, stream=None):
         e = self.pool[self.used]
         self.used += 1
-        e.record(self.stream)
+        e.record(self.stream if stream is None else stream)
         return e
 
     def add(self, name, a, b):
@@ -365,6 +371,11 @@ def bench_block(a, torch, np, B, block, W):
     stream = torch.cuda.current_stream()
     E = B.FFN_E4M3 if w.fp8 else B.FFN_BF16
     known = a.known_h_absmax and w.fp8
+    # the decode is independent of the prefill block: with an overlap it runs
+    # on a second stream (the default priority, like every stream here)
+    overlap = a.decode_overlap if M else "none"
+    side = torch.cuda.Stream() if overlap != "none" else None
+    fork_ev, join_ev = torch.cuda.Event(), torch.cuda.Event()
     if known:
         # ping-pong abs-max buffers: step i quantises with am[i % 2] and
         # records its own abs-max in am[(i + 1) % 2]; one ordinary forward
@@ -373,8 +384,22 @@ def bench_block(a, torch, np, B, block, W):
         am_pp = [pre.am_h.clone(), torch.empty_like(pre.am_h)]
         torch.cuda.synchronize()
 
+    def decode_on_side(i, tm, stream, forked=False):
+        # forked: fork_ev was recorded on `stream` already (before the launch
+        # that the decode is to run beside, so that that launch is queued first)
+        if not forked:
+            fork_ev.record(stream)
+        side.wait_event(fork_ev)
+        d0 = tm.mark(side) if tm else None
+        decs[i % DECODE_COPIES].forward(x_dec, M, side)
+        if tm:
+            tm.add("decode", d0, tm.mark(side))
+        join_ev.record(side)
+
     def step(i, tm, stream=stream):
         m0 = tm.mark() if tm else None
+        if overlap == "start":
+            decode_on_side(i, tm, stream)
         B.ffn_rmsnorm_fwd(pre.y, pre.rstd, pre.r, pre.am_y, inp, addend, pre.w_norm, pre.eps, N, C, stream)
         m1 = tm.mark() if tm else None
         if known:
@@ -384,6 +409,8 @@ def bench_block(a, torch, np, B, block, W):
                                       pre.w_gu, pre.s_gu, E, N, C, H, stream)
             m3 = tm.mark() if tm else None
             m4 = m3
+            if overlap == "tail":
+                fork_ev.record(stream)
             B.ffn_down(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, E, N, H, C, stream)
         elif w.fp8:
             B.ffn_quant_absmax(pre.qy, pre.s_y, pre.am_y, pre.y, N * C, 0, stream)
@@ -392,17 +419,27 @@ def bench_block(a, torch, np, B, block, W):
             m3 = tm.mark() if tm else None
             B.ffn_quant_absmax(pre.qh, pre.s_h, pre.am_h, pre.h, N * H, 0, stream)
             m4 = tm.mark() if tm else None
+            if overlap == "tail":
+                fork_ev.record(stream)
             B.ffn_down(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, E, N, H, C, stream)
         else:
             m2 = m1
             B.ffn_gateup(pre.h, pre.am_h, pre.y, None, pre.w_gu, None, E, 1, N, C, H, stream)
             m3 = tm.mark() if tm else None
             m4 = m3
+            if overlap == "tail":
+                fork_ev.record(stream)
             B.ffn_down(pre.out, pre.h, None, pre.w_d, None, E, N, H, C, stream)
+        if overlap == "tail":
+            decode_on_side(i, tm, stream, forked=True)
         m5 = tm.mark() if tm else None
-        if M:
+        if M and overlap == "none":
             decs[i % DECODE_COPIES].forward(x_dec, M, stream)
+        elif M:
+            stream.wait_event(join_ev)
         m6 = tm.mark() if (tm and M) else None
+        if tm and M and overlap == "none":
+            tm.add("decode", m5, m6)
         if tm:
             tm.add("step", m0, m6 if M else m5)
             tm.add("rmsnorm", m0, m1)
@@ -412,10 +449,8 @@ def bench_block(a, torch, np, B, block, W):
                     tm.add("quant_h", m3, m4)
             tm.add("gateup", m2, m3)
             tm.add("down", m4, m5)
-            if M:
-                tm.add("decode", m5, m6)
 
-    ms, km = run_steps(torch, stream, step, a)
+    ms, km = run_steps(torch, stream, step, a, marks_per_step=10)
     spread = run_steps.spread
 
     def issue(cur):
@@ -441,6 +476,7 @@ def bench_block(a, torch, np, B, block, W):
                         "prefill8": "llama-shaped FFN block, FP8: prefill N=4096 C=4096 H=14336 eps=1e-5, "
                                     "0.1% x50 outliers"}[a.workload],
            "N": N, "C": C, "H": H, "decode_M": M, "seed": w.seed,
+           **({"decode_overlap": overlap} if M else {}),
            "quant": ("per-tensor abs-max e4m3 activations and weights" if w.fp8 else "none (bf16)")
            + ("; h quantised in the gate+up epilogue with the previous step's abs-max" if known else "")
            + ("; decode: e4m3 weights, per-row fp32 scales, bf16 activations" if M else "")}

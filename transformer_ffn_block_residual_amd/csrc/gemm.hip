@@ -586,6 +586,20 @@ static int cu_count() {
     return cached[dev];
 }
 
+// Workgroups of the persistent grid for T tiles: as many rounds of tiles as
+// one workgroup per CU needs, dealt over as few workgroups as still finish in
+// that many rounds (a multiple of 8, so that tile b and its workgroup b % G sit
+// on the same XCD).  The makespan is the same as with one workgroup per CU;
+// the CUs left over (64 of 256 for the 448 tiles of a 3584 x 8192 output) stay
+// free for work on other streams.
+static int persistent_grid(int T) {
+    const int cu = cu_count();
+    if (T <= cu) return T;
+    const int rounds = (T + cu - 1) / cu;
+    const int g = ((T + rounds - 1) / rounds + 7) / 8 * 8;
+    return min(g, cu);
+}
+
 // Abs-max of a plain (unfused) GEMM output, when asked for: a separate pass.
 // q_absmax / q_scale (SwiGLU only, both or neither): store e4m3 codes of h
 // under that known abs-max instead of bf16 h, and its scale.  x_e5m2 (fp8,
@@ -618,7 +632,7 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const bool quant = fuse_swiglu && q_absmax;
     const int T = a.tiles_m * a.tiles_n;
     const int KT = a.K_bytes / kRowBytes;
-    const dim3 grid((unsigned)(KT >= kAhead ? min(T, cu_count()) : T)), block(kThreads);
+    const dim3 grid((unsigned)(KT >= kAhead ? persistent_grid(T) : T)), block(kThreads);
     const bool acc = accumulate && !fuse_swiglu;
     if (fp8 && x_e5m2) {
         if (acc) hipLaunchKernelGGL((gemm_kernel<true, false, false, true, true>), grid, block, 0, s, a);
