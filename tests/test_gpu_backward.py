@@ -175,6 +175,24 @@ def test_matmul_tn_random_fp8_scaled_accumulate(F, M, N, Kd):
     assert np.all(within_dot_bound(host_bits(out), exact, mag))
 
 
+@pytest.mark.parametrize("M,N,Kd", [(4300, 4096, 256), (6900, 4864, 512)])
+def test_matmul_tn_uneven_rounds_exact(F, M, N, Kd):
+    """Output tile counts just past one and two rounds of 256 CUs (17 x 16 =
+    272 and 27 x 19 = 513 tiles of 256 x 256): the persistent grid deals them
+    over 136 and 176 workgroups that take one to three tiles each, a ragged
+    last row of tiles included.  Integer-valued e4m3 codes, exact sums."""
+    say(f"matmul_tn uneven rounds M={M} N={N} K={Kd}")
+    rng = np.random.default_rng(M + N)
+    qa = K.e4m3_encode(rng.integers(-3, 4, (M, Kd)).astype(np.float64))
+    qb = K.e4m3_encode(rng.integers(-3, 4, (N, Kd)).astype(np.float64))
+    one = dev_f32([1.0])
+    out = empty_bf16(M, N).fill_(3.0)
+    F.ffn_matmul_tn(out, dev_u8(qa), one, dev_u8(qb), one, F.FFN_E4M3, 0, M, N, Kd)
+    torch.cuda.synchronize()
+    exact = K.e4m3_decode(qa) @ K.e4m3_decode(qb).T
+    assert np.array_equal(host_bits(out), O.f64_to_bf16_bits(exact))
+
+
 @pytest.mark.parametrize("M,N,Kd", MM_SHAPES)
 def test_matmul_tn_e5m2_gradient_exact(F, M, N, Kd):
     """a in e5m2, b in e4m3 (FFN_E5M2): integer-valued codes and e5m2
@@ -421,17 +439,19 @@ def test_block_backward_out_of_place_and_given_absmax(F, fp8):
         assert torch.equal(a, b)
 
 
-def test_block_backward_full_size_sampled(F):
+@pytest.mark.parametrize("grad", ["e4m3", "e5m2"])
+def test_block_backward_full_size_sampled(F, grad):
     """FP8 block backward at N=4096, C=4096, H=14336: each GEMM output checked
     on sampled entries against the exact product of the GPU's own codes, the
-    SwiGLU and RMSNorm backward on sampled rows."""
+    SwiGLU and RMSNorm backward on sampled rows.  grad: the gradients' codes."""
     N, C, H = 4096, 4096, 14336
-    say(f"block backward full size N={N} C={C} H={H} fp8")
+    say(f"block backward full size N={N} C={C} H={H} fp8, {grad} gradients")
     from transformer_ffn_block_residual_amd import block
     d = W.block_inputs(N, C, H, seed=1004, w_std=0.02)
     pb = block.PrefillBlock(N, C, H, 1e-5, True)
     pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pb)
+    bb = block.BackwardBlock(pb, grad_dtype=grad)
+    gdec = K.e5m2_decode if grad == "e5m2" else K.e4m3_decode
     gu_keep = empty_bf16(N, 2 * H)
     bb.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
     gu_keep.copy_(bb.gu)
@@ -444,7 +464,7 @@ def test_block_backward_full_size_sampled(F):
     wd = host_u8(pb.w_d).reshape(C, H)
     s = float(np.float32(host_f32(bb.s_dout)[0] * host_f32(pb.s_d)[0]))
     # dh rows: sum_c dec(qdout[n, c]) dec(Wd[c, h]) * s
-    dq = K.e4m3_decode(qdout[rows])
+    dq = gdec(qdout[rows])
     wdec = K.e4m3_decode(wd)
     exact = dq @ wdec * s
     mag = np.abs(dq) @ np.abs(wdec) * abs(s)
@@ -458,7 +478,7 @@ def test_block_backward_full_size_sampled(F):
     cols_c = rng.integers(0, C, 8)
     cols_h = rng.integers(0, H, 8)
     s_dw = float(np.float32(host_f32(bb.s_dout)[0] * host_f32(pb.s_h)[0]))
-    a = K.e4m3_decode(qdout[:, cols_c])            # [N, 8]
+    a = gdec(qdout[:, cols_c])                     # [N, 8]
     b = K.e4m3_decode(qh[:, cols_h])               # [N, 8]
     exact = a.T @ b * s_dw
     mag = np.abs(a).T @ np.abs(b) * abs(s_dw)
@@ -468,7 +488,7 @@ def test_block_backward_full_size_sampled(F):
     qy = host_u8(pb.qy).reshape(N, C)
     cols_o = rng.integers(0, 2 * H, 8)
     s_gu = float(np.float32(host_f32(bb.s_dgu)[0] * host_f32(pb.s_y)[0]))
-    a = K.e4m3_decode(qdgu[:, cols_o])
+    a = gdec(qdgu[:, cols_o])
     b = K.e4m3_decode(qy[:, cols_c])
     exact = a.T @ b * s_gu
     mag = np.abs(a).T @ np.abs(b) * abs(s_gu)
@@ -477,7 +497,7 @@ def test_block_backward_full_size_sampled(F):
     # dy rows and the RMSNorm backward rows
     wgu = host_u8(pb.w_gu).reshape(2 * H, C)
     s_dy = float(np.float32(host_f32(bb.s_dgu)[0] * host_f32(pb.s_gu)[0]))
-    dq = K.e4m3_decode(qdgu[rows])
+    dq = gdec(qdgu[rows])
     wdec = K.e4m3_decode(wgu)
     exact = dq @ wdec * s_dy
     mag = np.abs(dq) @ np.abs(wdec) * abs(s_dy)
@@ -487,17 +507,17 @@ def test_block_backward_full_size_sampled(F):
     assert rms_bwd_close(host_bits(bb.d_res)[rows], dres_ref, d_out[rows], g_dy, g_r, d["w_norm"], g_rstd)
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_block_backward_replays_from_a_hip_graph(F, fp8):
+@pytest.mark.parametrize("fp8,grad", [(False, "e4m3"), (True, "e4m3"), (True, "e5m2")])
+def test_block_backward_replays_from_a_hip_graph(F, fp8, grad):
     """Forward + backward (gradients zeroed first) captured once, replayed
     three times with eager work between, equals the eager result bit for bit."""
-    say(f"block backward graph replay fp8={fp8}")
+    say(f"block backward graph replay fp8={fp8} grad={grad}")
     from transformer_ffn_block_residual_amd import block
     N, C, H = 200, 384, 256
     d = W.block_inputs(N, C, H, seed=41, w_std=0.1)
     pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
     pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pb, in_place=False)
+    bb = block.BackwardBlock(pb, in_place=False, grad_dtype=grad)
     inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
     d_out = dev_bf16(rand_bits((N, C), 1.0, 42))
 
