@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--decode-m", type=int, default=1, help="decode workload: tokens per call (1..4 off split)")
     p.add_argument("--backward", action="store_true",
                    help="block workloads: time the FFN block backward (after one forward) instead of the forward")
+    p.add_argument("--decode-layout", default="auto", choices=["auto", "rows", "packed"],
+                   help="FP8 decode weights: row-major (ffn_decode_gemv) or the packed decode layout "
+                        "(ffn_decode_gemv_packed); auto: packed from 5 tokens on, row-major below")
     p.add_argument("--decode-overlap", default="none", choices=["none", "tail", "start"],
                    help="qwen7b8: where the step's decode runs.  none: after the down GEMM on the same stream; "
                         "tail: on a second stream from the end of the h quantisation on, beside the down GEMM "
@@ -343,6 +346,11 @@ def run_steps(torch, stream, step, a, marks_per_step=8):
     return ms, timer.mean_ms()
 
 
+def decode_packed(a, M):
+    """Whether the FP8 split-SiLU decode of M tokens runs on packed weights."""
+    return a.decode_layout == "packed" or (a.decode_layout == "auto" and M >= 5)
+
+
 def bench_block(a, torch, np, B, block, W):
     w = W.WORKLOADS[a.workload]
     N, C, H = w.N, w.C, w.H
@@ -361,8 +369,9 @@ def bench_block(a, torch, np, B, block, W):
     decs = []
     if M:
         x_dec = dev(dec_x)
+        packed = decode_packed(a, M)
         for _ in range(DECODE_COPIES):
-            db = block.DecodeBlock(M, C, H)
+            db = (block.DecodeBlockPacked if packed else block.DecodeBlock)(M, C, H)
             wgu = pre.w_gu.clone()
             sg = pre.s_gu.expand(H).contiguous()
             db.set_fp8_weights(wgu[:H], sg, wgu[H:], sg, pre.w_d.clone(), pre.s_d.expand(C).contiguous())
@@ -476,7 +485,8 @@ def bench_block(a, torch, np, B, block, W):
                         "prefill8": "llama-shaped FFN block, FP8: prefill N=4096 C=4096 H=14336 eps=1e-5, "
                                     "0.1% x50 outliers"}[a.workload],
            "N": N, "C": C, "H": H, "decode_M": M, "seed": w.seed,
-           **({"decode_overlap": overlap} if M else {}),
+           **({"decode_overlap": overlap, "decode_layout": "packed" if decode_packed(a, M) else "rows"}
+              if M else {}),
            "quant": ("per-tensor abs-max e4m3 activations and weights" if w.fp8 else "none (bf16)")
            + ("; h quantised in the gate+up epilogue with the previous step's abs-max" if known else "")
            + ("; decode: e4m3 weights, per-row fp32 scales, bf16 activations" if M else "")}
@@ -650,6 +660,7 @@ def bench_decode(a, torch, np, B, block, W):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
     decs = []
+    packed = False
     if bf16w:
         wts = [dev(d[k]) for k in ("w_gate", "w_up", "w_down")]
         for i in range(DECODE_COPIES):
@@ -657,14 +668,20 @@ def bench_decode(a, torch, np, B, block, W):
             db.load_weights(*(wts if i == 0 else [t.clone() for t in wts]))
             decs.append(db)
     else:
+        packed = arm is None and decode_packed(a, M)
         first = block.DecodeBlock(M, C, H)
         first.load_master_weights(d["w_gate"], d["w_up"], d["w_down"])
-        decs.append(first)
-        for _ in range(DECODE_COPIES - 1):
-            db = block.DecodeBlock(M, C, H)
+        for i in range(DECODE_COPIES):
+            if i == 0 and not packed:
+                decs.append(first)
+                continue
+            # each copy its own weights (packed ones are packed from the first's rows)
+            db = (block.DecodeBlockPacked if packed else block.DecodeBlock)(M, C, H)
             db.set_fp8_weights(first.wg.clone(), first.sg.clone(), first.wu.clone(), first.su.clone(),
                                first.wd.clone(), first.sd.clone())
             decs.append(db)
+        if packed:
+            del first
     x = dev(d["x"])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -700,14 +717,17 @@ def bench_decode(a, torch, np, B, block, W):
     call_ms = ms
     wdesc = ("bf16" if bf16w else "e4m3 with per-row fp32 scales")
     entry = {None: "ffn_decode_gemv", "bf16": "ffn_decode_gemv_bf16"}.get(arm, "ffn_decode_gemv_arm")
-    default = a.decode_arm == "split" and M == 1
+    if not bf16w and arm is None and packed:
+        entry = "ffn_decode_gemv_packed"
+    default = a.decode_arm == "split" and M == 1 and not packed
     out = {
         "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16w else "fp8", "data": "synthetic",
         "config": {"workload": f"{'single' if M == 1 else str(M)}-token decode FFN: x[{M},{C}] bf16, gate/up "
                                f"[{H},{C}] and down [{C},{H}] {wdesc}; {arm_what}",
-                   "M": M, "C": C, "H": H, "seed": w.seed, "weight_copies": DECODE_COPIES, "arm": a.decode_arm},
+                   "M": M, "C": C, "H": H, "seed": w.seed, "weight_copies": DECODE_COPIES, "arm": a.decode_arm,
+                   **({} if bf16w else {"weight_layout": "packed" if packed else "rows"})},
         "roofline": {"bound": "hbm", "kernel": f"{entry} ({arm_what})",
                      "achieved": nbytes / (call_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -211,6 +211,36 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
                                   const void* w_gate, const void* w_up, const void* w_down,
                                   int64_t M, int64_t C, int64_t H, hipStream_t stream);
 
+/* Packed decode weights: the same e4m3 codes re-laid so that the few-token
+ * decode of 5 to 32 tokens streams each 16-row block as one contiguous run,
+ * one KiB per load instruction, in the order the MFMA consumes it.
+ * packed: e4m3, rows * cols bytes; 16-byte piece p holds row 16 rb + l % 16,
+ * codes 64 kc + 16 (l / 16) .. + 15 of w, where l = p % 64 and
+ * p / 64 = rb * (cols / 64) + kc.  A one-time re-layout of the QuantizedWeight
+ * rows of [metrale] DenseFfnLayer::forward (FP8 arm); the row scales are
+ * unchanged.  Supported: rows % 16 == 0, cols % 128 == 0; packed must not
+ * alias w. */
+ffn_status_t ffn_decode_pack_weight(uint8_t* packed, const uint8_t* w, int64_t rows,
+                                    int64_t cols, hipStream_t stream);
+
+/* Workspace bytes of ffn_decode_gemv_packed for M tokens: 32 (C + H) bytes
+ * per 16-token block; -1 for sizes it does not support. */
+int64_t ffn_decode_packed_workspace_bytes(int64_t M, int64_t C, int64_t H);
+
+/* The split-SiLU decode of ffn_decode_gemv (same formulas, same results up to
+ * fp32 summation order) on packed weights: w_gate, w_up [H, C] and w_down
+ * [C, H] in the layout of ffn_decode_pack_weight; scales, x, h and out as in
+ * ffn_decode_gemv.  workspace: ffn_decode_packed_workspace_bytes(M, C, H)
+ * bytes, 16-byte aligned, caller-owned; it receives x and h in the order of
+ * the MFMA's activation operand (written and read within the call).
+ * Supported: 0 <= M <= 32, C % 128 == 0, H % 128 == 0; the workspace must not
+ * alias out, h or x.  Calls that share a workspace must not overlap. */
+ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const void* x,
+                                    const uint8_t* w_gate, const float* s_gate,
+                                    const uint8_t* w_up, const float* s_up,
+                                    const uint8_t* w_down, const float* s_down,
+                                    int64_t M, int64_t C, int64_t H, hipStream_t stream);
+
 /* ------------------------------------------------------------------ backward
  * The FFN half of [llmq model] LLamaModel::_backward_block, as the calls it
  * is made of: backward_qmm through the down projection, swiglu_backward,

@@ -38,6 +38,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
               "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16",
+              "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes", "ffn_decode_gemv_packed",
               "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
               "ffn_rmsnorm_bwd_scratch_bytes", "ffn_last_error", "ffn_version"]:
         assert n in names
@@ -123,6 +124,27 @@ def test_decode_validation(lib):
     mis = list(args)
     mis[3] = MIS
     assert f(*mis, 1, 4096, 14336, None) == UNSUPPORTED
+
+
+def test_decode_packed_validation(lib):
+    B, C_, D, E = 0x20000, 0x30000, 0x40000, 0x50000
+    p = lib.ffn_decode_pack_weight   # packed, w, rows, cols
+    assert p(A, B, 24, 256, None) == UNSUPPORTED        # rows % 16
+    assert p(A, B, 32, 200, None) == UNSUPPORTED        # cols % 128
+    assert p(A, A, 32, 256, None) == INVALID            # in place
+    assert p(None, B, 32, 256, None) == INVALID
+    assert p(A, MIS, 32, 256, None) == UNSUPPORTED
+    ws = lib.ffn_decode_packed_workspace_bytes
+    assert ws(16, 3584, 18944) == 32 * (3584 + 18944)
+    assert ws(17, 3584, 18944) == 64 * (3584 + 18944) and ws(1, 256, 256) == 32 * 512
+    assert ws(33, 256, 256) == -1 and ws(-1, 256, 256) == -1
+    g = lib.ffn_decode_gemv_packed   # out, h, ws, x, wg, sg, wu, su, wd, sd, M, C, H
+    assert g(A, B, None, D, A, A, A, A, A, A, 16, 256, 768, None) == INVALID       # no workspace
+    assert g(A, B, B, D, A, A, A, A, A, A, 16, 256, 768, None) == INVALID          # workspace aliases h
+    assert g(A, B, E, D, A, A, A, A, A, A, 33, 256, 768, None) == UNSUPPORTED      # M > 32
+    assert g(A, B, E, D, A, A, A, A, A, A, 16, 200, 768, None) == UNSUPPORTED      # C % 128
+    assert g(A, B, MIS, D, A, A, A, A, A, A, 16, 256, 768, None) == UNSUPPORTED    # misaligned workspace
+    assert g(A, B, E, D, A, None, A, A, A, A, 16, 256, 768, None) == INVALID       # no gate scales
 
 
 def test_decode_arm_and_bf16_validation(lib):

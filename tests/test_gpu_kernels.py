@@ -445,6 +445,82 @@ def test_decode_bf16_weights(F, M, C, H):
     assert rel_err(gy, y_ref) < 2e-2
 
 
+@pytest.mark.parametrize("rows,cols", [(16, 128), (48, 384), (384, 1152)])
+def test_decode_pack_weight_layout(F, rows, cols):
+    """The packed layout is the re-indexing the header defines: piece p = row
+    16 rb + l % 16, codes 64 kc + 16 (l / 16) .. + 15, l = p % 64,
+    p / 64 = rb * cols / 64 + kc."""
+    say(f"decode pack rows={rows} cols={cols}")
+    w = np.random.default_rng(rows + cols).integers(0, 256, (rows, cols)).astype(np.uint8)
+    out = empty_u8(rows, cols).fill_(0)
+    F.ffn_decode_pack_weight(out, dev_u8(w), rows, cols)
+    torch.cuda.synchronize()
+    want = w.reshape(rows // 16, 16, cols // 64, 4, 16).transpose(0, 2, 3, 1, 4).reshape(rows, cols)
+    assert np.array_equal(host_u8(out).reshape(rows, cols), want)
+
+
+PACKED_SHAPES = [(1, 1152, 640), (5, 3584, 384), (16, 384, 896), (16, 3584, 18944), (17, 256, 640), (32, 256, 256)]
+
+
+@pytest.mark.parametrize("M,C,H", PACKED_SHAPES)
+def test_decode_packed(F, M, C, H):
+    """ffn_decode_gemv_packed on packed weights against the oracle, as
+    test_decode; the bound form repeats the call exactly.  (16, 3584, 18944)
+    is the 16-token decode of the Qwen2-7B-shaped step."""
+    say(f"decode packed M={M} C={C} H={H}")
+    d = W.decode_inputs(M, C, H, seed=M * 19 + C + H)
+    wq, ws = _decode_weights(F, d)
+    pk = {}
+    for k in ("w_gate", "w_up", "w_down"):
+        rows, cols = d[k].shape
+        pk[k] = empty_u8(rows, cols)
+        F.ffn_decode_pack_weight(pk[k], wq[k], rows, cols)
+    wsp = empty_bf16(F.ffn_decode_packed_workspace_bytes(M, C, H) // 2).fill_(5.0)
+    out, h = empty_bf16(M, C).fill_(7.0), empty_bf16(M, H).fill_(7.0)
+    xd = dev_bf16(d["x"])
+    args = (xd, pk["w_gate"], ws["w_gate"], pk["w_up"], ws["w_up"], pk["w_down"], ws["w_down"], M, C, H)
+    F.ffn_decode_gemv_packed(out, h, wsp, *args)
+    out2, h2 = empty_bf16(M, C), empty_bf16(M, H)
+    call = F.bind_decode_gemv_packed(out2, h2, wsp, *args)
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(h2, h)
+    ref_q = {k: O.quant_rows(d[k]) for k in ("w_gate", "w_up", "w_down")}
+    (qg, sg), (qu, su), (qd, sd) = ref_q["w_gate"], ref_q["w_up"], ref_q["w_down"]
+    y_ref, h_ref = O.decode_gemv(d["x"], qg, sg, qu, su, qd, sd)
+    gh, gy = host_bits(h), host_bits(out)
+    assert rel_err(gh, h_ref) < 2e-2
+    assert rel_err(gy, O.decode_down(gh, qd, sd)) < 1e-2
+    assert rel_err(gy, y_ref) < 3e-2
+
+
+def test_decode_packed_workspace_reuse(F):
+    """One workspace, a 32-token call and then a 5-token one: the second
+    result equals a call on a fresh workspace bit for bit (nothing of the
+    first call's tokens leaks into the second)."""
+    say("decode packed workspace reuse")
+    C, H = 384, 512
+    d = W.decode_inputs(32, C, H, seed=123)
+    wq, ws = _decode_weights(F, d)
+    pk = {}
+    for k in ("w_gate", "w_up", "w_down"):
+        rows, cols = d[k].shape
+        pk[k] = empty_u8(rows, cols)
+        F.ffn_decode_pack_weight(pk[k], wq[k], rows, cols)
+    wts = (pk["w_gate"], ws["w_gate"], pk["w_up"], ws["w_up"], pk["w_down"], ws["w_down"])
+    shared = empty_bf16(F.ffn_decode_packed_workspace_bytes(32, C, H) // 2)
+    x32 = dev_bf16(d["x"])
+    F.ffn_decode_gemv_packed(empty_bf16(32, C), empty_bf16(32, H), shared, x32, *wts, 32, C, H)
+    x5 = x32[:5].contiguous()
+    o_a, h_a = empty_bf16(5, C), empty_bf16(5, H)
+    F.ffn_decode_gemv_packed(o_a, h_a, shared, x5, *wts, 5, C, H)
+    fresh = empty_bf16(F.ffn_decode_packed_workspace_bytes(5, C, H) // 2).fill_(-3.0)
+    o_b, h_b = empty_bf16(5, C), empty_bf16(5, H)
+    F.ffn_decode_gemv_packed(o_b, h_b, fresh, x5, *wts, 5, C, H)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(h_a, h_b)
+
+
 def test_decode_empty_batch(F):
     say("decode M=0")
     C, H = 256, 256

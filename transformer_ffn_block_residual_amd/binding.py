@@ -47,6 +47,8 @@ def _load():
         "ffn_decode_gemv": [P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_decode_gemv_arm": [P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_decode_gemv_bf16": [P, P, P, P, P, P, I64, I64, I64, P],
+        "ffn_decode_pack_weight": [P, P, I64, I64, P],
+        "ffn_decode_gemv_packed": [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_matmul_tn": [P, P, P, P, P, I32, I32, I64, I64, I64, P],
         "ffn_transpose": [P, P, I64, I64, I64, I32, P],
         "ffn_quant_transpose": [P, P, P, P, P, I32, I64, I64, I64, P],
@@ -59,6 +61,8 @@ def _load():
         fn.restype = ctypes.c_int
     lib.ffn_rmsnorm_bwd_scratch_bytes.argtypes = [I64, I64]
     lib.ffn_rmsnorm_bwd_scratch_bytes.restype = ctypes.c_int64
+    lib.ffn_decode_packed_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.ffn_decode_packed_workspace_bytes.restype = ctypes.c_int64
     lib.ffn_last_error.restype = ctypes.c_char_p
     lib.ffn_last_error.argtypes = []
     lib.ffn_version.restype = ctypes.c_char_p
@@ -247,6 +251,39 @@ def bind_decode_gemv_bf16(out, h, x, w_gate, w_up, w_down, M, C, H, stream=None)
     return _bound(_lib.ffn_decode_gemv_bf16, _decode_bf16_args(out, h, x, w_gate, w_up, w_down, M, C, H, stream))
 
 
+def ffn_decode_pack_weight(packed, w, rows, cols, stream=None):
+    _check(_lib.ffn_decode_pack_weight(
+        _ptr(packed, "packed", rows * cols, E4M3), _ptr(w, "w", rows * cols, E4M3), int(rows), int(cols),
+        _stream(stream)))
+
+
+def ffn_decode_packed_workspace_bytes(M, C, H):
+    return int(_lib.ffn_decode_packed_workspace_bytes(int(M), int(C), int(H)))
+
+
+def _decode_packed_args(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream):
+    need = ffn_decode_packed_workspace_bytes(M, C, H)
+    return (_ptr(out, "out", M * C, BF16), _ptr(h, "h", M * H, BF16),
+            _ptr(ws, "workspace", max(need, 0) // 2, BF16), _ptr(x, "x", M * C, BF16),
+            _ptr(w_gate, "w_gate", H * C, E4M3), _ptr(s_gate, "s_gate", H, F32),
+            _ptr(w_up, "w_up", H * C, E4M3), _ptr(s_up, "s_up", H, F32),
+            _ptr(w_down, "w_down", C * H, E4M3), _ptr(s_down, "s_down", C, F32),
+            int(M), int(C), int(H), _stream(stream))
+
+
+def ffn_decode_gemv_packed(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
+    """ffn_decode_gemv on packed weights (ffn_decode_pack_weight); ws: a bf16
+    tensor of at least ffn_decode_packed_workspace_bytes(M, C, H) bytes."""
+    _check(_lib.ffn_decode_gemv_packed(*_decode_packed_args(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down,
+                                                            s_down, M, C, H, stream)))
+
+
+def bind_decode_gemv_packed(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
+    """ffn_decode_gemv_packed bound once, as bind_decode_gemv."""
+    return _bound(_lib.ffn_decode_gemv_packed,
+                  _decode_packed_args(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream))
+
+
 # ----------------------------------------------------------------------------- backward
 
 def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, accumulate, M, N, K, stream=None):
@@ -301,7 +338,8 @@ def ffn_rmsnorm_bwd(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absm
 __all__ = [
     "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
     "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
-    "bind_decode_gemv_arm", "bind_decode_gemv_bf16",
+    "bind_decode_gemv_arm", "bind_decode_gemv_bf16", "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes",
+    "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
     "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "version", "last_error", "LIB_PATH",

@@ -283,6 +283,45 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x, const void*
                       "ffn_decode_gemv_bf16");
 }
 
+ffn_status_t ffn_decode_pack_weight(uint8_t* packed, const uint8_t* w, int64_t rows, int64_t cols,
+                                    hipStream_t stream) {
+    REQUIRE(packed);
+    REQUIRE(w);
+    if (rows < 0 || cols < 0) return fail(FFN_ERR_INVALID, "ffn_decode_pack_weight: negative size");
+    if (rows % 16 != 0 || cols % 128 != 0 || cols > kMaxDim || rows > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_pack_weight: rows = %lld must be a multiple of 16 and cols = "
+                    "%lld of 128", (long long)rows, (long long)cols);
+    if (misaligned(packed) || misaligned(w))
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_decode_pack_weight: a buffer is not 16-byte aligned");
+    if ((const void*)packed == (const void*)w)
+        return fail(FFN_ERR_INVALID, "ffn_decode_pack_weight: packed must not alias w");
+    return hip_status(ffn::launch_pack_weight(packed, w, rows, (int)cols, stream), "ffn_decode_pack_weight");
+}
+
+int64_t ffn_decode_packed_workspace_bytes(int64_t M, int64_t C, int64_t H) {
+    if (M < 0 || M > 32 || C < 0 || H < 0 || C > kMaxDim || H > kMaxDim) return -1;
+    return ffn::decode_packed_ws_elems((int)M, (int)C, (int)H) * 2;
+}
+
+ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const void* x, const uint8_t* w_gate,
+                                    const float* s_gate, const uint8_t* w_up, const float* s_up,
+                                    const uint8_t* w_down, const float* s_down, int64_t M, int64_t C, int64_t H,
+                                    hipStream_t stream) {
+    REQUIRE(s_gate);
+    REQUIRE(s_up);
+    REQUIRE(s_down);
+    REQUIRE(workspace);
+    if (ffn_status_t st = check_decode("ffn_decode_gemv_packed", out, h, x, w_gate, w_up, w_down, M, C, H, 1, 32))
+        return st;
+    ALIGNED(workspace);
+    if (workspace == out || workspace == h || workspace == x)
+        return fail(FFN_ERR_INVALID, "ffn_decode_gemv_packed: workspace must not alias out, h or x");
+    return hip_status(ffn::launch_decode_packed((uint16_t*)out, (uint16_t*)h, (uint16_t*)workspace,
+                                                (const uint16_t*)x, w_gate, s_gate, w_up, s_up, w_down, s_down,
+                                                (int)M, (int)C, (int)H, stream),
+                      "ffn_decode_gemv_packed");
+}
+
 // ----------------------------------------------------------------------------- backward
 
 ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const void* b, const float* b_scale,

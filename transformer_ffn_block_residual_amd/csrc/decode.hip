@@ -43,11 +43,19 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // else : rows of w0 (down) -> out = y [M, rows].  x: [M, K] bf16.  TB = 16-token
 // blocks (M <= 16 * TB); RB = 16-row blocks per workgroup (each activation
 // fragment is multiplied into RB * NMAT row blocks).
-template <bool kDual, int TB, int RB, int kWaves>
+// kPacked: the weights are in the packed decode layout (each 16-row block a
+// run of 1 KiB blocks, one per 64 codes, in which lane l's 16 bytes are row
+// l % 16, codes 16 (l / 16) .. + 15 of those 64: one contiguous KiB per load
+// instruction, landing in MFMA operand order), x is in fragment order (token
+// block tb, fragment f, lane l: 8 values of token 16 tb + l % 16 at
+// k = 64 (f / 2) + 16 (l / 16) + 8 (f % 2) + 0..7, zero past M: one contiguous
+// KiB per B operand), and the dual pass also writes h in fragment order to hp
+// (all 16 tokens of each block; zero past M) for the down pass.
+template <bool kDual, int TB, int RB, int kWaves, bool kPacked = false>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w0,
-    const float* __restrict__ s0, const uint8_t* __restrict__ w1, const float* __restrict__ s1, int M, int K,
-    int rows) {
+    uint16_t* __restrict__ out, uint16_t* __restrict__ hp, const uint16_t* __restrict__ x,
+    const uint8_t* __restrict__ w0, const float* __restrict__ s0, const uint8_t* __restrict__ w1,
+    const float* __restrict__ s1, int M, int K, int rows) {
     constexpr int NMAT = kDual ? 2 : 1;
     __shared__ f32x4_t red[kWaves][RB][NMAT][TB][64];
 
@@ -60,17 +68,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
     const uint8_t* wrow[RB][NMAT];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int row = min(row0 + rb * 16 + lr, rows - 1);
-        wrow[rb][0] = w0 + (int64_t)row * K + lq * 16;
-        if (kDual) wrow[rb][NMAT - 1] = w1 + (int64_t)row * K + lq * 16;
+        if (kPacked) {
+            // rows % 16 == 0: the block's region starts at its first row
+            const int64_t blk = (int64_t)(row0 + rb * 16) * K + lane * 16;
+            wrow[rb][0] = w0 + blk;
+            if (kDual) wrow[rb][NMAT - 1] = w1 + blk;
+        } else {
+            const int row = min(row0 + rb * 16 + lr, rows - 1);
+            wrow[rb][0] = w0 + (int64_t)row * K + lq * 16;
+            if (kDual) wrow[rb][NMAT - 1] = w1 + (int64_t)row * K + lq * 16;
+        }
     }
     const uint16_t* xrow[TB];
     bool tok_ok[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const int tok = tb * 16 + lr;
-        tok_ok[tb] = tok < M;
-        xrow[tb] = x + (int64_t)min(tok, M - 1) * K + lq * 16;
+        tok_ok[tb] = kPacked || tok < M;  // the fragment-order copy is zero past M
+        xrow[tb] = kPacked ? x + (int64_t)tb * 16 * K + lane * 8 : x + (int64_t)min(tok, M - 1) * K + lq * 16;
     }
 
     f32x4_t acc[RB][NMAT][TB];
@@ -99,8 +114,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                 for (int i = 0; i < kPieces; ++i)
-                    wq[rb][m][i] = (kb + 64 * i < K) ? *reinterpret_cast<const uint4*>(wrow[rb][m] + kb + 64 * i)
-                                                     : make_uint4(0, 0, 0, 0);
+                    wq[rb][m][i] = (kb + 64 * i < K)
+                                       ? *reinterpret_cast<const uint4*>(
+                                             wrow[rb][m] + (kPacked ? (int64_t)(kb + 64 * i) * 16 : kb + 64 * i))
+                                       : make_uint4(0, 0, 0, 0);
         // the matching activations: 8 values per MFMA, piece i half q
         bf16x8_t xb[TB][kPieces][2];
 #pragma unroll
@@ -111,7 +128,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
                 for (int q = 0; q < 2; ++q) {
                     uint4 v = make_uint4(0, 0, 0, 0);
                     if (tok_ok[tb] && kb + 64 * i < K)
-                        v = *reinterpret_cast<const uint4*>(xrow[tb] + kb + 64 * i + 8 * q);
+                        v = *reinterpret_cast<const uint4*>(
+                            xrow[tb] + (kPacked ? (int64_t)((kb + 64 * i) / 32 + q) * 512 : kb + 64 * i + 8 * q));
                     xb[tb][i][q] = __builtin_bit_cast(bf16x8_t, v);
                 }
 #pragma unroll
@@ -164,7 +182,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const int tok = tb * 16 + lr;
-        if (tok >= M || orow0 >= rows) continue;
+        if (orow0 >= rows) continue;
         float o[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -180,7 +198,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
         uint2 v;
         v.x = pack_bf16x2(o[0], o[1]);
         v.y = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<uint2*>(out + (int64_t)tok * rows + orow0) = v;
+        if (kPacked && kDual) {
+            // h in fragment order for the down pass, every token of the block
+            // (zero past M, whose activations are zero): features orow0 .. + 3
+            // are four consecutive values of one lane's fragment
+            const int k = orow0;  // a multiple of 4
+            const int64_t off = (int64_t)tb * 16 * rows + (int64_t)(2 * (k / 64) + (k % 16) / 8) * 512 +
+                                (lr + 16 * ((k % 64) / 16)) * 8 + (k % 8);
+            *reinterpret_cast<uint2*>(hp + off) = v;
+        }
+        if (tok < M) *reinterpret_cast<uint2*>(out + (int64_t)tok * rows + orow0) = v;
     }
 }
 
@@ -460,11 +487,11 @@ static hipError_t launch_decode_tb(uint16_t* out, uint16_t* h, const uint16_t* x
                                    const float* sd, int M, int C, int H, hipStream_t s) {
     // H and C are multiples of 128, so whole row blocks always
     hipLaunchKernelGGL((decode_kernel<true, TB, RB_DUAL, kDualWaves>), dim3(H / (16 * RB_DUAL)),
-                       dim3(64 * kDualWaves), 0, s, h, x, wg, sg, wu, su, M, C, H);
+                       dim3(64 * kDualWaves), 0, s, h, nullptr, x, wg, sg, wu, su, M, C, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_kernel<false, TB, 1, kDownWaves>), dim3(C / 16), dim3(64 * kDownWaves), 0, s, out, h,
-                       wd, sd, nullptr, nullptr, M, H, C);
+    hipLaunchKernelGGL((decode_kernel<false, TB, 1, kDownWaves>), dim3(C / 16), dim3(64 * kDownWaves), 0, s, out,
+                       nullptr, h, wd, sd, nullptr, nullptr, M, H, C);
     return hipGetLastError();
 }
 
@@ -477,6 +504,89 @@ hipError_t launch_decode(uint16_t* out, uint16_t* h, uint16_t* gu, const uint16_
     if (M <= 4) return launch_decode_small_m<false>(out, h, gu, x, wg, sg, wu, su, wd, sd, arm, M, C, H, s);
     if (M <= 16) return launch_decode_tb<1, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
     return launch_decode_tb<2, kDualRB>(out, h, x, wg, sg, wu, su, wd, sd, M, C, H, s);
+}
+
+// The packed decode layout of an e4m3 weight [rows, cols] (rows % 16 == 0,
+// cols % 64 == 0): 16-byte piece p of the output = lane l = p % 64 of 1 KiB
+// block b = p / 64; block b = (row block rb, 64-code chunk kc), b = rb * cols /
+// 64 + kc; the piece is row 16 rb + l % 16, codes 64 kc + 16 (l / 16) .. + 15.
+__global__ __launch_bounds__(256) void pack_weight_kernel(uint8_t* __restrict__ dst, const uint8_t* __restrict__ w,
+                                                          int64_t pieces, int cols) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= pieces) return;
+    const int l = (int)(p % 64);
+    const int64_t b = p / 64;
+    const int kcs = cols / 64;
+    const int64_t rb = b / kcs;
+    const int kc = (int)(b % kcs);
+    const uint8_t* src = w + (rb * 16 + l % 16) * cols + kc * 64 + 16 * (l / 16);
+    *reinterpret_cast<uint4*>(dst + p * 16) = *reinterpret_cast<const uint4*>(src);
+}
+
+hipError_t launch_pack_weight(uint8_t* dst, const uint8_t* w, int64_t rows, int cols, hipStream_t s) {
+    const int64_t pieces = rows * cols / 16;
+    if (pieces == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, dst, w, pieces,
+                       cols);
+    return hipGetLastError();
+}
+
+// x [M, K] bf16 -> fragment order for TB token blocks (see decode_kernel's
+// kPacked), zero for tokens past M.  One thread per 16-byte piece.
+__global__ __launch_bounds__(256) void pack_x_kernel(uint16_t* __restrict__ xp, const uint16_t* __restrict__ x,
+                                                     int M, int K, int64_t pieces) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= pieces) return;
+    const int l = (int)(p % 64);
+    const int64_t fa = p / 64;
+    const int nf = K / 32;
+    const int tb = (int)(fa / nf), f = (int)(fa % nf);
+    const int tok = tb * 16 + l % 16;
+    const int k0 = 64 * (f / 2) + 16 * (l / 16) + 8 * (f % 2);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (tok < M) v = *reinterpret_cast<const uint4*>(x + (int64_t)tok * K + k0);
+    *reinterpret_cast<uint4*>(xp + p * 8) = v;
+}
+
+// waves per workgroup of the packed passes (timed at M = 16 on the
+// Qwen2-7B and Llama-8B shapes over 4, 8 and 16 waves and 1 or 2 chunks in
+// flight per wave); the down pass of two token blocks keeps 8 waves, since
+// 16 waves of a workgroup have at most 128 registers each
+constexpr int kPackedDualWaves = 4;
+template <int TB> constexpr int packed_down_waves() { return TB == 1 ? 16 : 8; }
+
+int64_t decode_packed_ws_elems(int M, int C, int H) {
+    const int TB = M <= 16 ? 1 : 2;
+    return (int64_t)TB * 16 * ((int64_t)C + H);
+}
+
+template <int TB>
+static hipError_t launch_packed_tb(uint16_t* out, uint16_t* h, uint16_t* xp, uint16_t* hp, const uint8_t* wg,
+                                   const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
+                                   const float* sd, int M, int C, int H, hipStream_t s) {
+    hipLaunchKernelGGL((decode_kernel<true, TB, 1, kPackedDualWaves, true>), dim3(H / 16),
+                       dim3(64 * kPackedDualWaves), 0, s, h, hp, xp, wg, sg, wu, su, M, C, H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int kDownW = packed_down_waves<TB>();
+    hipLaunchKernelGGL((decode_kernel<false, TB, 1, kDownW, true>), dim3(C / 16), dim3(64 * kDownW), 0, s, out,
+                       nullptr, hp, wd, sd, nullptr, nullptr, M, H, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const uint16_t* x, const uint8_t* wg,
+                                const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
+                                const float* sd, int M, int C, int H, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const int TB = M <= 16 ? 1 : 2;
+    uint16_t* xp = ws;                        // [TB][16 C] fragment order
+    uint16_t* hp = ws + (int64_t)TB * 16 * C;  // [TB][16 H]
+    const int64_t pieces = (int64_t)TB * (C / 32) * 64;
+    hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, xp, x, M, C, pieces);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (TB == 1) return launch_packed_tb<1>(out, h, xp, hp, wg, sg, wu, su, wd, sd, M, C, H, s);
+    return launch_packed_tb<2>(out, h, xp, hp, wg, sg, wu, su, wd, sd, M, C, H, s);
 }
 
 }  // namespace ffn

@@ -49,5 +49,15 @@ enum : int { kDecodeSplitSilu = 0, kDecodeSiluInput = 1, kDecodePerProjection = 
 hipError_t launch_decode(uint16_t* out, uint16_t* h, uint16_t* gu, const uint16_t* x, const uint8_t* wg,
                          const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd, const float* sd,
                          int arm, bool bf16_weights, int M, int C, int H, hipStream_t s);
+// Packed decode: launch_pack_weight writes the packed layout of an e4m3
+// [rows, cols] weight (rows % 16 == 0, cols % 64 == 0); launch_decode_packed
+// runs the split-SiLU decode on packed weights for 1 <= M <= 32 with ws
+// (decode_packed_ws_elems(M, C, H) bf16 elements) for the fragment-order
+// copies of x and h.
+hipError_t launch_pack_weight(uint8_t* dst, const uint8_t* w, int64_t rows, int cols, hipStream_t s);
+int64_t decode_packed_ws_elems(int M, int C, int H);
+hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const uint16_t* x, const uint8_t* wg,
+                                const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
+                                const float* sd, int M, int C, int H, hipStream_t s);
 
 }  // namespace ffn
