@@ -78,6 +78,9 @@ def parse():
                         "(whose persistent grid leaves 32 CUs free); start: on a second stream from the start of "
                         "the step.  Each step joins the second stream before it ends.  Both overlaps measure "
                         "slower than none (the decode needs more than the free CUs)")
+    p.add_argument("--unfused-swiglu-bwd", action="store_true",
+                   help="backward: the down projection's data gradient and the SwiGLU backward as two calls "
+                        "(ffn_matmul_tn, ffn_swiglu_bwd) instead of ffn_matmul_tn_swiglu_bwd")
     p.add_argument("--grad-dtype", default="e4m3", choices=["e4m3", "e5m2"],
                    help="FP8 backward: the format of the quantised gradients (weights and activations stay e4m3)")
     p.add_argument("--known-h-absmax", action="store_true",
@@ -520,6 +523,8 @@ BWD_PHASES = {
     "quant_dout": ("hbm", lambda N, C, H, e: 4 * N * C),
     "transpose_w_down": ("hbm", lambda N, C, H, e: 2 * C * H * e),
     "dx_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
+    # the same product with the SwiGLU backward in its epilogue (dh never stored)
+    "dx_down_swiglu_bwd": ("mfma", lambda N, C, H, e: 2 * N * C * H),
     # bf16: the gradient and h transposed; FP8: the forward's codes of h
     "transpose_down_operands": ("hbm", lambda N, C, H, e: (4 * N * C if e == 2 else 0) + 2 * N * H * e),
     "dw_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
@@ -570,7 +575,7 @@ def bench_backward(a, torch, np, B, block, W):
     pre = block.PrefillBlock(N, C, H, w.eps, w.fp8)
     pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
     gd = a.grad_dtype if w.fp8 else "e4m3"
-    bb = block.BackwardBlock(pre, in_place=False, grad_dtype=gd)
+    bb = block.BackwardBlock(pre, in_place=False, grad_dtype=gd, fuse_swiglu_bwd=not a.unfused_swiglu_bwd)
     bb.forward(dev(d["inp"]), dev(d["addend"]))
     d_out = dev(_bwd_dout(np, w, N))
     # the abs-max of d_out, as its producer (the next block's RMSNorm backward)
@@ -631,6 +636,7 @@ def bench_backward(a, torch, np, B, block, W):
                                  "backward, weight transposes included; the abs-max of the incoming gradient comes "
                                  "with it (its producer, the next block's RMSNorm backward, writes it)",
                    "N": N, "C": C, "H": H, "seed": w.seed, "backward": True,
+                   "swiglu_bwd": "two calls" if a.unfused_swiglu_bwd else "fused into the down data gradient",
                    **({"grad_dtype": gd} if w.fp8 else {})},
         "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({(gd if w.fp8 else 'bf16')}, accumulate): "
                                                  "the up projection's weight gradient [2H, C], K = N",

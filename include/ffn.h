@@ -265,6 +265,23 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale,
                            int accumulate, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream);
 
+/* TN matmul fused with the SwiGLU backward: dh = bf16(sum_k a[m,k] * b[n,k]
+ * (* a_scale * b_scale for FP8)) as ffn_matmul_tn would store it, then,
+ * without storing dh, dgu = the gradient of h = silu(g) * u as
+ * ffn_swiglu_bwd computes it from dh and gu, with max |dgu| in absmax.
+ * [llmq model] LLamaModel::_backward_block: backward_qmm's data gradient
+ * through the down projection (dSwiGLU) followed by swiglu_backward(DMlpUp,
+ * DSwiGLU, MlpUp, ...); the two calls run as one kernel, so dSwiGLU never
+ * reaches memory.  dgu: bf16 [M, 2H] (gate columns, then up columns); gu: bf16
+ * [M, 2H], the forward's gate+up output (dgu may be gu: updated in place);
+ * a: [M,K], b: [H,K], dtype and scales as ffn_matmul_tn; absmax: fp32 [1] or
+ * NULL.  Supported: K % 128 == 0, H % 128 == 0, any M >= 0; dgu must not alias
+ * a or b. */
+ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a,
+                                      const float* a_scale, const void* b, const float* b_scale,
+                                      const void* gu, ffn_dtype_t dtype, int64_t M, int64_t H,
+                                      int64_t K, hipStream_t stream);
+
 /* Transpose: out[c, r] = in[r, c] for r < rows, and 0 for rows <= r < ld_out
  * (zero padding that rounds a token count up to ffn_matmul_tn's K granularity).
  * [llmq model] backward_qmm, transpose(weight_tp, ...), transpose(activation_tp,

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
     for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
               "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16",
               "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes", "ffn_decode_gemv_packed",
-              "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
+              "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
               "ffn_rmsnorm_bwd_scratch_bytes", "ffn_last_error", "ffn_version"]:
         assert n in names
 
@@ -178,6 +178,15 @@ def test_backward_validation(lib):
     assert m(A, A, None, C_, None, 0, 0, 64, 256, 128, None) == INVALID            # out aliases a
     assert m(A, B_, None, MIS, None, 0, 0, 64, 256, 128, None) == UNSUPPORTED      # misaligned b
     assert m(A, B_, None, C_, None, 0, 0, -1, 256, 128, None) == INVALID
+    f = lib.ffn_matmul_tn_swiglu_bwd  # dgu, absmax, a, sa, b, sb, gu, dtype, M, H, K
+    assert f(A, None, B_, None, C_, None, None, 0, 64, 256, 128, None) == INVALID      # no gu
+    assert f(A, None, B_, None, C_, None, D, 1, 64, 256, 128, None) == INVALID         # FP8 without scales
+    assert f(A, None, B_, None, C_, None, D, 7, 64, 256, 128, None) == INVALID         # unknown dtype
+    assert f(A, None, B_, None, C_, None, D, 0, 64, 200, 128, None) == UNSUPPORTED     # H % 128
+    assert f(A, None, B_, None, C_, None, D, 0, 64, 256, 96, None) == UNSUPPORTED      # K % 128
+    assert f(B_, None, B_, None, C_, None, D, 0, 64, 256, 128, None) == INVALID        # dgu aliases a
+    assert f(A, None, B_, None, C_, None, MIS, 0, 64, 256, 128, None) == UNSUPPORTED   # misaligned gu
+    assert f(A, None, B_, None, C_, None, D, 0, -1, 256, 128, None) == INVALID
     t = lib.ffn_transpose  # out, in, rows, cols, ld_out, elt
     assert t(A, B_, 37, 64, 48, 3, None) == INVALID                                # element size
     assert t(A, B_, 37, 64, 32, 2, None) == INVALID                                # ld_out < rows

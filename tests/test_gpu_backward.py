@@ -258,6 +258,77 @@ def test_swiglu_bwd(F, N, H):
     assert np.array_equal(host_bits(gdev), got)
 
 
+FUSED_SHAPES = [(37, 256, 640, "bf16"), (300, 384, 256, "e4m3"), (513, 128, 1024, "e5m2"), (1, 128, 128, "e4m3"),
+                (200, 640, 384, "bf16"), (0, 128, 128, "e4m3")]
+
+
+@pytest.mark.parametrize("M,H,Kd,dt", FUSED_SHAPES)
+@pytest.mark.parametrize("in_place", [False, True])
+def test_matmul_tn_swiglu_bwd_equals_two_calls(F, M, H, Kd, dt, in_place):
+    """The fused data gradient + SwiGLU backward equals ffn_matmul_tn then
+    ffn_swiglu_bwd bit for bit (dgu and its abs-max), in place over gu too;
+    with integer-valued operands dh is exact and dgu is the oracle's
+    swiglu_bwd of it up to the hardware exp's last bits."""
+    say(f"matmul_tn_swiglu_bwd M={M} H={H} K={Kd} {dt} in_place={in_place}")
+    rng = np.random.default_rng(M + H + Kd)
+    code = {"bf16": F.FFN_BF16, "e4m3": F.FFN_E4M3, "e5m2": F.FFN_E5M2}[dt]
+    Mr = max(M, 1)
+    ia = rng.integers(-2, 3, (Mr, Kd)).astype(np.float64)
+    ib = rng.integers(-2, 3, (H, Kd)).astype(np.float64)
+    if dt == "bf16":
+        a, b = dev_bf16(W.to_bf16_bits(ia.astype(np.float32))), dev_bf16(W.to_bf16_bits(ib.astype(np.float32)))
+        sa = sb = None
+        dh_exact = ia @ ib.T
+    else:
+        qa = K.e5m2_encode(ia) if dt == "e5m2" else K.e4m3_encode(ia)
+        qb = K.e4m3_encode(ib)
+        a, b = dev_u8(qa), dev_u8(qb)
+        sa, sb = dev_f32([0.5]), dev_f32([0.25])
+        dh_exact = (ia @ ib.T) * 0.125
+    gu = rand_bits((Mr, 2 * H), 2.0, M * 7 + H)
+    dh = empty_bf16(Mr, H)
+    F.ffn_matmul_tn(dh, a, sa, b, sb, code, 0, M, H, Kd)
+    ref, am_ref = empty_bf16(Mr, 2 * H).fill_(9.0), empty_f32(1).fill_(5.0)
+    F.ffn_swiglu_bwd(ref, am_ref, dh, dev_bf16(gu), M, H)
+    gdev = dev_bf16(gu)
+    out = gdev if in_place else empty_bf16(Mr, 2 * H).fill_(9.0)
+    am = empty_f32(1).fill_(5.0)
+    F.ffn_matmul_tn_swiglu_bwd(out, am, a, sa, b, sb, gdev, code, M, H, Kd)
+    torch.cuda.synchronize()
+    assert host_f32(am)[0] == host_f32(am_ref)[0]
+    if M == 0:
+        assert host_f32(am)[0] == 0.0
+        return
+    assert torch.equal(out[:M], ref[:M])
+    dgu_o, _ = O.swiglu_bwd(O.f64_to_bf16_bits(dh_exact[:M]), gu[:M])
+    d = ulp_diff(host_bits(out[:M]), dgu_o)
+    assert d.max() <= 2 and np.mean(d != 0) < 1e-2
+
+
+def test_matmul_tn_swiglu_bwd_full_size(F):
+    """At the Llama-8B shape (M=4096 tokens, H=14336, K=C=4096, e4m3) the
+    fused kernel equals the two calls bit for bit."""
+    M, H, Kd = 4096, 14336, 4096
+    say(f"matmul_tn_swiglu_bwd full size M={M} H={H} K={Kd}")
+    rng = np.random.default_rng(11)
+    a = torch.from_numpy(rng.integers(0, 256, (M, Kd), dtype=np.uint8)).cuda()
+    b = torch.from_numpy(rng.integers(0, 256, (H, Kd), dtype=np.uint8)).cuda()
+    # no NaN codes (0x7F, 0xFF) in the operands
+    a[(a & 0x7F) == 0x7F] = 0x40
+    b[(b & 0x7F) == 0x7F] = 0x40
+    sa, sb = dev_f32([2.0 ** -6]), dev_f32([2.0 ** -6])
+    gu = (torch.randn(M, 2 * H, device="cuda", generator=torch.Generator("cuda").manual_seed(3)) * 2).bfloat16()
+    dh = empty_bf16(M, H)
+    F.ffn_matmul_tn(dh, a, sa, b, sb, F.FFN_E4M3, 0, M, H, Kd)
+    ref, am_ref = empty_bf16(M, 2 * H), empty_f32(1)
+    F.ffn_swiglu_bwd(ref, am_ref, dh, gu, M, H)
+    out, am = empty_bf16(M, 2 * H), empty_f32(1)
+    F.ffn_matmul_tn_swiglu_bwd(out, am, a, sa, b, sb, gu, F.FFN_E4M3, M, H, Kd)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert host_f32(am)[0] == host_f32(am_ref)[0]
+
+
 # ----------------------------------------------------------------------------- RMSNorm backward
 
 @pytest.mark.parametrize("N,C", [(64, 256), (37, 3584), (300, 4096), (5, 8192), (1, 8), (1000, 384)])
@@ -295,12 +366,13 @@ def test_rmsnorm_bwd(F, N, C):
 
 # ----------------------------------------------------------------------------- the block
 
-def _run_block(F, N, C, H, fp8, seed, w_std=0.1, in_place=True, grad_dtype="e4m3"):
+def _run_block(F, N, C, H, fp8, seed, w_std=0.1, in_place=True, grad_dtype="e4m3", fuse=False):
+    """fuse=False: the two-call form, which keeps dh for the stage checks."""
     from transformer_ffn_block_residual_amd import block
     d = W.block_inputs(N, C, H, seed=seed, w_std=w_std)
     pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
     pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pb, in_place=in_place, grad_dtype=grad_dtype)
+    bb = block.BackwardBlock(pb, in_place=in_place, grad_dtype=grad_dtype, fuse_swiglu_bwd=fuse)
     d_out = rand_bits((N, C), 1.0, seed + 1)
     bb.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
     d_out_dev = dev_bf16(d_out)
@@ -398,6 +470,21 @@ def test_block_backward_e5m2_gradients(F, N, C, H):
     assert np.max(np.abs(host_f32(bb.dw_norm) - ref["dw_norm"])) <= 6e-2 * np.max(np.abs(ref["dw_norm"]))
 
 
+@pytest.mark.parametrize("fp8,grad,in_place", [(False, "e4m3", True), (True, "e4m3", False), (True, "e5m2", True)])
+def test_block_backward_fused_swiglu_equals_two_calls(F, fp8, grad, in_place):
+    """BackwardBlock with the fused data gradient + SwiGLU backward gives
+    every output of the two-call form bit for bit."""
+    say(f"block backward fused vs two calls fp8={fp8} grad={grad} in_place={in_place}")
+    N, C, H = 200, 384, 640
+    res = []
+    for fuse in (False, True):
+        d, pb, bb, d_out = _run_block(F, N, C, H, fp8, seed=77, in_place=in_place, grad_dtype=grad, fuse=fuse)
+        res.append({n: getattr(bb, n).clone() for n in ("dgu", "dy", "d_res", "dw_d", "dw_gu", "dw_norm",
+                                                           "am_dgu", "am_dres")})
+    for n in res[0]:
+        assert torch.equal(res[0][n], res[1][n]), n
+
+
 def test_block_backward_accumulates_weight_gradients(F):
     say("block backward twice")
     N, C, H = 128, 256, 384
@@ -450,7 +537,7 @@ def test_block_backward_full_size_sampled(F, grad):
     d = W.block_inputs(N, C, H, seed=1004, w_std=0.02)
     pb = block.PrefillBlock(N, C, H, 1e-5, True)
     pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pb, grad_dtype=grad)
+    bb = block.BackwardBlock(pb, grad_dtype=grad, fuse_swiglu_bwd=False)
     gdec = K.e5m2_decode if grad == "e5m2" else K.e4m3_decode
     gu_keep = empty_bf16(N, 2 * H)
     bb.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
@@ -528,7 +615,7 @@ def test_block_backward_replays_from_a_hip_graph(F, fp8, grad):
 
     run()
     torch.cuda.synchronize()
-    names = ["d_res", "dw_d", "dw_gu", "dw_norm", "dgu", "dh", "dy"]
+    names = ["d_res", "dw_d", "dw_gu", "dw_norm", "dgu", "dy"]   # dh: not written by the fused form
     eager = {n: getattr(bb, n).clone() for n in names}
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()

@@ -19,7 +19,7 @@ _BINDING_NAMES = {
     "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16", "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes",
     "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
-    "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
+    "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_OK", "FFN_ERR_INVALID",
     "FFN_ERR_UNSUPPORTED", "FFN_ERR_HIP", "version", "last_error", "LIB_PATH",

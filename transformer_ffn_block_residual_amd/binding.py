@@ -50,6 +50,7 @@ def _load():
         "ffn_decode_pack_weight": [P, P, I64, I64, P],
         "ffn_decode_gemv_packed": [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_matmul_tn": [P, P, P, P, P, I32, I32, I64, I64, I64, P],
+        "ffn_matmul_tn_swiglu_bwd": [P, P, P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_transpose": [P, P, I64, I64, I64, I32, P],
         "ffn_quant_transpose": [P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_swiglu_bwd": [P, P, P, P, I64, I64, P],
@@ -299,6 +300,19 @@ def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, accumulate, M, N, K, strea
         int(M), int(N), int(K), _stream(stream)))
 
 
+def ffn_matmul_tn_swiglu_bwd(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream=None):
+    """dgu = SwiGLU backward of gu with dh = a b^T (never stored); dtype as
+    ffn_matmul_tn.  dgu may be gu."""
+    fp8 = dtype in (FFN_E4M3, FFN_E5M2)
+    a_dt = E5M2 if dtype == FFN_E5M2 else _dt_elems(dtype)
+    b_dt = E4M3 if fp8 else BF16
+    _check(_lib.ffn_matmul_tn_swiglu_bwd(
+        _ptr(dgu, "dgu", M * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=True),
+        _ptr(a, "a", M * K, a_dt), _ptr(a_scale, "a_scale", 1, F32, optional=not fp8),
+        _ptr(b, "b", H * K, b_dt), _ptr(b_scale, "b_scale", 1, F32, optional=not fp8),
+        _ptr(gu, "gu", M * 2 * H, BF16), int(dtype), int(M), int(H), int(K), _stream(stream)))
+
+
 def ffn_transpose(out, inp, rows, cols, ld_out, elt_bytes, stream=None):
     dt = BF16 if elt_bytes == 2 else E4M3
     _check(_lib.ffn_transpose(
@@ -340,7 +354,7 @@ __all__ = [
     "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16", "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes",
     "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
-    "ffn_matmul_tn", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
+    "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "version", "last_error", "LIB_PATH",
 ]

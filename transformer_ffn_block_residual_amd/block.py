@@ -254,14 +254,18 @@ class BackwardBlock:
     survives for another backward.  grad_dtype ("e4m3" or "e5m2", FP8 blocks
     only): the format of the quantised gradients (the output gradient and
     dMlpUp), each scaled by its abs-max over that format's largest value;
-    weights and activations stay e4m3."""
+    weights and activations stay e4m3.  fuse_swiglu_bwd: the down
+    projection's data gradient and the SwiGLU backward run as one kernel
+    (ffn_matmul_tn_swiglu_bwd), which never writes dh; False runs them as
+    ffn_matmul_tn + ffn_swiglu_bwd and keeps dh (same results bit for bit)."""
 
-    def __init__(self, fwd, in_place=True, grad_dtype="e4m3"):
+    def __init__(self, fwd, in_place=True, grad_dtype="e4m3", fuse_swiglu_bwd=True):
         if grad_dtype not in ("e4m3", "e5m2"):
             raise ValueError(f"grad_dtype {grad_dtype!r}: need 'e4m3' or 'e5m2'")
         if grad_dtype == "e5m2" and not fwd.fp8:
             raise ValueError("an e5m2 gradient needs an FP8 block")
         self.grad_dtype = grad_dtype
+        self.fuse_swiglu_bwd = fuse_swiglu_bwd
         self.f = fwd
         N, C, H = fwd.N, fwd.C, fwd.H
         self.Np = _round_up(max(N, 1), 128)
@@ -338,14 +342,20 @@ class BackwardBlock:
             mk("quant_dout")
             B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, stream)
             mk("transpose_w_down")
-            B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, 0, N, H, C, stream)
-            mk("dx_down")
+            if self.fuse_swiglu_bwd:
+                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, self.qdout, self.s_dout, self.wd_t, f.s_d, self.gu,
+                                           E, N, H, C, stream)
+                mk("dx_down_swiglu_bwd")
+            else:
+                B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, 0, N, H, C, stream)
+                mk("dx_down")
             B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, stream)
             mk("transpose_down_operands")
             B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, 1, C, H, Np, stream)
             mk("dw_down")
-            B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
-            mk("swiglu_bwd")
+            if not self.fuse_swiglu_bwd:
+                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
+                mk("swiglu_bwd")
             # backward_qmm through the up projection (input y, weight [2H, C])
             B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream, E)
             mk("quant_dgu")
@@ -361,15 +371,21 @@ class BackwardBlock:
             Bf = B.FFN_BF16
             B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 2, stream)
             mk("transpose_w_down")
-            B.ffn_matmul_tn(self.dh, d_out, None, self.wd_t, None, Bf, 0, N, H, C, stream)
-            mk("dx_down")
+            if self.fuse_swiglu_bwd:
+                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, d_out, None, self.wd_t, None, self.gu, Bf, N, H, C,
+                                           stream)
+                mk("dx_down_swiglu_bwd")
+            else:
+                B.ffn_matmul_tn(self.dh, d_out, None, self.wd_t, None, Bf, 0, N, H, C, stream)
+                mk("dx_down")
             B.ffn_transpose(self.dout_t, d_out, N, C, Np, 2, stream)
             B.ffn_transpose(self.h_t, f.h, N, H, Np, 2, stream)
             mk("transpose_down_operands")
             B.ffn_matmul_tn(self.dw_d, self.dout_t, None, self.h_t, None, Bf, 1, C, H, Np, stream)
             mk("dw_down")
-            B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
-            mk("swiglu_bwd")
+            if not self.fuse_swiglu_bwd:
+                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
+                mk("swiglu_bwd")
             B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 2, stream)
             mk("transpose_w_up")
             B.ffn_matmul_tn(self.dy, dgu, None, self.wgu_t, None, Bf, 0, N, C, 2 * H, stream)

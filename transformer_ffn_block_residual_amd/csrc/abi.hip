@@ -350,6 +350,35 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const
                       "ffn_matmul_tn");
 }
 
+ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a, const float* a_scale, const void* b,
+                                      const float* b_scale, const void* gu, ffn_dtype_t dtype, int64_t M, int64_t H,
+                                      int64_t K, hipStream_t stream) {
+    REQUIRE(dgu);
+    REQUIRE(a);
+    REQUIRE(b);
+    REQUIRE(gu);
+    NONNEG(M);
+    NONNEG(H);
+    NONNEG(K);
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
+        return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: unknown dtype %d", (int)dtype);
+    const bool fp8 = dtype != FFN_BF16;
+    if (fp8) {
+        REQUIRE(a_scale);
+        REQUIRE(b_scale);
+    }
+    if (ffn_status_t st = check_gemm_dims("ffn_matmul_tn_swiglu_bwd", M, K, H, fp8 ? 1 : 2)) return st;
+    if (H > kMaxDim / 2) return fail(FFN_ERR_UNSUPPORTED, "ffn_matmul_tn_swiglu_bwd: H = %lld too large", (long long)H);
+    ALIGNED(dgu);
+    ALIGNED(a);
+    ALIGNED(b);
+    ALIGNED(gu);
+    if (dgu == a || dgu == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: dgu must not alias a or b");
+    return hip_status(ffn::launch_gemm(dgu, absmax, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)H, stream,
+                                       nullptr, nullptr, false, dtype == FFN_E5M2, gu),
+                      "ffn_matmul_tn_swiglu_bwd");
+}
+
 static ffn_status_t check_transpose(const char* fn, const void* out, const void* in, int64_t rows, int64_t cols,
                                     int64_t ld_out) {
     if (rows < 0 || cols < 0 || ld_out < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);

@@ -251,10 +251,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dgu, float* _
                 const float d = h ? bf16hi(dp[q]) : bf16lo(dp[q]);
                 const float g = h ? bf16hi(gp[q]) : bf16lo(gp[q]);
                 const float u = h ? bf16hi(up[q]) : bf16lo(up[q]);
-                const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-                const float sg = __builtin_amdgcn_rcpf(1.0f + e);
-                rg[h] = d * u * sg * (1.0f + g * (1.0f - sg));
-                ru[h] = d * g * sg;
+                swiglu_bwd_pair(d, g, u, rg[h], ru[h]);
             }
             ogp[q] = pack_bf16x2(rg[0], rg[1]);
             oup[q] = pack_bf16x2(ru[0], ru[1]);

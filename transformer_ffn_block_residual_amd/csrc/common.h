@@ -38,6 +38,18 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+// Gradient of h = silu(g) * u at one element, dh given (every operand a bf16
+// value held in fp32): s = 1 / (1 + exp(-g)),
+//   dg = dh * u * s * (1 + g * (1 - s)),  du = dh * g * s   (fp32, unrounded)
+// One function for the SwiGLU backward pass and the epilogue that fuses it
+// into the data-gradient GEMM, so both round the same fp32 values.
+__device__ __forceinline__ void swiglu_bwd_pair(float d, float g, float u, float& dg, float& du) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+    dg = d * u * sg * (1.0f + g * (1.0f - sg));
+    du = d * g * sg;
+}
+
 // Four fp32 -> four e4m3 codes in one dword (a in the lowest byte).  Values are
 // clamped to +-448 first so the conversion never depends on an overflow mode;
 // v_cvt_pk_fp8_f32 rounds to nearest even.

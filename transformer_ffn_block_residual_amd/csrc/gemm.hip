@@ -78,6 +78,7 @@ struct GemmArgs {
     int tiles_n;   // token-row tiles
     const float* q_absmax;  // SwiGLU + quantise: the known abs-max of h
     float* q_scale;         // ... and where its dequantisation scale goes
+    const uint8_t* aux;     // SwiGLU backward: gu [N, 2H], the layout of out
 };
 
 // A buffer resource (V#) for raw byte addressing: base address, no stride,
@@ -292,7 +293,13 @@ __device__ __forceinline__ u32x4_t regroup_runs(uint32_t x0, uint32_t x1, uint32
 // block j's, so each wait overlaps a block's work.  The loads and waits only
 // add memory operations after the pipeline's in-flight loads, which keeps its
 // counted waits safe (they wait for at least as much).
-template <bool kFP8, bool kFused, bool kQuant, bool kAccum>
+// kSwiBwd (plain output only): the product is dh, the gradient of the SwiGLU
+// output h = silu(g) * u; it is rounded to bf16 as a plain store would round
+// it, and instead of dh the epilogue stores dgu [N, 2H] (dg at feature o, du
+// at H + o) from gu [N, 2H] (a.aux, same layout; it may be out itself), with
+// swiglu_bwd_pair, keeping the running abs-max of the stored dgu.  Its loads
+// of g and u are double-buffered by half-blocks of 32 tokens x 64 features.
+template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kSwiBwd = false>
 __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmArgs& a, int t, float s, float qinv,
                                               int wm, int wn, int fr, int fh, float& amax) {
     int tm, tn;
@@ -307,7 +314,80 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)nrec, 0x00020000);
     const uint32_t row_bytes = (uint32_t)a.ld_out * kOutElt;
     const int r_base = wn * 128 + fr;  // token row within the tile, block j adds 32 j
-    if (!kFused) {
+    if (kSwiBwd) {
+        // gu has the layout of dgu: the same offsets from another base
+        const __amdgpu_buffer_rsrc_t grs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.aux) + n0 * a.ld_out * 2, 0, (int)nrec,
+                                              0x00020000);
+        const uint32_t up_off = (uint32_t)a.O * 2;  // u and du: H = O features further on
+        // half-block hb = (token block j = hb / 2, feature blocks i = 2 (hb % 2)
+        // + 0..1); its group gi = 2 (i % 2) + q: features o .. o + 7
+        auto off_of = [&](int hb, int gi) -> uint32_t {
+            const int j = hb >> 1, i = 2 * (hb & 1) + (gi >> 1), q = gi & 1;
+            const int o = tm * kBM + wm * 128 + i * 32 + 16 * q + 8 * fh;
+            return o < a.O ? (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * 2 : 0x7fffffffu;
+        };
+        u32x4_t gv[2][4], uv[2][4];
+        auto load_hb = [&](int hb, u32x4_t (&gd)[4], u32x4_t (&ud)[4]) {
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const uint32_t off = off_of(hb, gi);
+                gd[gi] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
+                ud[gi] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(grs, off + up_off, 0, 0));
+            }
+        };
+        load_hb(0, gv[0], uv[0]);
+#pragma unroll
+        for (int hb = 0; hb < 8; ++hb) {
+            // 8 loads and 8 stores per half-block; after half-block hb's loads
+            // come hb + 1's loads and (from hb = 1) hb - 1's stores
+            if (hb + 1 < 8) load_hb(hb + 1, gv[(hb + 1) & 1], uv[(hb + 1) & 1]);
+            if (hb == 0 || hb == 7) wait_vmcnt<8>();
+            else wait_vmcnt<16>();
+            __builtin_amdgcn_sched_barrier(0);
+            const int j = hb >> 1;
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * (hb & 1) + ii;
+                const f32x16_t blk = (i == 0 && j == 0) ? read_acc<true>(acc[i][j]) : read_acc<false>(acc[i][j]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    uint32_t d[4];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int g = 2 * q + h;
+                        d[2 * h] = pack_bf16x2(blk[4 * g + 0] * s, blk[4 * g + 1] * s);
+                        d[2 * h + 1] = pack_bf16x2(blk[4 * g + 2] * s, blk[4 * g + 3] * s);
+                    }
+                    const u32x4_t dv = regroup_runs(d[0], d[1], d[2], d[3]);  // dh, features o .. o + 7
+                    const int gi = 2 * ii + q;
+                    const u32x4_t gg = gv[hb & 1][gi], uu = uv[hb & 1][gi];
+                    u32x4_t og, ou;
+                    float m = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float g0, u0, g1, u1;
+                        swiglu_bwd_pair(bf16lo(dv[e]), bf16lo(gg[e]), bf16lo(uu[e]), g0, u0);
+                        swiglu_bwd_pair(bf16hi(dv[e]), bf16hi(gg[e]), bf16hi(uu[e]), g1, u1);
+                        og[e] = pack_bf16x2(g0, g1);
+                        ou[e] = pack_bf16x2(u0, u1);
+                        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(og[e])),
+                                                               __builtin_fabsf(bf16hi(og[e]))));
+                        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(ou[e])),
+                                                               __builtin_fabsf(bf16hi(ou[e]))));
+                    }
+                    // one running maximum, updated in order (left to itself the
+                    // compiler regroups the whole chain and runs out of registers)
+                    amax = __builtin_fmaxf(amax, m);
+                    asm volatile("" : "+v"(amax));
+                    const uint32_t off = off_of(hb, gi);
+                    __builtin_amdgcn_raw_buffer_store_b128(og, rsrc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(ou, rsrc, off + up_off, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    } else if (!kFused) {
         // the previous values of a block's outputs, in the stored (regrouped)
         // order; v_permlane32_swap is its own inverse, so swapping them back
         // gives the accumulator order.  Two blocks' worth, double-buffered.
@@ -417,12 +497,13 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     }
 }
 
-template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kXBf8 = false>
+template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kXBf8 = false, bool kSwiBwd = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a) {
     static_assert(kFused || !kQuant, "quantised output is a SwiGLU epilogue");
     static_assert(!(kFused && kAccum), "accumulation is a plain-output epilogue");
     static_assert(kFP8 || !kXBf8, "e5m2 x is an FP8 operand");
+    static_assert(!(kSwiBwd && (kFused || kAccum)), "the SwiGLU backward is a plain-output epilogue of its own");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
     constexpr int kStoreCnt = epilogue_stores<kFused>();
@@ -560,7 +641,7 @@ void gemm_kernel(GemmArgs a) {
             wait_vmcnt<kWait>();
             barrier();
         }
-        tile_epilogue<kFP8, kFused, kQuant, kAccum>(acc, a, c_t, s, qinv, wm, wn, fr, fh, amax);
+        tile_epilogue<kFP8, kFused, kQuant, kAccum, kSwiBwd>(acc, a, c_t, s, qinv, wm, wn, fr, fh, amax);
         const int t2 = c_t + 2 * G;
         tr_cur = tr_nxt;
         tr_nxt = tile_rsrc<kFused>(a, t2 < T ? t2 : (c_t + G < T ? c_t + G : c_t), wave_u);
@@ -568,7 +649,7 @@ void gemm_kernel(GemmArgs a) {
     // the loads past the end still write the ring: let them land before the
     // workgroup's LDS is reused or released
     wait_vmcnt<0>();
-    if (kFused && a.absmax) {
+    if ((kFused || kSwiBwd) && a.absmax) {
         __syncthreads();
         block_absmax_commit(amax, reinterpret_cast<float*>(lds), a.absmax);
     }
@@ -603,12 +684,17 @@ static int persistent_grid(int T) {
 // Abs-max of a plain (unfused) GEMM output, when asked for: a separate pass.
 // q_absmax / q_scale (SwiGLU only, both or neither): store e4m3 codes of h
 // under that known abs-max instead of bf16 h, and its scale.  x_e5m2 (fp8,
-// plain output): x holds e5m2 codes.
+// plain output): x holds e5m2 codes.  swiglu_gu (plain output, no
+// accumulation): the product is dh and out receives dgu [N, 2O] from gu
+// [N, 2O] (may be out), with its abs-max in absmax.
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
-                       hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2) {
+                       hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2,
+                       const void* swiglu_gu) {
     if (x_e5m2 && (!fp8 || fuse_swiglu)) return hipErrorInvalidValue;
-    if (absmax && (fuse_swiglu || N == 0)) {
+    const bool swi = swiglu_gu != nullptr;
+    if (swi && (fuse_swiglu || accumulate)) return hipErrorInvalidValue;
+    if (absmax && (fuse_swiglu || swi || N == 0)) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
     }
@@ -624,7 +710,9 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     a.K_bytes = K * (fp8 ? 1 : 2);
     a.O = O;
     a.H = O / 2;
-    a.ld_out = fuse_swiglu ? O / 2 : O;
+    a.ld_out = fuse_swiglu ? O / 2 : (swi ? 2 * O : O);
+    a.aux = static_cast<const uint8_t*>(swiglu_gu);
+    if (swi) a.absmax = absmax;
     a.tiles_m = fuse_swiglu ? (O / 2) / 128 : (O + kBM - 1) / kBM;
     a.tiles_n = (int)((N + kBN - 1) / kBN);
     a.q_absmax = q_absmax;
@@ -634,7 +722,11 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const int KT = a.K_bytes / kRowBytes;
     const dim3 grid((unsigned)(KT >= kAhead ? persistent_grid(T) : T)), block(kThreads);
     const bool acc = accumulate && !fuse_swiglu;
-    if (fp8 && x_e5m2) {
+    if (swi) {
+        if (fp8 && x_e5m2) hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true, true>), grid, block, 0, s, a);
+        else if (fp8) hipLaunchKernelGGL((gemm_kernel<true, false, false, false, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, false, false, false, true>), grid, block, 0, s, a);
+    } else if (fp8 && x_e5m2) {
         if (acc) hipLaunchKernelGGL((gemm_kernel<true, false, false, true, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true>), grid, block, 0, s, a);
     } else if (fp8) {
@@ -649,7 +741,7 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
         else hipLaunchKernelGGL((gemm_kernel<false, false, false, false>), grid, block, 0, s, a);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || fuse_swiglu || !absmax) return e;
+    if (e != hipSuccess || fuse_swiglu || swi || !absmax) return e;
     return launch_absmax(absmax, static_cast<const uint16_t*>(out), N * (int64_t)O, s);
 }
 
