@@ -134,7 +134,7 @@ def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m
         what = ("e5m2 x e4m3" if e5 else "e4m3") if w.fp8 else "bf16"
         # reads dgu^T [2H, N] and y^T [C, N] once, reads and writes dW_gu [2H, C]
         return (f"dwup{'5' if e5 else ''}_{workload}", "gemm.hip",
-                [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}>"],
+                [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}, false>"],
                 f"gemm_kernel ({what}, accumulating) of the up projection's weight "
                 f"gradient, [2H, C] = [{2 * H}, {C}], K = N = {N}",
                 2 * H * N * e + C * N * e + 2 * (2 * H * C * 2), 2)
@@ -146,10 +146,10 @@ def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m
     fp8 = "true" if w.fp8 else "false"
     if known_h_absmax:
         # reads x and w, writes the e4m3 codes of h
-        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false, false>"],
+        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false, false, false>"],
                 f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation) of ffn_gateup_swiglu_quant, "
                 f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, 1)
-    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false>"],
+    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false, false>"],
             f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
             N * C * elt + 2 * H * C * elt + N * H * 2, 1)
 
