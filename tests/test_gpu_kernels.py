@@ -521,6 +521,35 @@ def test_decode_packed_workspace_reuse(F):
     assert torch.equal(o_a, o_b) and torch.equal(h_a, h_b)
 
 
+def test_decode_block_packed(F):
+    """DecodeBlockPacked (packed copies of DecodeBlock's codes) against
+    DecodeBlock on the same master weights and through set_fp8_weights, and
+    against the oracle."""
+    from transformer_ffn_block_residual_amd import block
+    M, C, H = 12, 512, 1024
+    say(f"decode block packed M={M} C={C} H={H}")
+    d = W.decode_inputs(M, C, H, seed=321)
+    rows = block.DecodeBlock(M, C, H)
+    rows.load_master_weights(d["w_gate"], d["w_up"], d["w_down"])
+    pk = block.DecodeBlockPacked(M, C, H)
+    pk.load_master_weights(d["w_gate"], d["w_up"], d["w_down"])
+    pk2 = block.DecodeBlockPacked(M, C, H)
+    pk2.set_fp8_weights(rows.wg, rows.sg, rows.wu, rows.su, rows.wd, rows.sd)
+    x = dev_bf16(d["x"])
+    y_rows = rows.forward(x).clone()
+    y_pk = pk.forward(x).clone()
+    pk2.bind(x)()
+    torch.cuda.synchronize()
+    assert torch.equal(pk2.out, y_pk) and torch.equal(pk2.h, pk.h)
+    (qg, sg), (qu, su), (qd, sd) = (O.quant_rows(d[k]) for k in ("w_gate", "w_up", "w_down"))
+    y_ref, h_ref = O.decode_gemv(d["x"], qg, sg, qu, su, qd, sd)
+    assert rel_err(host_bits(pk.h)[:M], h_ref) < 2e-2
+    assert rel_err(host_bits(y_pk)[:M], y_ref) < 3e-2
+    assert rel_err(host_bits(y_pk)[:M], host_bits(y_rows)[:M]) < 2e-2
+    with pytest.raises(NotImplementedError):
+        pk.forward_arm(x, F.FFN_DECODE_SILU_INPUT)
+
+
 def test_decode_empty_batch(F):
     say("decode M=0")
     C, H = 256, 256
