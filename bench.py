@@ -78,6 +78,10 @@ def parse():
                         "(whose persistent grid leaves 32 CUs free); start: on a second stream from the start of "
                         "the step.  Each step joins the second stream before it ends.  Both overlaps measure "
                         "slower than none (the decode needs more than the free CUs)")
+    p.add_argument("--concurrent-backward", action="store_true",
+                   help="backward: each projection's weight gradient on a second stream beside its data gradient, "
+                        "one workgroup per tile (measured no faster than the default single stream); the per-phase "
+                        "times always come from the serial order")
     p.add_argument("--unfused-swiglu-bwd", action="store_true",
                    help="backward: the down projection's data gradient and the SwiGLU backward as two calls "
                         "(ffn_matmul_tn, ffn_swiglu_bwd) instead of ffn_matmul_tn_swiglu_bwd")
@@ -575,7 +579,8 @@ def bench_backward(a, torch, np, B, block, W):
     pre = block.PrefillBlock(N, C, H, w.eps, w.fp8)
     pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
     gd = a.grad_dtype if w.fp8 else "e4m3"
-    bb = block.BackwardBlock(pre, in_place=False, grad_dtype=gd, fuse_swiglu_bwd=not a.unfused_swiglu_bwd)
+    bb = block.BackwardBlock(pre, in_place=False, grad_dtype=gd, fuse_swiglu_bwd=not a.unfused_swiglu_bwd,
+                             concurrent=a.concurrent_backward)
     bb.forward(dev(d["inp"]), dev(d["addend"]))
     d_out = dev(_bwd_dout(np, w, N))
     # the abs-max of d_out, as its producer (the next block's RMSNorm backward)
@@ -637,6 +642,8 @@ def bench_backward(a, torch, np, B, block, W):
                                  "with it (its producer, the next block's RMSNorm backward, writes it)",
                    "N": N, "C": C, "H": H, "seed": w.seed, "backward": True,
                    "swiglu_bwd": "two calls" if a.unfused_swiglu_bwd else "fused into the down data gradient",
+                   "schedule": ("weight gradients on a second stream beside the data gradients"
+                                if a.concurrent_backward else "one stream"),
                    **({"grad_dtype": gd} if w.fp8 else {})},
         "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({(gd if w.fp8 else 'bf16')}, accumulate): "
                                                  "the up projection's weight gradient [2H, C], K = N",

@@ -250,9 +250,19 @@ ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const v
  * scaled TN matmuls; ffn_matmul_tn is that matmul (with bf16 operands as well)
  * and ffn_transpose / ffn_quant_transpose the transposes. */
 
+/* Flags of the TN products.  FFN_TN_ACCUMULATE: add to out (see below).
+ * FFN_TN_TILE_GRID: launch one workgroup per 256 x 256 output tile instead of
+ * a persistent grid sized to the CUs, so that the hardware hands CUs to work
+ * on other streams as tiles finish: for two independent products issued on
+ * two streams (the data and weight gradients of one projection), whose partial
+ * last rounds of tiles then fill each other.  Results do not depend on it. */
+#define FFN_TN_ACCUMULATE 1
+#define FFN_TN_TILE_GRID 2
+
 /* TN matmul: out[m,n] = bf16(acc + sum_k a[m,k] * b[n,k] (* a_scale * b_scale
- * for FP8)), acc = out[m,n] when accumulate != 0 (the accumulate_gradient flag
- * of backward_qmm: one rounding of the fp32 sum), else 0.  [llmq model]
+ * for FP8)), acc = out[m,n] when flags has FFN_TN_ACCUMULATE (the
+ * accumulate_gradient flag of backward_qmm: one rounding of the fp32 sum),
+ * else 0; FFN_TN_TILE_GRID as above; other flag bits are invalid.  [llmq model]
  * backward_qmm, matmul(..., EMMTranspose::TN, accumulate_gradient); the
  * gradient operand is allocated in the grad dtype (e4m3 or e5m2), the weight
  * and activation operands in e4m3.
@@ -262,7 +272,7 @@ ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const v
  * alias a or b. */
 ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale,
                            const void* b, const float* b_scale, ffn_dtype_t dtype,
-                           int accumulate, int64_t M, int64_t N, int64_t K,
+                           int flags, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream);
 
 /* TN matmul fused with the SwiGLU backward: dh = bf16(sum_k a[m,k] * b[n,k]
@@ -274,13 +284,13 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale,
  * DSwiGLU, MlpUp, ...); the two calls run as one kernel, so dSwiGLU never
  * reaches memory.  dgu: bf16 [M, 2H] (gate columns, then up columns); gu: bf16
  * [M, 2H], the forward's gate+up output (dgu may be gu: updated in place);
- * a: [M,K], b: [H,K], dtype and scales as ffn_matmul_tn; absmax: fp32 [1] or
- * NULL.  Supported: K % 128 == 0, H % 128 == 0, any M >= 0; dgu must not alias
- * a or b. */
+ * a: [M,K], b: [H,K], dtype and scales as ffn_matmul_tn; flags: 0 or
+ * FFN_TN_TILE_GRID; absmax: fp32 [1] or NULL.  Supported: K % 128 == 0,
+ * H % 128 == 0, any M >= 0; dgu must not alias a or b. */
 ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a,
                                       const float* a_scale, const void* b, const float* b_scale,
-                                      const void* gu, ffn_dtype_t dtype, int64_t M, int64_t H,
-                                      int64_t K, hipStream_t stream);
+                                      const void* gu, ffn_dtype_t dtype, int flags, int64_t M,
+                                      int64_t H, int64_t K, hipStream_t stream);
 
 /* Transpose: out[c, r] = in[r, c] for r < rows, and 0 for rows <= r < ld_out
  * (zero padding that rounds a token count up to ffn_matmul_tn's K granularity).

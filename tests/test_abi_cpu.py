@@ -167,26 +167,28 @@ def test_decode_arm_and_bf16_validation(lib):
 
 def test_backward_validation(lib):
     B_, C_, D = 0x20000, 0x30000, 0x40000
-    m = lib.ffn_matmul_tn  # out, a, sa, b, sb, dtype, accumulate, M, N, K
+    m = lib.ffn_matmul_tn  # out, a, sa, b, sb, dtype, flags, M, N, K
     assert m(None, B_, None, C_, None, 0, 0, 64, 256, 128, None) == INVALID
     assert m(A, B_, None, C_, None, 1, 0, 64, 256, 128, None) == INVALID           # E4M3 without scales
     assert m(A, B_, None, C_, None, 2, 0, 64, 256, 128, None) == INVALID           # E5M2 without scales
     assert m(A, B_, None, C_, None, 5, 0, 64, 256, 128, None) == INVALID           # unknown dtype
+    assert m(A, B_, None, C_, None, 0, 4, 64, 256, 128, None) == INVALID           # unknown flag bit
     assert m(A, B_, D, C_, D, 2, 0, 64, 200, 128, None) == UNSUPPORTED             # E5M2, N % 128
     assert m(A, B_, None, C_, None, 0, 0, 64, 200, 128, None) == UNSUPPORTED       # N % 128
     assert m(A, B_, None, C_, None, 0, 0, 64, 256, 96, None) == UNSUPPORTED        # K % 128
     assert m(A, A, None, C_, None, 0, 0, 64, 256, 128, None) == INVALID            # out aliases a
     assert m(A, B_, None, MIS, None, 0, 0, 64, 256, 128, None) == UNSUPPORTED      # misaligned b
     assert m(A, B_, None, C_, None, 0, 0, -1, 256, 128, None) == INVALID
-    f = lib.ffn_matmul_tn_swiglu_bwd  # dgu, absmax, a, sa, b, sb, gu, dtype, M, H, K
-    assert f(A, None, B_, None, C_, None, None, 0, 64, 256, 128, None) == INVALID      # no gu
-    assert f(A, None, B_, None, C_, None, D, 1, 64, 256, 128, None) == INVALID         # FP8 without scales
-    assert f(A, None, B_, None, C_, None, D, 7, 64, 256, 128, None) == INVALID         # unknown dtype
-    assert f(A, None, B_, None, C_, None, D, 0, 64, 200, 128, None) == UNSUPPORTED     # H % 128
-    assert f(A, None, B_, None, C_, None, D, 0, 64, 256, 96, None) == UNSUPPORTED      # K % 128
-    assert f(B_, None, B_, None, C_, None, D, 0, 64, 256, 128, None) == INVALID        # dgu aliases a
-    assert f(A, None, B_, None, C_, None, MIS, 0, 64, 256, 128, None) == UNSUPPORTED   # misaligned gu
-    assert f(A, None, B_, None, C_, None, D, 0, -1, 256, 128, None) == INVALID
+    f = lib.ffn_matmul_tn_swiglu_bwd  # dgu, absmax, a, sa, b, sb, gu, dtype, flags, M, H, K
+    assert f(A, None, B_, None, C_, None, None, 0, 0, 64, 256, 128, None) == INVALID      # no gu
+    assert f(A, None, B_, None, C_, None, D, 1, 0, 64, 256, 128, None) == INVALID         # FP8 without scales
+    assert f(A, None, B_, None, C_, None, D, 7, 0, 64, 256, 128, None) == INVALID         # unknown dtype
+    assert f(A, None, B_, None, C_, None, D, 0, 1, 64, 256, 128, None) == INVALID         # accumulate: no
+    assert f(A, None, B_, None, C_, None, D, 0, 0, 64, 200, 128, None) == UNSUPPORTED     # H % 128
+    assert f(A, None, B_, None, C_, None, D, 0, 2, 64, 256, 96, None) == UNSUPPORTED      # K % 128
+    assert f(B_, None, B_, None, C_, None, D, 0, 0, 64, 256, 128, None) == INVALID        # dgu aliases a
+    assert f(A, None, B_, None, C_, None, MIS, 0, 0, 64, 256, 128, None) == UNSUPPORTED   # misaligned gu
+    assert f(A, None, B_, None, C_, None, D, 0, 0, -1, 256, 128, None) == INVALID
     t = lib.ffn_transpose  # out, in, rows, cols, ld_out, elt
     assert t(A, B_, 37, 64, 48, 3, None) == INVALID                                # element size
     assert t(A, B_, 37, 64, 32, 2, None) == INVALID                                # ld_out < rows

@@ -188,9 +188,13 @@ def test_matmul_tn_uneven_rounds_exact(F, M, N, Kd):
     one = dev_f32([1.0])
     out = empty_bf16(M, N).fill_(3.0)
     F.ffn_matmul_tn(out, dev_u8(qa), one, dev_u8(qb), one, F.FFN_E4M3, 0, M, N, Kd)
+    # one workgroup per tile: the same products
+    out_t = empty_bf16(M, N).fill_(3.0)
+    F.ffn_matmul_tn(out_t, dev_u8(qa), one, dev_u8(qb), one, F.FFN_E4M3, F.FFN_TN_TILE_GRID, M, N, Kd)
     torch.cuda.synchronize()
     exact = K.e4m3_decode(qa) @ K.e4m3_decode(qb).T
     assert np.array_equal(host_bits(out), O.f64_to_bf16_bits(exact))
+    assert torch.equal(out_t, out)
 
 
 @pytest.mark.parametrize("M,N,Kd", MM_SHAPES)
@@ -293,9 +297,12 @@ def test_matmul_tn_swiglu_bwd_equals_two_calls(F, M, H, Kd, dt, in_place):
     gdev = dev_bf16(gu)
     out = gdev if in_place else empty_bf16(Mr, 2 * H).fill_(9.0)
     am = empty_f32(1).fill_(5.0)
+    out_t, am_t = empty_bf16(Mr, 2 * H).fill_(9.0), empty_f32(1).fill_(5.0)
+    F.ffn_matmul_tn_swiglu_bwd(out_t, am_t, a, sa, b, sb, dev_bf16(gu), code, M, H, Kd, flags=F.FFN_TN_TILE_GRID)
     F.ffn_matmul_tn_swiglu_bwd(out, am, a, sa, b, sb, gdev, code, M, H, Kd)
     torch.cuda.synchronize()
-    assert host_f32(am)[0] == host_f32(am_ref)[0]
+    assert host_f32(am)[0] == host_f32(am_ref)[0] and host_f32(am_t)[0] == host_f32(am_ref)[0]
+    assert torch.equal(out_t[:M], ref[:M])
     if M == 0:
         assert host_f32(am)[0] == 0.0
         return
@@ -485,6 +492,33 @@ def test_block_backward_fused_swiglu_equals_two_calls(F, fp8, grad, in_place):
         assert torch.equal(res[0][n], res[1][n]), n
 
 
+@pytest.mark.parametrize("fp8,grad,in_place,fuse", [(False, "e4m3", True, True), (False, "e4m3", False, False),
+                                                    (True, "e4m3", True, True), (True, "e5m2", False, True),
+                                                    (True, "e4m3", False, False)])
+def test_block_backward_concurrent_equals_serial(F, fp8, grad, in_place, fuse):
+    """The two-stream schedule (weight gradients beside the data gradients,
+    one workgroup per tile) gives every output of the serial one bit for bit,
+    over two accumulating calls."""
+    say(f"block backward concurrent vs serial fp8={fp8} grad={grad} in_place={in_place} fuse={fuse}")
+    from transformer_ffn_block_residual_amd import block
+    N, C, H = 300, 384, 640
+    d = W.block_inputs(N, C, H, seed=88, w_std=0.1)
+    d_out = dev_bf16(rand_bits((N, C), 1.0, 89))
+    res = []
+    for conc in (False, True):
+        pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
+        pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+        bb = block.BackwardBlock(pb, in_place=in_place, grad_dtype=grad, fuse_swiglu_bwd=fuse, concurrent=conc)
+        for _ in range(2):
+            bb.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
+            bb.backward(d_out)
+        torch.cuda.synchronize()
+        res.append({n: getattr(bb, n).clone() for n in ("dgu", "dy", "d_res", "dw_d", "dw_gu", "dw_norm",
+                                                           "am_dgu", "am_dres")})
+    for n in res[0]:
+        assert torch.equal(res[0][n], res[1][n]), n
+
+
 def test_block_backward_accumulates_weight_gradients(F):
     say("block backward twice")
     N, C, H = 128, 256, 384
@@ -594,17 +628,20 @@ def test_block_backward_full_size_sampled(F, grad):
     assert rms_bwd_close(host_bits(bb.d_res)[rows], dres_ref, d_out[rows], g_dy, g_r, d["w_norm"], g_rstd)
 
 
-@pytest.mark.parametrize("fp8,grad", [(False, "e4m3"), (True, "e4m3"), (True, "e5m2")])
-def test_block_backward_replays_from_a_hip_graph(F, fp8, grad):
+@pytest.mark.parametrize("fp8,grad,conc", [(False, "e4m3", False), (True, "e4m3", False), (True, "e5m2", False),
+                                           (True, "e4m3", True)])
+def test_block_backward_replays_from_a_hip_graph(F, fp8, grad, conc):
     """Forward + backward (gradients zeroed first) captured once, replayed
-    three times with eager work between, equals the eager result bit for bit."""
-    say(f"block backward graph replay fp8={fp8} grad={grad}")
+    three times with eager work between, equals the eager result bit for bit;
+    conc: the two-stream schedule, its second stream forked and joined inside
+    the capture."""
+    say(f"block backward graph replay fp8={fp8} grad={grad} concurrent={conc}")
     from transformer_ffn_block_residual_amd import block
     N, C, H = 200, 384, 256
     d = W.block_inputs(N, C, H, seed=41, w_std=0.1)
     pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
     pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pb, in_place=False, grad_dtype=grad)
+    bb = block.BackwardBlock(pb, in_place=False, grad_dtype=grad, concurrent=conc)
     inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
     d_out = dev_bf16(rand_bits((N, C), 1.0, 42))
 

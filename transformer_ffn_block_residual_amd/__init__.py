@@ -21,7 +21,7 @@ _BINDING_NAMES = {
     "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
     "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",
-    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_OK", "FFN_ERR_INVALID",
+    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "FFN_OK", "FFN_ERR_INVALID",
     "FFN_ERR_UNSUPPORTED", "FFN_ERR_HIP", "version", "last_error", "LIB_PATH",
 }
 

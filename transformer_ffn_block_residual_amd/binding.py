@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libffn.so")
 
 FFN_OK, FFN_ERR_INVALID, FFN_ERR_UNSUPPORTED, FFN_ERR_HIP = 0, 1, 2, 3
 FFN_BF16, FFN_E4M3, FFN_E5M2 = 0, 1, 2
+FFN_TN_ACCUMULATE, FFN_TN_TILE_GRID = 1, 2
 _STATUS = {1: "FFN_ERR_INVALID", 2: "FFN_ERR_UNSUPPORTED", 3: "FFN_ERR_HIP"}
 
 
@@ -50,7 +51,7 @@ def _load():
         "ffn_decode_pack_weight": [P, P, I64, I64, P],
         "ffn_decode_gemv_packed": [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_matmul_tn": [P, P, P, P, P, I32, I32, I64, I64, I64, P],
-        "ffn_matmul_tn_swiglu_bwd": [P, P, P, P, P, P, P, I32, I64, I64, I64, P],
+        "ffn_matmul_tn_swiglu_bwd": [P, P, P, P, P, P, P, I32, I32, I64, I64, I64, P],
         "ffn_transpose": [P, P, I64, I64, I64, I32, P],
         "ffn_quant_transpose": [P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_swiglu_bwd": [P, P, P, P, I64, I64, P],
@@ -287,22 +288,23 @@ def bind_decode_gemv_packed(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down, s
 
 # ----------------------------------------------------------------------------- backward
 
-def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, accumulate, M, N, K, stream=None):
+def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, flags, M, N, K, stream=None):
     """dtype FFN_BF16 / FFN_E4M3: both operands in it; FFN_E5M2: a holds e5m2
-    codes (the gradient), b e4m3 codes."""
+    codes (the gradient), b e4m3 codes.  flags: FFN_TN_ACCUMULATE (or True)
+    and/or FFN_TN_TILE_GRID."""
     fp8 = dtype in (FFN_E4M3, FFN_E5M2)
     a_dt = E5M2 if dtype == FFN_E5M2 else _dt_elems(dtype)
     b_dt = E4M3 if fp8 else BF16
     _check(_lib.ffn_matmul_tn(
         _ptr(out, "out", M * N, BF16), _ptr(a, "a", M * K, a_dt),
         _ptr(a_scale, "a_scale", 1, F32, optional=not fp8), _ptr(b, "b", N * K, b_dt),
-        _ptr(b_scale, "b_scale", 1, F32, optional=not fp8), int(dtype), int(bool(accumulate)),
+        _ptr(b_scale, "b_scale", 1, F32, optional=not fp8), int(dtype), int(flags),
         int(M), int(N), int(K), _stream(stream)))
 
 
-def ffn_matmul_tn_swiglu_bwd(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream=None):
+def ffn_matmul_tn_swiglu_bwd(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream=None, flags=0):
     """dgu = SwiGLU backward of gu with dh = a b^T (never stored); dtype as
-    ffn_matmul_tn.  dgu may be gu."""
+    ffn_matmul_tn; flags 0 or FFN_TN_TILE_GRID.  dgu may be gu."""
     fp8 = dtype in (FFN_E4M3, FFN_E5M2)
     a_dt = E5M2 if dtype == FFN_E5M2 else _dt_elems(dtype)
     b_dt = E4M3 if fp8 else BF16
@@ -310,7 +312,7 @@ def ffn_matmul_tn_swiglu_bwd(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, 
         _ptr(dgu, "dgu", M * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=True),
         _ptr(a, "a", M * K, a_dt), _ptr(a_scale, "a_scale", 1, F32, optional=not fp8),
         _ptr(b, "b", H * K, b_dt), _ptr(b_scale, "b_scale", 1, F32, optional=not fp8),
-        _ptr(gu, "gu", M * 2 * H, BF16), int(dtype), int(M), int(H), int(K), _stream(stream)))
+        _ptr(gu, "gu", M * 2 * H, BF16), int(dtype), int(flags), int(M), int(H), int(K), _stream(stream)))
 
 
 def ffn_transpose(out, inp, rows, cols, ld_out, elt_bytes, stream=None):
@@ -356,5 +358,5 @@ __all__ = [
     "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
     "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",
-    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "version", "last_error", "LIB_PATH",
+    "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "version", "last_error", "LIB_PATH",
 ]

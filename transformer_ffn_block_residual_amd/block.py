@@ -257,15 +257,25 @@ class BackwardBlock:
     weights and activations stay e4m3.  fuse_swiglu_bwd: the down
     projection's data gradient and the SwiGLU backward run as one kernel
     (ffn_matmul_tn_swiglu_bwd), which never writes dh; False runs them as
-    ffn_matmul_tn + ffn_swiglu_bwd and keeps dh (same results bit for bit)."""
+    ffn_matmul_tn + ffn_swiglu_bwd and keeps dh (same results bit for bit).
+    concurrent: each projection's weight gradient (with the transposes only it
+    needs) runs on a second stream beside the data gradient, both launched
+    with FFN_TN_TILE_GRID, so that the partial last round of tiles of one
+    product can fill with tiles of the other; the second stream joins before
+    backward returns.  Same results bit for bit; per-phase marks (``mark``)
+    take the serial order.  Off by default: at the Qwen2-7B shape it measures
+    the same as the serial order (the products are bound by the chip's power,
+    not by idle CUs)."""
 
-    def __init__(self, fwd, in_place=True, grad_dtype="e4m3", fuse_swiglu_bwd=True):
+    def __init__(self, fwd, in_place=True, grad_dtype="e4m3", fuse_swiglu_bwd=True, concurrent=False):
         if grad_dtype not in ("e4m3", "e5m2"):
             raise ValueError(f"grad_dtype {grad_dtype!r}: need 'e4m3' or 'e5m2'")
         if grad_dtype == "e5m2" and not fwd.fp8:
             raise ValueError("an e5m2 gradient needs an FP8 block")
         self.grad_dtype = grad_dtype
         self.fuse_swiglu_bwd = fuse_swiglu_bwd
+        self.concurrent = concurrent
+        self._side = None   # the second stream, made on first use (default priority)
         self.f = fwd
         N, C, H = fwd.N, fwd.C, fwd.H
         self.Np = _round_up(max(N, 1), 128)
@@ -325,6 +335,8 @@ class BackwardBlock:
         ``ffn_rmsnorm_bwd`` does, as the trainer's rmsnorm_backward does for
         DResFFN); None computes it here.  mark(label), when given, is called
         after each phase (for per-phase timing)."""
+        if self.concurrent and mark is None:
+            return self._backward_concurrent(d_out, stream, d_out_absmax)
         f = self.f
         N, C, H, Np = f.N, f.C, f.H, self.Np
         dgu = self.dgu
@@ -399,4 +411,74 @@ class BackwardBlock:
         B.ffn_rmsnorm_bwd(self.d_res, self.dw_norm, self.scratch, d_out, self.dy, self.r, f.w_norm, f.rstd,
                           self.am_dres, N, C, stream)
         mk("rmsnorm_bwd")
+        return self.d_res
+
+    def _backward_concurrent(self, d_out, stream, d_out_absmax):
+        """backward() with the weight gradients on a second stream: after the
+        down projection's operands are ready the second stream transposes h
+        and runs dW_d, while this stream runs the data gradient (with the
+        SwiGLU backward), quantises dMlpUp and transposes the up weight; then
+        the second stream transposes y and runs dW_gu while this one runs the
+        up projection's data gradient and the RMSNorm backward."""
+        f = self.f
+        N, C, H, Np = f.N, f.C, f.H, self.Np
+        dgu = self.dgu
+        main = stream if stream is not None else torch.cuda.current_stream()
+        if self._side is None:
+            self._side = torch.cuda.Stream()
+            self._ev = [torch.cuda.Event() for _ in range(3)]
+        side = self._side
+        T, ACC = B.FFN_TN_TILE_GRID, B.FFN_TN_ACCUMULATE
+
+        def fork(k):
+            self._ev[k].record(main)
+            side.wait_event(self._ev[k])
+
+        if f.fp8:
+            E = B.FFN_E5M2 if self.grad_dtype == "e5m2" else B.FFN_E4M3
+            if d_out_absmax is None:
+                B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, main)
+            else:
+                self.am_dout = d_out_absmax
+            B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, main, E)
+            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, main)
+            fork(0)
+            B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, side)
+            B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, ACC | T, C, H, Np, side)
+            if self.fuse_swiglu_bwd:
+                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, self.qdout, self.s_dout, self.wd_t, f.s_d, self.gu,
+                                           E, N, H, C, main, flags=T)
+            else:
+                B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, T, N, H, C, main)
+                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, main)
+            B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, main, E)
+            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 1, main)
+            fork(1)
+            B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, side)
+            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, ACC | T, 2 * H, C, Np, side)
+            B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, T, N, C, 2 * H, main)
+        else:
+            Bf = B.FFN_BF16
+            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 2, main)
+            fork(0)
+            B.ffn_transpose(self.dout_t, d_out, N, C, Np, 2, side)
+            B.ffn_transpose(self.h_t, f.h, N, H, Np, 2, side)
+            B.ffn_matmul_tn(self.dw_d, self.dout_t, None, self.h_t, None, Bf, ACC | T, C, H, Np, side)
+            if self.fuse_swiglu_bwd:
+                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, d_out, None, self.wd_t, None, self.gu, Bf, N, H, C,
+                                           main, flags=T)
+            else:
+                B.ffn_matmul_tn(self.dh, d_out, None, self.wd_t, None, Bf, T, N, H, C, main)
+                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, main)
+            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 2, main)
+            fork(1)
+            B.ffn_transpose(self.dgu_t, dgu, N, 2 * H, Np, 2, side)
+            B.ffn_transpose(self.y_t, f.y, N, C, Np, 2, side)
+            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, None, self.y_t, None, Bf, ACC | T, 2 * H, C, Np, side)
+            B.ffn_matmul_tn(self.dy, dgu, None, self.wgu_t, None, Bf, T, N, C, 2 * H, main)
+        B.ffn_rmsnorm_bwd(self.d_res, self.dw_norm, self.scratch, d_out, self.dy, self.r, f.w_norm, f.rstd,
+                          self.am_dres, N, C, main)
+        # the second stream's work joins this stream's
+        self._ev[2].record(side)
+        main.wait_event(self._ev[2])
         return self.d_res

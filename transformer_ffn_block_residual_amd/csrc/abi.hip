@@ -325,7 +325,7 @@ ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const v
 // ----------------------------------------------------------------------------- backward
 
 ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const void* b, const float* b_scale,
-                           ffn_dtype_t dtype, int accumulate, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                           ffn_dtype_t dtype, int flags, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     REQUIRE(out);
     REQUIRE(a);
     REQUIRE(b);
@@ -334,6 +334,8 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const
     NONNEG(K);
     if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
         return fail(FFN_ERR_INVALID, "ffn_matmul_tn: unknown dtype %d", (int)dtype);
+    if (flags & ~(FFN_TN_ACCUMULATE | FFN_TN_TILE_GRID))
+        return fail(FFN_ERR_INVALID, "ffn_matmul_tn: unknown flags 0x%x", (unsigned)flags);
     const bool fp8 = dtype != FFN_BF16;
     if (fp8) {
         REQUIRE(a_scale);
@@ -346,13 +348,14 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const
     ALIGNED(b);
     if (out == a || out == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn: out must not alias an operand");
     return hip_status(ffn::launch_gemm(out, nullptr, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)N, stream,
-                                       nullptr, nullptr, accumulate != 0, dtype == FFN_E5M2),
+                                       nullptr, nullptr, (flags & FFN_TN_ACCUMULATE) != 0, dtype == FFN_E5M2, nullptr,
+                                       (flags & FFN_TN_TILE_GRID) != 0),
                       "ffn_matmul_tn");
 }
 
 ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a, const float* a_scale, const void* b,
-                                      const float* b_scale, const void* gu, ffn_dtype_t dtype, int64_t M, int64_t H,
-                                      int64_t K, hipStream_t stream) {
+                                      const float* b_scale, const void* gu, ffn_dtype_t dtype, int flags, int64_t M,
+                                      int64_t H, int64_t K, hipStream_t stream) {
     REQUIRE(dgu);
     REQUIRE(a);
     REQUIRE(b);
@@ -362,6 +365,8 @@ ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a, c
     NONNEG(K);
     if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
         return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: unknown dtype %d", (int)dtype);
+    if (flags & ~FFN_TN_TILE_GRID)
+        return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: unknown flags 0x%x", (unsigned)flags);
     const bool fp8 = dtype != FFN_BF16;
     if (fp8) {
         REQUIRE(a_scale);
@@ -375,7 +380,7 @@ ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a, c
     ALIGNED(gu);
     if (dgu == a || dgu == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: dgu must not alias a or b");
     return hip_status(ffn::launch_gemm(dgu, absmax, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)H, stream,
-                                       nullptr, nullptr, false, dtype == FFN_E5M2, gu),
+                                       nullptr, nullptr, false, dtype == FFN_E5M2, gu, (flags & FFN_TN_TILE_GRID) != 0),
                       "ffn_matmul_tn_swiglu_bwd");
 }
 

@@ -686,11 +686,14 @@ static int persistent_grid(int T) {
 // under that known abs-max instead of bf16 h, and its scale.  x_e5m2 (fp8,
 // plain output): x holds e5m2 codes.  swiglu_gu (plain output, no
 // accumulation): the product is dh and out receives dgu [N, 2O] from gu
-// [N, 2O] (may be out), with its abs-max in absmax.
+// [N, 2O] (may be out), with its abs-max in absmax.  tile_grid: one
+// workgroup per output tile instead of the persistent grid, so that the
+// hardware hands CUs to kernels on other streams as tiles finish (the
+// partial last round of one product fills with the tiles of another).
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2,
-                       const void* swiglu_gu) {
+                       const void* swiglu_gu, bool tile_grid) {
     if (x_e5m2 && (!fp8 || fuse_swiglu)) return hipErrorInvalidValue;
     const bool swi = swiglu_gu != nullptr;
     if (swi && (fuse_swiglu || accumulate)) return hipErrorInvalidValue;
@@ -720,7 +723,7 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const bool quant = fuse_swiglu && q_absmax;
     const int T = a.tiles_m * a.tiles_n;
     const int KT = a.K_bytes / kRowBytes;
-    const dim3 grid((unsigned)(KT >= kAhead ? persistent_grid(T) : T)), block(kThreads);
+    const dim3 grid((unsigned)(KT >= kAhead && !tile_grid ? persistent_grid(T) : T)), block(kThreads);
     const bool acc = accumulate && !fuse_swiglu;
     if (swi) {
         if (fp8 && x_e5m2) hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true, true>), grid, block, 0, s, a);

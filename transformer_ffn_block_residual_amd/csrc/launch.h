@@ -25,11 +25,13 @@ hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t
 // x_e5m2 (fp8, plain output only): x holds e5m2 codes (w stays e4m3).
 // swiglu_gu (plain output, no accumulation): the product is dh = dL/dh of
 // h = silu(g) * u, rounded to bf16; out receives dgu [N, 2O] computed from
-// gu [N, 2O] (which out may be), and absmax max |dgu|.
+// gu [N, 2O] (which out may be), and absmax max |dgu|.  tile_grid: one
+// workgroup per output tile (for products that run beside others).
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr,
-                       bool accumulate = false, bool x_e5m2 = false, const void* swiglu_gu = nullptr);
+                       bool accumulate = false, bool x_e5m2 = false, const void* swiglu_gu = nullptr,
+                       bool tile_grid = false);
 
 // Backward: out[c, r] = in[r, c], zero for rows <= r < ld_out.  (in_bytes,
 // out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3
