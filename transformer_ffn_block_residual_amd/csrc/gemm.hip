@@ -13,8 +13,10 @@
 // 128 x 128 sub-tile = 4 x 4 blocks of the 32x32 MFMA (v_mfma_f32_32x32x16_bf16
 // or v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales): 256 fp32 accumulators
 // per lane, which live in the accumulation registers.  The weight is the MFMA's
-// A operand, so each lane ends up holding four consecutive output features of
-// one token: 8-byte bf16 stores.
+// A operand, so each lane ends up holding runs of four consecutive output
+// features of one token; lane pairs regroup them (v_permlane32_swap) into
+// 16-byte stores.  e4m3 weights may meet e5m2 activations (the backward's
+// gradients), selected by the MFMA's B-format field.
 //
 // LDS layout.  Row r of a stage occupies 64 bytes = 4 chunks of 16 bytes;
 // chunk c is stored at position c ^ ((r / 4) % 4).  The LDS serves a 16-byte
@@ -24,8 +26,8 @@
 // conflicts.  Global loads put 4 lanes on the 4 chunks of one row.
 //
 // Pipeline.  K-steps are loaded straight from global memory into a ring of
-// five LDS stages (global_load_lds_dwordx4, no registers), four steps ahead of
-// the MFMAs.  The fragments of step k+1 are read from LDS into a second
+// five LDS stages (buffer_load_dwordx4 ... lds, no registers), four steps ahead
+// of the MFMAs.  The fragments of step k+1 are read from LDS into a second
 // register set while the MFMAs of step k run, so a step's MFMAs never wait for
 // the LDS; one counted wait (vmcnt) and one barrier per step publish the next
 // stage and retire the oldest.  Inside a step the MFMAs, fragment reads and
@@ -35,13 +37,18 @@
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin; the linear id is
 // remapped so that each XCD receives a contiguous range of tiles, and inside it
 // tiles are grouped 4 weight-panels wide, so the tiles resident on one XCD at a
-// time share weight and token panels in that XCD's L2.
+// time share weight and token panels in that XCD's L2.  The grid is persistent
+// (workgroups walk tiles b, b + G, ..., their K-steps one stream across tiles)
+// or, on request, one workgroup per tile.
 //
 // SwiGLU fusion.  With fuse_swiglu the 256 weight rows of a tile are 128 gate
 // rows and the 128 matching up rows, arranged so that every wave holds gate and
 // up accumulators for the same (token, feature) pairs in matching registers:
 // the epilogue rounds g and u to bf16, forms bf16(silu(g) * u), and folds the
-// tile's abs-max into one atomic.
+// tile's abs-max into one atomic.  Other epilogues: a plain bf16 store; an
+// accumulating one (old + product, one rounding: the backward's weight
+// gradients); and the SwiGLU backward (dh rounded to bf16, then dgu from dh
+// and the forward's gu, with its abs-max).
 #include "common.h"
 #include "launch.h"
 
