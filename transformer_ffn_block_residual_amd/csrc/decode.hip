@@ -18,7 +18,9 @@
 // matching activations of up to 16 tokens (zero beyond M).  The MFMA's K order
 // is free as long as A and B agree, so each lane's 8 codes per MFMA are simply
 // the 8 it loaded.  The eight partial 16 x 16 results are summed through LDS;
-// the row scale multiplies the finished fp32 sum.
+// the row scale multiplies the finished fp32 sum.  The packed form of the same
+// kernel reads weights re-laid per 16-row block and activations re-laid in
+// operand order, one contiguous KiB per load instruction (see kPacked).
 #include "common.h"
 #include "launch.h"
 
