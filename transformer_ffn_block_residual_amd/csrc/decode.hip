@@ -410,36 +410,52 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
     }
 }
 
-// Rows per wave, windows in flight per wave and waves per workgroup of the
-// few-token passes (measured at M = 1 over R in 1..8, U in 1..8 and 2..8 waves:
-// more loads in flight per wave than this run slower, the HBM serving many
-// concurrent row streams less well than fewer longer ones).
-constexpr int kSmallDualR = 1, kSmallDualU = 4, kSmallDownR = 2, kSmallDownU = 2, kSmallWaves = 4;
-// the same at three and four tokens, where the activation loads outnumber the
-// weight loads (measured at M = 3, 4 over R in 1..8, U in 1..4): two rows per
-// wave share each activation load, one window in flight
-constexpr int kSmallDualR4 = 2, kSmallDualU4 = 1, kSmallDownR4 = 2, kSmallDownU4 = 1;
-// waves per row: bf16 rows (twice the windows of e4m3 rows) are split over
-// four waves, which took the single-token bf16 decode from 64 to 60 us; e4m3
-// rows gained nothing from a split (2 or 4 waves, the down pass alone or
-// both), nor from starting each row group's walk at a rotated window.  The
-// choice depends on the weight type alone, so every pass over e4m3 weights
-// sums in the same order.
-constexpr int kSmallKSFp8 = 1, kSmallKSBf16 = 4;
+// Rows per wave (R), windows in flight per wave (U) and waves per row (KS) of
+// a few-token pass, by weight type, projection (kDownW: the down
+// projection's weights) and token count.  Each
+// row group is split over KS waves of one workgroup; a workgroup holds
+// max(4, KS) waves.  Measured with C = 4096, H = 14336 and the weights
+// streamed from HBM:
+//  * e4m3, one token: the down projection's long rows ran at 4.8 TB/s as one
+//    wave per two rows (12.3 us) and at 5.05 TB/s as four rows over eight
+//    waves (11.6 us): each activation load then serves four rows and each
+//    wave's walk is short; one row per wave, or sixteen, ran slower.  The
+//    gate/up pass gained 1% from two rows over four waves.
+//  * e4m3, two tokens: one gate/up row and four windows in flight per wave,
+//    two down rows with two windows, no split (the one-token split: 1% slower).
+//  * e4m3, three and four tokens: the activation loads outnumber the weight
+//    loads; two rows per wave share each, one window in flight, no split (the
+//    one-token split took four tokens from 50 to 60 us).
+//  * bf16 rows (twice the windows of e4m3 rows) split over four waves in both
+//    projections (the single-token bf16 decode 64 -> 60 us); four down rows
+//    per wave at four tokens (74 -> 69 us).
+// More loads in flight per wave than these ran slower.  KS fixes the order of
+// every (row, token) sum (part p sums windows p, p + KS, ...; the parts are
+// added in part order) and R and U do not: at a given token count every arm
+// sums each projection alike, bit for bit.
+struct SmallCfg {
+    int R, U, KS;
+};
+template <bool kBf16W, bool kDownW, int MT>
+constexpr SmallCfg small_cfg() {
+    constexpr bool kWide = MT > 2;
+    if (kBf16W) return kDownW ? SmallCfg{kWide ? 4 : 2, kWide ? 1 : 2, 4} : SmallCfg{kWide ? 2 : 1, kWide ? 1 : 4, 4};
+    if (kWide) return SmallCfg{2, 1, 1};
+    if (MT == 2) return kDownW ? SmallCfg{2, 2, 1} : SmallCfg{1, 4, 1};
+    return kDownW ? SmallCfg{4, 2, 8} : SmallCfg{2, 1, 4};
+}
+constexpr int kSmallMinWaves = 4;
 
-template <int kMode, bool kBf16W, int MT>
+template <int kMode, bool kBf16W, int MT, bool kDownW>
 static hipError_t small_pass(uint16_t* out, int out_ld, const uint16_t* x, int x_ld, const uint8_t* w0,
                              const float* s0, const uint8_t* w1, const float* s1, int M, int K, int rows,
                              hipStream_t s) {
-    constexpr bool kDual = kMode == kSmallDualSilu || kMode == kSmallDualGU;
-    constexpr bool kWide = MT > 2;
-    constexpr int R = kDual ? (kWide ? kSmallDualR4 : kSmallDualR) : (kWide ? kSmallDownR4 : kSmallDownR);
-    constexpr int U = kDual ? (kWide ? kSmallDualU4 : kSmallDualU) : (kWide ? kSmallDownU4 : kSmallDownU);
-    const int waves = rows / R;  // rows are multiples of 128: whole waves of rows
-    constexpr int KS = kBf16W ? kSmallKSBf16 : kSmallKSFp8;
-    constexpr int G = kSmallWaves / KS;  // row groups per workgroup
-    hipLaunchKernelGGL((gemv_small_kernel<kMode, kBf16W, MT, R, U, kSmallWaves, KS>), dim3((waves + G - 1) / G),
-                       dim3(64 * kSmallWaves), 0, s, out, out_ld, x, x_ld, w0, s0, w1, s1, M, K, rows);
+    constexpr SmallCfg cfg = small_cfg<kBf16W, kDownW, MT>();
+    constexpr int kW = cfg.KS > kSmallMinWaves ? cfg.KS : kSmallMinWaves;  // waves per workgroup
+    constexpr int G = kW / cfg.KS;                                         // row groups per workgroup
+    const int groups = rows / cfg.R;  // rows are multiples of 128: whole row groups
+    hipLaunchKernelGGL((gemv_small_kernel<kMode, kBf16W, MT, cfg.R, cfg.U, kW, cfg.KS>), dim3((groups + G - 1) / G),
+                       dim3(64 * kW), 0, s, out, out_ld, x, x_ld, w0, s0, w1, s1, M, K, rows);
     return hipGetLastError();
 }
 
@@ -453,22 +469,22 @@ static hipError_t launch_decode_small(uint16_t* out, uint16_t* h, uint16_t* gu, 
     hipError_t e;
     switch (arm) {
         case kDecodeSiluInput:
-            e = small_pass<kSmallDualGU, kBf16W, MT>(gu, 2 * H, x, C, wg, sg, wu, su, M, C, H, s);
+            e = small_pass<kSmallDualGU, kBf16W, MT, false>(gu, 2 * H, x, C, wg, sg, wu, su, M, C, H, s);
             if (e != hipSuccess) return e;
-            return small_pass<kSmallSingleSiluIn, kBf16W, MT>(out, C, gu, 2 * H, wd, sd, nullptr, nullptr, M, H,
+            return small_pass<kSmallSingleSiluIn, kBf16W, MT, true>(out, C, gu, 2 * H, wd, sd, nullptr, nullptr, M, H,
                                                               C, s);
         case kDecodePerProjection:
-            e = small_pass<kSmallSingle, kBf16W, MT>(gu, 2 * H, x, C, wg, sg, nullptr, nullptr, M, C, H, s);
+            e = small_pass<kSmallSingle, kBf16W, MT, false>(gu, 2 * H, x, C, wg, sg, nullptr, nullptr, M, C, H, s);
             if (e != hipSuccess) return e;
-            e = small_pass<kSmallSingle, kBf16W, MT>(gu + H, 2 * H, x, C, wu, su, nullptr, nullptr, M, C, H, s);
+            e = small_pass<kSmallSingle, kBf16W, MT, false>(gu + H, 2 * H, x, C, wu, su, nullptr, nullptr, M, C, H, s);
             if (e != hipSuccess) return e;
             e = launch_swiglu(h, nullptr, gu, M, H, s);
             if (e != hipSuccess) return e;
-            return small_pass<kSmallSingle, kBf16W, MT>(out, C, h, H, wd, sd, nullptr, nullptr, M, H, C, s);
+            return small_pass<kSmallSingle, kBf16W, MT, true>(out, C, h, H, wd, sd, nullptr, nullptr, M, H, C, s);
         default:
-            e = small_pass<kSmallDualSilu, kBf16W, MT>(h, H, x, C, wg, sg, wu, su, M, C, H, s);
+            e = small_pass<kSmallDualSilu, kBf16W, MT, false>(h, H, x, C, wg, sg, wu, su, M, C, H, s);
             if (e != hipSuccess) return e;
-            return small_pass<kSmallSingle, kBf16W, MT>(out, C, h, H, wd, sd, nullptr, nullptr, M, H, C, s);
+            return small_pass<kSmallSingle, kBf16W, MT, true>(out, C, h, H, wd, sd, nullptr, nullptr, M, H, C, s);
     }
 }
 
