@@ -26,6 +26,13 @@
  *     returns a thread-local description of the last non-OK status.
  *   - Calls that share an output buffer on different streams race; calls on one
  *     stream are ordered.
+ *   - Size limits (FFN_ERR_UNSUPPORTED beyond them): each input operand of a
+ *     GEMM (ffn_gateup, ffn_gateup_swiglu_quant, ffn_down, ffn_matmul_tn,
+ *     ffn_matmul_tn_swiglu_bwd) is under 4 GiB and its row count under
+ *     2^31 - 256 (the kernels keep byte offsets inside one operand in 32 bits;
+ *     outputs may be larger); each decode weight matrix is under 2 GiB; row
+ *     counts of the row-wise kernels are at most 2^31; ffn_quant_absmax,
+ *     ffn_swiglu and ffn_swiglu_bwd take up to 2^36 elements.
  *
  * Citations name the page and the function on it that defines the operation:
  *   [llmq model]  IST-DASLab llmq, src/models/llama_model.cpp
