@@ -238,8 +238,9 @@ int64_t ffn_decode_packed_workspace_bytes(int64_t M, int64_t C, int64_t H);
  * fp32 summation order) on packed weights: w_gate, w_up [H, C] and w_down
  * [C, H] in the layout of ffn_decode_pack_weight; scales, x, h and out as in
  * ffn_decode_gemv.  workspace: ffn_decode_packed_workspace_bytes(M, C, H)
- * bytes, 16-byte aligned, caller-owned; it receives x and h in the order of
- * the MFMA's activation operand (written and read within the call).
+ * bytes, 16-byte aligned, caller-owned; it receives h (and, above 16 tokens
+ * or C > 4096, x) in the order of the MFMA's activation operand (written and
+ * read within the call).
  * Supported: 0 <= M <= 32, C % 128 == 0, H % 128 == 0; the workspace must not
  * alias out, h or x.  Calls that share a workspace must not overlap. */
 ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const void* x,

@@ -459,7 +459,13 @@ def test_decode_pack_weight_layout(F, rows, cols):
     assert np.array_equal(host_u8(out).reshape(rows, cols), want)
 
 
-PACKED_SHAPES = [(1, 1152, 640), (5, 3584, 384), (16, 384, 896), (16, 3584, 18944), (17, 256, 640), (32, 256, 256)]
+# Up to 16 tokens, C <= 4096 and row blocks (H / 16) that fill their rounds
+# on the 256 CUs to 90% or more, the dual pass keeps the activations in LDS:
+# here H = 4096, 8192 and 18944 (a half last chunk at C = 1152 and 640; C =
+# 4096 fills the LDS copy).  The other shapes take the fragment-order copy in
+# the workspace (too few row blocks, C > 4096, more than 16 tokens).
+PACKED_SHAPES = [(1, 1152, 640), (5, 3584, 384), (16, 384, 896), (16, 3584, 18944), (3, 4224, 256), (17, 256, 640),
+                 (32, 256, 256), (1, 1152, 4096), (5, 4096, 4096), (16, 384, 8192), (13, 640, 4096)]
 
 
 @pytest.mark.parametrize("M,C,H", PACKED_SHAPES)

@@ -213,6 +213,152 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
     }
 }
 
+// The dual pass of the packed decode for up to 16 tokens, persistent, with
+// the activations in LDS.  At 16 tokens each KiB of weight codes meets 2 KiB
+// of activation fragments, which decode_kernel reads from L2 once per row
+// block.  Here each workgroup (one per CU: the copy fills most of the LDS)
+// issues its first row block's weight loads, copies x from row-major order
+// into LDS in fragment order (the layout pack_x_kernel writes for token block
+// 0, zero past M; every load of the copy in flight before the first LDS
+// write), then walks the row blocks blk = blockIdx.x, + gridDim.x, ... with
+// the next block's weights loaded before the current block is multiplied:
+// only weights stream from memory, and x needs no separate re-layout launch.
+// Per row block the waves split the chunks as in decode_kernel (chunk
+// c = cw + rot, rot from the block index), the sums meet in LDS in wave
+// order, and wave 0 runs decode_kernel's epilogue (h to out, and to hp in
+// fragment order for the down pass); the results do not depend on the grid
+// size.  K <= kLdsDualMaxK, K % 128 == 0, rows % 16 == 0.
+constexpr int kLdsDualMaxK = 4096;
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void decode_dual_lds_kernel(
+    uint16_t* __restrict__ out, uint16_t* __restrict__ hp, const uint16_t* __restrict__ x,
+    const uint8_t* __restrict__ w0, const float* __restrict__ s0, const uint8_t* __restrict__ w1,
+    const float* __restrict__ s1, int M, int K, int rows) {
+    __shared__ uint4 xs[kLdsDualMaxK / 32 * 64];  // fragment f, lane l: piece 64 f + l (128 KiB at most)
+    __shared__ f32x4_t red[kWaves][2][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int nblocks = rows / 16;
+    const int nchunks = (K + kChunk - 1) / kChunk;  // <= kLdsDualMaxK / kChunk
+    constexpr int kCPW = (kLdsDualMaxK / kChunk + kWaves - 1) / kWaves;  // chunks per wave per block
+    // Chunk j of this wave in row block b starts at byte kb (K: no chunk).
+    auto chunk_kb = [&](int b, int j) {
+        const int cw = wave + j * kWaves;
+        const int rot = (int)(((unsigned)b * 5u) % (unsigned)nchunks);
+        const int c = cw + rot < nchunks ? cw + rot : cw + rot - nchunks;
+        return cw < nchunks ? c * kChunk : K;
+    };
+    // The weights of the next row block are loaded before the current one is
+    // multiplied and reduced, so the loads stay in flight across the barriers.
+    auto load_block = [&](int b, uint4 (&wq)[kCPW][2][kPieces]) {
+        const int64_t wbase = (int64_t)b * 16 * K + lane * 16;
+#pragma unroll
+        for (int j = 0; j < kCPW; ++j) {
+            const int kb = chunk_kb(b, j);
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) {
+                const bool in = kb + 64 * i < K;
+                wq[j][0][i] = in ? *reinterpret_cast<const uint4*>(w0 + wbase + (int64_t)(kb + 64 * i) * 16)
+                                 : make_uint4(0, 0, 0, 0);
+                wq[j][1][i] = in ? *reinterpret_cast<const uint4*>(w1 + wbase + (int64_t)(kb + 64 * i) * 16)
+                                 : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    uint4 wcur[kCPW][2][kPieces];
+    if (blockIdx.x < nblocks) load_block(blockIdx.x, wcur);
+    // the activations go to LDS while the first block's weights are in flight
+    // (every load of the copy is issued before the first LDS write)
+    {
+        const int pieces = K / 32 * 64;
+        constexpr int kPer = kLdsDualMaxK / 32 * 64 / (64 * kWaves);  // pieces per thread at most
+        uint4 v[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int p = threadIdx.x + j * 64 * kWaves;
+            const int l = p & 63, f = p >> 6;
+            const int k0 = 64 * (f >> 1) + 16 * (l >> 4) + 8 * (f & 1);
+            v[j] = p < pieces && (l & 15) < M ? *reinterpret_cast<const uint4*>(x + (int64_t)(l & 15) * K + k0)
+                                              : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int p = threadIdx.x + j * 64 * kWaves;
+            if (p < pieces) xs[p] = v[j];
+        }
+    }
+    __syncthreads();
+    for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+        const int row0 = blk * 16;
+        uint4 wnxt[kCPW][2][kPieces];
+        if (blk + (int)gridDim.x < nblocks) load_block(blk + gridDim.x, wnxt);
+        f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int j = 0; j < kCPW; ++j) {
+            const int kb = chunk_kb(blk, j);
+            if (kb >= K) continue;
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) {
+                const bool in = kb + 64 * i < K;
+                const int f = (kb + 64 * i) / 32;
+                const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, in ? xs[f * 64 + lane] : make_uint4(0, 0, 0, 0));
+                const bf16x8_t xb1 =
+                    __builtin_bit_cast(bf16x8_t, in ? xs[(f + 1) * 64 + lane] : make_uint4(0, 0, 0, 0));
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const bf16x8_t a0 = e4m3x8_to_bf16(wcur[j][m][i].x, wcur[j][m][i].y);
+                    const bf16x8_t a1 = e4m3x8_to_bf16(wcur[j][m][i].z, wcur[j][m][i].w);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xb0, acc[m], 0, 0, 0);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xb1, acc[m], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kCPW; ++j)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < kPieces; ++i) wcur[j][m][i] = wnxt[j][m][i];
+        red[wave][0][lane] = acc[0];
+        red[wave][1][lane] = acc[1];
+        __syncthreads();
+        if (wave == 0) {
+            f32x4_t fin[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                f32x4_t v = red[0][m][lane];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) {
+                    const f32x4_t u = red[w][m][lane];
+                    v[0] += u[0];
+                    v[1] += u[1];
+                    v[2] += u[2];
+                    v[3] += u[3];
+                }
+                fin[m] = v;
+            }
+            // lane: token lr, weight rows orow0 .. + 3 of the block
+            const int orow0 = row0 + 4 * lq;
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float g = round_bf16(s0[orow0 + r] * fin[0][r]);
+                const float u = round_bf16(s1[orow0 + r] * fin[1][r]);
+                o[r] = silu_mul(g, u);
+            }
+            uint2 v;
+            v.x = pack_bf16x2(o[0], o[1]);
+            v.y = pack_bf16x2(o[2], o[3]);
+            const int k = orow0;  // h in fragment order, as decode_kernel writes it
+            const int64_t off = (int64_t)(2 * (k / 64) + (k % 16) / 8) * 512 + (lr + 16 * ((k % 64) / 16)) * 8 + (k % 8);
+            *reinterpret_cast<uint2*>(hp + off) = v;
+            if (lr < M) *reinterpret_cast<uint2*>(out + (int64_t)lr * rows + orow0) = v;
+        }
+        __syncthreads();  // red is rewritten by the next block
+    }
+}
+
 // Few-token form (M <= 4) of the passes, on the vector ALU.  With one to
 // four tokens the MFMA above multiplies mostly zero columns and spends as many
 // load instructions on activations as on weights.  Here the 64 lanes of a wave
@@ -571,6 +717,7 @@ __global__ __launch_bounds__(256) void pack_x_kernel(uint16_t* __restrict__ xp, 
 // flight per wave); the down pass of two token blocks keeps 8 waves, since
 // 16 waves of a workgroup have at most 128 registers each
 constexpr int kPackedDualWaves = 4;
+constexpr int kLdsDualWaves = 8;  // waves per workgroup of decode_dual_lds_kernel
 template <int TB> constexpr int packed_down_waves() { return TB == 1 ? 16 : 8; }
 
 int64_t decode_packed_ws_elems(int M, int C, int H) {
@@ -599,6 +746,25 @@ hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const 
     const int TB = M <= 16 ? 1 : 2;
     uint16_t* xp = ws;                        // [TB][16 C] fragment order
     uint16_t* hp = ws + (int64_t)TB * 16 * C;  // [TB][16 H]
+    // The persistent LDS dual pass (one workgroup per CU: the activations fill
+    // most of its LDS) when its rounds of row blocks are nearly full: measured
+    // faster on the Qwen2-7B shape (1184 blocks, five rounds on 256 CUs, 93%
+    // full: 61.0 -> 58.6 us at 16 tokens) and slower on the Llama-8B shape (896
+    // blocks, four rounds 88% full: 45.0 -> 46.1 us), where decode_kernel's
+    // one workgroup per row block balances better.
+    const int nblk = H / 16, cus = device_cu_count();
+    const int rounds = (nblk + cus - 1) / cus;
+    if (TB == 1 && C <= kLdsDualMaxK && (int64_t)nblk * 10 >= (int64_t)rounds * cus * 9) {
+        const int grid = min(nblk, cus);
+        hipLaunchKernelGGL((decode_dual_lds_kernel<kLdsDualWaves>), dim3(grid), dim3(64 * kLdsDualWaves), 0, s, h, hp,
+                           x, wg, sg, wu, su, M, C, H);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        constexpr int kDownW = packed_down_waves<1>();
+        hipLaunchKernelGGL((decode_kernel<false, 1, 1, kDownW, true>), dim3(C / 16), dim3(64 * kDownW), 0, s, out,
+                           nullptr, hp, wd, sd, nullptr, nullptr, M, H, C);
+        return hipGetLastError();
+    }
     const int64_t pieces = (int64_t)TB * (C / 32) * 64;
     hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, xp, x, M, C, pieces);
     hipError_t e = hipGetLastError();

@@ -662,7 +662,7 @@ void gemm_kernel(GemmArgs a) {
     }
 }
 
-static int cu_count() {
+int device_cu_count() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -681,7 +681,7 @@ static int cu_count() {
 // the CUs left over (64 of 256 for the 448 tiles of a 3584 x 8192 output) stay
 // free for work on other streams.
 static int persistent_grid(int T) {
-    const int cu = cu_count();
+    const int cu = device_cu_count();
     if (T <= cu) return T;
     const int rounds = (T + cu - 1) / cu;
     const int g = ((T + rounds - 1) / rounds + 7) / 8 * 8;

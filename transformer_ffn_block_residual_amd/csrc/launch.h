@@ -8,6 +8,8 @@
 namespace ffn {
 
 hipError_t launch_fill(float* p, int n, float v, hipStream_t s);
+// compute units of the current device (cached per device; 256 if unknown)
+int device_cu_count();
 hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
                           const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s);
 hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_t s);
