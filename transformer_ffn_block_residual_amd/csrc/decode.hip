@@ -566,7 +566,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_small_kernel(
 //    wave per two rows (12.3 us) and at 5.05 TB/s as four rows over eight
 //    waves (11.6 us): each activation load then serves four rows and each
 //    wave's walk is short; one row per wave, or sixteen, ran slower.  The
-//    gate/up pass gained 1% from two rows over four waves.
+//    gate/up pass, one row over two waves with two windows in flight each,
+//    took the call from 32.1-32.4 to 31.9 us (two rows over four waves: 1%
+//    less; four or eight waves per row, or four rows per wave: slower).
 //  * e4m3, two tokens: one gate/up row and four windows in flight per wave,
 //    two down rows with two windows, no split (the one-token split: 1% slower).
 //  * e4m3, three and four tokens: the activation loads outnumber the weight
@@ -588,7 +590,7 @@ constexpr SmallCfg small_cfg() {
     if (kBf16W) return kDownW ? SmallCfg{kWide ? 4 : 2, kWide ? 1 : 2, 4} : SmallCfg{kWide ? 2 : 1, kWide ? 1 : 4, 4};
     if (kWide) return SmallCfg{2, 1, 1};
     if (MT == 2) return kDownW ? SmallCfg{2, 2, 1} : SmallCfg{1, 4, 1};
-    return kDownW ? SmallCfg{4, 2, 8} : SmallCfg{2, 1, 4};
+    return kDownW ? SmallCfg{4, 2, 8} : SmallCfg{1, 2, 2};
 }
 constexpr int kSmallMinWaves = 4;
 
