@@ -49,6 +49,8 @@
 // accumulating one (old + product, one rounding: the backward's weight
 // gradients); and the SwiGLU backward (dh rounded to bf16, then dgu from dh
 // and the forward's gu, with its abs-max).
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -663,15 +665,16 @@ void gemm_kernel(GemmArgs a) {
 }
 
 int device_cu_count() {
-    static int cached[64] = {0};
+    // per device, filled on first use; threads that race here store the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // Workgroups of the persistent grid for T tiles: as many rounds of tiles as
