@@ -500,6 +500,35 @@ def test_decode_packed(F, M, C, H):
     assert rel_err(gy, y_ref) < 3e-2
 
 
+def test_decode_packed_lds_and_copy_forms_agree(F):
+    """The persistent LDS dual pass (16 tokens) and the workspace-copy form
+    (the same 16 tokens plus one, two token blocks) on the same rows: the
+    sums differ only in fp32 order, so h agrees to one bf16 ulp, nearly
+    everywhere exactly, and y within the down pass's rounding."""
+    C, H = 1152, 4096   # 256 row blocks: one full round on 256 CUs
+    say(f"decode packed LDS vs copy form C={C} H={H}")
+    d = W.decode_inputs(17, C, H, seed=4242)
+    wq, ws = _decode_weights(F, d)
+    pk = {}
+    for k in ("w_gate", "w_up", "w_down"):
+        rows, cols = d[k].shape
+        pk[k] = empty_u8(rows, cols)
+        F.ffn_decode_pack_weight(pk[k], wq[k], rows, cols)
+    wts = (pk["w_gate"], ws["w_gate"], pk["w_up"], ws["w_up"], pk["w_down"], ws["w_down"])
+    x17 = dev_bf16(d["x"])
+    res = {}
+    for M in (16, 17):
+        wsp = empty_bf16(F.ffn_decode_packed_workspace_bytes(M, C, H) // 2)
+        o, h = empty_bf16(M, C), empty_bf16(M, H)
+        F.ffn_decode_gemv_packed(o, h, wsp, x17[:M].contiguous(), *wts, M, C, H)
+        res[M] = (o, h)
+    torch.cuda.synchronize()
+    h16, h17 = host_bits(res[16][1]), host_bits(res[17][1][:16])
+    dh = ulp_diff(h16, h17)
+    assert dh.max() <= 1 and np.mean(dh != 0) < 1e-2
+    assert rel_err(host_bits(res[16][0]), host_bits(res[17][0][:16])) < 1e-2
+
+
 def test_decode_packed_workspace_reuse(F):
     """One workspace, a 32-token call and then a 5-token one: the second
     result equals a call on a fresh workspace bit for bit (nothing of the
