@@ -23,8 +23,10 @@ docstring.  Shapes: N rows, C hidden, H intermediate; all matrices row-major;
 weights are ``[out, in]``.
 
 Precision: sums and dot products in fp64 (numpy), one rounding to each stored
-type.  bf16 tensors enter and leave as uint16 bit patterns, e4m3 as uint8,
-fp32 scalars and vectors as float32.
+type; the elementwise products the block takes in fp32 (the RMSNorm output's
+two products, the product that decides a code) are fp32 products here too.
+bf16 tensors enter and leave as uint16 bit patterns, e4m3 as uint8, fp32
+scalars and vectors as float32.
 """
 
 import numpy as np
@@ -55,11 +57,15 @@ def rms_rstd(r_bits, eps):
 
 
 def rms_apply(r_bits, rstd, weight_bits):
-    """y_ij = bf16( r_ij * rstd_i * w_j ) with the stored fp32 rstd, and
-    max |y| over the stored bf16 y.  Returns (y_bits, absmax float32)."""
-    r = bf16_bits_to_f64(r_bits)
-    w = bf16_bits_to_f64(weight_bits)
-    y = bf16_round(r * np.asarray(rstd, np.float32).astype(np.float64)[..., None] * w[None, :])
+    """y_ij = bf16( fp32( fp32(r_ij * rstd_i) * w_j ) ) with the stored fp32
+    rstd, and max |y| over the stored bf16 y.  The two products are fp32
+    products (the block's arithmetic is fp32), then one rounding to bf16.
+    Returns (y_bits, absmax float32)."""
+    r = bf16_bits_to_f64(r_bits).astype(np.float32)
+    w = bf16_bits_to_f64(weight_bits).astype(np.float32)
+    t = r * np.asarray(rstd, np.float32)[..., None]
+    y32 = t * w[None, :]
+    y = bf16_round(y32.astype(np.float64))
     absmax = _f32(np.max(np.abs(y))) if y.size else _f32(0.0)
     return f64_to_bf16_bits(y), absmax
 
@@ -73,7 +79,7 @@ def rmsnorm_fwd(inp_bits, addend_bits, weight_bits, eps):
 
       r_i    = bf16(inp_i + addend_i)            (r = inp when there is no addend)
       rstd_i = fp32( 1 / sqrt( sum_j r_ij^2 / C + eps ) )
-      y_ij   = bf16( r_ij * rstd_i * w_j )       (rstd as stored, fp32)
+      y_ij   = bf16( (r_ij * rstd_i) * w_j )     (fp32 products, rstd as stored)
       absmax = max_ij |y_ij|                     over the stored bf16 y
 
     Readings: eps inside the square root, mean by division by C; y from the
@@ -95,7 +101,8 @@ def rmsnorm_fwd(inp_bits, addend_bits, weight_bits, eps):
 
 def absmax_of(bits):
     """max |x| over a bf16 tensor, as fp32 (exact: a bf16 value is an fp32 value).
-    llama_model.cpp, ``_forward_block``: ``abs_max(...)``."""
+    llama_model.cpp, ``_forward_block``: ``abs_max(...)``.  A NaN element makes
+    the abs-max NaN."""
     x = bf16_bits_to_f64(bits)
     return _f32(np.max(np.abs(x))) if x.size else _f32(0.0)
 
@@ -107,11 +114,13 @@ def scales_from_absmax(absmax, fmt="e4m3"):
     llama_run_state.cpp ``allocate_fwd_quant_tensors``): scale is the
     dequantisation factor absmax/max and inv = max/absmax multiplies the input,
     with max the format's largest finite value (448 for e4m3, 57344 for e5m2);
-    both are IEEE fp32 quotients.  An all-zero tensor gets scale = inv = 1.
+    both are IEEE fp32 quotients.  An all-zero tensor (absmax == 0) gets
+    scale = inv = 1; a NaN abs-max (a NaN anywhere in the tensor) gives NaN for
+    both, so every code of the tensor is a NaN code.
     """
     fmax = FP8_FORMATS[fmt][2]
     am = np.float64(_f32(absmax))
-    if am > 0:
+    if am != 0:
         return _f32(am / fmax), _f32(fmax / am)
     return _f32(1.0), _f32(1.0)
 
@@ -189,27 +198,6 @@ def swiglu(gu_bits):
     h = bf16_round(silu(gu[..., :H]) * gu[..., H:])
     am = _f32(np.max(np.abs(h))) if h.size else _f32(0.0)
     return f64_to_bf16_bits(h), am
-
-
-def gateup(x, w, fuse_swiglu, x_scale=None, w_scale=None):
-    """The fused gate+up projection ``[N, C] x [2H, C]^T -> [N, 2H]`` (bf16 when
-    the scales are None, else e4m3 operands with their fp32 scales), optionally
-    followed by SwiGLU.  The fused form rounds g and u to bf16 before the
-    activation, so it equals ``swiglu(gateup(...))`` exactly.
-    Returns gu_bits, or (h_bits, absmax) when fused."""
-    if x_scale is None:
-        gu = gemm_bf16(x, w)
-    else:
-        gu = gemm_fp8(x, x_scale, w, w_scale)
-    return swiglu(gu) if fuse_swiglu else gu
-
-
-def down(h, w, h_scale=None, w_scale=None):
-    """The down projection ``[N, H] x [C, H]^T -> [N, C]`` (llama_model.cpp,
-    ``_forward_block``: ``forward_qmm(MlpDown, SwiGLu, MLP_Down_w, ..., D, C)``)."""
-    if h_scale is None:
-        return gemm_bf16(h, w)
-    return gemm_fp8(h, h_scale, w, w_scale)
 
 
 def decode_dual(x_bits, wg, sg, wu, su):
