@@ -230,17 +230,25 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
 ffn_status_t ffn_decode_pack_weight(uint8_t* packed, const uint8_t* w, int64_t rows,
                                     int64_t cols, hipStream_t stream);
 
-/* Workspace bytes of ffn_decode_gemv_packed for M tokens: 32 (C + H) bytes
- * per 16-token block; -1 for sizes it does not support. */
+/* Workspace bytes of ffn_decode_gemv_packed for M tokens; -1 for sizes it
+ * does not support.  Up to 16 tokens: 32 (C + H) bytes (x and h in the MFMA's
+ * operand order) plus 64 S C bytes of fp32 partial sums of the down
+ * projection, which is split along its reduction dimension H into
+ * S = max(1, min(H/64, max(256 / (C/128), ceil(H/64 / 64)))) slices (a
+ * function of the shape alone, so results do not depend on the device);
+ * 17 to 32 tokens: the larger of that and 64 (C + H) bytes.  Never smaller
+ * for more tokens, so a workspace sized for the largest batch serves every
+ * smaller one. */
 int64_t ffn_decode_packed_workspace_bytes(int64_t M, int64_t C, int64_t H);
 
 /* The split-SiLU decode of ffn_decode_gemv (same formulas, same results up to
  * fp32 summation order) on packed weights: w_gate, w_up [H, C] and w_down
  * [C, H] in the layout of ffn_decode_pack_weight; scales, x, h and out as in
  * ffn_decode_gemv.  workspace: ffn_decode_packed_workspace_bytes(M, C, H)
- * bytes, 16-byte aligned, caller-owned; it receives h (and, above 16 tokens
- * or C > 4096, x) in the order of the MFMA's activation operand (written and
- * read within the call).
+ * bytes, 16-byte aligned, caller-owned, any contents; it receives h (and,
+ * above 16 tokens or C > 4096, x) in the order of the MFMA's activation
+ * operand and, up to 16 tokens, the down projection's partial sums over its
+ * S slices, added in slice order (all written and read within the call).
  * Supported: 0 <= M <= 32, C % 128 == 0, H % 128 == 0; the workspace must not
  * alias out, h or x.  Calls that share a workspace must not overlap. */
 ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const void* x,

@@ -91,3 +91,27 @@ def within_dot_bound(got_bits, exact, mag, rel_out=2.0 ** -8, rel_sum=2.0 ** -14
     sum of magnitudes."""
     g = K.bf16_bits_to_f64(got_bits)
     return np.abs(g - exact) <= rel_out * np.abs(exact) + rel_sum * mag
+
+
+def flip_bound(dq_got, dq_ref, w_abs):
+    """Sum_j |dq_got[n, j] - dq_ref[n, j]| * w_abs[o, j]: how far an output of a
+    product with weights w can move when its input's dequantised values
+    differ between two chains (codes that one chain rounded to a neighbouring
+    grid point).  A sparse product over the differing entries, so the cost
+    follows their number."""
+    import scipy.sparse as sp
+    d = np.abs(np.asarray(dq_got, np.float64) - np.asarray(dq_ref, np.float64))
+    return np.asarray(sp.csr_matrix(d) @ np.asarray(w_abs, np.float64).T)
+
+
+def rel_err_with_bound(got_bits, ref_bits, bound):
+    """max_i (|g_i - r_i| - bound_i) / max(|r_i|, rms(r)): rel_err after the
+    allowed movement `bound` (>= 0, the ref's shape) has been taken off."""
+    g = K.bf16_bits_to_f64(got_bits)
+    r = K.bf16_bits_to_f64(ref_bits)
+    if r.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(r * r))
+    den = np.maximum(np.abs(r), rms)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max((np.abs(g - r) - bound) / den))

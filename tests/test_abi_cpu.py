@@ -89,6 +89,10 @@ def test_gemm_validation(lib):
     assert f(A, None, A, None, A, None, 0, 1, -64, 256, 768, None) == INVALID
     assert f(A, None, MIS, None, A, None, 0, 1, 64, 256, 768, None) == UNSUPPORTED
     assert f(A, None, A, None, A, None, 0, 1, 1 << 20, 4096, 768, None) == UNSUPPORTED  # > 4 GiB operand
+    E, S2 = 0x90000, 0xA0000
+    assert f(A, E, A, E, A, S2, 1, 1, 64, 256, 768, None) == INVALID           # abs-max aliases x_scale
+    assert f(A, S2, A, E, A, S2, 1, 1, 64, 256, 768, None) == INVALID          # abs-max aliases w_scale
+    assert "alias" in _err(lib)
     g = lib.ffn_gateup_swiglu_quant   # q, q_scale, h_absmax, h_absmax_known, x, xs, w, ws, dtype, N, C, H
     B, C_, D = 0x20000, 0x30000, 0x40000
     assert g(A, B, C_, None, A, None, A, None, 0, 64, 256, 768, None) == INVALID      # no known abs-max
@@ -100,6 +104,8 @@ def test_gemm_validation(lib):
     assert g(A, B, C_, D, A, None, A, None, 0, 64, 256, 100, None) == UNSUPPORTED     # H % 128
     assert g(MIS, B, C_, D, A, None, A, None, 0, 64, 256, 768, None) == UNSUPPORTED   # misaligned q
     assert g(A, None, C_, D, A, None, A, None, 0, 64, 256, 768, None) == INVALID      # no q_scale
+    assert g(A, B, C_, D, A, C_, A, 0x50000, 1, 64, 256, 768, None) == INVALID        # h_absmax aliases x_scale
+    assert g(A, B, C_, D, A, 0x50000, A, B, 1, 64, 256, 768, None) == INVALID         # q_scale aliases w_scale
     d = lib.ffn_down
     assert d(A, A, None, A, None, 1, 64, 768, 256, None) == INVALID
     assert d(A, A, None, A, None, 0, 64, 700, 256, None) == UNSUPPORTED
@@ -135,8 +141,19 @@ def test_decode_packed_validation(lib):
     assert p(None, B, 32, 256, None) == INVALID
     assert p(A, MIS, 32, 256, None) == UNSUPPORTED
     ws = lib.ffn_decode_packed_workspace_bytes
-    assert ws(16, 3584, 18944) == 32 * (3584 + 18944)
-    assert ws(17, 3584, 18944) == 64 * (3584 + 18944) and ws(1, 256, 256) == 32 * 512
+
+    def slices(C, H):   # the header's rule for the down pass's K slices
+        n = H // 64
+        return max(1, min(n, max(256 // (C // 128), -(-n // 64))))
+
+    def one_block(C, H):   # x and h in fragment order + fp32 partial sums
+        return 32 * (C + H) + 64 * slices(C, H) * C
+
+    assert slices(3584, 18944) == 9 and slices(4096, 14336) == 8 and slices(128, 128) == 2
+    assert ws(16, 3584, 18944) == one_block(3584, 18944) and ws(1, 256, 256) == one_block(256, 256)
+    assert ws(17, 3584, 18944) == max(64 * (3584 + 18944), one_block(3584, 18944))
+    assert ws(32, 8192, 256) == max(64 * (8192 + 256), one_block(8192, 256))
+    assert all(ws(m, 1152, 4096) <= ws(m + 1, 1152, 4096) for m in range(32))   # never smaller for more tokens
     assert ws(33, 256, 256) == -1 and ws(-1, 256, 256) == -1
     g = lib.ffn_decode_gemv_packed   # out, h, ws, x, wg, sg, wu, su, wd, sd, M, C, H
     assert g(A, B, None, D, A, A, A, A, A, A, 16, 256, 768, None) == INVALID       # no workspace
@@ -145,6 +162,7 @@ def test_decode_packed_validation(lib):
     assert g(A, B, E, D, A, A, A, A, A, A, 16, 200, 768, None) == UNSUPPORTED      # C % 128
     assert g(A, B, MIS, D, A, A, A, A, A, A, 16, 256, 768, None) == UNSUPPORTED    # misaligned workspace
     assert g(A, B, E, D, A, None, A, A, A, A, 16, 256, 768, None) == INVALID       # no gate scales
+
 
 
 def test_decode_arm_and_bf16_validation(lib):
@@ -189,6 +207,8 @@ def test_backward_validation(lib):
     assert f(B_, None, B_, None, C_, None, D, 0, 0, 64, 256, 128, None) == INVALID        # dgu aliases a
     assert f(A, None, B_, None, C_, None, MIS, 0, 0, 64, 256, 128, None) == UNSUPPORTED   # misaligned gu
     assert f(A, None, B_, None, C_, None, D, 0, 0, -1, 256, 128, None) == INVALID
+    assert f(A, 0x80000, B_, 0x80000, C_, 0x90000, D, 1, 0, 64, 256, 128, None) == INVALID  # absmax aliases a_scale
+    assert f(A, 0x90000, B_, 0x80000, C_, 0x90000, D, 1, 0, 64, 256, 128, None) == INVALID  # absmax aliases b_scale
     t = lib.ffn_transpose  # out, in, rows, cols, ld_out, elt
     assert t(A, B_, 37, 64, 48, 3, None) == INVALID                                # element size
     assert t(A, B_, 37, 64, 32, 2, None) == INVALID                                # ld_out < rows
@@ -203,6 +223,8 @@ def test_backward_validation(lib):
     assert q(A, MIS, B_, C_, D, 1, 37, 64, 48, None) == UNSUPPORTED                # misaligned q
     assert q(A, None, B_, C_, D, 0, 37, 64, 48, None) == INVALID                   # bf16 is no code format
     assert q(A, None, B_, C_, D, 3, 37, 64, 48, None) == INVALID                   # unknown code format
+    assert q(A, None, D, C_, D, 1, 37, 64, 48, None) == INVALID                    # scale aliases absmax
+    assert "scale and absmax alias" in _err(lib)
     g = lib.ffn_swiglu_bwd  # dgu, absmax, dh, gu, N, H
     assert g(A, None, A, C_, 4, 64, None) == INVALID                               # dgu aliases dh
     assert g(A, None, B_, C_, 4, 60, None) == UNSUPPORTED                          # H % 8

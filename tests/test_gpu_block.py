@@ -1,10 +1,18 @@
 """GPU parity of the whole FFN block and of the decode FFN against the oracle.
 
 Small workloads are compared element by element end to end.  The full-size
-workloads are compared on sampled rows, stage by stage, each stage fed the
-GPU's own upstream outputs (codes and scales given the same input are unique,
-so they are compared bit for bit), plus an end-to-end check of the sampled rows
-through the whole oracle chain conditioned on the GPU's per-tensor abs-maxes.
+workloads are compared on every row of every output, stage by stage (each
+stage fed the GPU's own upstream outputs: codes and scales given the same
+input are unique, so they are compared bit for bit), and end to end against
+the oracle's own chain.
+
+The FP8 end-to-end measure: the GPU's chain and the oracle's chain take their
+quantisation decisions separately, and a code that the two round to
+neighbouring grid points moves every output that reads it by
+|dequantised difference| x |weight|.  That movement is computed exactly from
+the codes that differ (flip_bound) and allowed on top of the per-element
+tolerance (max relative error 3e-2 with an RMS floor); the number of differing
+codes is reported and must stay a small fraction.
 """
 
 import numpy as np
@@ -15,19 +23,16 @@ import oracle as O
 from oracle import codecs as K
 from transformer_ffn_block_residual_amd import workloads as W
 from tests.gpu_util import (say, dev_bf16, dev_u8, dev_f32, host_bits, host_u8, host_f32, empty_bf16, empty_f32,
-                            empty_u8, rel_err, ulp_diff, normwise_err)
+                            empty_u8, rel_err, ulp_diff, flip_bound, rel_err_with_bound)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
 TOL_BF16, TOL_FP8 = 2e-2, 3e-2
-
-
-def e2e_err(got, ref, fp8):
-    """bf16 path: elementwise relative error (RMS floor).  FP8 path, when the
-    oracle takes its own quantisation decisions: error against the tensor's
-    abs-max, the scale of the per-tensor e4m3 grid (a code that flips between
-    the two chains moves an element by a grid step, not by a fraction of it)."""
-    return normwise_err(got, ref) if fp8 else rel_err(got, ref)
+# Codes the two chains round to different grid points: an input that moves by
+# one bf16 ulp (2^-8 relative; summation order, hardware exp) crosses an e4m3
+# rounding boundary (grid 2^-4 relative) about 1/16 of the time, and a few
+# percent of the GEMM outputs move by an ulp, so well under 1% of the codes.
+MAX_FLIP_FRAC = 1e-2
 
 
 @pytest.fixture(scope="module")
@@ -50,33 +55,102 @@ def _run_block(blk, d, N, C, H, eps, fp8):
     return b, nxt_r
 
 
+def _deq(q, s):
+    return K.e4m3_decode(q) * np.float64(s)
+
+
+# Each chain's GEMM is within 2^-14 sum_k |a_k b_k| of the exact sum before
+# its bf16 rounding (the bound the GEMM tests check), so two chains can differ
+# by twice that where an output cancels.
+REL_ACC = 2.0 * 2.0 ** -14
+
+
+def swiglu_bound(dx_got, dx_ref, w_gu_abs, gu_ref_bits, mag=None):
+    """How far h = bf16(silu(g) u) can move between two chains whose GEMM
+    inputs differ by dx_got - dx_ref, and (mag: sum |x| |w| of each g and u,
+    [N, 2H]) whose fp32 accumulations differ by up to REL_ACC mag: g and u move
+    by at most Bg, Bu; |silu'| <= 1.1, so h moves by at most
+    1.1 Bg (|u| + Bu) + |silu(g)| Bu."""
+    H = gu_ref_bits.shape[1] // 2
+    Bg, Bu = flip_bound(dx_got, dx_ref, w_gu_abs[:H]), flip_bound(dx_got, dx_ref, w_gu_abs[H:])
+    if mag is not None:
+        Bg += REL_ACC * mag[:, :H]
+        Bu += REL_ACC * mag[:, H:]
+    gu = K.bf16_bits_to_f64(gu_ref_bits)
+    return 1.1 * Bg * (np.abs(gu[:, H:]) + Bu) + np.abs(O.silu(gu[:, :H])) * Bu
+
+
+def check_bf16_end_to_end(tag, y, h, out, ref, w_gu_bits, mag):
+    """The GPU's bf16 chain against the oracle's own chain: the two RMSNorm
+    outputs differ where the rstds (fp32 sums in different orders) put an
+    element on either side of a bf16 rounding boundary; h may move by what
+    those differences and the two chains' accumulation orders propagate to
+    (swiglu_bound), on top of the per-element tolerance."""
+    yd = K.bf16_bits_to_f64(y) != K.bf16_bits_to_f64(ref["y"])
+    say(f"{tag}: RMSNorm outputs one ulp apart between the chains: {int(np.count_nonzero(yd))} of {y.size}")
+    bound_h = swiglu_bound(K.bf16_bits_to_f64(y), K.bf16_bits_to_f64(ref["y"]),
+                           np.abs(K.bf16_bits_to_f64(w_gu_bits)), ref["gu"], mag)
+    assert rel_err_with_bound(h, ref["h"], bound_h * (1 + 2 ** -6)) < TOL_BF16
+    assert rel_err(out, ref["down"]) < TOL_BF16
+
+
+def check_fp8_end_to_end(tag, g, ref):
+    """The GPU's FP8 chain against the oracle's own chain.  g: host copies of
+    the GPU's qy, s_y, h, qh, s_h, out (and next_residual, optional); ref: the
+    oracle's chain with qw_gu, s_gu, qw_d, s_d, qy, s_y, gu, h, qh, s_h, down
+    (and next_residual).  Returns the numbers of differing y and h codes."""
+    ny = int(np.count_nonzero(g["qy"] != ref["qy"]))
+    nh = int(np.count_nonzero(g["qh"] != ref["qh"]))
+    say(f"{tag}: codes rounded differently by the two chains: y {ny} of {g['qy'].size}, "
+        f"h {nh} of {g['qh'].size}")
+    assert ny <= MAX_FLIP_FRAC * g["qy"].size and nh <= MAX_FLIP_FRAC * g["qh"].size
+    bound_h = swiglu_bound(_deq(g["qy"], g["s_y"]), _deq(ref["qy"], ref["s_y"]),
+                           np.abs(_deq(ref["qw_gu"], ref["s_gu"])), ref["gu"])
+    assert rel_err_with_bound(g["h"], ref["h"], bound_h * (1 + 2 ** -6)) < TOL_FP8
+    bound_d = flip_bound(_deq(g["qh"], g["s_h"]), _deq(ref["qh"], ref["s_h"]), np.abs(_deq(ref["qw_d"], ref["s_d"])))
+    assert rel_err_with_bound(g["out"], ref["down"], bound_d * (1 + 2 ** -6)) < TOL_FP8
+    if "next_residual" in g:
+        assert rel_err_with_bound(g["next_residual"], ref["next_residual"], bound_d * (1 + 2 ** -6)) < TOL_FP8
+    return ny, nh
+
+
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("N,C,H,outl", [(64, 256, 768, False), (300, 512, 384, True), (1, 128, 128, False)])
+@pytest.mark.parametrize("N,C,H,outl", [(64, 256, 768, False), (300, 512, 384, True), (1, 128, 128, False),
+                                        (513, 1024, 1536, True)])
 def test_block_end_to_end_small(blk, fp8, N, C, H, outl):
     say(f"block e2e fp8={fp8} N={N} C={C} H={H}")
     d = W.block_inputs(N, C, H, seed=1001 if N == 64 else N + C, w_std=0.0, outliers=outl)
     b, nxt_r = _run_block(blk, d, N, C, H, 1e-5, fp8)
     ref = O.block_forward(d["inp"], d["addend"], d["w_norm"], d["w_gu"], d["w_d"], 1e-5, fp8=fp8)
-    tol = TOL_FP8 if fp8 else TOL_BF16
     assert np.array_equal(host_bits(b.r), ref["residual"])
-    assert rel_err(host_bits(b.y), ref["y"]) < TOL_BF16
-    assert e2e_err(host_bits(b.h), ref["h"], fp8) < tol
-    assert e2e_err(host_bits(b.out), ref["down"], fp8) < tol
-    assert e2e_err(host_bits(nxt_r), ref["next_residual"], fp8) < tol
-    if fp8:
-        # weights quantised on the GPU are the oracle's codes exactly
-        assert np.array_equal(host_u8(b.w_gu), ref["qw_gu"]) and host_f32(b.s_gu)[0] == ref["s_gu"]
-        assert np.array_equal(host_u8(b.w_d), ref["qw_d"]) and host_f32(b.s_d)[0] == ref["s_d"]
-        # activations: codes given the GPU's own y / h and abs-max are unique
-        qy, sy, _ = O.quant_absmax(host_bits(b.y), host_f32(b.am_y)[0])
-        assert np.array_equal(host_u8(b.qy), qy) and host_f32(b.s_y)[0] == sy
-        qh, sh, _ = O.quant_absmax(host_bits(b.h), host_f32(b.am_h)[0])
-        assert np.array_equal(host_u8(b.qh), qh) and host_f32(b.s_h)[0] == sh
-        # each stage fed the GPU's own upstream tensors: elementwise tolerance
-        h_c, _ = O.swiglu(O.gemm_fp8(host_u8(b.qy), host_f32(b.s_y)[0], ref["qw_gu"], ref["s_gu"]))
-        assert rel_err(host_bits(b.h), h_c) < TOL_FP8
-        d_c = O.gemm_fp8(host_u8(b.qh), host_f32(b.s_h)[0], ref["qw_d"], ref["s_d"])
-        assert rel_err(host_bits(b.out), d_c) < TOL_FP8
+    gy = host_bits(b.y)
+    # y given the GPU's own rstd: both take the two products in fp32
+    y_cond, _ = O.rms_apply(ref["residual"], host_f32(b.rstd), d["w_norm"])
+    assert np.array_equal(gy, y_cond)
+    assert rel_err(gy, ref["y"]) < TOL_BF16
+    if not fp8:
+        yv, wv = K.bf16_bits_to_f64(ref["y"]), K.bf16_bits_to_f64(d["w_gu"])
+        check_bf16_end_to_end(f"N={N} C={C} H={H}", gy, host_bits(b.h), host_bits(b.out), ref, d["w_gu"],
+                              np.abs(yv) @ np.abs(wv).T)
+        assert rel_err(host_bits(nxt_r), ref["next_residual"]) < TOL_BF16
+        return
+    # weights quantised on the GPU are the oracle's codes exactly
+    assert np.array_equal(host_u8(b.w_gu), ref["qw_gu"]) and host_f32(b.s_gu)[0] == ref["s_gu"]
+    assert np.array_equal(host_u8(b.w_d), ref["qw_d"]) and host_f32(b.s_d)[0] == ref["s_d"]
+    # activations: codes given the GPU's own y / h and abs-max are unique
+    qy, sy, _ = O.quant_absmax(gy, host_f32(b.am_y)[0])
+    assert np.array_equal(host_u8(b.qy), qy) and host_f32(b.s_y)[0] == sy
+    qh, sh, _ = O.quant_absmax(host_bits(b.h), host_f32(b.am_h)[0])
+    assert np.array_equal(host_u8(b.qh), qh) and host_f32(b.s_h)[0] == sh
+    # each stage fed the GPU's own upstream tensors: elementwise tolerance
+    h_c, _ = O.swiglu(O.gemm_fp8(host_u8(b.qy), host_f32(b.s_y)[0], ref["qw_gu"], ref["s_gu"]))
+    assert rel_err(host_bits(b.h), h_c) < TOL_FP8
+    d_c = O.gemm_fp8(host_u8(b.qh), host_f32(b.s_h)[0], ref["qw_d"], ref["s_d"])
+    assert rel_err(host_bits(b.out), d_c) < TOL_FP8
+    # end to end against the oracle's own chain
+    g = dict(qy=host_u8(b.qy), s_y=host_f32(b.s_y)[0], h=host_bits(b.h), qh=host_u8(b.qh), s_h=host_f32(b.s_h)[0],
+             out=host_bits(b.out), next_residual=host_bits(nxt_r))
+    check_fp8_end_to_end(f"N={N} C={C} H={H}", g, ref)
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -135,15 +209,15 @@ def test_block_deterministic(blk):
     assert torch.equal(o1, o2)
 
 
-def _sample_rows(N):
-    rows = {0, 1, 255, 256, 257, N // 2, N - 257, N - 256, N - 2, N - 1}
-    rows |= set(np.random.default_rng(N).integers(0, N, 22).tolist())
-    return np.array(sorted(r for r in rows if 0 <= r < N))
-
-
-@pytest.mark.timeout(400)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["prefill", "prefill8", "qwen7b8"])
-def test_block_full_size_sampled(blk, name):
+def test_block_full_size_whole_outputs(blk, name):
+    """Every row of every output of the full-size block against the C++
+    oracle (fp32, fixed summation order, all host cores): stage by stage on
+    the GPU's own upstream tensors, then end to end against the oracle's own
+    chain, which is conditioned only on the two per-tensor abs-maxes (global
+    reductions over all rows; the GPU's abs-maxes are checked exact)."""
+    from oracle import cpp as P
     w = W.WORKLOADS[name]
     N, C, H = w.N, w.C, w.H
     say(f"full-size block {name} N={N} C={C} H={H} fp8={w.fp8}")
@@ -152,56 +226,51 @@ def test_block_full_size_sampled(blk, name):
     b.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
     b.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
     torch.cuda.synchronize()
-    say(f"full-size block {name}: GPU done, checking on the CPU")
-    rows = _sample_rows(N)
-    # A1: every row (cheap)
-    r_ref, y_ref, rstd_ref, am_y_ref = O.rmsnorm_fwd(d["inp"], d["addend"], d["w_norm"], w.eps)
-    gy = host_bits(b.y)
-    assert np.array_equal(host_bits(b.r), r_ref)
+    say(f"full-size block {name}: GPU done, checking every row on the CPU ({P.threads()} threads)")
+    gr, gy, g_rstd = host_bits(b.r), host_bits(b.y), host_f32(b.rstd)
+    gh, gout = host_bits(b.h), host_bits(b.out)
+    am_y, am_h = host_f32(b.am_y)[0], host_f32(b.am_h)[0]
+    r_ref, y_ref, rstd_ref, _ = P.rmsnorm_fwd(d["inp"], d["addend"], d["w_norm"], w.eps)
+    assert np.array_equal(gr, r_ref)
+    assert np.max(np.abs(g_rstd / rstd_ref - 1)) < 1e-5
+    y_cond, _ = O.rms_apply(r_ref, g_rstd, d["w_norm"])
+    assert np.array_equal(gy, y_cond)                                  # y given the GPU's rstd
     assert rel_err(gy, y_ref) < TOL_BF16
-    assert np.max(np.abs(host_f32(b.rstd) / rstd_ref - 1)) < 1e-5
-    am_y = host_f32(b.am_y)[0]
-    assert am_y == np.max(np.abs(K.bf16_bits_to_f64(gy)))
-    gh = host_bits(b.h)
-    am_h = host_f32(b.am_h)[0]
-    assert am_h == np.max(np.abs(K.bf16_bits_to_f64(gh)))
-    w_gu, w_d = d["w_gu"], d["w_d"]
-    if w.fp8:
-        say(f"{name}: oracle weight quantisation")
-        qw_gu, s_gu, _ = O.quant_absmax(w_gu)
-        qw_d, s_d, _ = O.quant_absmax(w_d)
-        say(f"{name}: stage checks")
-        assert np.array_equal(host_u8(b.w_gu), qw_gu) and host_f32(b.s_gu)[0] == s_gu
-        assert np.array_equal(host_u8(b.w_d), qw_d) and host_f32(b.s_d)[0] == s_d
-        # A3: codes of the sampled rows given the GPU's y and abs-max
-        qy_all = host_u8(b.qy)
-        qy_ref, sy, _ = O.quant_absmax(gy[rows], am_y)
-        assert np.array_equal(qy_all[rows], qy_ref) and host_f32(b.s_y)[0] == sy
-        # A4+A5 on the sampled rows, from the GPU's codes
-        h_cond, _ = O.swiglu(O.gemm_fp8(qy_all[rows], sy, qw_gu, s_gu))
-        assert rel_err(gh[rows], h_cond) < TOL_FP8
-        # A6
-        qh_all = host_u8(b.qh)
-        qh_ref, sh, _ = O.quant_absmax(gh[rows], am_h)
-        assert np.array_equal(qh_all[rows], qh_ref) and host_f32(b.s_h)[0] == sh
-        # A7 from the GPU's codes
-        d_cond = O.gemm_fp8(qh_all[rows], sh, qw_d, s_d)
-        assert rel_err(host_bits(b.out)[rows], d_cond) < TOL_FP8
-        # end to end on the sampled rows, oracle all the way, conditioned only
-        # on the per-tensor abs-maxes (global reductions over every row)
-        qy_o, sy_o, _ = O.quant_absmax(y_ref[rows], am_y_ref)
-        h_o, _ = O.swiglu(O.gemm_fp8(qy_o, sy_o, qw_gu, s_gu))
-        qh_o, sh_o, _ = O.quant_absmax(h_o, am_h)
-        d_o = O.gemm_fp8(qh_o, sh_o, qw_d, s_d)
-        assert normwise_err(host_bits(b.out)[rows], d_o) < TOL_FP8
-    else:
-        h_cond, _ = O.swiglu(O.gemm_bf16(gy[rows], w_gu))
-        assert rel_err(gh[rows], h_cond) < TOL_BF16
-        d_cond = O.gemm_bf16(gh[rows], w_d)
-        assert rel_err(host_bits(b.out)[rows], d_cond) < TOL_BF16
-        h_o, _ = O.swiglu(O.gemm_bf16(y_ref[rows], w_gu))
-        d_o = O.gemm_bf16(h_o, w_d)
-        assert rel_err(host_bits(b.out)[rows], d_o) < TOL_BF16
+    assert am_y == P.absmax_of(gy) and am_h == P.absmax_of(gh)         # abs-max of what was stored
+    if not w.fp8:
+        say(f"{name}: stages")
+        h_c, _ = P.swiglu(P.gemm_bf16(gy, d["w_gu"]))
+        assert rel_err(gh, h_c) < TOL_BF16
+        assert rel_err(gout, P.gemm_bf16(gh, d["w_d"])) < TOL_BF16
+        say(f"{name}: end to end")
+        gu_o = P.gemm_bf16(y_ref, d["w_gu"])
+        h_o, _ = P.swiglu(gu_o)
+        check_bf16_end_to_end(name, gy, gh, gout, dict(y=y_ref, gu=gu_o, h=h_o, down=P.gemm_bf16(h_o, d["w_d"])),
+                              d["w_gu"], P.gemm_abs_bf16(y_ref, d["w_gu"]))
+        return
+    say(f"{name}: weights and stages")
+    qw_gu, s_gu, _ = P.quant_absmax(d["w_gu"])
+    qw_d, s_d, _ = P.quant_absmax(d["w_d"])
+    assert np.array_equal(host_u8(b.w_gu), qw_gu) and host_f32(b.s_gu)[0] == s_gu
+    assert np.array_equal(host_u8(b.w_d), qw_d) and host_f32(b.s_d)[0] == s_d
+    gqy, gqh = host_u8(b.qy), host_u8(b.qh)
+    qy_c, sy, _ = P.quant_absmax(gy, am_y)
+    assert np.array_equal(gqy, qy_c) and host_f32(b.s_y)[0] == sy
+    h_c, _ = P.swiglu(P.gemm_fp8(gqy, sy, qw_gu, s_gu))
+    assert rel_err(gh, h_c) < TOL_FP8
+    qh_c, sh, _ = P.quant_absmax(gh, am_h)
+    assert np.array_equal(gqh, qh_c) and host_f32(b.s_h)[0] == sh
+    assert rel_err(gout, P.gemm_fp8(gqh, sh, qw_d, s_d)) < TOL_FP8
+    say(f"{name}: end to end")
+    qy_o, sy_o, _ = P.quant_absmax(y_ref, am_y)
+    gu_o = P.gemm_fp8(qy_o, sy_o, qw_gu, s_gu)
+    h_o, _ = P.swiglu(gu_o)
+    qh_o, sh_o, _ = P.quant_absmax(h_o, am_h)
+    d_o = P.gemm_fp8(qh_o, sh_o, qw_d, s_d)
+    ref = dict(qw_gu=qw_gu, s_gu=s_gu, qw_d=qw_d, s_d=s_d, qy=qy_o, s_y=sy_o, gu=gu_o, h=h_o, qh=qh_o, s_h=sh_o,
+               down=d_o)
+    g = dict(qy=gqy, s_y=sy, h=gh, qh=gqh, s_h=sh, out=gout)
+    check_fp8_end_to_end(name, g, ref)
 
 
 @pytest.mark.timeout(300)
@@ -239,19 +308,20 @@ def test_decode_batch16_with_prefill_weights(blk):
     x = W.decode_inputs(M, C, H, w.seed, with_weights=False)["x"]
     b = blk.PrefillBlock(8, C, H, w.eps, True)
     b.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    db = blk.DecodeBlock(M, C, H)
     sg = b.s_gu.expand(H).contiguous()
     sdn = b.s_d.expand(C).contiguous()
-    db.set_fp8_weights(b.w_gu[:H], sg, b.w_gu[H:], sg, b.w_d, sdn)
-    db.forward(dev_bf16(x))
-    torch.cuda.synchronize()
-    say("decode M=16: GPU done, checking on the CPU")
     qw_gu, s_gu, _ = O.quant_absmax(d["w_gu"])
     qw_d, s_d, _ = O.quant_absmax(d["w_d"])
     sgv = np.full(H, s_gu, np.float32)
     sdv = np.full(C, s_d, np.float32)
     y_ref, h_ref = O.decode_gemv(x, qw_gu[:H], sgv, qw_gu[H:], sgv, qw_d, sdv)
-    gh, gy = host_bits(db.h)[:M], host_bits(db.out)[:M]
-    assert rel_err(gh, h_ref) < TOL_BF16
-    assert rel_err(gy, O.decode_down(gh, qw_d, sdv)) < TOL_BF16
-    assert rel_err(gy, y_ref) < TOL_FP8
+    for packed in (False, True):
+        db = (blk.DecodeBlockPacked if packed else blk.DecodeBlock)(M, C, H)
+        db.set_fp8_weights(b.w_gu[:H], sg, b.w_gu[H:], sg, b.w_d, sdn)
+        db.forward(dev_bf16(x))
+        torch.cuda.synchronize()
+        say(f"decode M=16 packed={packed}: GPU done, checking on the CPU")
+        gh, gy = host_bits(db.h)[:M], host_bits(db.out)[:M]
+        assert rel_err(gh, h_ref) < TOL_BF16
+        assert rel_err(gy, O.decode_down(gh, qw_d, sdv)) < TOL_BF16
+        assert rel_err(gy, y_ref) < TOL_FP8

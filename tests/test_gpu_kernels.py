@@ -54,11 +54,10 @@ def test_rmsnorm(F, N, C, add):
     g_rstd = host_f32(rstd)
     assert np.max(np.abs(g_rstd / rstd_ref - 1)) < 1e-5
     gy = host_bits(y)
-    # y given the GPU's own rstd: the oracle's single rounding vs the kernel's
-    # two fp32 roundings can differ by one bf16 ulp, rarely
+    # y given the GPU's own rstd: both take (r * rstd) * w as two fp32
+    # products and round once to bf16, so y is unique
     y_cond, _ = O.rms_apply(r_ref if add else inp, g_rstd, w)
-    assert ulp_diff(gy, y_cond).max() <= 1
-    assert np.mean(ulp_diff(gy, y_cond) != 0) < 1e-3
+    assert np.array_equal(gy, y_cond)
     assert rel_err(gy, y_ref) < 2e-2
     assert host_f32(am)[0] == np.max(np.abs(K.bf16_bits_to_f64(gy)))  # abs-max of what was stored
 
@@ -114,12 +113,21 @@ def test_quant_absmax_bit_exact(F, n, outl):
     assert np.array_equal(host_u8(q), q_ref)
 
 
+def _same_codes(got, want, fmt):
+    """Codes equal bit for bit, except that a NaN input may come out as any NaN
+    code of the format (the sign of a NaN is not specified)."""
+    if fmt == "e4m3":
+        nan_w, nan_g = (want & 0x7F) == 0x7F, (got & 0x7F) == 0x7F
+    else:
+        nan_w, nan_g = (want & 0x7F) > 0x7C, (got & 0x7F) > 0x7C
+    return np.array_equal(nan_w, nan_g) and np.array_equal(got[~nan_w], want[~nan_w])
+
+
 def test_quant_every_bf16_pattern_bit_exact(F):
-    # every finite bf16 value, quantised against several given abs-maxes
+    # all 65536 bf16 patterns (NaN and +-inf included), quantised against
+    # several given abs-maxes: a NaN stays NaN, +-inf saturates to +-448
     say("quant exhaustive bf16 patterns")
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    v = K.bf16_bits_to_f64(bits)
-    bits = bits[np.isfinite(v)]
     n = bits.size
     x = dev_bf16(bits)
     for am_v in [1.0, 3.5, 448.0, 1e-3, 2.0 ** -100, 3.0e38, 0.0]:
@@ -128,7 +136,58 @@ def test_quant_every_bf16_pattern_bit_exact(F):
         torch.cuda.synchronize()
         q_ref, s_ref, _ = O.quant_absmax(bits, np.float32(am_v))
         assert host_f32(scale)[0] == s_ref, am_v
-        assert np.array_equal(host_u8(q), q_ref), am_v
+        assert _same_codes(host_u8(q), q_ref, "e4m3"), am_v
+
+
+def test_quant_transpose_every_bf16_pattern_e5m2(F):
+    # the e5m2 gradient codes of all 65536 bf16 patterns (NaN and +-inf
+    # included), through the quantising transpose, against the oracle
+    say("quant transpose e5m2 exhaustive bf16 patterns")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    x = dev_bf16(bits)
+    for am_v in [1.0, 57344.0, 3.0e38, 2.0 ** -20]:
+        qt, q, sc = empty_u8(256, 256), empty_u8(256, 256), empty_f32(1)
+        F.ffn_quant_transpose(qt, q, sc, x, dev_f32([am_v]), 256, 256, 256, code_dtype=F.FFN_E5M2)
+        torch.cuda.synchronize()
+        q_ref, s_ref, _ = O.quant_absmax(bits, np.float32(am_v), fmt="e5m2")
+        assert host_f32(sc)[0] == s_ref, am_v
+        assert _same_codes(host_u8(q), q_ref, "e5m2"), am_v
+        assert _same_codes(host_u8(qt), q_ref.T, "e5m2"), am_v
+
+
+def test_absmax_propagates_nan_and_inf(F):
+    # max |x| is the unsigned maximum of the bit patterns of |x|: a NaN anywhere
+    # makes the abs-max NaN, so the scale and every code are NaN; an infinity
+    # gives an infinite abs-max, scale inf and inverse 0 (codes 0, the infinite
+    # element NaN).  The same in the RMSNorm and SwiGLU producers.
+    say("abs-max with NaN and inf")
+    n = 4096 + 37
+    base = W.normal_bf16((n,), 1.0, 5, 1)
+    for bad, where in ((0x7FC1, 1234), (0xFFC0, 4100), (0x7F80, 99), (0xFF80, 7)):
+        b = base.copy()
+        b[where] = bad
+        q, sc, am = empty_u8(n), empty_f32(1), empty_f32(1)
+        F.ffn_quant_absmax(q, sc, am, dev_bf16(b), n, 1)
+        torch.cuda.synchronize()
+        q_ref, s_ref, am_ref = O.quant_absmax(b)
+        g_am = host_f32(am)[0]
+        assert (np.isnan(g_am) and np.isnan(am_ref)) or g_am == am_ref, hex(bad)
+        assert (np.isnan(host_f32(sc)[0]) and np.isnan(s_ref)) or host_f32(sc)[0] == s_ref, hex(bad)
+        assert _same_codes(host_u8(q), q_ref, "e4m3"), hex(bad)
+    # producers: a NaN in one row of the RMSNorm input, and in the SwiGLU input
+    N, C = 6, 512
+    inp = W.normal_bf16((N, C), 1.0, 6, 1)
+    inp[3, 17] = 0x7FC0
+    y, rstd, am = empty_bf16(N, C), empty_f32(N), empty_f32(1)
+    F.ffn_rmsnorm_fwd(y, rstd, None, am, dev_bf16(inp), None, dev_bf16(W.uniform_bf16((C,), 0.5, 1.5, 6, 3)),
+                      1e-5, N, C)
+    gu = W.normal_bf16((N, 2 * C), 1.0, 6, 2)
+    gu[2, 5] = 0x7FC0
+    h, amh = empty_bf16(N, C), empty_f32(1)
+    F.ffn_swiglu(h, amh, dev_bf16(gu), N, C)
+    torch.cuda.synchronize()
+    assert np.isnan(host_f32(am)[0]) and np.isnan(host_f32(amh)[0])
+    assert np.isnan(host_f32(rstd)[3]) and np.all(np.isfinite(host_f32(rstd)[[0, 1, 2, 4, 5]]))
 
 
 @pytest.mark.parametrize("rows,cols", [(300, 1024), (64, 4104), (1, 8)])
@@ -197,6 +256,55 @@ def test_gateup_fp8_integer_inputs_bit_exact(F, N, C, H):
     F.ffn_gateup(out, None, dev_u8(qx), one, dev_u8(qw), one, F.FFN_E4M3, 0, N, C, H)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), O.gemm_fp8(qx, np.float32(1), qw, np.float32(1)))
+
+
+@pytest.mark.parametrize("N,Kd,O", [(257, 4096, 512), (64, 3584, 768)])
+def test_same_e4m3_operands_through_both_mfma_paths(F, N, Kd, O):
+    """The GEMM bound used for FP8 products: the same e4m3 operands, once as
+    bf16 values through the bf16 MFMA path and once as codes through the
+    f8f6f4 MFMA path (unit scales), against the exact sum.  (a) Operands whose
+    every partial sum is exact in fp32 (values (1 + m/8) 2^e, e in {-1, 0}:
+    products are multiples of 2^-8 below 4, sums below 2^14 for K <= 4096):
+    the bf16 path gives the exact sum's one bf16 rounding bit for bit.
+    (b) Codes of N(0, 1) data (full exponent range): the bf16 path is the
+    exact sum rounded once except where fp32 accumulation lands near a bf16
+    rounding boundary; the f8f6f4 path stays within
+    2^-8 |exact| + 2^-14 sum |a b| everywhere, and differs from the bf16 path
+    on a small fraction of outputs."""
+    say(f"e4m3 operands through bf16 and f8f6f4 MFMA N={N} K={Kd} O={O}")
+    rng = np.random.default_rng(N + Kd + O)
+    one = dev_f32([1.0])
+
+    def run(qx, qw):
+        xb = W.to_bf16_bits(K.e4m3_decode(qx).astype(np.float32))   # exact: e4m3 values are bf16 values
+        wb = W.to_bf16_bits(K.e4m3_decode(qw).astype(np.float32))
+        o_b, o_8 = empty_bf16(N, O), empty_bf16(N, O)
+        F.ffn_gateup(o_b, None, dev_bf16(xb), None, dev_bf16(wb), None, F.FFN_BF16, 0, N, Kd, O // 2)
+        F.ffn_gateup(o_8, None, dev_u8(qx), one, dev_u8(qw), one, F.FFN_E4M3, 0, N, Kd, O // 2)
+        torch.cuda.synchronize()
+        exact, mag = _exact_and_mag(K.e4m3_decode(qx), K.e4m3_decode(qw))
+        return host_bits(o_b), host_bits(o_8), exact, mag
+
+    def narrow(shape):   # sign, e in {-1, 0}, m in 0..7, or zero
+        e = rng.integers(6, 8, shape)
+        m = rng.integers(0, 8, shape)
+        code = (e << 3) | m
+        code = np.where(rng.random(shape) < 0.1, 0, code) | (rng.integers(0, 2, shape) << 7)
+        return code.astype(np.uint8)
+    gb, g8, exact, mag = run(narrow((N, Kd)), narrow((O, Kd)))
+    ref = K.f64_to_bf16_bits(exact)
+    assert np.array_equal(gb, ref)
+    assert np.all(within_dot_bound(g8, exact, mag))
+    qx = K.e4m3_encode(rng.standard_normal((N, Kd)).astype(np.float32) * 8)
+    qw = K.e4m3_encode(rng.standard_normal((O, Kd)).astype(np.float32) * 8)
+    gb, g8, exact, mag = run(qx, qw)
+    ref = K.f64_to_bf16_bits(exact)
+    assert np.mean(gb != ref) < 1e-3 and ulp_diff(gb, ref).max() <= 1
+    assert np.all(within_dot_bound(gb, exact, mag))
+    assert np.all(within_dot_bound(g8, exact, mag))
+    frac = float(np.mean(g8 != gb))
+    say(f"f8f6f4 path differs from the bf16 path on {frac:.2%} of outputs")
+    assert frac < 0.05
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -459,13 +567,15 @@ def test_decode_pack_weight_layout(F, rows, cols):
     assert np.array_equal(host_u8(out).reshape(rows, cols), want)
 
 
-# Up to 16 tokens, C <= 4096 and row blocks (H / 16) that fill their rounds
-# on the 256 CUs to 90% or more, the dual pass keeps the activations in LDS:
-# here H = 4096, 8192 and 18944 (a half last chunk at C = 1152 and 640; C =
-# 4096 fills the LDS copy).  The other shapes take the fragment-order copy in
-# the workspace (too few row blocks, C > 4096, more than 16 tokens).
+# Up to 16 tokens with C <= 4096 the dual pass keeps the activations in LDS
+# (a half last chunk at C = 1152 and 640; C = 4096 fills the LDS copy); above
+# C = 4096 it reads them from the fragment-order copy in the workspace.  Up to
+# 16 tokens the down pass is split along K over workgroups (slices of one
+# 64-code piece at H = 128 x 1 group of rows, up to 64 pieces) and reduced by
+# the last workgroup of each row group; 17 to 32 tokens take two token blocks.
 PACKED_SHAPES = [(1, 1152, 640), (5, 3584, 384), (16, 384, 896), (16, 3584, 18944), (3, 4224, 256), (17, 256, 640),
-                 (32, 256, 256), (1, 1152, 4096), (5, 4096, 4096), (16, 384, 8192), (13, 640, 4096)]
+                 (32, 256, 256), (1, 1152, 4096), (5, 4096, 4096), (16, 384, 8192), (13, 640, 4096),
+                 (16, 4096, 14336), (2, 128, 128), (9, 128, 8192), (16, 8192, 256)]
 
 
 @pytest.mark.parametrize("M,C,H", PACKED_SHAPES)
@@ -500,13 +610,14 @@ def test_decode_packed(F, M, C, H):
     assert rel_err(gy, y_ref) < 3e-2
 
 
-def test_decode_packed_lds_and_copy_forms_agree(F):
-    """The persistent LDS dual pass (16 tokens) and the workspace-copy form
-    (the same 16 tokens plus one, two token blocks) on the same rows: the
-    sums differ only in fp32 order, so h agrees to one bf16 ulp, nearly
-    everywhere exactly, and y within the down pass's rounding."""
-    C, H = 1152, 4096   # 256 row blocks: one full round on 256 CUs
-    say(f"decode packed LDS vs copy form C={C} H={H}")
+def test_decode_packed_one_and_two_token_blocks_agree(F):
+    """The 16-token form (activations in LDS, down pass split along K) and the
+    two-token-block form (the same 16 tokens plus one) on the same rows: the
+    sums differ only in fp32 order, so g and u can each land one bf16 ulp
+    apart and h = bf16(silu(g) u) up to two ulps, on a small fraction of the
+    elements; y agrees within the down pass's rounding."""
+    C, H = 1152, 4096
+    say(f"decode packed 16 vs 17 tokens C={C} H={H}")
     d = W.decode_inputs(17, C, H, seed=4242)
     wq, ws = _decode_weights(F, d)
     pk = {}
@@ -525,7 +636,7 @@ def test_decode_packed_lds_and_copy_forms_agree(F):
     torch.cuda.synchronize()
     h16, h17 = host_bits(res[16][1]), host_bits(res[17][1][:16])
     dh = ulp_diff(h16, h17)
-    assert dh.max() <= 1 and np.mean(dh != 0) < 1e-2
+    assert dh.max() <= 2 and np.mean(dh != 0) < 1e-2
     assert rel_err(host_bits(res[16][0]), host_bits(res[17][0][:16])) < 1e-2
 
 

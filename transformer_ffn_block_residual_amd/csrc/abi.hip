@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+
 #include "../../include/ffn.h"
 #include "launch.h"
 
@@ -139,6 +140,9 @@ ffn_status_t ffn_gateup(void* out, float* out_absmax, const void* x, const float
         REQUIRE(x_scale);
         REQUIRE(w_scale);
     }
+    // the abs-max is cleared before the scales are read: they must be other words
+    if (out_absmax && (out_absmax == x_scale || out_absmax == w_scale))
+        return fail(FFN_ERR_INVALID, "ffn_gateup: out_absmax must not alias x_scale or w_scale");
     const int elt = dtype == FFN_E4M3 ? 1 : 2;
     if (ffn_status_t st = check_gemm_dims("ffn_gateup", N, C, 2 * H, elt)) return st;
     if (H % 128 != 0) return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup: H = %lld must be a multiple of 128", (long long)H);
@@ -169,6 +173,8 @@ ffn_status_t ffn_gateup_swiglu_quant(uint8_t* q, float* q_scale, float* h_absmax
     }
     if (h_absmax_known == h_absmax || h_absmax_known == q_scale)
         return fail(FFN_ERR_INVALID, "ffn_gateup_swiglu_quant: h_absmax_known must not alias h_absmax or q_scale");
+    if ((h_absmax && (h_absmax == x_scale || h_absmax == w_scale)) || q_scale == x_scale || q_scale == w_scale)
+        return fail(FFN_ERR_INVALID, "ffn_gateup_swiglu_quant: h_absmax and q_scale must not alias x_scale or w_scale");
     const int elt = dtype == FFN_E4M3 ? 1 : 2;
     if (ffn_status_t st = check_gemm_dims("ffn_gateup_swiglu_quant", N, C, 2 * H, elt)) return st;
     if (H % 128 != 0)
@@ -379,6 +385,8 @@ ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a, c
     ALIGNED(b);
     ALIGNED(gu);
     if (dgu == a || dgu == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: dgu must not alias a or b");
+    if (absmax && (absmax == a_scale || absmax == b_scale))
+        return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: absmax must not alias a_scale or b_scale");
     return hip_status(ffn::launch_gemm(dgu, absmax, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)H, stream,
                                        nullptr, nullptr, false, dtype == FFN_E5M2, gu, (flags & FFN_TN_TILE_GRID) != 0),
                       "ffn_matmul_tn_swiglu_bwd");
@@ -423,6 +431,8 @@ ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const v
     ALIGNED(q);
     if (q && (q == q_t || (const void*)q == x))
         return fail(FFN_ERR_INVALID, "ffn_quant_transpose: q must not alias q_t or x");
+    // every block reads *absmax while the first one writes *scale
+    if ((const float*)scale == absmax) return fail(FFN_ERR_INVALID, "ffn_quant_transpose: scale and absmax alias");
     return hip_status(ffn::launch_transpose(q_t, q, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream,
                                             code_dtype == FFN_E5M2),
                       "ffn_quant_transpose");

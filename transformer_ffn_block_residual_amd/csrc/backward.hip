@@ -255,8 +255,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dgu, float* _
             }
             ogp[q] = pack_bf16x2(rg[0], rg[1]);
             oup[q] = pack_bf16x2(ru[0], ru[1]);
-            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(ogp[q])), __builtin_fabsf(bf16hi(ogp[q]))));
-            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(oup[q])), __builtin_fabsf(bf16hi(oup[q]))));
+            m = absmax_acc(absmax_acc(m, bf16lo(ogp[q])), bf16hi(ogp[q]));
+            m = absmax_acc(absmax_acc(m, bf16lo(oup[q])), bf16hi(oup[q]));
         }
         *reinterpret_cast<uint4*>(dgu + n * 2 * H + j) = og;
         *reinterpret_cast<uint4*>(dgu + n * 2 * H + H + j) = ou;
@@ -379,9 +379,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(uint16_t* dinp, float*
                     acc[i][2 * q + h] += ok ? yv * xh : 0.0f;
                 }
                 op[q] = pack_bf16x2(res[0], res[1]);
-                amax = __builtin_fmaxf(amax, ok ? __builtin_fmaxf(__builtin_fabsf(bf16lo(op[q])),
-                                                                  __builtin_fabsf(bf16hi(op[q])))
-                                                : 0.0f);
+                amax = ok ? absmax_acc(absmax_acc(amax, bf16lo(op[q])), bf16hi(op[q])) : amax;
             }
             if (ok) o4[c] = ov;
         }

@@ -50,26 +50,32 @@ __device__ __forceinline__ void swiglu_bwd_pair(float d, float g, float u, float
     du = d * g * sg;
 }
 
+// x clamped to [-m, m]; a NaN stays NaN (fmaxf/fminf alone would turn it into
+// -m, a finite code).
+__device__ __forceinline__ float clamp_keep_nan(float x, float m) {
+    return x != x ? x : __builtin_fminf(__builtin_fmaxf(x, -m), m);
+}
+
 // Four fp32 -> four e4m3 codes in one dword (a in the lowest byte).  Values are
 // clamped to +-448 first so the conversion never depends on an overflow mode;
-// v_cvt_pk_fp8_f32 rounds to nearest even.
+// v_cvt_pk_fp8_f32 rounds to nearest even and turns a NaN into a NaN code.
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-    a = __builtin_fminf(__builtin_fmaxf(a, -kE4M3Max), kE4M3Max);
-    b = __builtin_fminf(__builtin_fmaxf(b, -kE4M3Max), kE4M3Max);
-    c = __builtin_fminf(__builtin_fmaxf(c, -kE4M3Max), kE4M3Max);
-    d = __builtin_fminf(__builtin_fmaxf(d, -kE4M3Max), kE4M3Max);
+    a = clamp_keep_nan(a, kE4M3Max);
+    b = clamp_keep_nan(b, kE4M3Max);
+    c = clamp_keep_nan(c, kE4M3Max);
+    d = clamp_keep_nan(d, kE4M3Max);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
 
 // Four fp32 -> four e5m2 codes in one dword (a in the lowest byte), clamped
-// to +-57344 first; v_cvt_pk_bf8_f32 rounds to nearest even.
+// to +-57344 first (NaN kept); v_cvt_pk_bf8_f32 rounds to nearest even.
 __device__ __forceinline__ uint32_t pack_e5m2x4(float a, float b, float c, float d) {
-    a = __builtin_fminf(__builtin_fmaxf(a, -kE5M2Max), kE5M2Max);
-    b = __builtin_fminf(__builtin_fmaxf(b, -kE5M2Max), kE5M2Max);
-    c = __builtin_fminf(__builtin_fmaxf(c, -kE5M2Max), kE5M2Max);
-    d = __builtin_fminf(__builtin_fmaxf(d, -kE5M2Max), kE5M2Max);
+    a = clamp_keep_nan(a, kE5M2Max);
+    b = clamp_keep_nan(b, kE5M2Max);
+    c = clamp_keep_nan(c, kE5M2Max);
+    d = clamp_keep_nan(d, kE5M2Max);
     int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
     return (uint32_t)w;
@@ -78,13 +84,14 @@ __device__ __forceinline__ uint32_t pack_e5m2x4(float a, float b, float c, float
 // Per-tensor FP8 scale pair from an abs-max: the dequantisation factor
 // absmax/max and its quantisation inverse max/absmax (max = 448 for e4m3,
 // 57344 for e5m2), both IEEE fp32 quotients; 1 and 1 for an all-zero tensor.
+// A NaN abs-max gives NaN for both, so every code of the tensor is NaN.
 __device__ __forceinline__ void scale_pair(float am, float& scale, float& inv, float fmax = kE4M3Max) {
-    if (am > 0.0f) {
-        scale = am / fmax;
-        inv = fmax / am;
-    } else {
+    if (am == 0.0f) {
         scale = 1.0f;
         inv = 1.0f;
+    } else {
+        scale = am / fmax;
+        inv = fmax / am;
     }
 }
 
@@ -113,15 +120,26 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+// Abs-max accumulation: m = max(m, |v|) as the unsigned order of the bit
+// patterns of non-negative floats.  For numbers this is the IEEE order; a NaN
+// pattern lies above +inf, so a NaN anywhere in a tensor makes its abs-max NaN
+// (fmaxf would skip it).  m must be non-negative or NaN.
+__device__ __forceinline__ float absmax_acc(float m, float v) {
+    return __uint_as_float(max(__float_as_uint(m), __float_as_uint(v) & 0x7fffffffu));
+}
+
+// The same maximum over the 64 lanes (every value non-negative or NaN).
+__device__ __forceinline__ float wave_absmax(float v) {
+    unsigned int u = __float_as_uint(v);
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+    for (int m = 32; m >= 1; m >>= 1) u = max(u, (unsigned int)__shfl_xor((int)u, m, kWave));
+    return __uint_as_float(u);
 }
 
 // max into a non-negative fp32 in global memory: for v >= 0 the IEEE order is
-// the unsigned order of the bit patterns, so an integer atomic max is exact and
-// independent of the order in which blocks arrive.  The stored maximum only
+// the unsigned order of the bit patterns (a NaN pattern above all of them), so
+// an integer atomic max is exact and independent of the order in which blocks
+// arrive.  The stored maximum only
 // grows while blocks commit, so the atomic is skipped when the value already
 // there (read from L2, device scope) is at least v: a stale read can only
 // cost an unneeded atomic, never skip a needed one.  Thousands of blocks that
@@ -132,17 +150,18 @@ __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
     if (__float_as_uint(v) > cur) atomicMax(u, __float_as_uint(v));
 }
 
-// Block-wide max of a per-thread value, then one atomic per block.  All threads
-// of the block must call it.  `red` is LDS scratch of at least nwaves floats.
+// Block-wide abs-max of a per-thread value (non-negative or NaN, the order of
+// absmax_acc), then one atomic per block.  All threads of the block must call
+// it.  `red` is LDS scratch of at least nwaves floats.
 __device__ __forceinline__ void block_absmax_commit(float v, float* red, float* out) {
-    v = wave_max(v);
+    v = wave_absmax(v);
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     if (lane == 0) red[wid] = v;
     __syncthreads();
     if (threadIdx.x == 0) {
         float m = red[0];
-        for (int i = 1; i < (int)(blockDim.x / kWave); ++i) m = __builtin_fmaxf(m, red[i]);
+        for (int i = 1; i < (int)(blockDim.x / kWave); ++i) m = absmax_acc(m, red[i]);
         atomic_max_nonneg(out, m);
     }
 }

@@ -41,6 +41,16 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// A raw buffer resource over `bytes` bytes at p, and a 16-byte load from it
+// at voff (per lane) + soff (uniform); the streaming loops keep their bases
+// and piece offsets in scalar registers this way.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // kDual: rows of w0 (gate) and w1 (up) with the SiLU epilogue -> out = h [M, rows].
 // else : rows of w0 (down) -> out = y [M, rows].  x: [M, K] bf16.  TB = 16-token
 // blocks (M <= 16 * TB); RB = 16-row blocks per workgroup (each activation
@@ -213,66 +223,122 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
     }
 }
 
-// The dual pass of the packed decode for up to 16 tokens, persistent, with
-// the activations in LDS.  At 16 tokens each KiB of weight codes meets 2 KiB
-// of activation fragments, which decode_kernel reads from L2 once per row
-// block.  Here each workgroup (one per CU: the copy fills most of the LDS)
-// issues its first row block's weight loads, copies x from row-major order
-// into LDS in fragment order (the layout pack_x_kernel writes for token block
-// 0, zero past M; every load of the copy in flight before the first LDS
-// write), then walks the row blocks blk = blockIdx.x, + gridDim.x, ... with
-// the next block's weights loaded before the current block is multiplied:
-// only weights stream from memory, and x needs no separate re-layout launch.
-// Per row block the waves split the chunks as in decode_kernel (chunk
-// c = cw + rot, rot from the block index), the sums meet in LDS in wave
-// order, and wave 0 runs decode_kernel's epilogue (h to out, and to hp in
-// fragment order for the down pass); the results do not depend on the grid
-// size.  K <= kLdsDualMaxK, K % 128 == 0, rows % 16 == 0.
+// Largest K whose 16-token activations the dual pass keeps in LDS (128 KiB).
 constexpr int kLdsDualMaxK = 4096;
-template <int kWaves>
-__global__ __launch_bounds__(64 * kWaves) void decode_dual_lds_kernel(
+
+// The packed decode for up to 16 tokens, as three launches that keep every
+// CU streaming weights from HBM.  Both streaming kernels keep two register
+// buffers of kU KiB pieces per matrix and alternate between them (the loop is
+// unrolled by two): the loads of the next group are issued before the current
+// group is multiplied, and no buffer is ever copied to another (a copy would
+// wait for the loads in flight).  Every load is issued unconditionally: a
+// piece past the end loads an in-bounds piece again (a cache hit) and is not
+// multiplied, so the compiler's waits count exactly the younger loads.
+//
+// decode_dual_wave_kernel: the dual pass, persistent (one workgroup of kWaves
+// waves per CU) with x copied into LDS in fragment order.  Each wave owns
+// whole row blocks: it streams the block's gate and up codes front to back
+// and runs the block's epilogue itself, so after the copy of x no wave waits
+// for another.  Row blocks are dealt to the workgroups first (block b goes to
+// workgroup b % G, wave b / G % kWaves), so the CUs differ by at most one busy
+// wave.  Each wave starts its walk at a block-dependent group (the channel
+// spreading of decode_kernel).  The sums depend only on the block index, not
+// on the grid.  K <= kLdsDualMaxK, K % 128 == 0, rows % 16 == 0, M <= 16.
+template <int kU>
+struct DualBuf {
+    uint4 w[2][kU];
+    float sg[4], su[4];  // the row scales of the item's block (this lane's rows)
+};
+
+template <int kWaves, int kU>
+__global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
     uint16_t* __restrict__ out, uint16_t* __restrict__ hp, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ w0, const float* __restrict__ s0, const uint8_t* __restrict__ w1,
     const float* __restrict__ s1, int M, int K, int rows) {
-    __shared__ uint4 xs[kLdsDualMaxK / 32 * 64];  // fragment f, lane l: piece 64 f + l (128 KiB at most)
-    __shared__ f32x4_t red[kWaves][2][64];
+    __shared__ uint4 xs[kLdsDualMaxK / 32 * 64];  // fragment f, lane l: piece 64 f + l
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: loop bounds stay scalar
     const int lr = lane & 15, lq = lane >> 4;
     const int nblocks = rows / 16;
-    const int nchunks = (K + kChunk - 1) / kChunk;  // <= kLdsDualMaxK / kChunk
-    constexpr int kCPW = (kLdsDualMaxK / kChunk + kWaves - 1) / kWaves;  // chunks per wave per block
-    // Chunk j of this wave in row block b starts at byte kb (K: no chunk).
-    auto chunk_kb = [&](int b, int j) {
-        const int cw = wave + j * kWaves;
-        const int rot = (int)(((unsigned)b * 5u) % (unsigned)nchunks);
-        const int c = cw + rot < nchunks ? cw + rot : cw + rot - nchunks;
-        return cw < nchunks ? c * kChunk : K;
+    const int npieces = K / 64;                  // 1-KiB pieces per row block and matrix
+    const int ngroups = (npieces + kU - 1) / kU;
+    const int G = gridDim.x;
+    const int stride = kWaves * G;
+    const int b0 = wave * G + blockIdx.x;
+    const int nb = b0 < nblocks ? (nblocks - 1 - b0) / stride + 1 : 0;
+    const int nit = nb * ngroups;  // (block, group) items of this wave
+    // item it: block b0 + (it / ngroups) stride, group (it % ngroups + rot) % ngroups
+    auto item_group = [&](int it, int& b) {
+        b = b0 + (it / ngroups) * stride;
+        int g = it % ngroups + (int)(((unsigned)b * 5u) % (unsigned)ngroups);
+        return g < ngroups ? g : g - ngroups;
     };
-    // The weights of the next row block are loaded before the current one is
-    // multiplied and reduced, so the loads stay in flight across the barriers.
-    auto load_block = [&](int b, uint4 (&wq)[kCPW][2][kPieces]) {
-        const int64_t wbase = (int64_t)b * 16 * K + lane * 16;
+    auto load_item = [&](int it, DualBuf<kU>& q) {
+        int b;
+        const int g = item_group(it, b);
+        const uint32_t bytes = (uint32_t)(16 * K);
+        const __amdgpu_buffer_rsrc_t r0 = rsrc_of(w0 + (int64_t)b * bytes, bytes);
+        const __amdgpu_buffer_rsrc_t r1 = rsrc_of(w1 + (int64_t)b * bytes, bytes);
 #pragma unroll
-        for (int j = 0; j < kCPW; ++j) {
-            const int kb = chunk_kb(b, j);
+        for (int i = 0; i < kU; ++i) {
+            const uint32_t so = (uint32_t)min(g * kU + i, npieces - 1) * 1024u;
+            q.w[0][i] = bload16(r0, lane * 16, so);
+            q.w[1][i] = bload16(r1, lane * 16, so);
+        }
+        const uint4 vg = bload16(rsrc_of(s0 + b * 16, 64), lq * 16, 0);
+        const uint4 vu = bload16(rsrc_of(s1 + b * 16, 64), lq * 16, 0);
+        q.sg[0] = __uint_as_float(vg.x), q.sg[1] = __uint_as_float(vg.y);
+        q.sg[2] = __uint_as_float(vg.z), q.sg[3] = __uint_as_float(vg.w);
+        q.su[0] = __uint_as_float(vu.x), q.su[1] = __uint_as_float(vu.y);
+        q.su[2] = __uint_as_float(vu.z), q.su[3] = __uint_as_float(vu.w);
+    };
+    f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    auto run_item = [&](int it, const DualBuf<kU>& q) {
+        int b;
+        const int g = item_group(it, b);
+        if (it % ngroups == 0) {
+            acc[0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            acc[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
-                const bool in = kb + 64 * i < K;
-                wq[j][0][i] = in ? *reinterpret_cast<const uint4*>(w0 + wbase + (int64_t)(kb + 64 * i) * 16)
-                                 : make_uint4(0, 0, 0, 0);
-                wq[j][1][i] = in ? *reinterpret_cast<const uint4*>(w1 + wbase + (int64_t)(kb + 64 * i) * 16)
-                                 : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < kU; ++i) {
+            const int p = g * kU + i;
+            if (p < npieces) {
+                const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, xs[(2 * p) * 64 + lane]);
+                const bf16x8_t xb1 = __builtin_bit_cast(bf16x8_t, xs[(2 * p + 1) * 64 + lane]);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(q.w[m][i].x, q.w[m][i].y), xb0,
+                                                                    acc[m], 0, 0, 0);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(q.w[m][i].z, q.w[m][i].w), xb1,
+                                                                    acc[m], 0, 0, 0);
+                }
             }
         }
+        if (it % ngroups == ngroups - 1) {
+            // lane: token lr, rows orow0 .. + 3 of block b
+            const int orow0 = b * 16 + 4 * lq;
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                o[r] = silu_mul(round_bf16(q.sg[r] * acc[0][r]), round_bf16(q.su[r] * acc[1][r]));
+            uint2 v;
+            v.x = pack_bf16x2(o[0], o[1]);
+            v.y = pack_bf16x2(o[2], o[3]);
+            const int k = orow0;  // h in fragment order for the down pass (token block 0)
+            const int64_t off =
+                (int64_t)(2 * (k / 64) + (k % 16) / 8) * 512 + (lr + 16 * ((k % 64) / 16)) * 8 + (k % 8);
+            *reinterpret_cast<uint2*>(hp + off) = v;
+            if (lr < M) *reinterpret_cast<uint2*>(out + (int64_t)lr * rows + orow0) = v;
+        }
     };
-    uint4 wcur[kCPW][2][kPieces];
-    if (blockIdx.x < nblocks) load_block(blockIdx.x, wcur);
-    // the activations go to LDS while the first block's weights are in flight
-    // (every load of the copy is issued before the first LDS write)
+    DualBuf<kU> qa, qb;
+    if (nit > 0) load_item(0, qa);
+    // x into LDS while the first loads are in flight (every load of the copy
+    // issued before the first LDS write)
     {
         const int pieces = K / 32 * 64;
-        constexpr int kPer = kLdsDualMaxK / 32 * 64 / (64 * kWaves);  // pieces per thread at most
+        constexpr int kPer = kLdsDualMaxK / 32 * 64 / (64 * kWaves);
         uint4 v[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -289,74 +355,138 @@ __global__ __launch_bounds__(64 * kWaves) void decode_dual_lds_kernel(
         }
     }
     __syncthreads();
-    for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
-        const int row0 = blk * 16;
-        uint4 wnxt[kCPW][2][kPieces];
-        if (blk + (int)gridDim.x < nblocks) load_block(blk + gridDim.x, wnxt);
-        f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-        for (int j = 0; j < kCPW; ++j) {
-            const int kb = chunk_kb(blk, j);
-            if (kb >= K) continue;
-#pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
-                const bool in = kb + 64 * i < K;
-                const int f = (kb + 64 * i) / 32;
-                const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, in ? xs[f * 64 + lane] : make_uint4(0, 0, 0, 0));
-                const bf16x8_t xb1 =
-                    __builtin_bit_cast(bf16x8_t, in ? xs[(f + 1) * 64 + lane] : make_uint4(0, 0, 0, 0));
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const bf16x8_t a0 = e4m3x8_to_bf16(wcur[j][m][i].x, wcur[j][m][i].y);
-                    const bf16x8_t a1 = e4m3x8_to_bf16(wcur[j][m][i].z, wcur[j][m][i].w);
-                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xb0, acc[m], 0, 0, 0);
-                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xb1, acc[m], 0, 0, 0);
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kCPW; ++j)
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int i = 0; i < kPieces; ++i) wcur[j][m][i] = wnxt[j][m][i];
-        red[wave][0][lane] = acc[0];
-        red[wave][1][lane] = acc[1];
-        __syncthreads();
-        if (wave == 0) {
-            f32x4_t fin[2];
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                f32x4_t v = red[0][m][lane];
-#pragma unroll
-                for (int w = 1; w < kWaves; ++w) {
-                    const f32x4_t u = red[w][m][lane];
-                    v[0] += u[0];
-                    v[1] += u[1];
-                    v[2] += u[2];
-                    v[3] += u[3];
-                }
-                fin[m] = v;
-            }
-            // lane: token lr, weight rows orow0 .. + 3 of the block
-            const int orow0 = row0 + 4 * lq;
-            float o[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float g = round_bf16(s0[orow0 + r] * fin[0][r]);
-                const float u = round_bf16(s1[orow0 + r] * fin[1][r]);
-                o[r] = silu_mul(g, u);
-            }
-            uint2 v;
-            v.x = pack_bf16x2(o[0], o[1]);
-            v.y = pack_bf16x2(o[2], o[3]);
-            const int k = orow0;  // h in fragment order, as decode_kernel writes it
-            const int64_t off = (int64_t)(2 * (k / 64) + (k % 16) / 8) * 512 + (lr + 16 * ((k % 64) / 16)) * 8 + (k % 8);
-            *reinterpret_cast<uint2*>(hp + off) = v;
-            if (lr < M) *reinterpret_cast<uint2*>(out + (int64_t)lr * rows + orow0) = v;
-        }
-        __syncthreads();  // red is rewritten by the next block
+    for (int it = 0; it < nit; it += 2) {
+        load_item(min(it + 1, nit - 1), qb);
+        run_item(it, qa);
+        if (it + 1 >= nit) break;
+        load_item(min(it + 2, nit - 1), qa);
+        run_item(it + 1, qb);
     }
+}
+
+// decode_down_split_kernel: the down pass split along K.  Workgroup
+// (group, s), s = blockIdx.x % S, multiplies the 8 row blocks 8 group .. + 7
+// (one per wave) by the s-th of S slices of h: it first copies the slice of
+// the fragment-order h (2 KiB per 64-code piece, at most kDownMaxSlice pieces)
+// into LDS, then each wave streams its block's codes of the slice (kU KiB
+// pieces per group, two buffers as above) and writes its fp32 sums, 16 tokens
+// x 16 rows, to part[s][token][row].  Only weights stream from HBM: each slice
+// of h is read from L2 once per workgroup instead of once per row block.
+// decode_down_reduce_kernel then adds the S partial sums of each output in
+// slice order and applies the row scale; S depends on the shape alone, so the
+// result does not depend on the device.  K % 64 == 0, rows % 128 == 0.
+constexpr int kDownMaxSlice = 64;  // 64-code pieces of h per slice (128 KiB of LDS)
+template <int kU>
+__global__ __launch_bounds__(512) void decode_down_split_kernel(float* __restrict__ part,
+                                                                const uint16_t* __restrict__ hp,
+                                                                const uint8_t* __restrict__ w, int K, int rows,
+                                                                int S) {
+    __shared__ uint4 hs[kDownMaxSlice * 128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int s = blockIdx.x % S, grp = blockIdx.x / S;
+    const int npieces = K / 64;
+    const int p0 = (int)((int64_t)s * npieces / S), p1 = (int)((int64_t)(s + 1) * npieces / S);
+    const int np = p1 - p0;  // 1 .. kDownMaxSlice
+    const int ngroups = (np + kU - 1) / kU;
+    const int rb = grp * 8 + wave;
+    const __amdgpu_buffer_rsrc_t wr = rsrc_of(w + (int64_t)rb * 16 * K, (uint32_t)(16 * K));
+    auto load_group = [&](int g, uint4 (&wq)[kU]) {
+#pragma unroll
+        for (int i = 0; i < kU; ++i) wq[i] = bload16(wr, lane * 16, (uint32_t)(p0 + min(g * kU + i, np - 1)) * 1024u);
+    };
+    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto run_group = [&](int g, const uint4 (&wq)[kU]) {
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            const int p = g * kU + i;
+            if (p < np) {
+                const bf16x8_t h0 = __builtin_bit_cast(bf16x8_t, hs[(2 * p) * 64 + lane]);
+                const bf16x8_t h1 = __builtin_bit_cast(bf16x8_t, hs[(2 * p + 1) * 64 + lane]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(wq[i].x, wq[i].y), h0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(wq[i].z, wq[i].w), h1, acc, 0, 0, 0);
+            }
+        }
+    };
+    uint4 wa[kU], wbuf[kU];
+    load_group(0, wa);
+    {
+        // the slice: fragments 2 p0 .. 2 p1 - 1, 64 pieces of 16 bytes each
+        const uint4* src = reinterpret_cast<const uint4*>(hp) + (int64_t)p0 * 128;
+        constexpr int kPer = kDownMaxSlice * 128 / 512;
+        uint4 v[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = threadIdx.x + j * 512;
+            v[j] = i < np * 128 ? src[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = threadIdx.x + j * 512;
+            if (i < np * 128) hs[i] = v[j];
+        }
+    }
+    __syncthreads();
+    for (int g = 0; g < ngroups; g += 2) {
+        load_group(min(g + 1, ngroups - 1), wbuf);
+        run_group(g, wa);
+        if (g + 1 >= ngroups) break;
+        load_group(min(g + 2, ngroups - 1), wa);
+        run_group(g + 1, wbuf);
+    }
+    // lane: token lr, rows rb * 16 + 4 lq .. + 3
+    *reinterpret_cast<f32x4_t*>(part + ((int64_t)s * 16 + lr) * rows + rb * 16 + 4 * lq) = acc;
+}
+
+// out[m, c] = bf16(sd[c] * (part[0][m][c] + part[1][m][c] + ... + part[S-1][m][c])), m < M;
+// one thread per four consecutive outputs, the partial sums loaded eight
+// slices at a time (all eight loads in flight before the first add) and added
+// in slice order.
+__global__ __launch_bounds__(256) void decode_down_reduce_kernel(uint16_t* __restrict__ out,
+                                                                 const float* __restrict__ part,
+                                                                 const float* __restrict__ sd, int M, int rows,
+                                                                 int S) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int q = rows / 4;
+    if (t >= M * q) return;
+    const int m = t / q, c = (t - m * q) * 4;
+    f32x4_t a = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = *reinterpret_cast<const f32x4_t*>(part + ((int64_t)min(s0 + j, S - 1) * 16 + m) * rows + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (s0 + j >= S) break;
+            if (s0 + j == 0) {
+                a = v[0];
+            } else {
+                a[0] += v[j][0];
+                a[1] += v[j][1];
+                a[2] += v[j][2];
+                a[3] += v[j][3];
+            }
+        }
+    }
+    uint2 o;
+    o.x = pack_bf16x2(sd[c] * a[0], sd[c + 1] * a[1]);
+    o.y = pack_bf16x2(sd[c + 2] * a[2], sd[c + 3] * a[3]);
+    *reinterpret_cast<uint2*>(out + (int64_t)m * rows + c) = o;
+}
+
+// Slices of the split down pass for rows = C, K = H: enough workgroups (8 row
+// blocks each) for a 256-CU device, no slice longer than kDownMaxSlice pieces
+// and none empty.  A function of the shape alone.
+static int down_slices(int rows, int K) {
+    const int groups = rows / 128;
+    const int npieces = K / 64;
+    int S = 256 / groups;
+    const int min_s = (npieces + kDownMaxSlice - 1) / kDownMaxSlice;
+    if (S < min_s) S = min_s;
+    if (S > npieces) S = npieces;
+    return S < 1 ? 1 : S;
 }
 
 // Few-token form (M <= 4) of the passes, on the vector ALU.  With one to
@@ -719,12 +849,16 @@ __global__ __launch_bounds__(256) void pack_x_kernel(uint16_t* __restrict__ xp, 
 // flight per wave); the down pass of two token blocks keeps 8 waves, since
 // 16 waves of a workgroup have at most 128 registers each
 constexpr int kPackedDualWaves = 4;
-constexpr int kLdsDualWaves = 8;  // waves per workgroup of decode_dual_lds_kernel
 template <int TB> constexpr int packed_down_waves() { return TB == 1 ? 16 : 8; }
 
+// Workspace of the packed decode, in bf16 elements: x and h in fragment order,
+// then (up to 16 tokens) the split down pass's fp32 partial sums.  Never
+// smaller for more tokens, so a workspace for the largest batch serves all.
 int64_t decode_packed_ws_elems(int M, int C, int H) {
-    const int TB = M <= 16 ? 1 : 2;
-    return (int64_t)TB * 16 * ((int64_t)C + H);
+    const int64_t one_block = 16 * ((int64_t)C + H) + 2 * (int64_t)down_slices(C, H) * 16 * C;
+    if (M <= 16) return one_block;
+    const int64_t two_blocks = 2 * 16 * ((int64_t)C + H);
+    return one_block > two_blocks ? one_block : two_blocks;
 }
 
 template <int TB>
@@ -741,37 +875,51 @@ static hipError_t launch_packed_tb(uint16_t* out, uint16_t* h, uint16_t* xp, uin
     return hipGetLastError();
 }
 
+// waves per workgroup and 1-KiB pieces per load group of the 16-token passes
+constexpr int kWaveDualWaves = 8, kWaveDualU = 8, kDownSplitU = 8;
+
 hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const uint16_t* x, const uint8_t* wg,
                                 const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
                                 const float* sd, int M, int C, int H, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    const int TB = M <= 16 ? 1 : 2;
-    uint16_t* xp = ws;                        // [TB][16 C] fragment order
-    uint16_t* hp = ws + (int64_t)TB * 16 * C;  // [TB][16 H]
-    // The persistent LDS dual pass (one workgroup per CU: the activations fill
-    // most of its LDS) when its rounds of row blocks are nearly full: measured
-    // faster on the Qwen2-7B shape (1184 blocks, five rounds on 256 CUs, 93%
-    // full: 61.0 -> 58.6 us at 16 tokens) and slower on the Llama-8B shape (896
-    // blocks, four rounds 88% full: 45.0 -> 46.1 us), where decode_kernel's
-    // one workgroup per row block balances better.
-    const int nblk = H / 16, cus = device_cu_count();
-    const int rounds = (nblk + cus - 1) / cus;
-    if (TB == 1 && C <= kLdsDualMaxK && (int64_t)nblk * 10 >= (int64_t)rounds * cus * 9) {
-        const int grid = min(nblk, cus);
-        hipLaunchKernelGGL((decode_dual_lds_kernel<kLdsDualWaves>), dim3(grid), dim3(64 * kLdsDualWaves), 0, s, h, hp,
-                           x, wg, sg, wu, su, M, C, H);
-        hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (M <= 16) {
+        uint16_t* xp = ws;                 // [16 C] fragment order (C > kLdsDualMaxK only)
+        uint16_t* hp = ws + (int64_t)16 * C;  // [16 H]
+        float* part = reinterpret_cast<float*>(ws + (int64_t)16 * (C + H));  // [S][16][C]
+        if (C <= kLdsDualMaxK) {
+            // one persistent workgroup per CU (x fills most of its LDS); the
+            // grid size changes only which wave takes a row block, not the sums
+            const int grid = min(H / 16, device_cu_count());
+            hipLaunchKernelGGL((decode_dual_wave_kernel<kWaveDualWaves, kWaveDualU>), dim3(grid),
+                               dim3(64 * kWaveDualWaves), 0, s, h, hp, x, wg, sg, wu, su, M, C, H);
+        } else {
+            const int64_t pieces = (int64_t)(C / 32) * 64;
+            hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, xp, x, M, C,
+                               pieces);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((decode_kernel<true, 1, 1, kPackedDualWaves, true>), dim3(H / 16),
+                               dim3(64 * kPackedDualWaves), 0, s, h, hp, xp, wg, sg, wu, su, M, C, H);
+        }
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
-        constexpr int kDownW = packed_down_waves<1>();
-        hipLaunchKernelGGL((decode_kernel<false, 1, 1, kDownW, true>), dim3(C / 16), dim3(64 * kDownW), 0, s, out,
-                           nullptr, hp, wd, sd, nullptr, nullptr, M, H, C);
+        const int S = down_slices(C, H);
+        hipLaunchKernelGGL((decode_down_split_kernel<kDownSplitU>), dim3((C / 128) * S), dim3(512), 0, s, part, hp,
+                           wd, H, C, S);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int threads = M * (C / 4);
+        hipLaunchKernelGGL(decode_down_reduce_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, out, part, sd, M,
+                           C, S);
         return hipGetLastError();
     }
-    const int64_t pieces = (int64_t)TB * (C / 32) * 64;
+    uint16_t* xp = ws;                            // [2][16 C]
+    uint16_t* hp = ws + (int64_t)2 * 16 * C;      // [2][16 H]
+    const int64_t pieces = (int64_t)2 * (C / 32) * 64;
     hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, xp, x, M, C, pieces);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (TB == 1) return launch_packed_tb<1>(out, h, xp, hp, wg, sg, wu, su, wd, sd, M, C, H, s);
     return launch_packed_tb<2>(out, h, xp, hp, wg, sg, wu, su, wd, sd, M, C, H, s);
 }
 

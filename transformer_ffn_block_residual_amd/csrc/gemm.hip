@@ -380,14 +380,12 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
                         swiglu_bwd_pair(bf16hi(dv[e]), bf16hi(gg[e]), bf16hi(uu[e]), g1, u1);
                         og[e] = pack_bf16x2(g0, g1);
                         ou[e] = pack_bf16x2(u0, u1);
-                        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(og[e])),
-                                                               __builtin_fabsf(bf16hi(og[e]))));
-                        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(ou[e])),
-                                                               __builtin_fabsf(bf16hi(ou[e]))));
+                        m = absmax_acc(absmax_acc(m, bf16lo(og[e])), bf16hi(og[e]));
+                        m = absmax_acc(absmax_acc(m, bf16lo(ou[e])), bf16hi(ou[e]));
                     }
                     // one running maximum, updated in order (left to itself the
                     // compiler regroups the whole chain and runs out of registers)
-                    amax = __builtin_fmaxf(amax, m);
+                    amax = absmax_acc(amax, m);
                     asm volatile("" : "+v"(amax));
                     const uint32_t off = off_of(hb, gi);
                     __builtin_amdgcn_raw_buffer_store_b128(og, rsrc, off, 0, 0);
@@ -485,8 +483,8 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
                     float m = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(d[e])), __builtin_fabsf(bf16hi(d[e]))));
-                    amax = __builtin_fmaxf(amax, ok ? m : 0.0f);
+                        m = absmax_acc(absmax_acc(m, bf16lo(d[e])), bf16hi(d[e]));
+                    amax = absmax_acc(amax, ok ? m : 0.0f);
                     const u32x4_t v = regroup_runs(d[0], d[1], d[2], d[3]);
                     const int o = tm * 128 + wm * 64 + i * 32 + 16 * q + 8 * fh;
                     const uint32_t off = (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * kOutElt;

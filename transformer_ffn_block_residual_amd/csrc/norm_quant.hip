@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     yp[q] = pack_bf16x2((bf16lo(rp[q]) * rs) * bf16lo(wp[q]), (bf16hi(rp[q]) * rs) * bf16hi(wp[q]));
-                    amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16lo(yp[q])), __builtin_fabsf(bf16hi(yp[q]))));
+                    amax = absmax_acc(absmax_acc(amax, bf16lo(yp[q])), bf16hi(yp[q]));
                 }
                 if (kAdd) o4[c] = r[i];
                 y4[c] = yv;
@@ -155,10 +155,10 @@ __global__ __launch_bounds__(256) void absmax_kernel(float* out, const uint16_t*
             const uint32_t* p = reinterpret_cast<const uint32_t*>(&v[i]);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(p[q])), __builtin_fabsf(bf16hi(p[q]))));
+                m = absmax_acc(absmax_acc(m, bf16lo(p[q])), bf16hi(p[q]));
         }
     }
-    for (int64_t i = (nch << 3) + t0; i < n; i += stride) m = __builtin_fmaxf(m, __builtin_fabsf(bf16lo(x[i])));
+    for (int64_t i = (nch << 3) + t0; i < n; i += stride) m = absmax_acc(m, bf16lo(x[i]));
     block_absmax_commit(m, red, out);
 }
 
@@ -236,12 +236,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(uint8_t* __restrict__ q
         const uint32_t* p = reinterpret_cast<const uint32_t*>(&v);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(p[k])), __builtin_fabsf(bf16hi(p[k]))));
+            m = absmax_acc(absmax_acc(m, bf16lo(p[k])), bf16hi(p[k]));
     }
-    m = wave_max(m);
+    m = wave_absmax(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) am_s = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    if (threadIdx.x == 0) am_s = absmax_acc(absmax_acc(red[0], red[1]), absmax_acc(red[2], red[3]));
     __syncthreads();
     float scale, inv;
     scale_pair(am_s, scale, inv);
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(uint16_t* __restrict__ h, f
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             op[k] = pack_bf16x2(silu_mul(bf16lo(gp[k]), bf16lo(up[k])), silu_mul(bf16hi(gp[k]), bf16hi(up[k])));
-            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bf16lo(op[k])), __builtin_fabsf(bf16hi(op[k]))));
+            m = absmax_acc(absmax_acc(m, bf16lo(op[k])), bf16hi(op[k]));
         }
         reinterpret_cast<uint4*>(h + n * H)[c] = o;
     }
