@@ -8,14 +8,16 @@ h, down GEMM; then the 16-token FP8 decode FFN (dual gate/up GEMV with SiLU,
 down GEMV) over the same e4m3 weights with per-row scales.  Inputs are seeded
 synthetic tensors already resident in HBM when the timed region starts.
 
-Other workloads (same line format, for the per-configuration figures):
+The default run also times the other configurations, each in the same way,
+and puts them in the line's "configs" record (each with its own roofline line
+and CPU baseline); --workload prints one of them as the line itself:
   prefill   bf16 block, N=4096, C=4096, H=14336
   prefill8  FP8 block, same shape, 0.1% x50 outliers
   decode    single-token FP8 decode, C=4096, H=14336 (value in GB/s);
             --decode-arm picks the arm (split SiLU, fused SiLU input,
-            per projection, or bf16 weights), --decode-m the tokens (1..4)
+            per projection, or bf16 weights), --decode-m the tokens (1..32)
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 25] [--workload qwen7b8] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 25] [--workload W] [--no-configs] [--no-cpu-baseline]
 
 Prints one JSON line.  For block workloads value = whole-step algorithmic
 FLOP/s (the block's dense contractions: 6*N*C*H for the prefill, 6*M*C*H for
@@ -24,7 +26,8 @@ scales + activations, each once) per second.  "roofline" describes the
 dominant kernel from HIP events recorded on its launch stream around every
 launch of a second pass of the same steps (the timed region itself carries
 only its two bracketing events); "cpu_baseline" times the CPU oracle on a bounded
-sample of the same workload.
+sample of the same workload: the C++ oracle (fp32, std::thread over rows)
+for the forward and the FP8 decode, with the CPU model and core counts.
 """
 
 import argparse
@@ -58,15 +61,20 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=25)
-    p.add_argument("--workload", default="qwen7b8", choices=["qwen7b8", "prefill", "prefill8", "decode"])
+    p.add_argument("--workload", default=None, choices=["qwen7b8", "prefill", "prefill8", "decode"],
+                   help="one workload's line only (default: the qwen7b8 step, with the other configurations "
+                        "in its 'configs' record)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="default run: leave out the 'configs' record of the other configurations")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0,
-                   help="prefill rows in the CPU oracle sample (default: min(N, 4096), about 10 s)")
+                   help="prefill rows in the CPU oracle sample (default: all N rows, 10-30 s on 16 threads)")
     p.add_argument("--cpu-decodes", type=int, default=30,
                    help="decode calls in the CPU oracle sample of the decode workload (about 10 s)")
     p.add_argument("--decode-arm", default="split", choices=list(DECODE_ARMS),
                    help="decode workload: which arm of the decode FFN runs")
-    p.add_argument("--decode-m", type=int, default=1, help="decode workload: tokens per call (1..4 off split)")
+    p.add_argument("--decode-m", type=int, default=1,
+                   help="decode workload: tokens per call (1..32 on the split arm, 1..4 on the others)")
     p.add_argument("--backward", action="store_true",
                    help="block workloads: time the FFN block backward (after one forward) instead of the forward")
     p.add_argument("--decode-layout", default="auto", choices=["auto", "rows", "packed"],
@@ -206,58 +214,70 @@ def blas_threads():
         return os.cpu_count() or 1
 
 
+def host_desc():
+    """The host the CPU baseline runs on: CPU model, logical CPUs this process
+    may use, physical cores of the machine."""
+    from oracle import cpp
+    model, _, physical = cpp.cpu_info()
+    return {"cpu_model": model, "logical_cpus": cpp.threads(), "physical_cores": physical}
+
+
 def cpu_block_sample(w, d, rows, dec_x=None):
-    """The oracle, untuned, on a bounded sample: one block over the first
-    `rows` token rows (plus the full decode batch when given), FP8 weights
-    quantised beforehand, outside the timed region, as on the device."""
+    """The C++ oracle (fp32, std::thread over rows on every CPU this process
+    may use), untuned, on one block over the first `rows` token rows (plus
+    the full decode batch when given); FP8 weights quantised beforehand,
+    outside the timed region, as on the device."""
     import numpy as np
-    import oracle as O
+    from oracle import cpp as P
     H, C = w.H, w.C
     if w.fp8:
-        qw_gu, s_gu, _ = O.quant_absmax(d["w_gu"])
-        qw_d, s_d, _ = O.quant_absmax(d["w_d"])
+        qw_gu, s_gu, _ = P.quant_absmax(d["w_gu"])
+        qw_d, s_d, _ = P.quant_absmax(d["w_d"])
     inp, add = d["inp"][:rows], d["addend"][:rows]
     t0 = time.perf_counter()
-    r, y, rstd, am_y = O.rmsnorm_fwd(inp, add, d["w_norm"], w.eps)
+    r, y, rstd, am_y = P.rmsnorm_fwd(inp, add, d["w_norm"], w.eps)
     if w.fp8:
-        qy, sy, _ = O.quant_absmax(y, am_y)
-        h, am_h = O.swiglu(O.gemm_fp8(qy, sy, qw_gu, s_gu))
-        qh, sh, _ = O.quant_absmax(h, am_h)
-        O.gemm_fp8(qh, sh, qw_d, s_d)
+        qy, sy, _ = P.quant_absmax(y, am_y)
+        h, am_h = P.swiglu(P.gemm_fp8(qy, sy, qw_gu, s_gu))
+        qh, sh, _ = P.quant_absmax(h, am_h)
+        P.gemm_fp8(qh, sh, qw_d, s_d)
     else:
-        h, _ = O.swiglu(O.gemm_bf16(y, d["w_gu"]))
-        O.gemm_bf16(h, d["w_d"])
+        h, _ = P.swiglu(P.gemm_bf16(y, d["w_gu"]))
+        P.gemm_bf16(h, d["w_d"])
     flops = 6.0 * rows * C * H
-    what = f"prefill block over the first {rows} of {w.N} token rows"
+    what = f"prefill block over {'all' if rows == w.N else 'the first'} {rows} of {w.N} token rows"
     if dec_x is not None:
         sgv = np.full(H, s_gu, np.float32)
         sdv = np.full(C, s_d, np.float32)
-        O.decode_gemv(dec_x, qw_gu[:H], sgv, qw_gu[H:], sgv, qw_d, sdv)
+        P.decode_gemv(dec_x, qw_gu[:H], sgv, qw_gu[H:], sgv, qw_d, sdv)
         flops += 6.0 * dec_x.shape[0] * C * H
         what += f" + the full {dec_x.shape[0]}-token decode"
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"{what}; weights quantised beforehand; {dt:.2f} s wall"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": P.threads(), "kind": "oracle",
+            "impl": "C++ oracle, fp32, 16-way fixed-order sums, std::thread over rows",
+            "sample": f"{what}; weights quantised beforehand; {dt:.2f} s wall", **host_desc()}
 
 
 def cpu_decode_sample(d_q, x, calls):
-    """The oracle decode of x's M tokens over the full weights (already
+    """The C++ oracle decode of x's M tokens over the full weights (already
     quantised), `calls` times, in GB/s of algorithmic bytes."""
-    import oracle as O
+    from oracle import cpp as P
     qg, sg, qu, su, qd, sd = d_q
     H, C = qg.shape
     M = x.shape[0]
     t0 = time.perf_counter()
     for _ in range(calls):
-        O.decode_gemv(x, qg, sg, qu, su, qd, sd)
+        P.decode_gemv(x, qg, sg, qu, su, qd, sd)
     dt = time.perf_counter() - t0
     nbytes = calls * (3.0 * H * C + (2 * H + C) * 4 + 2.0 * M * (C + H) * 2)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"{calls} full {M}-token FP8 decodes (C={C}, H={H}); {dt:.2f} s wall"}
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": P.threads(), "kind": "oracle",
+            "impl": "C++ oracle, fp32, 16-way fixed-order sums, std::thread over rows",
+            "sample": f"{calls} full {M}-token FP8 decodes (C={C}, H={H}); {dt:.2f} s wall", **host_desc()}
 
 
 def cpu_decode_sample_bf16(d, calls):
-    """The oracle bf16-weight decode, `calls` times, in GB/s of algorithmic bytes."""
+    """The numpy oracle's bf16-weight decode, `calls` times, in GB/s of
+    algorithmic bytes (the C++ oracle has no bf16-weight arm)."""
     import oracle as O
     H, C = d["w_gate"].shape
     M = d["x"].shape[0]
@@ -267,7 +287,8 @@ def cpu_decode_sample_bf16(d, calls):
     dt = time.perf_counter() - t0
     nbytes = calls * (6.0 * H * C + 2.0 * M * (C + H) * 2)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"{calls} full {M}-token bf16-weight decodes (C={C}, H={H}); {dt:.2f} s wall"}
+            "impl": "numpy oracle, fp64 BLAS", "sample": f"{calls} full {M}-token bf16-weight decodes (C={C}, H={H}); "
+            f"{dt:.2f} s wall", **host_desc()}
 
 
 def graph_step_ms(torch, issue, steps):
@@ -517,7 +538,7 @@ def bench_block(a, torch, np, B, block, W):
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_block_sample(w, d, a.cpu_rows or min(N, 4096), dec_x)
+        out["cpu_baseline"] = cpu_block_sample(w, d, a.cpu_rows or N, dec_x)
     return out
 
 
@@ -555,7 +576,9 @@ def cpu_backward_sample(w, d, rows, grad_fmt="e4m3"):
     dt = time.perf_counter() - t0
     flops = 12.0 * rows * w.C * w.H
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"block backward over the first {rows} of {w.N} token rows (full weights); {dt:.2f} s wall"}
+            "impl": "numpy oracle, fp64 BLAS (the C++ oracle covers the forward only)",
+            "sample": f"block backward over the first {rows} of {w.N} token rows (full weights); {dt:.2f} s wall",
+            **host_desc()}
 
 
 def _bwd_dout(np, w, rows):
@@ -762,14 +785,24 @@ def bench_decode(a, torch, np, B, block, W):
     return out
 
 
+# the per-configuration figures of the default run: (workload, decode tokens)
+SUB_CONFIGS = (("decode", 1), ("prefill", 0), ("prefill8", 0))
+SUB_KEYS = ("metric", "value", "unit", "ms_per_step", "dtype", "config", "roofline", "kernels", "cpu_baseline")
+
+
 def main():
     a = parse()
     if a.ingest_pmc:
+        if a.workload is None:
+            a.workload = "qwen7b8"
         return ingest_pmc(a)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this FFN block path has no "
               "multi-GPU mode.", file=sys.stderr)
         return 2
+
+    import copy
+    import gc
 
     import numpy as np
     import torch
@@ -777,12 +810,28 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    all_configs = a.workload is None and not a.backward and not a.no_configs
+    if a.workload is None:
+        a.workload = "qwen7b8"
     if a.workload == "decode":
         out = bench_decode(a, torch, np, B, block, W)
     elif a.backward:
         out = bench_backward(a, torch, np, B, block, W)
     else:
         out = bench_block(a, torch, np, B, block, W)
+    if all_configs:
+        # the other configurations, each timed the same way (its own warmup
+        # and K steps), with its own roofline line and CPU baseline
+        out["configs"] = {}
+        for name, m in SUB_CONFIGS:
+            gc.collect()
+            torch.cuda.empty_cache()
+            sa = copy.copy(a)
+            sa.workload, sa.decode_m, sa.decode_arm = name, (m or a.decode_m), "split"
+            print(f"[bench] configuration {name}", file=sys.stderr, flush=True)
+            sub = bench_decode(sa, torch, np, B, block, W) if name == "decode" else \
+                bench_block(sa, torch, np, B, block, W)
+            out["configs"][name] = {k: sub[k] for k in SUB_KEYS if k in sub}
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
