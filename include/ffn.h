@@ -257,6 +257,24 @@ ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const v
                                     const uint8_t* w_down, const float* s_down,
                                     int64_t M, int64_t C, int64_t H, hipStream_t stream);
 
+/* ffn_decode_gemv_packed without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus the workspace),
+ * kernels and results as ffn_decode_gemv_packed; the workspace is a built-in
+ * device array of ffn_decode_noalloc_scratch_bytes() bytes (8 MiB) that every
+ * call on a device shares and that keeps the last call's contents (nothing in
+ * it needs to start at zero).  Calls that overlap on one device (on different
+ * streams, or from different threads) race on it; calls on one stream are
+ * ordered.  Sizes whose ffn_decode_packed_workspace_bytes exceed it give
+ * FFN_ERR_UNSUPPORTED.  The call allocates nothing: on its first use on a
+ * device it looks up the array's device address (hipGetSymbolAddress). */
+int64_t ffn_decode_noalloc_scratch_bytes(void);
+ffn_status_t ffn_decode_gemv_packed_noalloc(void* out, void* h, const void* x,
+                                            const uint8_t* w_gate, const float* s_gate,
+                                            const uint8_t* w_up, const float* s_up,
+                                            const uint8_t* w_down, const float* s_down,
+                                            int64_t M, int64_t C, int64_t H, hipStream_t stream);
+
 /* ------------------------------------------------------------------ backward
  * The FFN half of [llmq model] LLamaModel::_backward_block, as the calls it
  * is made of: backward_qmm through the down projection, swiglu_backward,

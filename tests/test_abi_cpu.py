@@ -162,7 +162,12 @@ def test_decode_packed_validation(lib):
     assert g(A, B, E, D, A, A, A, A, A, A, 16, 200, 768, None) == UNSUPPORTED      # C % 128
     assert g(A, B, MIS, D, A, A, A, A, A, A, 16, 256, 768, None) == UNSUPPORTED    # misaligned workspace
     assert g(A, B, E, D, A, None, A, A, A, A, 16, 256, 768, None) == INVALID       # no gate scales
-
+    n = lib.ffn_decode_gemv_packed_noalloc   # out, h, x, wg, sg, wu, su, wd, sd, M, C, H
+    assert lib.ffn_decode_noalloc_scratch_bytes() == 8 << 20
+    assert n(A, B, D, A, A, A, A, A, A, 16, 131072, 128, None) == UNSUPPORTED      # workspace beyond the scratch
+    assert "scratch" in _err(lib)
+    assert n(A, B, D, A, None, A, A, A, A, 16, 256, 768, None) == INVALID          # no gate scales
+    assert n(A, B, D, A, A, A, A, A, A, 33, 256, 768, None) == UNSUPPORTED         # M > 32
 
 
 def test_decode_arm_and_bf16_validation(lib):

@@ -18,7 +18,8 @@ _BINDING_NAMES = {
     "ffn_swiglu", "ffn_down",
     "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16", "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes",
-    "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
+    "ffn_decode_gemv_packed", "bind_decode_gemv_packed", "ffn_decode_noalloc_scratch_bytes",
+    "ffn_decode_gemv_packed_noalloc",
     "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "FFN_OK", "FFN_ERR_INVALID",

@@ -50,6 +50,7 @@ def _load():
         "ffn_decode_gemv_bf16": [P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_decode_pack_weight": [P, P, I64, I64, P],
         "ffn_decode_gemv_packed": [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
+        "ffn_decode_gemv_packed_noalloc": [P, P, P, P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_matmul_tn": [P, P, P, P, P, I32, I32, I64, I64, I64, P],
         "ffn_matmul_tn_swiglu_bwd": [P, P, P, P, P, P, P, I32, I32, I64, I64, I64, P],
         "ffn_transpose": [P, P, I64, I64, I64, I32, P],
@@ -65,6 +66,8 @@ def _load():
     lib.ffn_rmsnorm_bwd_scratch_bytes.restype = ctypes.c_int64
     lib.ffn_decode_packed_workspace_bytes.argtypes = [I64, I64, I64]
     lib.ffn_decode_packed_workspace_bytes.restype = ctypes.c_int64
+    lib.ffn_decode_noalloc_scratch_bytes.argtypes = []
+    lib.ffn_decode_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.ffn_last_error.restype = ctypes.c_char_p
     lib.ffn_last_error.argtypes = []
     lib.ffn_version.restype = ctypes.c_char_p
@@ -286,6 +289,21 @@ def bind_decode_gemv_packed(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down, s
                   _decode_packed_args(out, h, ws, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream))
 
 
+def ffn_decode_noalloc_scratch_bytes():
+    return int(_lib.ffn_decode_noalloc_scratch_bytes())
+
+
+def ffn_decode_gemv_packed_noalloc(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream=None):
+    """ffn_decode_gemv_packed with the library's built-in device scratch as
+    its workspace: no buffer beyond the inputs and outputs."""
+    _check(_lib.ffn_decode_gemv_packed_noalloc(
+        _ptr(out, "out", M * C, BF16), _ptr(h, "h", M * H, BF16), _ptr(x, "x", M * C, BF16),
+        _ptr(w_gate, "w_gate", H * C, E4M3), _ptr(s_gate, "s_gate", H, F32),
+        _ptr(w_up, "w_up", H * C, E4M3), _ptr(s_up, "s_up", H, F32),
+        _ptr(w_down, "w_down", C * H, E4M3), _ptr(s_down, "s_down", C, F32),
+        int(M), int(C), int(H), _stream(stream)))
+
+
 # ----------------------------------------------------------------------------- backward
 
 def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, flags, M, N, K, stream=None):
@@ -355,6 +373,7 @@ __all__ = [
     "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
     "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16", "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes",
+    "ffn_decode_noalloc_scratch_bytes", "ffn_decode_gemv_packed_noalloc",
     "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
     "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_rmsnorm_bwd_scratch_bytes",

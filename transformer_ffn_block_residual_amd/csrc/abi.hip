@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 
 #include "../../include/ffn.h"
 #include "launch.h"
@@ -42,6 +43,35 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
     } while (0)
 
 const int64_t kMaxDim = 1 << 20;
+
+// The workspace of ffn_decode_gemv_packed_noalloc: a fixed array in device
+// memory that every call on a device shares (each device holds its own copy
+// from the library's load until the process ends).  In host code the name
+// `scratch` is only a stand-in for the symbol: kernels are given its device
+// address, looked up once per device with hipGetSymbolAddress.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device; threads that race here store the same address).
+hipError_t scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -326,6 +356,33 @@ ffn_status_t ffn_decode_gemv_packed(void* out, void* h, void* workspace, const v
                                                 (const uint16_t*)x, w_gate, s_gate, w_up, s_up, w_down, s_down,
                                                 (int)M, (int)C, (int)H, stream),
                       "ffn_decode_gemv_packed");
+}
+
+int64_t ffn_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+ffn_status_t ffn_decode_gemv_packed_noalloc(void* out, void* h, const void* x, const uint8_t* w_gate,
+                                            const float* s_gate, const uint8_t* w_up, const float* s_up,
+                                            const uint8_t* w_down, const float* s_down, int64_t M, int64_t C,
+                                            int64_t H, hipStream_t stream) {
+    REQUIRE(s_gate);
+    REQUIRE(s_up);
+    REQUIRE(s_down);
+    if (ffn_status_t st =
+            check_decode("ffn_decode_gemv_packed_noalloc", out, h, x, w_gate, w_up, w_down, M, C, H, 1, 32))
+        return st;
+    const int64_t need = ffn::decode_packed_ws_elems((int)M, (int)C, (int)H) * 2;
+    if (need > kNoAllocScratchBytes)
+        return fail(FFN_ERR_UNSUPPORTED,
+                    "ffn_decode_gemv_packed_noalloc: M = %lld, C = %lld, H = %lld need %lld bytes of workspace, "
+                    "more than the %lld of the built-in scratch (use ffn_decode_gemv_packed)",
+                    (long long)M, (long long)C, (long long)H, (long long)need, (long long)kNoAllocScratchBytes);
+    if (M == 0) return FFN_OK;
+    void* ws = nullptr;
+    if (ffn_status_t st = hip_status(scratch_of_current_device(&ws), "ffn_decode_gemv_packed_noalloc")) return st;
+    return hip_status(ffn::launch_decode_packed((uint16_t*)out, (uint16_t*)h, (uint16_t*)ws, (const uint16_t*)x,
+                                                w_gate, s_gate, w_up, s_up, w_down, s_down, (int)M, (int)C, (int)H,
+                                                stream),
+                      "ffn_decode_gemv_packed_noalloc");
 }
 
 // ----------------------------------------------------------------------------- backward
