@@ -13,7 +13,14 @@
  *   - bf16 = IEEE binary32 truncated to 16 bits (round to nearest even);
  *     e4m3 = OCP E4M3FN (max 448, NaN 0x7F/0xFF, no infinities).
  *   - Abs-max outputs are OVERWRITTEN with max|x| of the tensor just written
- *     (the library clears them itself on `stream` first).
+ *     (the library clears them itself on `stream` first), except in the
+ *     calls whose names end in _acc, which max-accumulate into a word the
+ *     caller has zeroed (the convention of [llmq model] LLamaModel::forward:
+ *     the abs-max table is zeroed once and every producer accumulates into
+ *     its slot), and
+ *     ffn_quant_absmax_clear, which zeroes a slot for its next producer.
+ *     Abs-max is the maximum of |x| over the bit patterns, so a NaN element
+ *     makes it NaN (and every code of the tensor a NaN code).
  *   - A dequantisation scale is absmax/448 (1.0 when absmax == 0); codes are
  *     e4m3(x * (448/absmax)), with the product taken in fp32, rounded to
  *     nearest even and saturated at +-448.
@@ -98,6 +105,28 @@ ffn_status_t ffn_rmsnorm_fwd(void* y, float* rstd, void* residual_out, float* ab
 ffn_status_t ffn_quant_absmax(uint8_t* q, float* scale, float* absmax, const void* x,
                               int64_t n, int compute_absmax, hipStream_t stream);
 
+/* ffn_rmsnorm_fwd that max-accumulates max|y| into *absmax (required) as
+ * found, without clearing it first: the caller zeroes the word once (at
+ * allocation, or through ffn_quant_absmax_clear) rather than before every
+ * producer.  [llmq model] LLamaModel::forward zeroes the abs-max table once
+ * per forward (fill_zero) and every quantised tensor's producer accumulates
+ * into its slot.  Other arguments and results as ffn_rmsnorm_fwd. */
+ffn_status_t ffn_rmsnorm_fwd_acc(void* y, float* rstd, void* residual_out, float* absmax,
+                                 const void* inp, const void* addend, const void* weight,
+                                 float eps, int64_t N, int64_t C, hipStream_t stream);
+
+/* ffn_quant_absmax with the abs-max given (compute_absmax == 0) that also sets
+ * *clear = 0: the abs-max slot of a tensor whose consumer has run and whose
+ * producer (an _acc call) comes later on the stream.  [llmq model]
+ * LLamaModel::forward (the table's zeroing), forward_qmm
+ * (quantize_with_abs_max).  In the block's forward the quantiser of y clears
+ * h's slot and the quantiser of h clears y's slot for the next forward, so
+ * the table, zeroed once at allocation, needs no clearing launch.  clear must
+ * be a word other than scale and absmax.  Other arguments as
+ * ffn_quant_absmax. */
+ffn_status_t ffn_quant_absmax_clear(uint8_t* q, float* scale, const float* absmax, const void* x,
+                                    int64_t n, float* clear, hipStream_t stream);
+
 /* Per-row abs-max e4m3 quantisation of a bf16 weight [rows, cols]: the
  * QuantizedWeight { weight, row_scale } layout the FP8 decode consumes.
  * [metrale] DenseFfnLayer::forward, FP8 arm (gate_proj/up_proj/down_proj
@@ -124,6 +153,14 @@ ffn_status_t ffn_quant_rows(uint8_t* q, float* row_scale, const void* w,
 ffn_status_t ffn_gateup(void* out, float* out_absmax, const void* x, const float* x_scale,
                         const void* w, const float* w_scale, ffn_dtype_t dtype, int fuse_swiglu,
                         int64_t N, int64_t C, int64_t H, hipStream_t stream);
+
+/* ffn_gateup with the SwiGLU epilogue (fuse_swiglu = 1) that max-accumulates
+ * max|h| into *h_absmax (required) as found, as ffn_rmsnorm_fwd_acc does.
+ * h: bf16 [N, H]; other arguments as ffn_gateup; h_absmax must not alias the
+ * scales. */
+ffn_status_t ffn_gateup_acc(void* h, float* h_absmax, const void* x, const float* x_scale,
+                            const void* w, const float* w_scale, ffn_dtype_t dtype,
+                            int64_t N, int64_t C, int64_t H, hipStream_t stream);
 
 /* Fused gate+up projection with the SwiGLU epilogue storing e4m3 codes of h
  * quantised with an abs-max known beforehand (one pass instead of bf16 h, then

@@ -36,7 +36,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
+    for n in ["ffn_rmsnorm_fwd", "ffn_rmsnorm_fwd_acc", "ffn_quant_absmax", "ffn_quant_absmax_clear",
+              "ffn_quant_rows", "ffn_gateup", "ffn_gateup_acc", "ffn_gateup_swiglu_quant",
               "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16",
               "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes", "ffn_decode_gemv_packed",
               "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
@@ -77,6 +78,34 @@ def test_quant_validation(lib):
     g = lib.ffn_quant_rows
     assert g(A, A, A, 4, 12, None) == UNSUPPORTED
     assert g(A, None, A, 4, 16, None) == INVALID
+
+
+def test_absmax_accumulating_forms_validation(lib):
+    """The forms that accumulate into a caller-zeroed abs-max word, and the
+    quantiser that reads one word and zeroes another."""
+    f = lib.ffn_rmsnorm_fwd_acc
+    assert f(A, A, None, None, A, None, A, 1e-5, 4, 256, None) == INVALID        # no abs-max word
+    assert "absmax is NULL" in _err(lib)
+    assert f(None, A, None, A, A, None, A, 1e-5, 4, 256, None) == INVALID
+    assert "ffn_rmsnorm_fwd_acc: y is NULL" in _err(lib)
+    assert f(A, A, None, A, A, None, A, 1e-5, 4, 12, None) == UNSUPPORTED
+    q = lib.ffn_quant_absmax_clear          # q, scale, absmax, x, n, clear
+    B, C_, D = 0x20000, 0x30000, 0x40000
+    assert q(A, B, C_, A, 16, None, None) == INVALID                             # no word to clear
+    assert q(A, B, C_, A, 16, C_, None) == INVALID                               # clear aliases absmax
+    assert q(A, B, C_, A, 16, B, None) == INVALID                                # clear aliases scale
+    assert q(A, C_, C_, A, 16, D, None) == INVALID                               # scale aliases absmax
+    assert "three words" in _err(lib)
+    assert q(A, B, C_, A, -1, D, None) == INVALID
+    assert q(MIS, B, C_, A, 16, D, None) == UNSUPPORTED
+    g = lib.ffn_gateup_acc                  # h, h_absmax, x, xs, w, ws, dtype, N, C, H
+    assert g(A, None, A, None, A, None, 0, 64, 256, 768, None) == INVALID         # no abs-max word
+    assert g(A, B, A, None, A, None, 1, 64, 256, 768, None) == INVALID            # fp8 without scales
+    assert g(A, B, A, B, A, C_, 1, 64, 256, 768, None) == INVALID                 # abs-max aliases x_scale
+    assert "alias" in _err(lib)
+    assert g(A, B, A, None, A, None, 0, 64, 256, 100, None) == UNSUPPORTED        # H % 128
+    assert g(A, B, A, None, A, None, 0, 64, 200, 768, None) == UNSUPPORTED        # C % 128
+    assert g(MIS, B, A, None, A, None, 0, 64, 256, 768, None) == UNSUPPORTED
 
 
 def test_gemm_validation(lib):

@@ -15,7 +15,7 @@ synthetic inputs) and ``build`` import without the library.
 
 _BINDING_NAMES = {
     "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
-    "ffn_swiglu", "ffn_down",
+    "ffn_swiglu", "ffn_down", "ffn_rmsnorm_fwd_acc", "ffn_quant_absmax_clear", "ffn_gateup_acc",
     "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16", "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes",
     "ffn_decode_gemv_packed", "bind_decode_gemv_packed", "ffn_decode_noalloc_scratch_bytes",

@@ -39,6 +39,9 @@ def _load():
     P, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     sig = {
         "ffn_rmsnorm_fwd": [P, P, P, P, P, P, P, F32, I64, I64, P],
+        "ffn_rmsnorm_fwd_acc": [P, P, P, P, P, P, P, F32, I64, I64, P],
+        "ffn_quant_absmax_clear": [P, P, P, P, I64, P, P],
+        "ffn_gateup_acc": [P, P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_quant_absmax": [P, P, P, P, I64, I32, P],
         "ffn_quant_rows": [P, P, P, I64, I64, P],
         "ffn_gateup": [P, P, P, P, P, P, I32, I32, I64, I64, I64, P],
@@ -143,6 +146,23 @@ def ffn_quant_absmax(q, scale, absmax, x, n, compute_absmax, stream=None):
         _ptr(x, "x", n, BF16), int(n), int(bool(compute_absmax)), _stream(stream)))
 
 
+def ffn_rmsnorm_fwd_acc(y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C, stream=None):
+    """ffn_rmsnorm_fwd max-accumulating into a caller-zeroed abs-max word."""
+    _check(_lib.ffn_rmsnorm_fwd_acc(
+        _ptr(y, "y", N * C, BF16), _ptr(rstd, "rstd", N, F32),
+        _ptr(residual_out, "residual_out", N * C, BF16, optional=True),
+        _ptr(absmax, "absmax", 1, F32),
+        _ptr(inp, "inp", N * C, BF16), _ptr(addend, "addend", N * C, BF16, optional=True),
+        _ptr(weight, "weight", C, BF16), float(eps), int(N), int(C), _stream(stream)))
+
+
+def ffn_quant_absmax_clear(q, scale, absmax, x, n, clear, stream=None):
+    """Quantise with the given abs-max and zero the abs-max word `clear`."""
+    _check(_lib.ffn_quant_absmax_clear(
+        _ptr(q, "q", n, E4M3), _ptr(scale, "scale", 1, F32), _ptr(absmax, "absmax", 1, F32),
+        _ptr(x, "x", n, BF16), int(n), _ptr(clear, "clear", 1, F32), _stream(stream)))
+
+
 def ffn_quant_rows(q, row_scale, w, rows, cols, stream=None):
     _check(_lib.ffn_quant_rows(
         _ptr(q, "q", rows * cols, E4M3), _ptr(row_scale, "row_scale", rows, F32),
@@ -161,6 +181,17 @@ def ffn_gateup(out, out_absmax, x, x_scale, w, w_scale, dtype, fuse_swiglu, N, C
         _ptr(x, "x", N * C, _dt_elems(dtype)), _ptr(x_scale, "x_scale", 1, F32, optional=not fp8),
         _ptr(w, "w", 2 * H * C, _dt_elems(dtype)), _ptr(w_scale, "w_scale", 1, F32, optional=not fp8),
         int(dtype), int(bool(fuse_swiglu)), int(N), int(C), int(H), _stream(stream)))
+
+
+def ffn_gateup_acc(h, h_absmax, x, x_scale, w, w_scale, dtype, N, C, H, stream=None):
+    """ffn_gateup with the SwiGLU epilogue, max-accumulating into a
+    caller-zeroed abs-max word."""
+    fp8 = dtype == FFN_E4M3
+    _check(_lib.ffn_gateup_acc(
+        _ptr(h, "h", N * H, BF16), _ptr(h_absmax, "h_absmax", 1, F32),
+        _ptr(x, "x", N * C, _dt_elems(dtype)), _ptr(x_scale, "x_scale", 1, F32, optional=not fp8),
+        _ptr(w, "w", 2 * H * C, _dt_elems(dtype)), _ptr(w_scale, "w_scale", 1, F32, optional=not fp8),
+        int(dtype), int(N), int(C), int(H), _stream(stream)))
 
 
 def ffn_gateup_swiglu_quant(q, q_scale, h_absmax, h_absmax_known, x, x_scale, w, w_scale, dtype, N, C, H,
@@ -370,7 +401,7 @@ def ffn_rmsnorm_bwd(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absm
 
 
 __all__ = [
-    "ffn_rmsnorm_fwd", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
+    "ffn_rmsnorm_fwd", "ffn_rmsnorm_fwd_acc", "ffn_quant_absmax_clear", "ffn_gateup_acc", "ffn_quant_absmax", "ffn_quant_rows", "ffn_gateup", "ffn_gateup_swiglu_quant",
     "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16", "bind_decode_gemv",
     "bind_decode_gemv_arm", "bind_decode_gemv_bf16", "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes",
     "ffn_decode_noalloc_scratch_bytes", "ffn_decode_gemv_packed_noalloc",

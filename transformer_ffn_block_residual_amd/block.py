@@ -66,9 +66,13 @@ class PrefillBlock:
         self.r = _bf16(N, C)
         self.y = _bf16(N, C)
         self.rstd = _f32(N)
-        self.am_y = _f32(1)
+        # the abs-max table, zeroed once here: am_y and am_h in words 0 and 4
+        # (16 bytes apart); forward() overwrites them, forward_zero_once()
+        # accumulates into them and clears each after its consumer
+        self.am_tab = torch.zeros(8, dtype=torch.float32, device="cuda")
+        self.am_y = self.am_tab[0:1]
         self.h = _bf16(N, H)
-        self.am_h = _f32(1)
+        self.am_h = self.am_tab[4:5]
         self.out = _bf16(N, C)
         if self.fp8:
             self.qy, self.s_y = _u8(N, C), _f32(1)
@@ -106,6 +110,30 @@ class PrefillBlock:
         else:
             B.ffn_gateup(self.h, self.am_h, self.y, None, self.w_gu, None, B.FFN_BF16, 1, N, C, H, stream)
             B.ffn_down(self.out, self.h, None, self.w_d, None, B.FFN_BF16, N, H, C, stream)
+        return self.out
+
+    def forward_zero_once(self, inp, addend, stream=None):
+        """The same forward with the trainer's abs-max convention (llmq
+        llama_model.cpp, ``LLamaModel::forward``: the abs-max table is zeroed
+        once and every producer accumulates into its slot): the RMSNorm and
+        the gate+up epilogue accumulate into the table; the quantiser of y
+        clears h's slot and the quantiser of h clears y's slot, so the next
+        call finds both zero and no call clears a word with a launch of its
+        own.  Results equal forward()'s bit for bit.  Afterwards am_y reads 0
+        (cleared for the next call) and am_h holds max|h|.  The bf16 block has
+        no quantiser, so it takes no abs-max at all."""
+        N, C, H = self.N, self.C, self.H
+        r = self.r if addend is not None else None
+        if not self.fp8:
+            B.ffn_rmsnorm_fwd(self.y, self.rstd, r, None, inp, addend, self.w_norm, self.eps, N, C, stream)
+            B.ffn_gateup(self.h, None, self.y, None, self.w_gu, None, B.FFN_BF16, 1, N, C, H, stream)
+            B.ffn_down(self.out, self.h, None, self.w_d, None, B.FFN_BF16, N, H, C, stream)
+            return self.out
+        B.ffn_rmsnorm_fwd_acc(self.y, self.rstd, r, self.am_y, inp, addend, self.w_norm, self.eps, N, C, stream)
+        B.ffn_quant_absmax_clear(self.qy, self.s_y, self.am_y, self.y, N * C, self.am_h, stream)
+        B.ffn_gateup_acc(self.h, self.am_h, self.qy, self.s_y, self.w_gu, self.s_gu, B.FFN_E4M3, N, C, H, stream)
+        B.ffn_quant_absmax_clear(self.qh, self.s_h, self.am_h, self.h, N * H, self.am_y, stream)
+        B.ffn_down(self.out, self.qh, self.s_h, self.w_d, self.s_d, B.FFN_E4M3, N, H, C, stream)
         return self.out
 
     def forward_known_h_absmax(self, inp, addend, h_absmax_known, h_absmax_out, stream=None):

@@ -81,34 +81,43 @@ const char* ffn_last_error(void) { return g_err; }
 
 const char* ffn_version(void) { return "ffn-mi355x 0.1 (gfx950)"; }
 
+static ffn_status_t rmsnorm_entry(const char* fn, void* y, float* rstd, void* residual_out, float* absmax,
+                                  const void* inp, const void* addend, const void* weight, float eps, int64_t N,
+                                  int64_t C, hipStream_t stream, bool clear_absmax) {
+    if (!y) return fail(FFN_ERR_INVALID, "%s: y is NULL", fn);
+    if (!rstd) return fail(FFN_ERR_INVALID, "%s: rstd is NULL", fn);
+    if (!inp) return fail(FFN_ERR_INVALID, "%s: inp is NULL", fn);
+    if (!weight) return fail(FFN_ERR_INVALID, "%s: weight is NULL", fn);
+    if (N < 0 || C < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);
+    if (addend && !residual_out) return fail(FFN_ERR_INVALID, "%s: addend given without residual_out", fn);
+    if (!addend && residual_out) return fail(FFN_ERR_INVALID, "%s: residual_out given without addend", fn);
+    if (!(eps >= 0.0f)) return fail(FFN_ERR_INVALID, "%s: eps must be >= 0", fn);
+    if (C < 8 || C > 16384 || C % 8 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: C = %lld (need 8 <= C <= 16384, C %% 8 == 0)", fn, (long long)C);
+    if (N > (int64_t)1 << 31) return fail(FFN_ERR_UNSUPPORTED, "%s: N too large", fn);
+    if (misaligned(y) || misaligned(inp) || misaligned(addend) || misaligned(residual_out) || misaligned(weight))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
+    if (residual_out && (residual_out == y || residual_out == addend))
+        return fail(FFN_ERR_INVALID, "%s: residual_out may alias only inp", fn);
+    return hip_status(ffn::launch_rmsnorm((uint16_t*)y, rstd, (uint16_t*)residual_out, absmax,
+                                          (const uint16_t*)inp, (const uint16_t*)addend, (const uint16_t*)weight,
+                                          eps, N, (int)C, stream, clear_absmax),
+                      fn);
+}
+
 ffn_status_t ffn_rmsnorm_fwd(void* y, float* rstd, void* residual_out, float* absmax, const void* inp,
                              const void* addend, const void* weight, float eps, int64_t N, int64_t C,
                              hipStream_t stream) {
-    REQUIRE(y);
-    REQUIRE(rstd);
-    REQUIRE(inp);
-    REQUIRE(weight);
-    NONNEG(N);
-    NONNEG(C);
-    if (addend && !residual_out) return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: addend given without residual_out");
-    if (!addend && residual_out)
-        return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: residual_out given without addend");
-    if (!(eps >= 0.0f)) return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: eps must be >= 0");
-    if (C < 8 || C > 16384 || C % 8 != 0)
-        return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_fwd: C = %lld (need 8 <= C <= 16384, C %% 8 == 0)",
-                    (long long)C);
-    if (N > (int64_t)1 << 31) return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_fwd: N too large");
-    ALIGNED(y);
-    ALIGNED(inp);
-    ALIGNED(addend);
-    ALIGNED(residual_out);
-    ALIGNED(weight);
-    if (residual_out && (residual_out == y || residual_out == addend))
-        return fail(FFN_ERR_INVALID, "ffn_rmsnorm_fwd: residual_out may alias only inp");
-    return hip_status(ffn::launch_rmsnorm((uint16_t*)y, rstd, (uint16_t*)residual_out, absmax,
-                                          (const uint16_t*)inp, (const uint16_t*)addend, (const uint16_t*)weight,
-                                          eps, N, (int)C, stream),
-                      "ffn_rmsnorm_fwd");
+    return rmsnorm_entry("ffn_rmsnorm_fwd", y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C, stream,
+                         true);
+}
+
+ffn_status_t ffn_rmsnorm_fwd_acc(void* y, float* rstd, void* residual_out, float* absmax, const void* inp,
+                                 const void* addend, const void* weight, float eps, int64_t N, int64_t C,
+                                 hipStream_t stream) {
+    REQUIRE(absmax);
+    return rmsnorm_entry("ffn_rmsnorm_fwd_acc", y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C,
+                         stream, false);
 }
 
 ffn_status_t ffn_quant_absmax(uint8_t* q, float* scale, float* absmax, const void* x, int64_t n,
@@ -124,6 +133,24 @@ ffn_status_t ffn_quant_absmax(uint8_t* q, float* scale, float* absmax, const voi
     ALIGNED(x);
     return hip_status(ffn::launch_quant(q, scale, absmax, (const uint16_t*)x, n, compute_absmax != 0, stream),
                       "ffn_quant_absmax");
+}
+
+ffn_status_t ffn_quant_absmax_clear(uint8_t* q, float* scale, const float* absmax, const void* x, int64_t n,
+                                    float* clear, hipStream_t stream) {
+    REQUIRE(q);
+    REQUIRE(scale);
+    REQUIRE(absmax);
+    REQUIRE(x);
+    REQUIRE(clear);
+    NONNEG(n);
+    if ((const float*)scale == absmax || (const float*)clear == absmax || clear == scale)
+        return fail(FFN_ERR_INVALID, "ffn_quant_absmax_clear: scale, absmax and clear must be three words");
+    if (n > ((int64_t)1 << 36)) return fail(FFN_ERR_UNSUPPORTED, "ffn_quant_absmax_clear: n too large");
+    ALIGNED(q);
+    ALIGNED(x);
+    return hip_status(ffn::launch_quant(q, scale, const_cast<float*>(absmax), (const uint16_t*)x, n, false, stream,
+                                        clear),
+                      "ffn_quant_absmax_clear");
 }
 
 ffn_status_t ffn_quant_rows(uint8_t* q, float* row_scale, const void* w, int64_t rows, int64_t cols,
@@ -182,6 +209,35 @@ ffn_status_t ffn_gateup(void* out, float* out_absmax, const void* x, const float
     return hip_status(ffn::launch_gemm(out, out_absmax, x, x_scale, w, w_scale, dtype == FFN_E4M3, fuse_swiglu != 0,
                                        N, (int)C, (int)(2 * H), stream),
                       "ffn_gateup");
+}
+
+ffn_status_t ffn_gateup_acc(void* h, float* h_absmax, const void* x, const float* x_scale, const void* w,
+                            const float* w_scale, ffn_dtype_t dtype, int64_t N, int64_t C, int64_t H,
+                            hipStream_t stream) {
+    REQUIRE(h);
+    REQUIRE(h_absmax);
+    REQUIRE(x);
+    REQUIRE(w);
+    NONNEG(N);
+    NONNEG(C);
+    NONNEG(H);
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3)
+        return fail(FFN_ERR_INVALID, "ffn_gateup_acc: unknown dtype %d", (int)dtype);
+    if (dtype == FFN_E4M3) {
+        REQUIRE(x_scale);
+        REQUIRE(w_scale);
+    }
+    if (h_absmax == x_scale || h_absmax == w_scale)
+        return fail(FFN_ERR_INVALID, "ffn_gateup_acc: h_absmax must not alias x_scale or w_scale");
+    const int elt = dtype == FFN_E4M3 ? 1 : 2;
+    if (ffn_status_t st = check_gemm_dims("ffn_gateup_acc", N, C, 2 * H, elt)) return st;
+    if (H % 128 != 0) return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup_acc: H = %lld must be a multiple of 128", (long long)H);
+    ALIGNED(h);
+    ALIGNED(x);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(h, h_absmax, x, x_scale, w, w_scale, dtype == FFN_E4M3, true, N, (int)C,
+                                       (int)(2 * H), stream, nullptr, nullptr, false, false, nullptr, false, false),
+                      "ffn_gateup_acc");
 }
 
 ffn_status_t ffn_gateup_swiglu_quant(uint8_t* q, float* q_scale, float* h_absmax, const float* h_absmax_known,

@@ -690,6 +690,8 @@ static int persistent_grid(int T) {
 }
 
 // Abs-max of a plain (unfused) GEMM output, when asked for: a separate pass.
+// clear_absmax == false (fused epilogues only): the abs-max is max-accumulated
+// into the word as found (the caller zeroed it) instead of cleared first.
 // q_absmax / q_scale (SwiGLU only, both or neither): store e4m3 codes of h
 // under that known abs-max instead of bf16 h, and its scale.  x_e5m2 (fp8,
 // plain output): x holds e5m2 codes.  swiglu_gu (plain output, no
@@ -701,11 +703,11 @@ static int persistent_grid(int T) {
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2,
-                       const void* swiglu_gu, bool tile_grid) {
+                       const void* swiglu_gu, bool tile_grid, bool clear_absmax) {
     if (x_e5m2 && (!fp8 || fuse_swiglu)) return hipErrorInvalidValue;
     const bool swi = swiglu_gu != nullptr;
     if (swi && (fuse_swiglu || accumulate)) return hipErrorInvalidValue;
-    if (absmax && (fuse_swiglu || swi || N == 0)) {
+    if (absmax && (fuse_swiglu || swi || N == 0) && clear_absmax) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
     }

@@ -10,11 +10,15 @@ namespace ffn {
 hipError_t launch_fill(float* p, int n, float v, hipStream_t s);
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();
+// clear_absmax == false: *absmax is max-accumulated into as found (the
+// caller zeroed it), not cleared first.
 hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
-                          const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s);
+                          const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s,
+                          bool clear_absmax = true);
 hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_t s);
+// clear (nullable): another abs-max word that the kernel sets to zero.
 hipError_t launch_quant(uint8_t* q, float* scale, float* absmax, const uint16_t* x, int64_t n, bool compute,
-                        hipStream_t s);
+                        hipStream_t s, float* clear = nullptr);
 hipError_t launch_quant_rows(uint8_t* q, float* row_scale, const uint16_t* w, int64_t rows, int cols,
                              hipStream_t s);
 hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t N, int H, hipStream_t s);
@@ -33,7 +37,7 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr,
                        bool accumulate = false, bool x_e5m2 = false, const void* swiglu_gu = nullptr,
-                       bool tile_grid = false);
+                       bool tile_grid = false, bool clear_absmax = true);
 
 // Backward: out[c, r] = in[r, c], zero for rows <= r < ld_out.  (in_bytes,
 // out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3

@@ -116,8 +116,9 @@ static void launch_rmsnorm_cpl(uint16_t* y, float* rstd, uint16_t* res, float* a
 }
 
 hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
-                          const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s) {
-    if (absmax) {
+                          const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s,
+                          bool clear_absmax) {
+    if (absmax && clear_absmax) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
     }
@@ -166,14 +167,19 @@ __global__ __launch_bounds__(256) void absmax_kernel(float* out, const uint16_t*
 // Per-tensor e4m3 quantisation with a known abs-max (llmq llama_model.cpp,
 // forward_qmm, quantize_with_abs_max).  16 elements per thread: two 16-byte
 // loads, one 16-byte store.  inv = 448/absmax in IEEE fp32; codes from the fp32
-// product x*inv.  Block 0 also writes the scale absmax/448.
+// product x*inv.  Block 0 also writes the scale absmax/448 and, when given,
+// zero to *clear (another tensor's abs-max word, for its next producer).
 
 __global__ __launch_bounds__(256) void quant_kernel(uint8_t* __restrict__ q, float* __restrict__ scale_out,
                                                     const float* __restrict__ absmax,
-                                                    const uint16_t* __restrict__ x, int64_t n) {
+                                                    const uint16_t* __restrict__ x, int64_t n,
+                                                    float* __restrict__ clear) {
     float scale, inv;
     scale_pair(*absmax, scale, inv);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = scale;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *scale_out = scale;
+        if (clear) *clear = 0.0f;
+    }
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t base = t * 16;
     if (base + 16 <= n) {
@@ -207,14 +213,14 @@ hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_
 }
 
 hipError_t launch_quant(uint8_t* q, float* scale, float* absmax, const uint16_t* x, int64_t n, bool compute,
-                        hipStream_t s) {
+                        hipStream_t s, float* clear) {
     if (compute) {
         hipError_t e = launch_absmax(absmax, x, n, s);
         if (e != hipSuccess) return e;
     }
     const int64_t threads = (n + 15) / 16;
     const int64_t blocks = threads > 0 ? (threads + 255) / 256 : 1;  // n == 0 still writes the scale
-    hipLaunchKernelGGL(quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, absmax, x, n);
+    hipLaunchKernelGGL(quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, absmax, x, n, clear);
     return hipGetLastError();
 }
 
