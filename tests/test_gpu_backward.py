@@ -535,6 +535,49 @@ def test_block_backward_accumulates_weight_gradients(F):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_block_backward_remakes_weight_transposes_after_a_weight_update(F, fp8):
+    """The transposed weights are cached across backward calls; new weights
+    (load_weights, or an in-place update declared with weights_changed) must
+    be seen by the next backward exactly as by a block built with them."""
+    say(f"block backward after a weight update fp8={fp8}")
+    from transformer_ffn_block_residual_amd import block
+    N, C, H = 96, 256, 384
+    d1 = W.block_inputs(N, C, H, seed=21, w_std=0.1)
+    d2 = W.block_inputs(N, C, H, seed=22, w_std=0.1)
+    d_out = dev_bf16(rand_bits((N, C), 1.0, 23))
+    inp, add = dev_bf16(d1["inp"]), dev_bf16(d1["addend"])
+
+    def grads(bb):
+        bb.zero_grads()
+        bb.forward(inp, add)
+        bb.backward(d_out)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (bb.d_res, bb.dw_d, bb.dw_gu, bb.dw_norm)]
+
+    pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
+    pb.load_weights(d1["w_norm"], d1["w_gu"], d1["w_d"])
+    bb = block.BackwardBlock(pb)
+    grads(bb)
+    pb.load_weights(d2["w_norm"], d2["w_gu"], d2["w_d"])
+    got = grads(bb)
+    fresh_pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
+    fresh_pb.load_weights(d2["w_norm"], d2["w_gu"], d2["w_d"])
+    want = grads(block.BackwardBlock(fresh_pb))
+    for a, b in zip(got, want):
+        assert torch.equal(a, b)
+    if fp8:
+        return
+    # an in-place update of the bf16 weights, declared
+    for t in (pb.w_gu, pb.w_d, fresh_pb.w_gu, fresh_pb.w_d):
+        t.mul_(0.5)
+    pb.weights_changed()
+    got = grads(bb)
+    want = grads(block.BackwardBlock(fresh_pb))
+    for a, b in zip(got, want):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 def test_block_backward_out_of_place_and_given_absmax(F, fp8):
     say(f"block backward out of place fp8={fp8}")
     from transformer_ffn_block_residual_amd import block

@@ -30,7 +30,9 @@ projection, ``swiglu_backward``, ``backward_qmm`` through the up projection and
 ``rmsnorm_backward`` (llmq llama_model.cpp, ``LLamaModel::_backward_block``,
 ``backward_qmm``).  The transposed operands that the TN products need are made
 by ``ffn_transpose`` / ``ffn_quant_transpose`` with the token dimension padded
-to a multiple of 128 (zeros), the GEMM's K granularity.
+to a multiple of 128 (zeros), the GEMM's K granularity.  The transposed
+weights are made once per weight update (``PrefillBlock.weights_version``) and
+reused by every backward until the weights change again.
 
 Buffers are allocated once, at construction, through torch; the calls
 themselves allocate nothing.  Every step of the arithmetic runs in libffn.so.
@@ -77,10 +79,19 @@ class PrefillBlock:
         if self.fp8:
             self.qy, self.s_y = _u8(N, C), _f32(1)
             self.qh, self.s_h = _u8(N, H), _f32(1)
+        # bumped whenever the projection weights change; what is derived from
+        # them (the backward's transposed weights) is remade when it moves
+        self.weights_version = 0
+
+    def weights_changed(self):
+        """Declare that the projection weights were updated in place (an
+        optimizer step), so that what is derived from them is remade."""
+        self.weights_version += 1
 
     def load_weights(self, w_norm, w_gu, w_d):
         """Device bf16 weights (tensors or host bit-pattern arrays).  For FP8 the
         projections are quantised here, per tensor, with their own abs-max."""
+        self.weights_changed()
         as_dev = (lambda w: w if isinstance(w, torch.Tensor) else _bf16_dev(w))
         self.w_norm = as_dev(w_norm)
         w_gu, w_d = as_dev(w_gu), as_dev(w_d)
@@ -304,6 +315,7 @@ class BackwardBlock:
         self.fuse_swiglu_bwd = fuse_swiglu_bwd
         self.concurrent = concurrent
         self._side = None   # the second stream, made on first use (default priority)
+        self._wt_version = None   # weights_version the transposed weights were made from
         self.f = fwd
         N, C, H = fwd.N, fwd.C, fwd.H
         self.Np = _round_up(max(N, 1), 128)
@@ -333,6 +345,20 @@ class BackwardBlock:
         self.dw_d.zero_()
         self.dw_gu.zero_()
         self.dw_norm.zero_()
+
+    def _weight_transposes(self, stream, mk):
+        """W_down^T [H, C] and W_gu^T [C, 2H] (the codes for FP8), the b
+        operands of the two data gradients, made only when the weights have
+        changed since they were last made (backward_qmm transposes its
+        weight on every call; within one weight update they do not change)."""
+        f = self.f
+        if self._wt_version == f.weights_version:
+            return
+        e = 1 if f.fp8 else 2
+        B.ffn_transpose(self.wd_t, f.w_d, f.C, f.H, f.C, e, stream)
+        B.ffn_transpose(self.wgu_t, f.w_gu, 2 * f.H, f.C, 2 * f.H, e, stream)
+        self._wt_version = f.weights_version
+        mk("transpose_weights")
 
     def forward(self, inp, addend, stream=None):
         """The block forward with the up-projection output kept: RMSNorm,
@@ -369,6 +395,7 @@ class BackwardBlock:
         N, C, H, Np = f.N, f.C, f.H, self.Np
         dgu = self.dgu
         mk = mark or (lambda label: None)
+        self._weight_transposes(stream, mk)
         if f.fp8:
             # gradient codes (the TN matmuls' a operand) in the grad dtype
             E = B.FFN_E5M2 if self.grad_dtype == "e5m2" else B.FFN_E4M3
@@ -380,8 +407,6 @@ class BackwardBlock:
                 self.am_dout = d_out_absmax
             B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, stream, E)
             mk("quant_dout")
-            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, stream)
-            mk("transpose_w_down")
             if self.fuse_swiglu_bwd:
                 B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, self.qdout, self.s_dout, self.wd_t, f.s_d, self.gu,
                                            E, N, H, C, stream)
@@ -399,8 +424,6 @@ class BackwardBlock:
             # backward_qmm through the up projection (input y, weight [2H, C])
             B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream, E)
             mk("quant_dgu")
-            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 1, stream)
-            mk("transpose_w_up")
             B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, 0, N, C, 2 * H, stream)
             mk("dx_up")
             B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, stream)
@@ -409,8 +432,6 @@ class BackwardBlock:
             mk("dw_up")
         else:
             Bf = B.FFN_BF16
-            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 2, stream)
-            mk("transpose_w_down")
             if self.fuse_swiglu_bwd:
                 B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, d_out, None, self.wd_t, None, self.gu, Bf, N, H, C,
                                            stream)
@@ -426,8 +447,6 @@ class BackwardBlock:
             if not self.fuse_swiglu_bwd:
                 B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
                 mk("swiglu_bwd")
-            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 2, stream)
-            mk("transpose_w_up")
             B.ffn_matmul_tn(self.dy, dgu, None, self.wgu_t, None, Bf, 0, N, C, 2 * H, stream)
             mk("dx_up")
             B.ffn_transpose(self.dgu_t, dgu, N, 2 * H, Np, 2, stream)
@@ -462,6 +481,8 @@ class BackwardBlock:
             self._ev[k].record(main)
             side.wait_event(self._ev[k])
 
+        self._weight_transposes(main, lambda label: None)
+
         if f.fp8:
             E = B.FFN_E5M2 if self.grad_dtype == "e5m2" else B.FFN_E4M3
             if d_out_absmax is None:
@@ -469,7 +490,6 @@ class BackwardBlock:
             else:
                 self.am_dout = d_out_absmax
             B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, main, E)
-            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 1, main)
             fork(0)
             B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, side)
             B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, ACC | T, C, H, Np, side)
@@ -480,14 +500,12 @@ class BackwardBlock:
                 B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, T, N, H, C, main)
                 B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, main)
             B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, main, E)
-            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 1, main)
             fork(1)
             B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, side)
             B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, ACC | T, 2 * H, C, Np, side)
             B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, T, N, C, 2 * H, main)
         else:
             Bf = B.FFN_BF16
-            B.ffn_transpose(self.wd_t, f.w_d, C, H, C, 2, main)
             fork(0)
             B.ffn_transpose(self.dout_t, d_out, N, C, Np, 2, side)
             B.ffn_transpose(self.h_t, f.h, N, H, Np, 2, side)
@@ -498,7 +516,6 @@ class BackwardBlock:
             else:
                 B.ffn_matmul_tn(self.dh, d_out, None, self.wd_t, None, Bf, T, N, H, C, main)
                 B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, main)
-            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * H, C, 2 * H, 2, main)
             fork(1)
             B.ffn_transpose(self.dgu_t, dgu, N, 2 * H, Np, 2, side)
             B.ffn_transpose(self.y_t, f.y, N, C, Np, 2, side)
