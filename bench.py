@@ -127,15 +127,17 @@ def measured_traffic(key, src):
         return None
 
 
-# dominant kernel per workload: traffic.json key, its source file, the kernel
-# name fragments whose per-dispatch counters make up one launch of the entry
-# point, and the algorithmic bytes of that launch
-def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3"):
-    """(traffic.json key, source file, kernel-name fragments of one launch,
-    description, algorithmic bytes of one launch, dispatch stride) for the
-    dominant kernel.  A stride of 2 takes every second matching dispatch
-    (starting with the second): the backward's two weight-gradient GEMMs share
-    one kernel, and the up projection's is the second of each step."""
+# kernels with counter entries per workload: traffic.json key, source file,
+# the kernel name fragments whose per-dispatch counters make up one launch of
+# the entry point, which dispatches are that launch, and its algorithmic bytes
+def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3"):
+    """[(traffic.json key, source file, kernel-name fragments of one launch,
+    description, algorithmic bytes of one launch, (skip, stride, offset))],
+    the dominant kernel first.  Matching dispatches are taken from the
+    skip-th on, every stride-th from offset: the backward's two
+    weight-gradient GEMMs share one kernel (the up projection's is the second
+    of each step), and the forward's two activation quantisations share one
+    kernel after the two weight quantisations of the set-up."""
     from transformer_ffn_block_residual_amd import workloads as W
     w = W.WORKLOADS[workload]
     N, C, H = w.N, w.C, w.H
@@ -145,64 +147,97 @@ def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m
         e5 = w.fp8 and grad_dtype == "e5m2"
         what = ("e5m2 x e4m3" if e5 else "e4m3") if w.fp8 else "bf16"
         # reads dgu^T [2H, N] and y^T [C, N] once, reads and writes dW_gu [2H, C]
-        return (f"dwup{'5' if e5 else ''}_{workload}", "gemm.hip",
-                [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}, false>"],
-                f"gemm_kernel ({what}, accumulating) of the up projection's weight "
-                f"gradient, [2H, C] = [{2 * H}, {C}], K = N = {N}",
-                2 * H * N * e + C * N * e + 2 * (2 * H * C * 2), 2)
+        return [(f"dwup{'5' if e5 else ''}_{workload}", "gemm.hip",
+                 [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}, false>"],
+                 f"gemm_kernel ({what}, accumulating) of the up projection's weight "
+                 f"gradient, [2H, C] = [{2 * H}, {C}], K = N = {N}",
+                 2 * H * N * e + C * N * e + 2 * (2 * H * C * 2), (0, 2, 1))]
     if workload == "decode":
-        return ("decode_decode", "decode.hip", ["gemv_small_kernel<0, false, 1,", "gemv_small_kernel<2, false, 1,"],
-                f"gemv_small_kernel<dual SiLU> + gemv_small_kernel<single> (one ffn_decode_gemv), M=1 C={C} H={H}",
-                3 * H * C + (2 * H + C) * 4 + 2 * (C + H) * 2, 1)
+        return [("decode_decode", "decode.hip", ["gemv_small_kernel<0, false, 1,", "gemv_small_kernel<2, false, 1,"],
+                 f"gemv_small_kernel<dual SiLU> + gemv_small_kernel<single> (one ffn_decode_gemv), M=1 C={C} H={H}",
+                 3 * H * C + (2 * H + C) * 4 + 2 * (C + H) * 2, (0, 1, 0))]
     elt = 1 if w.fp8 else 2
     fp8 = "true" if w.fp8 else "false"
+    dt = "e4m3" if w.fp8 else "bf16"
+    every = (0, 1, 0)
     if known_h_absmax:
         # reads x and w, writes the e4m3 codes of h
-        return (f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false, false, false>"],
-                f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation) of ffn_gateup_swiglu_quant, "
-                f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, 1)
-    return (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false, false>"],
-            f"gemm_kernel ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
-            N * C * elt + 2 * H * C * elt + N * H * 2, 1)
+        return [(f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false, false, false>"],
+                 f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation) of ffn_gateup_swiglu_quant, "
+                 f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, every)]
+    specs = [
+        (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false, false>"],
+         f"gemm_kernel ({dt}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
+         N * C * elt + 2 * H * C * elt + N * H * 2, every),
+        (f"down_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, false, false, false, false, false>"],
+         f"gemm_kernel ({dt}) of ffn_down, N={N} H={H} C={C}",
+         N * H * elt + C * H * elt + N * C * 2, every),
+        # reads inp and addend, writes r and y, rstd; the weight once
+        (f"rmsnorm_{workload}", "norm_quant.hip", ["rmsnorm_kernel<"],
+         f"rmsnorm_kernel (residual add + RMSNorm + rstd{' + abs-max' if w.fp8 else ''}) of ffn_rmsnorm_fwd, "
+         f"N={N} C={C}",
+         4 * N * C * 2 + N * 4 + C * 2, every),
+    ]
+    if w.fp8:
+        specs += [(f"quant_{t}_{workload}", "norm_quant.hip", ["quant_kernel("],
+                   f"quant_kernel (per-tensor e4m3 with a given abs-max) of {t}, {N} x {K}",
+                   3 * N * K, (2, 2, o)) for t, K, o in (("y", C, 0), ("h", H, 1))]
+    if w.decode_M:
+        M = w.decode_M
+        specs.append((f"decode{M}_{workload}", "decode.hip",
+                      ["decode_dual_wave_kernel<", "decode_down_split_kernel<", "decode_down_reduce_kernel("],
+                      f"decode_dual_wave_kernel + decode_down_split_kernel + decode_down_reduce_kernel (one "
+                      f"ffn_decode_gemv_packed), M={M} C={C} H={H}",
+                      3 * H * C + (2 * H + C) * 4 + 2 * M * (C + H) * 2, every))
+    return specs
+
+
+def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3"):
+    """The dominant kernel's entry of traffic_specs."""
+    return traffic_specs(workload, known_h_absmax, backward, grad_dtype)[0]
 
 
 def ingest_pmc(a):
-    """HBM bytes per launch of the workload's dominant kernel from two
+    """HBM bytes per launch of the workload's kernels (traffic_specs) from two
     rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
     scaled by what the counter reads for the 1 GiB calibration copy."""
     import csv
-    key, src, frags, desc, algo, stride = traffic_spec(a.workload, a.known_h_absmax, a.backward, a.grad_dtype)
-    rec = {"kernel": desc, "src": f"transformer_ffn_block_residual_amd/csrc/{src}", "src_sha256": src_digest(src)}
-    total = 0.0
-    for counter, path, truth_kb in (("FETCH_SIZE", a.ingest_pmc[0], 1 << 20), ("WRITE_SIZE", a.ingest_pmc[1], 1 << 20)):
+    tables = {}
+    for counter, path in (("FETCH_SIZE", a.ingest_pmc[0]), ("WRITE_SIZE", a.ingest_pmc[1])):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         if not copies:
             raise SystemExit(f"{path}: no calibration copy (run bench.py with --copy-calibration)")
-        factor = truth_kb / max(copies)
-        per_launch = 0.0
-        for f in frags:
-            vals = [float(r["Counter_Value"]) for r in rows if f in r["Kernel_Name"]]
-            vals = vals[stride - 1::stride]
-            if not vals:
-                raise SystemExit(f"{path}: no dispatch of {f}")
-            per_launch += sum(vals) / len(vals)
-        tag = counter.split("_")[0].lower()
-        rec[f"{tag}_kb_raw"] = per_launch
-        rec[f"{tag}_factor"] = factor
-        total += per_launch * factor * 1024
-    rec["bytes_per_launch"] = total
-    rec["algorithmic_bytes"] = algo
+        tables[counter] = (rows, (1 << 20) / max(copies))
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         data = {}
-    data[key] = rec
+    for key, src, frags, desc, algo, (skip, stride, offset) in traffic_specs(a.workload, a.known_h_absmax,
+                                                                             a.backward, a.grad_dtype):
+        rec = {"kernel": desc, "src": f"transformer_ffn_block_residual_amd/csrc/{src}",
+               "src_sha256": src_digest(src)}
+        total = 0.0
+        for counter, (rows, factor) in tables.items():
+            per_launch = 0.0
+            for f in frags:
+                vals = [float(r["Counter_Value"]) for r in rows if f in r["Kernel_Name"]]
+                vals = vals[skip:][offset::stride]
+                if not vals:
+                    raise SystemExit(f"no dispatch of {f} with {counter}")
+                per_launch += sum(vals) / len(vals)
+            tag = counter.split("_")[0].lower()
+            rec[f"{tag}_kb_raw"] = per_launch
+            rec[f"{tag}_factor"] = factor
+            total += per_launch * factor * 1024
+        rec["bytes_per_launch"] = total
+        rec["algorithmic_bytes"] = algo
+        data[key] = rec
+        print(json.dumps({key: rec}))
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
-    print(json.dumps({key: rec}))
     return 0
 
 
@@ -531,6 +566,16 @@ def bench_block(a, torch, np, B, block, W):
         kernels["decode"] = {"ms": km["decode"], "GB/s": dec_bytes / km["decode"] / 1e6,
                              "frac_hbm": dec_bytes / km["decode"] / 1e6 / PEAK_HBM_GBS}
         flops += 6.0 * M * C * H
+    # HBM-side bytes per launch from the committed counter runs, where the
+    # kernel's source is unchanged since they were taken
+    names = {"gateup": "gateup_swiglu", "gateupq": "gateup_swiglu", "down": "down", "rmsnorm": "rmsnorm_fwd",
+             "quant_y": "quant_y", "quant_h": "quant_h", f"decode{M}": "decode"}
+    for key, src, _, _, algo, _ in traffic_specs(a.workload, known):
+        name = names.get(key[:-len(a.workload) - 1])
+        if name in kernels:
+            t = measured_traffic(key, src)
+            kernels[name]["traffic"] = t
+            kernels[name]["traffic_over_algorithmic"] = None if t is None else t / algo
     out = {
         "metric": METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
