@@ -80,6 +80,9 @@ def parse():
     p.add_argument("--decode-layout", default="auto", choices=["auto", "rows", "packed"],
                    help="FP8 decode weights: row-major (ffn_decode_gemv) or the packed decode layout "
                         "(ffn_decode_gemv_packed); auto: packed from 5 tokens on, row-major below")
+    p.add_argument("--decode-at", default="end", choices=["end", "start", "mid"],
+                   help="qwen7b8: where the decode runs in the step's one stream: after the down GEMM, "
+                        "before the RMSNorm, or between the quantisation of y and the gate+up GEMM")
     p.add_argument("--decode-overlap", default="none", choices=["none", "tail", "start"],
                    help="qwen7b8: where the step's decode runs.  none: after the down GEMM on the same stream; "
                         "tail: on a second stream from the end of the h quantisation on, beside the down GEMM "
@@ -468,10 +471,21 @@ def bench_block(a, torch, np, B, block, W):
             tm.add("decode", d0, tm.mark(side))
         join_ev.record(side)
 
+    serial_at = a.decode_at if (M and overlap == "none") else None
+
+    def decode_serial(i, tm, stream):
+        d0 = tm.mark() if tm else None
+        decs[i % DECODE_COPIES].forward(x_dec, M, stream)
+        d1 = tm.mark() if tm else None
+        if tm:
+            tm.add("decode", d0, d1)
+        return d1
+
     def step(i, tm, stream=stream):
-        m0 = tm.mark() if tm else None
+        first = tm.mark() if tm else None
         if overlap == "start":
             decode_on_side(i, tm, stream)
+        m0 = decode_serial(i, tm, stream) if serial_at == "start" else first
         # the abs-max words follow the zero-once convention: the FP8 chain
         # accumulates into words that the previous consumer cleared, so no
         # launch in the step exists only to clear one; bf16 takes no abs-max
@@ -495,6 +509,9 @@ def bench_block(a, torch, np, B, block, W):
         elif w.fp8:
             B.ffn_quant_absmax_clear(pre.qy, pre.s_y, pre.am_y, pre.y, N * C, pre.am_h, stream)
             m2 = tm.mark() if tm else None
+            m2q = m2
+            if serial_at == "mid":
+                m2 = decode_serial(i, tm, stream)
             B.ffn_gateup_acc(pre.h, pre.am_h, pre.qy, pre.s_y, pre.w_gu, pre.s_gu, E, N, C, H, stream)
             m3 = tm.mark() if tm else None
             B.ffn_quant_absmax_clear(pre.qh, pre.s_h, pre.am_h, pre.h, N * H, pre.am_y, stream)
@@ -504,6 +521,8 @@ def bench_block(a, torch, np, B, block, W):
             B.ffn_down(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, E, N, H, C, stream)
         else:
             m2 = m1
+            if serial_at == "mid":
+                m2 = decode_serial(i, tm, stream)
             B.ffn_gateup(pre.h, None, pre.y, None, pre.w_gu, None, E, 1, N, C, H, stream)
             m3 = tm.mark() if tm else None
             m4 = m3
@@ -513,18 +532,17 @@ def bench_block(a, torch, np, B, block, W):
         if overlap == "tail":
             decode_on_side(i, tm, stream, forked=True)
         m5 = tm.mark() if tm else None
-        if M and overlap == "none":
-            decs[i % DECODE_COPIES].forward(x_dec, M, stream)
-        elif M:
+        last = m5
+        if serial_at == "end":
+            last = decode_serial(i, tm, stream)
+        elif M and overlap != "none":
             stream.wait_event(join_ev)
-        m6 = tm.mark() if (tm and M) else None
-        if tm and M and overlap == "none":
-            tm.add("decode", m5, m6)
+            last = tm.mark() if tm else None
         if tm:
-            tm.add("step", m0, m6 if M else m5)
+            tm.add("step", first, last)
             tm.add("rmsnorm", m0, m1)
             if w.fp8:
-                tm.add("quant_y", m1, m2)
+                tm.add("quant_y", m1, m2q if (w.fp8 and not known) else m2)
                 if not known:
                     tm.add("quant_h", m3, m4)
             tm.add("gateup", m2, m3)
@@ -556,8 +574,8 @@ def bench_block(a, torch, np, B, block, W):
                         "prefill8": "llama-shaped FFN block, FP8: prefill N=4096 C=4096 H=14336 eps=1e-5, "
                                     "0.1% x50 outliers"}[a.workload],
            "N": N, "C": C, "H": H, "decode_M": M, "seed": w.seed,
-           **({"decode_overlap": overlap, "decode_layout": "packed" if decode_packed(a, M) else "rows"}
-              if M else {}),
+           **({"decode_overlap": overlap, "decode_at": serial_at,
+               "decode_layout": "packed" if decode_packed(a, M) else "rows"} if M else {}),
            "quant": ("per-tensor abs-max e4m3 activations and weights" if w.fp8 else "none (bf16)")
            + ("; h quantised in the gate+up epilogue with the previous step's abs-max" if known else "")
            + ("; decode: e4m3 weights, per-row fp32 scales, bf16 activations" if M else "")}
