@@ -79,7 +79,7 @@ def parse():
                    help="block workloads: time the FFN block backward (after one forward) instead of the forward")
     p.add_argument("--decode-layout", default="auto", choices=["auto", "rows", "packed"],
                    help="FP8 decode weights: row-major (ffn_decode_gemv) or the packed decode layout "
-                        "(ffn_decode_gemv_packed); auto: packed from 5 tokens on, row-major below")
+                        "(ffn_decode_gemv_packed); auto: packed from 4 tokens on, row-major below")
     p.add_argument("--decode-at", default="end", choices=["end", "start", "mid"],
                    help="qwen7b8: where the decode runs in the step's one stream: after the down GEMM, "
                         "before the RMSNorm, or between the quantisation of y and the gate+up GEMM")
@@ -414,7 +414,7 @@ def run_steps(torch, stream, step, a, marks_per_step=8):
 
 def decode_packed(a, M):
     """Whether the FP8 split-SiLU decode of M tokens runs on packed weights."""
-    return a.decode_layout == "packed" or (a.decode_layout == "auto" and M >= 5)
+    return a.decode_layout == "packed" or (a.decode_layout == "auto" and M >= 4)
 
 
 def bench_block(a, torch, np, B, block, W):
