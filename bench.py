@@ -860,7 +860,8 @@ def bench_decode(a, torch, np, B, block, W):
 
 # the per-configuration figures of the default run: (workload, decode tokens)
 SUB_CONFIGS = (("decode", 1), ("prefill", 0), ("prefill8", 0))
-SUB_KEYS = ("metric", "value", "unit", "ms_per_step", "dtype", "config", "roofline", "kernels", "cpu_baseline")
+SUB_KEYS = ("metric", "value", "unit", "ms_per_step", "dtype", "config", "roofline", "kernels", "spread_ms",
+            "ms_per_step_in_hip_graph", "ms_in_hip_graph", "cpu_baseline")
 
 
 def main():
