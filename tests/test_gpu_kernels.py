@@ -308,7 +308,8 @@ def test_same_e4m3_operands_through_both_mfma_paths(F, N, Kd, O):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("N,C,H", [(64, 256, 768), (300, 512, 384), (1100, 256, 7680)])
+# (256, 4096, 1792): the gate+up shape of one GPU's share under 8-way tensor parallelism
+@pytest.mark.parametrize("N,C,H", [(64, 256, 768), (300, 512, 384), (1100, 256, 7680), (256, 4096, 1792)])
 def test_gateup_random_and_fused_equals_unfused(F, fp8, N, C, H):
     say(f"gateup random fp8={fp8} N={N} C={C} H={H}")
     d = W.block_inputs(N, C, H, seed=N + C + H, w_std=0.0)
@@ -374,7 +375,8 @@ def test_gateup_swiglu_quant_known_absmax(F, fp8, N, C, H):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("N,H,C", [(64, 768, 256), (300, 384, 512), (513, 256, 384), (3100, 384, 5248)])
+@pytest.mark.parametrize("N,H,C", [(64, 768, 256), (300, 384, 512), (513, 256, 384), (3100, 384, 5248),
+                                   (256, 1792, 4096)])
 def test_down(F, fp8, N, H, C):
     say(f"down fp8={fp8} N={N} H={H} C={C}")
     h = W.normal_bf16((N, H), 1.0, N + H, 3)
@@ -452,8 +454,9 @@ def test_gemm_integer_down_bit_exact_and_deterministic(F):
 
 # ----------------------------------------------------------------------------- decode
 
+# (1, 4096, 1792): one GPU's share of the single-token decode under 8-way tensor parallelism
 @pytest.mark.parametrize("M,C,H", [(1, 256, 768), (1, 4096, 1024), (1, 3584, 384), (2, 1152, 640), (3, 512, 640), (4, 1024, 9216), (4, 640, 2304), (16, 384, 896),
-                                   (32, 256, 256)])
+                                   (32, 256, 256), (1, 4096, 1792)])
 def test_decode(F, M, C, H):
     say(f"decode M={M} C={C} H={H}")
     d = W.decode_inputs(M, C, H, seed=M * 13 + C + H)
@@ -571,11 +574,13 @@ def test_decode_pack_weight_layout(F, rows, cols):
 # (a half last chunk at C = 1152 and 640; C = 4096 fills the LDS copy); above
 # C = 4096 it reads them from the fragment-order copy in the workspace.  Up to
 # 16 tokens the down pass is split along K over workgroups (slices of one
-# 64-code piece at H = 128 x 1 group of rows, up to 64 pieces) and reduced by
-# the last workgroup of each row group; 17 to 32 tokens take two token blocks.
+# 64-code piece at H = 128 x 1 group of rows, up to 64 pieces) whose fp32
+# partial sums a second kernel adds in slice order; 17 to 32 tokens take two
+# token blocks.  (16, 3584, 4736) is one GPU's share of the Qwen2-7B-shaped
+# decode under 4-way tensor parallelism.
 PACKED_SHAPES = [(1, 1152, 640), (5, 3584, 384), (16, 384, 896), (16, 3584, 18944), (3, 4224, 256), (17, 256, 640),
                  (32, 256, 256), (1, 1152, 4096), (5, 4096, 4096), (16, 384, 8192), (13, 640, 4096),
-                 (16, 4096, 14336), (2, 128, 128), (9, 128, 8192), (16, 8192, 256)]
+                 (16, 4096, 14336), (2, 128, 128), (9, 128, 8192), (16, 8192, 256), (16, 3584, 4736)]
 
 
 @pytest.mark.parametrize("M,C,H", PACKED_SHAPES)
