@@ -256,7 +256,8 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
                                   int64_t M, int64_t C, int64_t H, hipStream_t stream);
 
 /* Packed decode weights: the same e4m3 codes re-laid so that the few-token
- * decode of 5 to 32 tokens streams each 16-row block as one contiguous run,
+ * decode (faster than on row-major weights from four tokens on, up to 32)
+ * streams each 16-row block as one contiguous run,
  * one KiB per load instruction, in the order the MFMA consumes it.
  * packed: e4m3, rows * cols bytes; 16-byte piece p holds row 16 rb + l % 16,
  * codes 64 kc + 16 (l / 16) .. + 15 of w, where l = p % 64 and
