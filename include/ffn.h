@@ -29,7 +29,10 @@
  *     FFN_ERR_INVALID; a size the kernels do not support, or a pointer not
  *     aligned to 16 bytes, gives FFN_ERR_UNSUPPORTED; a failed launch gives
  *     FFN_ERR_HIP.  Nothing is launched when validation fails.  A zero row
- *     count (N or M == 0) is valid and launches nothing.  ffn_last_error()
+ *     count (N or M == 0) is valid and writes no rows; the per-tensor outputs
+ *     keep their meaning (an abs-max of no elements is 0, accumulated ones
+ *     stay as found, scales are still written from their abs-max, dweight
+ *     stays as found).  ffn_last_error()
  *     returns a thread-local description of the last non-OK status.
  *   - Calls that share an output buffer on different streams race; calls on one
  *     stream are ordered.

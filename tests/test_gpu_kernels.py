@@ -452,6 +452,38 @@ def test_gemm_integer_down_bit_exact_and_deterministic(F):
     assert torch.equal(out1, out2)
 
 
+def test_zero_rows_still_write_the_per_tensor_outputs(F):
+    # N = 0: no rows are written; an abs-max of no elements is 0 (the _acc form
+    # leaves its word as found) and the quantising calls still write their
+    # scale from the given abs-max (the oracle's scale of that abs-max)
+    say("zero rows: GEMM entry points and the quantising transpose")
+    C, H = 256, 256
+    xs, ws = dev_f32([0.5]), dev_f32([0.25])
+    x, w, wd = empty_u8(1, C).zero_(), empty_u8(2 * H, C).zero_(), empty_u8(C, H).zero_()
+    h = empty_bf16(1, H).fill_(3.0)
+    am = dev_f32([7.0])
+    F.ffn_gateup(h, am, x, xs, w, ws, F.FFN_E4M3, 1, 0, C, H)
+    acc = dev_f32([7.0])
+    F.ffn_gateup_acc(h, acc, x, xs, w, ws, F.FFN_E4M3, 0, C, H)
+    q, qs, ham = empty_u8(1, H).fill_(0x11), dev_f32([-1.0]), dev_f32([7.0])
+    F.ffn_gateup_swiglu_quant(q, qs, ham, dev_f32([3.5]), x, xs, w, ws, F.FFN_E4M3, 0, C, H)
+    qs0 = dev_f32([-1.0])
+    F.ffn_gateup_swiglu_quant(q, qs0, None, dev_f32([0.0]), x, xs, w, ws, F.FFN_E4M3, 0, C, H)
+    out = empty_bf16(1, C).fill_(2.0)
+    F.ffn_down(out, empty_u8(1, H).zero_(), xs, wd, ws, F.FFN_E4M3, 0, H, C)
+    xb = empty_bf16(16, 16).zero_()
+    sc4, sc5 = dev_f32([-1.0]), dev_f32([-1.0])
+    F.ffn_quant_transpose(empty_u8(16, 16), None, sc4, xb, dev_f32([114.0]), 16, 0, 16)
+    F.ffn_quant_transpose(empty_u8(16, 16), None, sc5, xb, dev_f32([114.0]), 16, 0, 16, code_dtype=F.FFN_E5M2)
+    torch.cuda.synchronize()
+    assert host_f32(am)[0] == 0.0 and host_f32(acc)[0] == 7.0 and host_f32(ham)[0] == 0.0
+    assert host_f32(qs)[0] == O.quant_absmax(np.zeros(1, np.uint16), np.float32(3.5))[1]
+    assert host_f32(qs0)[0] == 1.0
+    assert host_f32(sc4)[0] == O.quant_absmax(np.zeros(1, np.uint16), np.float32(114.0))[1]
+    assert host_f32(sc5)[0] == O.quant_absmax(np.zeros(1, np.uint16), np.float32(114.0), fmt="e5m2")[1]
+    assert np.all(host_u8(q) == 0x11) and torch.all(h == 3.0) and torch.all(out == 2.0)
+
+
 # ----------------------------------------------------------------------------- decode
 
 # (1, 4096, 1792): one GPU's share of the single-token decode under 8-way tensor parallelism

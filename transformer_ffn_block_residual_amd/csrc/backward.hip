@@ -190,10 +190,28 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
     }
 }
 
+// The scale of a quantising transpose with nothing to transpose (one thread).
+template <bool kBf8>
+__global__ __launch_bounds__(64) void fp8_scale_kernel(float* __restrict__ scale_out, const float* __restrict__ absmax) {
+    if (threadIdx.x == 0) {
+        float scale, inv;
+        scale_pair(*absmax, scale, inv, kBf8 ? kE5M2Max : kE4M3Max);
+        *scale_out = scale;
+    }
+}
+
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
                             int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s,
                             bool e5m2) {
-    if (cols == 0 || ld_out == 0) return hipSuccess;
+    if (cols == 0 || ld_out == 0) {
+        // no codes to write; a quantising call still writes its scale
+        if (in_bytes == 2 && out_bytes == 1) {
+            if (e5m2) hipLaunchKernelGGL(fp8_scale_kernel<true>, dim3(1), dim3(64), 0, s, scale, absmax);
+            else hipLaunchKernelGGL(fp8_scale_kernel<false>, dim3(1), dim3(64), 0, s, scale, absmax);
+            return hipGetLastError();
+        }
+        return hipSuccess;
+    }
     uint8_t* o = static_cast<uint8_t*>(out);
     const uint8_t* x = static_cast<const uint8_t*>(in);
     const dim3 block(256);
