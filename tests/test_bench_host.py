@@ -118,3 +118,12 @@ def test_ingest_needs_the_calibration_copy(tmp_path, monkeypatch):
                               ingest_pmc=(str(f), str(f)))
     with pytest.raises(SystemExit, match="calibration"):
         bench.ingest_pmc(a)
+
+
+def test_committed_traffic_entries_match_their_sources():
+    # bench.py reports a counter entry only while its kernel's source is the
+    # one the counters were taken from; every committed entry is current
+    data = json.load(open(bench.TRAFFIC_FILE))
+    assert data
+    for key, e in data.items():
+        assert e["src_sha256"] == bench.src_digest(os.path.basename(e["src"])), key

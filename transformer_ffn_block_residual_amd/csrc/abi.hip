@@ -268,6 +268,17 @@ ffn_status_t ffn_gateup_swiglu_quant(uint8_t* q, float* q_scale, float* h_absmax
     ALIGNED(q);
     ALIGNED(x);
     ALIGNED(w);
+    if (N == 0) {
+        // no rows: the abs-max of no elements is 0, and the scale is still
+        // published from the known abs-max (the quantisation kernel's n = 0 path)
+        if (h_absmax) {
+            const ffn_status_t st = hip_status(ffn::launch_fill(h_absmax, 1, 0.0f, stream), "ffn_gateup_swiglu_quant");
+            if (st != FFN_OK) return st;
+        }
+        return hip_status(ffn::launch_quant(nullptr, q_scale, const_cast<float*>(h_absmax_known), nullptr, 0, false,
+                                            stream),
+                          "ffn_gateup_swiglu_quant");
+    }
     return hip_status(ffn::launch_gemm(q, h_absmax, x, x_scale, w, w_scale, dtype == FFN_E4M3, true, N, (int)C,
                                        (int)(2 * H), stream, h_absmax_known, q_scale),
                       "ffn_gateup_swiglu_quant");

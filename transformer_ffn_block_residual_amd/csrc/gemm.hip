@@ -711,13 +711,7 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
     }
-    if (N == 0) {
-        // no rows; a quantising epilogue still publishes its scale, computed
-        // from the known abs-max as the quantisation pass computes it
-        if (fuse_swiglu && q_absmax)
-            return launch_quant(nullptr, q_scale, const_cast<float*>(q_absmax), nullptr, 0, false, s);
-        return hipSuccess;
-    }
+    if (N == 0) return hipSuccess;
     GemmArgs a;
     a.out = out;
     a.absmax = fuse_swiglu ? absmax : nullptr;
