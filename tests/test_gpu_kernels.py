@@ -35,7 +35,7 @@ def F():
 # ----------------------------------------------------------------------------- RMSNorm
 
 RMS_SHAPES = [(64, 256, True), (37, 384, True), (300, 4096, True), (129, 3584, True), (5, 8192, False),
-              (3, 16384, True), (1, 8, True), (77, 1000, False)]
+              (3, 16384, True), (1, 8, True), (77, 1000, False), (4, 12288, False), (2, 16384, False)]
 
 
 @pytest.mark.parametrize("N,C,add", RMS_SHAPES)

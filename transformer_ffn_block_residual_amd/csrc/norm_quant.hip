@@ -46,17 +46,36 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
         // All loads are issued before any use: chunks past the row end load
         // the row's last chunk again (in bounds, no branch that would make the
         // compiler wait after every load) and are left out of the sum.
-        uint4 r[CPL], bv[CPL];
+        // The longest rows add the addend in groups of 8 chunks as well.
+        constexpr bool kGroupAdd = kAdd && CPL > 16;
+        uint4 r[CPL], bv[kGroupAdd ? 1 : CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = min(lane + i * 64, nch - 1);
             r[i] = a4[c];
-            if (kAdd) bv[i] = b4[c];
+            if (kAdd && !kGroupAdd) bv[i] = b4[c];
+        }
+        if (kGroupAdd) {
+#pragma unroll
+            for (int i0 = 0; i0 < CPL; i0 += 8) {
+                __builtin_amdgcn_sched_barrier(0);
+                uint4 bg[8];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) bg[ii] = b4[min(lane + (i0 + ii) * 64, nch - 1)];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    uint32_t* ap = reinterpret_cast<uint32_t*>(&r[i0 + ii]);
+                    const uint32_t* bp = reinterpret_cast<const uint32_t*>(&bg[ii]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        ap[q] = pack_bf16x2(bf16lo(ap[q]) + bf16lo(bp[q]), bf16hi(ap[q]) + bf16hi(bp[q]));
+                }
+            }
         }
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            if (kAdd) {
+            if (kAdd && !kGroupAdd) {
                 uint32_t* ap = reinterpret_cast<uint32_t*>(&r[i]);
                 const uint32_t* bp = reinterpret_cast<const uint32_t*>(&bv[i]);
 #pragma unroll
@@ -73,20 +92,37 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
             }
             ss += lane + i * 64 < nch ? part : 0.0f;
         }
+        if (CPL > 16) {
+            // the longest rows: keep the row packed between the two passes
+            // (the compiler would otherwise hold its unpacked fp32 copy too)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                uint32_t* rp = reinterpret_cast<uint32_t*>(&r[i]);
+                asm volatile("" : "+v"(rp[0]), "+v"(rp[1]), "+v"(rp[2]), "+v"(rp[3]));
+            }
+        }
         ss = wave_sum(ss);
         const float rs = 1.0f / sqrtf(ss / (float)C + eps);
         if (lane == 0) rstd_out[row] = rs;
         const uint4* w4 = reinterpret_cast<const uint4*>(w);
         uint4* y4 = reinterpret_cast<uint4*>(y + row * C);
         uint4* o4 = kAdd ? reinterpret_cast<uint4*>(res_out + row * C) : nullptr;
-        uint4 wr[CPL];
+        // the longest rows (32 chunks per lane) take their weights in groups of
+        // 8 chunks, so that the row and its weights never fill the registers
+        constexpr int kWG = CPL > 16 ? 8 : CPL;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) wr[i] = w4[min(lane + i * 64, nch - 1)];
+        for (int i0 = 0; i0 < CPL; i0 += kWG) {
+        // (a group's loads are not hoisted above the previous group's use)
+        if (kWG < CPL) __builtin_amdgcn_sched_barrier(0);
+        uint4 wr[kWG];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
+        for (int i = 0; i < kWG; ++i) wr[i] = w4[min(lane + (i0 + i) * 64, nch - 1)];
+#pragma unroll
+        for (int ii = 0; ii < kWG; ++ii) {
+            const int i = i0 + ii;
             const int c = lane + i * 64;
             if (c < nch) {
-                const uint4 wv = wr[i];
+                const uint4 wv = wr[ii];
                 const uint32_t* rp = reinterpret_cast<const uint32_t*>(&r[i]);
                 const uint32_t* wp = reinterpret_cast<const uint32_t*>(&wv);
                 uint4 yv;
@@ -99,6 +135,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
                 if (kAdd) o4[c] = r[i];
                 y4[c] = yv;
             }
+        }
         }
     }
     if (absmax) block_absmax_commit(amax, red, absmax);
