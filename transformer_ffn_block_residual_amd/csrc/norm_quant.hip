@@ -112,30 +112,31 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
         constexpr int kWG = CPL > 16 ? 8 : CPL;
 #pragma unroll
         for (int i0 = 0; i0 < CPL; i0 += kWG) {
-        // (a group's loads are not hoisted above the previous group's use)
-        if (kWG < CPL) __builtin_amdgcn_sched_barrier(0);
-        uint4 wr[kWG];
+            // (a group's loads are not hoisted above the previous group's use)
+            if (kWG < CPL) __builtin_amdgcn_sched_barrier(0);
+            uint4 wr[kWG];
 #pragma unroll
-        for (int i = 0; i < kWG; ++i) wr[i] = w4[min(lane + (i0 + i) * 64, nch - 1)];
+            for (int i = 0; i < kWG; ++i) wr[i] = w4[min(lane + (i0 + i) * 64, nch - 1)];
 #pragma unroll
-        for (int ii = 0; ii < kWG; ++ii) {
-            const int i = i0 + ii;
-            const int c = lane + i * 64;
-            if (c < nch) {
-                const uint4 wv = wr[ii];
-                const uint32_t* rp = reinterpret_cast<const uint32_t*>(&r[i]);
-                const uint32_t* wp = reinterpret_cast<const uint32_t*>(&wv);
-                uint4 yv;
-                uint32_t* yp = reinterpret_cast<uint32_t*>(&yv);
+            for (int ii = 0; ii < kWG; ++ii) {
+                const int i = i0 + ii;
+                const int c = lane + i * 64;
+                if (c < nch) {
+                    const uint4 wv = wr[ii];
+                    const uint32_t* rp = reinterpret_cast<const uint32_t*>(&r[i]);
+                    const uint32_t* wp = reinterpret_cast<const uint32_t*>(&wv);
+                    uint4 yv;
+                    uint32_t* yp = reinterpret_cast<uint32_t*>(&yv);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    yp[q] = pack_bf16x2((bf16lo(rp[q]) * rs) * bf16lo(wp[q]), (bf16hi(rp[q]) * rs) * bf16hi(wp[q]));
-                    amax = absmax_acc(absmax_acc(amax, bf16lo(yp[q])), bf16hi(yp[q]));
+                    for (int q = 0; q < 4; ++q) {
+                        yp[q] = pack_bf16x2((bf16lo(rp[q]) * rs) * bf16lo(wp[q]),
+                                            (bf16hi(rp[q]) * rs) * bf16hi(wp[q]));
+                        amax = absmax_acc(absmax_acc(amax, bf16lo(yp[q])), bf16hi(yp[q]));
+                    }
+                    if (kAdd) o4[c] = r[i];
+                    y4[c] = yv;
                 }
-                if (kAdd) o4[c] = r[i];
-                y4[c] = yv;
             }
-        }
         }
     }
     if (absmax) block_absmax_commit(amax, red, absmax);
