@@ -674,8 +674,9 @@ def bench_backward(a, torch, np, B, block, W):
     pre = block.PrefillBlock(N, C, H, w.eps, w.fp8)
     pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
     gd = a.grad_dtype if w.fp8 else "e4m3"
+    # the zero-once abs-max convention, as in the forward step: no clearing launches in a step
     bb = block.BackwardBlock(pre, in_place=False, grad_dtype=gd, fuse_swiglu_bwd=not a.unfused_swiglu_bwd,
-                             concurrent=a.concurrent_backward)
+                             concurrent=a.concurrent_backward, zero_once=True)
     bb.forward(dev(d["inp"]), dev(d["addend"]))
     d_out = dev(_bwd_dout(np, w, N))
     # the abs-max of d_out, as its producer (the next block's RMSNorm backward)
@@ -740,6 +741,8 @@ def bench_backward(a, torch, np, B, block, W):
                    "swiglu_bwd": "two calls" if a.unfused_swiglu_bwd else "fused into the down data gradient",
                    "schedule": ("weight gradients on a second stream beside the data gradients"
                                 if a.concurrent_backward else "one stream"),
+                   "absmax": ("zero-once: dMlpUp's and d_res's words accumulated into, each cleared by the other's "
+                              "consumer" if w.fp8 else "none (no quantised gradient)"),
                    **({"grad_dtype": gd} if w.fp8 else {})},
         "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({(gd if w.fp8 else 'bf16')}, accumulate): "
                                                  "the up projection's weight gradient [2H, C], K = N",

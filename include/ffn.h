@@ -16,9 +16,10 @@
  *     (the library clears them itself on `stream` first), except in the
  *     calls whose names end in _acc, which max-accumulate into a word the
  *     caller has zeroed (the convention of [llmq model] LLamaModel::forward:
- *     the abs-max table is zeroed once and every producer accumulates into
- *     its slot), and
- *     ffn_quant_absmax_clear, which zeroes a slot for its next producer.
+ *     the abs-max table, whose slots include the backward's gradients, is
+ *     zeroed once and every producer accumulates into its slot), and
+ *     ffn_quant_absmax_clear, ffn_quant_transpose_clear and
+ *     ffn_rmsnorm_bwd_acc, which zero a slot for its next producer.
  *     Abs-max is the maximum of |x| over the bit patterns, so a NaN element
  *     makes it NaN (and every code of the tensor a NaN code).
  *   - A dequantisation scale is absmax/448 (1.0 when absmax == 0); codes are
@@ -367,6 +368,16 @@ ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a,
                                       const void* gu, ffn_dtype_t dtype, int flags, int64_t M,
                                       int64_t H, int64_t K, hipStream_t stream);
 
+/* ffn_matmul_tn_swiglu_bwd that max-accumulates max|dgu| into *absmax
+ * (required) as found instead of clearing it first (the dMlpUp slot of the
+ * abs-max table, [llmq model] LLamaRunState: DMlpUp.Quant.Stats); other
+ * arguments and checks as ffn_matmul_tn_swiglu_bwd. */
+ffn_status_t ffn_matmul_tn_swiglu_bwd_acc(void* dgu, float* absmax, const void* a,
+                                          const float* a_scale, const void* b,
+                                          const float* b_scale, const void* gu, ffn_dtype_t dtype,
+                                          int flags, int64_t M, int64_t H, int64_t K,
+                                          hipStream_t stream);
+
 /* Transpose: out[c, r] = in[r, c] for r < rows, and 0 for rows <= r < ld_out
  * (zero padding that rounds a token count up to ffn_matmul_tn's K granularity).
  * [llmq model] backward_qmm, transpose(weight_tp, ...), transpose(activation_tp,
@@ -390,6 +401,15 @@ ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const v
                                  const float* absmax, ffn_dtype_t code_dtype, int64_t rows,
                                  int64_t cols, int64_t ld_out, hipStream_t stream);
 
+/* ffn_quant_transpose that also sets *clear (required; fp32 [1], another
+ * word than scale and absmax) to zero: the consumer of one abs-max slot
+ * clears the slot of the next producer, so that a backward step needs no
+ * clearing launch (ffn_quant_absmax_clear is the forward's counterpart). */
+ffn_status_t ffn_quant_transpose_clear(uint8_t* q_t, uint8_t* q, float* scale, const void* x,
+                                       const float* absmax, float* clear, ffn_dtype_t code_dtype,
+                                       int64_t rows, int64_t cols, int64_t ld_out,
+                                       hipStream_t stream);
+
 /* SwiGLU backward.  [llmq model] _backward_block, swiglu_backward(DMlpUp,
  * DSwiGLU, MlpUp, DMlpUp abs-max, B, T, D).  With g = gu[n,j], u = gu[n,H+j],
  * s = 1/(1+exp(-g)):
@@ -400,6 +420,11 @@ ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const v
  * dgu must not alias dh. */
 ffn_status_t ffn_swiglu_bwd(void* dgu, float* absmax, const void* dh, const void* gu,
                             int64_t N, int64_t H, hipStream_t stream);
+
+/* ffn_swiglu_bwd that max-accumulates max|dgu| into *absmax (required) as
+ * found; other arguments and checks as ffn_swiglu_bwd. */
+ffn_status_t ffn_swiglu_bwd_acc(void* dgu, float* absmax, const void* dh, const void* gu,
+                                int64_t N, int64_t H, hipStream_t stream);
 
 /* RMSNorm backward with the saved rstd, added to the residual stream's
  * gradient.  [llmq model] _backward_block, rmsnorm_backward(DResAtt, LN2_w
@@ -417,6 +442,16 @@ ffn_status_t ffn_rmsnorm_bwd(void* dinp, float* dweight, float* scratch,
                              const void* dresidual, const void* dy, const void* r,
                              const void* weight, const float* rstd, float* absmax,
                              int64_t N, int64_t C, hipStream_t stream);
+
+/* ffn_rmsnorm_bwd that max-accumulates max|dinp| into *absmax (required; the
+ * DResAtt slot) as found, and sets *clear (nullable; another word than
+ * absmax) to zero: the slot whose consumer ran before this pass (dMlpUp's,
+ * read by ffn_quant_transpose_clear), ready for the next step's producer.
+ * Other arguments and checks as ffn_rmsnorm_bwd. */
+ffn_status_t ffn_rmsnorm_bwd_acc(void* dinp, float* dweight, float* scratch,
+                                 const void* dresidual, const void* dy, const void* r,
+                                 const void* weight, const float* rstd, float* absmax,
+                                 float* clear, int64_t N, int64_t C, hipStream_t stream);
 
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
 const char* ffn_last_error(void);

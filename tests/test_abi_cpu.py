@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
               "ffn_swiglu", "ffn_down", "ffn_decode_gemv", "ffn_decode_gemv_arm", "ffn_decode_gemv_bf16",
               "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes", "ffn_decode_gemv_packed",
               "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
-              "ffn_rmsnorm_bwd_scratch_bytes", "ffn_last_error", "ffn_version"]:
+              "ffn_rmsnorm_bwd_scratch_bytes", "ffn_last_error", "ffn_version", "ffn_matmul_tn_swiglu_bwd_acc",
+              "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc"]:
         assert n in names
 
 
@@ -272,6 +273,35 @@ def test_backward_validation(lib):
     sb = lib.ffn_rmsnorm_bwd_scratch_bytes
     assert sb(0, 4096) == 0 and sb(8192, 4096) == 512 * 4096 * 4 and sb(3, 256) == 3 * 256 * 4
     assert sb(4, 9000) == -1
+
+
+def test_backward_absmax_accumulating_forms_validation(lib):
+    B_, C_, D, W1, W2 = 0x20000, 0x30000, 0x40000, 0x80000, 0x90000
+    f = lib.ffn_matmul_tn_swiglu_bwd_acc  # dgu, absmax, a, sa, b, sb, gu, dtype, flags, M, H, K
+    assert f(A, None, B_, None, C_, None, D, 0, 0, 64, 256, 128, None) == INVALID          # absmax required
+    assert "absmax is NULL" in _err(lib)
+    assert f(A, W1, B_, None, C_, None, D, 1, 0, 64, 256, 128, None) == INVALID            # FP8 without scales
+    assert f(A, W1, B_, W1, C_, W2, D, 1, 0, 64, 256, 128, None) == INVALID                # absmax aliases a_scale
+    assert f(A, W1, B_, None, C_, None, D, 0, 0, 64, 200, 128, None) == UNSUPPORTED        # H % 128
+    assert "ffn_matmul_tn_swiglu_bwd_acc" in _err(lib)
+    q = lib.ffn_quant_transpose_clear  # q_t, q, scale, x, absmax, clear, code dtype, rows, cols, ld_out
+    assert q(A, None, B_, C_, D, None, 1, 37, 64, 48, None) == INVALID                     # clear required
+    assert q(A, None, B_, C_, D, D, 1, 37, 64, 48, None) == INVALID                        # clear aliases absmax
+    assert "clear must not alias" in _err(lib)
+    assert q(A, None, B_, C_, D, B_, 1, 37, 64, 48, None) == INVALID                       # clear aliases scale
+    assert q(A, None, D, C_, D, W1, 1, 37, 64, 48, None) == INVALID                        # scale aliases absmax
+    assert q(A, None, B_, C_, D, W1, 0, 37, 64, 48, None) == INVALID                       # bf16 is no code format
+    assert q(A, None, B_, C_, D, W1, 1, 37, 64, 32, None) == INVALID                       # ld_out < rows
+    g = lib.ffn_swiglu_bwd_acc  # dgu, absmax, dh, gu, N, H
+    assert g(A, None, B_, C_, 4, 64, None) == INVALID                                      # absmax required
+    assert g(A, W1, A, C_, 4, 64, None) == INVALID                                         # dgu aliases dh
+    assert g(A, W1, B_, C_, 4, 60, None) == UNSUPPORTED                                    # H % 8
+    r = lib.ffn_rmsnorm_bwd_acc  # dinp, dweight, scratch, dres, dy, r, w, rstd, absmax, clear, N, C
+    assert r(A, B_, C_, A, D, 0x50000, 0x60000, 0x70000, None, None, 4, 256, None) == INVALID  # absmax required
+    assert r(A, B_, C_, A, D, 0x50000, 0x60000, 0x70000, W1, W1, 4, 256, None) == INVALID      # clear aliases absmax
+    assert r(A, B_, C_, A, D, 0x50000, 0x60000, 0x70000, W1, W2, 4, 8200, None) == UNSUPPORTED  # C > 8192
+    assert r(A, B_, C_, A, A, 0x50000, 0x60000, 0x70000, W1, W2, 4, 256, None) == INVALID      # dinp aliases dy
+    assert r(A, B_, C_, A, D, 0x50000, 0x60000, 0x70000, W1, None, -4, 256, None) == INVALID
 
 
 def test_binding_rejects_host_tensors_and_short_buffers():

@@ -519,6 +519,46 @@ def test_block_backward_concurrent_equals_serial(F, fp8, grad, in_place, fuse):
         assert torch.equal(res[0][n], res[1][n]), n
 
 
+@pytest.mark.parametrize("fp8,grad,in_place,fuse,conc", [(True, "e4m3", True, True, False),
+                                                         (True, "e5m2", False, False, False),
+                                                         (True, "e4m3", True, True, True),
+                                                         (False, "e4m3", True, True, False)])
+def test_block_backward_zero_once_equals_default(F, fp8, grad, in_place, fuse, conc):
+    """The zero-once abs-max form of the backward (the SwiGLU and RMSNorm
+    backwards accumulate into zeroed words; the quantiser of dMlpUp and the
+    RMSNorm backward clear each other's word) gives every gradient, scale and
+    d_res abs-max of the default form bit for bit, over three calls whose
+    output gradients shrink and grow again (a word left uncleared would show
+    in the next call's scale), and leaves dMlpUp's word at zero."""
+    say(f"block backward zero-once fp8={fp8} grad={grad} in_place={in_place} fuse={fuse} conc={conc}")
+    from transformer_ffn_block_residual_amd import block
+    N, C, H = 300, 384, 640
+    d = W.block_inputs(N, C, H, seed=91, w_std=0.1)
+    outs = [dev_bf16(rand_bits((N, C), std, 92 + k)) for k, std in enumerate((1.0, 0.01, 3.0))]
+    blocks = []
+    for zo in (False, True):
+        pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
+        pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+        blocks.append(block.BackwardBlock(pb, in_place=in_place, grad_dtype=grad, fuse_swiglu_bwd=fuse,
+                                          concurrent=conc, zero_once=zo))
+    names = ["dgu", "dy", "d_res", "dw_d", "dw_gu", "dw_norm"] + (["s_dgu", "am_dres"] if fp8 else [])
+    for k, d_out in enumerate(outs):
+        got = []
+        for bb in blocks:
+            bb.forward(dev_bf16(d["inp"]), dev_bf16(d["addend"]))
+            bb.backward(d_out)
+            torch.cuda.synchronize()
+            got.append({n: getattr(bb, n).clone() for n in names})
+        for n in names:
+            assert torch.equal(got[0][n], got[1][n]), (k, n)
+        zo = blocks[1]
+        assert host_f32(zo.am_dgu)[0] == 0.0, k
+        if fp8:
+            assert host_f32(zo.am_dres)[0] > 0.0, k
+        else:
+            assert host_f32(zo.am_dres)[0] == 0.0 and host_f32(zo.am_tab).max() == 0.0, k
+
+
 def test_block_backward_accumulates_weight_gradients(F):
     say("block backward twice")
     N, C, H = 128, 256, 384

@@ -60,6 +60,10 @@ def _load():
         "ffn_quant_transpose": [P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_swiglu_bwd": [P, P, P, P, I64, I64, P],
         "ffn_rmsnorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, P],
+        "ffn_matmul_tn_swiglu_bwd_acc": [P, P, P, P, P, P, P, I32, I32, I64, I64, I64, P],
+        "ffn_quant_transpose_clear": [P, P, P, P, P, P, I32, I64, I64, I64, P],
+        "ffn_swiglu_bwd_acc": [P, P, P, P, I64, I64, P],
+        "ffn_rmsnorm_bwd_acc": [P, P, P, P, P, P, P, P, P, P, I64, I64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -351,17 +355,28 @@ def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, flags, M, N, K, stream=Non
         int(M), int(N), int(K), _stream(stream)))
 
 
-def ffn_matmul_tn_swiglu_bwd(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream=None, flags=0):
-    """dgu = SwiGLU backward of gu with dh = a b^T (never stored); dtype as
-    ffn_matmul_tn; flags 0 or FFN_TN_TILE_GRID.  dgu may be gu."""
+def _matmul_tn_swiglu_bwd(fn, dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream, flags, acc):
     fp8 = dtype in (FFN_E4M3, FFN_E5M2)
     a_dt = E5M2 if dtype == FFN_E5M2 else _dt_elems(dtype)
     b_dt = E4M3 if fp8 else BF16
-    _check(_lib.ffn_matmul_tn_swiglu_bwd(
-        _ptr(dgu, "dgu", M * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=True),
+    _check(fn(
+        _ptr(dgu, "dgu", M * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=not acc),
         _ptr(a, "a", M * K, a_dt), _ptr(a_scale, "a_scale", 1, F32, optional=not fp8),
         _ptr(b, "b", H * K, b_dt), _ptr(b_scale, "b_scale", 1, F32, optional=not fp8),
         _ptr(gu, "gu", M * 2 * H, BF16), int(dtype), int(flags), int(M), int(H), int(K), _stream(stream)))
+
+
+def ffn_matmul_tn_swiglu_bwd(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream=None, flags=0):
+    """dgu = SwiGLU backward of gu with dh = a b^T (never stored); dtype as
+    ffn_matmul_tn; flags 0 or FFN_TN_TILE_GRID.  dgu may be gu."""
+    _matmul_tn_swiglu_bwd(_lib.ffn_matmul_tn_swiglu_bwd, dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K,
+                          stream, flags, False)
+
+
+def ffn_matmul_tn_swiglu_bwd_acc(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream=None, flags=0):
+    """ffn_matmul_tn_swiglu_bwd, max-accumulating into a caller-zeroed absmax."""
+    _matmul_tn_swiglu_bwd(_lib.ffn_matmul_tn_swiglu_bwd_acc, dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H,
+                          K, stream, flags, True)
 
 
 def ffn_transpose(out, inp, rows, cols, ld_out, elt_bytes, stream=None):
@@ -380,9 +395,27 @@ def ffn_quant_transpose(q_t, q, scale, x, absmax, rows, cols, ld_out, stream=Non
         _ptr(absmax, "absmax", 1, F32), int(code_dtype), int(rows), int(cols), int(ld_out), _stream(stream)))
 
 
+def ffn_quant_transpose_clear(q_t, q, scale, x, absmax, clear, rows, cols, ld_out, stream=None,
+                              code_dtype=FFN_E4M3):
+    """ffn_quant_transpose that also zeroes the abs-max word `clear`."""
+    dt = E5M2 if code_dtype == FFN_E5M2 else E4M3
+    _check(_lib.ffn_quant_transpose_clear(
+        _ptr(q_t, "q_t", cols * ld_out, dt), _ptr(q, "q", rows * cols, dt, optional=True),
+        _ptr(scale, "scale", 1, F32), _ptr(x, "x", rows * cols, BF16),
+        _ptr(absmax, "absmax", 1, F32), _ptr(clear, "clear", 1, F32), int(code_dtype), int(rows), int(cols),
+        int(ld_out), _stream(stream)))
+
+
 def ffn_swiglu_bwd(dgu, absmax, dh, gu, N, H, stream=None):
     _check(_lib.ffn_swiglu_bwd(
         _ptr(dgu, "dgu", N * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=True),
+        _ptr(dh, "dh", N * H, BF16), _ptr(gu, "gu", N * 2 * H, BF16), int(N), int(H), _stream(stream)))
+
+
+def ffn_swiglu_bwd_acc(dgu, absmax, dh, gu, N, H, stream=None):
+    """ffn_swiglu_bwd, max-accumulating into a caller-zeroed absmax."""
+    _check(_lib.ffn_swiglu_bwd_acc(
+        _ptr(dgu, "dgu", N * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32),
         _ptr(dh, "dh", N * H, BF16), _ptr(gu, "gu", N * 2 * H, BF16), int(N), int(H), _stream(stream)))
 
 
@@ -390,13 +423,26 @@ def ffn_rmsnorm_bwd_scratch_bytes(N, C):
     return int(_lib.ffn_rmsnorm_bwd_scratch_bytes(int(N), int(C)))
 
 
-def ffn_rmsnorm_bwd(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absmax, N, C, stream=None):
+def _rmsnorm_bwd_args(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, N, C):
     need = ffn_rmsnorm_bwd_scratch_bytes(N, C)
+    return (_ptr(dinp, "dinp", N * C, BF16), _ptr(dweight, "dweight", C, F32),
+            _ptr(scratch, "scratch", max(need, 0) // 4, F32), _ptr(dresidual, "dresidual", N * C, BF16),
+            _ptr(dy, "dy", N * C, BF16), _ptr(r, "r", N * C, BF16), _ptr(weight, "weight", C, BF16),
+            _ptr(rstd, "rstd", N, F32))
+
+
+def ffn_rmsnorm_bwd(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absmax, N, C, stream=None):
     _check(_lib.ffn_rmsnorm_bwd(
-        _ptr(dinp, "dinp", N * C, BF16), _ptr(dweight, "dweight", C, F32),
-        _ptr(scratch, "scratch", max(need, 0) // 4, F32), _ptr(dresidual, "dresidual", N * C, BF16),
-        _ptr(dy, "dy", N * C, BF16), _ptr(r, "r", N * C, BF16), _ptr(weight, "weight", C, BF16),
-        _ptr(rstd, "rstd", N, F32), _ptr(absmax, "absmax", 1, F32, optional=True), int(N), int(C),
+        *_rmsnorm_bwd_args(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, N, C),
+        _ptr(absmax, "absmax", 1, F32, optional=True), int(N), int(C), _stream(stream)))
+
+
+def ffn_rmsnorm_bwd_acc(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absmax, clear, N, C, stream=None):
+    """ffn_rmsnorm_bwd, max-accumulating into a caller-zeroed absmax and
+    zeroing the abs-max word `clear` (nullable)."""
+    _check(_lib.ffn_rmsnorm_bwd_acc(
+        *_rmsnorm_bwd_args(dinp, dweight, scratch, dresidual, dy, r, weight, rstd, N, C),
+        _ptr(absmax, "absmax", 1, F32), _ptr(clear, "clear", 1, F32, optional=True), int(N), int(C),
         _stream(stream)))
 
 
@@ -407,6 +453,7 @@ __all__ = [
     "ffn_decode_noalloc_scratch_bytes", "ffn_decode_gemv_packed_noalloc",
     "ffn_decode_gemv_packed", "bind_decode_gemv_packed",
     "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
+    "ffn_matmul_tn_swiglu_bwd_acc", "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc",
     "ffn_rmsnorm_bwd_scratch_bytes",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "version", "last_error", "LIB_PATH",
 ]

@@ -304,9 +304,21 @@ class BackwardBlock:
     backward returns.  Same results bit for bit; per-phase marks (``mark``)
     take the serial order.  Off by default: at the Qwen2-7B shape it measures
     the same as the serial order (the products are bound by the chip's power,
-    not by idle CUs)."""
+    not by idle CUs).
+    zero_once: the trainer's abs-max convention for the backward's two
+    gradient slots (llmq llama_model.cpp, LLamaRunState: DMlpUp.Quant.Stats
+    and DResAtt.Quant.Stats in the abs-max table that LLamaModel::forward
+    zeroes once): the SwiGLU backward and the RMSNorm backward accumulate
+    into zeroed words; the quantiser of dMlpUp clears d_res's word and the
+    RMSNorm backward clears dMlpUp's after its consumer has run, so no call
+    clears a word with a launch of its own.  Gradients equal the default
+    form's bit for bit; afterwards am_dres holds max|d_res| (the upstream
+    block's d_out_absmax) and am_dgu reads 0.  A bf16 block has no quantiser
+    of these gradients and so takes no abs-max at all.  Chosen at
+    construction (the words start at zero then)."""
 
-    def __init__(self, fwd, in_place=True, grad_dtype="e4m3", fuse_swiglu_bwd=True, concurrent=False):
+    def __init__(self, fwd, in_place=True, grad_dtype="e4m3", fuse_swiglu_bwd=True, concurrent=False,
+                 zero_once=False):
         if grad_dtype not in ("e4m3", "e5m2"):
             raise ValueError(f"grad_dtype {grad_dtype!r}: need 'e4m3' or 'e5m2'")
         if grad_dtype == "e5m2" and not fwd.fp8:
@@ -328,7 +340,11 @@ class BackwardBlock:
         self.dw_gu = _bf16(2 * H, C)
         self.dw_norm = _f32(C)
         self.scratch = _f32(max(B.ffn_rmsnorm_bwd_scratch_bytes(N, C), 4) // 4)
-        self.am_dout, self.am_dgu, self.am_dres = _f32(1), _f32(1), _f32(1)
+        self.zero_once = zero_once
+        # the gradient abs-max words, dMlpUp's and d_res's 16 bytes apart,
+        # zeroed here (the zero-once form relies on that)
+        self.am_tab = torch.zeros(8, dtype=torch.float32, device="cuda")
+        self.am_dout, self.am_dgu, self.am_dres = _f32(1), self.am_tab[0:1], self.am_tab[4:5]
         if fwd.fp8:
             self.qdout, self.s_dout = _u8(N, C), _f32(1)
             self.qdgu, self.s_dgu = _u8(N, 2 * H), _f32(1)
@@ -340,6 +356,41 @@ class BackwardBlock:
             self.dout_t, self.h_t = _bf16(C, self.Np), _bf16(H, self.Np)
             self.dgu_t, self.y_t = _bf16(2 * H, self.Np), _bf16(C, self.Np)
         self.zero_grads()
+
+    def _swiglu_bwd_fused(self, a, a_scale, dtype, stream, flags=0):
+        f = self.f
+        if self.zero_once:
+            am = self.am_dgu if f.fp8 else None
+            fn = B.ffn_matmul_tn_swiglu_bwd_acc if am is not None else B.ffn_matmul_tn_swiglu_bwd
+        else:
+            am, fn = self.am_dgu, B.ffn_matmul_tn_swiglu_bwd
+        fn(self.dgu, am, a, a_scale, self.wd_t, f.s_d if f.fp8 else None, self.gu, dtype, f.N, f.H, f.C, stream,
+           flags=flags)
+
+    def _swiglu_bwd(self, stream):
+        f = self.f
+        if self.zero_once and f.fp8:
+            B.ffn_swiglu_bwd_acc(self.dgu, self.am_dgu, self.dh, self.gu, f.N, f.H, stream)
+        else:
+            B.ffn_swiglu_bwd(self.dgu, None if self.zero_once else self.am_dgu, self.dh, self.gu, f.N, f.H, stream)
+
+    def _quant_dgu(self, E, stream):
+        f = self.f
+        if self.zero_once:
+            B.ffn_quant_transpose_clear(self.dgu_t, self.qdgu, self.s_dgu, self.dgu, self.am_dgu, self.am_dres,
+                                        f.N, 2 * f.H, self.Np, stream, E)
+        else:
+            B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, self.dgu, self.am_dgu, f.N, 2 * f.H, self.Np,
+                                  stream, E)
+
+    def _rmsnorm_bwd(self, d_out, stream):
+        f = self.f
+        if self.zero_once and f.fp8:
+            B.ffn_rmsnorm_bwd_acc(self.d_res, self.dw_norm, self.scratch, d_out, self.dy, self.r, f.w_norm, f.rstd,
+                                  self.am_dres, self.am_dgu, f.N, f.C, stream)
+        else:
+            B.ffn_rmsnorm_bwd(self.d_res, self.dw_norm, self.scratch, d_out, self.dy, self.r, f.w_norm, f.rstd,
+                              None if self.zero_once else self.am_dres, f.N, f.C, stream)
 
     def zero_grads(self):
         self.dw_d.zero_()
@@ -408,8 +459,7 @@ class BackwardBlock:
             B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, stream, E)
             mk("quant_dout")
             if self.fuse_swiglu_bwd:
-                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, self.qdout, self.s_dout, self.wd_t, f.s_d, self.gu,
-                                           E, N, H, C, stream)
+                self._swiglu_bwd_fused(self.qdout, self.s_dout, E, stream)
                 mk("dx_down_swiglu_bwd")
             else:
                 B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, 0, N, H, C, stream)
@@ -419,10 +469,10 @@ class BackwardBlock:
             B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, 1, C, H, Np, stream)
             mk("dw_down")
             if not self.fuse_swiglu_bwd:
-                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
+                self._swiglu_bwd(stream)
                 mk("swiglu_bwd")
             # backward_qmm through the up projection (input y, weight [2H, C])
-            B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, stream, E)
+            self._quant_dgu(E, stream)
             mk("quant_dgu")
             B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, 0, N, C, 2 * H, stream)
             mk("dx_up")
@@ -433,8 +483,7 @@ class BackwardBlock:
         else:
             Bf = B.FFN_BF16
             if self.fuse_swiglu_bwd:
-                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, d_out, None, self.wd_t, None, self.gu, Bf, N, H, C,
-                                           stream)
+                self._swiglu_bwd_fused(d_out, None, Bf, stream)
                 mk("dx_down_swiglu_bwd")
             else:
                 B.ffn_matmul_tn(self.dh, d_out, None, self.wd_t, None, Bf, 0, N, H, C, stream)
@@ -445,7 +494,7 @@ class BackwardBlock:
             B.ffn_matmul_tn(self.dw_d, self.dout_t, None, self.h_t, None, Bf, 1, C, H, Np, stream)
             mk("dw_down")
             if not self.fuse_swiglu_bwd:
-                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, stream)
+                self._swiglu_bwd(stream)
                 mk("swiglu_bwd")
             B.ffn_matmul_tn(self.dy, dgu, None, self.wgu_t, None, Bf, 0, N, C, 2 * H, stream)
             mk("dx_up")
@@ -455,8 +504,7 @@ class BackwardBlock:
             B.ffn_matmul_tn(self.dw_gu, self.dgu_t, None, self.y_t, None, Bf, 1, 2 * H, C, Np, stream)
             mk("dw_up")
         # rmsnorm_backward: DResAtt = DResFFN + the RMSNorm input's gradient
-        B.ffn_rmsnorm_bwd(self.d_res, self.dw_norm, self.scratch, d_out, self.dy, self.r, f.w_norm, f.rstd,
-                          self.am_dres, N, C, stream)
+        self._rmsnorm_bwd(d_out, stream)
         mk("rmsnorm_bwd")
         return self.d_res
 
@@ -494,12 +542,11 @@ class BackwardBlock:
             B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, side)
             B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, ACC | T, C, H, Np, side)
             if self.fuse_swiglu_bwd:
-                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, self.qdout, self.s_dout, self.wd_t, f.s_d, self.gu,
-                                           E, N, H, C, main, flags=T)
+                self._swiglu_bwd_fused(self.qdout, self.s_dout, E, main, flags=T)
             else:
                 B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, T, N, H, C, main)
-                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, main)
-            B.ffn_quant_transpose(self.dgu_t, self.qdgu, self.s_dgu, dgu, self.am_dgu, N, 2 * H, Np, main, E)
+                self._swiglu_bwd(main)
+            self._quant_dgu(E, main)
             fork(1)
             B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, side)
             B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, ACC | T, 2 * H, C, Np, side)
@@ -511,18 +558,16 @@ class BackwardBlock:
             B.ffn_transpose(self.h_t, f.h, N, H, Np, 2, side)
             B.ffn_matmul_tn(self.dw_d, self.dout_t, None, self.h_t, None, Bf, ACC | T, C, H, Np, side)
             if self.fuse_swiglu_bwd:
-                B.ffn_matmul_tn_swiglu_bwd(dgu, self.am_dgu, d_out, None, self.wd_t, None, self.gu, Bf, N, H, C,
-                                           main, flags=T)
+                self._swiglu_bwd_fused(d_out, None, Bf, main, flags=T)
             else:
                 B.ffn_matmul_tn(self.dh, d_out, None, self.wd_t, None, Bf, T, N, H, C, main)
-                B.ffn_swiglu_bwd(dgu, self.am_dgu, self.dh, self.gu, N, H, main)
+                self._swiglu_bwd(main)
             fork(1)
             B.ffn_transpose(self.dgu_t, dgu, N, 2 * H, Np, 2, side)
             B.ffn_transpose(self.y_t, f.y, N, C, Np, 2, side)
             B.ffn_matmul_tn(self.dw_gu, self.dgu_t, None, self.y_t, None, Bf, ACC | T, 2 * H, C, Np, side)
             B.ffn_matmul_tn(self.dy, dgu, None, self.wgu_t, None, Bf, T, N, C, 2 * H, main)
-        B.ffn_rmsnorm_bwd(self.d_res, self.dw_norm, self.scratch, d_out, self.dy, self.r, f.w_norm, f.rstd,
-                          self.am_dres, N, C, main)
+        self._rmsnorm_bwd(d_out, main)
         # the second stream's work joins this stream's
         self._ev[2].record(side)
         main.wait_event(self._ev[2])

@@ -483,37 +483,47 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const
                       "ffn_matmul_tn");
 }
 
+static ffn_status_t matmul_tn_swiglu_bwd_entry(const char* fn, void* dgu, float* absmax, const void* a,
+                                               const float* a_scale, const void* b, const float* b_scale,
+                                               const void* gu, ffn_dtype_t dtype, int flags, int64_t M, int64_t H,
+                                               int64_t K, hipStream_t stream, bool clear_absmax) {
+    if (!dgu) return fail(FFN_ERR_INVALID, "%s: dgu is NULL", fn);
+    if (!a) return fail(FFN_ERR_INVALID, "%s: a is NULL", fn);
+    if (!b) return fail(FFN_ERR_INVALID, "%s: b is NULL", fn);
+    if (!gu) return fail(FFN_ERR_INVALID, "%s: gu is NULL", fn);
+    if (M < 0 || H < 0 || K < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);
+    if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
+        return fail(FFN_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dtype);
+    if (flags & ~FFN_TN_TILE_GRID) return fail(FFN_ERR_INVALID, "%s: unknown flags 0x%x", fn, (unsigned)flags);
+    const bool fp8 = dtype != FFN_BF16;
+    if (fp8 && !a_scale) return fail(FFN_ERR_INVALID, "%s: a_scale is NULL", fn);
+    if (fp8 && !b_scale) return fail(FFN_ERR_INVALID, "%s: b_scale is NULL", fn);
+    if (ffn_status_t st = check_gemm_dims(fn, M, K, H, fp8 ? 1 : 2)) return st;
+    if (H > kMaxDim / 2) return fail(FFN_ERR_UNSUPPORTED, "%s: H = %lld too large", fn, (long long)H);
+    if (misaligned(dgu) || misaligned(a) || misaligned(b) || misaligned(gu))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
+    if (dgu == a || dgu == b) return fail(FFN_ERR_INVALID, "%s: dgu must not alias a or b", fn);
+    if (absmax && (absmax == a_scale || absmax == b_scale))
+        return fail(FFN_ERR_INVALID, "%s: absmax must not alias a_scale or b_scale", fn);
+    return hip_status(ffn::launch_gemm(dgu, absmax, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)H, stream,
+                                       nullptr, nullptr, false, dtype == FFN_E5M2, gu, (flags & FFN_TN_TILE_GRID) != 0,
+                                       clear_absmax),
+                      fn);
+}
+
 ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a, const float* a_scale, const void* b,
                                       const float* b_scale, const void* gu, ffn_dtype_t dtype, int flags, int64_t M,
                                       int64_t H, int64_t K, hipStream_t stream) {
-    REQUIRE(dgu);
-    REQUIRE(a);
-    REQUIRE(b);
-    REQUIRE(gu);
-    NONNEG(M);
-    NONNEG(H);
-    NONNEG(K);
-    if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
-        return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: unknown dtype %d", (int)dtype);
-    if (flags & ~FFN_TN_TILE_GRID)
-        return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: unknown flags 0x%x", (unsigned)flags);
-    const bool fp8 = dtype != FFN_BF16;
-    if (fp8) {
-        REQUIRE(a_scale);
-        REQUIRE(b_scale);
-    }
-    if (ffn_status_t st = check_gemm_dims("ffn_matmul_tn_swiglu_bwd", M, K, H, fp8 ? 1 : 2)) return st;
-    if (H > kMaxDim / 2) return fail(FFN_ERR_UNSUPPORTED, "ffn_matmul_tn_swiglu_bwd: H = %lld too large", (long long)H);
-    ALIGNED(dgu);
-    ALIGNED(a);
-    ALIGNED(b);
-    ALIGNED(gu);
-    if (dgu == a || dgu == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: dgu must not alias a or b");
-    if (absmax && (absmax == a_scale || absmax == b_scale))
-        return fail(FFN_ERR_INVALID, "ffn_matmul_tn_swiglu_bwd: absmax must not alias a_scale or b_scale");
-    return hip_status(ffn::launch_gemm(dgu, absmax, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)H, stream,
-                                       nullptr, nullptr, false, dtype == FFN_E5M2, gu, (flags & FFN_TN_TILE_GRID) != 0),
-                      "ffn_matmul_tn_swiglu_bwd");
+    return matmul_tn_swiglu_bwd_entry("ffn_matmul_tn_swiglu_bwd", dgu, absmax, a, a_scale, b, b_scale, gu, dtype,
+                                      flags, M, H, K, stream, true);
+}
+
+ffn_status_t ffn_matmul_tn_swiglu_bwd_acc(void* dgu, float* absmax, const void* a, const float* a_scale,
+                                          const void* b, const float* b_scale, const void* gu, ffn_dtype_t dtype,
+                                          int flags, int64_t M, int64_t H, int64_t K, hipStream_t stream) {
+    REQUIRE(absmax);
+    return matmul_tn_swiglu_bwd_entry("ffn_matmul_tn_swiglu_bwd_acc", dgu, absmax, a, a_scale, b, b_scale, gu,
+                                      dtype, flags, M, H, K, stream, false);
 }
 
 static ffn_status_t check_transpose(const char* fn, const void* out, const void* in, int64_t rows, int64_t cols,
@@ -542,43 +552,68 @@ ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols
                       "ffn_transpose");
 }
 
+static ffn_status_t quant_transpose_entry(const char* fn, uint8_t* q_t, uint8_t* q, float* scale, const void* x,
+                                          const float* absmax, float* clear, ffn_dtype_t code_dtype, int64_t rows,
+                                          int64_t cols, int64_t ld_out, hipStream_t stream) {
+    if (!q_t) return fail(FFN_ERR_INVALID, "%s: q_t is NULL", fn);
+    if (!scale) return fail(FFN_ERR_INVALID, "%s: scale is NULL", fn);
+    if (!x) return fail(FFN_ERR_INVALID, "%s: x is NULL", fn);
+    if (!absmax) return fail(FFN_ERR_INVALID, "%s: absmax is NULL", fn);
+    if (code_dtype != FFN_E4M3 && code_dtype != FFN_E5M2)
+        return fail(FFN_ERR_INVALID, "%s: code dtype %d (need FFN_E4M3 or FFN_E5M2)", fn, (int)code_dtype);
+    if (ffn_status_t st = check_transpose(fn, q_t, x, rows, cols, ld_out)) return st;
+    if (misaligned(q)) return fail(FFN_ERR_UNSUPPORTED, "%s: q is not 16-byte aligned", fn);
+    if (q && (q == q_t || (const void*)q == x)) return fail(FFN_ERR_INVALID, "%s: q must not alias q_t or x", fn);
+    // every block reads *absmax while the first one writes *scale (and *clear)
+    if ((const float*)scale == absmax) return fail(FFN_ERR_INVALID, "%s: scale and absmax alias", fn);
+    if (clear && ((const float*)clear == absmax || clear == scale))
+        return fail(FFN_ERR_INVALID, "%s: clear must not alias absmax or scale", fn);
+    return hip_status(ffn::launch_transpose(q_t, q, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream,
+                                            code_dtype == FFN_E5M2, clear),
+                      fn);
+}
+
 ffn_status_t ffn_quant_transpose(uint8_t* q_t, uint8_t* q, float* scale, const void* x, const float* absmax,
                                  ffn_dtype_t code_dtype, int64_t rows, int64_t cols, int64_t ld_out,
                                  hipStream_t stream) {
-    REQUIRE(q_t);
-    REQUIRE(scale);
-    REQUIRE(x);
-    REQUIRE(absmax);
-    if (code_dtype != FFN_E4M3 && code_dtype != FFN_E5M2)
-        return fail(FFN_ERR_INVALID, "ffn_quant_transpose: code dtype %d (need FFN_E4M3 or FFN_E5M2)", (int)code_dtype);
-    if (ffn_status_t st = check_transpose("ffn_quant_transpose", q_t, x, rows, cols, ld_out)) return st;
-    ALIGNED(q);
-    if (q && (q == q_t || (const void*)q == x))
-        return fail(FFN_ERR_INVALID, "ffn_quant_transpose: q must not alias q_t or x");
-    // every block reads *absmax while the first one writes *scale
-    if ((const float*)scale == absmax) return fail(FFN_ERR_INVALID, "ffn_quant_transpose: scale and absmax alias");
-    return hip_status(ffn::launch_transpose(q_t, q, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream,
-                                            code_dtype == FFN_E5M2),
-                      "ffn_quant_transpose");
+    return quant_transpose_entry("ffn_quant_transpose", q_t, q, scale, x, absmax, nullptr, code_dtype, rows, cols,
+                                 ld_out, stream);
+}
+
+ffn_status_t ffn_quant_transpose_clear(uint8_t* q_t, uint8_t* q, float* scale, const void* x, const float* absmax,
+                                       float* clear, ffn_dtype_t code_dtype, int64_t rows, int64_t cols,
+                                       int64_t ld_out, hipStream_t stream) {
+    REQUIRE(clear);
+    return quant_transpose_entry("ffn_quant_transpose_clear", q_t, q, scale, x, absmax, clear, code_dtype, rows,
+                                 cols, ld_out, stream);
+}
+
+static ffn_status_t swiglu_bwd_entry(const char* fn, void* dgu, float* absmax, const void* dh, const void* gu,
+                                     int64_t N, int64_t H, hipStream_t stream, bool clear_absmax) {
+    if (!dgu) return fail(FFN_ERR_INVALID, "%s: dgu is NULL", fn);
+    if (!dh) return fail(FFN_ERR_INVALID, "%s: dh is NULL", fn);
+    if (!gu) return fail(FFN_ERR_INVALID, "%s: gu is NULL", fn);
+    if (N < 0 || H < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);
+    if (H < 8 || H % 8 != 0 || H > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: H = %lld (need H %% 8 == 0)", fn, (long long)H);
+    if (N * H > ((int64_t)1 << 36)) return fail(FFN_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+    if (misaligned(dgu) || misaligned(dh) || misaligned(gu))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
+    if (dgu == dh) return fail(FFN_ERR_INVALID, "%s: dgu must not alias dh", fn);
+    return hip_status(ffn::launch_swiglu_bwd((uint16_t*)dgu, absmax, (const uint16_t*)dh, (const uint16_t*)gu, N,
+                                             (int)H, stream, clear_absmax),
+                      fn);
 }
 
 ffn_status_t ffn_swiglu_bwd(void* dgu, float* absmax, const void* dh, const void* gu, int64_t N, int64_t H,
                             hipStream_t stream) {
-    REQUIRE(dgu);
-    REQUIRE(dh);
-    REQUIRE(gu);
-    NONNEG(N);
-    NONNEG(H);
-    if (H < 8 || H % 8 != 0 || H > kMaxDim)
-        return fail(FFN_ERR_UNSUPPORTED, "ffn_swiglu_bwd: H = %lld (need H %% 8 == 0)", (long long)H);
-    if (N * H > ((int64_t)1 << 36)) return fail(FFN_ERR_UNSUPPORTED, "ffn_swiglu_bwd: tensor too large");
-    ALIGNED(dgu);
-    ALIGNED(dh);
-    ALIGNED(gu);
-    if (dgu == dh) return fail(FFN_ERR_INVALID, "ffn_swiglu_bwd: dgu must not alias dh");
-    return hip_status(ffn::launch_swiglu_bwd((uint16_t*)dgu, absmax, (const uint16_t*)dh, (const uint16_t*)gu, N,
-                                             (int)H, stream),
-                      "ffn_swiglu_bwd");
+    return swiglu_bwd_entry("ffn_swiglu_bwd", dgu, absmax, dh, gu, N, H, stream, true);
+}
+
+ffn_status_t ffn_swiglu_bwd_acc(void* dgu, float* absmax, const void* dh, const void* gu, int64_t N, int64_t H,
+                                hipStream_t stream) {
+    REQUIRE(absmax);
+    return swiglu_bwd_entry("ffn_swiglu_bwd_acc", dgu, absmax, dh, gu, N, H, stream, false);
 }
 
 int64_t ffn_rmsnorm_bwd_scratch_bytes(int64_t N, int64_t C) {
@@ -586,34 +621,46 @@ int64_t ffn_rmsnorm_bwd_scratch_bytes(int64_t N, int64_t C) {
     return ffn::rmsnorm_bwd_scratch_floats(N, (int)C) * (int64_t)sizeof(float);
 }
 
+static ffn_status_t rmsnorm_bwd_entry(const char* fn, void* dinp, float* dweight, float* scratch,
+                                      const void* dresidual, const void* dy, const void* r, const void* weight,
+                                      const float* rstd, float* absmax, float* clear, int64_t N, int64_t C,
+                                      hipStream_t stream, bool clear_absmax) {
+    if (!dinp) return fail(FFN_ERR_INVALID, "%s: dinp is NULL", fn);
+    if (!dweight) return fail(FFN_ERR_INVALID, "%s: dweight is NULL", fn);
+    if (!scratch) return fail(FFN_ERR_INVALID, "%s: scratch is NULL", fn);
+    if (!dresidual) return fail(FFN_ERR_INVALID, "%s: dresidual is NULL", fn);
+    if (!dy) return fail(FFN_ERR_INVALID, "%s: dy is NULL", fn);
+    if (!r) return fail(FFN_ERR_INVALID, "%s: r is NULL", fn);
+    if (!weight) return fail(FFN_ERR_INVALID, "%s: weight is NULL", fn);
+    if (!rstd) return fail(FFN_ERR_INVALID, "%s: rstd is NULL", fn);
+    if (N < 0 || C < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);
+    if (C < 8 || C % 8 != 0 || C > 8192)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: C = %lld (need C %% 8 == 0, C <= 8192)", fn, (long long)C);
+    if (N > ((int64_t)1 << 31)) return fail(FFN_ERR_UNSUPPORTED, "%s: N too large", fn);
+    if (misaligned(dinp) || misaligned(dweight) || misaligned(scratch) || misaligned(dresidual) || misaligned(dy) ||
+        misaligned(r) || misaligned(weight))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
+    if (dinp == dy || dinp == r) return fail(FFN_ERR_INVALID, "%s: dinp must not alias dy or r", fn);
+    if (clear && clear == absmax) return fail(FFN_ERR_INVALID, "%s: clear must not alias absmax", fn);
+    return hip_status(ffn::launch_rmsnorm_bwd((uint16_t*)dinp, dweight, scratch, (const uint16_t*)dresidual,
+                                              (const uint16_t*)dy, (const uint16_t*)r, (const uint16_t*)weight, rstd,
+                                              absmax, N, (int)C, stream, clear_absmax, clear),
+                      fn);
+}
+
 ffn_status_t ffn_rmsnorm_bwd(void* dinp, float* dweight, float* scratch, const void* dresidual, const void* dy,
                              const void* r, const void* weight, const float* rstd, float* absmax, int64_t N,
                              int64_t C, hipStream_t stream) {
-    REQUIRE(dinp);
-    REQUIRE(dweight);
-    REQUIRE(scratch);
-    REQUIRE(dresidual);
-    REQUIRE(dy);
-    REQUIRE(r);
-    REQUIRE(weight);
-    REQUIRE(rstd);
-    NONNEG(N);
-    NONNEG(C);
-    if (C < 8 || C % 8 != 0 || C > 8192)
-        return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_bwd: C = %lld (need C %% 8 == 0, C <= 8192)", (long long)C);
-    if (N > ((int64_t)1 << 31)) return fail(FFN_ERR_UNSUPPORTED, "ffn_rmsnorm_bwd: N too large");
-    ALIGNED(dinp);
-    ALIGNED(dweight);
-    ALIGNED(scratch);
-    ALIGNED(dresidual);
-    ALIGNED(dy);
-    ALIGNED(r);
-    ALIGNED(weight);
-    if (dinp == dy || dinp == r) return fail(FFN_ERR_INVALID, "ffn_rmsnorm_bwd: dinp must not alias dy or r");
-    return hip_status(ffn::launch_rmsnorm_bwd((uint16_t*)dinp, dweight, scratch, (const uint16_t*)dresidual,
-                                              (const uint16_t*)dy, (const uint16_t*)r, (const uint16_t*)weight, rstd,
-                                              absmax, N, (int)C, stream),
-                      "ffn_rmsnorm_bwd");
+    return rmsnorm_bwd_entry("ffn_rmsnorm_bwd", dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absmax,
+                             nullptr, N, C, stream, true);
+}
+
+ffn_status_t ffn_rmsnorm_bwd_acc(void* dinp, float* dweight, float* scratch, const void* dresidual, const void* dy,
+                                 const void* r, const void* weight, const float* rstd, float* absmax, float* clear,
+                                 int64_t N, int64_t C, hipStream_t stream) {
+    REQUIRE(absmax);
+    return rmsnorm_bwd_entry("ffn_rmsnorm_bwd_acc", dinp, dweight, scratch, dresidual, dy, r, weight, rstd, absmax,
+                             clear, N, C, stream, false);
 }
 
 }  // extern "C"

@@ -113,12 +113,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ ou
 // each store instruction writes whole 128-byte lines of eight output rows; the
 // row pitch (35 dwords) spreads those lanes' LDS reads over four bank groups.
 // kBf8: the quantised codes are e5m2 (scale absmax / 57344) instead of e4m3.
+// clear (quantising only, nullable): another abs-max word, set to zero by the
+// first thread (the zero-once convention: the word of the next producer).
 template <int kIn, bool kQuant, bool kBf8 = false>
 __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ out, uint8_t* __restrict__ q_rows,
                                                          float* __restrict__ scale_out,
                                                          const float* __restrict__ absmax,
                                                          const uint8_t* __restrict__ in, int64_t rows, int cols,
-                                                         int64_t ld_out) {
+                                                         int64_t ld_out, float* __restrict__ clear) {
     constexpr int kT = 128;                   // tile edge (elements)
     constexpr int kPitch = kT + 12;           // LDS bytes per tile row (35 dwords)
     constexpr int kInEl = 16 / kIn;           // input elements per 16-byte chunk
@@ -131,7 +133,10 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
     if (kQuant) {
         float scale;
         scale_pair(*absmax, scale, inv, kBf8 ? kE5M2Max : kE4M3Max);
-        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *scale_out = scale;
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+            *scale_out = scale;
+            if (clear) *clear = 0.0f;
+        }
     }
     auto pack4 = [](float a, float b, float c, float d) {
         return kBf8 ? pack_e5m2x4(a, b, c, d) : pack_e4m3x4(a, b, c, d);
@@ -192,22 +197,25 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
 
 // The scale of a quantising transpose with nothing to transpose (one thread).
 template <bool kBf8>
-__global__ __launch_bounds__(64) void fp8_scale_kernel(float* __restrict__ scale_out, const float* __restrict__ absmax) {
+__global__ __launch_bounds__(64) void fp8_scale_kernel(float* __restrict__ scale_out, const float* __restrict__ absmax,
+                                                       float* __restrict__ clear) {
     if (threadIdx.x == 0) {
         float scale, inv;
         scale_pair(*absmax, scale, inv, kBf8 ? kE5M2Max : kE4M3Max);
         *scale_out = scale;
+        if (clear) *clear = 0.0f;
     }
 }
 
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
                             int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s,
-                            bool e5m2) {
+                            bool e5m2, float* clear) {
     if (cols == 0 || ld_out == 0) {
-        // no codes to write; a quantising call still writes its scale
+        // no codes to write; a quantising call still writes its scale (and
+        // clears its word)
         if (in_bytes == 2 && out_bytes == 1) {
-            if (e5m2) hipLaunchKernelGGL(fp8_scale_kernel<true>, dim3(1), dim3(64), 0, s, scale, absmax);
-            else hipLaunchKernelGGL(fp8_scale_kernel<false>, dim3(1), dim3(64), 0, s, scale, absmax);
+            if (e5m2) hipLaunchKernelGGL(fp8_scale_kernel<true>, dim3(1), dim3(64), 0, s, scale, absmax, clear);
+            else hipLaunchKernelGGL(fp8_scale_kernel<false>, dim3(1), dim3(64), 0, s, scale, absmax, clear);
             return hipGetLastError();
         }
         return hipSuccess;
@@ -223,13 +231,13 @@ hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const floa
         const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((ld_out + 127) / 128));
         if (in_bytes == 1)
             hipLaunchKernelGGL((transpose8_kernel<1, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x,
-                               rows, cols, ld_out);
+                               rows, cols, ld_out, nullptr);
         else if (e5m2)
             hipLaunchKernelGGL((transpose8_kernel<2, true, true>), grid, block, 0, s, o, q_rows, scale, absmax, x,
-                               rows, cols, ld_out);
+                               rows, cols, ld_out, clear);
         else
             hipLaunchKernelGGL((transpose8_kernel<2, true>), grid, block, 0, s, o, q_rows, scale, absmax, x, rows,
-                               cols, ld_out);
+                               cols, ld_out, clear);
     }
     return hipGetLastError();
 }
@@ -283,8 +291,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dgu, float* _
 }
 
 hipError_t launch_swiglu_bwd(uint16_t* dgu, float* absmax, const uint16_t* dh, const uint16_t* gu, int64_t N, int H,
-                             hipStream_t s) {
-    if (absmax) {
+                             hipStream_t s, bool clear_absmax) {
+    if (absmax && clear_absmax) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
     }
@@ -420,10 +428,14 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(uint16_t* dinp, float*
 // workgroup covers 16 columns.
 constexpr int kReduceParts = 16;
 
+// clear (nullable): an abs-max word set to zero by the first thread (the
+// zero-once convention: the word whose consumer ran before this pass).
 __global__ __launch_bounds__(256) void rmsnorm_dw_reduce_kernel(float* __restrict__ dweight,
-                                                                const float* __restrict__ scratch, int rows, int C) {
+                                                                const float* __restrict__ scratch, int rows, int C,
+                                                                float* __restrict__ clear) {
     __shared__ float part[kReduceParts][16];
     const int col = threadIdx.x & 15, p = threadIdx.x >> 4;
+    if (clear && blockIdx.x == 0 && threadIdx.x == 0) *clear = 0.0f;
     const int c = blockIdx.x * 16 + col;
     float s = 0.0f;
     if (c < C) {
@@ -457,12 +469,12 @@ static void launch_rmsnorm_bwd_cpt(uint16_t* dinp, float* scratch, float* absmax
 
 hipError_t launch_rmsnorm_bwd(uint16_t* dinp, float* dweight, float* scratch, const uint16_t* dres,
                               const uint16_t* dy, const uint16_t* r, const uint16_t* w, const float* rstd,
-                              float* absmax, int64_t N, int C, hipStream_t s) {
-    if (absmax) {
+                              float* absmax, int64_t N, int C, hipStream_t s, bool clear_absmax, float* clear) {
+    if (absmax && clear_absmax) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
     }
-    if (N == 0) return hipSuccess;
+    if (N == 0) return clear ? launch_fill(clear, 1, 0.0f, s) : hipSuccess;
     const int groups = rmsnorm_bwd_groups(N);
     const int need = (C / 8 + 255) / 256;  // chunks per thread
     if (need <= 1) launch_rmsnorm_bwd_cpt<1>(dinp, scratch, absmax, dres, dy, r, w, rstd, N, C, groups, s);
@@ -471,7 +483,7 @@ hipError_t launch_rmsnorm_bwd(uint16_t* dinp, float* dweight, float* scratch, co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(rmsnorm_dw_reduce_kernel, dim3((unsigned)((C + 15) / 16)), dim3(256), 0, s, dweight, scratch,
-                       groups, C);
+                       groups, C, clear);
     return hipGetLastError();
 }
 

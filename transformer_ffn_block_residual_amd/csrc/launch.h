@@ -42,17 +42,22 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
 // Backward: out[c, r] = in[r, c], zero for rows <= r < ld_out.  (in_bytes,
 // out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3
 // with *absmax on the way (scale written to *scale; q_rows, if not null, also
-// receives the codes in the input's [rows, cols] layout; e5m2: e5m2 codes).
+// receives the codes in the input's [rows, cols] layout; e5m2: e5m2 codes;
+// clear, if not null, another abs-max word that the quantising pass zeroes).
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
                             int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s,
-                            bool e5m2 = false);
+                            bool e5m2 = false, float* clear = nullptr);
+// clear_absmax == false: *absmax is max-accumulated into as found.
 hipError_t launch_swiglu_bwd(uint16_t* dgu, float* absmax, const uint16_t* dh, const uint16_t* gu, int64_t N, int H,
-                             hipStream_t s);
-// scratch: rmsnorm_bwd_scratch_floats(N, C) floats.
+                             hipStream_t s, bool clear_absmax = true);
+// scratch: rmsnorm_bwd_scratch_floats(N, C) floats.  clear_absmax == false:
+// *absmax is max-accumulated into as found; clear (nullable): another abs-max
+// word that the pass zeroes.
 int64_t rmsnorm_bwd_scratch_floats(int64_t N, int C);
 hipError_t launch_rmsnorm_bwd(uint16_t* dinp, float* dweight, float* scratch, const uint16_t* dres,
                               const uint16_t* dy, const uint16_t* r, const uint16_t* w, const float* rstd,
-                              float* absmax, int64_t N, int C, hipStream_t s);
+                              float* absmax, int64_t N, int C, hipStream_t s, bool clear_absmax = true,
+                              float* clear = nullptr);
 
 // Decode arms (the caller has checked: arms other than the split one, and bf16
 // weights, only for M <= 4; gu is a [M, 2H] bf16 workspace for those arms).
