@@ -236,26 +236,34 @@ constexpr int kLdsDualMaxK = 4096;
 // multiplied, so the compiler's waits count exactly the younger loads.
 //
 // decode_dual_wave_kernel: the dual pass, persistent (one workgroup of kWaves
-// waves per CU) with x copied into LDS in fragment order.  Each wave owns
-// whole row blocks: it streams the block's gate and up codes front to back
-// and runs the block's epilogue itself, so after the copy of x no wave waits
-// for another.  Row blocks are dealt to the workgroups first (block b goes to
-// workgroup b % G, wave b / G % kWaves), so the CUs differ by at most one busy
-// wave.  Each wave starts its walk at a block-dependent group (the channel
-// spreading of decode_kernel).  The sums depend only on the block index, not
-// on the grid.  K <= kLdsDualMaxK, K % 128 == 0, rows % 16 == 0, M <= 16.
-template <int kU>
+// waves per CU).  Each wave owns whole row blocks: it streams the block's
+// gate and up codes front to back and runs the block's epilogue itself, so
+// no wave waits for another.  Row blocks are dealt to the workgroups first
+// (block b goes to workgroup b % G, wave b / G % kWaves), so the CUs differ
+// by at most one busy wave.  Each wave starts its walk at a block-dependent
+// group (the channel spreading of decode_kernel).  The sums depend only on
+// the block index and kU, not on the grid.  The activations' B operands come
+// either from a copy of x in LDS in fragment order, made by the workgroup
+// before its first item (kXLds), or from global memory with every item's
+// weights (two 16-byte loads per piece and lane, rows past M read as
+// zeros): the copy costs every CU the whole of x before it can start (about
+// 3.6 us at 16 tokens of 3584), the per-item loads cost L1 and L2 traffic in
+// proportion to the tokens; at the Qwen2-7B shape the loads are 1-3.5 us
+// faster up to 12 tokens and the copy 1.3 us faster at 16.  K % 128 == 0,
+// rows % 16 == 0, M <= 16; with kXLds K <= kLdsDualMaxK.
+template <int kU, bool kXLds>
 struct DualBuf {
     uint4 w[2][kU];
-    float sg[4], su[4];  // the row scales of the item's block (this lane's rows)
+    uint4 x[kXLds ? 1 : kU][2];  // the activations' fragments 2p, 2p + 1 of piece p (not kXLds)
+    float sg[4], su[4];          // the row scales of the item's block (this lane's rows)
 };
 
-template <int kWaves, int kU>
+template <int kWaves, int kU, bool kXLds>
 __global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
     uint16_t* __restrict__ out, uint16_t* __restrict__ hp, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ w0, const float* __restrict__ s0, const uint8_t* __restrict__ w1,
     const float* __restrict__ s1, int M, int K, int rows) {
-    __shared__ uint4 xs[kLdsDualMaxK / 32 * 64];  // fragment f, lane l: piece 64 f + l
+    __shared__ uint4 xs[kXLds ? kLdsDualMaxK / 32 * 64 : 1];  // fragment f, lane l: piece 64 f + l
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: loop bounds stay scalar
     const int lr = lane & 15, lq = lane >> 4;
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
         int g = it % ngroups + (int)(((unsigned)b * 5u) % (unsigned)ngroups);
         return g < ngroups ? g : g - ngroups;
     };
-    auto load_item = [&](int it, DualBuf<kU>& q) {
+    auto load_item = [&](int it, DualBuf<kU, kXLds>& q) {
         int b;
         const int g = item_group(it, b);
         const uint32_t bytes = (uint32_t)(16 * K);
@@ -285,6 +293,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
             q.w[0][i] = bload16(r0, lane * 16, so);
             q.w[1][i] = bload16(r1, lane * 16, so);
         }
+        if (!kXLds) {
+            // lane l: token l % 16 (zeros past M through the range check),
+            // codes 64 p + 16 (l / 16) + 0..7 and + 8..15
+            const __amdgpu_buffer_rsrc_t rx = rsrc_of(x, (uint32_t)(M * K * 2));
+#pragma unroll
+            for (int i = 0; i < (kXLds ? 1 : kU); ++i) {
+                const int pp = min(g * kU + i, npieces - 1);
+                const uint32_t xo = lr < M ? (uint32_t)((lr * K + 64 * pp + 16 * lq) * 2) : 0x80000000u;
+                q.x[i][0] = bload16(rx, xo, 0);
+                q.x[i][1] = bload16(rx, xo + 16u, 0);
+            }
+        }
         const uint4 vg = bload16(rsrc_of(s0 + b * 16, 64), lq * 16, 0);
         const uint4 vu = bload16(rsrc_of(s1 + b * 16, 64), lq * 16, 0);
         q.sg[0] = __uint_as_float(vg.x), q.sg[1] = __uint_as_float(vg.y);
@@ -293,7 +313,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
         q.su[2] = __uint_as_float(vu.z), q.su[3] = __uint_as_float(vu.w);
     };
     f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-    auto run_item = [&](int it, const DualBuf<kU>& q) {
+    auto run_item = [&](int it, const DualBuf<kU, kXLds>& q) {
         int b;
         const int g = item_group(it, b);
         if (it % ngroups == 0) {
@@ -304,8 +324,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
         for (int i = 0; i < kU; ++i) {
             const int p = g * kU + i;
             if (p < npieces) {
-                const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, xs[(2 * p) * 64 + lane]);
-                const bf16x8_t xb1 = __builtin_bit_cast(bf16x8_t, xs[(2 * p + 1) * 64 + lane]);
+                const bf16x8_t xb0 = __builtin_bit_cast(bf16x8_t, kXLds ? xs[(2 * p) * 64 + lane] : q.x[i][0]);
+                const bf16x8_t xb1 =
+                    __builtin_bit_cast(bf16x8_t, kXLds ? xs[(2 * p + 1) * 64 + lane] : q.x[i][kXLds ? 0 : 1]);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(q.w[m][i].x, q.w[m][i].y), xb0,
@@ -332,11 +353,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
             if (lr < M) *reinterpret_cast<uint2*>(out + (int64_t)lr * rows + orow0) = v;
         }
     };
-    DualBuf<kU> qa, qb;
+    DualBuf<kU, kXLds> qa, qb;
     if (nit > 0) load_item(0, qa);
     // x into LDS while the first loads are in flight (every load of the copy
     // issued before the first LDS write)
-    {
+    if (kXLds) {
         const int pieces = K / 32 * 64;
         constexpr int kPer = kLdsDualMaxK / 32 * 64 / (64 * kWaves);
         uint4 v[kPer];
@@ -353,8 +374,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_dual_wave_kernel(
             const int p = threadIdx.x + j * 64 * kWaves;
             if (p < pieces) xs[p] = v[j];
         }
+        __syncthreads();
     }
-    __syncthreads();
     for (int it = 0; it < nit; it += 2) {
         load_item(min(it + 1, nit - 1), qb);
         run_item(it, qa);
@@ -876,7 +897,10 @@ static hipError_t launch_packed_tb(uint16_t* out, uint16_t* h, uint16_t* xp, uin
 }
 
 // waves per workgroup and 1-KiB pieces per load group of the 16-token passes
-constexpr int kWaveDualWaves = 8, kWaveDualU = 8, kDownSplitU = 8;
+// (the dual pass with x in LDS, and with x loaded per item), and the most
+// tokens that load x per item
+constexpr int kWaveDualWaves = 8, kWaveDualU = 8, kWaveDualRegU = 2, kDownSplitU = 8;
+constexpr int kDualRegMaxM = 12;
 
 hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const uint16_t* x, const uint8_t* wg,
                                 const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
@@ -884,14 +908,18 @@ hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const 
     if (M == 0) return hipSuccess;
     hipError_t e;
     if (M <= 16) {
-        uint16_t* xp = ws;                 // [16 C] fragment order (C > kLdsDualMaxK only)
+        uint16_t* xp = ws;                 // [16 C] fragment order (more than 12 tokens and C > kLdsDualMaxK)
         uint16_t* hp = ws + (int64_t)16 * C;  // [16 H]
         float* part = reinterpret_cast<float*>(ws + (int64_t)16 * (C + H));  // [S][16][C]
-        if (C <= kLdsDualMaxK) {
-            // one persistent workgroup per CU (x fills most of its LDS); the
-            // grid size changes only which wave takes a row block, not the sums
-            const int grid = min(H / 16, device_cu_count());
-            hipLaunchKernelGGL((decode_dual_wave_kernel<kWaveDualWaves, kWaveDualU>), dim3(grid),
+        // one persistent workgroup per CU (with x in LDS it fills most of the
+        // LDS); the grid size changes only which wave takes a row block, not
+        // the sums
+        const int grid = min(H / 16, device_cu_count());
+        if (M <= kDualRegMaxM) {
+            hipLaunchKernelGGL((decode_dual_wave_kernel<kWaveDualWaves, kWaveDualRegU, false>), dim3(grid),
+                               dim3(64 * kWaveDualWaves), 0, s, h, hp, x, wg, sg, wu, su, M, C, H);
+        } else if (C <= kLdsDualMaxK) {
+            hipLaunchKernelGGL((decode_dual_wave_kernel<kWaveDualWaves, kWaveDualU, true>), dim3(grid),
                                dim3(64 * kWaveDualWaves), 0, s, h, hp, x, wg, sg, wu, su, M, C, H);
         } else {
             const int64_t pieces = (int64_t)(C / 32) * 64;
