@@ -414,7 +414,7 @@ def run_steps(torch, stream, step, a, marks_per_step=8):
 
 def decode_packed(a, M):
     """Whether the FP8 split-SiLU decode of M tokens runs on packed weights."""
-    return a.decode_layout == "packed" or (a.decode_layout == "auto" and M >= 4)
+    return a.decode_layout == "packed" or (a.decode_layout == "auto" and M >= 3)
 
 
 def bench_block(a, torch, np, B, block, W):

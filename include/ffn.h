@@ -260,7 +260,7 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
                                   int64_t M, int64_t C, int64_t H, hipStream_t stream);
 
 /* Packed decode weights: the same e4m3 codes re-laid so that the few-token
- * decode (faster than on row-major weights from four tokens on, up to 32)
+ * decode (faster than on row-major weights from three tokens on, up to 32)
  * streams each 16-row block as one contiguous run,
  * one KiB per load instruction, in the order the MFMA consumes it.
  * packed: e4m3, rows * cols bytes; 16-byte piece p holds row 16 rb + l % 16,

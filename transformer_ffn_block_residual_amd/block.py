@@ -219,7 +219,7 @@ class DecodeBlock:
 class DecodeBlockPacked(DecodeBlock):
     """DecodeBlock with its e4m3 weights kept in the packed decode layout
     (ffn_decode_pack_weight) and run through ffn_decode_gemv_packed: the
-    faster form from four to 32 tokens.  The row scales are DecodeBlock's; the
+    faster form from three to 32 tokens.  The row scales are DecodeBlock's; the
     row-major codes are not kept."""
 
     def __init__(self, M, C, H):
