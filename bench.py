@@ -98,6 +98,9 @@ def parse():
                         "(ffn_matmul_tn, ffn_swiglu_bwd) instead of ffn_matmul_tn_swiglu_bwd")
     p.add_argument("--grad-dtype", default="e4m3", choices=["e4m3", "e5m2"],
                    help="FP8 backward: the format of the quantised gradients (weights and activations stay e4m3)")
+    p.add_argument("--gemm-layout", default="tiled", choices=["tiled", "rows"],
+                   help="FP8 block workloads: the e4m3 GEMM operands (weights, codes of y and h) in the tiled "
+                        "layout (ffn_tile_pack; every GEMM load one contiguous KiB) or row-major")
     p.add_argument("--known-h-absmax", action="store_true",
                    help="FP8 block workloads: quantise h in the gate+up epilogue with the previous step's abs-max "
                         "(ffn_gateup_swiglu_quant, the recompute form) instead of bf16 h + ffn_quant_absmax")
@@ -133,14 +136,16 @@ def measured_traffic(key, src):
 # kernels with counter entries per workload: traffic.json key, source file,
 # the kernel name fragments whose per-dispatch counters make up one launch of
 # the entry point, which dispatches are that launch, and its algorithmic bytes
-def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3"):
+def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3", rows_layout=False):
     """[(traffic.json key, source file, kernel-name fragments of one launch,
     description, algorithmic bytes of one launch, (skip, stride, offset))],
     the dominant kernel first.  Matching dispatches are taken from the
     skip-th on, every stride-th from offset: the backward's two
     weight-gradient GEMMs share one kernel (the up projection's is the second
-    of each step), and the forward's two activation quantisations share one
-    kernel after the two weight quantisations of the set-up."""
+    of each step), and the forward's two row-major activation quantisations
+    share one kernel after the two weight quantisations of the set-up.  The
+    FP8 forward's GEMMs and quantisations run on tiled operands unless
+    rows_layout; the row-major forms' keys carry "_rows"."""
     from transformer_ffn_block_residual_amd import workloads as W
     w = W.WORKLOADS[workload]
     N, C, H = w.N, w.C, w.H
@@ -151,7 +156,7 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
         what = ("e5m2 x e4m3" if e5 else "e4m3") if w.fp8 else "bf16"
         # reads dgu^T [2H, N] and y^T [C, N] once, reads and writes dW_gu [2H, C]
         return [(f"dwup{'5' if e5 else ''}_{workload}", "gemm.hip",
-                 [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}, false>"],
+                 [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}, false, false>"],
                  f"gemm_kernel ({what}, accumulating) of the up projection's weight "
                  f"gradient, [2H, C] = [{2 * H}, {C}], K = N = {N}",
                  2 * H * N * e + C * N * e + 2 * (2 * H * C * 2), (0, 2, 1))]
@@ -162,18 +167,22 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
     elt = 1 if w.fp8 else 2
     fp8 = "true" if w.fp8 else "false"
     dt = "e4m3" if w.fp8 else "bf16"
+    tiled = w.fp8 and not rows_layout
+    tl = "true" if tiled else "false"
+    lay = ", tiled operands" if tiled else ""
+    tag = "_rows" if w.fp8 and rows_layout else ""
     every = (0, 1, 0)
     if known_h_absmax:
         # reads x and w, writes the e4m3 codes of h
-        return [(f"gateupq_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false, false, false>"],
-                 f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation) of ffn_gateup_swiglu_quant, "
-                 f"N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, every)]
+        return [(f"gateupq{tag}_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, true, false, false, false, {tl}>"],
+                 f"gemm_kernel (e4m3, fused SwiGLU + e4m3 quantisation{lay}) of ffn_gateup_swiglu_quant"
+                 f"{'_tiled' if tiled else ''}, N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, every)]
     specs = [
-        (f"gateup_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false, false>"],
-         f"gemm_kernel ({dt}, fused SwiGLU) of ffn_gateup, N={N} C={C} H={H}",
+        (f"gateup{tag}_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false, false, {tl}>"],
+         f"gemm_kernel ({dt}, fused SwiGLU{lay}) of ffn_gateup{'_acc_tiled' if tiled else ''}, N={N} C={C} H={H}",
          N * C * elt + 2 * H * C * elt + N * H * 2, every),
-        (f"down_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, false, false, false, false, false>"],
-         f"gemm_kernel ({dt}) of ffn_down, N={N} H={H} C={C}",
+        (f"down{tag}_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, false, false, false, false, false, {tl}>"],
+         f"gemm_kernel ({dt}{lay}) of ffn_down{'_tiled' if tiled else ''}, N={N} H={H} C={C}",
          N * H * elt + C * H * elt + N * C * 2, every),
         # reads inp and addend, writes r and y, rstd; the weight once
         (f"rmsnorm_{workload}", "norm_quant.hip", ["rmsnorm_kernel<"],
@@ -182,9 +191,12 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
          4 * N * C * 2 + N * 4 + C * 2, every),
     ]
     if w.fp8:
-        specs += [(f"quant_{t}_{workload}", "norm_quant.hip", ["quant_kernel("],
-                   f"quant_kernel (per-tensor e4m3 with a given abs-max) of {t}, {N} x {K}",
-                   3 * N * K, (2, 2, o)) for t, K, o in (("y", C, 0), ("h", H, 1))]
+        # row-major: after the two weight quantisations, y and h alternate on
+        # quant_kernel; tiled: y and h alternate on quant_tiled_kernel
+        qk = "quant_tiled_kernel(" if tiled else "quant_kernel("
+        specs += [(f"quant_{t}{tag}_{workload}", "norm_quant.hip", [qk],
+                   f"{qk[:-1]} (per-tensor e4m3 with a given abs-max{', tiled codes' if tiled else ''}) of {t}, "
+                   f"{N} x {K}", 3 * N * K, (0 if tiled else 2, 2, o)) for t, K, o in (("y", C, 0), ("h", H, 1))]
     if w.decode_M:
         M = w.decode_M
         specs.append((f"decode{M}_{workload}", "decode.hip",
@@ -217,8 +229,8 @@ def ingest_pmc(a):
             data = json.load(f)
     except (OSError, ValueError):
         data = {}
-    for key, src, frags, desc, algo, (skip, stride, offset) in traffic_specs(a.workload, a.known_h_absmax,
-                                                                             a.backward, a.grad_dtype):
+    for key, src, frags, desc, algo, (skip, stride, offset) in traffic_specs(
+            a.workload, a.known_h_absmax, a.backward, a.grad_dtype, rows_layout=a.gemm_layout == "rows"):
         rec = {"kernel": desc, "src": f"transformer_ffn_block_residual_amd/csrc/{src}",
                "src_sha256": src_digest(src)}
         total = 0.0
@@ -429,7 +441,8 @@ def bench_block(a, torch, np, B, block, W):
     def dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    pre = block.PrefillBlock(N, C, H, w.eps, w.fp8)
+    tiled = w.fp8 and a.gemm_layout == "tiled"
+    pre = block.PrefillBlock(N, C, H, w.eps, w.fp8, tiled=tiled)
     pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
     inp, addend = dev(d["inp"]), dev(d["addend"])
     decs = []
@@ -438,9 +451,9 @@ def bench_block(a, torch, np, B, block, W):
         packed = decode_packed(a, M)
         for _ in range(DECODE_COPIES):
             db = (block.DecodeBlockPacked if packed else block.DecodeBlock)(M, C, H)
-            wgu = pre.w_gu.clone()
+            wgu = pre.w_gu_rows.clone()
             sg = pre.s_gu.expand(H).contiguous()
-            db.set_fp8_weights(wgu[:H], sg, wgu[H:], sg, pre.w_d.clone(), pre.s_d.expand(C).contiguous())
+            db.set_fp8_weights(wgu[:H], sg, wgu[H:], sg, pre.w_d_rows.clone(), pre.s_d.expand(C).contiguous())
             decs.append(db)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -455,7 +468,7 @@ def bench_block(a, torch, np, B, block, W):
         # ping-pong abs-max buffers: step i quantises with am[i % 2] and
         # records its own abs-max in am[(i + 1) % 2]; one ordinary forward
         # provides the first known value
-        pre.forward(inp, addend, stream)
+        pre.forward_zero_once(inp, addend, stream)
         am_pp = [pre.am_h.clone(), torch.empty_like(pre.am_h)]
         torch.cuda.synchronize()
 
@@ -497,28 +510,50 @@ def bench_block(a, torch, np, B, block, W):
             B.ffn_rmsnorm_fwd(pre.y, pre.rstd, pre.r, None, inp, addend, pre.w_norm, pre.eps, N, C, stream)
         m1 = tm.mark() if tm else None
         if known:
-            B.ffn_quant_absmax(pre.qy, pre.s_y, pre.am_y, pre.y, N * C, 0, stream)
+            if tiled:
+                B.ffn_quant_absmax_clear_tiled(pre.qy, pre.s_y, pre.am_y, pre.y, N, C, None, stream)
+            else:
+                B.ffn_quant_absmax(pre.qy, pre.s_y, pre.am_y, pre.y, N * C, 0, stream)
             m2 = tm.mark() if tm else None
-            B.ffn_gateup_swiglu_quant(pre.qh, pre.s_h, am_pp[(i + 1) % 2], am_pp[i % 2], pre.qy, pre.s_y,
-                                      pre.w_gu, pre.s_gu, E, N, C, H, stream)
+            if tiled:
+                B.ffn_gateup_swiglu_quant_tiled(pre.qh, pre.s_h, am_pp[(i + 1) % 2], am_pp[i % 2], pre.qy,
+                                                pre.s_y, pre.w_gu, pre.s_gu, N, C, H, stream)
+            else:
+                B.ffn_gateup_swiglu_quant(pre.qh, pre.s_h, am_pp[(i + 1) % 2], am_pp[i % 2], pre.qy, pre.s_y,
+                                          pre.w_gu, pre.s_gu, E, N, C, H, stream)
             m3 = tm.mark() if tm else None
             m4 = m3
             if overlap == "tail":
                 fork_ev.record(stream)
-            B.ffn_down(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, E, N, H, C, stream)
+            if tiled:
+                B.ffn_down_tiled(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, N, H, C, stream)
+            else:
+                B.ffn_down(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, E, N, H, C, stream)
         elif w.fp8:
-            B.ffn_quant_absmax_clear(pre.qy, pre.s_y, pre.am_y, pre.y, N * C, pre.am_h, stream)
+            if tiled:
+                B.ffn_quant_absmax_clear_tiled(pre.qy, pre.s_y, pre.am_y, pre.y, N, C, pre.am_h, stream)
+            else:
+                B.ffn_quant_absmax_clear(pre.qy, pre.s_y, pre.am_y, pre.y, N * C, pre.am_h, stream)
             m2 = tm.mark() if tm else None
             m2q = m2
             if serial_at == "mid":
                 m2 = decode_serial(i, tm, stream)
-            B.ffn_gateup_acc(pre.h, pre.am_h, pre.qy, pre.s_y, pre.w_gu, pre.s_gu, E, N, C, H, stream)
+            if tiled:
+                B.ffn_gateup_acc_tiled(pre.h, pre.am_h, pre.qy, pre.s_y, pre.w_gu, pre.s_gu, N, C, H, stream)
+            else:
+                B.ffn_gateup_acc(pre.h, pre.am_h, pre.qy, pre.s_y, pre.w_gu, pre.s_gu, E, N, C, H, stream)
             m3 = tm.mark() if tm else None
-            B.ffn_quant_absmax_clear(pre.qh, pre.s_h, pre.am_h, pre.h, N * H, pre.am_y, stream)
+            if tiled:
+                B.ffn_quant_absmax_clear_tiled(pre.qh, pre.s_h, pre.am_h, pre.h, N, H, pre.am_y, stream)
+            else:
+                B.ffn_quant_absmax_clear(pre.qh, pre.s_h, pre.am_h, pre.h, N * H, pre.am_y, stream)
             m4 = tm.mark() if tm else None
             if overlap == "tail":
                 fork_ev.record(stream)
-            B.ffn_down(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, E, N, H, C, stream)
+            if tiled:
+                B.ffn_down_tiled(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, N, H, C, stream)
+            else:
+                B.ffn_down(pre.out, pre.qh, pre.s_h, pre.w_d, pre.s_d, E, N, H, C, stream)
         else:
             m2 = m1
             if serial_at == "mid":
@@ -576,6 +611,7 @@ def bench_block(a, torch, np, B, block, W):
            "N": N, "C": C, "H": H, "decode_M": M, "seed": w.seed,
            **({"decode_overlap": overlap, "decode_at": serial_at,
                "decode_layout": "packed" if decode_packed(a, M) else "rows"} if M else {}),
+           **({"gemm_operands": "tiled" if tiled else "row-major"} if w.fp8 else {}),
            "quant": ("per-tensor abs-max e4m3 activations and weights" if w.fp8 else "none (bf16)")
            + ("; h quantised in the gate+up epilogue with the previous step's abs-max" if known else "")
            + ("; decode: e4m3 weights, per-row fp32 scales, bf16 activations" if M else "")}
@@ -588,8 +624,9 @@ def bench_block(a, torch, np, B, block, W):
     # kernel's source is unchanged since they were taken
     names = {"gateup": "gateup_swiglu", "gateupq": "gateup_swiglu", "down": "down", "rmsnorm": "rmsnorm_fwd",
              "quant_y": "quant_y", "quant_h": "quant_h", f"decode{M}": "decode"}
-    for key, src, _, _, algo, _ in traffic_specs(a.workload, known):
-        name = names.get(key[:-len(a.workload) - 1])
+    specs = traffic_specs(a.workload, known, rows_layout=not tiled)
+    for key, src, _, _, algo, _ in specs:
+        name = names.get(key[:-len(a.workload) - 1].replace("_rows", ""))
         if name in kernels:
             t = measured_traffic(key, src)
             kernels[name]["traffic"] = t
@@ -600,9 +637,10 @@ def bench_block(a, torch, np, B, block, W):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": cfg,
         "roofline": {"bound": "mfma", "kernel": ("ffn_gateup_swiglu_quant (e4m3, SwiGLU + e4m3 h)" if known else
-                                                  f"ffn_gateup ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU)"),
+                                                  f"ffn_gateup ({'e4m3' if w.fp8 else 'bf16'}, fused SwiGLU)")
+                     + (", tiled operands" if tiled else ""),
                      "achieved": gu_tflops, "peak": peak, "unit": "TFLOP/s", "frac": gu_tflops / peak,
-                     "traffic": measured_traffic(("gateupq_" if known else "gateup_") + a.workload, "gemm.hip")},
+                     "traffic": measured_traffic(specs[0][0], "gemm.hip")},
         "kernels": kernels,
         "spread_ms": spread,
         "ms_per_step_in_hip_graph": graph_ms,

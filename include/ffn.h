@@ -204,6 +204,69 @@ ffn_status_t ffn_down(void* out, const void* h, const float* h_scale,
                       const void* w, const float* w_scale, ffn_dtype_t dtype,
                       int64_t N, int64_t H, int64_t C, hipStream_t stream);
 
+/* ---------------------------------------------------------- tiled operands
+ * The e4m3 prefill products on operands stored in this library's tiled
+ * layout instead of row-major: the same products as ffn_gateup_acc,
+ * ffn_gateup_swiglu_quant and ffn_down (bit for bit: the same sums in the
+ * same order), with every global load of the GEMM reading one contiguous
+ * KiB.  The pages fix only the row-major tensors; the layout is a storage
+ * choice of this library, made once for the weights (ffn_tile_pack) and by
+ * the quantisers for the activations.
+ *
+ * Layout of a [R, K] e4m3 operand (K bytes per row, K % 64 == 0): rows in
+ * groups of 64, group g at byte g*64*K; inside a group, K-step s (bytes
+ * 64s .. 64s+63 of each row) at s*4096, and its 16-row sub-group i at
+ * + i*1024; there, lane l = 0..63 holds 16 bytes at + 16*l: bytes
+ * 16*((l % 4) XOR (l / 16)) .. +15 of K-step s of row 64g + 16i + l/4.  A
+ * tiled buffer holds whole groups: ffn_tile_bytes(R, K) = ceil(R/64)*64*K
+ * bytes; the rows past R in the last group are don't-care for the GEMMs (a
+ * token row only feeds its own output row, which is not stored). */
+
+/* Bytes of the tiled form of [rows, row_bytes] (-1 if row_bytes % 64 != 0
+ * or a size is negative). */
+int64_t ffn_tile_bytes(int64_t rows, int64_t row_bytes);
+
+/* Tiled copy of a row-major [rows, row_bytes] operand (the weights, once per
+ * update); rows past `rows` in the last group are written as zeros.  out:
+ * ffn_tile_bytes(rows, row_bytes) bytes, must not overlap in.  Supported:
+ * row_bytes % 64 == 0, 64 <= row_bytes <= 2^21, the tiled size < 2^36. */
+ffn_status_t ffn_tile_pack(void* out, const void* in, int64_t rows, int64_t row_bytes,
+                           hipStream_t stream);
+
+/* ffn_quant_absmax_clear for a [rows, cols] bf16 x whose codes are stored in
+ * the tiled layout (the same codes, moved): *scale = A/448 (1 if A == 0),
+ * q = e4m3(x * 448/A), A = *absmax; clear (nullable) is zeroed.  q:
+ * ffn_tile_bytes(rows, cols) bytes (rows past `rows` are left as found).
+ * Supported: cols % 128 == 0, cols <= 2^20, ffn_tile_bytes(rows, cols) <= 2^36. */
+ffn_status_t ffn_quant_absmax_clear_tiled(uint8_t* q, float* scale, const float* absmax,
+                                          const void* x, int64_t rows, int64_t cols, float* clear,
+                                          hipStream_t stream);
+
+/* ffn_gateup_acc (E4M3) with x [N, C] and w [2H, C] tiled; h bf16 [N, H]
+ * row-major.  [llmq model] LLamaModel::_forward_block, forward_qmm and
+ * swiglu_forward.  Supported as ffn_gateup_acc, and ffn_tile_bytes(N, C) <
+ * 2^32. */
+ffn_status_t ffn_gateup_acc_tiled(void* h, float* h_absmax, const uint8_t* x, const float* x_scale,
+                                  const uint8_t* w, const float* w_scale, int64_t N, int64_t C,
+                                  int64_t H, hipStream_t stream);
+
+/* ffn_gateup_swiglu_quant (E4M3) with x and w tiled and the codes q of h
+ * stored tiled [N, H] (ffn_tile_bytes(N, H) bytes; rows past N are not
+ * written).  [llmq model] LLamaModel::_recompute_block,
+ * swiglu_forward_quant.  Supported as ffn_gateup_swiglu_quant. */
+ffn_status_t ffn_gateup_swiglu_quant_tiled(uint8_t* q, float* q_scale, float* h_absmax,
+                                           const float* h_absmax_known, const uint8_t* x,
+                                           const float* x_scale, const uint8_t* w,
+                                           const float* w_scale, int64_t N, int64_t C, int64_t H,
+                                           hipStream_t stream);
+
+/* ffn_down (E4M3) with h [N, H] and w [C, H] tiled; out bf16 [N, C]
+ * row-major.  [llmq model] LLamaModel::_forward_block, forward_qmm(MlpDown,
+ * ...).  Supported as ffn_down, and ffn_tile_bytes(N, H) < 2^32. */
+ffn_status_t ffn_down_tiled(void* out, const uint8_t* h, const float* h_scale, const uint8_t* w,
+                            const float* w_scale, int64_t N, int64_t H, int64_t C,
+                            hipStream_t stream);
+
 /* FP8-weight, bf16-activation decode FFN for M tokens (split-SiLU arm).
  * [metrale] DenseFfnLayer::forward, FP8 arm: w8a16_gemv_dual (gate and up in
  * one pass, per-row scales), silu_mul in place, w8a16_gemv for the down

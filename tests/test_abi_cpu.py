@@ -42,7 +42,9 @@ def test_header_declares_the_entry_points():
               "ffn_decode_pack_weight", "ffn_decode_packed_workspace_bytes", "ffn_decode_gemv_packed",
               "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
               "ffn_rmsnorm_bwd_scratch_bytes", "ffn_last_error", "ffn_version", "ffn_matmul_tn_swiglu_bwd_acc",
-              "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc"]:
+              "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc", "ffn_tile_bytes",
+              "ffn_tile_pack", "ffn_quant_absmax_clear_tiled", "ffn_gateup_acc_tiled",
+              "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled"]:
         assert n in names
 
 
@@ -143,6 +145,46 @@ def test_gemm_validation(lib):
     s = lib.ffn_swiglu
     assert s(A, None, A, 4, 12, None) == UNSUPPORTED
     assert s(None, None, A, 4, 16, None) == INVALID
+
+
+def test_tiled_layout_validation(lib):
+    tb = lib.ffn_tile_bytes
+    assert tb(1, 64) == 64 * 64 and tb(64, 128) == 64 * 128 and tb(65, 128) == 128 * 128 and tb(0, 64) == 0
+    assert tb(10, 100) == -1 and tb(-1, 64) == -1
+    p = lib.ffn_tile_pack                       # out, in, rows, row_bytes
+    assert p(None, A, 64, 128, None) == INVALID
+    assert p(A, A, 64, 100, None) == UNSUPPORTED          # row_bytes % 64
+    assert p(A, A, -1, 128, None) == INVALID
+    assert p(MIS, 0x900000, 64, 128, None) == UNSUPPORTED
+    assert p(A, A + 64, 64, 128, None) == INVALID          # out overlaps in
+    assert "overlaps" in _err(lib)
+    assert p(A, 0x900000, 0, 128, None) == 0              # no rows: nothing to launch, no HIP call
+    q = lib.ffn_quant_absmax_clear_tiled       # q, scale, absmax, x, rows, cols, clear
+    S, M, Z = 0x20000, 0x30000, 0x40000
+    assert q(A, S, S, A, 64, 256, Z, None) == INVALID      # scale aliases absmax
+    assert q(A, S, M, A, 64, 256, M, None) == INVALID      # clear aliases absmax
+    assert q(A, S, M, A, 64, 256, S, None) == INVALID      # clear aliases scale
+    assert q(A, S, M, A, 64, 192, Z, None) == UNSUPPORTED  # cols % 128
+    assert q(A, S, M, A, -2, 256, None, None) == INVALID
+    assert q(A, S, M, MIS, 64, 256, None, None) == UNSUPPORTED
+    assert q(None, S, M, A, 64, 256, None, None) == INVALID
+    g = lib.ffn_gateup_acc_tiled               # h, h_absmax, x, xs, w, ws, N, C, H
+    assert g(A, M, A, None, A, S, 64, 256, 768, None) == INVALID           # no x_scale
+    assert g(A, M, A, M, A, S, 64, 256, 768, None) == INVALID              # abs-max aliases x_scale
+    assert g(A, M, A, Z, A, S, 64, 200, 768, None) == UNSUPPORTED          # C % 128
+    assert g(A, M, A, Z, A, S, 64, 256, 100, None) == UNSUPPORTED          # H % 128
+    assert g(A, M, A, Z, A, S, (1 << 20), 4096, 768, None) == UNSUPPORTED  # > 4 GiB operand
+    assert g(A, M, MIS, Z, A, S, 64, 256, 768, None) == UNSUPPORTED
+    k = lib.ffn_gateup_swiglu_quant_tiled      # q, q_scale, h_absmax, known, x, xs, w, ws, N, C, H
+    assert k(A, S, M, None, A, Z, A, 0x50000, 64, 256, 768, None) == INVALID   # no known abs-max
+    assert k(A, S, M, M, A, Z, A, 0x50000, 64, 256, 768, None) == INVALID      # known aliases h_absmax
+    assert k(A, S, M, 0x60000, A, S, A, 0x50000, 64, 256, 768, None) == INVALID  # q_scale aliases x_scale
+    assert k(A, S, M, 0x60000, A, Z, A, 0x50000, 64, 256, 100, None) == UNSUPPORTED
+    d = lib.ffn_down_tiled                     # out, h, hs, w, ws, N, H, C
+    assert d(A, A, None, A, S, 64, 768, 256, None) == INVALID
+    assert d(A, A, Z, A, S, 64, 700, 256, None) == UNSUPPORTED
+    assert d(A, A, Z, A, S, 64, 768, 200, None) == UNSUPPORTED
+    assert d(None, A, Z, A, S, 64, 768, 256, None) == INVALID
 
 
 def test_decode_validation(lib):

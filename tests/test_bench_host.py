@@ -37,11 +37,20 @@ def test_block_traffic_specs(wl):
     assert specs[f"down_{wl}"][4] == N * H * e + C * H * e + N * C * 2
     assert specs[f"rmsnorm_{wl}"][4] == 4 * N * C * 2 + 4 * N + 2 * C
     if w.fp8:
-        # after the two weight quantisations, y and h alternate
-        assert specs[f"quant_y_{wl}"][4] == 3 * N * C and specs[f"quant_y_{wl}"][5] == (2, 2, 0)
-        assert specs[f"quant_h_{wl}"][4] == 3 * N * H and specs[f"quant_h_{wl}"][5] == (2, 2, 1)
+        # tiled operands by default: y and h alternate on the tiled quantiser
+        assert specs[f"quant_y_{wl}"][4] == 3 * N * C and specs[f"quant_y_{wl}"][5] == (0, 2, 0)
+        assert specs[f"quant_h_{wl}"][4] == 3 * N * H and specs[f"quant_h_{wl}"][5] == (0, 2, 1)
+        assert specs[f"quant_y_{wl}"][2] == ["quant_tiled_kernel("]
+        assert specs[f"gateup_{wl}"][2] == ["gemm_kernel<true, true, false, false, false, false, true>"]
+        # row-major operands: keys of their own; after the two weight
+        # quantisations, y and h alternate on the row-major quantiser
+        rows = {s[0]: s for s in bench.traffic_specs(wl, rows_layout=True)}
+        assert rows[f"quant_y_rows_{wl}"][5] == (2, 2, 0) and rows[f"quant_h_rows_{wl}"][5] == (2, 2, 1)
+        assert rows[f"gateup_rows_{wl}"][2] == ["gemm_kernel<true, true, false, false, false, false, false>"]
+        assert rows[f"gateup_rows_{wl}"][4] == specs[f"gateup_{wl}"][4]
     else:
         assert f"quant_y_{wl}" not in specs
+        assert bench.traffic_specs(wl, rows_layout=True) == bench.traffic_specs(wl)   # bf16: row-major only
     if w.decode_M:
         M = w.decode_M
         assert specs[f"decode{M}_{wl}"][4] == 3 * H * C + 4 * (2 * H + C) + 2 * M * (C + H) * 2
@@ -72,17 +81,18 @@ def _counter_csv(path, counter, rows):
 
 def test_ingest_scales_by_the_copy_and_selects_dispatches(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
-    gu = "void ffn::gemm_kernel<true, true, false, false, false, false>(ffn::GemmArgs)"
-    dn = "void ffn::gemm_kernel<true, false, false, false, false, false>(ffn::GemmArgs)"
+    gu = "void ffn::gemm_kernel<true, true, false, false, false, false, true>(ffn::GemmArgs)"
+    dn = "void ffn::gemm_kernel<true, false, false, false, false, false, true>(ffn::GemmArgs)"
     rn = "void ffn::rmsnorm_kernel<8, true>(...)"
     qk = "ffn::quant_kernel(unsigned char*, float*, float const*, unsigned short const*, long, float*)"
+    qt = "ffn::quant_tiled_kernel(unsigned char*, float*, float const*, unsigned short const*, long, long, float*)"
     dd = ["void ffn::decode_dual_wave_kernel<8, 8>(...)", "void ffn::decode_down_split_kernel<8>(...)",
           "ffn::decode_down_reduce_kernel(...)"]
 
     def rows(scale):
         r = [(qk, 1000.0 * scale), (qk, 2000.0 * scale)]                 # the two weight quantisations
         for step in range(3):
-            r += [(rn, 10.0 * scale), (qk, 3.0 * scale), (gu, 100.0 * scale + step), (qk, 30.0 * scale),
+            r += [(rn, 10.0 * scale), (qt, 3.0 * scale), (gu, 100.0 * scale + step), (qt, 30.0 * scale),
                   (dn, 50.0 * scale)]
             r += [(d, (7.0 + k) * scale) for k, d in enumerate(dd)]
         r.append(("__amd_rocclr_copyBuffer", 524288.0 if scale == 1 else 1048576.0))
@@ -92,7 +102,7 @@ def test_ingest_scales_by_the_copy_and_selects_dispatches(tmp_path, monkeypatch)
     _counter_csv(fetch, "FETCH_SIZE", rows(1))
     _counter_csv(write, "WRITE_SIZE", rows(2))
     a = types.SimpleNamespace(workload="qwen7b8", known_h_absmax=False, backward=False, grad_dtype="e4m3",
-                              ingest_pmc=(str(fetch), str(write)))
+                              gemm_layout="tiled", ingest_pmc=(str(fetch), str(write)))
     assert bench.ingest_pmc(a) == 0
     data = json.load(open(tmp_path / "traffic.json"))
     # FETCH raw KiB scaled by 2 (the 1 GiB copy read as 512 MiB), WRITE by 1
@@ -115,7 +125,7 @@ def test_ingest_needs_the_calibration_copy(tmp_path, monkeypatch):
     f = tmp_path / "f.csv"
     _counter_csv(f, "FETCH_SIZE", [("ffn::gemv_small_kernel<0, false, 1, 1, 2, 4, 2>(...)", 1.0)])
     a = types.SimpleNamespace(workload="decode", known_h_absmax=False, backward=False, grad_dtype="e4m3",
-                              ingest_pmc=(str(f), str(f)))
+                              gemm_layout="tiled", ingest_pmc=(str(f), str(f)))
     with pytest.raises(SystemExit, match="calibration"):
         bench.ingest_pmc(a)
 

@@ -1,0 +1,240 @@
+"""The tiled operand layout of the e4m3 prefill GEMMs.
+
+The tiled entry points run the same kernels as the row-major ones with only
+the global load (and, for the codes of h, store) offsets changed, so their
+results must equal the row-major results bit for bit; the row-major results
+are themselves checked against the oracle elsewhere.  The layout is checked
+against a numpy re-indexing written from the header's definition, which a
+CPU test pins to a per-element loop over that definition.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from transformer_ffn_block_residual_amd import workloads as W
+from tests.gpu_util import say, dev_bf16, dev_u8, dev_f32, host_bits, host_u8, empty_bf16, empty_f32, empty_u8
+
+
+def tiled_ref(a):
+    """The tiled layout of a [rows, rb] uint8 array (rb % 64 == 0), whole
+    64-row groups, pad rows zero: block (g, s, i) at g*64*rb + s*4096 + i*1024
+    holds, at 16*l + b, byte 64 s + 16 ((l % 4) ^ (l // 16)) + b of row
+    64 g + 16 i + l // 4."""
+    rows, rb = a.shape
+    G, S = -(-rows // 64), rb // 64
+    p = np.zeros((G * 64, rb), np.uint8)
+    p[:rows] = a
+    v = p.reshape(G, 4, 16, S, 4, 16)                  # [g, i, row in sub-group, s, chunk, b]
+    lane = np.arange(64)
+    lr, ch = lane // 4, (lane % 4) ^ (lane // 16)
+    t = v[:, :, lr, :, ch, :]                          # [lane, g, i, s, b]
+    return np.ascontiguousarray(t.transpose(1, 3, 2, 0, 4)).reshape(-1)
+
+
+def tiled_ref_loop(a):
+    """The same layout, one byte at a time from the definition."""
+    rows, rb = a.shape
+    G = -(-rows // 64)
+    out = np.zeros(G * 64 * rb, np.uint8)
+    for r in range(rows):
+        g, i, lr = r // 64, (r % 64) // 16, r % 16
+        for c in range(rb):
+            s, chunk, b = c // 64, (c % 64) // 16, c % 16
+            lane = 4 * lr + (chunk ^ (lr // 4))
+            out[g * 64 * rb + s * 4096 + i * 1024 + 16 * lane + b] = a[r, c]
+    return out
+
+
+@pytest.mark.parametrize("rows,rb", [(64, 64), (16, 128), (100, 192), (130, 256)])
+def test_tiled_reference_matches_its_definition(rows, rb):
+    a = np.random.default_rng(rows * rb).integers(0, 256, (rows, rb)).astype(np.uint8)
+    assert np.array_equal(tiled_ref(a), tiled_ref_loop(a))
+
+
+def _codes(shape, seed, top=0x58):
+    """Random finite e4m3 codes with magnitudes up to about 2^4, both signs."""
+    rng = np.random.default_rng(seed)
+    mag = rng.integers(0, top, shape)
+    return (mag | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from transformer_ffn_block_residual_amd import binding
+    return binding
+
+
+def _pack(B, q, rows, rb):
+    t = empty_u8(B.ffn_tile_bytes(rows, rb)).fill_(0xA5)
+    B.ffn_tile_pack(t, q, rows, rb)
+    return t
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,rb", [(64, 64), (1, 128), (100, 192), (300, 3584), (37888, 3584)])
+def test_tile_pack_layout(B, rows, rb):
+    say(f"tile pack rows={rows} row_bytes={rb}")
+    a = np.random.default_rng(rows + rb).integers(0, 256, (rows, rb)).astype(np.uint8)
+    t = _pack(B, dev_u8(a), rows, rb)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(t), tiled_ref(a))   # pad rows written as zeros
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,cols", [(1, 128), (64, 256), (300, 384), (8192, 3584)])
+def test_quant_tiled_is_the_row_major_codes_moved(B, rows, cols):
+    say(f"quant tiled rows={rows} cols={cols}")
+    x = W.normal_bf16((rows, cols), 1.0, rows + cols, 11)
+    xd = dev_bf16(x)
+    am = dev_f32(np.array([3.5], np.float32))          # values past it saturate
+    q, s = empty_u8(rows, cols), empty_f32(1)
+    clear1 = dev_f32(np.array([7.0], np.float32))
+    B.ffn_quant_absmax_clear(q, s, am, xd, rows * cols, clear1)
+    qt, st = empty_u8(B.ffn_tile_bytes(rows, cols)).fill_(0xA5), empty_f32(1)
+    clear2 = dev_f32(np.array([7.0], np.float32))
+    B.ffn_quant_absmax_clear_tiled(qt, st, am, xd, rows, cols, clear2)
+    torch.cuda.synchronize()
+    want = tiled_ref(host_u8(q).reshape(rows, cols))
+    got = host_u8(qt)
+    valid = tiled_ref(np.ones((rows, cols), np.uint8)).astype(bool)
+    assert np.array_equal(got[valid], want[valid])
+    assert np.all(got[~valid] == 0xA5)                  # rows past `rows` are left as found
+    assert torch.equal(st, s) and clear2.item() == 0.0
+
+
+# (N, C, H): ragged token counts (a partial 64-row group and empty slabs in
+# the last tile), output widths that are not a multiple of 256 (down), a
+# persistent grid of several rounds, and the Qwen2-7B-shaped prefill.
+GEMM_SHAPES = [(1, 128, 128), (64, 256, 128), (300, 512, 384), (1000, 384, 640), (4096, 1024, 4096),
+               (8192, 3584, 18944)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,C,H", GEMM_SHAPES)
+def test_tiled_gemms_equal_the_row_major_ones(B, N, C, H):
+    say(f"tiled gemms N={N} C={C} H={H}")
+    x, wgu = dev_u8(_codes((N, C), N + 1)), dev_u8(_codes((2 * H, C), C + 2))
+    hq, wd = dev_u8(_codes((N, H), N + 3)), dev_u8(_codes((C, H), H + 4))
+    sx, sw = dev_f32(np.array([0.011], np.float32)), dev_f32(np.array([0.013], np.float32))
+    xt, wgut, hqt, wdt = _pack(B, x, N, C), _pack(B, wgu, 2 * H, C), _pack(B, hq, N, H), _pack(B, wd, C, H)
+    # gate+up with SwiGLU, accumulating abs-max
+    h1, h2 = empty_bf16(N, H), empty_bf16(N, H)
+    am1, am2 = torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda")
+    B.ffn_gateup_acc(h1, am1, x, sx, wgu, sw, B.FFN_E4M3, N, C, H)
+    B.ffn_gateup_acc_tiled(h2, am2, xt, sx, wgut, sw, N, C, H)
+    # down
+    o1, o2 = empty_bf16(N, C), empty_bf16(N, C)
+    B.ffn_down(o1, hq, sx, wd, sw, B.FFN_E4M3, N, H, C)
+    B.ffn_down_tiled(o2, hqt, sx, wdt, sw, N, H, C)
+    # gate+up with the codes of h under a known abs-max
+    known = dev_f32(np.array([0.75], np.float32))
+    q1, qs1, qa1 = empty_u8(N, H), empty_f32(1), empty_f32(1)
+    q2, qs2, qa2 = empty_u8(B.ffn_tile_bytes(N, H)).fill_(0xA5), empty_f32(1), empty_f32(1)
+    B.ffn_gateup_swiglu_quant(q1, qs1, qa1, known, x, sx, wgu, sw, B.FFN_E4M3, N, C, H)
+    B.ffn_gateup_swiglu_quant_tiled(q2, qs2, qa2, known, xt, sx, wgut, sw, N, C, H)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(am1, am2)
+    assert torch.equal(o1, o2)
+    want = tiled_ref(host_u8(q1).reshape(N, H))
+    got = host_u8(q2)
+    valid = tiled_ref(np.ones((N, H), np.uint8)).astype(bool)
+    assert np.array_equal(got[valid], want[valid])
+    assert np.all(got[~valid] == 0xA5)                  # rows past N are not written
+    assert torch.equal(qs1, qs2) and torch.equal(qa1, qa2)
+
+
+@pytest.mark.gpu
+def test_tiled_token_rows_past_n_do_not_matter(B):
+    """The rows past N of the last 64-row group are don't-care: filling them
+    with other codes (NaN codes included) changes nothing that is stored."""
+    N, C, H = 100, 256, 256
+    say("tiled pad rows")
+    x, wgu = _codes((N, C), 5), dev_u8(_codes((2 * H, C), 6))
+    wgut = _pack(B, wgu, 2 * H, C)
+    sx, sw = dev_f32(np.array([0.02], np.float32)), dev_f32(np.array([0.02], np.float32))
+    res = []
+    for fill in (0, 0x7F):
+        pad = np.full((128, C), fill, np.uint8)
+        pad[:N] = x
+        xt = empty_u8(B.ffn_tile_bytes(N, C))
+        B.ffn_tile_pack(xt, dev_u8(pad), 128, C)          # 128 rows: two whole groups
+        h, am = empty_bf16(N, H), torch.zeros(1, device="cuda")
+        B.ffn_gateup_acc_tiled(h, am, xt, sx, wgut, sw, N, C, H)
+        res.append((h, am))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+@pytest.fixture(scope="module")
+def blk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from transformer_ffn_block_residual_amd import block
+    return block
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,C,H", [(300, 512, 384), (8192, 3584, 18944)])
+def test_tiled_block_equals_the_row_major_block(blk, B, N, C, H):
+    """PrefillBlock(tiled=True): both forwards give the row-major block's
+    outputs bit for bit (and its codes, moved)."""
+    say(f"tiled block N={N} C={C} H={H}")
+    d = W.block_inputs(N, C, H, seed=N + 5, outliers=True)
+    inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
+    res = {}
+    for tiled in (False, True):
+        b = blk.PrefillBlock(N, C, H, 1e-5, True, tiled=tiled)
+        b.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+        out = b.forward_zero_once(inp, add).clone()
+        st = {n: getattr(b, n).clone() for n in ("r", "y", "rstd", "h", "am_h", "am_y", "s_y", "s_h", "qy", "qh")}
+        known, am_out = dev_f32(np.array([0.9], np.float32)), empty_f32(1)
+        out_k = b.forward_known_h_absmax(inp, add, known, am_out).clone()
+        res[tiled] = (out, st, out_k, am_out.clone(), b.qh.clone(), b.s_h.clone())
+    torch.cuda.synchronize()
+    (o0, s0, k0, a0, qh0, sh0), (o1, s1, k1, a1, qh1, sh1) = res[False], res[True]
+    assert torch.equal(o0, o1) and torch.equal(k0, k1) and torch.equal(a0, a1) and torch.equal(sh0, sh1)
+    for n in ("r", "y", "rstd", "h", "am_h", "am_y", "s_y", "s_h"):
+        assert torch.equal(s0[n], s1[n]), n
+    for n, rb in (("qy", C), ("qh", H)):
+        valid = tiled_ref(np.ones((N, rb), np.uint8)).astype(bool)
+        assert np.array_equal(host_u8(s1[n])[valid], tiled_ref(host_u8(s0[n]).reshape(N, rb))[valid]), n
+    valid = tiled_ref(np.ones((N, H), np.uint8)).astype(bool)
+    assert np.array_equal(host_u8(qh1)[valid], tiled_ref(host_u8(qh0).reshape(N, H))[valid])
+
+
+@pytest.mark.gpu
+def test_tiled_block_replays_from_a_hip_graph(blk, B):
+    N, C, H = 300, 512, 384
+    say("tiled block graph replay")
+    d = W.block_inputs(N, C, H, seed=79)
+    b = blk.PrefillBlock(N, C, H, 1e-5, True, tiled=True)
+    b.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+    inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
+    b.forward_zero_once(inp, add)
+    torch.cuda.synchronize()
+    names = ["r", "y", "rstd", "am_y", "h", "am_h", "out", "qy", "s_y", "qh", "s_h"]
+    eager = {n: getattr(b, n).clone() for n in names}
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        b.forward_zero_once(inp, add)
+    scratch_y, scratch_rstd = empty_bf16(N, C), empty_f32(N)
+    masks = {n: torch.from_numpy(tiled_ref(np.ones((N, rb), np.uint8)).astype(bool)).cuda()
+             for n, rb in (("qy", C), ("qh", H))}
+    for rep in range(3):
+        for n in names:
+            if n not in ("am_y", "am_h"):      # the zero-once words must stay as the last call left them
+                getattr(b, n).zero_()
+        B.ffn_rmsnorm_fwd(scratch_y, scratch_rstd, None, None, inp, None, b.w_norm, 1e-5, N, C)  # eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            if n in masks:      # the rows past N of the tiled codes are don't-care
+                assert torch.equal(getattr(b, n)[masks[n]], eager[n][masks[n]]), (rep, n)
+            else:
+                assert torch.equal(getattr(b, n), eager[n]), (rep, n)

@@ -64,6 +64,11 @@ def _load():
         "ffn_quant_transpose_clear": [P, P, P, P, P, P, I32, I64, I64, I64, P],
         "ffn_swiglu_bwd_acc": [P, P, P, P, I64, I64, P],
         "ffn_rmsnorm_bwd_acc": [P, P, P, P, P, P, P, P, P, P, I64, I64, P],
+        "ffn_tile_pack": [P, P, I64, I64, P],
+        "ffn_quant_absmax_clear_tiled": [P, P, P, P, I64, I64, P, P],
+        "ffn_gateup_acc_tiled": [P, P, P, P, P, P, I64, I64, I64, P],
+        "ffn_gateup_swiglu_quant_tiled": [P, P, P, P, P, P, P, P, I64, I64, I64, P],
+        "ffn_down_tiled": [P, P, P, P, P, I64, I64, I64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -73,6 +78,8 @@ def _load():
     lib.ffn_rmsnorm_bwd_scratch_bytes.restype = ctypes.c_int64
     lib.ffn_decode_packed_workspace_bytes.argtypes = [I64, I64, I64]
     lib.ffn_decode_packed_workspace_bytes.restype = ctypes.c_int64
+    lib.ffn_tile_bytes.argtypes = [I64, I64]
+    lib.ffn_tile_bytes.restype = ctypes.c_int64
     lib.ffn_decode_noalloc_scratch_bytes.argtypes = []
     lib.ffn_decode_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.ffn_last_error.restype = ctypes.c_char_p
@@ -222,6 +229,63 @@ def ffn_down(out, h, h_scale, w, w_scale, dtype, N, H, C, stream=None):
         _ptr(h_scale, "h_scale", 1, F32, optional=not fp8),
         _ptr(w, "w", C * H, _dt_elems(dtype)), _ptr(w_scale, "w_scale", 1, F32, optional=not fp8),
         int(dtype), int(N), int(H), int(C), _stream(stream)))
+
+
+def ffn_tile_bytes(rows, row_bytes):
+    """Bytes of the tiled form of a [rows, row_bytes] operand (whole 64-row
+    groups); raises for a row_bytes that is not a multiple of 64."""
+    n = _lib.ffn_tile_bytes(int(rows), int(row_bytes))
+    if n < 0:
+        raise FFNError(FFN_ERR_UNSUPPORTED, f"no tiled layout for rows={rows}, row_bytes={row_bytes}")
+    return n
+
+
+def _tiled_numel(rows, row_bytes):
+    return _lib.ffn_tile_bytes(int(rows), int(row_bytes)) if row_bytes % 64 == 0 and rows >= 0 else 0
+
+
+def ffn_tile_pack(out, inp, rows, row_bytes, stream=None):
+    """Tiled copy of a row-major [rows, row_bytes] byte operand."""
+    _check(_lib.ffn_tile_pack(
+        _ptr(out, "out", _tiled_numel(rows, row_bytes), E4M3), _ptr(inp, "in", rows * row_bytes, E4M3),
+        int(rows), int(row_bytes), _stream(stream)))
+
+
+def ffn_quant_absmax_clear_tiled(q, scale, absmax, x, rows, cols, clear, stream=None):
+    """ffn_quant_absmax_clear with the codes of [rows, cols] stored tiled;
+    clear may be None."""
+    _check(_lib.ffn_quant_absmax_clear_tiled(
+        _ptr(q, "q", _tiled_numel(rows, cols), E4M3), _ptr(scale, "scale", 1, F32),
+        _ptr(absmax, "absmax", 1, F32), _ptr(x, "x", rows * cols, BF16), int(rows), int(cols),
+        _ptr(clear, "clear", 1, F32, optional=True), _stream(stream)))
+
+
+def ffn_gateup_acc_tiled(h, h_absmax, x, x_scale, w, w_scale, N, C, H, stream=None):
+    """ffn_gateup_acc (e4m3) on tiled x and w."""
+    _check(_lib.ffn_gateup_acc_tiled(
+        _ptr(h, "h", N * H, BF16), _ptr(h_absmax, "h_absmax", 1, F32),
+        _ptr(x, "x", _tiled_numel(N, C), E4M3), _ptr(x_scale, "x_scale", 1, F32),
+        _ptr(w, "w", _tiled_numel(2 * H, C), E4M3), _ptr(w_scale, "w_scale", 1, F32),
+        int(N), int(C), int(H), _stream(stream)))
+
+
+def ffn_gateup_swiglu_quant_tiled(q, q_scale, h_absmax, h_absmax_known, x, x_scale, w, w_scale, N, C, H,
+                                  stream=None):
+    """ffn_gateup_swiglu_quant (e4m3) on tiled x and w, storing tiled codes."""
+    _check(_lib.ffn_gateup_swiglu_quant_tiled(
+        _ptr(q, "q", _tiled_numel(N, H), E4M3), _ptr(q_scale, "q_scale", 1, F32),
+        _ptr(h_absmax, "h_absmax", 1, F32, optional=True), _ptr(h_absmax_known, "h_absmax_known", 1, F32),
+        _ptr(x, "x", _tiled_numel(N, C), E4M3), _ptr(x_scale, "x_scale", 1, F32),
+        _ptr(w, "w", _tiled_numel(2 * H, C), E4M3), _ptr(w_scale, "w_scale", 1, F32),
+        int(N), int(C), int(H), _stream(stream)))
+
+
+def ffn_down_tiled(out, h, h_scale, w, w_scale, N, H, C, stream=None):
+    """ffn_down (e4m3) on tiled h and w."""
+    _check(_lib.ffn_down_tiled(
+        _ptr(out, "out", N * C, BF16), _ptr(h, "h", _tiled_numel(N, H), E4M3), _ptr(h_scale, "h_scale", 1, F32),
+        _ptr(w, "w", _tiled_numel(C, H), E4M3), _ptr(w_scale, "w_scale", 1, F32),
+        int(N), int(H), int(C), _stream(stream)))
 
 
 def _decode_gemv_args(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream):
@@ -455,5 +519,7 @@ __all__ = [
     "ffn_matmul_tn", "ffn_matmul_tn_swiglu_bwd", "ffn_transpose", "ffn_quant_transpose", "ffn_swiglu_bwd", "ffn_rmsnorm_bwd",
     "ffn_matmul_tn_swiglu_bwd_acc", "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc",
     "ffn_rmsnorm_bwd_scratch_bytes",
+    "ffn_tile_bytes", "ffn_tile_pack", "ffn_quant_absmax_clear_tiled", "ffn_gateup_acc_tiled",
+    "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "version", "last_error", "LIB_PATH",
 ]

@@ -63,8 +63,16 @@ def _u8(*shape):
 
 
 class PrefillBlock:
-    def __init__(self, N, C, H, eps, fp8):
+    """One FFN block's prefill forward over N tokens.  tiled (FP8 only): the
+    e4m3 operands of both GEMMs (the weights, and the codes of y and h) are
+    kept in the library's tiled layout (``ffn_tile_pack``), which the GEMMs
+    read a contiguous KiB at a time; the results are those of the row-major
+    operands bit for bit.  ``qy`` and ``qh`` then hold tiled codes."""
+
+    def __init__(self, N, C, H, eps, fp8, tiled=False):
+        assert fp8 or not tiled, "the tiled layout is for the e4m3 operands"
         self.N, self.C, self.H, self.eps, self.fp8 = N, C, H, float(eps), bool(fp8)
+        self.tiled = bool(tiled)
         self.r = _bf16(N, C)
         self.y = _bf16(N, C)
         self.rstd = _f32(N)
@@ -77,8 +85,11 @@ class PrefillBlock:
         self.am_h = self.am_tab[4:5]
         self.out = _bf16(N, C)
         if self.fp8:
-            self.qy, self.s_y = _u8(N, C), _f32(1)
-            self.qh, self.s_h = _u8(N, H), _f32(1)
+            if self.tiled:
+                self.qy, self.qh = _u8(B.ffn_tile_bytes(N, C)), _u8(B.ffn_tile_bytes(N, H))
+            else:
+                self.qy, self.qh = _u8(N, C), _u8(N, H)
+            self.s_y, self.s_h = _f32(1), _f32(1)
         # bumped whenever the projection weights change; what is derived from
         # them (the backward's transposed weights) is remade when it moves
         self.weights_version = 0
@@ -104,12 +115,19 @@ class PrefillBlock:
         B.ffn_quant_absmax(self.w_gu, self.s_gu, am, w_gu, 2 * H * C, 1)
         self.w_d, self.s_d, am2 = _u8(C, H), _f32(1), _f32(1)
         B.ffn_quant_absmax(self.w_d, self.s_d, am2, w_d, C * H, 1)
+        # the row-major codes stay available (the decode reads them)
+        self.w_gu_rows, self.w_d_rows = self.w_gu, self.w_d
+        if self.tiled:
+            self.w_gu, self.w_d = _u8(B.ffn_tile_bytes(2 * H, C)), _u8(B.ffn_tile_bytes(C, H))
+            B.ffn_tile_pack(self.w_gu, self.w_gu_rows, 2 * H, C)
+            B.ffn_tile_pack(self.w_d, self.w_d_rows, C, H)
         torch.cuda.current_stream().synchronize()
 
     def forward(self, inp, addend, stream=None):
         """One block forward; returns the down-projection output [N, C] (the
         tensor the next block adds to ``self.r``)."""
         N, C, H = self.N, self.C, self.H
+        assert not self.tiled, "the tiled block runs forward_zero_once or forward_known_h_absmax"
         B.ffn_rmsnorm_fwd(self.y, self.rstd, self.r if addend is not None else None, self.am_y,
                           inp, addend, self.w_norm, self.eps, N, C, stream)
         if self.fp8:
@@ -141,6 +159,12 @@ class PrefillBlock:
             B.ffn_down(self.out, self.h, None, self.w_d, None, B.FFN_BF16, N, H, C, stream)
             return self.out
         B.ffn_rmsnorm_fwd_acc(self.y, self.rstd, r, self.am_y, inp, addend, self.w_norm, self.eps, N, C, stream)
+        if self.tiled:
+            B.ffn_quant_absmax_clear_tiled(self.qy, self.s_y, self.am_y, self.y, N, C, self.am_h, stream)
+            B.ffn_gateup_acc_tiled(self.h, self.am_h, self.qy, self.s_y, self.w_gu, self.s_gu, N, C, H, stream)
+            B.ffn_quant_absmax_clear_tiled(self.qh, self.s_h, self.am_h, self.h, N, H, self.am_y, stream)
+            B.ffn_down_tiled(self.out, self.qh, self.s_h, self.w_d, self.s_d, N, H, C, stream)
+            return self.out
         B.ffn_quant_absmax_clear(self.qy, self.s_y, self.am_y, self.y, N * C, self.am_h, stream)
         B.ffn_gateup_acc(self.h, self.am_h, self.qy, self.s_y, self.w_gu, self.s_gu, B.FFN_E4M3, N, C, H, stream)
         B.ffn_quant_absmax_clear(self.qh, self.s_h, self.am_h, self.h, N * H, self.am_y, stream)
@@ -158,6 +182,12 @@ class PrefillBlock:
         N, C, H = self.N, self.C, self.H
         B.ffn_rmsnorm_fwd(self.y, self.rstd, self.r if addend is not None else None, self.am_y,
                           inp, addend, self.w_norm, self.eps, N, C, stream)
+        if self.tiled:
+            B.ffn_quant_absmax_clear_tiled(self.qy, self.s_y, self.am_y, self.y, N, C, None, stream)
+            B.ffn_gateup_swiglu_quant_tiled(self.qh, self.s_h, h_absmax_out, h_absmax_known, self.qy, self.s_y,
+                                            self.w_gu, self.s_gu, N, C, H, stream)
+            B.ffn_down_tiled(self.out, self.qh, self.s_h, self.w_d, self.s_d, N, H, C, stream)
+            return self.out
         B.ffn_quant_absmax(self.qy, self.s_y, self.am_y, self.y, N * C, 0, stream)
         B.ffn_gateup_swiglu_quant(self.qh, self.s_h, h_absmax_out, h_absmax_known, self.qy, self.s_y, self.w_gu,
                                   self.s_gu, B.FFN_E4M3, N, C, H, stream)
@@ -319,6 +349,8 @@ class BackwardBlock:
 
     def __init__(self, fwd, in_place=True, grad_dtype="e4m3", fuse_swiglu_bwd=True, concurrent=False,
                  zero_once=False):
+        if getattr(fwd, "tiled", False):
+            raise ValueError("the backward takes a forward block with row-major operands (tiled=False)")
         if grad_dtype not in ("e4m3", "e5m2"):
             raise ValueError(f"grad_dtype {grad_dtype!r}: need 'e4m3' or 'e5m2'")
         if grad_dtype == "e5m2" and not fwd.fp8:

@@ -321,6 +321,157 @@ ffn_status_t ffn_down(void* out, const void* h, const float* h_scale, const void
                       "ffn_down");
 }
 
+// ---- tiled operands (whole 64-row groups; common.h, tiled_offset)
+
+static int64_t tiled_bytes(int64_t rows, int64_t row_bytes) { return (rows + 63) / 64 * 64 * row_bytes; }
+
+int64_t ffn_tile_bytes(int64_t rows, int64_t row_bytes) {
+    if (rows < 0 || row_bytes < 0 || row_bytes % 64 != 0 || row_bytes > ((int64_t)1 << 21) ||
+        rows > ((int64_t)1 << 40))
+        return -1;
+    return tiled_bytes(rows, row_bytes);
+}
+
+ffn_status_t ffn_tile_pack(void* out, const void* in, int64_t rows, int64_t row_bytes, hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(in);
+    NONNEG(rows);
+    NONNEG(row_bytes);
+    if (row_bytes < 64 || row_bytes % 64 != 0 || row_bytes > ((int64_t)1 << 21))
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_tile_pack: row_bytes = %lld (need a multiple of 64, 64 .. 2^21)",
+                    (long long)row_bytes);
+    if (rows > ((int64_t)1 << 36) / row_bytes || tiled_bytes(rows, row_bytes) >= ((int64_t)1 << 36))
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_tile_pack: operand too large");
+    ALIGNED(out);
+    ALIGNED(in);
+    const uint8_t* i8 = static_cast<const uint8_t*>(in);
+    const uint8_t* o8 = static_cast<const uint8_t*>(out);
+    if (o8 < i8 + rows * row_bytes && i8 < o8 + tiled_bytes(rows, row_bytes))
+        return fail(FFN_ERR_INVALID, "ffn_tile_pack: out overlaps in");
+    return hip_status(ffn::launch_tile_pack(static_cast<uint8_t*>(out), i8, rows, row_bytes, stream),
+                      "ffn_tile_pack");
+}
+
+ffn_status_t ffn_quant_absmax_clear_tiled(uint8_t* q, float* scale, const float* absmax, const void* x,
+                                          int64_t rows, int64_t cols, float* clear, hipStream_t stream) {
+    REQUIRE(q);
+    REQUIRE(scale);
+    REQUIRE(absmax);
+    REQUIRE(x);
+    NONNEG(rows);
+    NONNEG(cols);
+    if ((const float*)scale == absmax || (clear && ((const float*)clear == absmax || clear == scale)))
+        return fail(FFN_ERR_INVALID, "ffn_quant_absmax_clear_tiled: scale, absmax and clear must be distinct words");
+    if (cols < 128 || cols % 128 != 0 || cols > kMaxDim)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_quant_absmax_clear_tiled: cols = %lld (need a positive multiple of 128)",
+                    (long long)cols);
+    // the quantiser's thread index (64 per row pair and 8 K-steps) stays in 32 bits
+    if (rows > ((int64_t)1 << 36) / cols || tiled_bytes(rows, cols) > ((int64_t)1 << 36) ||
+        (rows + 1) / 2 * ((cols / 64 + 7) / 8) * 64 >= ((int64_t)1 << 32))
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_quant_absmax_clear_tiled: too large");
+    ALIGNED(q);
+    ALIGNED(x);
+    return hip_status(ffn::launch_quant_tiled(q, scale, const_cast<float*>(absmax), (const uint16_t*)x, rows, cols,
+                                              stream, clear),
+                      "ffn_quant_absmax_clear_tiled");
+}
+
+// The checks of the row-major entry point, plus the tiled token operand's
+// whole groups within the 32-bit offsets of one operand.
+static ffn_status_t check_tiled_gemm(const char* fn, int64_t N, int64_t K, int64_t O) {
+    if (ffn_status_t st = check_gemm_dims(fn, N, K, O, 1)) return st;
+    if (tiled_bytes(N, K) >= ((int64_t)1 << 32)) return fail(FFN_ERR_UNSUPPORTED, "%s: an operand exceeds 4 GiB", fn);
+    return FFN_OK;
+}
+
+ffn_status_t ffn_gateup_acc_tiled(void* h, float* h_absmax, const uint8_t* x, const float* x_scale, const uint8_t* w,
+                                  const float* w_scale, int64_t N, int64_t C, int64_t H, hipStream_t stream) {
+    REQUIRE(h);
+    REQUIRE(h_absmax);
+    REQUIRE(x);
+    REQUIRE(x_scale);
+    REQUIRE(w);
+    REQUIRE(w_scale);
+    NONNEG(N);
+    NONNEG(C);
+    NONNEG(H);
+    if (h_absmax == x_scale || h_absmax == w_scale)
+        return fail(FFN_ERR_INVALID, "ffn_gateup_acc_tiled: h_absmax must not alias x_scale or w_scale");
+    if (ffn_status_t st = check_tiled_gemm("ffn_gateup_acc_tiled", N, C, 2 * H)) return st;
+    if (H % 128 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup_acc_tiled: H = %lld must be a multiple of 128", (long long)H);
+    ALIGNED(h);
+    ALIGNED(x);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(h, h_absmax, x, x_scale, w, w_scale, true, true, N, (int)C, (int)(2 * H),
+                                       stream, nullptr, nullptr, false, false, nullptr, false, false, true),
+                      "ffn_gateup_acc_tiled");
+}
+
+ffn_status_t ffn_gateup_swiglu_quant_tiled(uint8_t* q, float* q_scale, float* h_absmax, const float* h_absmax_known,
+                                           const uint8_t* x, const float* x_scale, const uint8_t* w,
+                                           const float* w_scale, int64_t N, int64_t C, int64_t H,
+                                           hipStream_t stream) {
+    REQUIRE(q);
+    REQUIRE(q_scale);
+    REQUIRE(h_absmax_known);
+    REQUIRE(x);
+    REQUIRE(x_scale);
+    REQUIRE(w);
+    REQUIRE(w_scale);
+    NONNEG(N);
+    NONNEG(C);
+    NONNEG(H);
+    if (h_absmax_known == h_absmax || h_absmax_known == q_scale)
+        return fail(FFN_ERR_INVALID,
+                    "ffn_gateup_swiglu_quant_tiled: h_absmax_known must not alias h_absmax or q_scale");
+    if ((h_absmax && (h_absmax == x_scale || h_absmax == w_scale)) || q_scale == x_scale || q_scale == w_scale)
+        return fail(FFN_ERR_INVALID,
+                    "ffn_gateup_swiglu_quant_tiled: h_absmax and q_scale must not alias x_scale or w_scale");
+    if (ffn_status_t st = check_tiled_gemm("ffn_gateup_swiglu_quant_tiled", N, C, 2 * H)) return st;
+    if (H % 128 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup_swiglu_quant_tiled: H = %lld must be a multiple of 128",
+                    (long long)H);
+    if (tiled_bytes(N, H) >= ((int64_t)1 << 32))
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup_swiglu_quant_tiled: the codes of h exceed 4 GiB");
+    ALIGNED(q);
+    ALIGNED(x);
+    ALIGNED(w);
+    if (N == 0) {
+        // as ffn_gateup_swiglu_quant: abs-max 0, the scale from the known abs-max
+        if (h_absmax) {
+            const ffn_status_t st =
+                hip_status(ffn::launch_fill(h_absmax, 1, 0.0f, stream), "ffn_gateup_swiglu_quant_tiled");
+            if (st != FFN_OK) return st;
+        }
+        return hip_status(ffn::launch_quant(nullptr, q_scale, const_cast<float*>(h_absmax_known), nullptr, 0, false,
+                                            stream),
+                          "ffn_gateup_swiglu_quant_tiled");
+    }
+    return hip_status(ffn::launch_gemm(q, h_absmax, x, x_scale, w, w_scale, true, true, N, (int)C, (int)(2 * H),
+                                       stream, h_absmax_known, q_scale, false, false, nullptr, false, true, true),
+                      "ffn_gateup_swiglu_quant_tiled");
+}
+
+ffn_status_t ffn_down_tiled(void* out, const uint8_t* h, const float* h_scale, const uint8_t* w,
+                            const float* w_scale, int64_t N, int64_t H, int64_t C, hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(h);
+    REQUIRE(h_scale);
+    REQUIRE(w);
+    REQUIRE(w_scale);
+    NONNEG(N);
+    NONNEG(H);
+    NONNEG(C);
+    if (ffn_status_t st = check_tiled_gemm("ffn_down_tiled", N, H, C)) return st;
+    ALIGNED(out);
+    ALIGNED(h);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(out, nullptr, h, h_scale, w, w_scale, true, false, N, (int)H, (int)C, stream,
+                                       nullptr, nullptr, false, false, nullptr, false, true, true),
+                      "ffn_down_tiled");
+}
+
 // Checks shared by the decode entry points (elt: weight bytes per element).
 static ffn_status_t check_decode(const char* fn, const void* out, const void* h, const void* x, const void* wg,
                                  const void* wu, const void* wd, int64_t M, int64_t C, int64_t H, int elt,

@@ -15,6 +15,20 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// The tiled operand layout of a K-contiguous GEMM operand [R, row_bytes]
+// (row_bytes % 64 == 0): rows in groups of 64, each group one contiguous run
+// of 64 row_bytes; inside a group, for each 64-byte K-step s and each 16-row
+// sub-group i, the 1 KiB block at s * 4096 + i * 1024 holds exactly what one
+// wave-wide 16-byte-per-lane load puts into the GEMM's LDS stage: lane l's 16
+// bytes are chunk (l % 4) ^ (l / 16) of row 16 i + l / 4 at K-step s (the
+// stage's XOR swizzle).  Byte offset of byte c of row r; an aligned 16-byte
+// chunk of a row stays contiguous.
+__device__ __forceinline__ int64_t tiled_offset(int64_t r, int64_t c, int64_t row_bytes) {
+    const int rr = (int)(r & 63), lr = rr & 15;
+    const int l = 4 * lr + ((int)((c >> 4) & 3) ^ (lr >> 2));
+    return (r >> 6) * 64 * row_bytes + (c >> 6) * 4096 + (int64_t)((rr >> 4) * 1024 + l * 16) + (c & 15);
+}
+
 // bf16 bits (low 16 bits of u) -> fp32, exact.
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }

@@ -34,6 +34,15 @@
 // global loads are issued in a fixed interleave (the compiler's scheduler is
 // fenced off), one MFMA at a time.
 //
+// Tiled operands.  A load instruction above reads 16 rows x 64 bytes, half of
+// sixteen 128-byte lines (the other halves are the next K-step's).  With both
+// operands in the tiled layout (common.h, tiled_offset: the 1 KiB each load
+// puts into LDS stored contiguously, swizzle included) every load reads eight
+// whole lines, one contiguous KiB; the LDS stages, fragment reads and MFMA
+// order stay as they are, so the products are bit for bit those of the
+// row-major operands.  Only the load offsets change (and, for the e4m3 codes
+// of h from the quantising SwiGLU epilogue, the store offsets).
+//
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin; the linear id is
 // remapped so that each XCD receives a contiguous range of tiles, and inside it
 // tiles are grouped 4 weight-panels wide, so the tiles resident on one XCD at a
@@ -69,6 +78,7 @@ constexpr int kThreads = 256;   // 4 waves
 constexpr int kLoads = kBM / 4 / 16;  // load instructions per operand per wave per K-step
 constexpr int kBlockBytes = 32 * kRowBytes;  // one 32-row MFMA block of a stage
 constexpr int kGroupM = 4;
+constexpr int kTiledStep = 64 * kRowBytes;  // bytes of one K-step of a 64-row group, tiled layout
 static_assert(kAhead < kStages, "a stage is refilled only after the barrier that retires it");
 
 struct GemmArgs {
@@ -166,9 +176,11 @@ __device__ __forceinline__ void read_frags(Frags& f, const StepIO& io, int g) {
 }
 
 // Load instruction l (0 .. 2 kLoads - 1; A first) of K-step kk of the tile
-// whose slabs are `tr`, into ring slot `stage`.
+// whose slabs are `tr`, into ring slot `stage`.  kTiled: the slabs are in the
+// tiled layout, where K-step kk of a 64-row group starts kk * 4 KiB in.
+template <bool kTiled>
 __device__ __forceinline__ void load_part(const StepIO& io, const TileRsrc& tr, int stage, int kk, int l) {
-    const uint32_t kb = (uint32_t)kk * kRowBytes;
+    const uint32_t kb = (uint32_t)kk * (kTiled ? kTiledStep : kRowBytes);
     const uint32_t st = io.lds_wave + (uint32_t)(stage * kStage);
     if (l < kLoads) load_lds16(io.voff[l], tr.a, kb, st + l * 16 * kRowBytes);
     else load_lds16(io.voff[l - kLoads], tr.b, kb, st + kBM * kRowBytes + (l - kLoads) * 16 * kRowBytes);
@@ -180,7 +192,7 @@ __device__ __forceinline__ void load_part(const StepIO& io, const TileRsrc& tr, 
 // scheduling fences order instructions within a basic block only.
 // kXBf8: the x fragments (the MFMA's B operand) hold e5m2 codes, selected by
 // the instruction's B-format field; the w fragments stay e4m3.
-template <bool kFP8, bool kXBf8 = false>
+template <bool kFP8, bool kXBf8, bool kTiled>
 __device__ __forceinline__ void k_step(f32x16_t (&acc)[4][4], const Frags& cur, Frags& nxt, const GemmArgs& a,
                                        const StepIO& io, int g, const TileRsrc& tr, int ld_k) {
     constexpr int kM = kFP8 ? 16 : 32;  // MFMAs per step
@@ -207,7 +219,7 @@ __device__ __forceinline__ void k_step(f32x16_t (&acc)[4][4], const Frags& cur, 
                                                                 __builtin_bit_cast(bf16x8_t, cur.b[j][p]),
                                                                 acc[i][j], 0, 0, 0);
         }
-        if (m % kPerLoad == kPerLoad - 1) load_part(io, tr, ld_stage, ld_k, m / kPerLoad);
+        if (m % kPerLoad == kPerLoad - 1) load_part<kTiled>(io, tr, ld_stage, ld_k, m / kPerLoad);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -217,8 +229,11 @@ __device__ __forceinline__ void k_step(f32x16_t (&acc)[4][4], const Frags& cur, 
 // tile's 128 gate rows [128 tm, +128) of w followed by the matching up rows
 // [H + 128 tm, +128), so wave w takes gate rows (w & 1) = 0 or up rows
 // (w & 1) = 1, half w >> 1.  Rows past O (plain) and tokens past N are cut
-// off by num_records and load as zeros.
-template <bool kFused>
+// off by num_records and load as zeros.  Every slab starts at a multiple of
+// 64 rows, so in the tiled layout it is one 64-row group at the same byte
+// offset; a group with any valid row is read whole (the tiled operands hold
+// whole groups), one with none as zeros.
+template <bool kFused, bool kTiled>
 __device__ __forceinline__ TileRsrc tile_rsrc(const GemmArgs& a, int t, int wave) {
     int tm, tn;
     tile_coords(t, a.tiles_m, a.tiles_n, tm, tn);
@@ -232,7 +247,11 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const GemmArgs& a, int t, int wave
         wrows = min((int64_t)64, max((int64_t)0, (int64_t)a.O - wrow0));
     }
     const int64_t xrow0 = (int64_t)tn * kBN + wave * 64;
-    const int64_t xrows = min((int64_t)64, max((int64_t)0, a.N - xrow0));
+    int64_t xrows = min((int64_t)64, max((int64_t)0, a.N - xrow0));
+    if (kTiled) {
+        wrows = wrows > 0 ? 64 : 0;
+        xrows = xrows > 0 ? 64 : 0;
+    }
     TileRsrc r;
     r.a = make_rsrc(a.w + wrow0 * kb, (uint32_t)(wrows * kb));
     r.b = make_rsrc(a.x + xrow0 * kb, (uint32_t)(xrows * kb));
@@ -308,7 +327,7 @@ __device__ __forceinline__ u32x4_t regroup_runs(uint32_t x0, uint32_t x1, uint32
 // at H + o) from gu [N, 2H] (a.aux, same layout; it may be out itself), with
 // swiglu_bwd_pair, keeping the running abs-max of the stored dgu.  Its loads
 // of g and u are double-buffered by half-blocks of 32 tokens x 64 features.
-template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kSwiBwd = false>
+template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kSwiBwd, bool kTiled>
 __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmArgs& a, int t, float s, float qinv,
                                               int wm, int wn, int fr, int fh, float& amax) {
     int tm, tn;
@@ -318,7 +337,11 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     const int64_t n0 = (int64_t)tn * kBN;
     constexpr int kOutElt = kQuant ? 1 : 2;  // bytes per output element
     uint8_t* base = reinterpret_cast<uint8_t*>(a.out) + n0 * a.ld_out * kOutElt;
-    const int64_t rem = (a.N - n0) * (int64_t)a.ld_out * kOutElt;
+    // tiled e4m3 h: the tile's rows are whole 64-row groups from the same
+    // byte offset, with rows past N skipped by offset (not a prefix there);
+    // every other output is row-major, its rows past N cut off by the range
+    const int64_t rows_left = (kTiled && kQuant) ? (a.N - n0 + 63) / 64 * 64 : a.N - n0;
+    const int64_t rem = rows_left * (int64_t)a.ld_out * kOutElt;
     const uint32_t nrec = (uint32_t)(rem < ((int64_t)1 << 30) ? rem : ((int64_t)1 << 30));
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)nrec, 0x00020000);
     const uint32_t row_bytes = (uint32_t)a.ld_out * kOutElt;
@@ -487,7 +510,9 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
                     amax = absmax_acc(amax, ok ? m : 0.0f);
                     const u32x4_t v = regroup_runs(d[0], d[1], d[2], d[3]);
                     const int o = tm * 128 + wm * 64 + i * 32 + 16 * q + 8 * fh;
-                    const uint32_t off = (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * kOutElt;
+                    uint32_t off = (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * kOutElt;
+                    if (kTiled && kQuant)  // tiled codes; rows past N skipped by offset
+                        off = ok ? (uint32_t)tiled_offset(r_base + 32 * j, o, row_bytes) : 0x7fffffffu;
                     if (kQuant) {
                         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
                         const u32x2_t c = {
@@ -504,13 +529,15 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     }
 }
 
-template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kXBf8 = false, bool kSwiBwd = false>
+template <bool kFP8, bool kFused, bool kQuant, bool kAccum, bool kXBf8 = false, bool kSwiBwd = false,
+          bool kTiled = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a) {
     static_assert(kFused || !kQuant, "quantised output is a SwiGLU epilogue");
     static_assert(!(kFused && kAccum), "accumulation is a plain-output epilogue");
     static_assert(kFP8 || !kXBf8, "e5m2 x is an FP8 operand");
     static_assert(!(kSwiBwd && (kFused || kAccum)), "the SwiGLU backward is a plain-output epilogue of its own");
+    static_assert(!kTiled || (kFP8 && !kAccum && !kXBf8 && !kSwiBwd), "tiled operands: the e4m3 forward products");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
     constexpr int kStoreCnt = epilogue_stores<kFused>();
@@ -549,7 +576,9 @@ void gemm_kernel(GemmArgs a) {
     const int lrow = lane >> 2;
     const int lch = (lane & 3) ^ ((lane >> 4) & 3);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) io.voff[i] = (uint32_t)(i * 16 + lrow) * (uint32_t)a.K_bytes + (uint32_t)(lch << 4);
+    for (int i = 0; i < kLoads; ++i)
+        io.voff[i] = kTiled ? (uint32_t)(i * 1024 + lane * 16)
+                            : (uint32_t)(i * 16 + lrow) * (uint32_t)a.K_bytes + (uint32_t)(lch << 4);
     io.lds_wave = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 16 * kLoads * kRowBytes);
 
@@ -571,8 +600,8 @@ void gemm_kernel(GemmArgs a) {
     // one tile ahead; such problems get one tile per workgroup (G = T), where
     // every load past the tile's own steps is one of these stand-ins.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    TileRsrc tr_cur = tile_rsrc<kFused>(a, b, wave_u);
-    TileRsrc tr_nxt = tile_rsrc<kFused>(a, b + G < T ? b + G : b, wave_u);
+    TileRsrc tr_cur = tile_rsrc<kFused, kTiled>(a, b, wave_u);
+    TileRsrc tr_nxt = tile_rsrc<kFused, kTiled>(a, b + G < T ? b + G : b, wave_u);
     // K-step of the load issued during step kk of a tile (tile-relative
     // kk + kAhead, wrapped into the next tile)
     auto wrap_k = [&](int k) {
@@ -597,7 +626,7 @@ void gemm_kernel(GemmArgs a) {
         const TileRsrc tr = select_rsrc(g < KT, tr_cur, tr_nxt);
         const int k = g < KT ? g : wrap_k(g);
 #pragma unroll
-        for (int l = 0; l < 2 * kLoads; ++l) load_part(io, tr, g, k, l);
+        for (int l = 0; l < 2 * kLoads; ++l) load_part<kTiled>(io, tr, g, k, l);
     }
     // Stand-ins for the stores of a previous tile's epilogue (dropped by the
     // range check: num_records is 0), so that the first tile's first two
@@ -629,10 +658,10 @@ void gemm_kernel(GemmArgs a) {
             const TileRsrc tr = select_rsrc(own, tr_cur, tr_nxt);
             const int k0 = own ? kAhead : wrap_k(kAhead);
             const int k1 = own ? kAhead + 1 : wrap_k(kAhead + 1);
-            k_step<kFP8, kXBf8>(acc, f0, f1, a, io, g, tr, k0);
+            k_step<kFP8, kXBf8, kTiled>(acc, f0, f1, a, io, g, tr, k0);
             wait_vmcnt<kWait + kStoreCnt>();
             barrier();
-            k_step<kFP8, kXBf8>(acc, f1, f0, a, io, g + 1, tr, k1);
+            k_step<kFP8, kXBf8, kTiled>(acc, f1, f0, a, io, g + 1, tr, k1);
             wait_vmcnt<kWait + kStoreCnt>();
             barrier();
             g += 2;
@@ -641,17 +670,17 @@ void gemm_kernel(GemmArgs a) {
             const bool own = kk + kAhead < KT;
             const TileRsrc tr = select_rsrc(own, tr_cur, tr_nxt);
             const int k0 = own ? kk + kAhead : wrap_k(kk + kAhead);
-            k_step<kFP8, kXBf8>(acc, f0, f1, a, io, g, tr, k0);
+            k_step<kFP8, kXBf8, kTiled>(acc, f0, f1, a, io, g, tr, k0);
             wait_vmcnt<kWait>();
             barrier();
-            k_step<kFP8, kXBf8>(acc, f1, f0, a, io, g + 1, tr, k0 + 1);
+            k_step<kFP8, kXBf8, kTiled>(acc, f1, f0, a, io, g + 1, tr, k0 + 1);
             wait_vmcnt<kWait>();
             barrier();
         }
-        tile_epilogue<kFP8, kFused, kQuant, kAccum, kSwiBwd>(acc, a, c_t, s, qinv, wm, wn, fr, fh, amax);
+        tile_epilogue<kFP8, kFused, kQuant, kAccum, kSwiBwd, kTiled>(acc, a, c_t, s, qinv, wm, wn, fr, fh, amax);
         const int t2 = c_t + 2 * G;
         tr_cur = tr_nxt;
-        tr_nxt = tile_rsrc<kFused>(a, t2 < T ? t2 : (c_t + G < T ? c_t + G : c_t), wave_u);
+        tr_nxt = tile_rsrc<kFused, kTiled>(a, t2 < T ? t2 : (c_t + G < T ? c_t + G : c_t), wave_u);
     }
     // the loads past the end still write the ring: let them land before the
     // workgroup's LDS is reused or released
@@ -660,6 +689,33 @@ void gemm_kernel(GemmArgs a) {
         __syncthreads();
         block_absmax_commit(amax, reinterpret_cast<float*>(lds), a.absmax);
     }
+}
+
+// The tiled layout of a [rows, row_bytes] operand: thread t writes the
+// t-th 16 bytes of the output (whole 64-row groups), read from the row and
+// chunk that tiled_offset puts there (zeros past `rows`).
+__global__ __launch_bounds__(256) void tile_pack_kernel(uint8_t* __restrict__ out, const uint8_t* __restrict__ in,
+                                                        int64_t rows, int64_t row_bytes, int64_t chunks) {
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < chunks;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t off = t * 16, group_bytes = 64 * row_bytes;
+        const int64_t grp = off / group_bytes, in_grp = off - grp * group_bytes;
+        const int64_t step = in_grp >> 12;
+        const int blk = (int)(in_grp & 4095), l = (blk & 1023) >> 4;
+        const int64_t r = 64 * grp + 16 * (blk >> 10) + (l >> 2);
+        const int64_t c = 64 * step + 16 * ((l & 3) ^ (l >> 4));
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (r < rows) v = *reinterpret_cast<const uint4*>(in + r * row_bytes + c);
+        *reinterpret_cast<uint4*>(out + off) = v;
+    }
+}
+
+hipError_t launch_tile_pack(uint8_t* out, const uint8_t* in, int64_t rows, int64_t row_bytes, hipStream_t s) {
+    const int64_t chunks = (rows + 63) / 64 * 64 * row_bytes / 16;
+    if (chunks == 0) return hipSuccess;
+    const int64_t blocks = min((chunks + 255) / 256, (int64_t)65536);
+    hipLaunchKernelGGL(tile_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, in, rows, row_bytes, chunks);
+    return hipGetLastError();
 }
 
 int device_cu_count() {
@@ -703,8 +759,9 @@ static int persistent_grid(int T) {
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2,
-                       const void* swiglu_gu, bool tile_grid, bool clear_absmax) {
+                       const void* swiglu_gu, bool tile_grid, bool clear_absmax, bool tiled) {
     if (x_e5m2 && (!fp8 || fuse_swiglu)) return hipErrorInvalidValue;
+    if (tiled && (!fp8 || accumulate || x_e5m2 || swiglu_gu)) return hipErrorInvalidValue;
     const bool swi = swiglu_gu != nullptr;
     if (swi && (fuse_swiglu || accumulate)) return hipErrorInvalidValue;
     if (absmax && (fuse_swiglu || swi || N == 0) && clear_absmax) {
@@ -735,7 +792,12 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const int KT = a.K_bytes / kRowBytes;
     const dim3 grid((unsigned)(KT >= kAhead && !tile_grid ? persistent_grid(T) : T)), block(kThreads);
     const bool acc = accumulate && !fuse_swiglu;
-    if (swi) {
+    if (tiled) {
+        if (quant) hipLaunchKernelGGL((gemm_kernel<true, true, true, false, false, false, true>), grid, block, 0, s, a);
+        else if (fuse_swiglu)
+            hipLaunchKernelGGL((gemm_kernel<true, true, false, false, false, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<true, false, false, false, false, false, true>), grid, block, 0, s, a);
+    } else if (swi) {
         if (fp8 && x_e5m2) hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true, true>), grid, block, 0, s, a);
         else if (fp8) hipLaunchKernelGGL((gemm_kernel<true, false, false, false, false, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gemm_kernel<false, false, false, false, false, true>), grid, block, 0, s, a);

@@ -32,12 +32,22 @@ hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t
 // swiglu_gu (plain output, no accumulation): the product is dh = dL/dh of
 // h = silu(g) * u, rounded to bf16; out receives dgu [N, 2O] computed from
 // gu [N, 2O] (which out may be), and absmax max |dgu|.  tile_grid: one
-// workgroup per output tile (for products that run beside others).
+// workgroup per output tile (for products that run beside others).  tiled
+// (e4m3, no accumulation, e5m2 or SwiGLU backward): x and w in the tiled
+// layout (whole 64-row groups; common.h, tiled_offset), and with q_absmax the
+// e4m3 codes of h stored in it too.
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr,
                        bool accumulate = false, bool x_e5m2 = false, const void* swiglu_gu = nullptr,
-                       bool tile_grid = false, bool clear_absmax = true);
+                       bool tile_grid = false, bool clear_absmax = true, bool tiled = false);
+// The tiled layout of a [rows, row_bytes] operand (row_bytes % 64 == 0), in
+// whole 64-row groups: rows past `rows` in the last group are zero.
+hipError_t launch_tile_pack(uint8_t* out, const uint8_t* in, int64_t rows, int64_t row_bytes, hipStream_t s);
+// launch_quant with the codes of x [rows, cols] stored in the tiled layout
+// (cols % 64 == 0; rows past `rows` in the last group are left as they are).
+hipError_t launch_quant_tiled(uint8_t* q, float* scale, float* absmax, const uint16_t* x, int64_t rows, int64_t cols,
+                              hipStream_t s, float* clear = nullptr);
 
 // Backward: out[c, r] = in[r, c], zero for rows <= r < ld_out.  (in_bytes,
 // out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3

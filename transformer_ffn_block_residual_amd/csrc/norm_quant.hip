@@ -208,6 +208,16 @@ __global__ __launch_bounds__(256) void absmax_kernel(float* out, const uint16_t*
 // product x*inv.  Block 0 also writes the scale absmax/448 and, when given,
 // zero to *clear (another tensor's abs-max word, for its next producer).
 
+// 16 bf16 values (v0: the first 8) -> their 16 e4m3 codes of x * inv.
+__device__ __forceinline__ uint4 quant16(const uint4 v0, const uint4 v1, float inv) {
+    uint4 o;
+    o.x = pack_e4m3x4(bf16lo(v0.x) * inv, bf16hi(v0.x) * inv, bf16lo(v0.y) * inv, bf16hi(v0.y) * inv);
+    o.y = pack_e4m3x4(bf16lo(v0.z) * inv, bf16hi(v0.z) * inv, bf16lo(v0.w) * inv, bf16hi(v0.w) * inv);
+    o.z = pack_e4m3x4(bf16lo(v1.x) * inv, bf16hi(v1.x) * inv, bf16lo(v1.y) * inv, bf16hi(v1.y) * inv);
+    o.w = pack_e4m3x4(bf16lo(v1.z) * inv, bf16hi(v1.z) * inv, bf16lo(v1.w) * inv, bf16hi(v1.w) * inv);
+    return o;
+}
+
 __global__ __launch_bounds__(256) void quant_kernel(uint8_t* __restrict__ q, float* __restrict__ scale_out,
                                                     const float* __restrict__ absmax,
                                                     const uint16_t* __restrict__ x, int64_t n,
@@ -222,21 +232,51 @@ __global__ __launch_bounds__(256) void quant_kernel(uint8_t* __restrict__ q, flo
     const int64_t base = t * 16;
     if (base + 16 <= n) {
         const uint4* x4 = reinterpret_cast<const uint4*>(x + base);
-        const uint4 v0 = x4[0], v1 = x4[1];
-        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&v0);
-        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&v1);
-        uint4 o;
-        o.x = pack_e4m3x4(bf16lo(p0[0]) * inv, bf16hi(p0[0]) * inv, bf16lo(p0[1]) * inv, bf16hi(p0[1]) * inv);
-        o.y = pack_e4m3x4(bf16lo(p0[2]) * inv, bf16hi(p0[2]) * inv, bf16lo(p0[3]) * inv, bf16hi(p0[3]) * inv);
-        o.z = pack_e4m3x4(bf16lo(p1[0]) * inv, bf16hi(p1[0]) * inv, bf16lo(p1[1]) * inv, bf16hi(p1[1]) * inv);
-        o.w = pack_e4m3x4(bf16lo(p1[2]) * inv, bf16hi(p1[2]) * inv, bf16lo(p1[3]) * inv, bf16hi(p1[3]) * inv);
-        *reinterpret_cast<uint4*>(q + base) = o;
+        *reinterpret_cast<uint4*>(q + base) = quant16(x4[0], x4[1], inv);
     } else if (base < n) {
         for (int64_t i = base; i < n; ++i) {
             const float v = bf16lo(x[i]) * inv;
             q[i] = (uint8_t)(pack_e4m3x4(v, 0.0f, 0.0f, 0.0f) & 0xff);
         }
     }
+}
+
+// The same codes stored in the tiled GEMM operand layout of [rows, cols]
+// (common.h, tiled_offset; cols % 64 == 0, rows * cols / 16 < 2^32).  In
+// that layout the 64 codes of K-step s of rows 2m and 2m + 1 share one
+// 128-byte line, so a wave takes such a row pair over 8 K-steps: lane l
+// quantises the 16 elements of chunk l % 4 of K-step (l / 4) % 8 of row
+// 2m + l / 32.  Each wave reads 1 KiB of each of its two rows and stores
+// eight whole lines.  Rows past `rows` are not written.
+__global__ __launch_bounds__(256) void quant_tiled_kernel(uint8_t* __restrict__ q, float* __restrict__ scale_out,
+                                                          const float* __restrict__ absmax,
+                                                          const uint16_t* __restrict__ x, int64_t rows,
+                                                          int64_t cols, float* __restrict__ clear) {
+    float scale, inv;
+    scale_pair(*absmax, scale, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *scale_out = scale;
+        if (clear) *clear = 0.0f;
+    }
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t wv = t >> 6, l = t & 63;
+    const uint32_t steps = (uint32_t)(cols >> 6), runs = (steps + 7) / 8;
+    const uint32_t pair = wv / runs, run = wv - pair * runs;
+    const int64_t r = 2 * (int64_t)pair + (l >> 5);
+    const uint32_t s = run * 8 + ((l >> 2) & 7);
+    if (r >= rows || s >= steps) return;
+    const int64_t c = 64 * (int64_t)s + 16 * (l & 3);
+    const uint4* x4 = reinterpret_cast<const uint4*>(x + r * cols + c);
+    *reinterpret_cast<uint4*>(q + tiled_offset(r, c, cols)) = quant16(x4[0], x4[1], inv);
+}
+
+hipError_t launch_quant_tiled(uint8_t* q, float* scale, float* absmax, const uint16_t* x, int64_t rows, int64_t cols,
+                              hipStream_t s, float* clear) {
+    const int64_t waves = (rows + 1) / 2 * (((cols >> 6) + 7) / 8);
+    const int64_t blocks = waves > 0 ? (waves + 3) / 4 : 1;  // no rows: still writes the scale
+    hipLaunchKernelGGL(quant_tiled_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, absmax, x, rows, cols,
+                       clear);
+    return hipGetLastError();
 }
 
 hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_t s) {
