@@ -238,3 +238,30 @@ def test_tiled_block_replays_from_a_hip_graph(blk, B):
                 assert torch.equal(getattr(b, n)[masks[n]], eager[n][masks[n]]), (rep, n)
             else:
                 assert torch.equal(getattr(b, n), eager[n]), (rep, n)
+
+
+@pytest.mark.gpu
+def test_tiled_zero_rows(B):
+    """No rows: nothing is written but the per-tensor words, as for the
+    row-major calls (the _acc word as found, the known abs-max's scale, an
+    abs-max of no elements 0, the cleared word 0)."""
+    say("tiled zero rows")
+    C, H = 256, 256
+    xs, ws = dev_f32([0.5]), dev_f32([0.25])
+    x, w, wd = empty_u8(64 * C).zero_(), empty_u8(2 * H * C).zero_(), empty_u8(C * H).zero_()
+    h = empty_bf16(1, H).fill_(3.0)
+    acc = dev_f32([7.0])
+    B.ffn_gateup_acc_tiled(h, acc, x, xs, w, ws, 0, C, H)
+    q, qs, ham = empty_u8(64 * H).fill_(0x11), dev_f32([-1.0]), dev_f32([7.0])
+    B.ffn_gateup_swiglu_quant_tiled(q, qs, ham, dev_f32([3.5]), x, xs, w, ws, 0, C, H)
+    out = empty_bf16(1, C).fill_(2.0)
+    B.ffn_down_tiled(out, empty_u8(64 * H).zero_(), xs, wd, ws, 0, H, C)
+    qy, sy, clear = empty_u8(64 * C).fill_(0x22), dev_f32([-1.0]), dev_f32([5.0])
+    B.ffn_quant_absmax_clear_tiled(qy, sy, dev_f32([3.5]), empty_bf16(1, C).zero_(), 0, C, clear)
+    packed = empty_u8(64 * C).fill_(0x33)
+    B.ffn_tile_pack(packed, empty_u8(C).zero_(), 0, C)
+    torch.cuda.synchronize()
+    assert acc.item() == 7.0 and ham.item() == 0.0 and clear.item() == 0.0
+    assert qs.item() == sy.item() == np.float32(3.5) / np.float32(448.0)
+    assert torch.all(h == 3.0) and torch.all(out == 2.0)
+    assert torch.all(q == 0x11) and torch.all(qy == 0x22) and torch.all(packed == 0x33)
