@@ -99,7 +99,7 @@ def parse():
     p.add_argument("--grad-dtype", default="e4m3", choices=["e4m3", "e5m2"],
                    help="FP8 backward: the format of the quantised gradients (weights and activations stay e4m3)")
     p.add_argument("--gemm-layout", default="tiled", choices=["tiled", "rows"],
-                   help="FP8 block workloads: the e4m3 GEMM operands (weights, codes of y and h) in the tiled "
+                   help="block workloads: the GEMM operands (weights; y and h, or their e4m3 codes) in the tiled "
                         "layout (ffn_tile_pack; every GEMM load one contiguous KiB) or row-major")
     p.add_argument("--known-h-absmax", action="store_true",
                    help="FP8 block workloads: quantise h in the gate+up epilogue with the previous step's abs-max "
@@ -144,7 +144,7 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
     weight-gradient GEMMs share one kernel (the up projection's is the second
     of each step), and the forward's two row-major activation quantisations
     share one kernel after the two weight quantisations of the set-up.  The
-    FP8 forward's GEMMs and quantisations run on tiled operands unless
+    forward's GEMMs (and FP8 quantisations) run on tiled operands unless
     rows_layout; the row-major forms' keys carry "_rows"."""
     from transformer_ffn_block_residual_amd import workloads as W
     w = W.WORKLOADS[workload]
@@ -167,10 +167,10 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
     elt = 1 if w.fp8 else 2
     fp8 = "true" if w.fp8 else "false"
     dt = "e4m3" if w.fp8 else "bf16"
-    tiled = w.fp8 and not rows_layout
+    tiled = not rows_layout
     tl = "true" if tiled else "false"
     lay = ", tiled operands" if tiled else ""
-    tag = "_rows" if w.fp8 and rows_layout else ""
+    tag = "_rows" if rows_layout else ""
     every = (0, 1, 0)
     if known_h_absmax:
         # reads x and w, writes the e4m3 codes of h
@@ -179,13 +179,16 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
                  f"{'_tiled' if tiled else ''}, N={N} C={C} H={H}", N * C * elt + 2 * H * C * elt + N * H, every)]
     specs = [
         (f"gateup{tag}_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, true, false, false, false, false, {tl}>"],
-         f"gemm_kernel ({dt}, fused SwiGLU{lay}) of ffn_gateup{'_acc_tiled' if tiled else ''}, N={N} C={C} H={H}",
+         f"gemm_kernel ({dt}, fused SwiGLU{lay}) of ffn_gateup"
+         f"{('_acc_tiled' if w.fp8 else '_tiled_bf16') if tiled else ''}, N={N} C={C} H={H}",
          N * C * elt + 2 * H * C * elt + N * H * 2, every),
         (f"down{tag}_{workload}", "gemm.hip", [f"gemm_kernel<{fp8}, false, false, false, false, false, {tl}>"],
-         f"gemm_kernel ({dt}{lay}) of ffn_down{'_tiled' if tiled else ''}, N={N} H={H} C={C}",
+         f"gemm_kernel ({dt}{lay}) of ffn_down{('_tiled' if w.fp8 else '_tiled_bf16') if tiled else ''}, "
+         f"N={N} H={H} C={C}",
          N * H * elt + C * H * elt + N * C * 2, every),
         # reads inp and addend, writes r and y, rstd; the weight once
-        (f"rmsnorm_{workload}", "norm_quant.hip", ["rmsnorm_kernel<"],
+        # (the bf16 block's RMSNorm stores y for the tiled GEMM: a form of its own)
+        (f"rmsnorm{'' if w.fp8 else tag}_{workload}", "norm_quant.hip", ["rmsnorm_kernel<"],
          f"rmsnorm_kernel (residual add + RMSNorm + rstd{' + abs-max' if w.fp8 else ''}) of ffn_rmsnorm_fwd, "
          f"N={N} C={C}",
          4 * N * C * 2 + N * 4 + C * 2, every),
@@ -441,7 +444,7 @@ def bench_block(a, torch, np, B, block, W):
     def dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    tiled = w.fp8 and a.gemm_layout == "tiled"
+    tiled = a.gemm_layout == "tiled"
     pre = block.PrefillBlock(N, C, H, w.eps, w.fp8, tiled=tiled)
     pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
     inp, addend = dev(d["inp"]), dev(d["addend"])
@@ -506,6 +509,8 @@ def bench_block(a, torch, np, B, block, W):
             B.ffn_rmsnorm_fwd(pre.y, pre.rstd, pre.r, pre.am_y, inp, addend, pre.w_norm, pre.eps, N, C, stream)
         elif w.fp8:
             B.ffn_rmsnorm_fwd_acc(pre.y, pre.rstd, pre.r, pre.am_y, inp, addend, pre.w_norm, pre.eps, N, C, stream)
+        elif tiled:
+            B.ffn_rmsnorm_fwd_tiled(pre.y, pre.rstd, pre.r, None, inp, addend, pre.w_norm, pre.eps, N, C, stream)
         else:
             B.ffn_rmsnorm_fwd(pre.y, pre.rstd, pre.r, None, inp, addend, pre.w_norm, pre.eps, N, C, stream)
         m1 = tm.mark() if tm else None
@@ -558,12 +563,18 @@ def bench_block(a, torch, np, B, block, W):
             m2 = m1
             if serial_at == "mid":
                 m2 = decode_serial(i, tm, stream)
-            B.ffn_gateup(pre.h, None, pre.y, None, pre.w_gu, None, E, 1, N, C, H, stream)
+            if tiled:
+                B.ffn_gateup_tiled_bf16(pre.h, None, pre.y, pre.w_gu, N, C, H, stream)
+            else:
+                B.ffn_gateup(pre.h, None, pre.y, None, pre.w_gu, None, E, 1, N, C, H, stream)
             m3 = tm.mark() if tm else None
             m4 = m3
             if overlap == "tail":
                 fork_ev.record(stream)
-            B.ffn_down(pre.out, pre.h, None, pre.w_d, None, E, N, H, C, stream)
+            if tiled:
+                B.ffn_down_tiled_bf16(pre.out, pre.h, pre.w_d, N, H, C, stream)
+            else:
+                B.ffn_down(pre.out, pre.h, None, pre.w_d, None, E, N, H, C, stream)
         if overlap == "tail":
             decode_on_side(i, tm, stream, forked=True)
         m5 = tm.mark() if tm else None
@@ -611,7 +622,7 @@ def bench_block(a, torch, np, B, block, W):
            "N": N, "C": C, "H": H, "decode_M": M, "seed": w.seed,
            **({"decode_overlap": overlap, "decode_at": serial_at,
                "decode_layout": "packed" if decode_packed(a, M) else "rows"} if M else {}),
-           **({"gemm_operands": "tiled" if tiled else "row-major"} if w.fp8 else {}),
+           "gemm_operands": "tiled" if tiled else "row-major",
            "quant": ("per-tensor abs-max e4m3 activations and weights" if w.fp8 else "none (bf16)")
            + ("; h quantised in the gate+up epilogue with the previous step's abs-max" if known else "")
            + ("; decode: e4m3 weights, per-row fp32 scales, bf16 activations" if M else "")}

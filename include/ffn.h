@@ -205,15 +205,16 @@ ffn_status_t ffn_down(void* out, const void* h, const float* h_scale,
                       int64_t N, int64_t H, int64_t C, hipStream_t stream);
 
 /* ---------------------------------------------------------- tiled operands
- * The e4m3 prefill products on operands stored in this library's tiled
- * layout instead of row-major: the same products as ffn_gateup_acc,
+ * The prefill products on operands stored in this library's tiled layout
+ * instead of row-major: the same products as ffn_gateup_acc,
  * ffn_gateup_swiglu_quant and ffn_down (bit for bit: the same sums in the
  * same order), with every global load of the GEMM reading one contiguous
  * KiB.  The pages fix only the row-major tensors; the layout is a storage
  * choice of this library, made once for the weights (ffn_tile_pack) and by
  * the quantisers for the activations.
  *
- * Layout of a [R, K] e4m3 operand (K bytes per row, K % 64 == 0): rows in
+ * Layout of a [R, K] operand (K bytes per row, K % 64 == 0; e4m3 codes or
+ * bf16 values alike): rows in
  * groups of 64, group g at byte g*64*K; inside a group, K-step s (bytes
  * 64s .. 64s+63 of each row) at s*4096, and its 16-row sub-group i at
  * + i*1024; there, lane l = 0..63 holds 16 bytes at + 16*l: bytes
@@ -266,6 +267,23 @@ ffn_status_t ffn_gateup_swiglu_quant_tiled(uint8_t* q, float* q_scale, float* h_
 ffn_status_t ffn_down_tiled(void* out, const uint8_t* h, const float* h_scale, const uint8_t* w,
                             const float* w_scale, int64_t N, int64_t H, int64_t C,
                             hipStream_t stream);
+
+/* The bf16 block on tiled operands.  ffn_rmsnorm_fwd with y [N, C] bf16
+ * stored tiled (rows of 2C bytes: ffn_tile_bytes(N, 2C) bytes; rows past N
+ * are left as found; y must not overlap inp, addend or residual_out, and
+ * C % 32 == 0); ffn_gateup (BF16, fuse_swiglu = 1) with x [N, C] and w
+ * [2H, C] tiled and h [N, H] stored tiled (out_absmax nullable, as there);
+ * ffn_down (BF16) with h and w [C, H] tiled and out row-major.  [llmq model]
+ * LLamaModel::_forward_block (fused_residual_rmsnorm_forward, forward_qmm,
+ * swiglu_forward).  Results equal the row-major calls' bit for bit.
+ * Supported as the row-major calls, and each tiled operand < 4 GiB. */
+ffn_status_t ffn_rmsnorm_fwd_tiled(void* y, float* rstd, void* residual_out, float* absmax,
+                                   const void* inp, const void* addend, const void* weight,
+                                   float eps, int64_t N, int64_t C, hipStream_t stream);
+ffn_status_t ffn_gateup_tiled_bf16(void* h, float* h_absmax, const void* x, const void* w,
+                                   int64_t N, int64_t C, int64_t H, hipStream_t stream);
+ffn_status_t ffn_down_tiled_bf16(void* out, const void* h, const void* w, int64_t N, int64_t H,
+                                 int64_t C, hipStream_t stream);
 
 /* FP8-weight, bf16-activation decode FFN for M tokens (split-SiLU arm).
  * [metrale] DenseFfnLayer::forward, FP8 arm: w8a16_gemv_dual (gate and up in

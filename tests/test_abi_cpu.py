@@ -44,7 +44,8 @@ def test_header_declares_the_entry_points():
               "ffn_rmsnorm_bwd_scratch_bytes", "ffn_last_error", "ffn_version", "ffn_matmul_tn_swiglu_bwd_acc",
               "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc", "ffn_tile_bytes",
               "ffn_tile_pack", "ffn_quant_absmax_clear_tiled", "ffn_gateup_acc_tiled",
-              "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled"]:
+              "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled", "ffn_rmsnorm_fwd_tiled", "ffn_gateup_tiled_bf16",
+              "ffn_down_tiled_bf16"]:
         assert n in names
 
 
@@ -185,6 +186,21 @@ def test_tiled_layout_validation(lib):
     assert d(A, A, Z, A, S, 64, 700, 256, None) == UNSUPPORTED
     assert d(A, A, Z, A, S, 64, 768, 200, None) == UNSUPPORTED
     assert d(None, A, Z, A, S, 64, 768, 256, None) == INVALID
+    r = lib.ffn_rmsnorm_fwd_tiled              # y, rstd, res, absmax, inp, addend, w, eps, N, C
+    Y, X = 0x100000, 0x200000
+    assert r(Y, A, None, None, X, None, A, 1e-5, 64, 200, None) == UNSUPPORTED  # C % 32
+    assert r(X + 64, A, None, None, X, None, A, 1e-5, 64, 256, None) == INVALID  # tiled y overlaps inp
+    assert "overlap" in _err(lib)
+    assert r(0x300040, A, 0x400000, None, X, 0x300000, A, 1e-5, 64, 256, None) == INVALID  # overlaps addend
+    gb = lib.ffn_gateup_tiled_bf16             # h, absmax, x, w, N, C, H
+    assert gb(A, None, A, A, 64, 200, 768, None) == UNSUPPORTED
+    assert gb(A, None, A, A, 64, 256, 100, None) == UNSUPPORTED
+    assert gb(None, None, A, A, 64, 256, 768, None) == INVALID
+    assert gb(A, None, MIS, A, 64, 256, 768, None) == UNSUPPORTED
+    db = lib.ffn_down_tiled_bf16               # out, h, w, N, H, C
+    assert db(A, A, A, 64, 700, 256, None) == UNSUPPORTED
+    assert db(A, None, A, 64, 768, 256, None) == INVALID
+    assert db(A, A, A, -1, 768, 256, None) == INVALID
 
 
 def test_decode_validation(lib):

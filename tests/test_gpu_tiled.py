@@ -265,3 +265,81 @@ def test_tiled_zero_rows(B):
     assert qs.item() == sy.item() == np.float32(3.5) / np.float32(448.0)
     assert torch.all(h == 3.0) and torch.all(out == 2.0)
     assert torch.all(q == 0x11) and torch.all(qy == 0x22) and torch.all(packed == 0x33)
+
+
+# ----------------------------------------------------------------------------- the bf16 block on tiled operands
+
+def _bytes_of_bf16(t, rows, cols):
+    """A row-major bf16 device tensor as its [rows, 2 cols] bytes."""
+    return host_bits(t).reshape(rows, cols).view(np.uint8).reshape(rows, 2 * cols)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,C,add", [(1, 128, False), (100, 512, True), (300, 4096, True), (64, 8192, False),
+                                     (8192, 3584, True)])
+def test_rmsnorm_tiled_y_is_the_row_major_y_moved(B, N, C, add):
+    say(f"rmsnorm tiled y N={N} C={C} add={add}")
+    d = W.block_inputs(N, C, 128, seed=N + C)
+    inp, w = dev_bf16(d["inp"]), dev_bf16(d["w_norm"])
+    addend = dev_bf16(d["addend"]) if add else None
+    y1, r1, s1, a1 = empty_bf16(N, C), empty_bf16(N, C) if add else None, empty_f32(N), empty_f32(1)
+    B.ffn_rmsnorm_fwd(y1, s1, r1, a1, inp, addend, w, 1e-5, N, C)
+    y2 = empty_bf16(B.ffn_tile_bytes(N, 2 * C) // 2).fill_(-5.0)
+    r2, s2, a2 = empty_bf16(N, C) if add else None, empty_f32(N), empty_f32(1)
+    B.ffn_rmsnorm_fwd_tiled(y2, s2, r2, a2, inp, addend, w, 1e-5, N, C)
+    torch.cuda.synchronize()
+    valid = tiled_ref(np.ones((N, 2 * C), np.uint8)).astype(bool)
+    got = host_bits(y2).view(np.uint8)
+    assert np.array_equal(got[valid], tiled_ref(_bytes_of_bf16(y1, N, C))[valid])
+    pad = host_bits(y2).view(np.uint8)[~valid]
+    assert np.array_equal(pad, np.tile(host_bits(empty_bf16(1).fill_(-5.0)).view(np.uint8), pad.size // 2))
+    assert torch.equal(s1, s2) and torch.equal(a1, a2) and (not add or torch.equal(r1, r2))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,C,H", [(1, 128, 128), (300, 512, 384), (1000, 384, 640), (4096, 4096, 14336)])
+def test_tiled_bf16_gemms_equal_the_row_major_ones(B, N, C, H):
+    say(f"tiled bf16 gemms N={N} C={C} H={H}")
+    x = W.normal_bf16((N, C), 1.0, N + 1, 21)
+    wgu = W.normal_bf16((2 * H, C), 0.05, C + 2, 22)
+    hh = W.normal_bf16((N, H), 1.0, N + 3, 23)
+    wd = W.normal_bf16((C, H), 0.05, H + 4, 24)
+    xd, wgud, hd, wdd = dev_bf16(x), dev_bf16(wgu), dev_bf16(hh), dev_bf16(wd)
+
+    def tiled(t, rows, cols):
+        o = empty_bf16(B.ffn_tile_bytes(rows, 2 * cols) // 2)
+        B.ffn_tile_pack(o.view(torch.uint8), t.view(torch.uint8), rows, 2 * cols)
+        return o
+    xt, wgut, ht, wdt = tiled(xd, N, C), tiled(wgud, 2 * H, C), tiled(hd, N, H), tiled(wdd, C, H)
+    h1, am1 = empty_bf16(N, H), empty_f32(1)
+    B.ffn_gateup(h1, am1, xd, None, wgud, None, B.FFN_BF16, 1, N, C, H)
+    h2, am2 = empty_bf16(B.ffn_tile_bytes(N, 2 * H) // 2).fill_(-5.0), empty_f32(1)
+    B.ffn_gateup_tiled_bf16(h2, am2, xt, wgut, N, C, H)
+    o1, o2 = empty_bf16(N, C), empty_bf16(N, C)
+    B.ffn_down(o1, hd, None, wdd, None, B.FFN_BF16, N, H, C)
+    B.ffn_down_tiled_bf16(o2, ht, wdt, N, H, C)
+    torch.cuda.synchronize()
+    valid = tiled_ref(np.ones((N, 2 * H), np.uint8)).astype(bool)
+    got = host_bits(h2).view(np.uint8)
+    assert np.array_equal(got[valid], tiled_ref(_bytes_of_bf16(h1, N, H))[valid])
+    assert torch.equal(am1, am2) and torch.equal(o1, o2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,C,H", [(300, 512, 384), (4096, 4096, 14336)])
+def test_tiled_bf16_block_equals_the_row_major_block(blk, B, N, C, H):
+    say(f"tiled bf16 block N={N} C={C} H={H}")
+    d = W.block_inputs(N, C, H, seed=N + 7)
+    inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
+    res = {}
+    for tiled in (False, True):
+        b = blk.PrefillBlock(N, C, H, 1e-5, False, tiled=tiled)
+        b.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+        out = b.forward_zero_once(inp, add).clone()
+        res[tiled] = (out, b.r.clone(), b.rstd.clone(), b.y.clone(), b.h.clone())
+    torch.cuda.synchronize()
+    (o0, r0, s0, y0, h0), (o1, r1, s1, y1, h1) = res[False], res[True]
+    assert torch.equal(o0, o1) and torch.equal(r0, r1) and torch.equal(s0, s1)
+    for a, b_, cols in ((y0, y1, C), (h0, h1, H)):
+        valid = tiled_ref(np.ones((N, 2 * cols), np.uint8)).astype(bool)
+        assert np.array_equal(host_bits(b_).view(np.uint8)[valid], tiled_ref(_bytes_of_bf16(a, N, cols))[valid])

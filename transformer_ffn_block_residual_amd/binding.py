@@ -69,6 +69,9 @@ def _load():
         "ffn_gateup_acc_tiled": [P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_gateup_swiglu_quant_tiled": [P, P, P, P, P, P, P, P, I64, I64, I64, P],
         "ffn_down_tiled": [P, P, P, P, P, I64, I64, I64, P],
+        "ffn_rmsnorm_fwd_tiled": [P, P, P, P, P, P, P, F32, I64, I64, P],
+        "ffn_gateup_tiled_bf16": [P, P, P, P, I64, I64, I64, P],
+        "ffn_down_tiled_bf16": [P, P, P, I64, I64, I64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -286,6 +289,31 @@ def ffn_down_tiled(out, h, h_scale, w, w_scale, N, H, C, stream=None):
         _ptr(out, "out", N * C, BF16), _ptr(h, "h", _tiled_numel(N, H), E4M3), _ptr(h_scale, "h_scale", 1, F32),
         _ptr(w, "w", _tiled_numel(C, H), E4M3), _ptr(w_scale, "w_scale", 1, F32),
         int(N), int(H), int(C), _stream(stream)))
+
+
+def ffn_rmsnorm_fwd_tiled(y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C, stream=None):
+    """ffn_rmsnorm_fwd with y stored tiled (rows of 2C bytes)."""
+    _check(_lib.ffn_rmsnorm_fwd_tiled(
+        _ptr(y, "y", _tiled_numel(N, 2 * C) // 2, BF16), _ptr(rstd, "rstd", N, F32),
+        _ptr(residual_out, "residual_out", N * C, BF16, optional=True),
+        _ptr(absmax, "absmax", 1, F32, optional=True),
+        _ptr(inp, "inp", N * C, BF16), _ptr(addend, "addend", N * C, BF16, optional=True),
+        _ptr(weight, "weight", C, BF16), float(eps), int(N), int(C), _stream(stream)))
+
+
+def ffn_gateup_tiled_bf16(h, h_absmax, x, w, N, C, H, stream=None):
+    """bf16 gate+up with the SwiGLU epilogue on tiled x and w, h stored tiled."""
+    _check(_lib.ffn_gateup_tiled_bf16(
+        _ptr(h, "h", _tiled_numel(N, 2 * H) // 2, BF16), _ptr(h_absmax, "h_absmax", 1, F32, optional=True),
+        _ptr(x, "x", _tiled_numel(N, 2 * C) // 2, BF16), _ptr(w, "w", _tiled_numel(2 * H, 2 * C) // 2, BF16),
+        int(N), int(C), int(H), _stream(stream)))
+
+
+def ffn_down_tiled_bf16(out, h, w, N, H, C, stream=None):
+    """bf16 down projection on tiled h and w."""
+    _check(_lib.ffn_down_tiled_bf16(
+        _ptr(out, "out", N * C, BF16), _ptr(h, "h", _tiled_numel(N, 2 * H) // 2, BF16),
+        _ptr(w, "w", _tiled_numel(C, 2 * H) // 2, BF16), int(N), int(H), int(C), _stream(stream)))
 
 
 def _decode_gemv_args(out, h, x, w_gate, s_gate, w_up, s_up, w_down, s_down, M, C, H, stream):
@@ -520,6 +548,7 @@ __all__ = [
     "ffn_matmul_tn_swiglu_bwd_acc", "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc",
     "ffn_rmsnorm_bwd_scratch_bytes",
     "ffn_tile_bytes", "ffn_tile_pack", "ffn_quant_absmax_clear_tiled", "ffn_gateup_acc_tiled",
-    "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled",
+    "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled", "ffn_rmsnorm_fwd_tiled", "ffn_gateup_tiled_bf16",
+    "ffn_down_tiled_bf16",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "version", "last_error", "LIB_PATH",
 ]

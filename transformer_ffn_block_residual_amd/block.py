@@ -63,25 +63,27 @@ def _u8(*shape):
 
 
 class PrefillBlock:
-    """One FFN block's prefill forward over N tokens.  tiled (FP8 only): the
-    e4m3 operands of both GEMMs (the weights, and the codes of y and h) are
-    kept in the library's tiled layout (``ffn_tile_pack``), which the GEMMs
-    read a contiguous KiB at a time; the results are those of the row-major
-    operands bit for bit.  ``qy`` and ``qh`` then hold tiled codes."""
+    """One FFN block's prefill forward over N tokens.  tiled: the operands of
+    both GEMMs (the weights, and y and h, or their e4m3 codes) are kept in
+    the library's tiled layout (``ffn_tile_pack``), which the GEMMs read a
+    contiguous KiB at a time; the results are those of the row-major operands
+    bit for bit.  ``qy`` and ``qh`` (FP8), or ``y`` and ``h`` (bf16), then
+    hold tiled data; the tiled block runs ``forward_zero_once`` (and, FP8,
+    ``forward_known_h_absmax``)."""
 
     def __init__(self, N, C, H, eps, fp8, tiled=False):
-        assert fp8 or not tiled, "the tiled layout is for the e4m3 operands"
         self.N, self.C, self.H, self.eps, self.fp8 = N, C, H, float(eps), bool(fp8)
         self.tiled = bool(tiled)
+        bf16_tiled = self.tiled and not self.fp8
         self.r = _bf16(N, C)
-        self.y = _bf16(N, C)
+        self.y = _bf16(B.ffn_tile_bytes(N, 2 * C) // 2) if bf16_tiled else _bf16(N, C)
         self.rstd = _f32(N)
         # the abs-max table, zeroed once here: am_y and am_h in words 0 and 4
         # (16 bytes apart); forward() overwrites them, forward_zero_once()
         # accumulates into them and clears each after its consumer
         self.am_tab = torch.zeros(8, dtype=torch.float32, device="cuda")
         self.am_y = self.am_tab[0:1]
-        self.h = _bf16(N, H)
+        self.h = _bf16(B.ffn_tile_bytes(N, 2 * H) // 2) if bf16_tiled else _bf16(N, H)
         self.am_h = self.am_tab[4:5]
         self.out = _bf16(N, C)
         if self.fp8:
@@ -108,8 +110,15 @@ class PrefillBlock:
         w_gu, w_d = as_dev(w_gu), as_dev(w_d)
         C, H = self.C, self.H
         if not self.fp8:
+            self.w_gu_rows, self.w_d_rows = w_gu, w_d
             self.w_gu, self.w_d = w_gu, w_d
             self.s_gu = self.s_d = None
+            if self.tiled:
+                self.w_gu = _bf16(B.ffn_tile_bytes(2 * H, 2 * C) // 2)
+                self.w_d = _bf16(B.ffn_tile_bytes(C, 2 * H) // 2)
+                B.ffn_tile_pack(self.w_gu.view(torch.uint8), w_gu.view(torch.uint8), 2 * H, 2 * C)
+                B.ffn_tile_pack(self.w_d.view(torch.uint8), w_d.view(torch.uint8), C, 2 * H)
+                torch.cuda.current_stream().synchronize()
             return
         self.w_gu, self.s_gu, am = _u8(2 * H, C), _f32(1), _f32(1)
         B.ffn_quant_absmax(self.w_gu, self.s_gu, am, w_gu, 2 * H * C, 1)
@@ -154,6 +163,11 @@ class PrefillBlock:
         N, C, H = self.N, self.C, self.H
         r = self.r if addend is not None else None
         if not self.fp8:
+            if self.tiled:
+                B.ffn_rmsnorm_fwd_tiled(self.y, self.rstd, r, None, inp, addend, self.w_norm, self.eps, N, C, stream)
+                B.ffn_gateup_tiled_bf16(self.h, None, self.y, self.w_gu, N, C, H, stream)
+                B.ffn_down_tiled_bf16(self.out, self.h, self.w_d, N, H, C, stream)
+                return self.out
             B.ffn_rmsnorm_fwd(self.y, self.rstd, r, None, inp, addend, self.w_norm, self.eps, N, C, stream)
             B.ffn_gateup(self.h, None, self.y, None, self.w_gu, None, B.FFN_BF16, 1, N, C, H, stream)
             B.ffn_down(self.out, self.h, None, self.w_d, None, B.FFN_BF16, N, H, C, stream)

@@ -81,9 +81,16 @@ const char* ffn_last_error(void) { return g_err; }
 
 const char* ffn_version(void) { return "ffn-mi355x 0.1 (gfx950)"; }
 
+static int64_t tiled_bytes(int64_t rows, int64_t row_bytes) { return (rows + 63) / 64 * 64 * row_bytes; }
+
+static bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uint8_t *pa = static_cast<const uint8_t*>(a), *pb = static_cast<const uint8_t*>(b);
+    return a && b && na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
+
 static ffn_status_t rmsnorm_entry(const char* fn, void* y, float* rstd, void* residual_out, float* absmax,
                                   const void* inp, const void* addend, const void* weight, float eps, int64_t N,
-                                  int64_t C, hipStream_t stream, bool clear_absmax) {
+                                  int64_t C, hipStream_t stream, bool clear_absmax, bool tiled_y = false) {
     if (!y) return fail(FFN_ERR_INVALID, "%s: y is NULL", fn);
     if (!rstd) return fail(FFN_ERR_INVALID, "%s: rstd is NULL", fn);
     if (!inp) return fail(FFN_ERR_INVALID, "%s: inp is NULL", fn);
@@ -99,9 +106,16 @@ static ffn_status_t rmsnorm_entry(const char* fn, void* y, float* rstd, void* re
         return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
     if (residual_out && (residual_out == y || residual_out == addend))
         return fail(FFN_ERR_INVALID, "%s: residual_out may alias only inp", fn);
+    if (tiled_y) {
+        // a row's tiled chunks land among the bytes of its whole 64-row group
+        if (C % 32 != 0) return fail(FFN_ERR_UNSUPPORTED, "%s: C = %lld (need C %% 32 == 0)", fn, (long long)C);
+        const int64_t ny = tiled_bytes(N, 2 * C), nx = N * C * 2;
+        if (overlaps(y, ny, inp, nx) || overlaps(y, ny, addend, nx) || overlaps(y, ny, residual_out, nx))
+            return fail(FFN_ERR_INVALID, "%s: the tiled y must not overlap inp, addend or residual_out", fn);
+    }
     return hip_status(ffn::launch_rmsnorm((uint16_t*)y, rstd, (uint16_t*)residual_out, absmax,
                                           (const uint16_t*)inp, (const uint16_t*)addend, (const uint16_t*)weight,
-                                          eps, N, (int)C, stream, clear_absmax),
+                                          eps, N, (int)C, stream, clear_absmax, tiled_y),
                       fn);
 }
 
@@ -110,6 +124,13 @@ ffn_status_t ffn_rmsnorm_fwd(void* y, float* rstd, void* residual_out, float* ab
                              hipStream_t stream) {
     return rmsnorm_entry("ffn_rmsnorm_fwd", y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C, stream,
                          true);
+}
+
+ffn_status_t ffn_rmsnorm_fwd_tiled(void* y, float* rstd, void* residual_out, float* absmax, const void* inp,
+                                   const void* addend, const void* weight, float eps, int64_t N, int64_t C,
+                                   hipStream_t stream) {
+    return rmsnorm_entry("ffn_rmsnorm_fwd_tiled", y, rstd, residual_out, absmax, inp, addend, weight, eps, N, C,
+                         stream, true, true);
 }
 
 ffn_status_t ffn_rmsnorm_fwd_acc(void* y, float* rstd, void* residual_out, float* absmax, const void* inp,
@@ -323,8 +344,6 @@ ffn_status_t ffn_down(void* out, const void* h, const float* h_scale, const void
 
 // ---- tiled operands (whole 64-row groups; common.h, tiled_offset)
 
-static int64_t tiled_bytes(int64_t rows, int64_t row_bytes) { return (rows + 63) / 64 * 64 * row_bytes; }
-
 int64_t ffn_tile_bytes(int64_t rows, int64_t row_bytes) {
     if (rows < 0 || row_bytes < 0 || row_bytes % 64 != 0 || row_bytes > ((int64_t)1 << 21) ||
         rows > ((int64_t)1 << 40))
@@ -378,9 +397,10 @@ ffn_status_t ffn_quant_absmax_clear_tiled(uint8_t* q, float* scale, const float*
 
 // The checks of the row-major entry point, plus the tiled token operand's
 // whole groups within the 32-bit offsets of one operand.
-static ffn_status_t check_tiled_gemm(const char* fn, int64_t N, int64_t K, int64_t O) {
-    if (ffn_status_t st = check_gemm_dims(fn, N, K, O, 1)) return st;
-    if (tiled_bytes(N, K) >= ((int64_t)1 << 32)) return fail(FFN_ERR_UNSUPPORTED, "%s: an operand exceeds 4 GiB", fn);
+static ffn_status_t check_tiled_gemm(const char* fn, int64_t N, int64_t K, int64_t O, int elt = 1) {
+    if (ffn_status_t st = check_gemm_dims(fn, N, K, O, elt)) return st;
+    if (tiled_bytes(N, K * elt) >= ((int64_t)1 << 32))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: an operand exceeds 4 GiB", fn);
     return FFN_OK;
 }
 
@@ -470,6 +490,42 @@ ffn_status_t ffn_down_tiled(void* out, const uint8_t* h, const float* h_scale, c
     return hip_status(ffn::launch_gemm(out, nullptr, h, h_scale, w, w_scale, true, false, N, (int)H, (int)C, stream,
                                        nullptr, nullptr, false, false, nullptr, false, true, true),
                       "ffn_down_tiled");
+}
+
+ffn_status_t ffn_gateup_tiled_bf16(void* h, float* h_absmax, const void* x, const void* w, int64_t N, int64_t C,
+                                   int64_t H, hipStream_t stream) {
+    REQUIRE(h);
+    REQUIRE(x);
+    REQUIRE(w);
+    NONNEG(N);
+    NONNEG(C);
+    NONNEG(H);
+    if (ffn_status_t st = check_tiled_gemm("ffn_gateup_tiled_bf16", N, C, 2 * H, 2)) return st;
+    if (H % 128 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_gateup_tiled_bf16: H = %lld must be a multiple of 128", (long long)H);
+    ALIGNED(h);
+    ALIGNED(x);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(h, h_absmax, x, nullptr, w, nullptr, false, true, N, (int)C, (int)(2 * H),
+                                       stream, nullptr, nullptr, false, false, nullptr, false, true, true),
+                      "ffn_gateup_tiled_bf16");
+}
+
+ffn_status_t ffn_down_tiled_bf16(void* out, const void* h, const void* w, int64_t N, int64_t H, int64_t C,
+                                 hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(h);
+    REQUIRE(w);
+    NONNEG(N);
+    NONNEG(H);
+    NONNEG(C);
+    if (ffn_status_t st = check_tiled_gemm("ffn_down_tiled_bf16", N, H, C, 2)) return st;
+    ALIGNED(out);
+    ALIGNED(h);
+    ALIGNED(w);
+    return hip_status(ffn::launch_gemm(out, nullptr, h, nullptr, w, nullptr, false, false, N, (int)H, (int)C, stream,
+                                       nullptr, nullptr, false, false, nullptr, false, true, true),
+                      "ffn_down_tiled_bf16");
 }
 
 // Checks shared by the decode entry points (elt: weight bytes per element).

@@ -40,8 +40,9 @@
 // puts into LDS stored contiguously, swizzle included) every load reads eight
 // whole lines, one contiguous KiB; the LDS stages, fragment reads and MFMA
 // order stay as they are, so the products are bit for bit those of the
-// row-major operands.  Only the load offsets change (and, for the e4m3 codes
-// of h from the quantising SwiGLU epilogue, the store offsets).
+// row-major operands.  Only the load offsets change, and the store offsets
+// of a SwiGLU output that is itself the down projection's operand (the e4m3
+// codes of h, or bf16 h of a bf16 product).
 //
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin; the linear id is
 // remapped so that each XCD receives a contiguous range of tiles, and inside it
@@ -337,10 +338,13 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
     const int64_t n0 = (int64_t)tn * kBN;
     constexpr int kOutElt = kQuant ? 1 : 2;  // bytes per output element
     uint8_t* base = reinterpret_cast<uint8_t*>(a.out) + n0 * a.ld_out * kOutElt;
-    // tiled e4m3 h: the tile's rows are whole 64-row groups from the same
-    // byte offset, with rows past N skipped by offset (not a prefix there);
-    // every other output is row-major, its rows past N cut off by the range
-    const int64_t rows_left = (kTiled && kQuant) ? (a.N - n0 + 63) / 64 * 64 : a.N - n0;
+    // a tiled SwiGLU output (the e4m3 codes of h, or bf16 h of a bf16
+    // product: the next GEMM's operand) has the tile's rows as whole 64-row
+    // groups from the same byte offset, rows past N skipped by offset (they
+    // are not a prefix there); every other output is row-major, its rows past
+    // N cut off by the range
+    constexpr bool kTiledOut = kTiled && kFused && (kQuant || !kFP8);
+    const int64_t rows_left = kTiledOut ? (a.N - n0 + 63) / 64 * 64 : a.N - n0;
     const int64_t rem = rows_left * (int64_t)a.ld_out * kOutElt;
     const uint32_t nrec = (uint32_t)(rem < ((int64_t)1 << 30) ? rem : ((int64_t)1 << 30));
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)nrec, 0x00020000);
@@ -511,8 +515,9 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
                     const u32x4_t v = regroup_runs(d[0], d[1], d[2], d[3]);
                     const int o = tm * 128 + wm * 64 + i * 32 + 16 * q + 8 * fh;
                     uint32_t off = (uint32_t)(r_base + 32 * j) * row_bytes + (uint32_t)o * kOutElt;
-                    if (kTiled && kQuant)  // tiled codes; rows past N skipped by offset
-                        off = ok ? (uint32_t)tiled_offset(r_base + 32 * j, o, row_bytes) : 0x7fffffffu;
+                    if (kTiledOut)  // rows past N skipped by offset
+                        off = ok ? (uint32_t)tiled_offset(r_base + 32 * j, (int64_t)o * kOutElt, row_bytes)
+                                 : 0x7fffffffu;
                     if (kQuant) {
                         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
                         const u32x2_t c = {
@@ -537,7 +542,7 @@ void gemm_kernel(GemmArgs a) {
     static_assert(!(kFused && kAccum), "accumulation is a plain-output epilogue");
     static_assert(kFP8 || !kXBf8, "e5m2 x is an FP8 operand");
     static_assert(!(kSwiBwd && (kFused || kAccum)), "the SwiGLU backward is a plain-output epilogue of its own");
-    static_assert(!kTiled || (kFP8 && !kAccum && !kXBf8 && !kSwiBwd), "tiled operands: the e4m3 forward products");
+    static_assert(!kTiled || (!kAccum && !kXBf8 && !kSwiBwd), "tiled operands: the forward products");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
     constexpr int kStoreCnt = epilogue_stores<kFused>();
@@ -761,7 +766,7 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
                        hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2,
                        const void* swiglu_gu, bool tile_grid, bool clear_absmax, bool tiled) {
     if (x_e5m2 && (!fp8 || fuse_swiglu)) return hipErrorInvalidValue;
-    if (tiled && (!fp8 || accumulate || x_e5m2 || swiglu_gu)) return hipErrorInvalidValue;
+    if (tiled && (accumulate || x_e5m2 || swiglu_gu || (!fp8 && q_absmax))) return hipErrorInvalidValue;
     const bool swi = swiglu_gu != nullptr;
     if (swi && (fuse_swiglu || accumulate)) return hipErrorInvalidValue;
     if (absmax && (fuse_swiglu || swi || N == 0) && clear_absmax) {
@@ -792,11 +797,15 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const int KT = a.K_bytes / kRowBytes;
     const dim3 grid((unsigned)(KT >= kAhead && !tile_grid ? persistent_grid(T) : T)), block(kThreads);
     const bool acc = accumulate && !fuse_swiglu;
-    if (tiled) {
+    if (tiled && fp8) {
         if (quant) hipLaunchKernelGGL((gemm_kernel<true, true, true, false, false, false, true>), grid, block, 0, s, a);
         else if (fuse_swiglu)
             hipLaunchKernelGGL((gemm_kernel<true, true, false, false, false, false, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gemm_kernel<true, false, false, false, false, false, true>), grid, block, 0, s, a);
+    } else if (tiled) {
+        if (fuse_swiglu)
+            hipLaunchKernelGGL((gemm_kernel<false, true, false, false, false, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, false, false, false, false, true>), grid, block, 0, s, a);
     } else if (swi) {
         if (fp8 && x_e5m2) hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true, true>), grid, block, 0, s, a);
         else if (fp8) hipLaunchKernelGGL((gemm_kernel<true, false, false, false, false, true>), grid, block, 0, s, a);

@@ -11,10 +11,11 @@ hipError_t launch_fill(float* p, int n, float v, hipStream_t s);
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();
 // clear_absmax == false: *absmax is max-accumulated into as found (the
-// caller zeroed it), not cleared first.
+// caller zeroed it), not cleared first.  tiled_y: y in the tiled GEMM
+// operand layout of [N, 2C bytes] (common.h, tiled_offset).
 hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
                           const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s,
-                          bool clear_absmax = true);
+                          bool clear_absmax = true, bool tiled_y = false);
 hipError_t launch_absmax(float* absmax, const uint16_t* x, int64_t n, hipStream_t s);
 // clear (nullable): another abs-max word that the kernel sets to zero.
 hipError_t launch_quant(uint8_t* q, float* scale, float* absmax, const uint16_t* x, int64_t n, bool compute,
@@ -33,9 +34,11 @@ hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t
 // h = silu(g) * u, rounded to bf16; out receives dgu [N, 2O] computed from
 // gu [N, 2O] (which out may be), and absmax max |dgu|.  tile_grid: one
 // workgroup per output tile (for products that run beside others).  tiled
-// (e4m3, no accumulation, e5m2 or SwiGLU backward): x and w in the tiled
-// layout (whole 64-row groups; common.h, tiled_offset), and with q_absmax the
-// e4m3 codes of h stored in it too.
+// (no accumulation, e5m2 or SwiGLU backward): x and w in the tiled layout
+// (whole 64-row groups; common.h, tiled_offset); the SwiGLU output is stored
+// in it too when it is a GEMM operand itself (the e4m3 codes of q_absmax, or
+// bf16 h of a bf16 product), row-major otherwise (bf16 h of an e4m3 product,
+// which a quantiser reads).
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr,

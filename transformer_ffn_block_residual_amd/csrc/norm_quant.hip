@@ -30,7 +30,10 @@ hipError_t launch_fill(float* p, int n, float v, hipStream_t s) {
 // registers (CPL 16-byte chunks per lane), so y may overwrite inp or addend.
 //   r = bf16(inp + addend); rstd = 1/sqrt(sum r^2 / C + eps);
 //   y = bf16((r * rstd) * w); absmax = max |y|.
-template <int CPL, bool kAdd>
+// kTiledY: y is stored in the tiled GEMM operand layout of [N, 2C bytes]
+// (common.h, tiled_offset; each 16-byte chunk stays whole), for a bf16
+// gate+up projection on tiled operands.
+template <int CPL, bool kAdd, bool kTiledY>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(
     uint16_t* y, float* rstd_out, uint16_t* res_out, float* absmax,
     const uint16_t* inp, const uint16_t* addend, const uint16_t* w,
@@ -134,7 +137,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
                         amax = absmax_acc(absmax_acc(amax, bf16lo(yp[q])), bf16hi(yp[q]));
                     }
                     if (kAdd) o4[c] = r[i];
-                    y4[c] = yv;
+                    if (kTiledY)
+                        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(y) +
+                                                  tiled_offset(row, (int64_t)c * 16, 2 * (int64_t)C)) = yv;
+                    else
+                        y4[c] = yv;
                 }
             }
         }
@@ -142,32 +149,42 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
     if (absmax) block_absmax_commit(amax, red, absmax);
 }
 
-template <int CPL>
+template <int CPL, bool kTiledY>
 static void launch_rmsnorm_cpl(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
                                const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C,
                                hipStream_t s) {
     dim3 grid((unsigned)((N + 3) / 4)), block(256);
     if (add)
-        hipLaunchKernelGGL((rmsnorm_kernel<CPL, true>), grid, block, 0, s, y, rstd, res, absmax, inp, add, w, eps, N, C);
+        hipLaunchKernelGGL((rmsnorm_kernel<CPL, true, kTiledY>), grid, block, 0, s, y, rstd, res, absmax, inp, add, w,
+                           eps, N, C);
     else
-        hipLaunchKernelGGL((rmsnorm_kernel<CPL, false>), grid, block, 0, s, y, rstd, res, absmax, inp, add, w, eps, N, C);
+        hipLaunchKernelGGL((rmsnorm_kernel<CPL, false, kTiledY>), grid, block, 0, s, y, rstd, res, absmax, inp, add, w,
+                           eps, N, C);
+}
+
+template <bool kTiledY>
+static void launch_rmsnorm_any(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
+                               const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C,
+                               hipStream_t s) {
+    const int need = (C / 8 + 63) / 64;  // chunks per lane
+    if (need <= 1) launch_rmsnorm_cpl<1, kTiledY>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 2) launch_rmsnorm_cpl<2, kTiledY>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 4) launch_rmsnorm_cpl<4, kTiledY>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 8) launch_rmsnorm_cpl<8, kTiledY>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else if (need <= 16) launch_rmsnorm_cpl<16, kTiledY>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else launch_rmsnorm_cpl<32, kTiledY>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
 }
 
 hipError_t launch_rmsnorm(uint16_t* y, float* rstd, uint16_t* res, float* absmax, const uint16_t* inp,
                           const uint16_t* add, const uint16_t* w, float eps, int64_t N, int C, hipStream_t s,
-                          bool clear_absmax) {
+                          bool clear_absmax, bool tiled_y) {
     if (absmax && clear_absmax) {
         hipError_t e = launch_fill(absmax, 1, 0.0f, s);
         if (e != hipSuccess) return e;
     }
     if (N == 0) return hipSuccess;
-    const int need = (C / 8 + 63) / 64;  // chunks per lane
-    if (need <= 1) launch_rmsnorm_cpl<1>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
-    else if (need <= 2) launch_rmsnorm_cpl<2>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
-    else if (need <= 4) launch_rmsnorm_cpl<4>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
-    else if (need <= 8) launch_rmsnorm_cpl<8>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
-    else if (need <= 16) launch_rmsnorm_cpl<16>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
-    else launch_rmsnorm_cpl<32>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    if (tiled_y) launch_rmsnorm_any<true>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
+    else launch_rmsnorm_any<false>(y, rstd, res, absmax, inp, add, w, eps, N, C, s);
     return hipGetLastError();
 }
 
