@@ -154,10 +154,13 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
         fp8 = "true" if w.fp8 else "false"
         e5 = w.fp8 and grad_dtype == "e5m2"
         what = ("e5m2 x e4m3" if e5 else "e4m3") if w.fp8 else "bf16"
+        # the FP8 backward's products read tiled operands unless rows_layout
+        btl = w.fp8 and not rows_layout
         # reads dgu^T [2H, N] and y^T [C, N] once, reads and writes dW_gu [2H, C]
-        return [(f"dwup{'5' if e5 else ''}_{workload}", "gemm.hip",
-                 [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}, false, false>"],
-                 f"gemm_kernel ({what}, accumulating) of the up projection's weight "
+        return [(f"dwup{'5' if e5 else ''}{'_rows' if w.fp8 and rows_layout else ''}_{workload}", "gemm.hip",
+                 [f"gemm_kernel<{fp8}, false, false, true, {'true' if e5 else 'false'}, false, "
+                  f"{'true' if btl else 'false'}>"],
+                 f"gemm_kernel ({what}, accumulating{', tiled operands' if btl else ''}) of the up projection's weight "
                  f"gradient, [2H, C] = [{2 * H}, {C}], K = N = {N}",
                  2 * H * N * e + C * N * e + 2 * (2 * H * C * 2), (0, 2, 1))]
     if workload == "decode":
@@ -210,9 +213,9 @@ def traffic_specs(workload, known_h_absmax=False, backward=False, grad_dtype="e4
     return specs
 
 
-def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3"):
+def traffic_spec(workload, known_h_absmax=False, backward=False, grad_dtype="e4m3", rows_layout=False):
     """The dominant kernel's entry of traffic_specs."""
-    return traffic_specs(workload, known_h_absmax, backward, grad_dtype)[0]
+    return traffic_specs(workload, known_h_absmax, backward, grad_dtype, rows_layout)[0]
 
 
 def ingest_pmc(a):
@@ -724,8 +727,9 @@ def bench_backward(a, torch, np, B, block, W):
     pre.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
     gd = a.grad_dtype if w.fp8 else "e4m3"
     # the zero-once abs-max convention, as in the forward step: no clearing launches in a step
+    btiled = w.fp8 and a.gemm_layout == "tiled"
     bb = block.BackwardBlock(pre, in_place=False, grad_dtype=gd, fuse_swiglu_bwd=not a.unfused_swiglu_bwd,
-                             concurrent=a.concurrent_backward, zero_once=True)
+                             concurrent=a.concurrent_backward, zero_once=True, tiled=btiled)
     bb.forward(dev(d["inp"]), dev(d["addend"]))
     d_out = dev(_bwd_dout(np, w, N))
     # the abs-max of d_out, as its producer (the next block's RMSNorm backward)
@@ -792,12 +796,12 @@ def bench_backward(a, torch, np, B, block, W):
                                 if a.concurrent_backward else "one stream"),
                    "absmax": ("zero-once: dMlpUp's and d_res's words accumulated into, each cleared by the other's "
                               "consumer" if w.fp8 else "none (no quantised gradient)"),
-                   **({"grad_dtype": gd} if w.fp8 else {})},
+                   **({"grad_dtype": gd, "gemm_operands": "tiled" if btiled else "row-major"} if w.fp8 else {})},
         "roofline": {"bound": "mfma", "kernel": f"ffn_matmul_tn ({(gd if w.fp8 else 'bf16')}, accumulate): "
                                                  "the up projection's weight gradient [2H, C], K = N",
                      "achieved": dw_tf, "peak": peak, "unit": "TFLOP/s", "frac": dw_tf / peak,
-                     "traffic": measured_traffic(traffic_spec(a.workload, backward=True, grad_dtype=gd)[0],
-                                                 "gemm.hip")},
+                     "traffic": measured_traffic(traffic_spec(a.workload, backward=True, grad_dtype=gd,
+                                                              rows_layout=not btiled)[0], "gemm.hip")},
         "kernels": kernels,
         "spread_ms": spread,
         "ms_per_step_in_hip_graph": graph_ms,

@@ -412,14 +412,19 @@ ffn_status_t ffn_decode_gemv_packed_noalloc(void* out, void* h, const void* x,
  * a persistent grid sized to the CUs, so that the hardware hands CUs to work
  * on other streams as tiles finish: for two independent products issued on
  * two streams (the data and weight gradients of one projection), whose partial
- * last rounds of tiles then fill each other.  Results do not depend on it. */
+ * last rounds of tiles then fill each other.  Results do not depend on it.
+ * FFN_TN_TILED (FP8 only): a and b are in the tiled layout (see the tiled
+ * operands below: whole 64-row groups), the output row-major; the results
+ * equal the row-major operands' bit for bit. */
 #define FFN_TN_ACCUMULATE 1
 #define FFN_TN_TILE_GRID 2
+#define FFN_TN_TILED 4
 
 /* TN matmul: out[m,n] = bf16(acc + sum_k a[m,k] * b[n,k] (* a_scale * b_scale
  * for FP8)), acc = out[m,n] when flags has FFN_TN_ACCUMULATE (the
  * accumulate_gradient flag of backward_qmm: one rounding of the fp32 sum),
- * else 0; FFN_TN_TILE_GRID as above; other flag bits are invalid.  [llmq model]
+ * else 0; FFN_TN_TILE_GRID and FFN_TN_TILED as above; other flag bits are
+ * invalid.  [llmq model]
  * backward_qmm, matmul(..., EMMTranspose::TN, accumulate_gradient); the
  * gradient operand is allocated in the grad dtype (e4m3 or e5m2), the weight
  * and activation operands in e4m3.
@@ -441,8 +446,8 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale,
  * DSwiGLU, MlpUp, ...); the two calls run as one kernel, so dSwiGLU never
  * reaches memory.  dgu: bf16 [M, 2H] (gate columns, then up columns); gu: bf16
  * [M, 2H], the forward's gate+up output (dgu may be gu: updated in place);
- * a: [M,K], b: [H,K], dtype and scales as ffn_matmul_tn; flags: 0 or
- * FFN_TN_TILE_GRID; absmax: fp32 [1] or NULL.  Supported: K % 128 == 0,
+ * a: [M,K], b: [H,K], dtype and scales as ffn_matmul_tn; flags: 0,
+ * FFN_TN_TILE_GRID and/or FFN_TN_TILED; absmax: fp32 [1] or NULL.  Supported: K % 128 == 0,
  * H % 128 == 0, any M >= 0; dgu must not alias a or b. */
 ffn_status_t ffn_matmul_tn_swiglu_bwd(void* dgu, float* absmax, const void* a,
                                       const float* a_scale, const void* b, const float* b_scale,
@@ -535,6 +540,24 @@ ffn_status_t ffn_rmsnorm_bwd_acc(void* dinp, float* dweight, float* scratch,
                                  float* clear, int64_t N, int64_t C, hipStream_t stream);
 
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
+/* The backward's FP8 products on tiled operands (the layout of the tiled
+ * prefill entry points, with whole 64-row groups).  FFN_TN_TILED in the
+ * flags of ffn_matmul_tn, ffn_matmul_tn_swiglu_bwd and
+ * ffn_matmul_tn_swiglu_bwd_acc: a [M, K] and b [N, K] (codes) are tiled, the
+ * outputs stay row-major; the results equal the row-major call's bit for
+ * bit.  ffn_transpose_tiled: ffn_transpose of e4m3 codes (1-byte elements)
+ * with out [cols, ld_out] stored tiled (ffn_tile_bytes(cols, ld_out) bytes).
+ * ffn_quant_transpose_tiled: ffn_quant_transpose with q_t [cols, ld_out] and
+ * q [rows, cols] (if given) stored tiled and clear (nullable) zeroed as in
+ * ffn_quant_transpose_clear.  Both need cols % 64 == 0 and ld_out % 64 ==
+ * 0; the rows past cols (q_t) or rows (q) in the last group are not
+ * written.  [llmq model] LLamaModel::_backward_block, backward_qmm. */
+ffn_status_t ffn_transpose_tiled(uint8_t* out, const uint8_t* in, int64_t rows, int64_t cols,
+                                 int64_t ld_out, hipStream_t stream);
+ffn_status_t ffn_quant_transpose_tiled(uint8_t* q_t, uint8_t* q, float* scale, const void* x,
+                                       const float* absmax, float* clear, ffn_dtype_t code_dtype,
+                                       int64_t rows, int64_t cols, int64_t ld_out, hipStream_t stream);
+
 const char* ffn_last_error(void);
 
 /* Library version string. */

@@ -45,7 +45,7 @@ def test_header_declares_the_entry_points():
               "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc", "ffn_rmsnorm_bwd_acc", "ffn_tile_bytes",
               "ffn_tile_pack", "ffn_quant_absmax_clear_tiled", "ffn_gateup_acc_tiled",
               "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled", "ffn_rmsnorm_fwd_tiled", "ffn_gateup_tiled_bf16",
-              "ffn_down_tiled_bf16"]:
+              "ffn_down_tiled_bf16", "ffn_transpose_tiled", "ffn_quant_transpose_tiled"]:
         assert n in names
 
 
@@ -197,6 +197,22 @@ def test_tiled_layout_validation(lib):
     assert gb(A, None, A, A, 64, 256, 100, None) == UNSUPPORTED
     assert gb(None, None, A, A, 64, 256, 768, None) == INVALID
     assert gb(A, None, MIS, A, 64, 256, 768, None) == UNSUPPORTED
+    TILED = 4
+    tn = lib.ffn_matmul_tn                     # out, a, as, b, bs, dtype, flags, M, N, K
+    assert tn(A, 0x20000, S, 0x30000, Z, 0, TILED, 64, 256, 256, None) == UNSUPPORTED   # bf16 operands
+    assert tn(A, 0x20000, S, 0x30000, Z, 1, 8, 64, 256, 256, None) == INVALID          # unknown flag
+    sb = lib.ffn_matmul_tn_swiglu_bwd          # dgu, absmax, a, as, b, bs, gu, dtype, flags, M, H, K
+    assert sb(A, None, 0x20000, S, 0x30000, Z, 0x40000, 0, TILED, 64, 256, 256, None) == UNSUPPORTED
+    tt = lib.ffn_transpose_tiled               # out, in, rows, cols, ld_out
+    assert tt(A, 0x20000, 64, 96, 128, None) == UNSUPPORTED     # cols % 64
+    assert tt(A, 0x20000, 64, 128, 80, None) == UNSUPPORTED     # ld_out % 64
+    assert tt(A, 0x20000, 128, 128, 64, None) == INVALID        # ld_out < rows
+    assert tt(A, A, 64, 128, 128, None) == INVALID              # out aliases in
+    qt = lib.ffn_quant_transpose_tiled         # q_t, q, scale, x, absmax, clear, dtype, rows, cols, ld_out
+    assert qt(A, None, S, 0x20000, M, None, 1, 64, 96, 128, None) == UNSUPPORTED
+    assert qt(A, None, S, 0x20000, S, None, 1, 64, 128, 128, None) == INVALID   # scale aliases absmax
+    assert qt(A, None, S, 0x20000, M, M, 1, 64, 128, 128, None) == INVALID      # clear aliases absmax
+    assert qt(A, None, S, 0x20000, M, None, 0, 64, 128, 128, None) == INVALID   # bf16 codes
     db = lib.ffn_down_tiled_bf16               # out, h, w, N, H, C
     assert db(A, A, A, 64, 700, 256, None) == UNSUPPORTED
     assert db(A, None, A, 64, 768, 256, None) == INVALID
@@ -283,7 +299,7 @@ def test_backward_validation(lib):
     assert m(A, B_, None, C_, None, 1, 0, 64, 256, 128, None) == INVALID           # E4M3 without scales
     assert m(A, B_, None, C_, None, 2, 0, 64, 256, 128, None) == INVALID           # E5M2 without scales
     assert m(A, B_, None, C_, None, 5, 0, 64, 256, 128, None) == INVALID           # unknown dtype
-    assert m(A, B_, None, C_, None, 0, 4, 64, 256, 128, None) == INVALID           # unknown flag bit
+    assert m(A, B_, None, C_, None, 0, 8, 64, 256, 128, None) == INVALID           # unknown flag bit
     assert m(A, B_, D, C_, D, 2, 0, 64, 200, 128, None) == UNSUPPORTED             # E5M2, N % 128
     assert m(A, B_, None, C_, None, 0, 0, 64, 200, 128, None) == UNSUPPORTED       # N % 128
     assert m(A, B_, None, C_, None, 0, 0, 64, 256, 96, None) == UNSUPPORTED        # K % 128

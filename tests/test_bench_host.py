@@ -72,6 +72,10 @@ def test_decode_and_backward_specs():
     assert algo == 2 * q.H * q.N + q.C * q.N + 2 * (2 * q.H * q.C * 2)
     (key5, _, frags5, _, _, _), = bench.traffic_specs("qwen7b8", backward=True, grad_dtype="e5m2")
     assert key5 == "dwup5_qwen7b8" and frags5 != frags
+    # the FP8 backward's products read tiled operands by default
+    assert frags == ["gemm_kernel<true, false, false, true, false, false, true>"]
+    (keyr, _, fragsr, _, _, _), = bench.traffic_specs("qwen7b8", backward=True, rows_layout=True)
+    assert keyr == "dwup_rows_qwen7b8" and fragsr == ["gemm_kernel<true, false, false, true, false, false, false>"]
 
 
 def _counter_csv(path, counter, rows):

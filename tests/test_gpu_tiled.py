@@ -343,3 +343,122 @@ def test_tiled_bf16_block_equals_the_row_major_block(blk, B, N, C, H):
     for a, b_, cols in ((y0, y1, C), (h0, h1, H)):
         valid = tiled_ref(np.ones((N, 2 * cols), np.uint8)).astype(bool)
         assert np.array_equal(host_bits(b_).view(np.uint8)[valid], tiled_ref(_bytes_of_bf16(a, N, cols))[valid])
+
+
+# ----------------------------------------------------------------------------- the FP8 backward on tiled operands
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,cols,ld_out", [(64, 128, 128), (300, 512, 384), (1000, 384, 1024)])
+@pytest.mark.parametrize("e5", [False, True])
+def test_tiled_transposes_are_the_row_major_ones_moved(B, rows, cols, ld_out, e5):
+    say(f"tiled transposes rows={rows} cols={cols} ld_out={ld_out} e5m2={e5}")
+    E = B.FFN_E5M2 if e5 else B.FFN_E4M3
+    x = dev_bf16(W.normal_bf16((rows, cols), 1.0, rows + cols, 31))
+    am = dev_f32([3.0])
+    qt1, q1, s1 = empty_u8(cols, ld_out), empty_u8(rows, cols), empty_f32(1)
+    B.ffn_quant_transpose(qt1, q1, s1, x, am, rows, cols, ld_out, code_dtype=E)
+    qt2 = empty_u8(B.ffn_tile_bytes(cols, ld_out)).fill_(0xA5)
+    q2 = empty_u8(B.ffn_tile_bytes(rows, cols)).fill_(0xA5)
+    s2, clear = empty_f32(1), dev_f32([9.0])
+    B.ffn_quant_transpose_tiled(qt2, q2, s2, x, am, clear, rows, cols, ld_out, code_dtype=E)
+    codes = dev_u8(_codes((rows, cols), rows))
+    t1 = empty_u8(cols, ld_out)
+    B.ffn_transpose(t1, codes, rows, cols, ld_out, 1)
+    t2 = empty_u8(B.ffn_tile_bytes(cols, ld_out)).fill_(0xA5)
+    B.ffn_transpose_tiled(t2, codes, rows, cols, ld_out)
+    torch.cuda.synchronize()
+    for got, want, r, c in ((qt2, qt1, cols, ld_out), (q2, q1, rows, cols), (t2, t1, cols, ld_out)):
+        valid = tiled_ref(np.ones((r, c), np.uint8)).astype(bool)
+        g = host_u8(got)
+        assert np.array_equal(g[valid], tiled_ref(host_u8(want).reshape(r, c))[valid])
+        assert np.all(g[~valid] == 0xA5)
+    assert torch.equal(s1, s2) and clear.item() == 0.0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,N,K", [(300, 384, 512), (1000, 1024, 640), (8192, 3584, 8192)])
+@pytest.mark.parametrize("e5", [False, True])
+def test_tiled_tn_products_equal_the_row_major_ones(B, M, N, K, e5):
+    """The backward's products on tiled operands: plain, accumulating and with
+    the SwiGLU backward in the epilogue, e4m3 or e5m2 gradient codes."""
+    say(f"tiled TN M={M} N={N} K={K} e5m2={e5}")
+    E = B.FFN_E5M2 if e5 else B.FFN_E4M3
+    a = _codes((M, K), M + 1, top=0x50)
+    b = _codes((N, K), N + 2, top=0x50)
+    ad, bd = dev_u8(a), dev_u8(b)
+    at, bt = _pack(B, ad, M, K), _pack(B, bd, N, K)
+    sa, sb = dev_f32([0.02]), dev_f32([0.03])
+    T = B.FFN_TN_TILED
+    o1, o2 = empty_bf16(M, N), empty_bf16(M, N)
+    B.ffn_matmul_tn(o1, ad, sa, bd, sb, E, 0, M, N, K)
+    B.ffn_matmul_tn(o2, at, sa, bt, sb, E, T, M, N, K)
+    acc0 = dev_bf16(W.normal_bf16((M, N), 1.0, M + N, 33))
+    c1, c2 = acc0.clone(), acc0.clone()
+    B.ffn_matmul_tn(c1, ad, sa, bd, sb, E, B.FFN_TN_ACCUMULATE, M, N, K)
+    B.ffn_matmul_tn(c2, at, sa, bt, sb, E, B.FFN_TN_ACCUMULATE | T | B.FFN_TN_TILE_GRID, M, N, K)
+    gu = dev_bf16(W.normal_bf16((M, 2 * N), 1.0, M + 2 * N, 34))
+    d1, d2 = empty_bf16(M, 2 * N), empty_bf16(M, 2 * N)
+    m1, m2 = empty_f32(1), empty_f32(1)
+    B.ffn_matmul_tn_swiglu_bwd(d1, m1, ad, sa, bd, sb, gu, E, M, N, K)
+    B.ffn_matmul_tn_swiglu_bwd(d2, m2, at, sa, bt, sb, gu, E, M, N, K, flags=T)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(c1, c2)
+    assert torch.equal(d1, d2) and torch.equal(m1, m2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,C,H,gd,zo,conc", [(300, 512, 384, "e4m3", True, False), (300, 512, 384, "e5m2", False, False),
+                                              (1000, 1024, 1536, "e4m3", True, True),
+                                              (8192, 3584, 18944, "e4m3", True, False)])
+def test_tiled_backward_equals_the_row_major_backward(blk, B, N, C, H, gd, zo, conc):
+    """BackwardBlock(tiled=True): gradients, scales and abs-max words equal the
+    row-major backward's bit for bit, over two calls (the weight gradients
+    accumulate)."""
+    say(f"tiled backward N={N} C={C} H={H} grad={gd} zero_once={zo} concurrent={conc}")
+    d = W.block_inputs(N, C, H, seed=N + 11)
+    inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
+    dout = dev_bf16(W.normal_bf16((N, C), 0.01, N + 12, 35))
+    res = {}
+    for tiled in (False, True):
+        f = blk.PrefillBlock(N, C, H, 1e-5, True)
+        f.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
+        bb = blk.BackwardBlock(f, in_place=False, grad_dtype=gd, concurrent=conc, zero_once=zo, tiled=tiled)
+        outs = []
+        for rep in range(2):
+            bb.forward(inp, add)
+            d_res = bb.backward(dout if rep == 0 else dout * 0.5).clone()
+            outs.append((d_res, bb.dgu.clone(), bb.s_dout.clone(), bb.s_dgu.clone(), bb.am_dres.clone()))
+        res[tiled] = (outs, bb.dw_d.clone(), bb.dw_gu.clone(), bb.dw_norm.clone())
+    torch.cuda.synchronize()
+    (o0, a0, g0, n0), (o1, a1, g1, n1) = res[False], res[True]
+    assert torch.equal(a0, a1) and torch.equal(g0, g1) and torch.equal(n0, n1)
+    for x0, x1 in zip(o0, o1):
+        for t0, t1 in zip(x0, x1):
+            assert torch.equal(t0, t1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("e5", [False, True])
+def test_tiled_swiglu_bwd_rows_past_n_do_not_matter(B, e5):
+    """The SwiGLU-backward epilogue on tiled operands: padding rows of the
+    gradient codes that decode to NaN or infinity (e4m3 0x7F, e5m2 0x7C..0x7F)
+    change neither dgu nor its abs-max."""
+    M, H, K = 100, 256, 256
+    say(f"tiled swiglu bwd pad rows e5m2={e5}")
+    E = B.FFN_E5M2 if e5 else B.FFN_E4M3
+    a = _codes((M, K), 7, top=0x40)
+    bt = _pack(B, dev_u8(_codes((H, K), 8, top=0x40)), H, K)
+    sa, sb = dev_f32([0.02]), dev_f32([0.02])
+    gu = dev_bf16(W.normal_bf16((M, 2 * H), 1.0, 9, 36))
+    res = []
+    for fill in (0x00, 0x7F, 0x7C):
+        pad = np.full((128, K), fill, np.uint8)
+        pad[:M] = a
+        at = empty_u8(B.ffn_tile_bytes(M, K))
+        B.ffn_tile_pack(at, dev_u8(pad), 128, K)
+        dgu, am = empty_bf16(M, 2 * H), empty_f32(1)
+        B.ffn_matmul_tn_swiglu_bwd(dgu, am, at, sa, bt, sb, gu, E, M, H, K, flags=B.FFN_TN_TILED)
+        res.append((dgu, am))
+    torch.cuda.synchronize()
+    for dgu, am in res[1:]:
+        assert torch.equal(dgu, res[0][0]) and torch.equal(am, res[0][1]) and np.isfinite(am.item())

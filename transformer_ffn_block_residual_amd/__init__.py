@@ -24,7 +24,7 @@ _BINDING_NAMES = {
     "ffn_rmsnorm_bwd_scratch_bytes", "ffn_matmul_tn_swiglu_bwd_acc", "ffn_quant_transpose_clear", "ffn_swiglu_bwd_acc",
     "ffn_rmsnorm_bwd_acc", "ffn_tile_bytes", "ffn_tile_pack", "ffn_quant_absmax_clear_tiled", "ffn_gateup_acc_tiled",
     "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled", "ffn_rmsnorm_fwd_tiled", "ffn_gateup_tiled_bf16",
-    "ffn_down_tiled_bf16",
+    "ffn_down_tiled_bf16", "ffn_transpose_tiled", "ffn_quant_transpose_tiled", "FFN_TN_TILED",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "FFN_OK", "FFN_ERR_INVALID",
     "FFN_ERR_UNSUPPORTED", "FFN_ERR_HIP", "version", "last_error", "LIB_PATH",
 }

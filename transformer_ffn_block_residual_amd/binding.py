@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libffn.so")
 
 FFN_OK, FFN_ERR_INVALID, FFN_ERR_UNSUPPORTED, FFN_ERR_HIP = 0, 1, 2, 3
 FFN_BF16, FFN_E4M3, FFN_E5M2 = 0, 1, 2
-FFN_TN_ACCUMULATE, FFN_TN_TILE_GRID = 1, 2
+FFN_TN_ACCUMULATE, FFN_TN_TILE_GRID, FFN_TN_TILED = 1, 2, 4
 _STATUS = {1: "FFN_ERR_INVALID", 2: "FFN_ERR_UNSUPPORTED", 3: "FFN_ERR_HIP"}
 
 
@@ -72,6 +72,8 @@ def _load():
         "ffn_rmsnorm_fwd_tiled": [P, P, P, P, P, P, P, F32, I64, I64, P],
         "ffn_gateup_tiled_bf16": [P, P, P, P, I64, I64, I64, P],
         "ffn_down_tiled_bf16": [P, P, P, I64, I64, I64, P],
+        "ffn_transpose_tiled": [P, P, I64, I64, I64, P],
+        "ffn_quant_transpose_tiled": [P, P, P, P, P, P, I32, I64, I64, I64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -435,14 +437,15 @@ def ffn_decode_gemv_packed_noalloc(out, h, x, w_gate, s_gate, w_up, s_up, w_down
 
 def ffn_matmul_tn(out, a, a_scale, b, b_scale, dtype, flags, M, N, K, stream=None):
     """dtype FFN_BF16 / FFN_E4M3: both operands in it; FFN_E5M2: a holds e5m2
-    codes (the gradient), b e4m3 codes.  flags: FFN_TN_ACCUMULATE (or True)
-    and/or FFN_TN_TILE_GRID."""
+    codes (the gradient), b e4m3 codes.  flags: FFN_TN_ACCUMULATE (or True),
+    FFN_TN_TILE_GRID and/or FFN_TN_TILED (tiled FP8 operands)."""
     fp8 = dtype in (FFN_E4M3, FFN_E5M2)
     a_dt = E5M2 if dtype == FFN_E5M2 else _dt_elems(dtype)
     b_dt = E4M3 if fp8 else BF16
+    tl = int(flags) & FFN_TN_TILED
     _check(_lib.ffn_matmul_tn(
-        _ptr(out, "out", M * N, BF16), _ptr(a, "a", M * K, a_dt),
-        _ptr(a_scale, "a_scale", 1, F32, optional=not fp8), _ptr(b, "b", N * K, b_dt),
+        _ptr(out, "out", M * N, BF16), _ptr(a, "a", _tiled_numel(M, K) if tl else M * K, a_dt),
+        _ptr(a_scale, "a_scale", 1, F32, optional=not fp8), _ptr(b, "b", _tiled_numel(N, K) if tl else N * K, b_dt),
         _ptr(b_scale, "b_scale", 1, F32, optional=not fp8), int(dtype), int(flags),
         int(M), int(N), int(K), _stream(stream)))
 
@@ -451,16 +454,17 @@ def _matmul_tn_swiglu_bwd(fn, dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M,
     fp8 = dtype in (FFN_E4M3, FFN_E5M2)
     a_dt = E5M2 if dtype == FFN_E5M2 else _dt_elems(dtype)
     b_dt = E4M3 if fp8 else BF16
+    tl = int(flags) & FFN_TN_TILED
     _check(fn(
         _ptr(dgu, "dgu", M * 2 * H, BF16), _ptr(absmax, "absmax", 1, F32, optional=not acc),
-        _ptr(a, "a", M * K, a_dt), _ptr(a_scale, "a_scale", 1, F32, optional=not fp8),
-        _ptr(b, "b", H * K, b_dt), _ptr(b_scale, "b_scale", 1, F32, optional=not fp8),
+        _ptr(a, "a", _tiled_numel(M, K) if tl else M * K, a_dt), _ptr(a_scale, "a_scale", 1, F32, optional=not fp8),
+        _ptr(b, "b", _tiled_numel(H, K) if tl else H * K, b_dt), _ptr(b_scale, "b_scale", 1, F32, optional=not fp8),
         _ptr(gu, "gu", M * 2 * H, BF16), int(dtype), int(flags), int(M), int(H), int(K), _stream(stream)))
 
 
 def ffn_matmul_tn_swiglu_bwd(dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K, stream=None, flags=0):
     """dgu = SwiGLU backward of gu with dh = a b^T (never stored); dtype as
-    ffn_matmul_tn; flags 0 or FFN_TN_TILE_GRID.  dgu may be gu."""
+    ffn_matmul_tn; flags 0, FFN_TN_TILE_GRID and/or FFN_TN_TILED.  dgu may be gu."""
     _matmul_tn_swiglu_bwd(_lib.ffn_matmul_tn_swiglu_bwd, dgu, absmax, a, a_scale, b, b_scale, gu, dtype, M, H, K,
                           stream, flags, False)
 
@@ -496,6 +500,24 @@ def ffn_quant_transpose_clear(q_t, q, scale, x, absmax, clear, rows, cols, ld_ou
         _ptr(scale, "scale", 1, F32), _ptr(x, "x", rows * cols, BF16),
         _ptr(absmax, "absmax", 1, F32), _ptr(clear, "clear", 1, F32), int(code_dtype), int(rows), int(cols),
         int(ld_out), _stream(stream)))
+
+
+def ffn_transpose_tiled(out, inp, rows, cols, ld_out, stream=None):
+    """ffn_transpose of e4m3 codes with out [cols, ld_out] stored tiled."""
+    _check(_lib.ffn_transpose_tiled(
+        _ptr(out, "out", _tiled_numel(cols, ld_out), E4M3), _ptr(inp, "in", rows * cols, E4M3), int(rows),
+        int(cols), int(ld_out), _stream(stream)))
+
+
+def ffn_quant_transpose_tiled(q_t, q, scale, x, absmax, clear, rows, cols, ld_out, stream=None,
+                              code_dtype=FFN_E4M3):
+    """ffn_quant_transpose(_clear) with q_t and q stored tiled; clear may be None."""
+    dt = E5M2 if code_dtype == FFN_E5M2 else E4M3
+    _check(_lib.ffn_quant_transpose_tiled(
+        _ptr(q_t, "q_t", _tiled_numel(cols, ld_out), dt), _ptr(q, "q", _tiled_numel(rows, cols), dt, optional=True),
+        _ptr(scale, "scale", 1, F32), _ptr(x, "x", rows * cols, BF16), _ptr(absmax, "absmax", 1, F32),
+        _ptr(clear, "clear", 1, F32, optional=True), int(code_dtype), int(rows), int(cols), int(ld_out),
+        _stream(stream)))
 
 
 def ffn_swiglu_bwd(dgu, absmax, dh, gu, N, H, stream=None):
@@ -549,6 +571,6 @@ __all__ = [
     "ffn_rmsnorm_bwd_scratch_bytes",
     "ffn_tile_bytes", "ffn_tile_pack", "ffn_quant_absmax_clear_tiled", "ffn_gateup_acc_tiled",
     "ffn_gateup_swiglu_quant_tiled", "ffn_down_tiled", "ffn_rmsnorm_fwd_tiled", "ffn_gateup_tiled_bf16",
-    "ffn_down_tiled_bf16",
+    "ffn_down_tiled_bf16", "ffn_transpose_tiled", "ffn_quant_transpose_tiled", "FFN_TN_TILED",
     "FFN_DECODE_SPLIT_SILU", "FFN_DECODE_SILU_INPUT", "FFN_DECODE_PER_PROJECTION", "FFNError", "FFN_BF16", "FFN_E4M3", "FFN_E5M2", "FFN_TN_ACCUMULATE", "FFN_TN_TILE_GRID", "version", "last_error", "LIB_PATH",
 ]

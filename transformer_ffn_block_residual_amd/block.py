@@ -359,12 +359,21 @@ class BackwardBlock:
     form's bit for bit; afterwards am_dres holds max|d_res| (the upstream
     block's d_out_absmax) and am_dgu reads 0.  A bf16 block has no quantiser
     of these gradients and so takes no abs-max at all.  Chosen at
-    construction (the words start at zero then)."""
+    construction (the words start at zero then).
+    tiled (FP8 only): the four TN products read their operands (gradient,
+    weight and activation codes, as transposed or quantised here) in the
+    library's tiled layout (FFN_TN_TILED), which the transposing quantisers
+    and transposes write directly; gradients equal the row-major form's bit
+    for bit."""
 
     def __init__(self, fwd, in_place=True, grad_dtype="e4m3", fuse_swiglu_bwd=True, concurrent=False,
-                 zero_once=False):
+                 zero_once=False, tiled=False):
         if getattr(fwd, "tiled", False):
             raise ValueError("the backward takes a forward block with row-major operands (tiled=False)")
+        if tiled and not fwd.fp8:
+            raise ValueError("tiled backward operands are FP8 codes")
+        self.tiled = bool(tiled)
+        self._tn = B.FFN_TN_TILED if self.tiled else 0
         if grad_dtype not in ("e4m3", "e5m2"):
             raise ValueError(f"grad_dtype {grad_dtype!r}: need 'e4m3' or 'e5m2'")
         if grad_dtype == "e5m2" and not fwd.fp8:
@@ -391,7 +400,14 @@ class BackwardBlock:
         # zeroed here (the zero-once form relies on that)
         self.am_tab = torch.zeros(8, dtype=torch.float32, device="cuda")
         self.am_dout, self.am_dgu, self.am_dres = _f32(1), self.am_tab[0:1], self.am_tab[4:5]
-        if fwd.fp8:
+        if fwd.fp8 and self.tiled:
+            t = B.ffn_tile_bytes
+            self.qdout, self.s_dout = _u8(t(N, C)), _f32(1)
+            self.qdgu, self.s_dgu = _u8(t(N, 2 * H)), _f32(1)
+            self.wd_t, self.wgu_t = _u8(t(H, C)), _u8(t(C, 2 * H))
+            self.dout_t, self.h_t = _u8(t(C, self.Np)), _u8(t(H, self.Np))
+            self.dgu_t, self.y_t = _u8(t(2 * H, self.Np)), _u8(t(C, self.Np))
+        elif fwd.fp8:
             self.qdout, self.s_dout = _u8(N, C), _f32(1)
             self.qdgu, self.s_dgu = _u8(N, 2 * H), _f32(1)
             self.wd_t, self.wgu_t = _u8(H, C), _u8(C, 2 * H)
@@ -411,7 +427,7 @@ class BackwardBlock:
         else:
             am, fn = self.am_dgu, B.ffn_matmul_tn_swiglu_bwd
         fn(self.dgu, am, a, a_scale, self.wd_t, f.s_d if f.fp8 else None, self.gu, dtype, f.N, f.H, f.C, stream,
-           flags=flags)
+           flags=flags | self._tn)
 
     def _swiglu_bwd(self, stream):
         f = self.f
@@ -420,9 +436,28 @@ class BackwardBlock:
         else:
             B.ffn_swiglu_bwd(self.dgu, None if self.zero_once else self.am_dgu, self.dh, self.gu, f.N, f.H, stream)
 
+    def _transpose8(self, out, inp, rows, cols, ld_out, stream):
+        """Transposed e4m3 codes (tiled when the products read tiled operands)."""
+        if self.tiled:
+            B.ffn_transpose_tiled(out, inp, rows, cols, ld_out, stream)
+        else:
+            B.ffn_transpose(out, inp, rows, cols, ld_out, 1, stream)
+
+    def _quant_dout(self, d_out, E, stream):
+        f = self.f
+        if self.tiled:
+            B.ffn_quant_transpose_tiled(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, None, f.N, f.C,
+                                        self.Np, stream, E)
+        else:
+            B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, f.N, f.C, self.Np,
+                                  stream, E)
+
     def _quant_dgu(self, E, stream):
         f = self.f
-        if self.zero_once:
+        if self.tiled:
+            B.ffn_quant_transpose_tiled(self.dgu_t, self.qdgu, self.s_dgu, self.dgu, self.am_dgu,
+                                        self.am_dres if self.zero_once else None, f.N, 2 * f.H, self.Np, stream, E)
+        elif self.zero_once:
             B.ffn_quant_transpose_clear(self.dgu_t, self.qdgu, self.s_dgu, self.dgu, self.am_dgu, self.am_dres,
                                         f.N, 2 * f.H, self.Np, stream, E)
         else:
@@ -451,9 +486,12 @@ class BackwardBlock:
         f = self.f
         if self._wt_version == f.weights_version:
             return
-        e = 1 if f.fp8 else 2
-        B.ffn_transpose(self.wd_t, f.w_d, f.C, f.H, f.C, e, stream)
-        B.ffn_transpose(self.wgu_t, f.w_gu, 2 * f.H, f.C, 2 * f.H, e, stream)
+        if f.fp8:
+            self._transpose8(self.wd_t, f.w_d, f.C, f.H, f.C, stream)
+            self._transpose8(self.wgu_t, f.w_gu, 2 * f.H, f.C, 2 * f.H, stream)
+        else:
+            B.ffn_transpose(self.wd_t, f.w_d, f.C, f.H, f.C, 2, stream)
+            B.ffn_transpose(self.wgu_t, f.w_gu, 2 * f.H, f.C, 2 * f.H, 2, stream)
         self._wt_version = f.weights_version
         mk("transpose_weights")
 
@@ -502,17 +540,18 @@ class BackwardBlock:
                 B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, stream)
             else:
                 self.am_dout = d_out_absmax
-            B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, stream, E)
+            self._quant_dout(d_out, E, stream)
             mk("quant_dout")
+            TL = self._tn
             if self.fuse_swiglu_bwd:
                 self._swiglu_bwd_fused(self.qdout, self.s_dout, E, stream)
                 mk("dx_down_swiglu_bwd")
             else:
-                B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, 0, N, H, C, stream)
+                B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, TL, N, H, C, stream)
                 mk("dx_down")
-            B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, stream)
+            self._transpose8(self.h_t, f.qh, N, H, Np, stream)
             mk("transpose_down_operands")
-            B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, 1, C, H, Np, stream)
+            B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, 1 | TL, C, H, Np, stream)
             mk("dw_down")
             if not self.fuse_swiglu_bwd:
                 self._swiglu_bwd(stream)
@@ -520,11 +559,11 @@ class BackwardBlock:
             # backward_qmm through the up projection (input y, weight [2H, C])
             self._quant_dgu(E, stream)
             mk("quant_dgu")
-            B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, 0, N, C, 2 * H, stream)
+            B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, TL, N, C, 2 * H, stream)
             mk("dx_up")
-            B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, stream)
+            self._transpose8(self.y_t, f.qy, N, C, Np, stream)
             mk("transpose_up_operands")
-            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, 1, 2 * H, C, Np, stream)
+            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, 1 | TL, 2 * H, C, Np, stream)
             mk("dw_up")
         else:
             Bf = B.FFN_BF16
@@ -583,20 +622,21 @@ class BackwardBlock:
                 B.ffn_quant_absmax(self.qdout, self.s_dout, self.am_dout, d_out, N * C, 1, main)
             else:
                 self.am_dout = d_out_absmax
-            B.ffn_quant_transpose(self.dout_t, self.qdout, self.s_dout, d_out, self.am_dout, N, C, Np, main, E)
+            self._quant_dout(d_out, E, main)
+            TL = self._tn
             fork(0)
-            B.ffn_transpose(self.h_t, f.qh, N, H, Np, 1, side)
-            B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, ACC | T, C, H, Np, side)
+            self._transpose8(self.h_t, f.qh, N, H, Np, side)
+            B.ffn_matmul_tn(self.dw_d, self.dout_t, self.s_dout, self.h_t, f.s_h, E, ACC | T | TL, C, H, Np, side)
             if self.fuse_swiglu_bwd:
                 self._swiglu_bwd_fused(self.qdout, self.s_dout, E, main, flags=T)
             else:
-                B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, T, N, H, C, main)
+                B.ffn_matmul_tn(self.dh, self.qdout, self.s_dout, self.wd_t, f.s_d, E, T | TL, N, H, C, main)
                 self._swiglu_bwd(main)
             self._quant_dgu(E, main)
             fork(1)
-            B.ffn_transpose(self.y_t, f.qy, N, C, Np, 1, side)
-            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, ACC | T, 2 * H, C, Np, side)
-            B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, T, N, C, 2 * H, main)
+            self._transpose8(self.y_t, f.qy, N, C, Np, side)
+            B.ffn_matmul_tn(self.dw_gu, self.dgu_t, self.s_dgu, self.y_t, f.s_y, E, ACC | T | TL, 2 * H, C, Np, side)
+            B.ffn_matmul_tn(self.dy, self.qdgu, self.s_dgu, self.wgu_t, f.s_gu, E, T | TL, N, C, 2 * H, main)
         else:
             Bf = B.FFN_BF16
             fork(0)

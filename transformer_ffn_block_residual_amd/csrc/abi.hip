@@ -671,22 +671,26 @@ ffn_status_t ffn_matmul_tn(void* out, const void* a, const float* a_scale, const
     NONNEG(K);
     if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
         return fail(FFN_ERR_INVALID, "ffn_matmul_tn: unknown dtype %d", (int)dtype);
-    if (flags & ~(FFN_TN_ACCUMULATE | FFN_TN_TILE_GRID))
+    if (flags & ~(FFN_TN_ACCUMULATE | FFN_TN_TILE_GRID | FFN_TN_TILED))
         return fail(FFN_ERR_INVALID, "ffn_matmul_tn: unknown flags 0x%x", (unsigned)flags);
     const bool fp8 = dtype != FFN_BF16;
+    const bool tiled = (flags & FFN_TN_TILED) != 0;
     if (fp8) {
         REQUIRE(a_scale);
         REQUIRE(b_scale);
     }
+    if (tiled && !fp8) return fail(FFN_ERR_UNSUPPORTED, "ffn_matmul_tn: tiled operands are FP8 codes");
     const int elt = fp8 ? 1 : 2;
     if (ffn_status_t st = check_gemm_dims("ffn_matmul_tn", M, K, N, elt)) return st;
+    if (tiled && tiled_bytes(M, K) >= ((int64_t)1 << 32))
+        return fail(FFN_ERR_UNSUPPORTED, "ffn_matmul_tn: an operand exceeds 4 GiB");
     ALIGNED(out);
     ALIGNED(a);
     ALIGNED(b);
     if (out == a || out == b) return fail(FFN_ERR_INVALID, "ffn_matmul_tn: out must not alias an operand");
     return hip_status(ffn::launch_gemm(out, nullptr, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)N, stream,
                                        nullptr, nullptr, (flags & FFN_TN_ACCUMULATE) != 0, dtype == FFN_E5M2, nullptr,
-                                       (flags & FFN_TN_TILE_GRID) != 0),
+                                       (flags & FFN_TN_TILE_GRID) != 0, true, tiled),
                       "ffn_matmul_tn");
 }
 
@@ -701,11 +705,16 @@ static ffn_status_t matmul_tn_swiglu_bwd_entry(const char* fn, void* dgu, float*
     if (M < 0 || H < 0 || K < 0) return fail(FFN_ERR_INVALID, "%s: negative size", fn);
     if (dtype != FFN_BF16 && dtype != FFN_E4M3 && dtype != FFN_E5M2)
         return fail(FFN_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dtype);
-    if (flags & ~FFN_TN_TILE_GRID) return fail(FFN_ERR_INVALID, "%s: unknown flags 0x%x", fn, (unsigned)flags);
+    if (flags & ~(FFN_TN_TILE_GRID | FFN_TN_TILED))
+        return fail(FFN_ERR_INVALID, "%s: unknown flags 0x%x", fn, (unsigned)flags);
     const bool fp8 = dtype != FFN_BF16;
+    const bool tiled = (flags & FFN_TN_TILED) != 0;
     if (fp8 && !a_scale) return fail(FFN_ERR_INVALID, "%s: a_scale is NULL", fn);
     if (fp8 && !b_scale) return fail(FFN_ERR_INVALID, "%s: b_scale is NULL", fn);
+    if (tiled && !fp8) return fail(FFN_ERR_UNSUPPORTED, "%s: tiled operands are FP8 codes", fn);
     if (ffn_status_t st = check_gemm_dims(fn, M, K, H, fp8 ? 1 : 2)) return st;
+    if (tiled && tiled_bytes(M, K) >= ((int64_t)1 << 32))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: an operand exceeds 4 GiB", fn);
     if (H > kMaxDim / 2) return fail(FFN_ERR_UNSUPPORTED, "%s: H = %lld too large", fn, (long long)H);
     if (misaligned(dgu) || misaligned(a) || misaligned(b) || misaligned(gu))
         return fail(FFN_ERR_UNSUPPORTED, "%s: a buffer is not 16-byte aligned", fn);
@@ -714,7 +723,7 @@ static ffn_status_t matmul_tn_swiglu_bwd_entry(const char* fn, void* dgu, float*
         return fail(FFN_ERR_INVALID, "%s: absmax must not alias a_scale or b_scale", fn);
     return hip_status(ffn::launch_gemm(dgu, absmax, a, a_scale, b, b_scale, fp8, false, M, (int)K, (int)H, stream,
                                        nullptr, nullptr, false, dtype == FFN_E5M2, gu, (flags & FFN_TN_TILE_GRID) != 0,
-                                       clear_absmax),
+                                       clear_absmax, tiled),
                       fn);
 }
 
@@ -759,9 +768,31 @@ ffn_status_t ffn_transpose(void* out, const void* in, int64_t rows, int64_t cols
                       "ffn_transpose");
 }
 
+// The tiled output of a transposing call: rows of ld_out bytes (and, for the
+// row-layout codes q, of cols bytes), whole 64-row groups within 32-bit
+// offsets of one GEMM operand.
+static ffn_status_t check_tiled_transpose(const char* fn, int64_t rows, int64_t cols, int64_t ld_out) {
+    if (ld_out % 64 != 0 || cols % 64 != 0)
+        return fail(FFN_ERR_UNSUPPORTED, "%s: cols and ld_out must be multiples of 64", fn);
+    if (tiled_bytes(cols, ld_out) >= ((int64_t)1 << 32) || tiled_bytes(rows, cols) >= ((int64_t)1 << 32))
+        return fail(FFN_ERR_UNSUPPORTED, "%s: an output exceeds 4 GiB", fn);
+    return FFN_OK;
+}
+
+ffn_status_t ffn_transpose_tiled(uint8_t* out, const uint8_t* in, int64_t rows, int64_t cols, int64_t ld_out,
+                                 hipStream_t stream) {
+    REQUIRE(out);
+    REQUIRE(in);
+    if (ffn_status_t st = check_transpose("ffn_transpose_tiled", out, in, rows, cols, ld_out)) return st;
+    if (ffn_status_t st = check_tiled_transpose("ffn_transpose_tiled", rows, cols, ld_out)) return st;
+    return hip_status(ffn::launch_transpose(out, nullptr, nullptr, nullptr, in, rows, (int)cols, ld_out, 1, 1, stream,
+                                            false, nullptr, true),
+                      "ffn_transpose_tiled");
+}
+
 static ffn_status_t quant_transpose_entry(const char* fn, uint8_t* q_t, uint8_t* q, float* scale, const void* x,
                                           const float* absmax, float* clear, ffn_dtype_t code_dtype, int64_t rows,
-                                          int64_t cols, int64_t ld_out, hipStream_t stream) {
+                                          int64_t cols, int64_t ld_out, hipStream_t stream, bool tiled = false) {
     if (!q_t) return fail(FFN_ERR_INVALID, "%s: q_t is NULL", fn);
     if (!scale) return fail(FFN_ERR_INVALID, "%s: scale is NULL", fn);
     if (!x) return fail(FFN_ERR_INVALID, "%s: x is NULL", fn);
@@ -775,8 +806,10 @@ static ffn_status_t quant_transpose_entry(const char* fn, uint8_t* q_t, uint8_t*
     if ((const float*)scale == absmax) return fail(FFN_ERR_INVALID, "%s: scale and absmax alias", fn);
     if (clear && ((const float*)clear == absmax || clear == scale))
         return fail(FFN_ERR_INVALID, "%s: clear must not alias absmax or scale", fn);
+    if (tiled)
+        if (ffn_status_t st = check_tiled_transpose(fn, rows, cols, ld_out)) return st;
     return hip_status(ffn::launch_transpose(q_t, q, scale, absmax, x, rows, (int)cols, ld_out, 2, 1, stream,
-                                            code_dtype == FFN_E5M2, clear),
+                                            code_dtype == FFN_E5M2, clear, tiled),
                       fn);
 }
 
@@ -793,6 +826,13 @@ ffn_status_t ffn_quant_transpose_clear(uint8_t* q_t, uint8_t* q, float* scale, c
     REQUIRE(clear);
     return quant_transpose_entry("ffn_quant_transpose_clear", q_t, q, scale, x, absmax, clear, code_dtype, rows,
                                  cols, ld_out, stream);
+}
+
+ffn_status_t ffn_quant_transpose_tiled(uint8_t* q_t, uint8_t* q, float* scale, const void* x, const float* absmax,
+                                       float* clear, ffn_dtype_t code_dtype, int64_t rows, int64_t cols,
+                                       int64_t ld_out, hipStream_t stream) {
+    return quant_transpose_entry("ffn_quant_transpose_tiled", q_t, q, scale, x, absmax, clear, code_dtype, rows,
+                                 cols, ld_out, stream, true);
 }
 
 static ffn_status_t swiglu_bwd_entry(const char* fn, void* dgu, float* absmax, const void* dh, const void* gu,

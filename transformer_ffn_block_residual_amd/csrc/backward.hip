@@ -115,7 +115,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(uint8_t* __restrict__ ou
 // kBf8: the quantised codes are e5m2 (scale absmax / 57344) instead of e4m3.
 // clear (quantising only, nullable): another abs-max word, set to zero by the
 // first thread (the zero-once convention: the word of the next producer).
-template <int kIn, bool kQuant, bool kBf8 = false>
+// kTiledOut: out and q_rows are stored in the tiled GEMM operand layout
+// (common.h, tiled_offset; rows of ld_out and cols bytes); every store stays
+// one piece of an aligned 16-byte chunk.
+template <int kIn, bool kQuant, bool kBf8 = false, bool kTiledOut = false>
 __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ out, uint8_t* __restrict__ q_rows,
                                                          float* __restrict__ scale_out,
                                                          const float* __restrict__ absmax,
@@ -166,7 +169,8 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
             const int64_t gr = r0 + row;
             const int gc = c0 + cc * kInEl;
             if (q_rows && gr < rows && gc < cols)
-                *reinterpret_cast<uint2*>(q_rows + gr * cols + gc) = make_uint2(q0, q1);
+                *reinterpret_cast<uint2*>(q_rows + (kTiledOut ? tiled_offset(gr, gc, cols) : gr * cols + gc)) =
+                    make_uint2(q0, q1);
         } else {
             dst[0] = v[i].x;
             dst[1] = v[i].y;
@@ -191,7 +195,9 @@ __global__ __launch_bounds__(256) void transpose8_kernel(uint8_t* __restrict__ o
                    (((d[4 * e + 2] >> (8 * j)) & 0xffu) << 16) | (((d[4 * e + 3] >> (8 * j)) & 0xffu) << 24);
         const int go_row = c0 + 4 * cg + j;
         if (go_row < cols && go_col < ld_out)
-            *reinterpret_cast<uint4*>(out + (int64_t)go_row * ld_out + go_col) = make_uint4(w[0], w[1], w[2], w[3]);
+            *reinterpret_cast<uint4*>(out + (kTiledOut ? tiled_offset(go_row, go_col, ld_out)
+                                                       : (int64_t)go_row * ld_out + go_col)) =
+                make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
@@ -207,9 +213,26 @@ __global__ __launch_bounds__(64) void fp8_scale_kernel(float* __restrict__ scale
     }
 }
 
+template <bool kTiledOut>
+static void launch_transpose8(uint8_t* o, uint8_t* q_rows, float* scale, const float* absmax, const uint8_t* x,
+                              int64_t rows, int cols, int64_t ld_out, int in_bytes, hipStream_t s, bool e5m2,
+                              float* clear) {
+    const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((ld_out + 127) / 128)), block(256);
+    if (in_bytes == 1)
+        hipLaunchKernelGGL((transpose8_kernel<1, false, false, kTiledOut>), grid, block, 0, s, o, nullptr, nullptr,
+                           nullptr, x, rows, cols, ld_out, nullptr);
+    else if (e5m2)
+        hipLaunchKernelGGL((transpose8_kernel<2, true, true, kTiledOut>), grid, block, 0, s, o, q_rows, scale, absmax,
+                           x, rows, cols, ld_out, clear);
+    else
+        hipLaunchKernelGGL((transpose8_kernel<2, true, false, kTiledOut>), grid, block, 0, s, o, q_rows, scale,
+                           absmax, x, rows, cols, ld_out, clear);
+}
+
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
                             int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s,
-                            bool e5m2, float* clear) {
+                            bool e5m2, float* clear, bool tiled_out) {
+    if (tiled_out && out_bytes != 1) return hipErrorInvalidValue;
     if (cols == 0 || ld_out == 0) {
         // no codes to write; a quantising call still writes its scale (and
         // clears its word)
@@ -222,22 +245,14 @@ hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const floa
     }
     uint8_t* o = static_cast<uint8_t*>(out);
     const uint8_t* x = static_cast<const uint8_t*>(in);
-    const dim3 block(256);
     if (in_bytes == 2 && out_bytes == 2) {
-        const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((ld_out + 63) / 64));
+        const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((ld_out + 63) / 64)), block(256);
         hipLaunchKernelGGL((transpose_kernel<2, 2, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x, rows,
                            cols, ld_out);
+    } else if (tiled_out) {
+        launch_transpose8<true>(o, q_rows, scale, absmax, x, rows, cols, ld_out, in_bytes, s, e5m2, clear);
     } else {
-        const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((ld_out + 127) / 128));
-        if (in_bytes == 1)
-            hipLaunchKernelGGL((transpose8_kernel<1, false>), grid, block, 0, s, o, nullptr, nullptr, nullptr, x,
-                               rows, cols, ld_out, nullptr);
-        else if (e5m2)
-            hipLaunchKernelGGL((transpose8_kernel<2, true, true>), grid, block, 0, s, o, q_rows, scale, absmax, x,
-                               rows, cols, ld_out, clear);
-        else
-            hipLaunchKernelGGL((transpose8_kernel<2, true>), grid, block, 0, s, o, q_rows, scale, absmax, x, rows,
-                               cols, ld_out, clear);
+        launch_transpose8<false>(o, q_rows, scale, absmax, x, rows, cols, ld_out, in_bytes, s, e5m2, clear);
     }
     return hipGetLastError();
 }

@@ -410,11 +410,18 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[4][4], const GemmA
                         m = absmax_acc(absmax_acc(m, bf16lo(og[e])), bf16hi(og[e]));
                         m = absmax_acc(absmax_acc(m, bf16lo(ou[e])), bf16hi(ou[e]));
                     }
+                    // rows past N (and features past O) have offsets past the
+                    // range, so their stores are dropped; they stay out of the
+                    // abs-max too (with tiled operands their codes are whatever
+                    // the group's padding holds, so dh there need not be zero).
+                    // The mask is the sign of off - nrec, all ones in range: no
+                    // lane mask, as the scalar registers are all taken here.
+                    const uint32_t off = off_of(hb, gi);
+                    const uint32_t keep = (uint32_t)((int32_t)(off - nrec) >> 31);
                     // one running maximum, updated in order (left to itself the
                     // compiler regroups the whole chain and runs out of registers)
-                    amax = absmax_acc(amax, m);
+                    amax = absmax_acc(amax, __uint_as_float(__float_as_uint(m) & keep));
                     asm volatile("" : "+v"(amax));
-                    const uint32_t off = off_of(hb, gi);
                     __builtin_amdgcn_raw_buffer_store_b128(og, rsrc, off, 0, 0);
                     __builtin_amdgcn_raw_buffer_store_b128(ou, rsrc, off + up_off, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
@@ -542,7 +549,6 @@ void gemm_kernel(GemmArgs a) {
     static_assert(!(kFused && kAccum), "accumulation is a plain-output epilogue");
     static_assert(kFP8 || !kXBf8, "e5m2 x is an FP8 operand");
     static_assert(!(kSwiBwd && (kFused || kAccum)), "the SwiGLU backward is a plain-output epilogue of its own");
-    static_assert(!kTiled || (!kAccum && !kXBf8 && !kSwiBwd), "tiled operands: the forward products");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
     static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds the 160 KiB of a CU");
     constexpr int kStoreCnt = epilogue_stores<kFused>();
@@ -766,7 +772,7 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
                        hipStream_t s, const float* q_absmax, float* q_scale, bool accumulate, bool x_e5m2,
                        const void* swiglu_gu, bool tile_grid, bool clear_absmax, bool tiled) {
     if (x_e5m2 && (!fp8 || fuse_swiglu)) return hipErrorInvalidValue;
-    if (tiled && (accumulate || x_e5m2 || swiglu_gu || (!fp8 && q_absmax))) return hipErrorInvalidValue;
+    if (tiled && !fp8 && (accumulate || swiglu_gu || q_absmax)) return hipErrorInvalidValue;
     const bool swi = swiglu_gu != nullptr;
     if (swi && (fuse_swiglu || accumulate)) return hipErrorInvalidValue;
     if (absmax && (fuse_swiglu || swi || N == 0) && clear_absmax) {
@@ -798,9 +804,20 @@ hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_s
     const dim3 grid((unsigned)(KT >= kAhead && !tile_grid ? persistent_grid(T) : T)), block(kThreads);
     const bool acc = accumulate && !fuse_swiglu;
     if (tiled && fp8) {
-        if (quant) hipLaunchKernelGGL((gemm_kernel<true, true, true, false, false, false, true>), grid, block, 0, s, a);
+        if (swi && x_e5m2)
+            hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true, true, true>), grid, block, 0, s, a);
+        else if (swi)
+            hipLaunchKernelGGL((gemm_kernel<true, false, false, false, false, true, true>), grid, block, 0, s, a);
+        else if (quant)
+            hipLaunchKernelGGL((gemm_kernel<true, true, true, false, false, false, true>), grid, block, 0, s, a);
         else if (fuse_swiglu)
             hipLaunchKernelGGL((gemm_kernel<true, true, false, false, false, false, true>), grid, block, 0, s, a);
+        else if (acc && x_e5m2)
+            hipLaunchKernelGGL((gemm_kernel<true, false, false, true, true, false, true>), grid, block, 0, s, a);
+        else if (acc)
+            hipLaunchKernelGGL((gemm_kernel<true, false, false, true, false, false, true>), grid, block, 0, s, a);
+        else if (x_e5m2)
+            hipLaunchKernelGGL((gemm_kernel<true, false, false, false, true, false, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gemm_kernel<true, false, false, false, false, false, true>), grid, block, 0, s, a);
     } else if (tiled) {
         if (fuse_swiglu)

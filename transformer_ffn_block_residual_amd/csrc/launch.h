@@ -33,12 +33,14 @@ hipError_t launch_swiglu(uint16_t* h, float* absmax, const uint16_t* gu, int64_t
 // swiglu_gu (plain output, no accumulation): the product is dh = dL/dh of
 // h = silu(g) * u, rounded to bf16; out receives dgu [N, 2O] computed from
 // gu [N, 2O] (which out may be), and absmax max |dgu|.  tile_grid: one
-// workgroup per output tile (for products that run beside others).  tiled
-// (no accumulation, e5m2 or SwiGLU backward): x and w in the tiled layout
-// (whole 64-row groups; common.h, tiled_offset); the SwiGLU output is stored
-// in it too when it is a GEMM operand itself (the e4m3 codes of q_absmax, or
-// bf16 h of a bf16 product), row-major otherwise (bf16 h of an e4m3 product,
-// which a quantiser reads).
+// workgroup per output tile (for products that run beside others).  tiled:
+// x and w in the tiled layout (whole 64-row groups; common.h, tiled_offset),
+// with every epilogue for FP8 operands and the SwiGLU and plain ones for
+// bf16; the SwiGLU output is stored in it too when it is a GEMM operand
+// itself (the e4m3 codes of q_absmax, or bf16 h of a bf16 product),
+// row-major otherwise (bf16 h of an e4m3 product, which a quantiser reads;
+// the products and gradients of the plain, accumulating and SwiGLU-backward
+// epilogues).
 hipError_t launch_gemm(void* out, float* absmax, const void* x, const float* x_scale, const void* w,
                        const float* w_scale, bool fp8, bool fuse_swiglu, int64_t N, int K, int O,
                        hipStream_t s, const float* q_absmax = nullptr, float* q_scale = nullptr,
@@ -56,10 +58,12 @@ hipError_t launch_quant_tiled(uint8_t* q, float* scale, float* absmax, const uin
 // out_bytes) = (2, 2) bf16, (1, 1) e4m3 codes, (2, 1) bf16 quantised to e4m3
 // with *absmax on the way (scale written to *scale; q_rows, if not null, also
 // receives the codes in the input's [rows, cols] layout; e5m2: e5m2 codes;
-// clear, if not null, another abs-max word that the quantising pass zeroes).
+// clear, if not null, another abs-max word that the quantising pass zeroes;
+// tiled_out (byte outputs only): out and q_rows in the tiled GEMM operand
+// layout, rows of ld_out and cols bytes).
 hipError_t launch_transpose(void* out, uint8_t* q_rows, float* scale, const float* absmax, const void* in,
                             int64_t rows, int cols, int64_t ld_out, int in_bytes, int out_bytes, hipStream_t s,
-                            bool e5m2 = false, float* clear = nullptr);
+                            bool e5m2 = false, float* clear = nullptr, bool tiled_out = false);
 // clear_absmax == false: *absmax is max-accumulated into as found.
 hipError_t launch_swiglu_bwd(uint16_t* dgu, float* absmax, const uint16_t* dh, const uint16_t* gu, int64_t N, int H,
                              hipStream_t s, bool clear_absmax = true);
