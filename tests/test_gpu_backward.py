@@ -711,22 +711,26 @@ def test_block_backward_full_size_sampled(F, grad):
     assert rms_bwd_close(host_bits(bb.d_res)[rows], dres_ref, d_out[rows], g_dy, g_r, d["w_norm"], g_rstd)
 
 
-@pytest.mark.parametrize("fp8,grad,conc,zo", [(False, "e4m3", False, False), (True, "e4m3", False, False),
-                                              (True, "e5m2", False, False), (True, "e4m3", True, False),
-                                              (True, "e4m3", False, True)])
-def test_block_backward_replays_from_a_hip_graph(F, fp8, grad, conc, zo):
+@pytest.mark.parametrize("fp8,grad,conc,zo,tl", [(False, "e4m3", False, False, False),
+                                                 (True, "e4m3", False, False, False),
+                                                 (True, "e5m2", False, False, False),
+                                                 (True, "e4m3", True, False, False),
+                                                 (True, "e4m3", False, True, False),
+                                                 (True, "e4m3", False, True, True),
+                                                 (True, "e5m2", True, False, True)])
+def test_block_backward_replays_from_a_hip_graph(F, fp8, grad, conc, zo, tl):
     """Forward + backward (gradients zeroed first) captured once, replayed
     three times with eager work between, equals the eager result bit for bit;
     conc: the two-stream schedule, its second stream forked and joined inside
     the capture; zo: the zero-once abs-max form (its words cleared by the
-    captured kernels themselves)."""
-    say(f"block backward graph replay fp8={fp8} grad={grad} concurrent={conc} zero_once={zo}")
+    captured kernels themselves); tl: tiled operands."""
+    say(f"block backward graph replay fp8={fp8} grad={grad} concurrent={conc} zero_once={zo} tiled={tl}")
     from transformer_ffn_block_residual_amd import block
     N, C, H = 200, 384, 256
     d = W.block_inputs(N, C, H, seed=41, w_std=0.1)
     pb = block.PrefillBlock(N, C, H, 1e-5, fp8)
     pb.load_weights(d["w_norm"], d["w_gu"], d["w_d"])
-    bb = block.BackwardBlock(pb, in_place=False, grad_dtype=grad, concurrent=conc, zero_once=zo)
+    bb = block.BackwardBlock(pb, in_place=False, grad_dtype=grad, concurrent=conc, zero_once=zo, tiled=tl)
     inp, add = dev_bf16(d["inp"]), dev_bf16(d["addend"])
     d_out = dev_bf16(rand_bits((N, C), 1.0, 42))
 
