@@ -214,14 +214,14 @@ ffn_status_t ffn_down(void* out, const void* h, const float* h_scale,
  * the quantisers for the activations.
  *
  * Layout of a [R, K] operand (K bytes per row, K % 64 == 0; e4m3 codes or
- * bf16 values alike): rows in
- * groups of 64, group g at byte g*64*K; inside a group, K-step s (bytes
- * 64s .. 64s+63 of each row) at s*4096, and its 16-row sub-group i at
- * + i*1024; there, lane l = 0..63 holds 16 bytes at + 16*l: bytes
- * 16*((l % 4) XOR (l / 16)) .. +15 of K-step s of row 64g + 16i + l/4.  A
- * tiled buffer holds whole groups: ffn_tile_bytes(R, K) = ceil(R/64)*64*K
- * bytes; the rows past R in the last group are don't-care for the GEMMs (a
- * token row only feeds its own output row, which is not stored). */
+ * bf16 values alike): rows in groups of 64, group g at byte g*64*K; inside
+ * a group, K-step s (bytes 64s .. 64s+63 of each row) at s*4096, and its
+ * 16-row sub-group i at + i*1024; there, lane l = 0..63 holds 16 bytes at
+ * + 16*l: bytes 16*((l % 4) XOR (l / 16)) .. +15 of K-step s of row
+ * 64g + 16i + l/4.  A tiled buffer holds whole groups: ffn_tile_bytes(R, K)
+ * = ceil(R/64)*64*K bytes; the rows past R in the last group are don't-care
+ * for the GEMMs (a token row only feeds its own output row, which is
+ * neither stored nor counted in an abs-max). */
 
 /* Bytes of the tiled form of [rows, row_bytes] (-1 if row_bytes % 64 != 0
  * or a size is negative). */
