@@ -237,8 +237,9 @@ ffn_status_t ffn_tile_pack(void* out, const void* in, int64_t rows, int64_t row_
 /* ffn_quant_absmax_clear for a [rows, cols] bf16 x whose codes are stored in
  * the tiled layout (the same codes, moved): *scale = A/448 (1 if A == 0),
  * q = e4m3(x * 448/A), A = *absmax; clear (nullable) is zeroed.  q:
- * ffn_tile_bytes(rows, cols) bytes (rows past `rows` are left as found).
- * Supported: cols % 128 == 0, cols <= 2^20, ffn_tile_bytes(rows, cols) <= 2^36. */
+ * ffn_tile_bytes(rows, cols) bytes (rows past `rows` are left as found),
+ * must not overlap x.  Supported: cols % 128 == 0, cols <= 2^20,
+ * ffn_tile_bytes(rows, cols) <= 2^36. */
 ffn_status_t ffn_quant_absmax_clear_tiled(uint8_t* q, float* scale, const float* absmax,
                                           const void* x, int64_t rows, int64_t cols, float* clear,
                                           hipStream_t stream);

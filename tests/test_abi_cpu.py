@@ -167,8 +167,9 @@ def test_tiled_layout_validation(lib):
     assert q(A, S, M, A, 64, 256, S, None) == INVALID      # clear aliases scale
     assert q(A, S, M, A, 64, 192, Z, None) == UNSUPPORTED  # cols % 128
     assert q(A, S, M, A, -2, 256, None, None) == INVALID
-    assert q(A, S, M, MIS, 64, 256, None, None) == UNSUPPORTED
+    assert q(A, S, M, 0x900004, 64, 256, None, None) == UNSUPPORTED     # misaligned x
     assert q(None, S, M, A, 64, 256, None, None) == INVALID
+    assert q(0x100000 + 1024, S, M, 0x100000, 64, 256, None, None) == INVALID   # q overlaps x
     g = lib.ffn_gateup_acc_tiled               # h, h_absmax, x, xs, w, ws, N, C, H
     assert g(A, M, A, None, A, S, 64, 256, 768, None) == INVALID           # no x_scale
     assert g(A, M, A, M, A, S, 64, 256, 768, None) == INVALID              # abs-max aliases x_scale

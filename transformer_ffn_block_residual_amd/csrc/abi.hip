@@ -388,6 +388,9 @@ ffn_status_t ffn_quant_absmax_clear_tiled(uint8_t* q, float* scale, const float*
     if (rows > ((int64_t)1 << 36) / cols || tiled_bytes(rows, cols) > ((int64_t)1 << 36) ||
         (rows + 1) / 2 * ((cols / 64 + 7) / 8) * 64 >= ((int64_t)1 << 32))
         return fail(FFN_ERR_UNSUPPORTED, "ffn_quant_absmax_clear_tiled: too large");
+    // a row's tiled codes land among the bytes of its whole 64-row group
+    if (overlaps(q, tiled_bytes(rows, cols), x, rows * cols * 2))
+        return fail(FFN_ERR_INVALID, "ffn_quant_absmax_clear_tiled: q must not overlap x");
     ALIGNED(q);
     ALIGNED(x);
     return hip_status(ffn::launch_quant_tiled(q, scale, const_cast<float*>(absmax), (const uint16_t*)x, rows, cols,
