@@ -962,6 +962,14 @@ def main():
             sub = bench_decode(sa, torch, np, B, block, W) if name == "decode" else \
                 bench_block(sa, torch, np, B, block, W)
             out["configs"][name] = {k: sub[k] for k in SUB_KEYS if k in sub}
+        # and the FP8 block's backward at the same shape
+        gc.collect()
+        torch.cuda.empty_cache()
+        sa = copy.copy(a)
+        sa.workload, sa.backward = "qwen7b8", True
+        print("[bench] configuration backward", file=sys.stderr, flush=True)
+        sub = bench_backward(sa, torch, np, B, block, W)
+        out["configs"]["backward"] = {k: sub[k] for k in SUB_KEYS if k in sub}
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
