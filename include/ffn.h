@@ -343,11 +343,12 @@ ffn_status_t ffn_decode_gemv_bf16(void* out, void* h, const void* x,
 
 /* Packed decode weights: the same e4m3 codes re-laid so that the few-token
  * decode (faster than on row-major weights from three tokens on, up to 32)
- * streams each 16-row block as one contiguous run,
- * one KiB per load instruction, in the order the MFMA consumes it.
+ * reads one KiB (16 rows x 64 codes) per load instruction, in the order the
+ * MFMA consumes it, and its waves, each walking its own 16-row blocks along
+ * K, read neighbouring KiBs at any one moment (piece-major).
  * packed: e4m3, rows * cols bytes; 16-byte piece p holds row 16 rb + l % 16,
  * codes 64 kc + 16 (l / 16) .. + 15 of w, where l = p % 64 and
- * p / 64 = rb * (cols / 64) + kc.  A one-time re-layout of the QuantizedWeight
+ * p / 64 = kc * (rows / 16) + rb.  A one-time re-layout of the QuantizedWeight
  * rows of [metrale] DenseFfnLayer::forward (FP8 arm); the row scales are
  * unchanged.  Supported: rows % 16 == 0, cols % 128 == 0; packed must not
  * alias w. */

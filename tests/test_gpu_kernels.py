@@ -592,13 +592,13 @@ def test_decode_bf16_weights(F, M, C, H):
 def test_decode_pack_weight_layout(F, rows, cols):
     """The packed layout is the re-indexing the header defines: piece p = row
     16 rb + l % 16, codes 64 kc + 16 (l / 16) .. + 15, l = p % 64,
-    p / 64 = rb * cols / 64 + kc."""
+    p / 64 = kc * rows / 16 + rb."""
     say(f"decode pack rows={rows} cols={cols}")
     w = np.random.default_rng(rows + cols).integers(0, 256, (rows, cols)).astype(np.uint8)
     out = empty_u8(rows, cols).fill_(0)
     F.ffn_decode_pack_weight(out, dev_u8(w), rows, cols)
     torch.cuda.synchronize()
-    want = w.reshape(rows // 16, 16, cols // 64, 4, 16).transpose(0, 2, 3, 1, 4).reshape(rows, cols)
+    want = w.reshape(rows // 16, 16, cols // 64, 4, 16).transpose(2, 0, 3, 1, 4).reshape(rows, cols)
     assert np.array_equal(host_u8(out).reshape(rows, cols), want)
 
 
