@@ -602,8 +602,8 @@ def test_decode_pack_weight_layout(F, rows, cols):
     assert np.array_equal(host_u8(out).reshape(rows, cols), want)
 
 
-# Up to 12 tokens the dual pass loads the activations with every item's
-# weights (at any C: (3, 4224, 256) is past the LDS copy's limit); from 13 to
+# Up to 14 tokens the dual pass loads the activations with every item's
+# weights (at any C: (3, 4224, 256) is past the LDS copy's limit); from 15 to
 # 16 tokens with C <= 4096 it keeps them in LDS (a half last chunk at C = 640;
 # C = 4096 fills the LDS copy), above C = 4096 it reads them from the
 # fragment-order copy in the workspace.  Up to
@@ -614,7 +614,8 @@ def test_decode_pack_weight_layout(F, rows, cols):
 # decode under 4-way tensor parallelism.
 PACKED_SHAPES = [(1, 1152, 640), (5, 3584, 384), (16, 384, 896), (16, 3584, 18944), (3, 4224, 256), (17, 256, 640),
                  (32, 256, 256), (1, 1152, 4096), (5, 4096, 4096), (16, 384, 8192), (13, 640, 4096),
-                 (16, 4096, 14336), (2, 128, 128), (9, 128, 8192), (16, 8192, 256), (16, 3584, 4736)]
+                 (16, 4096, 14336), (2, 128, 128), (9, 128, 8192), (16, 8192, 256), (16, 3584, 4736),
+                 (14, 640, 1024), (15, 640, 1024)]
 
 
 @pytest.mark.parametrize("M,C,H", PACKED_SHAPES)

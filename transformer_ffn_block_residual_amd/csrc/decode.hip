@@ -113,9 +113,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(
     // Chunks go to the waves round-robin.  Each workgroup starts its walk
     // along K at a different chunk, so the rows that the workgroups stream at
     // one moment are not all at the same column offset (with power-of-two row
-    // lengths those addresses crowd the same HBM channels).
+    // lengths those addresses crowd the same HBM channels).  Packed weights
+    // are piece-major: there every workgroup starts at chunk 0, so that the
+    // workgroups sweep each matrix in address order (about 1 us faster).
     const int nchunks = (K + kChunk - 1) / kChunk;  // K % 128 == 0: the last chunk may be half
-    const int rot = (int)(((unsigned)blockIdx.x * 5u) % (unsigned)nchunks);
+    const int rot = kPacked ? 0 : (int)(((unsigned)blockIdx.x * 5u) % (unsigned)nchunks);
     for (int cw = wave; cw < nchunks; cw += kWaves) {
         const int c = cw + rot < nchunks ? cw + rot : cw + rot - nchunks;
         const int kb = c * kChunk;
@@ -253,8 +255,9 @@ constexpr int kLdsDualMaxK = 4096;
 // weights (two 16-byte loads per piece and lane, rows past M read as
 // zeros): the copy costs every CU the whole of x before it can start (about
 // 3.6 us at 16 tokens of 3584), the per-item loads cost L1 and L2 traffic in
-// proportion to the tokens; at the Qwen2-7B shape the loads are 1-3.5 us
-// faster up to 12 tokens and the copy 1.3 us faster at 16.  K % 128 == 0,
+// proportion to the tokens; at the Qwen2-7B shape the loads are faster up to
+// 14 tokens (0.6-1.4 us at 13 and 14) and the copy 0.7-1.3 us faster at 16.
+// K % 128 == 0,
 // rows % 16 == 0, M <= 16; with kXLds K <= kLdsDualMaxK.
 template <int kU, bool kXLds>
 struct DualBuf {
@@ -909,7 +912,7 @@ static hipError_t launch_packed_tb(uint16_t* out, uint16_t* h, uint16_t* xp, uin
 // (the dual pass with x in LDS, and with x loaded per item), and the most
 // tokens that load x per item
 constexpr int kWaveDualWaves = 8, kWaveDualU = 8, kWaveDualRegU = 2, kDownSplitU = 8;
-constexpr int kDualRegMaxM = 12;
+constexpr int kDualRegMaxM = 14;
 
 hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const uint16_t* x, const uint8_t* wg,
                                 const float* sg, const uint8_t* wu, const float* su, const uint8_t* wd,
@@ -917,7 +920,7 @@ hipError_t launch_decode_packed(uint16_t* out, uint16_t* h, uint16_t* ws, const 
     if (M == 0) return hipSuccess;
     hipError_t e;
     if (M <= 16) {
-        uint16_t* xp = ws;                 // [16 C] fragment order (more than 12 tokens and C > kLdsDualMaxK)
+        uint16_t* xp = ws;                 // [16 C] fragment order (more than kDualRegMaxM tokens and C > kLdsDualMaxK)
         uint16_t* hp = ws + (int64_t)16 * C;  // [16 H]
         float* part = reinterpret_cast<float*>(ws + (int64_t)16 * (C + H));  // [S][16][C]
         // one persistent workgroup per CU (with x in LDS it fills most of the
